@@ -1,0 +1,191 @@
+"""ctypes front end of the CPU oracle (kascade_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg. The product library never imports or calls it.
+
+All inputs are numpy float32 arrays (bf16 values are exactly representable);
+all floating outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kascade_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkascade_oracle.so")
+_lib = None
+
+_i32, _i64, _dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+_fp = ctypes.POINTER(ctypes.c_float)
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_lp = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O3, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.orc_topk_count.argtypes = [_i64, _i32]
+        L.orc_topk_count.restype = _i64
+        L.orc_prefill_offsets.argtypes = [_i64, _i32, _i32, _lp]
+        L.orc_prefill_offsets.restype = _i64
+        L.orc_dense_attention.argtypes = [_fp, _fp, _fp, _dp, _i32, _i32, _i32, _i64, _i64,
+                                          _i32, _i32, _dbl]
+        L.orc_decode_anchor.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _dbl,
+                                        _ip, _dp, _dp]
+        L.orc_decode_reuse.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _dbl,
+                                       _ip, _i32, _i64, _ip, _dp]
+        L.orc_prefill_pooled.argtypes = [_fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _dbl,
+                                         _i64, _i64, _i64, _i64, _i64, _dp]
+        L.orc_prefill_anchor.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                         _dbl, _i64, _i64, _ip, _dp]
+        L.orc_prefill_reuse.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                        _dbl, _i64, _i64, _ip, _i32, _ip, _dp]
+        for name in ("orc_dense_attention", "orc_decode_anchor", "orc_decode_reuse",
+                     "orc_prefill_pooled", "orc_prefill_anchor", "orc_prefill_reuse"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.float32 or not a.flags.c_contiguous:
+        a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _i32a(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with status {rc}")
+
+
+def topk_count(n: int, pct: int) -> int:
+    return int(lib().orc_topk_count(n, pct))
+
+
+def decode_k(n: int, pct: int) -> int:
+    return max(1, topk_count(n, pct)) if n >= 1 else 0
+
+
+def prefill_offsets(n: int, tile: int, pct: int) -> np.ndarray:
+    T = (n + tile - 1) // tile
+    off = np.zeros(T + 1, dtype=np.int64)
+    lib().orc_prefill_offsets(n, tile, pct, _ptr(off, _lp))
+    return off
+
+
+def dense_attention(q, k, v, causal: bool, scale: float = 0.0) -> np.ndarray:
+    """q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] -> o [B,Hq,Nq,D] (float64)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    o = np.zeros((B, Hq, Nq, D), dtype=np.float64)
+    _check(lib().orc_dense_attention(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(o, _dp),
+                                     B, Hq, Hkv, Nq, Nk, D, int(causal), scale), "dense")
+    return o
+
+
+def decode_anchor(q, k, v, pct: int, scale: float = 0.0, want_pooled: bool = False
+                  ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hkv,kk], o [B,Hq,D], pooled [B,Hkv,N])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, Hq, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    kk = decode_k(N, pct)
+    idx = np.zeros((B, Hkv, kk), dtype=np.int32)
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    pooled = np.zeros((B, Hkv, N), dtype=np.float64) if want_pooled else None
+    _check(lib().orc_decode_anchor(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
+                                   pct, scale, _ptr(idx, _ip), _ptr(o, _dp),
+                                   _ptr(pooled, _dp) if want_pooled else None), "decode_anchor")
+    return idx, o, pooled
+
+
+def decode_reuse(q, k, v, anchor_idx, head_map, scale: float = 0.0) -> np.ndarray:
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    anchor_idx, head_map = _i32a(anchor_idx), _i32a(head_map)
+    B, Hq, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    Hkv_a, kk = anchor_idx.shape[1], anchor_idx.shape[2]
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    _check(lib().orc_decode_reuse(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
+                                  scale, _ptr(anchor_idx, _ip), Hkv_a, kk, _ptr(head_map, _ip),
+                                  _ptr(o, _dp)), "decode_reuse")
+    return o
+
+
+def prefill_anchor(q_rows, k, v, pct: int, tile: int = 32, t0: int = 0, t1: Optional[int] = None,
+                   scale: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
+    """q_rows [B,Hq,R,D] = query rows of tiles [t0,t1); k/v [B,Hkv,N,D].
+
+    Returns (idx int32 [B,Hkv,off[t1]-off[t0]], o float64 [B,Hq,R,D])."""
+    q_rows, k, v = _f32(q_rows), _f32(k), _f32(v)
+    B, Hq, R, D = q_rows.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    T = (N + tile - 1) // tile
+    t1 = T if t1 is None else t1
+    off = prefill_offsets(N, tile, pct)
+    assert R == min(N, tile * t1) - tile * t0, "q_rows must hold exactly the tile range"
+    idx = np.zeros((B, Hkv, int(off[t1] - off[t0])), dtype=np.int32)
+    o = np.zeros((B, Hq, R, D), dtype=np.float64)
+    _check(lib().orc_prefill_anchor(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
+                                    D, tile, pct, scale, t0, t1, _ptr(idx, _ip), _ptr(o, _dp)),
+           "prefill_anchor")
+    return idx, o
+
+
+def prefill_pooled(q_rows, k, b: int, t: int, g: int, tile: int = 32, t0: int = 0,
+                   t1: Optional[int] = None, scale: float = 0.0) -> np.ndarray:
+    q_rows, k = _f32(q_rows), _f32(k)
+    B, Hq, R, D = q_rows.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    T = (N + tile - 1) // tile
+    t1 = T if t1 is None else t1
+    P = np.zeros(min(N, tile * (t + 1)), dtype=np.float64)
+    _check(lib().orc_prefill_pooled(_ptr(q_rows, _fp), _ptr(k, _fp), B, Hq, Hkv, N, D, tile,
+                                    scale, t0, t1, b, t, g, _ptr(P, _dp)), "prefill_pooled")
+    return P
+
+
+def prefill_reuse(q_rows, k, v, anchor_idx, head_map, pct: int, tile: int = 32, t0: int = 0,
+                  t1: Optional[int] = None, scale: float = 0.0) -> np.ndarray:
+    """anchor_idx: the anchor's FULL CSR array [B, Hkv_a, total]."""
+    q_rows, k, v = _f32(q_rows), _f32(k), _f32(v)
+    anchor_idx, head_map = _i32a(anchor_idx), _i32a(head_map)
+    B, Hq, R, D = q_rows.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    T = (N + tile - 1) // tile
+    t1 = T if t1 is None else t1
+    o = np.zeros((B, Hq, R, D), dtype=np.float64)
+    _check(lib().orc_prefill_reuse(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
+                                   D, tile, pct, scale, t0, t1, _ptr(anchor_idx, _ip),
+                                   anchor_idx.shape[1], _ptr(head_map, _ip), _ptr(o, _dp)),
+           "prefill_reuse")
+    return o

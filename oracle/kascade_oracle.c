@@ -1,0 +1,522 @@
+/*
+ * kascade_oracle.c -- plain, slow CPU reference of Kascade's cross-layer
+ * Top-k sparse attention (decode and prefill, anchor and reuse layers).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header or constant with the
+ * HIP library.
+ *
+ * What it follows (pages: "microsoft/kascade" README, abstract; the
+ * "I/O complexity of attention" abstract on thelatestinai.com/papers/2510.01718):
+ *   - Dense attention is the textbook A = softmax(Q K^T / sqrt(d)) V
+ *     (I/O-complexity abstract).
+ *   - Anchor layers compute exact post-softmax scores, pool them per KV head
+ *     over the query heads that share it (the abstract's "head-aware"
+ *     selection; GQA grouping h -> h / G), and in prefill also over each
+ *     32-query tile (abstract: "tile-level operations"; README notes: tile
+ *     size 32), then take the exact Top-k key indices, k given as a percentage
+ *     (README: "k=10", "--topk 10").
+ *   - Reuse layers attend only over an anchor's index set, read through a
+ *     per-KV-head map to an anchor KV head (abstract: indices reused in
+ *     intermediate layers, head-aware; README "Running Evaluations": head
+ *     mappings stored per model).
+ * Readings taken where the pages are silent (each one is a documented
+ * choice, not something the pages state):
+ *   - pooling is the SUM of each head's own softmax probabilities (each head
+ *     normalised over its full causal row first);
+ *   - k = round-half-up(pct * n / 100), clamped to [0, n]; decode uses at
+ *     least 1 key;
+ *   - exact ties are broken toward the lower key index; the decision is
+ *     taken on the pooled score rounded to fp32 (the precision in which the
+ *     GPU path takes it); index sets are stored in ascending order;
+ *   - prefill tile t (rows [32t, 32t+32)) selects from the keys before the
+ *     tile, [0, 32t), and always adds its own causal diagonal block;
+ *     tile 0 selects nothing;
+ *   - the output of a selected set is attention renormalised over that set
+ *     (prefill: the set plus the causal diagonal keys of the row);
+ *   - query head h uses KV head h / G.
+ *
+ * Arithmetic is IEEE double throughout (inputs arrive as float, which holds
+ * bf16 values exactly). Work units are independent and each is computed by
+ * one thread in a fixed order, so results do not depend on the thread count.
+ *
+ * Status codes: 0 ok, 1 bad argument, 2 allocation failure, 3 index out of
+ * range in a supplied index set.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD_ARG 1
+#define ORC_NOMEM 2
+#define ORC_BAD_INDEX 3
+
+/* ------------------------------------------------------------------ */
+/* k rule                                                              */
+/* ------------------------------------------------------------------ */
+
+/* round-half-up(pct * n / 100), clamped to [0, n]. */
+int64_t orc_topk_count(int64_t n, int32_t pct)
+{
+    if (n <= 0 || pct <= 0) return 0;
+    int64_t k = ((int64_t)pct * n + 50) / 100;
+    if (k > n) k = n;
+    if (k < 0) k = 0;
+    return k;
+}
+
+static int64_t decode_k(int64_t n, int32_t pct)
+{
+    int64_t k = orc_topk_count(n, pct);
+    if (k < 1 && n >= 1) k = 1;
+    return k;
+}
+
+/* Number of tiles and per-tile index-set offsets (CSR) for prefill.
+ * offsets has n_tiles + 1 entries; returns the total index count. */
+int64_t orc_prefill_offsets(int64_t n, int32_t tile, int32_t pct, int64_t *offsets)
+{
+    int64_t T = (n + tile - 1) / tile;
+    int64_t acc = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (offsets) offsets[t] = acc;
+        acc += orc_topk_count(t * (int64_t)tile, pct);
+    }
+    if (offsets) offsets[T] = acc;
+    return acc;
+}
+
+/* ------------------------------------------------------------------ */
+/* small helpers                                                       */
+/* ------------------------------------------------------------------ */
+
+static double dot_scaled(const float *a, const float *b, int D, double scale)
+{
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += (double)a[d] * (double)b[d];
+    return acc * scale;
+}
+
+typedef struct { float val; int64_t idx; } orc_pair;
+
+/* Order: larger value first; equal values -> lower index first. */
+static int cmp_pair(const void *pa, const void *pb)
+{
+    const orc_pair *a = (const orc_pair *)pa, *b = (const orc_pair *)pb;
+    if (a->val > b->val) return -1;
+    if (a->val < b->val) return 1;
+    if (a->idx < b->idx) return -1;
+    if (a->idx > b->idx) return 1;
+    return 0;
+}
+
+static int cmp_i32(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/* Exact Top-k of `score` (n entries) under (value desc, index asc), values
+ * compared after rounding to float. Writes k indices in ascending order. */
+static int select_topk(const double *score, int64_t n, int64_t k, int32_t *out)
+{
+    if (k <= 0) return ORC_OK;
+    orc_pair *p = (orc_pair *)malloc((size_t)n * sizeof(orc_pair));
+    if (!p) return ORC_NOMEM;
+    for (int64_t j = 0; j < n; ++j) { p[j].val = (float)score[j]; p[j].idx = j; }
+    qsort(p, (size_t)n, sizeof(orc_pair), cmp_pair);
+    for (int64_t i = 0; i < k; ++i) out[i] = (int32_t)p[i].idx;
+    free(p);
+    qsort(out, (size_t)k, sizeof(int32_t), cmp_i32);
+    return ORC_OK;
+}
+
+/* Softmax-weighted sum of V rows over the key list `keys` (n_keys entries)
+ * given their logits: o = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m). */
+static void weighted_rows(const double *logit, const int64_t *keys, int64_t n_keys,
+                          const float *vbase, int D, double *o)
+{
+    double m = -INFINITY;
+    for (int64_t a = 0; a < n_keys; ++a) if (logit[a] > m) m = logit[a];
+    double l = 0.0;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t a = 0; a < n_keys; ++a) {
+        double e = exp(logit[a] - m);
+        l += e;
+        const float *vr = vbase + keys[a] * (int64_t)D;
+        for (int d = 0; d < D; ++d) o[d] += e * (double)vr[d];
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+}
+
+static int check_shape(int B, int Hq, int Hkv, int64_t N, int D)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || D <= 0) return ORC_BAD_ARG;
+    if (Hq % Hkv) return ORC_BAD_ARG;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* dense attention (the textbook definition)                          */
+/* ------------------------------------------------------------------ */
+
+/* q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], o [B,Hq,Nq,D]. With causal != 0, query
+ * row i sees keys j <= i + (Nk - Nq) (its position at the end of the key
+ * sequence). scale <= 0 means 1/sqrt(D). */
+int orc_dense_attention(const float *q, const float *k, const float *v, double *o,
+                        int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int D,
+                        int causal, double scale)
+{
+    if (check_shape(B, Hq, Hkv, Nk, D) || Nq <= 0 || Nq > Nk) return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    const int G = Hq / Hkv;
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Nk * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)Nk * sizeof(int64_t));
+        if (!s || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+            for (int64_t j = 0; j < Nk; ++j) keys[j] = j;
+#pragma omp for collapse(2) schedule(dynamic)
+            for (int64_t bh = 0; bh < (int64_t)B * Hq; ++bh) {
+                for (int64_t i = 0; i < Nq; ++i) {
+                    int64_t b = bh / Hq, h = bh % Hq, g = h / G;
+                    const float *qi = q + ((b * Hq + h) * Nq + i) * D;
+                    const float *kb = k + (b * Hkv + g) * Nk * D;
+                    const float *vb = v + (b * Hkv + g) * Nk * D;
+                    int64_t nvis = causal ? (i + (Nk - Nq) + 1) : Nk;
+                    for (int64_t j = 0; j < nvis; ++j) s[j] = dot_scaled(qi, kb + j * D, D, scale);
+                    weighted_rows(s, keys, nvis, vb, D, o + ((b * Hq + h) * Nq + i) * D);
+                }
+            }
+        }
+        free(s);
+        free(keys);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* decode                                                              */
+/* ------------------------------------------------------------------ */
+
+/* Anchor layer, one new token per sequence.
+ * q [B,Hq,D]; k/v [B,Hkv,N,D]; idx_out [B,Hkv,kk] (kk = decode k);
+ * o_out [B,Hq,D]; pooled_out [B,Hkv,N] or NULL.
+ * For each (b, g): every query head of the group gets its softmax over all N
+ * keys; the probabilities are summed over the group; the Top-k of that pooled
+ * score is the index set; each head's output is attention over the set. */
+int orc_decode_anchor(const float *q, const float *k, const float *v,
+                      int B, int Hq, int Hkv, int64_t N, int D, int32_t pct, double scale,
+                      int32_t *idx_out, double *o_out, double *pooled_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || pct < 1 || pct > 100) return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    const int G = Hq / Hkv;
+    const int64_t kk = decode_k(N, pct);
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)G * N * sizeof(double));
+        double *P = (double *)malloc((size_t)N * sizeof(double));
+        double *mrow = (double *)malloc((size_t)G * sizeof(double));
+        double *lrow = (double *)malloc((size_t)G * sizeof(double));
+        double *sel = (double *)malloc((size_t)kk * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)kk * sizeof(int64_t));
+        if (!s || !P || !mrow || !lrow || !sel || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (int64_t u = 0; u < (int64_t)B * Hkv; ++u) {
+                int64_t b = u / Hkv, g = u % Hkv;
+                const float *kb = k + (b * Hkv + g) * N * D;
+                const float *vb = v + (b * Hkv + g) * N * D;
+                /* 1. per-head logits and softmax statistics over all keys */
+                for (int r = 0; r < G; ++r) {
+                    const float *qh = q + (b * Hq + g * G + r) * D;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < N; ++j) {
+                        s[r * N + j] = dot_scaled(qh, kb + j * D, D, scale);
+                        if (s[r * N + j] > m) m = s[r * N + j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < N; ++j) l += exp(s[r * N + j] - m);
+                    mrow[r] = m;
+                    lrow[r] = l;
+                }
+                /* 2. pool the post-softmax probabilities over the group */
+                for (int64_t j = 0; j < N; ++j) {
+                    double acc = 0.0;
+                    for (int r = 0; r < G; ++r) acc += exp(s[r * N + j] - mrow[r]) / lrow[r];
+                    P[j] = acc;
+                }
+                if (pooled_out) memcpy(pooled_out + u * N, P, (size_t)N * sizeof(double));
+                /* 3. exact Top-k */
+                int32_t *S = idx_out + u * kk;
+                if (select_topk(P, N, kk, S) != ORC_OK) {
+#pragma omp atomic write
+                    status = ORC_NOMEM;
+                    continue;
+                }
+                /* 4. attention over the selected keys, per head */
+                for (int64_t a = 0; a < kk; ++a) keys[a] = S[a];
+                for (int r = 0; r < G; ++r) {
+                    for (int64_t a = 0; a < kk; ++a) sel[a] = s[r * N + S[a]];
+                    weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + g * G + r) * D);
+                }
+            }
+        }
+        free(s); free(P); free(mrow); free(lrow); free(sel); free(keys);
+    }
+    return status;
+}
+
+/* Reuse layer: attention over the anchor's index set of the mapped KV head.
+ * anchor_idx [B, Hkv_a, kk]; head_map [Hkv] with values in [0, Hkv_a). */
+int orc_decode_reuse(const float *q, const float *k, const float *v,
+                     int B, int Hq, int Hkv, int64_t N, int D, double scale,
+                     const int32_t *anchor_idx, int Hkv_a, int64_t kk,
+                     const int32_t *head_map, double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || Hkv_a <= 0 || kk <= 0) return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int g = 0; g < Hkv; ++g)
+        if (head_map[g] < 0 || head_map[g] >= Hkv_a) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < (int64_t)B * Hkv_a * kk; ++i)
+        if (anchor_idx[i] < 0 || anchor_idx[i] >= N) return ORC_BAD_INDEX;
+    const int G = Hq / Hkv;
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *sel = (double *)malloc((size_t)kk * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)kk * sizeof(int64_t));
+        if (!sel || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (int64_t u = 0; u < (int64_t)B * Hkv; ++u) {
+                int64_t b = u / Hkv, g = u % Hkv;
+                const int32_t *S = anchor_idx + (b * Hkv_a + head_map[g]) * kk;
+                const float *kb = k + (b * Hkv + g) * N * D;
+                const float *vb = v + (b * Hkv + g) * N * D;
+                for (int64_t a = 0; a < kk; ++a) keys[a] = S[a];
+                for (int r = 0; r < G; ++r) {
+                    const float *qh = q + (b * Hq + g * G + r) * D;
+                    for (int64_t a = 0; a < kk; ++a) sel[a] = dot_scaled(qh, kb + keys[a] * D, D, scale);
+                    weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + g * G + r) * D);
+                }
+            }
+        }
+        free(sel); free(keys);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* prefill                                                             */
+/* ------------------------------------------------------------------ */
+/*
+ * Layouts. The oracle works on a tile range [t0, t1) so that single tiles of
+ * long prompts can be checked:
+ *   q      [B, Hq, R, D]  holding query rows [tile*t0, tile*t0 + R)
+ *   k, v   [B, Hkv, N, D] the whole prompt
+ *   o_out  [B, Hq, R, D]
+ *   idx    [B, Hkv, off[t1] - off[t0]]  index sets of tiles t0..t1-1 (CSR,
+ *          offsets from orc_prefill_offsets, rebased to off[t0])
+ * where R = min(N, tile*t1) - tile*t0.
+ */
+
+static int64_t range_rows(int64_t N, int32_t tile, int64_t t0, int64_t t1)
+{
+    int64_t end = t1 * tile < N ? t1 * tile : N;
+    return end - t0 * tile;
+}
+
+/* Pooled score of one (b, t, g) unit over keys [0, min(N, tile*(t+1))):
+ * P[j] = sum over the group's heads and the tile's rows i >= j of the row's
+ * softmax probability of key j (softmax over the causal row j' <= i).
+ * `rowbuf` holds at least N doubles. */
+static void prefill_pool_unit(const float *q, const float *k, int B, int Hq, int Hkv,
+                              int64_t N, int D, int32_t tile, double scale,
+                              int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g,
+                              double *P, double *rowbuf)
+{
+    (void)B;
+    const int G = Hq / Hkv;
+    const int64_t i0 = t * tile;
+    const int64_t i1 = (i0 + tile < N) ? i0 + tile : N;
+    const float *kb = k + (b * Hkv + g) * N * D;
+    for (int64_t j = 0; j < i1; ++j) P[j] = 0.0;
+    for (int r = 0; r < G; ++r) {
+        const int64_t h = g * G + r;
+        for (int64_t i = i0; i < i1; ++i) {
+            const float *qi = q + ((b * Hq + h) * R + (i - t0 * tile)) * D;
+            double m = -INFINITY;
+            for (int64_t j = 0; j <= i; ++j) {
+                rowbuf[j] = dot_scaled(qi, kb + j * D, D, scale);
+                if (rowbuf[j] > m) m = rowbuf[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j <= i; ++j) l += exp(rowbuf[j] - m);
+            for (int64_t j = 0; j <= i; ++j) P[j] += exp(rowbuf[j] - m) / l;
+        }
+    }
+}
+
+/* Output rows of one (b, t, g) unit: each row attends over the index set S
+ * (n_sel keys, all before the tile) plus its causal diagonal keys [i0, i]. */
+static void prefill_output_unit(const float *q, const float *k, const float *v,
+                                int Hq, int Hkv, int64_t N, int D, int32_t tile, double scale,
+                                int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g,
+                                const int32_t *S, int64_t n_sel,
+                                double *o_out, double *logit, int64_t *keys)
+{
+    const int G = Hq / Hkv;
+    const int64_t i0 = t * tile;
+    const int64_t i1 = (i0 + tile < N) ? i0 + tile : N;
+    const float *kb = k + (b * Hkv + g) * N * D;
+    const float *vb = v + (b * Hkv + g) * N * D;
+    for (int r = 0; r < G; ++r) {
+        const int64_t h = g * G + r;
+        for (int64_t i = i0; i < i1; ++i) {
+            const float *qi = q + ((b * Hq + h) * R + (i - t0 * tile)) * D;
+            int64_t n = 0;
+            for (int64_t a = 0; a < n_sel; ++a) keys[n++] = S[a];
+            for (int64_t j = i0; j <= i; ++j) keys[n++] = j;
+            for (int64_t a = 0; a < n; ++a) logit[a] = dot_scaled(qi, kb + keys[a] * D, D, scale);
+            weighted_rows(logit, keys, n, vb, D, o_out + ((b * Hq + h) * R + (i - t0 * tile)) * D);
+        }
+    }
+}
+
+/* Pooled scores of a single unit, for checking: P_out has
+ * min(N, tile*(t+1)) entries (selection candidates are the first tile*t). */
+int orc_prefill_pooled(const float *q, const float *k, int B, int Hq, int Hkv, int64_t N,
+                       int D, int32_t tile, double scale, int64_t t0, int64_t t1,
+                       int64_t b, int64_t t, int64_t g, double *P_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || tile <= 0) return ORC_BAD_ARG;
+    int64_t T = (N + tile - 1) / tile;
+    if (t0 < 0 || t1 > T || t0 >= t1 || t < t0 || t >= t1 || b < 0 || b >= B || g < 0 || g >= Hkv)
+        return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    double *rowbuf = (double *)malloc((size_t)N * sizeof(double));
+    if (!rowbuf) return ORC_NOMEM;
+    prefill_pool_unit(q, k, B, Hq, Hkv, N, D, tile, scale, t0, range_rows(N, tile, t0, t1),
+                      b, t, g, P_out, rowbuf);
+    free(rowbuf);
+    return ORC_OK;
+}
+
+/* Prefill anchor layer over tiles [t0, t1): pooled tile scores, exact Top-k_t
+ * per (b, t, g), and the output rows. */
+int orc_prefill_anchor(const float *q, const float *k, const float *v,
+                       int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                       double scale, int64_t t0, int64_t t1,
+                       int32_t *idx_out, double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || tile <= 0 || pct < 1 || pct > 100) return ORC_BAD_ARG;
+    const int64_t T = (N + tile - 1) / tile;
+    if (t0 < 0 || t1 > T || t0 >= t1) return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int64_t *off = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
+    if (!off) return ORC_NOMEM;
+    orc_prefill_offsets(N, tile, pct, off);
+    const int64_t R = range_rows(N, tile, t0, t1);
+    const int64_t tot = off[t1] - off[t0];
+    const int64_t n_units = (int64_t)B * (t1 - t0) * Hkv;
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *P = (double *)malloc((size_t)N * sizeof(double));
+        double *rowbuf = (double *)malloc((size_t)(N + tile) * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)(N + tile) * sizeof(int64_t));
+        if (!P || !rowbuf || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+            /* big tiles first: better balance */
+#pragma omp for schedule(dynamic)
+            for (int64_t u = 0; u < n_units; ++u) {
+                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hkv));
+                int64_t rem = u % ((int64_t)B * Hkv);
+                int64_t b = rem / Hkv, g = rem % Hkv;
+                int64_t kt = off[tt + 1] - off[tt];
+                int32_t *S = idx_out + (b * Hkv + g) * tot + (off[tt] - off[t0]);
+                prefill_pool_unit(q, k, B, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g, P, rowbuf);
+                if (select_topk(P, tt * (int64_t)tile, kt, S) != ORC_OK) {
+#pragma omp atomic write
+                    status = ORC_NOMEM;
+                    continue;
+                }
+                prefill_output_unit(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g,
+                                    S, kt, o_out, rowbuf, keys);
+            }
+        }
+        free(P); free(rowbuf); free(keys);
+    }
+    free(off);
+    return status;
+}
+
+/* Prefill reuse layer over tiles [t0, t1): tile t of KV head g attends over
+ * the anchor's set of tile t for anchor KV head head_map[g] plus the causal
+ * diagonal. anchor_idx is the anchor's full CSR array [B, Hkv_a, total]. */
+int orc_prefill_reuse(const float *q, const float *k, const float *v,
+                      int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                      double scale, int64_t t0, int64_t t1,
+                      const int32_t *anchor_idx, int Hkv_a, const int32_t *head_map,
+                      double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || tile <= 0 || pct < 1 || pct > 100 || Hkv_a <= 0)
+        return ORC_BAD_ARG;
+    const int64_t T = (N + tile - 1) / tile;
+    if (t0 < 0 || t1 > T || t0 >= t1) return ORC_BAD_ARG;
+    for (int g = 0; g < Hkv; ++g)
+        if (head_map[g] < 0 || head_map[g] >= Hkv_a) return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int64_t *off = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
+    if (!off) return ORC_NOMEM;
+    const int64_t total = orc_prefill_offsets(N, tile, pct, off);
+    /* every index of tile t must lie before the tile */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ga = 0; ga < Hkv_a; ++ga)
+            for (int64_t t = t0; t < t1; ++t)
+                for (int64_t a = off[t]; a < off[t + 1]; ++a) {
+                    int32_t j = anchor_idx[(b * Hkv_a + ga) * total + a];
+                    if (j < 0 || j >= t * tile) { free(off); return ORC_BAD_INDEX; }
+                }
+    const int64_t R = range_rows(N, tile, t0, t1);
+    const int64_t n_units = (int64_t)B * (t1 - t0) * Hkv;
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *rowbuf = (double *)malloc((size_t)(N + tile) * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)(N + tile) * sizeof(int64_t));
+        if (!rowbuf || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (int64_t u = 0; u < n_units; ++u) {
+                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hkv));
+                int64_t rem = u % ((int64_t)B * Hkv);
+                int64_t b = rem / Hkv, g = rem % Hkv;
+                const int32_t *S = anchor_idx + (b * Hkv_a + head_map[g]) * total + off[tt];
+                prefill_output_unit(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g,
+                                    S, off[tt + 1] - off[tt], o_out, rowbuf, keys);
+            }
+        }
+        free(rowbuf); free(keys);
+    }
+    free(off);
+    return status;
+}
