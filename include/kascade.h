@@ -1,0 +1,154 @@
+/*
+ * kascade.h -- C ABI of the MI355X (gfx950) Kascade sparse-attention library.
+ *
+ * The method (Kascade README, "Abstract"): anchor layers compute exact Top-k
+ * key indices from post-softmax attention scores; intermediate reuse layers
+ * attend only over those indices; selection and reuse are head-aware; prefill
+ * works on tiles of queries (README notes: tile size 32). One call of this
+ * library is one attention layer of one kind (anchor or reuse) in one phase
+ * (decode or prefill), the granularity of the README's kernel benchmarks
+ * ("Kernel Benchmarks": --kernel recompute|reuse, decode and prefill).
+ *
+ * Conventions for every call
+ *   - Pointers named q, k, v, o, idx, head_map, ws are DEVICE pointers; the
+ *     caller allocates and owns them (including the workspace, sized by
+ *     kas_workspace_size). The library never allocates device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     is asynchronous; no call synchronises the stream.
+ *   - All shape/argument checks run on the host before anything is enqueued;
+ *     on failure nothing is enqueued and the status says why
+ *     (kas_last_error() gives text, per calling thread).
+ *   - Calls are thread-safe and keep no state between calls, except the
+ *     optional kernel-timing registry (kas_profile_*).
+ *   - Layouts are row-major with head_dim contiguous:
+ *       decode : q, o [B, Hq, D];        k, v [B, Hkv, N, D] (strides below)
+ *       prefill: q, o [B, Hq, N, D];     k, v [B, Hkv, N, D] (strides below)
+ *     Query head h uses KV head h / (Hq / Hkv).
+ *   - Index sets are int32 key positions in ascending order.
+ *       decode : [B, Hkv, kd]     kd = max(1, kas_topk_count(N, pct))
+ *       prefill: [B, Hkv, total]  CSR over query tiles; tile t's set is
+ *                [offsets[t], offsets[t+1]) of kas_prefill_index_offsets.
+ *   - Selection is exact: the k largest pooled scores, ties to the lower key
+ *     index, scores compared as fp32.
+ */
+#ifndef KASCADE_H
+#define KASCADE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KAS_OK = 0,
+  KAS_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad shape, bad value */
+  KAS_ERR_UNSUPPORTED = 2,        /* valid request this build does not run */
+  KAS_ERR_WORKSPACE_TOO_SMALL = 3,
+  KAS_ERR_HIP = 4                 /* a HIP launch/runtime call failed */
+} kas_status_t;
+
+typedef enum { KAS_DTYPE_F32 = 0, KAS_DTYPE_BF16 = 1 } kas_dtype_t;
+
+typedef enum {
+  KAS_OP_DECODE_ANCHOR = 0,
+  KAS_OP_DECODE_REUSE = 1,
+  KAS_OP_PREFILL_ANCHOR = 2,
+  KAS_OP_PREFILL_REUSE = 3
+} kas_op_t;
+
+/* Problem description shared by all calls of one layer. */
+typedef struct kas_desc {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads, Hq / Hkv <= 16 */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* D in {64, 128} */
+  int64_t seq_len;      /* decode: keys in the cache (the new token's key
+                           included); prefill: prompt length, a multiple of
+                           the tile. N < 2^31. */
+  int32_t topk_pct;     /* 1..100: k is this percentage of the candidates
+                           (README: "k=10", "--topk 10") */
+  int32_t tile;         /* prefill query tile; must be 32 (README notes) */
+  int32_t dtype;        /* kas_dtype_t. decode: F32 or BF16; prefill: BF16 */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
+  int64_t kv_batch_stride;  /* elements between batches of k/v; 0 = Hkv*N*D */
+  int64_t kv_head_stride;   /* elements between KV heads of k/v; 0 = N*D */
+} kas_desc_t;
+
+/* round-half-up(pct * n / 100) clamped to [0, n]; 0 for n <= 0 or pct <= 0.
+ * Host-only, no GPU needed. */
+int64_t kas_topk_count(int64_t n_candidates, int32_t pct);
+
+/* Prefill CSR layout: tile t (rows [tile*t, tile*t+tile)) selects
+ * kas_topk_count(tile*t, pct) keys among the keys before it, so tile 0
+ * selects none. offsets (may be NULL) receives T+1 entries, T = N / tile;
+ * *total receives offsets[T]. Host-only. */
+kas_status_t kas_prefill_index_offsets(const kas_desc_t* desc, int64_t* offsets, int64_t* total);
+
+/* Device workspace bytes needed by `op` (a kas_op_t) for this description.
+ * Host-only. The workspace carries no state between calls. */
+kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* bytes);
+
+/* Decode anchor layer (README "Abstract": exact Top-k in anchor layers).
+ * For each (b, KV head g): the logits of the G = Hq/Hkv query heads over all
+ * N keys, each head's softmax, the probabilities summed over the G heads
+ * (head-aware pooling), the exact Top-kd of that pooled score written to
+ * idx_out[b, g, :] ascending, and o[b, h] = attention of head h renormalised
+ * over the selected keys. idx_out: [B, Hkv, kd] int32; o: [B, Hq, D]. */
+kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void* k,
+                               const void* v, int32_t* idx_out, void* o,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Decode reuse layer (README "Abstract": indices reused in intermediate
+ * layers, head-aware). KV head g attends, for each of its query heads, only
+ * over anchor_idx[b, head_map[g], :] (kd keys from the anchor call with the
+ * same N and pct) using this layer's own q, k, v.
+ * anchor_idx: [B, anchor_kv_heads, kd]; head_map: device int32 [Hkv] with
+ * values in [0, anchor_kv_heads) (trusted on the device; NULL = identity,
+ * which needs anchor_kv_heads == Hkv). o: [B, Hq, D]. */
+kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void* k,
+                              const void* v, const int32_t* anchor_idx,
+                              int32_t anchor_kv_heads, const int32_t* head_map, void* o,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill anchor layer (README "Abstract": tile-level operations). For each
+ * (b, tile t, KV head g): every query row of the tile and every head of the
+ * group gets its causal softmax; the probabilities of keys before the tile
+ * are summed over the tile's rows and the group's heads; the exact Top-k_t
+ * is tile t's set. Row i of tile t then attends over that set plus its causal
+ * diagonal keys [tile*t, i]. idx_out: [B, Hkv, total] CSR; o: [B, Hq, N, D].
+ * bf16 only. */
+kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k,
+                                const void* v, int32_t* idx_out, void* o,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill reuse layer: tile t of KV head g attends over the anchor's set of
+ * tile t for anchor KV head head_map[g] plus the causal diagonal keys.
+ * anchor_idx: [B, anchor_kv_heads, total] CSR from kas_prefill_anchor with the
+ * same N, tile and pct; every index of tile t must be < tile*t (trusted on
+ * the device). head_map as in kas_decode_reuse. bf16 only. */
+kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void* k,
+                               const void* v, const int32_t* anchor_idx,
+                               int32_t anchor_kv_heads, const int32_t* head_map, void* o,
+                               void* ws, size_t ws_bytes, void* stream);
+
+const char* kas_status_string(kas_status_t status);
+/* Text of the last failure on the calling thread ("" if none). */
+const char* kas_last_error(void);
+
+/* Optional kernel timing (for benchmarks). While enabled, every kernel the
+ * library launches is bracketed by HIP events on its stream. kas_profile_query
+ * waits for the recorded events and returns the summed device time (ms) and
+ * launch count of kernels whose name equals `kernel`; kas_profile_names writes
+ * the known kernel names, comma separated. Not thread-safe against concurrent
+ * calls that launch work. */
+kas_status_t kas_profile_enable(int32_t enable);
+kas_status_t kas_profile_reset(void);
+kas_status_t kas_profile_query(const char* kernel, double* total_ms, int64_t* launches);
+kas_status_t kas_profile_names(char* buf, size_t buf_len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KASCADE_H */

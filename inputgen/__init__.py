@@ -102,7 +102,7 @@ def heavy_positions(w: Workload) -> List[np.ndarray]:
     """Per layer, int64 [B, Hkv, n_heavy] heavy key positions in [4, N)."""
     rng = np.random.default_rng(w.wid)
     lo, n = 4, w.seq_len
-    pool = n - lo
+    pool = max(0, n - lo)
     h = min(w.n_heavy, pool)
     out = []
     prev = None

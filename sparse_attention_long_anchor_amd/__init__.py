@@ -1,0 +1,33 @@
+"""Kascade cross-layer Top-k sparse attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/kascade.h (libkascade_mi355x.so).
+Every computation runs in the HIP library; this module only marshals torch
+tensors (device memory) and the current HIP stream into the C calls. There is
+no CPU or PyTorch fallback: if the library is missing, importing the binding
+raises.
+"""
+from .binding import (  # noqa: F401
+    KasError,
+    decode_anchor,
+    decode_k,
+    decode_reuse,
+    lib_path,
+    make_desc,
+    prefill_anchor,
+    prefill_offsets,
+    prefill_reuse,
+    profile_enable,
+    profile_names,
+    profile_query,
+    profile_reset,
+    topk_count,
+    workspace_size,
+    OP_DECODE_ANCHOR,
+    OP_DECODE_REUSE,
+    OP_PREFILL_ANCHOR,
+    OP_PREFILL_REUSE,
+)
+from .binding import _load as _load_library
+
+# Fail loudly at import when the HIP library is missing: there is no fallback.
+_load_library()

@@ -1,0 +1,242 @@
+"""ctypes binding of libkascade_mi355x.so (argument marshalling only).
+
+Names follow the C ABI (include/kascade.h): decode_anchor, decode_reuse,
+prefill_anchor, prefill_reuse, topk_count, prefill_offsets, workspace_size.
+Tensors must already live on the GPU in the documented layouts; outputs may be
+passed in (preallocated) or are allocated with torch.empty on the inputs'
+device. Work is enqueued on torch's current stream of that device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libkascade_mi355x.so")
+
+OP_DECODE_ANCHOR, OP_DECODE_REUSE, OP_PREFILL_ANCHOR, OP_PREFILL_REUSE = 0, 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+class KasError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: status {status}: {text}")
+        self.status = status
+
+
+class KasDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("seq_len", ctypes.c_int64),
+        ("topk_pct", ctypes.c_int32),
+        ("tile", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("kv_batch_stride", ctypes.c_int64),
+        ("kv_head_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise ImportError(f"HIP library {_LIB} is not built; run "
+                              "`python -m sparse_attention_long_anchor_amd.build`")
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        st = ctypes.c_int
+        dp = ctypes.POINTER(KasDesc)
+        L.kas_topk_count.argtypes = [ctypes.c_int64, ctypes.c_int32]
+        L.kas_topk_count.restype = ctypes.c_int64
+        L.kas_prefill_index_offsets.argtypes = [dp, P, ctypes.POINTER(ctypes.c_int64)]
+        L.kas_workspace_size.argtypes = [dp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kas_decode_anchor.argtypes = [dp, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_decode_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_anchor.argtypes = [dp, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+        L.kas_status_string.argtypes = [st]
+        L.kas_status_string.restype = ctypes.c_char_p
+        L.kas_last_error.restype = ctypes.c_char_p
+        L.kas_profile_enable.argtypes = [ctypes.c_int32]
+        L.kas_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
+        L.kas_profile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+        for n in ("kas_prefill_index_offsets", "kas_workspace_size", "kas_decode_anchor",
+                  "kas_decode_reuse", "kas_prefill_anchor", "kas_prefill_reuse",
+                  "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
+                  "kas_profile_names"):
+            getattr(L, n).restype = st
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        L = _load()
+        raise KasError(rc, where, L.kas_last_error().decode())
+
+
+def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
+              topk_pct: int, dtype: torch.dtype, tile: int = 32, softmax_scale: float = 0.0,
+              kv_batch_stride: int = 0, kv_head_stride: int = 0) -> KasDesc:
+    if dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif dtype == torch.float32:
+        dt = DTYPE_F32
+    else:
+        raise KasError(2, "make_desc", f"dtype {dtype} not supported")
+    return KasDesc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, topk_pct, tile, dt,
+                   softmax_scale, kv_batch_stride, kv_head_stride)
+
+
+def topk_count(n: int, pct: int) -> int:
+    return int(_load().kas_topk_count(n, pct))
+
+
+def decode_k(n: int, pct: int) -> int:
+    return max(1, topk_count(n, pct)) if n >= 1 else 0
+
+
+def prefill_offsets(desc: KasDesc) -> np.ndarray:
+    L = _load()
+    total = ctypes.c_int64(0)
+    _check(L.kas_prefill_index_offsets(ctypes.byref(desc), None, ctypes.byref(total)), "prefill_offsets")
+    off = np.zeros(desc.seq_len // desc.tile + 1, dtype=np.int64)
+    _check(L.kas_prefill_index_offsets(ctypes.byref(desc), off.ctypes.data_as(ctypes.c_void_p),
+                                       ctypes.byref(total)), "prefill_offsets")
+    return off
+
+
+def workspace_size(desc: KasDesc, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kas_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)), "workspace_size")
+    return int(n.value)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ws(desc: KasDesc, op: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
+    need = workspace_size(desc, op)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale: float,
+               tile: int = 32) -> KasDesc:
+    if prefill:
+        B, Hq, N, D = q.shape
+    else:
+        B, Hq, D = q.shape
+        N = k.shape[2]
+    Hkv = k.shape[1]
+    if k.stride(3) != 1 or k.stride(2) != D:
+        raise KasError(1, "desc", "k/v rows must be contiguous [.., N, D]")
+    return make_desc(B, Hq, Hkv, D, N, pct, q.dtype, tile=tile, softmax_scale=scale,
+                     kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1))
+
+
+def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hkv,kd], o [B,Hq,D])."""
+    desc = _desc_from(q, k, pct, False, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "decode_anchor", "k and v must share strides")
+    kd = decode_k(desc.seq_len, pct)
+    if idx_out is None:
+        idx_out = torch.empty((desc.batch, desc.n_kv_heads, kd), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    ws = _ws(desc, OP_DECODE_ANCHOR, ws, q.device)
+    _check(_load().kas_decode_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
+                                     _ptr(o), _ptr(ws), ws.numel(), _stream(q)), "decode_anchor")
+    return idx_out, o
+
+
+def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None
+                 ) -> torch.Tensor:
+    """anchor_idx [B,Hkv_a,kd] int32 (device), head_map int32 [Hkv] (device) or None."""
+    desc = _desc_from(q, k, pct, False, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "decode_reuse", "k and v must share strides")
+    if o is None:
+        o = torch.empty_like(q)
+    ws = _ws(desc, OP_DECODE_REUSE, ws, q.device)
+    _check(_load().kas_decode_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
+                                    anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws),
+                                    ws.numel(), _stream(q)), "decode_reuse")
+    return o
+
+
+def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> (idx int32 [B,Hkv,total] CSR, o [B,Hq,N,D])."""
+    desc = _desc_from(q, k, pct, True, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "prefill_anchor", "k and v must share strides")
+    total = int(prefill_offsets(desc)[-1])
+    if idx_out is None:
+        idx_out = torch.empty((desc.batch, desc.n_kv_heads, max(total, 1)), dtype=torch.int32,
+                              device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    ws = _ws(desc, OP_PREFILL_ANCHOR, ws, q.device)
+    _check(_load().kas_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
+                                      _ptr(o), _ptr(ws), ws.numel(), _stream(q)), "prefill_anchor")
+    return idx_out, o
+
+
+def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None
+                  ) -> torch.Tensor:
+    desc = _desc_from(q, k, pct, True, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "prefill_reuse", "k and v must share strides")
+    if o is None:
+        o = torch.empty_like(q)
+    ws = _ws(desc, OP_PREFILL_REUSE, ws, q.device)
+    _check(_load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
+                                     anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws),
+                                     ws.numel(), _stream(q)), "prefill_reuse")
+    return o
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(_load().kas_profile_enable(1 if on else 0), "profile_enable")
+
+
+def profile_reset() -> None:
+    _check(_load().kas_profile_reset(), "profile_reset")
+
+
+def profile_query(kernel: str) -> Tuple[float, int]:
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check(_load().kas_profile_query(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)), "profile_query")
+    return ms.value, n.value
+
+
+def profile_names():
+    buf = ctypes.create_string_buffer(1024)
+    _check(_load().kas_profile_names(buf, 1024), "profile_names")
+    return buf.value.decode().split(",")

@@ -1,0 +1,567 @@
+// Decode-phase kernels for gfx950 (one new query token per sequence).
+//
+//  dec_score    anchor: stream the K cache once, logits of the G query heads
+//               of each KV head on a 16x16 MFMA tile, base-2 logits to the
+//               workspace, per-chunk softmax statistics (max, sum of exp).
+//  dec_pool     anchor: global softmax statistics per head, pooled score
+//               P_j = sum over the group's heads of the post-softmax
+//               probability (Kascade README "Abstract": exact post-softmax
+//               Top-k, head-aware), first radix digit histogram.
+//  sel_*        anchor: exact k-th largest pooled score by a three-digit
+//               radix select over the fp32 bit pattern, then a stable
+//               compaction of {P > tau} plus the lowest-index ties.
+//  dec_attn     anchor and reuse: index-driven gather of K/V rows, online
+//               softmax, split-K partial (o, m, l) per workgroup.
+//  dec_combine  merge of the split-K partials into the output.
+#include "kas_device.hpp"
+#include "kas_block.hpp"
+#include "kas_internal.hpp"
+
+namespace kas {
+
+constexpr int kMaxSplitRows = 2048;
+
+// ------------------------------------------------------------------ dec_score
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
+  using QK = QKMfma<T, D>;
+  __shared__ float s_m[4][G], s_l[4][G];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int64_t row0 = (int64_t)chunk * a.score_rows;
+  const int nrows = (int)min((int64_t)a.score_rows, a.N - row0);
+  const int64_t unit = (int64_t)b * a.Hkv + g;
+
+  if (chunk == 0) {
+    uint32_t* h = a.hist + unit * kHistWords;
+    for (int i = tid; i < kHistWords; i += 256) h[i] = 0u;
+  }
+  const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + row0 * D;
+  typename QK::QFrag qf;
+  QK::load_q(qf, (const T*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
+  float* lg = a.logits + (unit * a.N + row0) * G;
+
+  float ml[4], ls[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { ml[r] = kNegInf; ls[r] = 0.f; }
+
+  const int nblk = (nrows + 15) >> 4;
+  QK cur;
+  if (wave < nblk) {
+    int jr = wave * 16 + c16;
+    cur.load_k(kb + (int64_t)(jr < nrows ? jr : 0) * D, q4);
+  }
+  for (int blk = wave; blk < nblk; blk += 4) {
+    const int jr = blk * 16 + c16;
+    const bool val = jr < nrows;
+    QK nxt;
+    if (blk + 4 < nblk) {
+      int jn = jr + 64;
+      nxt.load_k(kb + (int64_t)(jn < nrows ? jn : 0) * D, q4);
+    }
+    f32x4 s = cur.run(qf);
+    float t[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = val ? s[r] * a.scale_log2 : kNegInf;
+    if (val) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * q4 + r < G) lg[(int64_t)jr * G + 4 * q4 + r] = t[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float bm = row16_max(t[r]);
+      float mn = fmaxf(ml[r], bm);
+      float al = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
+      float p = (t[r] == kNegInf) ? 0.f : exp2_fast(t[r] - mn);
+      ls[r] = ls[r] * al + p;
+      ml[r] = mn;
+    }
+    cur = nxt;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float lsum = row16_sum(ls[h & 3]);
+    float M = readlane_f(ml[h & 3], 16 * (h >> 2));
+    float L = readlane_f(lsum, 16 * (h >> 2));
+    if (lane == 0) { s_m[wave][h] = M; s_l[wave][h] = L; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    const int h = tid;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += (s_m[w][h] == kNegInf) ? 0.f : s_l[w][h] * exp2_fast(s_m[w][h] - M);
+    float* st = a.stats + ((unit * a.n_score_chunks + chunk) * G + h) * 2;
+    st[0] = M;
+    st[1] = L;
+  }
+}
+
+// ------------------------------------------------------------------ dec_pool
+
+template <int G>
+__global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
+  __shared__ uint32_t s_hist[kBins1];
+  __shared__ float s_tmp[4];
+  __shared__ float s_M[G], s_iL[G];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t unit = (int64_t)b * a.Hkv + g;
+  for (int i = tid; i < kBins1; i += 256) s_hist[i] = 0u;
+
+  const float* st = a.stats + unit * a.n_score_chunks * G * 2;
+  for (int h = 0; h < G; ++h) {
+    float m = kNegInf;
+    for (int c = tid; c < a.n_score_chunks; c += 256) m = fmaxf(m, st[(c * G + h) * 2]);
+    const float M = block_max_256(m, s_tmp);
+    float l = 0.f;
+    for (int c = tid; c < a.n_score_chunks; c += 256) {
+      float mc = st[(c * G + h) * 2];
+      l += (mc == kNegInf) ? 0.f : st[(c * G + h) * 2 + 1] * exp2_fast(mc - M);
+    }
+    const float L = block_sum_256(l, s_tmp);
+    if (tid == 0) { s_M[h] = M; s_iL[h] = 1.0f / L; }
+  }
+  __syncthreads();
+  float M[G], iL[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { M[h] = s_M[h]; iL[h] = s_iL[h]; }
+
+  const float* lg = a.logits + unit * a.N * G;
+  float* P = a.pooled + unit * a.N;
+  const int64_t base = (int64_t)chunk * kSelChunk;
+#pragma unroll 4
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int64_t j = base + i * 256 + tid;
+    if (j < a.N) {
+      float acc = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc += exp2_fast(lg[j * G + h] - M[h]) * iL[h];
+      P[j] = acc;
+      atomicAdd(&s_hist[__float_as_uint(acc) >> 21], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + unit * kHistWords;
+  for (int i = tid; i < kBins1; i += 256)
+    if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
+}
+
+// ------------------------------------------------------------------ radix select
+
+template <int PASS>
+__global__ __launch_bounds__(256) void sel_digit_kernel(DecodeArgs a) {
+  __shared__ uint32_t s_h[kBins2];
+  __shared__ uint32_t s_tmp[4];
+  __shared__ int s_res[2];
+  const int chunk = blockIdx.x;
+  const int64_t unit = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint32_t* gh = a.hist + unit * kHistWords;
+  int b1, b2 = 0;
+  uint32_t ab1, ab2;
+  block_find_bin(gh, kBins1, (uint32_t)a.kk, s_tmp, s_res, b1, ab1);
+  if (PASS == 3) block_find_bin(gh + kBins1, kBins2, (uint32_t)a.kk - ab1, s_tmp, s_res, b2, ab2);
+  constexpr int NB = PASS == 2 ? kBins2 : kBins3;
+  for (int i = tid; i < NB; i += 256) s_h[i] = 0u;
+  __syncthreads();
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  const int64_t base = (int64_t)chunk * kSelChunk;
+  const uint32_t pre = PASS == 2 ? (uint32_t)b1 : (((uint32_t)b1 << 11) | (uint32_t)b2);
+#pragma unroll 4
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int64_t j = base + i * 256 + tid;
+    if (j < a.N) {
+      uint32_t u = P[j];
+      if (PASS == 2) {
+        if ((u >> 21) == pre) atomicAdd(&s_h[(u >> 10) & 0x7ffu], 1u);
+      } else {
+        if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* out = a.hist + unit * kHistWords + (PASS == 2 ? kBins1 : kBins1 + kBins2);
+  for (int i = tid; i < NB; i += 256)
+    if (s_h[i]) atomicAdd(&out[i], s_h[i]);
+}
+
+// tau (bit pattern of the k-th largest) and r = ties at tau to keep; per-chunk
+// counts of elements above / equal to tau.
+__global__ __launch_bounds__(256) void sel_count_kernel(DecodeArgs a) {
+  __shared__ uint32_t s_tmp[4];
+  __shared__ int s_res[2];
+  const int chunk = blockIdx.x;
+  const int64_t unit = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint32_t* gh = a.hist + unit * kHistWords;
+  int b1, b2, b3;
+  uint32_t ab1, ab2, ab3;
+  const uint32_t k = (uint32_t)a.kk;
+  block_find_bin(gh, kBins1, k, s_tmp, s_res, b1, ab1);
+  block_find_bin(gh + kBins1, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+  block_find_bin(gh + kBins1 + kBins2, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  const uint32_t tau = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10) | (uint32_t)b3;
+  const uint32_t r = k - ab1 - ab2 - ab3;
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  const int64_t base = (int64_t)chunk * kSelChunk;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll 4
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int64_t j = base + i * 256 + tid;
+    if (j < a.N) {
+      uint32_t u = P[j];
+      gt += u > tau;
+      eq += u == tau;
+    }
+  }
+  uint32_t tg, te;
+  block_excl_scan_256(gt, s_tmp, &tg);
+  block_excl_scan_256(eq, s_tmp, &te);
+  if (tid == 0) {
+    uint32_t* c = a.counts + (unit * a.n_sel_chunks + chunk) * 2;
+    c[0] = tg;
+    c[1] = te;
+    if (chunk == 0) {
+      uint32_t* ss = a.selstate + unit * 4;
+      ss[0] = tau;
+      ss[1] = r;
+    }
+  }
+}
+
+// Stable compaction: key j is kept if P_j > tau, or P_j == tau and fewer than
+// r equal keys precede it. Output position = kept keys before j.
+__global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
+  __shared__ uint32_t s_tmp[4];
+  const int chunk = blockIdx.x;
+  const int64_t unit = blockIdx.y;
+  const int tid = threadIdx.x;
+  const uint32_t tau = a.selstate[unit * 4 + 0];
+  const uint32_t r = a.selstate[unit * 4 + 1];
+  uint32_t gt_before = 0, eq_before = 0;
+  const uint32_t* c = a.counts + unit * a.n_sel_chunks * 2;
+  for (int x = 0; x < chunk; ++x) { gt_before += c[2 * x]; eq_before += c[2 * x + 1]; }
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  // thread owns 16 consecutive keys
+  constexpr int PER = kSelChunk / 256;
+  const int64_t j0 = (int64_t)chunk * kSelChunk + tid * PER;
+  uint32_t u[PER];
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    u[i] = (j0 + i < a.N) ? P[j0 + i] : 0u;
+    bool in = j0 + i < a.N;
+    gt += in && u[i] > tau;
+    eq += in && u[i] == tau;
+  }
+  uint32_t g_ex = block_excl_scan_256(gt, s_tmp, nullptr) + gt_before;
+  uint32_t e_ex = block_excl_scan_256(eq, s_tmp, nullptr) + eq_before;
+  int32_t* out = a.idx_out + unit * a.kk;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (j0 + i >= a.N) break;
+    if (u[i] > tau) {
+      const uint32_t pos = g_ex + min(e_ex, r);
+      if (pos < (uint32_t)a.kk) out[pos] = (int32_t)(j0 + i);
+      ++g_ex;
+    } else if (u[i] == tau) {
+      if (e_ex < r && g_ex + e_ex < (uint32_t)a.kk) out[g_ex + e_ex] = (int32_t)(j0 + i);
+      ++e_ex;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dec_attn
+
+// One workgroup = one split of one (b, g): rows [split*split_rows, ...) of the
+// index set. Wave w takes 16-row blocks w, w+4, ...; per block: Q.K^T on a
+// 16x16 MFMA tile (or the anchor's stored logits), online softmax with
+// wave-uniform running max per head, P.V on the VALU with 16 lanes per V row.
+template <typename T, int D, int G, bool FROM_LOGITS>
+__global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
+  using QK = QKMfma<T, D>;
+  constexpr int EPL = D / 16;
+  __shared__ int32_t s_idx[kMaxSplitRows];
+  __shared__ float s_p[4][16 * G];
+  __shared__ float s_o[4][G * D];
+  __shared__ float s_m[4][G], s_l[4][G];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int64_t row0 = (int64_t)split * a.split_rows;
+  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  // Index values and the head map are trusted inputs; clamping keeps every
+  // access inside the cache even if they are not.
+  int ga = a.head_map ? a.head_map[g] : g;
+  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+  const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
+  for (int i = tid; i < nrows; i += 256) {
+    const int32_t j = idx[i];
+    s_idx[i] = ((uint32_t)j < (uint32_t)a.N) ? j : 0;
+  }
+  __syncthreads();
+
+  const int64_t unit = (int64_t)b * a.Hkv + g;
+  const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const T* vb = (const T*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
+
+  typename QK::QFrag qf;
+  if (!FROM_LOGITS)
+    QK::load_q(qf, (const T*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
+
+  float o[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+  float ml[4], ls[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { ml[r] = kNegInf; ls[r] = 0.f; }
+
+  struct Blk {
+    QK kq;
+    f32x4 lgt;
+    RowFrag<T, EPL> vf[4];
+  };
+  auto load_blk = [&](int blk, Blk& B_) {
+    const int r0 = blk * 16;
+    const int jr = r0 + c16;
+    const int jk = s_idx[jr < nrows ? jr : 0];
+    if (FROM_LOGITS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        B_.lgt[r] = (4 * q4 + r < G) ? lg[(int64_t)jk * G + 4 * q4 + r] : 0.f;
+    } else {
+      B_.kq.load_k(kb + (int64_t)jk * D, q4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jr2 = r0 + 4 * i + q4;
+      const int jv = s_idx[jr2 < nrows ? jr2 : 0];
+      B_.vf[i].load(vb + (int64_t)jv * D + c16 * EPL);
+    }
+  };
+
+  float* sp = s_p[wave];
+  const int nblk = (nrows + 15) >> 4;
+  Blk cur;
+  if (wave < nblk) load_blk(wave, cur);
+  for (int blk = wave; blk < nblk; blk += 4) {
+    Blk nxt;
+    if (blk + 4 < nblk) load_blk(blk + 4, nxt);
+    const bool kval = blk * 16 + c16 < nrows;
+    f32x4 s;
+    if (FROM_LOGITS) s = cur.lgt;
+    else s = cur.kq.run(qf) * a.scale_log2;
+    float t[4], p[4], al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      t[r] = kval ? s[r] : kNegInf;
+      float bm = row16_max(t[r]);
+      float mn = fmaxf(ml[r], bm);
+      al[r] = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
+      p[r] = (t[r] == kNegInf) ? 0.f : exp2_fast(t[r] - mn);
+      ls[r] = ls[r] * al[r] + p[r];
+      ml[r] = mn;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = readlane_f(al[h & 3], 16 * (h >> 2));
+      if (ah != 1.f) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] *= ah;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q4 + r < G) sp[c16 * G + 4 * q4 + r] = p[r];
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + q4;
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = sp[row * G + h];
+      float vv[EPL];
+      cur.vf[i].widen(vv);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] += pv[h] * vv[e];
+    }
+    wave_lds_fence();
+    cur = nxt;
+  }
+
+  // reduce over the four lane rows (each saw different keys, same running max)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      o[h][e] += __shfl_xor(o[h][e], 16);
+      o[h][e] += __shfl_xor(o[h][e], 32);
+    }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float lsum = row16_sum(ls[h & 3]);
+    float M = readlane_f(ml[h & 3], 16 * (h >> 2));
+    float L = readlane_f(lsum, 16 * (h >> 2));
+    if (lane == 0) { s_m[wave][h] = M; s_l[wave][h] = L; }
+  }
+  if (q4 == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][h * D + c16 * EPL + e] = o[h][e];
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += 256) {
+    const int h = x / D, d = x % D;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += (s_m[w][h] == kNegInf) ? 0.f : s_o[w][x] * exp2_fast(s_m[w][h] - M);
+    a.part_o[(((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * D + d] = acc;
+  }
+  if (tid < G) {
+    const int h = tid;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      L += (s_m[w][h] == kNegInf) ? 0.f : s_l[w][h] * exp2_fast(s_m[w][h] - M);
+    float* ml_out = a.part_ml + (((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * 2;
+    ml_out[0] = M;
+    ml_out[1] = L;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float x);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_out<__bf16>(__bf16* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_rne(x);
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void dec_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (d >= a.D) return;
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  const float* ml = a.part_ml + bh * a.nsplit * 2;
+  const float* po = a.part_o + bh * a.nsplit * a.D;
+  float M = kNegInf;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float w = exp2_fast(ml[2 * s] - M);
+    L += ml[2 * s + 1] * w;
+    acc += po[(int64_t)s * a.D + d] * w;
+  }
+  store_out<T>((T*)a.o + bh * a.D + d, acc / L);
+}
+
+// ------------------------------------------------------------------ launchers
+
+#define KAS_LAUNCH(kernel, grid, block, stream, arg) \
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, arg)
+
+template <typename T, int D>
+static hipError_t score_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8>), grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
+  dim3 grid(a.n_score_chunks, a.Hkv, a.B);
+  ctx.begin(K_DEC_SCORE);
+  hipError_t e;
+  if (dtype == 1) e = (a.D == 128) ? score_launch<__bf16, 128>(a, grid, ctx.stream)
+                                   : score_launch<__bf16, 64>(a, grid, ctx.stream);
+  else e = (a.D == 128) ? score_launch<float, 128>(a, grid, ctx.stream)
+                        : score_launch<float, 64>(a, grid, ctx.stream);
+  if (e != hipSuccess) return e;
+  return ctx.end(K_DEC_SCORE);
+}
+
+hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
+  dim3 grid(a.n_sel_chunks, a.Hkv, a.B);
+  ctx.begin(K_DEC_POOL);
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_pool_kernel<1>), grid, dim3(256), ctx.stream, a); break;
+    case 2: KAS_LAUNCH((dec_pool_kernel<2>), grid, dim3(256), ctx.stream, a); break;
+    case 4: KAS_LAUNCH((dec_pool_kernel<4>), grid, dim3(256), ctx.stream, a); break;
+    case 8: KAS_LAUNCH((dec_pool_kernel<8>), grid, dim3(256), ctx.stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return ctx.end(K_DEC_POOL);
+}
+
+hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
+  dim3 grid(a.n_sel_chunks, a.B * a.Hkv);
+  hipError_t e;
+  ctx.begin(K_SEL_DIGIT2);
+  KAS_LAUNCH((sel_digit_kernel<2>), grid, dim3(256), ctx.stream, a);
+  if ((e = ctx.end(K_SEL_DIGIT2)) != hipSuccess) return e;
+  ctx.begin(K_SEL_DIGIT3);
+  KAS_LAUNCH((sel_digit_kernel<3>), grid, dim3(256), ctx.stream, a);
+  if ((e = ctx.end(K_SEL_DIGIT3)) != hipSuccess) return e;
+  ctx.begin(K_SEL_COUNT);
+  KAS_LAUNCH(sel_count_kernel, grid, dim3(256), ctx.stream, a);
+  if ((e = ctx.end(K_SEL_COUNT)) != hipSuccess) return e;
+  ctx.begin(K_SEL_COMPACT);
+  KAS_LAUNCH(sel_compact_kernel, grid, dim3(256), ctx.stream, a);
+  return ctx.end(K_SEL_COMPACT);
+}
+
+template <typename T, int D, bool FL>
+static hipError_t attn_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_attn_kernel<T, D, 1, FL>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_attn_kernel<T, D, 2, FL>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_attn_kernel<T, D, 4, FL>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_attn_kernel<T, D, 8, FL>), grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+template <typename T, bool FL>
+static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  return a.D == 128 ? attn_launch<T, 128, FL>(a, grid, st) : attn_launch<T, 64, FL>(a, grid, st);
+}
+
+hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx) {
+  dim3 grid(a.nsplit, a.Hkv, a.B);
+  hipError_t e;
+  ctx.begin(K_DEC_ATTN);
+  if (dtype == 1) e = from_logits ? attn_by_d<__bf16, true>(a, grid, ctx.stream)
+                                  : attn_by_d<__bf16, false>(a, grid, ctx.stream);
+  else e = from_logits ? attn_by_d<float, true>(a, grid, ctx.stream)
+                       : attn_by_d<float, false>(a, grid, ctx.stream);
+  if (e != hipSuccess) return e;
+  if ((e = ctx.end(K_DEC_ATTN)) != hipSuccess) return e;
+  ctx.begin(K_DEC_COMBINE);
+  dim3 cgrid(a.Hq, a.B);
+  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(128), ctx.stream, a);
+  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(128), ctx.stream, a);
+  return ctx.end(K_DEC_COMBINE);
+}
+
+}  // namespace kas

@@ -1,0 +1,204 @@
+// Device helpers shared by the gfx950 kernels: element loads and conversion,
+// wavefront reductions, MFMA wrappers and the base-2 exponential.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kas {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// log2(e): logits are kept in base-2 units so that softmax uses v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 bit pattern in the low / high half of a dword -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- DPP
+// Reductions inside each row of 16 lanes; afterwards every lane of the row
+// holds the row's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuad1032>(x));
+  x = fmaxf(x, dpp_f<kDppQuad2301>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<kDppQuad1032>(x);
+  x += dpp_f<kDppQuad2301>(x);
+  x += dpp_f<kDppRowHalfMirror>(x);
+  x += dpp_f<kDppRowMirror>(x);
+  return x;
+}
+
+// Full 64-lane reductions through cross-lane permutes.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// ---------------------------------------------------------------- loads
+// 16-byte global load of 8 bf16 (as raw dwords).
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ldg8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Load EPL consecutive elements of T at p and widen to fp32.
+template <typename T, int EPL>
+struct RowFrag;
+
+template <>
+struct RowFrag<__bf16, 8> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = ldg16(p); }
+  __device__ __forceinline__ void widen(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[2 * i] = bf16lo(w[i]); f[2 * i + 1] = bf16hi(w[i]); }
+  }
+};
+template <>
+struct RowFrag<__bf16, 4> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = ldg8(p); }
+  __device__ __forceinline__ void widen(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) { f[2 * i] = bf16lo(w[i]); f[2 * i + 1] = bf16hi(w[i]); }
+  }
+};
+template <>
+struct RowFrag<float, 4> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = ldg16(p); }
+  __device__ __forceinline__ void widen(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+};
+template <>
+struct RowFrag<float, 8> {
+  u32x4 w0, w1;
+  __device__ __forceinline__ void load(const float* p) { w0 = ldg16(p); w1 = ldg16(p + 4); }
+  __device__ __forceinline__ void widen(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = __uint_as_float(w0[i]); f[4 + i] = __uint_as_float(w1[i]); }
+  }
+};
+
+// ---------------------------------------------------------------- MFMA QK
+// Q.K^T for one block of 16 keys against up to 16 query heads on a 16x16
+// MFMA tile: A = Q (row m = head = lane % 16), B = K^T (column n = key =
+// lane % 16), contraction over head_dim. Output lane l, reg r holds
+// S[head = 4*(l/16) + r][key = l % 16]. Both operands use the same split of
+// head_dim across lanes, so the hardware's k-order inside an instruction does
+// not matter.
+template <typename T, int D>
+struct QKMfma;
+
+// bf16: v_mfma_f32_16x16x32_bf16; instruction c covers dims [32c, 32c+32),
+// lane quarter q = l/16 supplies dims 32c + 8q .. +8.
+template <int D>
+struct QKMfma<__bf16, D> {
+  static constexpr int NI = D / 32;
+  u32x4 kf[NI];
+  __device__ __forceinline__ static int dim_of(int c, int q) { return 32 * c + 8 * q; }
+  __device__ __forceinline__ void load_k(const __bf16* row, int q) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) kf[c] = ldg16(row + dim_of(c, q));
+  }
+  struct QFrag { u32x4 a[NI]; };
+  __device__ __forceinline__ static void load_q(QFrag& f, const __bf16* qrow, bool valid, int q) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) f.a[c] = valid ? ldg16(qrow + dim_of(c, q)) : u32x4{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ f32x4 run(const QFrag& f) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NI; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[c]),
+                                                    __builtin_bit_cast(bf16x8, kf[c]), acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+// fp32: v_mfma_f32_16x16x4_f32; lane quarter q owns dims [q*D/4, (q+1)*D/4)
+// (contiguous, loaded 16 B at a time) and instruction c uses its c-th dim.
+template <int D>
+struct QKMfma<float, D> {
+  static constexpr int NI = D / 4;
+  static constexpr int NV = NI / 4;   // 16-byte vectors per lane
+  u32x4 kf[NV];
+  __device__ __forceinline__ void load_k(const float* row, int q) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) kf[c] = ldg16(row + q * NI + 4 * c);
+  }
+  struct QFrag { u32x4 a[NV]; };
+  __device__ __forceinline__ static void load_q(QFrag& f, const float* qrow, bool valid, int q) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) f.a[c] = valid ? ldg16(qrow + q * NI + 4 * c) : u32x4{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ f32x4 run(const QFrag& f) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.a[c][e]), __uint_as_float(kf[c][e]),
+                                                   acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+}  // namespace kas

@@ -1,0 +1,73 @@
+// Internal launch interface between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kas {
+
+// Names under which kernel timings are reported (kas_profile_query).
+enum KernelId {
+  K_DEC_SCORE = 0,
+  K_DEC_POOL,
+  K_SEL_DIGIT2,
+  K_SEL_DIGIT3,
+  K_SEL_COUNT,
+  K_SEL_COMPACT,
+  K_DEC_ATTN,
+  K_DEC_COMBINE,
+  K_PRE_STATS,
+  K_PRE_POOL,
+  K_PRE_SELECT,
+  K_PRE_ATTN,
+  K_COUNT_
+};
+const char* kernel_name(int id);
+
+// Wraps every launch: optional event timing + launch error check.
+struct LaunchCtx {
+  hipStream_t stream;
+  void begin(int kid);
+  hipError_t end(int kid);
+};
+
+// Radix-select digit layout over the fp32 bit pattern of a non-negative score:
+// digit 1 = bits [31:21], digit 2 = bits [20:10], digit 3 = bits [9:0].
+constexpr int kBins1 = 2048, kBins2 = 2048, kBins3 = 1024;
+constexpr int kHistWords = kBins1 + kBins2 + kBins3;
+constexpr int kSelChunk = 4096;         // scores per selection workgroup
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t kv_bstride, kv_hstride;   // elements
+  int B, Hq, Hkv, D, G;
+  int64_t N;
+  float scale_log2;                 // softmax scale * log2(e)
+  // index sets
+  const int32_t* idx;               // [B, Hkv_a, kk]
+  int64_t kk;
+  int Hkv_a;
+  const int32_t* head_map;          // [Hkv] or null
+  int32_t* idx_out;                 // anchor: [B, Hkv, kk]
+  // workspace regions
+  float* logits;                    // [B, Hkv, N, G] base-2 logits
+  float* stats;                     // [B, Hkv, n_score_chunks, G, 2]
+  int n_score_chunks, score_rows;
+  float* pooled;                    // [B, Hkv, N]
+  uint32_t* hist;                   // [B, Hkv, kHistWords]
+  uint32_t* counts;                 // [B, Hkv, n_sel_chunks, 2]
+  uint32_t* selstate;               // [B, Hkv, 4]
+  int n_sel_chunks;
+  float* part_o;                    // [B, Hq, nsplit, D]
+  float* part_ml;                   // [B, Hq, nsplit, 2]
+  int nsplit, split_rows;
+};
+
+hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
+hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx);
+hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx);
+hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx);
+
+}  // namespace kas

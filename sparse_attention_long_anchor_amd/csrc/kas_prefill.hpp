@@ -1,0 +1,42 @@
+// Internal interface of the prefill kernels (tiles of 32 query rows).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kas_internal.hpp"
+
+namespace kas {
+
+constexpr int kTile = 32;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t kv_bstride, kv_hstride;   // elements
+  int B, Hq, Hkv, D, G, T, pct;
+  int64_t N;
+  float scale_log2;
+  // index sets (CSR over tiles, per (b, KV head))
+  const int32_t* idx;               // reuse: anchor sets [B, Hkv_a, total]
+  int Hkv_a;
+  const int32_t* head_map;
+  int32_t* idx_out;                 // anchor: [B, Hkv, total]
+  int64_t total;
+  // workspace
+  int32_t* offsets;                 // [T + 1]
+  float* lse;                       // [B, Hq, N] base-2 log-sum-exp of each causal row
+  float* pooled;                    // pooled rows of the current tile range
+  size_t pooled_floats;             // capacity of `pooled`
+  int t_begin, t_end;               // tile range of the current pool/select launch
+};
+
+size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);
+void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N, int pct, float scale,
+                       int64_t kv_bs, int64_t kv_hs, char* ws, bool anchor);
+hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx);
+hipError_t launch_prefill_reuse(PrefillArgs& a, LaunchCtx& ctx);
+
+}  // namespace kas

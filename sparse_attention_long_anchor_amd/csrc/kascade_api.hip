@@ -1,0 +1,455 @@
+// C ABI of the Kascade sparse-attention library (declared in include/kascade.h):
+// host-side argument checks, workspace layout, kernel sequencing, optional
+// kernel timing. Every launch goes to the caller's stream; nothing here
+// allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kascade.h"
+#include "kas_internal.hpp"
+#include "kas_prefill.hpp"
+
+namespace kas {
+
+// ------------------------------------------------------------------ errors
+
+static thread_local std::string t_last_error;
+
+static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return st;
+}
+
+// ------------------------------------------------------------------ timing registry
+
+static const char* const kKernelNames[K_COUNT_] = {
+    "decode_score", "decode_pool", "select_digit2", "select_digit3", "select_count",
+    "select_compact", "decode_attn", "decode_combine", "prefill_stats", "prefill_pool",
+    "prefill_select", "prefill_attn"};
+
+const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
+
+struct Record { int kid; hipEvent_t e0, e1; };
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<Record> g_pending;
+static std::vector<hipEvent_t> g_free_events;
+static double g_total_ms[K_COUNT_];
+static int64_t g_launches[K_COUNT_];
+static thread_local hipEvent_t t_open_event = nullptr;
+
+static hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void LaunchCtx::begin(int kid) {
+  (void)kid;
+  t_open_event = nullptr;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, stream) == hipSuccess) t_open_event = e;
+}
+
+hipError_t LaunchCtx::end(int kid) {
+  hipError_t err = hipGetLastError();
+  if (t_open_event) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t e1 = take_event();
+    if (e1 && hipEventRecord(e1, stream) == hipSuccess) g_pending.push_back({kid, t_open_event, e1});
+    t_open_event = nullptr;
+  }
+  return err;
+}
+
+static void drain_pending_locked() {
+  for (auto& r : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) == hipSuccess && hipEventElapsedTime(&ms, r.e0, r.e1) == hipSuccess) {
+      g_total_ms[r.kid] += ms;
+      g_launches[r.kid] += 1;
+    }
+    g_free_events.push_back(r.e0);
+    g_free_events.push_back(r.e1);
+  }
+  g_pending.clear();
+}
+
+// ------------------------------------------------------------------ descriptors
+
+struct Shape {
+  int B, Hq, Hkv, D, G;
+  int64_t N;
+  int pct, tile, dtype;
+  float scale;
+  int64_t kv_hs, kv_bs;
+  size_t esize;
+};
+
+static int64_t topk_count(int64_t n, int32_t pct) {
+  if (n <= 0 || pct <= 0) return 0;
+  int64_t k = ((int64_t)pct * n + 50) / 100;
+  return k > n ? n : k;
+}
+static int64_t decode_k(int64_t n, int32_t pct) {
+  int64_t k = topk_count(n, pct);
+  return (k < 1 && n >= 1) ? 1 : k;
+}
+
+static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
+  if (!d) return fail(KAS_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "batch/heads must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                d->n_q_heads, d->n_kv_heads);
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(KAS_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KAS_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->seq_len < 1 || d->seq_len >= (int64_t(1) << 31))
+    return fail(KAS_ERR_INVALID_ARGUMENT, "seq_len must be in [1, 2^31)");
+  if (d->topk_pct < 1 || d->topk_pct > 100)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "topk_pct must be in [1, 100]");
+  if (d->dtype != KAS_DTYPE_F32 && d->dtype != KAS_DTYPE_BF16)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
+  if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
+    return fail(KAS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (prefill) {
+    if (d->dtype != KAS_DTYPE_BF16) return fail(KAS_ERR_UNSUPPORTED, "prefill supports bf16 only");
+    if (d->tile != 32) return fail(KAS_ERR_UNSUPPORTED, "prefill tile must be 32 (got %d)", d->tile);
+    if (d->seq_len % 32) return fail(KAS_ERR_UNSUPPORTED, "prefill seq_len must be a multiple of 32");
+  }
+  s.B = d->batch; s.Hq = d->n_q_heads; s.Hkv = d->n_kv_heads; s.D = d->head_dim; s.G = G;
+  s.N = d->seq_len; s.pct = d->topk_pct; s.tile = d->tile; s.dtype = d->dtype;
+  s.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
+  s.esize = d->dtype == KAS_DTYPE_BF16 ? 2 : 4;
+  s.kv_hs = d->kv_head_stride ? d->kv_head_stride : s.N * s.D;
+  s.kv_bs = d->kv_batch_stride ? d->kv_batch_stride : s.Hkv * s.kv_hs;
+  if (s.kv_hs < s.N * s.D || s.kv_bs < (s.Hkv - 1) * s.kv_hs + s.N * s.D)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "kv strides overlap the [N, D] rows of a head");
+  const int64_t vec = 16 / (int64_t)s.esize;
+  if (s.kv_hs % vec || s.kv_bs % vec)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "kv strides must be multiples of 16 bytes");
+  return KAS_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static kas_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(KAS_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(KAS_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return KAS_OK;
+}
+
+// ------------------------------------------------------------------ workspace plans
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  int x = atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Rows of the index set per decode attention workgroup: enough workgroups to
+// cover the machine a few times over, at most kMaxSplitRows (LDS staging).
+static int decode_split_rows(int64_t units, int64_t kk) {
+  int r = env_int("KAS_DECODE_SPLIT_ROWS", 0);
+  if (r <= 0) {
+    const int64_t target_wgs = 2048;
+    int64_t per = (units * kk + target_wgs - 1) / target_wgs;
+    per = (per + 63) / 64 * 64;
+    r = (int)(per < 64 ? 64 : per);
+  }
+  r = (r + 15) / 16 * 16;
+  if (r > 2048) r = 2048;
+  if (r < 16) r = 16;
+  return r;
+}
+static int decode_score_rows() {
+  int r = env_int("KAS_DECODE_SCORE_ROWS", 1024);
+  return (r + 63) / 64 * 64;
+}
+
+struct DecodePlan {
+  int64_t kk;
+  int score_rows, n_score_chunks, n_sel_chunks, split_rows, nsplit;
+  size_t off_logits, off_stats, off_pooled, off_hist, off_counts, off_selstate, off_part_o,
+      off_part_ml, total;
+};
+
+static DecodePlan plan_decode(const Shape& s, bool anchor) {
+  DecodePlan p{};
+  p.kk = decode_k(s.N, s.pct);
+  p.score_rows = decode_score_rows();
+  p.n_score_chunks = (int)((s.N + p.score_rows - 1) / p.score_rows);
+  p.n_sel_chunks = (int)((s.N + kSelChunk - 1) / kSelChunk);
+  p.split_rows = decode_split_rows((int64_t)s.B * s.Hkv, p.kk);
+  p.nsplit = (int)((p.kk + p.split_rows - 1) / p.split_rows);
+  const size_t units = (size_t)s.B * s.Hkv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  if (anchor) {
+    p.off_logits = take(units * s.N * s.G * sizeof(float));
+    p.off_stats = take(units * p.n_score_chunks * s.G * 2 * sizeof(float));
+    p.off_pooled = take(units * s.N * sizeof(float));
+    p.off_hist = take(units * kHistWords * sizeof(uint32_t));
+    p.off_counts = take(units * p.n_sel_chunks * 2 * sizeof(uint32_t));
+    p.off_selstate = take(units * 4 * sizeof(uint32_t));
+  }
+  p.off_part_o = take((size_t)s.B * s.Hq * p.nsplit * s.D * sizeof(float));
+  p.off_part_ml = take((size_t)s.B * s.Hq * p.nsplit * 2 * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, char* ws, DecodeArgs& a) {
+  memset(&a, 0, sizeof(a));
+  a.kv_bstride = s.kv_bs; a.kv_hstride = s.kv_hs;
+  a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.G = s.G; a.N = s.N;
+  a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+  a.kk = p.kk;
+  a.score_rows = p.score_rows; a.n_score_chunks = p.n_score_chunks; a.n_sel_chunks = p.n_sel_chunks;
+  a.split_rows = p.split_rows; a.nsplit = p.nsplit;
+  if (anchor) {
+    a.logits = (float*)(ws + p.off_logits);
+    a.stats = (float*)(ws + p.off_stats);
+    a.pooled = (float*)(ws + p.off_pooled);
+    a.hist = (uint32_t*)(ws + p.off_hist);
+    a.counts = (uint32_t*)(ws + p.off_counts);
+    a.selstate = (uint32_t*)(ws + p.off_selstate);
+  }
+  a.part_o = (float*)(ws + p.off_part_o);
+  a.part_ml = (float*)(ws + p.off_part_ml);
+}
+
+static kas_status_t check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(KAS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  if (need && !ws) return fail(KAS_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (need && ((uintptr_t)ws & 255u)) return fail(KAS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return KAS_OK;
+}
+
+static kas_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(KAS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+}  // namespace kas
+
+using namespace kas;
+
+// ------------------------------------------------------------------ exported
+
+extern "C" {
+
+int64_t kas_topk_count(int64_t n, int32_t pct) { return kas::topk_count(n, pct); }
+
+kas_status_t kas_prefill_index_offsets(const kas_desc_t* desc, int64_t* offsets, int64_t* total) {
+  Shape s;
+  kas_status_t st = check_desc(desc, true, s);
+  if (st != KAS_OK) return st;
+  if (!total) return fail(KAS_ERR_INVALID_ARGUMENT, "total is NULL");
+  const int64_t T = s.N / s.tile;
+  int64_t acc = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (offsets) offsets[t] = acc;
+    acc += kas::topk_count(t * s.tile, s.pct);
+  }
+  if (offsets) offsets[T] = acc;
+  *total = acc;
+  if (acc >= (int64_t(1) << 31)) return fail(KAS_ERR_UNSUPPORTED, "index set larger than 2^31 entries");
+  return KAS_OK;
+}
+
+kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* bytes) {
+  if (!bytes) return fail(KAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Shape s;
+  const bool prefill = op == KAS_OP_PREFILL_ANCHOR || op == KAS_OP_PREFILL_REUSE;
+  if (op < 0 || op > 3) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown op %d", op);
+  kas_status_t st = check_desc(desc, prefill, s);
+  if (st != KAS_OK) return st;
+  if (!prefill) {
+    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR).total;
+  } else {
+    *bytes = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, op == KAS_OP_PREFILL_ANCHOR);
+  }
+  return KAS_OK;
+}
+
+kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                               int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  kas_status_t st = check_desc(desc, false, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
+  DecodePlan p = plan_decode(s, true);
+  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  DecodeArgs a;
+  fill_decode_args(s, p, true, (char*)ws, a);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx_out = idx_out;
+  a.idx = idx_out; a.Hkv_a = s.Hkv; a.head_map = nullptr;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e;
+  if ((e = launch_decode_score(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
+  if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
+  if ((e = launch_decode_select(a, ctx)) != hipSuccess) return hip_fail(e, "decode_select");
+  if ((e = launch_decode_attn(a, s.dtype, true, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
+  return KAS_OK;
+}
+
+kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                              const int32_t* anchor_idx, int32_t anchor_kv_heads,
+                              const int32_t* head_map, void* o, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Shape s;
+  kas_status_t st = check_desc(desc, false, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!anchor_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_idx is NULL");
+  if (anchor_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_kv_heads must be >= 1");
+  if (!head_map && anchor_kv_heads != s.Hkv)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "identity head map needs anchor_kv_heads == n_kv_heads");
+  DecodePlan p = plan_decode(s, false);
+  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  DecodeArgs a;
+  fill_decode_args(s, p, false, (char*)ws, a);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e;
+  if ((e = launch_decode_attn(a, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
+  return KAS_OK;
+}
+
+kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                                int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  kas_status_t st = check_desc(desc, true, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
+  int64_t total = 0;
+  if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
+  size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, true);
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  PrefillArgs a;
+  fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, true);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
+  a.idx = idx_out; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = total;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e = launch_prefill_anchor(a, ctx);
+  if (e != hipSuccess) return hip_fail(e, "prefill_anchor");
+  return KAS_OK;
+}
+
+kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                               const int32_t* anchor_idx, int32_t anchor_kv_heads,
+                               const int32_t* head_map, void* o, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Shape s;
+  kas_status_t st = check_desc(desc, true, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!anchor_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_idx is NULL");
+  if (anchor_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_kv_heads must be >= 1");
+  if (!head_map && anchor_kv_heads != s.Hkv)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "identity head map needs anchor_kv_heads == n_kv_heads");
+  int64_t total = 0;
+  if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
+  size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, false);
+  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  PrefillArgs a;
+  fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, false);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map; a.total = total;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e = launch_prefill_reuse(a, ctx);
+  if (e != hipSuccess) return hip_fail(e, "prefill_reuse");
+  return KAS_OK;
+}
+
+const char* kas_status_string(kas_status_t status) {
+  switch (status) {
+    case KAS_OK: return "ok";
+    case KAS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KAS_ERR_UNSUPPORTED: return "unsupported";
+    case KAS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KAS_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kas_last_error(void) { return kas::t_last_error.c_str(); }
+
+kas_status_t kas_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return KAS_OK;
+}
+
+kas_status_t kas_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending_locked();
+  for (int i = 0; i < K_COUNT_; ++i) { g_total_ms[i] = 0.0; g_launches[i] = 0; }
+  return KAS_OK;
+}
+
+kas_status_t kas_profile_query(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(KAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending_locked();
+  for (int i = 0; i < K_COUNT_; ++i)
+    if (!strcmp(kernel, kKernelNames[i])) {
+      *total_ms = g_total_ms[i];
+      *launches = g_launches[i];
+      return KAS_OK;
+    }
+  return fail(KAS_ERR_INVALID_ARGUMENT, "unknown kernel name '%s'", kernel);
+}
+
+kas_status_t kas_profile_names(char* buf, size_t buf_len) {
+  if (!buf || !buf_len) return fail(KAS_ERR_INVALID_ARGUMENT, "NULL buffer");
+  std::string all;
+  for (int i = 0; i < K_COUNT_; ++i) {
+    if (i) all += ",";
+    all += kKernelNames[i];
+  }
+  if (all.size() + 1 > buf_len) return fail(KAS_ERR_INVALID_ARGUMENT, "buffer too small");
+  memcpy(buf, all.c_str(), all.size() + 1);
+  return KAS_OK;
+}
+
+}  // extern "C"

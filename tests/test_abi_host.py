@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kascade.h")
+
+
+def _kas():
+    import sparse_attention_long_anchor_amd.binding as b
+    if not os.path.exists(b.lib_path()):
+        from sparse_attention_long_anchor_amd import build as bld
+        bld.build()
+    return b
+
+
+def test_library_exports_every_declared_symbol():
+    b = _kas()
+    declared = set(re.findall(r"\b(kas_[a-z0-9_]+)\s*\(", open(HEADER).read()))
+    assert len(declared) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", b.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kas_[a-z0-9_]+)$", out, re.M))
+    assert declared <= exported, declared - exported
+    L = ctypes.CDLL(b.lib_path())
+    for name in declared:
+        getattr(L, name)
+
+
+def test_topk_count_and_offsets_agree_with_oracle():
+    import oracle
+    b = _kas()
+    for n in [0, 1, 2, 4, 5, 31, 32, 100, 2048, 32768, 131072, 10**6 + 7]:
+        for pct in [1, 5, 10, 33, 50, 99, 100]:
+            assert b.topk_count(n, pct) == oracle.topk_count(n, pct)
+            assert b.decode_k(n, pct) == oracle.decode_k(n, pct)
+    for n in [32, 64, 96, 4096, 32768, 131072]:
+        for pct in [1, 10, 100]:
+            d = b.make_desc(1, 32, 8, 128, n, pct, __import__("torch").bfloat16)
+            np.testing.assert_array_equal(b.prefill_offsets(d), oracle.prefill_offsets(n, 32, pct))
+
+
+def _status(fn):
+    b = _kas()
+    with pytest.raises(b.KasError) as e:
+        fn()
+    return e.value.status
+
+
+def test_descriptor_validation():
+    import torch
+    b = _kas()
+    ok = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16)
+    assert b.workspace_size(ok, b.OP_DECODE_ANCHOR) > b.workspace_size(ok, b.OP_DECODE_REUSE) > 0
+    assert b.workspace_size(ok, b.OP_PREFILL_REUSE) >= 0
+    bad = [
+        (b.make_desc(1, 12, 4, 128, 64, 10, torch.bfloat16), b.OP_DECODE_REUSE, 2),    # G = 3
+        (b.make_desc(1, 32, 8, 96, 64, 10, torch.bfloat16), b.OP_DECODE_REUSE, 2),     # head_dim
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.float32), b.OP_PREFILL_ANCHOR, 2),   # prefill f32
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, tile=16), b.OP_PREFILL_ANCHOR, 2),
+        (b.make_desc(1, 32, 8, 128, 70, 10, torch.bfloat16), b.OP_PREFILL_REUSE, 2),   # N % 32
+        (b.make_desc(1, 32, 8, 128, 64, 0, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),    # pct
+        (b.make_desc(1, 32, 8, 128, 64, 101, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),
+        (b.make_desc(1, 30, 8, 128, 64, 10, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),   # Hq % Hkv
+        (b.make_desc(0, 32, 8, 128, 64, 10, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),   # batch
+        (b.make_desc(1, 32, 8, 128, 0, 10, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),    # seq_len
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, kv_head_stride=64), b.OP_DECODE_ANCHOR, 1),
+    ]
+    for d, op, want in bad:
+        assert _status(lambda: b.workspace_size(d, op)) == want
+    L = b._load()
+    n = ctypes.c_size_t(0)
+    assert L.kas_workspace_size(None, 0, ctypes.byref(n)) == 1
+    assert L.kas_workspace_size(ctypes.byref(ok), 7, ctypes.byref(n)) == 1
+
+
+def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
+    import torch
+    b = _kas()
+    L = b._load()
+    d = b.make_desc(1, 8, 2, 64, 2048, 10, torch.float32)
+    need = b.workspace_size(d, b.OP_DECODE_ANCHOR)
+    fake = ctypes.c_void_p(1 << 20)           # never dereferenced: checks fail first
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    r = L.kas_decode_anchor(ctypes.byref(d), None, fake, fake, fake, fake, fake, need, None)
+    assert r == 1 and b"q is NULL" in L.kas_last_error()
+    r = L.kas_decode_anchor(ctypes.byref(d), mis, fake, fake, fake, fake, fake, need, None)
+    assert r == 1 and b"aligned" in L.kas_last_error()
+    r = L.kas_decode_anchor(ctypes.byref(d), fake, fake, fake, fake, fake, fake, need - 1, None)
+    assert r == 3
+    r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, fake, 3, None, fake, fake, 1 << 30, None)
+    assert r == 1 and b"identity head map" in L.kas_last_error()
+    r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, None, 2, None, fake, fake, 1 << 30, None)
+    assert r == 1
+    dp = b.make_desc(1, 8, 2, 64, 96, 10, torch.float32)
+    r = L.kas_prefill_anchor(ctypes.byref(dp), fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    assert r == 2
+    assert L.kas_status_string(3) == b"workspace too small"
+
+
+def test_profile_names():
+    b = _kas()
+    names = b.profile_names()
+    for n in ["decode_score", "decode_pool", "decode_attn", "decode_combine", "select_compact"]:
+        assert n in names
+    with pytest.raises(b.KasError):
+        b.profile_query("no_such_kernel")
