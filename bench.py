@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kascade sparse-attention hot path on one MI355X.
+
+One step = one decode step of the 32-layer Llama-3.1-8B-shaped schedule at
+131072 context (batch 4, anchors {0,2,8,13,22}, Top-k 10 %) followed by one
+prefill of the 32-layer Llama-3.1-8B-shaped schedule at 131072 tokens (tile 32,
+Top-k 10 %). Every layer has its own synthetic, seeded Q/K/V resident in HBM
+before timing starts; anchor layers write their index sets, reuse layers read
+the nearest preceding anchor's sets through their head map.
+
+Prints one JSON line. `value` is the decode step's algorithmic HBM throughput
+(GB/s over all layers); per-layer microseconds, prefill TFLOP/s, the roofline
+of the dominant kernel (device time from HIP events recorded by the library
+around each launch during the timed steps) and the CPU oracle baseline are
+reported alongside.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn μs/layer + HBM GB/s at 128K ctx, Top-k 10%; prefill attn TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def decode_work(w, k):
+    """Algorithmic bytes of one decode layer call and of its main kernels."""
+    B, Hq, Hkv, D, N, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.group
+    s = 2 if w.dtype == "bf16" else 4
+    qo = 2 * B * Hq * D * s
+    reuse = B * Hkv * k * 2 * D * s + B * Hkv * k * 4 + qo
+    anchor = B * Hkv * N * D * s + B * Hkv * k * D * s + B * Hkv * k * 4 + qo
+    kern = {
+        "decode_attn": B * Hkv * k * (2 * D * s + 4) + B * Hq * D * s,
+        "decode_attn_anchor": B * Hkv * k * (D * s + 4 + 4 * G),
+        "decode_score": B * Hkv * N * D * s + B * Hq * D * s,
+    }
+    return reuse, anchor, kern
+
+
+def prefill_work(w, offsets):
+    B, Hq, D, N = w.batch, w.n_q_heads, w.head_dim, w.seq_len
+    T = N // 32
+    sum_k = int(offsets[-1])
+    stats = D * Hq * B * N * (N + 1)                       # causal Q.K^T, 2 flop / MAC
+    pool = 2 * D * Hq * B * 1024 * T * (T - 1) // 2        # Q.K^T over keys before each tile
+    attn = 4 * D * Hq * B * (32 * sum_k + 528 * T)         # Q.K^T + P.V over set + diagonal
+    return {"prefill_stats": stats, "prefill_pool": pool, "prefill_attn": attn}
+
+
+# ---------------------------------------------------------------- setup
+
+def build_decode(w, dev, torch, inputgen, kas):
+    pos = inputgen.heavy_positions(w)
+    maps = inputgen.head_maps(w)
+    layers = []
+    for l in range(w.n_layers):
+        q, k, v = inputgen.layer_inputs(w, l, dev, pos)
+        hm = None if maps[l] is None else torch.as_tensor(maps[l], device=dev)
+        layers.append((q, k, v, hm))
+    kd = kas.decode_k(w.seq_len, w.topk_pct)
+    idx = {a: torch.empty((w.batch, w.n_kv_heads, kd), dtype=torch.int32, device=dev) for a in w.anchors}
+    o = torch.empty_like(layers[0][0])
+    d = kas.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.topk_pct, w.torch_dtype)
+    ws_a = torch.empty(kas.workspace_size(d, kas.OP_DECODE_ANCHOR), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(kas.workspace_size(d, kas.OP_DECODE_REUSE), dtype=torch.uint8, device=dev)
+    return layers, idx, o, ws_a, ws_r, kd
+
+
+def run_decode_step(w, st, inputgen, kas, events=None):
+    layers, idx, o, ws_a, ws_r, _ = st
+    for l, (q, k, v, hm) in enumerate(layers):
+        if events is not None:
+            events[l][0].record()
+        if l in w.anchors:
+            kas.decode_anchor(q, k, v, w.topk_pct, idx_out=idx[l], o=o, ws=ws_a)
+        else:
+            kas.decode_reuse(q, k, v, idx[inputgen.anchor_of(w, l)], hm, w.topk_pct, o=o, ws=ws_r)
+        if events is not None:
+            events[l][1].record()
+
+
+def build_prefill(w, dev, torch, inputgen, kas):
+    pos = inputgen.heavy_positions(w)
+    maps = inputgen.head_maps(w)
+    layers = []
+    for l in range(w.n_layers):
+        q, k, v = inputgen.layer_inputs(w, l, dev, pos)
+        hm = None if maps[l] is None else torch.as_tensor(maps[l], device=dev)
+        layers.append((q, k, v, hm))
+    d = kas.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.topk_pct, w.torch_dtype)
+    off = kas.prefill_offsets(d)
+    idx = {a: torch.empty((w.batch, w.n_kv_heads, int(off[-1])), dtype=torch.int32, device=dev)
+           for a in w.anchors}
+    o = torch.empty_like(layers[0][0])
+    ws_a = torch.empty(kas.workspace_size(d, kas.OP_PREFILL_ANCHOR), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(max(256, kas.workspace_size(d, kas.OP_PREFILL_REUSE)), dtype=torch.uint8, device=dev)
+    return layers, idx, o, ws_a, ws_r, off
+
+
+def run_prefill_step(w, st, inputgen, kas, events=None):
+    layers, idx, o, ws_a, ws_r, _ = st
+    for l, (q, k, v, hm) in enumerate(layers):
+        if events is not None:
+            events[l][0].record()
+        if l in w.anchors:
+            kas.prefill_anchor(q, k, v, w.topk_pct, idx_out=idx[l], o=o, ws=ws_a)
+        else:
+            kas.prefill_reuse(q, k, v, idx[inputgen.anchor_of(w, l)], hm, w.topk_pct, o=o, ws=ws_r)
+        if events is not None:
+            events[l][1].record()
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(wd, dec_state, wp, pre_state, budget_s, inputgen):
+    """Time the (untuned) oracle on a bounded sample of the same workloads."""
+    import numpy as np
+    import oracle
+    layers, idx, *_ = dec_state
+    reuse_b, anchor_b, _ = decode_work(wd, oracle.decode_k(wd.seq_len, wd.topk_pct))
+    maps = inputgen.head_maps(wd)
+    f = lambda t: t.float().cpu().numpy()
+    done_bytes, spent, n_layers = 0, 0.0, 0
+    cur_idx = None
+    for l, (q, k, v, _) in enumerate(layers):
+        if spent > budget_s and n_layers >= 2:
+            break
+        qn, kn, vn = f(q), f(k), f(v)
+        t0 = time.perf_counter()
+        if l in wd.anchors:
+            cur_idx, _, _ = oracle.decode_anchor(qn, kn, vn, wd.topk_pct)
+            done_bytes += anchor_b
+        else:
+            oracle.decode_reuse(qn, kn, vn, cur_idx, maps[l])
+            done_bytes += reuse_b
+        spent += time.perf_counter() - t0
+        n_layers += 1
+        del qn, kn, vn
+    dec_gbs = done_bytes / spent / 1e9
+    # prefill: anchor layer 0 on the last tile and on one mid tile
+    pl = pre_state[0][0]
+    q, k, v, _ = pl
+    kn, vn = f(k), f(v)
+    T = wp.seq_len // 32
+    tiles = [T - 1, T // 2]
+    flops, tp = 0, 0.0
+    D, G = wp.head_dim, wp.group
+    for t in tiles:
+        qr = f(q[:, :, 32 * t: 32 * t + 32])
+        t0 = time.perf_counter()
+        oracle.prefill_anchor(qr, kn, vn, wp.topk_pct, t0=t, t1=t + 1)
+        tp += time.perf_counter() - t0
+        kt = oracle.topk_count(32 * t, wp.topk_pct)
+        rows = wp.batch * wp.n_q_heads * 32
+        flops += 2 * D * rows * (32 * t + 16.5)      # row statistics (causal)
+        flops += 2 * D * rows * 32 * t               # pooled scores
+        flops += 4 * D * rows * (kt + 16.5)          # output over set + diagonal
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {
+        "value": round(dec_gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"{wd.name}: first {n_layers} layers of the schedule (full B,Hkv,N per layer); "
+                  f"oracle fp64 C with OpenMP; {spent:.1f} s",
+        "prefill": {"value": round(flops / tp / 1e12, 6), "unit": "TFLOP/s",
+                    "sample": f"{wp.name} anchor layer 0, tiles {tiles} (all KV heads); {tp:.1f} s"},
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--phase", choices=["both", "decode", "prefill"], default="both")
+    ap.add_argument("--decode-workload", default="llama8b_decode_128k")
+    ap.add_argument("--prefill-workload", default="llama8b_prefill_128k")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import inputgen
+    import sparse_attention_long_anchor_amd as kas
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wd = inputgen.WORKLOADS[args.decode_workload]
+    wp = inputgen.WORKLOADS[args.prefill_workload]
+    do_dec = args.phase in ("both", "decode")
+    do_pre = args.phase in ("both", "prefill")
+
+    dec_state = pre_state = None
+    if do_dec:
+        log(f"[bench] generating {wd.name} ({wd.n_layers} layers)")
+        dec_state = build_decode(wd, dev, torch, inputgen, kas)
+    if do_pre:
+        log(f"[bench] generating {wp.name} ({wp.n_layers} layers)")
+        pre_state = build_prefill(wp, dev, torch, inputgen, kas)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        if do_dec:
+            run_decode_step(wd, dec_state, inputgen, kas)
+        if do_pre:
+            run_prefill_step(wp, pre_state, inputgen, kas)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    dec_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(wd.n_layers)] for _ in range(args.steps)] if do_dec else None
+    pre_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(wp.n_layers)] for _ in range(args.steps)] if do_pre else None
+    kas.profile_reset()
+    kas.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if do_dec:
+            run_decode_step(wd, dec_state, inputgen, kas, dec_ev[s])
+        if do_pre:
+            run_prefill_step(wp, pre_state, inputgen, kas, pre_ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kas.profile_enable(False)
+    log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    kern_ms = {}
+    for name in kas.profile_names():
+        ms, n = kas.profile_query(name)
+        if n:
+            kern_ms[name] = (ms, n)
+
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": " + ".join(([wd.name] if do_dec else []) + ([wp.name] if do_pre else [])),
+                      "phase": args.phase}}
+    roof = []
+    if do_dec:
+        kd = dec_state[5]
+        reuse_b, anchor_b, kern_b = decode_work(wd, kd)
+        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in dec_ev]
+        per_layer = [sum(x[l] for x in lay_ms) / args.steps for l in range(wd.n_layers)]
+        anc = [per_layer[l] for l in range(wd.n_layers) if l in wd.anchors]
+        reu = [per_layer[l] for l in range(wd.n_layers) if l not in wd.anchors]
+        step_ms = sum(per_layer)
+        step_bytes = len(anc) * anchor_b + len(reu) * reuse_b
+        gbs = step_bytes / (step_ms * 1e-3) / 1e9
+        out["value"] = round(gbs, 3)
+        out["decode"] = {
+            "workload": wd.name, "batch": wd.batch, "seq_len": wd.seq_len, "layers": wd.n_layers,
+            "anchors": list(wd.anchors), "topk_pct": wd.topk_pct, "k": kd,
+            "us_per_layer": {"anchor": round(1e3 * sum(anc) / len(anc), 3),
+                             "reuse": round(1e3 * sum(reu) / len(reu), 3),
+                             "mean": round(1e3 * step_ms / wd.n_layers, 3)},
+            "GB_per_s": {"anchor": round(anchor_b / (sum(anc) / len(anc) * 1e-3) / 1e9, 2),
+                         "reuse": round(reuse_b / (sum(reu) / len(reu) * 1e-3) / 1e9, 2),
+                         "step": round(gbs, 2)},
+            "ms_per_step": round(step_ms, 4),
+            "tokens_per_s": round(wd.batch / (step_ms * 1e-3), 2),
+        }
+        n_anc, n_reu = len(anc) * args.steps, len(reu) * args.steps
+        ops = {"decode_attn": n_reu, "decode_attn_anchor": n_anc, "decode_score": n_anc}
+        for name, b in kern_b.items():
+            if name in kern_ms:
+                roof.append(_roof_entry(name, "hbm", b * ops[name], kern_ms[name], HBM_PEAK_GBS, "GB/s", 1e9))
+    if do_pre:
+        off = pre_state[5]
+        work = prefill_work(wp, off)
+        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in pre_ev]
+        per_layer = [sum(x[l] for x in lay_ms) / args.steps for l in range(wp.n_layers)]
+        anc = [per_layer[l] for l in range(wp.n_layers) if l in wp.anchors]
+        reu = [per_layer[l] for l in range(wp.n_layers) if l not in wp.anchors]
+        step_ms = sum(per_layer)
+        anc_flops = work["prefill_stats"] + work["prefill_pool"] + work["prefill_attn"]
+        out["prefill"] = {
+            "workload": wp.name, "batch": wp.batch, "seq_len": wp.seq_len, "layers": wp.n_layers,
+            "anchors": list(wp.anchors), "topk_pct": wp.topk_pct, "index_entries_per_kv_head": int(off[-1]),
+            "ms_per_layer": {"anchor": round(sum(anc) / len(anc), 4), "reuse": round(sum(reu) / len(reu), 4)},
+            "TFLOP_per_s": {"anchor_layer": round(anc_flops / (sum(anc) / len(anc) * 1e-3) / 1e12, 3),
+                            "reuse_layer": round(work["prefill_attn"] / (sum(reu) / len(reu) * 1e-3) / 1e12, 3)},
+            "ms_per_step": round(step_ms, 3),
+            "tokens_per_s": round(wp.batch * wp.seq_len / (step_ms * 1e-3), 1),
+        }
+        n_anc, n_all = len(anc) * args.steps, wp.n_layers * args.steps
+        ops = {"prefill_stats": n_anc, "prefill_pool": n_anc, "prefill_attn": n_all}
+        for name, f in work.items():
+            if name in kern_ms:
+                roof.append(_roof_entry(name, "mfma", f * ops[name], kern_ms[name], BF16_PEAK_TFLOPS,
+                                        "TFLOP/s", 1e12))
+    for r in roof:
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+    out["kernels"] = {n: {"total_ms": round(ms, 3), "launches": c, "avg_us": round(1e3 * ms / c, 3)}
+                      for n, (ms, c) in sorted(kern_ms.items(), key=lambda x: -x[1][0])}
+    if roof:
+        dom = max(roof, key=lambda r: r["total_ms"])
+        traffic = _traffic(dom["kernel"])
+        out["roofline"] = {"kernel": dom["kernel"], "bound": dom["bound"], "achieved": dom["achieved"],
+                           "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
+        for r in roof:
+            if r["kernel"] == "decode_attn":
+                out["roofline_decode_reuse"] = {"kernel": "decode_attn", "bound": "hbm", "achieved": r["achieved"],
+                                                "peak": r["peak"], "unit": "GB/s", "frac": r["frac"],
+                                                "traffic": _traffic("decode_attn")}
+        out["roofline_all"] = [{k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac", "avg_us")}
+                               for r in roof]
+    if not args.no_cpu_baseline and do_dec and do_pre:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
+    print(json.dumps(out), flush=True)
+
+
+def _roof_entry(name, bound, total_work, ms_n, peak, unit, scale):
+    """Algorithmic work per launch / average launch duration (equal to total
+    work / total device time of the kernel over the timed region)."""
+    ms, n = ms_n
+    per_launch = total_work / n
+    avg_s = ms * 1e-3 / n
+    return {"kernel": name, "bound": bound, "achieved": round(per_launch / avg_s / scale, 3), "peak": peak,
+            "unit": unit, "total_ms": ms, "avg_us": avg_s * 1e6, "launches": n, "work_per_launch": per_launch}
+
+
+def _traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except Exception:
+        return None
+    ent = data.get(kernel)
+    if not ent:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_long_anchor_amd", "csrc", ent["source"])
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except Exception:
+        return None
+    return ent["bytes_per_launch"] if h == ent.get("source_sha256_16") else None
+
+
+if __name__ == "__main__":
+    main()

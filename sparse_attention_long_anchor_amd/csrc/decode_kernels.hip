@@ -550,13 +550,14 @@ static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx) {
   dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
-  ctx.begin(K_DEC_ATTN);
+  const int kid = from_logits ? K_DEC_ATTN_ANCHOR : K_DEC_ATTN;
+  ctx.begin(kid);
   if (dtype == 1) e = from_logits ? attn_by_d<__bf16, true>(a, grid, ctx.stream)
                                   : attn_by_d<__bf16, false>(a, grid, ctx.stream);
   else e = from_logits ? attn_by_d<float, true>(a, grid, ctx.stream)
                        : attn_by_d<float, false>(a, grid, ctx.stream);
   if (e != hipSuccess) return e;
-  if ((e = ctx.end(K_DEC_ATTN)) != hipSuccess) return e;
+  if ((e = ctx.end(kid)) != hipSuccess) return e;
   ctx.begin(K_DEC_COMBINE);
   dim3 cgrid(a.Hq, a.B);
   if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(128), ctx.stream, a);

@@ -14,6 +14,7 @@ enum KernelId {
   K_SEL_COUNT,
   K_SEL_COMPACT,
   K_DEC_ATTN,
+  K_DEC_ATTN_ANCHOR,
   K_DEC_COMBINE,
   K_PRE_STATS,
   K_PRE_POOL,

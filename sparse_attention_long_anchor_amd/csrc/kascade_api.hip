@@ -36,7 +36,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_digit2", "select_digit3", "select_count",
-    "select_compact", "decode_attn", "decode_combine", "prefill_stats", "prefill_pool",
+    "select_compact", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
     "prefill_select", "prefill_attn"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
