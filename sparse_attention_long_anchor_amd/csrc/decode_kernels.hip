@@ -453,22 +453,42 @@ __device__ __forceinline__ void store_out<__bf16>(__bf16* p, float x) {
   *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_rne(x);
 }
 
+// Merge of the split-K partials of one (b, query head): weights
+// exp2(m_s - M) staged in LDS, 256 threads = (256 / D) interleaved split
+// streams per output dim.
 template <typename T>
-__global__ __launch_bounds__(128) void dec_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  if (d >= a.D) return;
+__global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
+  constexpr int WCH = 1024;
+  __shared__ float s_w[WCH];
+  __shared__ float s_tmp[4];
+  __shared__ float s_acc[256];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t bh = (int64_t)b * a.Hq + h;
   const float* ml = a.part_ml + bh * a.nsplit * 2;
   const float* po = a.part_o + bh * a.nsplit * a.D;
-  float M = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float w = exp2_fast(ml[2 * s] - M);
-    L += ml[2 * s + 1] * w;
-    acc += po[(int64_t)s * a.D + d] * w;
+  float m = kNegInf;
+  for (int s = tid; s < a.nsplit; s += 256) m = fmaxf(m, ml[2 * s]);
+  const float M = block_max_256(m, s_tmp);
+  float l = 0.f;
+  for (int s = tid; s < a.nsplit; s += 256) l += ml[2 * s + 1] * exp2_fast(ml[2 * s] - M);
+  const float L = block_sum_256(l, s_tmp);
+  const int D = a.D, nparts = 256 / D, d = tid % D, part = tid / D;
+  float acc = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += WCH) {
+    const int n = min(WCH, a.nsplit - s0);
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) s_w[i] = exp2_fast(ml[2 * (s0 + i)] - M);
+    __syncthreads();
+#pragma unroll 4
+    for (int i = part; i < n; i += nparts) acc += po[(int64_t)(s0 + i) * D + d] * s_w[i];
   }
-  store_out<T>((T*)a.o + bh * a.D + d, acc / L);
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float tot = 0.f;
+    for (int x = 0; x < nparts; ++x) tot += s_acc[x * D + d];
+    store_out<T>((T*)a.o + bh * D + d, tot / L);
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -560,8 +580,8 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, 
   if ((e = ctx.end(kid)) != hipSuccess) return e;
   ctx.begin(K_DEC_COMBINE);
   dim3 cgrid(a.Hq, a.B);
-  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(128), ctx.stream, a);
-  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(128), ctx.stream, a);
+  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx.stream, a);
+  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx.stream, a);
   return ctx.end(K_DEC_COMBINE);
 }
 

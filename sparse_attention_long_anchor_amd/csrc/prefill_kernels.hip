@@ -17,6 +17,8 @@
 //               head), gathered K rows and transposed V rows in LDS, S^T and
 //               P.V on MFMA, online softmax over the tile's index set plus
 //               its causal diagonal block.
+#include <type_traits>
+
 #include "kas_block.hpp"
 #include "kas_prefill.hpp"
 
@@ -62,118 +64,217 @@ __global__ __launch_bounds__(256) void pre_offsets_kernel(PrefillArgs a) {
   if (threadIdx.x == 0) a.offsets[a.T] = (int32_t)carry;
 }
 
-// ------------------------------------------------------------------ K tile staging
+// ------------------------------------------------------------------ XCD-aware order
 
-// 32 consecutive (or gathered) K rows -> LDS, row stride KROW bytes.
-template <int D, int NT>
-__device__ __forceinline__ void stage_k_rows(char* s_k, int krow_bytes, const __bf16* kbase,
-                                             const int* rows /* nullptr: contiguous from row0 */,
-                                             int64_t row0) {
-  constexpr int PARTS = D / 8;
-  for (int x = threadIdx.x; x < 32 * PARTS; x += NT) {
-    const int r = x / PARTS, part = x % PARTS;
-    const int64_t src = rows ? (int64_t)rows[r] : row0 + r;
-    *reinterpret_cast<u32x4*>(s_k + r * krow_bytes + part * 16) = ldg16(kbase + src * D + part * 8);
-  }
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Within every group of 64 consecutive workgroups, the 8 that land on
+// one XCD get 8 consecutive work items (adjacent tiles share K/V rows and
+// index sets). Items are otherwise processed longest first.
+__device__ __forceinline__ int xcd_local_order(int j, int n) {
+  const int base = j & ~63;
+  if (base + 64 > n) return j;
+  const int w = j & 63;
+  return base + (w & 7) * 8 + (w >> 3);
 }
+
+// ------------------------------------------------------------------ K block staging
+
+// 32 consecutive K rows: global -> registers (issued early), registers -> LDS.
+template <int D, int NT>
+struct KStage {
+  static constexpr int PARTS = D / 8;
+  static constexpr int KROW = 2 * D + 16;   // padded LDS row (bytes)
+  static constexpr int NK = (32 * PARTS + NT - 1) / NT;
+  u32x4 r[NK];
+  __device__ __forceinline__ void load(const __bf16* kbase, int64_t row0) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = threadIdx.x + i * NT;
+      if (x < 32 * PARTS) r[i] = ldg16(kbase + (row0 + x / PARTS) * D + (x % PARTS) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(char* s_k) const {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = threadIdx.x + i * NT;
+      if (x < 32 * PARTS) *reinterpret_cast<u32x4*>(s_k + (x / PARTS) * KROW + (x % PARTS) * 16) = r[i];
+    }
+  }
+};
 
 // ------------------------------------------------------------------ pass 1: row statistics
 
+// Online (max, sum of exp) of one lane's query row over the 16 keys it holds
+// in a 32x32 S^T tile.
+__device__ __forceinline__ void row_stats_update(const f32x16& acc, bool diag, int n32, int hh, float cs,
+                                                 float& m, float& l) {
+  float v[16];
+  if (diag) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = (mrow(r, hh) > n32) ? kNegInf : acc[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = acc[r];
+  }
+  float bm = fmaxf(fmaxf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, v[r]), v[r + 1]);
+  bm = fmaxf(bm, v[15]);
+  const float mn = fmaxf(m, bm * cs);
+  if (mn != kNegInf) {
+    const float al = (mn == m) ? 1.f : exp2_fast(m - mn);
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(v[r], cs, -mn));
+    l = l * al + s;
+    m = mn;
+  }
+}
+
+// One workgroup = two consecutive tiles (t0 = 2p, t1 = 2p+1) of one KV head;
+// wave w = query head g*G + w; each staged K block feeds both tiles.
 template <int D, int G>
 __global__ __launch_bounds__(64 * G) void pre_stats_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16, KROW = 2 * D + 16;
-  __shared__ __align__(16) char s_k[32 * KROW];
-  const int t = a.T - 1 - blockIdx.x;          // long rows first
+  constexpr int NT = 64 * G, KC = D / 16;
+  using KS = KStage<D, NT>;
+  __shared__ __align__(16) char s_k[2][32 * KS::KROW];
+  const int npairs = (a.T + 1) / 2;
+  const int p = npairs - 1 - xcd_local_order(blockIdx.x, npairs);
+  const int t0 = 2 * p, t1 = 2 * p + 1;
+  const bool has1 = t1 < a.T;
+  const int tl = has1 ? t1 : t0;
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
-  const __bf16* qrow = (const __bf16*)a.q + (((int64_t)b * a.Hq + h) * a.N + kTile * t + n32) * D;
-  u32x4 qb[KC];
+  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N;
+  u32x4 qb0[KC], qb1[KC];
+  {
+    const __bf16* q0 = (const __bf16*)a.q + (qoff + kTile * t0 + n32) * D;
+    const __bf16* q1 = (const __bf16*)a.q + (qoff + kTile * (has1 ? t1 : t0) + n32) * D;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) qb[c] = ldg16(qrow + 16 * c + 8 * hh);
+    for (int c = 0; c < KC; ++c) { qb0[c] = ldg16(q0 + 16 * c + 8 * hh); qb1[c] = ldg16(q1 + 16 * c + 8 * hh); }
+  }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
-  float m = kNegInf, l = 0.f;
-  for (int kb = 0; kb <= t; ++kb) {
-    __syncthreads();
-    stage_k_rows<D, NT>(s_k, KROW, kbase, nullptr, (int64_t)kTile * kb);
-    __syncthreads();
-    f32x16 acc = {};
+  float m0 = kNegInf, l0 = 0.f, m1 = kNegInf, l1 = 0.f;
+  KS st;
+  st.load(kbase, 0);
+  st.store(s_k[0]);
+  __syncthreads();
+  for (int kb = 0; kb <= tl; ++kb) {
+    const int buf = kb & 1;
+    if (kb < tl) st.load(kbase, (int64_t)kTile * (kb + 1));
+    const char* sk = s_k[buf];
+    f32x16 acc0 = {}, acc1 = {};
+    const bool do0 = kb <= t0;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(s_k + n32 * KROW + (16 * c + 8 * hh) * 2);
-      acc = mfma32(ka, qb[c], acc);             // S^T[key][query]
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+      if (do0) acc0 = mfma32(ka, qb0[c], acc0);   // S^T[key][query]
+      if (has1) acc1 = mfma32(ka, qb1[c], acc1);
     }
-    if (kb == t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (mrow(r, hh) > n32) acc[r] = kNegInf;
-    }
-    float bm = acc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) bm = fmaxf(bm, acc[r]);
-    const float mn = fmaxf(m, bm * cs);
-    if (mn != kNegInf) {
-      const float al = (mn == m) ? 1.f : exp2_fast(m - mn);
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(acc[r], cs, -mn));
-      l = l * al + s;
-      m = mn;
-    }
+    if (do0) row_stats_update(acc0, kb == t0, n32, hh, cs, m0, l0);
+    if (has1) row_stats_update(acc1, kb == t1, n32, hh, cs, m1, l1);
+    if (kb < tl) st.store(s_k[buf ^ 1]);
+    __syncthreads();
   }
-  const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
-  const float M = fmaxf(m, m2);
-  const float L = (m == kNegInf ? 0.f : l * exp2_fast(m - M)) + (m2 == kNegInf ? 0.f : l2 * exp2_fast(m2 - M));
-  if (hh == 0) a.lse[((int64_t)b * a.Hq + h) * a.N + kTile * t + n32] = M + log2f(L);
+  auto finish = [&](float m, float l, int t) {
+    const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
+    const float M = fmaxf(m, m2);
+    const float L = (m == kNegInf ? 0.f : l * exp2_fast(m - M)) + (m2 == kNegInf ? 0.f : l2 * exp2_fast(m2 - M));
+    if (hh == 0) a.lse[qoff + kTile * t + n32] = M + log2f(L);
+  };
+  finish(m0, l0, t0);
+  if (has1) finish(m1, l1, t1);
 }
 
 // ------------------------------------------------------------------ pass 2: pooled scores
 
+// One workgroup = tiles (t0 = 2p, t1 = 2p+1) of one KV head. For every staged
+// key block before a tile, each wave (query head) forms S = Q.K^T, the
+// probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
+// waves' sums are added through LDS (double-buffered, one barrier per block).
 template <int D, int G>
 __global__ __launch_bounds__(64 * G) void pre_pool_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16, KROW = 2 * D + 16;
-  __shared__ __align__(16) char s_k[32 * KROW];
-  __shared__ float s_col[G][32];
-  const int t = a.t_end - 1 - blockIdx.x;
+  constexpr int NT = 64 * G, KC = D / 16;
+  using KS = KStage<D, NT>;
+  __shared__ __align__(16) char s_k[2][32 * KS::KROW];
+  __shared__ float s_col[2][2][G][32];
+  const int pa0 = a.t_begin / 2;
+  const int npairs = (a.t_end + 1) / 2 - pa0;
+  const int p = pa0 + npairs - 1 - xcd_local_order(blockIdx.x, npairs);
+  const int t0 = 2 * p, t1 = 2 * p + 1;
+  const bool has1 = t1 < a.T;
+  const int nkb = has1 ? t1 : t0;              // key blocks before the later tile
+  if (nkb == 0) return;
   const int g = blockIdx.y, b = blockIdx.z;
-  if (t < 1) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + kTile * t;
-  const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
-  u32x4 qa[KC];
+  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N;
+  u32x4 qa0[KC], qa1[KC];
+  float lse0[16], lse1[16];
+  {
+    const int tq1 = has1 ? t1 : t0;
+    const __bf16* q0 = (const __bf16*)a.q + (qoff + kTile * t0 + n32) * D;
+    const __bf16* q1 = (const __bf16*)a.q + (qoff + kTile * tq1 + n32) * D;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) qa[c] = ldg16(qrow + 16 * c + 8 * hh);
-  float lse[16];
+    for (int c = 0; c < KC; ++c) { qa0[c] = ldg16(q0 + 16 * c + 8 * hh); qa1[c] = ldg16(q1 + 16 * c + 8 * hh); }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) lse[r] = a.lse[qoff + mrow(r, hh)];
+    for (int r = 0; r < 16; ++r) {
+      lse0[r] = a.lse[qoff + kTile * t0 + mrow(r, hh)];
+      lse1[r] = a.lse[qoff + kTile * tq1 + mrow(r, hh)];
+    }
+  }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  float* out = a.pooled + pool_slot(a, b, g, t);
+  float* out0 = a.pooled + pool_slot(a, b, g, t0);
+  float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
-  for (int kb = 0; kb < t; ++kb) {
-    __syncthreads();
-    stage_k_rows<D, NT>(s_k, KROW, kbase, nullptr, (int64_t)kTile * kb);
-    __syncthreads();
-    f32x16 acc = {};
+  KS st;
+  st.load(kbase, 0);
+  st.store(s_k[0]);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) st.load(kbase, (int64_t)kTile * (kb + 1));
+    const char* sk = s_k[buf];
+    const bool do0 = kb < t0;
+    f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 kbv = *reinterpret_cast<const u32x4*>(s_k + n32 * KROW + (16 * c + 8 * hh) * 2);
-      acc = mfma32(qa[c], kbv, acc);            // S[query][key]
+      const u32x4 kbv = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+      if (do0) acc0 = mfma32(qa0[c], kbv, acc0);   // S[query][key]
+      if (has1) acc1 = mfma32(qa1[c], kbv, acc1);
     }
-    float col = 0.f;
+    if (do0) {
+      float col = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc[r], cs, -lse[r]));
-    col += __shfl_xor(col, 32);
-    if (hh == 0) s_col[w][n32] = col;
+      for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc0[r], cs, -lse0[r]));
+      col += __shfl_xor(col, 32);
+      if (hh == 0) s_col[buf][0][w][n32] = col;
+    }
+    if (has1) {
+      float col = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc1[r], cs, -lse1[r]));
+      col += __shfl_xor(col, 32);
+      if (hh == 0) s_col[buf][1][w][n32] = col;
+    }
+    if (kb + 1 < nkb) st.store(s_k[buf ^ 1]);
     __syncthreads();
-    if (w == 0 && hh == 0) {
-      float s = 0.f;
+    // block kb's per-head column sums are complete: one wave per tile adds them
+    if (hh == 0 && w < 2) {
+      const int tile = (G == 1) ? -1 : w;
+      if (G == 1) {
+        if (do0) out0[kTile * kb + n32] = s_col[buf][0][0][n32];
+        if (has1) out1[kTile * kb + n32] = s_col[buf][1][0][n32];
+      } else if ((tile == 0 && do0) || (tile == 1 && has1)) {
+        float sum = 0.f;
 #pragma unroll
-      for (int x = 0; x < G; ++x) s += s_col[x][n32];
-      out[kTile * kb + n32] = s;
+        for (int x = 0; x < G; ++x) sum += s_col[buf][tile][x][n32];
+        (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
+      }
     }
   }
 }
@@ -184,7 +285,7 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   __shared__ uint32_t s_h[kBins1];
   __shared__ uint32_t s_tmp[4];
   __shared__ int s_res[2];
-  const int t = a.t_end - 1 - blockIdx.x;
+  const int t = a.t_end - 1 - xcd_local_order(blockIdx.x, a.t_end - a.t_begin);
   const int g = blockIdx.y, b = blockIdx.z;
   if (t < 1) return;
   const int tid = threadIdx.x;
@@ -264,16 +365,17 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
 // ------------------------------------------------------------------ sparse tile attention
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * G) void pre_attn_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32;
+__global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
+  constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
   constexpr int KROW = 2 * D + 16;   // bytes per K row in LDS
   constexpr int VROW = 2 * 32 + 8;   // bytes per V^T row (32 keys + pad)
-  __shared__ __align__(16) char s_k[32 * KROW];
-  __shared__ __align__(16) char s_vt[D * VROW];
-  __shared__ int s_key[32];
+  constexpr int NK = (32 * PARTS + NT - 1) / NT;   // K 16-byte loads per thread per block
+  constexpr int NV = (16 * PARTS + NT - 1) / NT;   // V key-pair loads per thread per block
+  __shared__ __align__(16) char s_k[2][32 * KROW];
+  __shared__ __align__(16) char s_vt[2][D * VROW];
   __shared__ float s_x[G][32];
 
-  const int t = a.T - 1 - blockIdx.x;
+  const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
   const int g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n32 = lane & 31, hh = lane >> 5;
@@ -284,8 +386,9 @@ __global__ __launch_bounds__(64 * G) void pre_attn_kernel(PrefillArgs a) {
   const int kt = a.offsets[t + 1] - o0;
   const int32_t* S = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
   const int nsel = (kt + 31) / 32;
+  const int tile_key0 = kTile * t;
 
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + kTile * t;
+  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
   u32x4 qb[KC];
   {
     const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
@@ -295,96 +398,128 @@ __global__ __launch_bounds__(64 * G) void pre_attn_kernel(PrefillArgs a) {
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
-  const int tile_key0 = kTile * t;
+
+  // key of row r of block blk; padding rows read row 0 and are masked later
+  auto key_of = [&](int blk, int r) -> int {
+    if (blk == nsel) return tile_key0 + r;
+    const int s = blk * 32 + r;
+    if (s >= kt) return 0;
+    const int j = S[s];
+    return ((unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
+  };
+  u32x4 kreg[NK], v0r[NV], v1r[NV];
+  auto load_block = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = tid + i * NT;
+      if (x < 32 * PARTS) kreg[i] = ldg16(kbase + (int64_t)key_of(blk, x / PARTS) * D + (x % PARTS) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int x = tid + i * NT;
+      if (x < 16 * PARTS) {
+        const int kp = x / PARTS, part = x % PARTS;
+        v0r[i] = ldg16(vbase + (int64_t)key_of(blk, 2 * kp) * D + part * 8);
+        v1r[i] = ldg16(vbase + (int64_t)key_of(blk, 2 * kp + 1) * D + part * 8);
+      }
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int x = tid + i * NT;
+      if (x < 32 * PARTS)
+        *reinterpret_cast<u32x4*>(s_k[buf] + (x / PARTS) * KROW + (x % PARTS) * 16) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int x = tid + i * NT;
+      if (x < 16 * PARTS) {
+        const int kp = x / PARTS, part = x % PARTS;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (v0r[i][e] & 0xffffu) | (v1r[i][e] << 16);          // dim 2e
+          const uint32_t hi = (v0r[i][e] >> 16) | (v1r[i][e] & 0xffff0000u);      // dim 2e+1
+          *reinterpret_cast<uint32_t*>(s_vt[buf] + (part * 8 + 2 * e) * VROW + 4 * kp) = lo;
+          *reinterpret_cast<uint32_t*>(s_vt[buf] + (part * 8 + 2 * e + 1) * VROW + 4 * kp) = hi;
+        }
+      }
+    }
+  };
 
   float m_run = kNegInf, l_run = 0.f;
   f32x16 o[NDC];
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x16{};
 
-  for (int blk = 0; blk <= nsel; ++blk) {
-    const bool diag = blk == nsel;
-    __syncthreads();
-    if (tid < 32) {
-      int key;
-      if (diag) {
-        key = tile_key0 + tid;
-      } else {
-        const int s = blk * 32 + tid;
-        key = -1;
-        if (s < kt) {
-          const int j = S[s];
-          key = ((unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
-        }
-      }
-      s_key[tid] = key;
-    }
-    __syncthreads();
-    // K rows (row-major) and V rows transposed to [d][key]
-    {
-      constexpr int PARTS = D / 8;
-      for (int x = tid; x < 32 * PARTS; x += NT) {
-        const int r = x / PARTS, part = x % PARTS;
-        const int key = s_key[r];
-        *reinterpret_cast<u32x4*>(s_k + r * KROW + part * 16) =
-            ldg16(kbase + (int64_t)(key < 0 ? 0 : key) * D + part * 8);
-      }
-      for (int x = tid; x < 16 * PARTS; x += NT) {
-        const int kp = x / PARTS, part = x % PARTS;
-        const int k0 = s_key[2 * kp], k1 = s_key[2 * kp + 1];
-        const u32x4 v0 = ldg16(vbase + (int64_t)(k0 < 0 ? 0 : k0) * D + part * 8);
-        const u32x4 v1 = ldg16(vbase + (int64_t)(k1 < 0 ? 0 : k1) * D + part * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (v0[e] & 0xffffu) | (v1[e] << 16);          // dim 2e
-          const uint32_t hi = (v0[e] >> 16) | (v1[e] & 0xffff0000u);      // dim 2e+1
-          *reinterpret_cast<uint32_t*>(s_vt + (part * 8 + 2 * e) * VROW + 4 * kp) = lo;
-          *reinterpret_cast<uint32_t*>(s_vt + (part * 8 + 2 * e + 1) * VROW + 4 * kp) = hi;
-        }
-      }
-    }
-    __syncthreads();
+  // One key block: S^T on MFMA, online softmax, P.V on MFMA. MODE 0: 32
+  // selected keys; 1: the last, partial selected block; 2: the causal
+  // diagonal block. The next block's rows are loaded into registers before
+  // the math and written to the other LDS buffer after it.
+  auto step = [&](int blk, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    const int buf = blk & 1;
+    if (MODE != 2) load_block(blk + 1);
+    const char* sk = s_k[buf];
+    const char* svt = s_vt[buf];
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(s_k + n32 * KROW + (16 * c + 8 * hh) * 2);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KROW + (16 * c + 8 * hh) * 2);
       acc = mfma32(ka, qb[c], acc);             // S^T[key slot][query]
     }
     float x[16];
-    float bm = kNegInf;
+    if (MODE == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int slot = mrow(r, hh);
-      const bool ok = diag ? (slot <= n32) : (s_key[slot] >= 0);
-      x[r] = ok ? acc[r] * cs : kNegInf;
-      bm = fmaxf(bm, x[r]);
+      for (int r = 0; r < 16; ++r) x[r] = acc[r] * cs;
+    } else {
+      const int nvalid = kt - blk * 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int slot = mrow(r, hh);
+        const bool ok = (MODE == 2) ? (slot <= n32) : (slot < nvalid);
+        x[r] = ok ? acc[r] * cs : kNegInf;
+      }
     }
+    float bm = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, x[r]), x[r + 1]);
+    bm = fmaxf(bm, x[15]);
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    // lazy rescale: keep the running max unless a score exceeds it by 2^8
-    const bool bump = (m_run == kNegInf) ? (bm != kNegInf) : (bm > m_run + 8.f);
-    const float m_new = bump ? bm : m_run;
-    const float alpha = bump ? ((m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new)) : 1.f;
-    if (__any(bump)) {
-      if (hh == 0) s_x[w][n32] = alpha;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      float ar[16];
+    // Every row has a valid key in block 0 (the first selected keys, or its
+    // own diagonal key), so the running max is set there while O is still
+    // zero. Later blocks keep it unless a score exceeds it by 2^8 (lazy
+    // rescale: exponentials stay <= 2^8, exact after the final division).
+    if (blk == 0) {
+      m_run = bm;
+    } else {
+      const bool bump = bm > m_run + 8.f;
+      if (__builtin_expect(__any(bump), 0)) {
+        const float m_new = bump ? bm : m_run;
+        const float alpha = exp2_fast(m_run - m_new);
+        if (hh == 0) s_x[w][n32] = alpha;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        float ar[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ar[r] = s_x[w][mrow(r, hh)];
+        for (int r = 0; r < 16; ++r) ar[r] = s_x[w][mrow(r, hh)];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+        for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dc][r] *= ar[r];
-      __builtin_amdgcn_wave_barrier();
+          for (int r = 0; r < 16; ++r) o[dc][r] *= ar[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        l_run *= alpha;
+        m_run = m_new;
+      }
     }
-    l_run *= alpha;
-    m_run = m_new;
     float p[16];
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = (x[r] == kNegInf) ? 0.f : exp2_fast(x[r] - m_run);
+      p[r] = exp2_fast(x[r] - m_run);       // x = -inf -> 0
       ps += p[r];
     }
     l_run += ps;
@@ -392,21 +527,29 @@ __global__ __launch_bounds__(64 * G) void pre_attn_kernel(PrefillArgs a) {
     for (int c2 = 0; c2 < 2; ++c2) {
       u32x4 pa;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pa[e] = (uint32_t)f32_to_bf16_rne(p[8 * c2 + 2 * e]) | ((uint32_t)f32_to_bf16_rne(p[8 * c2 + 2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) pa[e] = pack_bf16x2(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        const char* vr = s_vt + (n32 + 32 * dc) * VROW;
+        const char* vr = svt + (n32 + 32 * dc) * VROW;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + (16 * c2 + 4 * hh) * 2);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (16 * c2 + 8 + 4 * hh) * 2);
         const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
         o[dc] = mfma32(pa, vb, o[dc]);
       }
     }
-  }
+    if (MODE != 2) store_block(buf ^ 1);
+    __syncthreads();
+  };
+
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  const int nfull = kt / 32;
+  for (int blk = 0; blk < nfull; ++blk) step(blk, std::integral_constant<int, 0>{});
+  if (nsel > nfull) step(nfull, std::integral_constant<int, 1>{});
+  step(nsel, std::integral_constant<int, 2>{});
   // normalise: row sums live with the query's lanes, output rows with registers
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  __syncthreads();
   if (hh == 0) s_x[w][n32] = 1.0f / l_tot;
   __syncthreads();
   float inv[16];
@@ -431,21 +574,22 @@ static int64_t pool_budget_floats() {
 }
 
 // Tiles [ta, tb) per pool/select launch so that the pooled rows fit the budget.
+// Chunks start at even tiles so that tile pairs (2p, 2p+1) never straddle two.
 static int next_chunk_end(int ta, int T, int64_t units, int64_t budget) {
   int64_t used = 0;
   int tb = ta;
   while (tb < T) {
-    const int64_t need = units * kTile * (int64_t)tb;
+    const int64_t need = units * kTile * ((int64_t)tb + (tb + 1 < T ? tb + 1 : 0));
     if (tb > ta && used + need > budget) break;
     used += need;
-    ++tb;
+    tb = (tb + 2 < T) ? tb + 2 : T;
   }
   return tb;
 }
 
 static int64_t max_chunk_floats(int T, int64_t units, int64_t budget) {
   int64_t best = 0;
-  for (int ta = 1; ta < T;) {
+  for (int ta = 0; ta < T;) {
     const int tb = next_chunk_end(ta, T, units, budget);
     const int64_t f = units * kTile * ((int64_t)tb * (tb - 1) / 2 - (int64_t)ta * (ta - 1) / 2);
     best = f > best ? f : best;
@@ -536,20 +680,21 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   if ((e = launch_offsets(a, ctx)) != hipSuccess) return e;
   ctx.begin(K_PRE_STATS);
   {
-    dim3 grid(a.T, a.Hkv, a.B);
+    dim3 grid((a.T + 1) / 2, a.Hkv, a.B);
     KAS_DISPATCH_DG(pre_stats_kernel, grid, ctx.stream, a);
   }
   if ((e = ctx.end(K_PRE_STATS)) != hipSuccess) return e;
   const int64_t units = (int64_t)a.B * a.Hkv;
   const int64_t budget = pool_budget_floats();
-  for (int ta = 1; ta < a.T;) {
+  for (int ta = 0; ta < a.T;) {
     const int tb = next_chunk_end(ta, a.T, units, budget);
     a.t_begin = ta;
     a.t_end = tb;
-    dim3 grid(tb - ta, a.Hkv, a.B);
+    dim3 pgrid((tb + 1) / 2 - ta / 2, a.Hkv, a.B);
     ctx.begin(K_PRE_POOL);
-    KAS_DISPATCH_DG(pre_pool_kernel, grid, ctx.stream, a);
+    KAS_DISPATCH_DG(pre_pool_kernel, pgrid, ctx.stream, a);
     if ((e = ctx.end(K_PRE_POOL)) != hipSuccess) return e;
+    dim3 grid(tb - ta, a.Hkv, a.B);
     ctx.begin(K_PRE_SELECT);
     KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx.stream, a);
     if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;
