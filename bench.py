@@ -189,6 +189,11 @@ def main():
     ap.add_argument("--prefill-workload", default="llama8b_prefill_128k")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="profiling runs only: keep the first N layers of each schedule")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="profiling runs only: one device copy of this size before timing, as the "
+                         "reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -203,6 +208,18 @@ def main():
     torch.cuda.set_device(0)
     wd = inputgen.WORKLOADS[args.decode_workload]
     wp = inputgen.WORKLOADS[args.prefill_workload]
+    if args.layers:
+        import dataclasses
+        wd = dataclasses.replace(wd, n_layers=min(args.layers, wd.n_layers))
+        wp = dataclasses.replace(wp, n_layers=min(args.layers, wp.n_layers))
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 19
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del src, dst
     do_dec = args.phase in ("both", "decode")
     do_pre = args.phase in ("both", "prefill")
 
@@ -252,6 +269,8 @@ def main():
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": " + ".join(([wd.name] if do_dec else []) + ([wp.name] if do_pre else [])),
                       "phase": args.phase}}
+    if args.layers:
+        out["config"]["layers_kept"] = args.layers
     roof = []
     if do_dec:
         kd = dec_state[5]

@@ -134,7 +134,7 @@ __device__ __forceinline__ void row_stats_update(const f32x16& acc, bool diag, i
 // One workgroup = two consecutive tiles (t0 = 2p, t1 = 2p+1) of one KV head;
 // wave w = query head g*G + w; each staged K block feeds both tiles.
 template <int D, int G>
-__global__ __launch_bounds__(64 * G) void pre_stats_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16;
   using KS = KStage<D, NT>;
   __shared__ __align__(16) char s_k[2][32 * KS::KROW];
@@ -159,25 +159,38 @@ __global__ __launch_bounds__(64 * G) void pre_stats_kernel(PrefillArgs a) {
   const float cs = a.scale_log2;
   float m0 = kNegInf, l0 = 0.f, m1 = kNegInf, l1 = 0.f;
   KS st;
-  st.load(kbase, 0);
-  st.store(s_k[0]);
-  __syncthreads();
-  for (int kb = 0; kb <= tl; ++kb) {
+  // One staged key block: tile 0 and/or tile 1 (compile-time), each either
+  // a full block or its causal diagonal block.
+  auto step = [&](int kb, auto d0_tag, auto d1_tag, auto m0_tag, auto m1_tag) {
+    constexpr bool DO0 = decltype(d0_tag)::value, DO1 = decltype(d1_tag)::value;
+    constexpr bool DIAG0 = decltype(m0_tag)::value, DIAG1 = decltype(m1_tag)::value;
     const int buf = kb & 1;
     if (kb < tl) st.load(kbase, (int64_t)kTile * (kb + 1));
     const char* sk = s_k[buf];
     f32x16 acc0 = {}, acc1 = {};
-    const bool do0 = kb <= t0;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
-      if (do0) acc0 = mfma32(ka, qb0[c], acc0);   // S^T[key][query]
-      if (has1) acc1 = mfma32(ka, qb1[c], acc1);
+      if (DO0) acc0 = mfma32(ka, qb0[c], acc0);   // S^T[key][query]
+      if (DO1) acc1 = mfma32(ka, qb1[c], acc1);
     }
-    if (do0) row_stats_update(acc0, kb == t0, n32, hh, cs, m0, l0);
-    if (has1) row_stats_update(acc1, kb == t1, n32, hh, cs, m1, l1);
+    if (DO0) row_stats_update(acc0, DIAG0, n32, hh, cs, m0, l0);
+    if (DO1) row_stats_update(acc1, DIAG1, n32, hh, cs, m1, l1);
     if (kb < tl) st.store(s_k[buf ^ 1]);
     __syncthreads();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  st.load(kbase, 0);
+  st.store(s_k[0]);
+  __syncthreads();
+  if (has1) {
+    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, T_{}, F_{}, F_{});
+    step(t0, T_{}, T_{}, T_{}, F_{});
+    step(t1, F_{}, T_{}, F_{}, T_{});
+  } else {
+    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, F_{}, F_{}, F_{});
+    step(t0, T_{}, F_{}, T_{}, F_{});
   }
   auto finish = [&](float m, float l, int t) {
     const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(64 * G) void pre_stats_kernel(PrefillArgs a) {
 // probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
 // waves' sums are added through LDS (double-buffered, one barrier per block).
 template <int D, int G>
-__global__ __launch_bounds__(64 * G) void pre_pool_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16;
   using KS = KStage<D, NT>;
   __shared__ __align__(16) char s_k[2][32 * KS::KROW];
@@ -232,29 +245,26 @@ __global__ __launch_bounds__(64 * G) void pre_pool_kernel(PrefillArgs a) {
   float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
   KS st;
-  st.load(kbase, 0);
-  st.store(s_k[0]);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto step = [&](int kb, auto d0_tag, auto d1_tag) {
+    constexpr bool DO0 = decltype(d0_tag)::value, DO1 = decltype(d1_tag)::value;
     const int buf = kb & 1;
     if (kb + 1 < nkb) st.load(kbase, (int64_t)kTile * (kb + 1));
     const char* sk = s_k[buf];
-    const bool do0 = kb < t0;
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 kbv = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
-      if (do0) acc0 = mfma32(qa0[c], kbv, acc0);   // S[query][key]
-      if (has1) acc1 = mfma32(qa1[c], kbv, acc1);
+      if (DO0) acc0 = mfma32(qa0[c], kbv, acc0);   // S[query][key]
+      if (DO1) acc1 = mfma32(qa1[c], kbv, acc1);
     }
-    if (do0) {
+    if (DO0) {
       float col = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc0[r], cs, -lse0[r]));
       col += __shfl_xor(col, 32);
       if (hh == 0) s_col[buf][0][w][n32] = col;
     }
-    if (has1) {
+    if (DO1) {
       float col = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc1[r], cs, -lse1[r]));
@@ -264,18 +274,31 @@ __global__ __launch_bounds__(64 * G) void pre_pool_kernel(PrefillArgs a) {
     if (kb + 1 < nkb) st.store(s_k[buf ^ 1]);
     __syncthreads();
     // block kb's per-head column sums are complete: one wave per tile adds them
-    if (hh == 0 && w < 2) {
-      const int tile = (G == 1) ? -1 : w;
-      if (G == 1) {
-        if (do0) out0[kTile * kb + n32] = s_col[buf][0][0][n32];
-        if (has1) out1[kTile * kb + n32] = s_col[buf][1][0][n32];
-      } else if ((tile == 0 && do0) || (tile == 1 && has1)) {
+    if (hh == 0) {
+      if (DO0 && w == 0) {
         float sum = 0.f;
 #pragma unroll
-        for (int x = 0; x < G; ++x) sum += s_col[buf][tile][x][n32];
-        (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
+        for (int x = 0; x < G; ++x) sum += s_col[buf][0][x][n32];
+        out0[kTile * kb + n32] = sum;
+      }
+      if (DO1 && w == (G > 1 ? 1 : 0)) {
+        float sum = 0.f;
+#pragma unroll
+        for (int x = 0; x < G; ++x) sum += s_col[buf][1][x][n32];
+        out1[kTile * kb + n32] = sum;
       }
     }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  st.load(kbase, 0);
+  st.store(s_k[0]);
+  __syncthreads();
+  if (has1) {
+    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, T_{});
+    step(t0, F_{}, T_{});
+  } else {
+    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, F_{});
   }
 }
 
@@ -364,15 +387,25 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------------ sparse tile attention
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, source lane j supplies the address of 4 consecutive 16-bit values;
+// lane i receives value i%4 of source lanes i/4, i/4+4, i/4+8, i/4+12
+// (verified on the device with an index-grid probe).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
-  constexpr int KROW = 2 * D + 16;   // bytes per K row in LDS
-  constexpr int VROW = 2 * 32 + 8;   // bytes per V^T row (32 keys + pad)
-  constexpr int NK = (32 * PARTS + NT - 1) / NT;   // K 16-byte loads per thread per block
-  constexpr int NV = (16 * PARTS + NT - 1) / NT;   // V key-pair loads per thread per block
+  constexpr int KROW = 2 * D + 16;   // bytes per K row in LDS (b128 reads across rows)
+  constexpr int VROW = 2 * D + 32;   // bytes per V row in LDS (transposing b64 reads of 4 rows)
+  constexpr int NR = (32 * PARTS + NT - 1) / NT;   // 16-byte loads per thread per block, K and V each
   __shared__ __align__(16) char s_k[2][32 * KROW];
-  __shared__ __align__(16) char s_vt[2][D * VROW];
+  __shared__ __align__(16) char s_v[2][32 * VROW];
   __shared__ float s_x[G][32];
 
   const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
@@ -407,45 +440,34 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
     const int j = S[s];
     return ((unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
   };
-  u32x4 kreg[NK], v0r[NV], v1r[NV];
+  u32x4 kreg[NR], vreg[NR];
   auto load_block = [&](int blk) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int x = tid + i * NT;
-      if (x < 32 * PARTS) kreg[i] = ldg16(kbase + (int64_t)key_of(blk, x / PARTS) * D + (x % PARTS) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int x = tid + i * NT;
-      if (x < 16 * PARTS) {
-        const int kp = x / PARTS, part = x % PARTS;
-        v0r[i] = ldg16(vbase + (int64_t)key_of(blk, 2 * kp) * D + part * 8);
-        v1r[i] = ldg16(vbase + (int64_t)key_of(blk, 2 * kp + 1) * D + part * 8);
+      if (x < 32 * PARTS) {
+        const int64_t row = (int64_t)key_of(blk, x / PARTS) * D + (x % PARTS) * 8;
+        kreg[i] = ldg16(kbase + row);
+        vreg[i] = ldg16(vbase + row);
       }
     }
   };
   auto store_block = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int x = tid + i * NT;
-      if (x < 32 * PARTS)
+      if (x < 32 * PARTS) {
         *reinterpret_cast<u32x4*>(s_k[buf] + (x / PARTS) * KROW + (x % PARTS) * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int x = tid + i * NT;
-      if (x < 16 * PARTS) {
-        const int kp = x / PARTS, part = x % PARTS;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (v0r[i][e] & 0xffffu) | (v1r[i][e] << 16);          // dim 2e
-          const uint32_t hi = (v0r[i][e] >> 16) | (v1r[i][e] & 0xffff0000u);      // dim 2e+1
-          *reinterpret_cast<uint32_t*>(s_vt[buf] + (part * 8 + 2 * e) * VROW + 4 * kp) = lo;
-          *reinterpret_cast<uint32_t*>(s_vt[buf] + (part * 8 + 2 * e + 1) * VROW + 4 * kp) = hi;
-        }
+        *reinterpret_cast<u32x4*>(s_v[buf] + (x / PARTS) * VROW + (x % PARTS) * 16) = vreg[i];
       }
     }
   };
+  // P.V operand addressing: lane group g16 = lane/16 (its half hh = g16/2),
+  // member j = lane%16 supplies row 4*hh + j/4 (+8 for the upper four keys)
+  // and columns 16*(g16%2) + 4*(j%4) of each 32-wide column block.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int tr_row = 4 * hh + (j16 >> 2);
+  const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
 
   float m_run = kNegInf, l_run = 0.f;
   f32x16 o[NDC];
@@ -461,7 +483,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
     const int buf = blk & 1;
     if (MODE != 2) load_block(blk + 1);
     const char* sk = s_k[buf];
-    const char* svt = s_vt[buf];
+    const char* sv = s_v[buf];
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
@@ -530,9 +552,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) pa[e] = pack_bf16x2(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        const char* vr = svt + (n32 + 32 * dc) * VROW;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + (16 * c2 + 4 * hh) * 2);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (16 * c2 + 8 + 4 * hh) * 2);
+        // B[k-slot (hh, e)][d = n32 + 32 dc] = V[key 16 c2 + 8 (e/4) + 4 hh + e%4][d]
+        const char* vr = sv + (16 * c2 + tr_row) * VROW + (32 * dc + tr_col) * 2;
+        const u32x2 lo = lds_read_tr16(vr);
+        const u32x2 hi = lds_read_tr16(vr + 8 * VROW);
         const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
         o[dc] = mfma32(pa, vb, o[dc]);
       }
