@@ -444,6 +444,188 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
   }
 }
 
+// bf16 variant of dec_attn with P.V on MFMA. One workgroup = one split of
+// one (b, g); wave w takes 32-row blocks w, w+4, ...; per block: Q.K^T on two
+// 16x16x32 MFMA tiles (or the anchor's stored logits), online softmax with a
+// running max per head shared by the 16 lanes of each lane row, P (bf16) and
+// the gathered V rows staged in the wave's own LDS slice, and O += P.V on
+// 16x16x32 MFMA with V read through the transposing LDS load. Next block's K
+// and V rows are loaded into registers while the current one is processed
+// (ping-pong, no register copies).
+typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dec_i16x4 dec_lds_i16x4;
+__device__ __forceinline__ u32x2 dec_lds_read_tr16(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_i16x4*)(p)));
+}
+
+template <int D, int G, bool FROM_LOGITS>
+__global__ __launch_bounds__(256, 2) void dec_attn_bf16_kernel(DecodeArgs a) {
+  using QK = QKMfma<__bf16, D>;
+  constexpr int NT = D / 16;            // output tiles of 16 dims
+  constexpr int VROW = 2 * D + 32;      // bytes per staged V row (transposing reads of 4 rows)
+  constexpr int VP = D / 8;             // 16-byte parts per V row
+  constexpr int NVL = 16 * VP / 64;     // V 16-byte loads per lane per 16-row block
+  __shared__ int32_t s_idx[kMaxSplitRows];
+  __shared__ __align__(16) char s_v[4][16 * VROW];
+  __shared__ __align__(16) uint16_t s_p[4][16 * 16];   // [head][key] bf16; heads >= G stay 0
+  __shared__ float s_o[4][G * D];
+  __shared__ float s_m[4][G], s_l[4][G];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int64_t row0 = (int64_t)split * a.split_rows;
+  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  // Index values and the head map are trusted inputs; clamping keeps every
+  // access inside the cache even if they are not.
+  int ga = a.head_map ? a.head_map[g] : g;
+  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+  const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
+  for (int i = tid; i < nrows; i += 256) {
+    const int32_t j = idx[i];
+    s_idx[i] = ((uint32_t)j < (uint32_t)a.N) ? j : 0;
+  }
+  for (int i = tid; i < 4 * 16 * 16 / 2; i += 256) reinterpret_cast<uint32_t*>(&s_p[0][0])[i] = 0u;
+  __syncthreads();
+
+  const int64_t unit = (int64_t)b * a.Hkv + g;
+  const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const __bf16* vb = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
+  typename QK::QFrag qf;
+  if (!FROM_LOGITS)
+    QK::load_q(qf, (const __bf16*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
+
+  f32x4 o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ml[4], ls[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { ml[r] = kNegInf; ls[r] = 0.f; }
+
+  struct Blk {
+    QK kq;
+    f32x4 lgt;
+    u32x4 v[NVL];
+  };
+  auto load_blk = [&](int blk, Blk& B_) {
+    const int jr = blk * 16 + c16;
+    const int jk = s_idx[jr < nrows ? jr : 0];
+    if (FROM_LOGITS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) B_.lgt[r] = (4 * q4 + r < G) ? lg[(int64_t)jk * G + 4 * q4 + r] : 0.f;
+    } else {
+      B_.kq.load_k(kb + (int64_t)jk * D, q4);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int x = lane + 64 * i;
+      const int jr2 = blk * 16 + x / VP;
+      const int jv = s_idx[jr2 < nrows ? jr2 : 0];
+      B_.v[i] = ldg16(vb + (int64_t)jv * D + (x % VP) * 8);
+    }
+  };
+
+  char* sv = s_v[wave];
+  uint16_t* sp = s_p[wave];
+  // transposing-read source address of this lane: key row 4*(lane/16) + (lane%16)/4,
+  // dims 4*(lane%4) of each 16-dim output tile
+  const char* tr_base = sv + (4 * q4 + (c16 >> 2)) * VROW + 4 * (lane & 3) * 2;
+
+  auto process = [&](int blk, const Blk& B_) {
+    const f32x4 s = FROM_LOGITS ? B_.lgt : B_.kq.run(qf) * a.scale_log2;
+    const bool kval = blk * 16 + c16 < nrows;
+    float al[4];
+    bool grew = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float t = kval ? s[r] : kNegInf;
+      const float bm = row16_max(t);
+      const float mn = fmaxf(ml[r], bm);
+      al[r] = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
+      grew |= al[r] != 1.f;
+      const float p = exp2_fast(t - mn);   // -inf -> 0
+      ls[r] = ls[r] * al[r] + p;
+      ml[r] = mn;
+      if (4 * q4 + r < G) sp[(4 * q4 + r) * 16 + c16] = f32_to_bf16_rne(p);
+    }
+    // the head of (lane row, reg r) is the same in the S and O tiles
+    if (__any(grew)) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[n][r] *= al[r];
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int x = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(sv + (x / VP) * VROW + (x % VP) * 16) = B_.v[i];
+    }
+    wave_lds_fence();
+    // A = P[head c16][keys 4 q4 .. 4 q4 + 3]; B = V[keys 4 q4 ..][dims 16 n + c16]
+    const u32x2 pa = *reinterpret_cast<const u32x2*>(sp + c16 * 16 + 4 * q4);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x2 vbf = dec_lds_read_tr16(tr_base + 32 * n);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(dec_i16x4, pa),
+                                                       __builtin_bit_cast(dec_i16x4, vbf), o[n], 0, 0, 0);
+    }
+    wave_lds_fence();
+  };
+
+  const int nblk = (nrows + 15) >> 4;
+  Blk bA, bB;
+  int blk = wave;
+  if (blk < nblk) load_blk(blk, bA);
+  while (blk < nblk) {
+    if (blk + 4 < nblk) load_blk(blk + 4, bB);
+    process(blk, bA);
+    blk += 4;
+    if (blk >= nblk) break;
+    if (blk + 4 < nblk) load_blk(blk + 4, bA);
+    process(blk, bB);
+    blk += 4;
+  }
+
+  // O rows: head 4*(lane/16) + r, dims 16 n + lane%16
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lsum = row16_sum(ls[h & 3]);
+    const float M = readlane_f(ml[h & 3], 16 * (h >> 2));
+    const float L = readlane_f(lsum, 16 * (h >> 2));
+    if (lane == 0) { s_m[wave][h] = M; s_l[wave][h] = L; }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * q4 + r;
+    if (h < G) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s_o[wave][h * D + 16 * n + c16] = o[n][r];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += 256) {
+    const int h = x / D, d = x % D;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += (s_m[w][h] == kNegInf) ? 0.f : s_o[w][x] * exp2_fast(s_m[w][h] - M);
+    a.part_o[(((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * D + d] = acc;
+  }
+  if (tid < G) {
+    const int h = tid;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      L += (s_m[w][h] == kNegInf) ? 0.f : s_l[w][h] * exp2_fast(s_m[w][h] - M);
+    float* ml_out = a.part_ml + (((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * 2;
+    ml_out[0] = M;
+    ml_out[1] = L;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, float x);
 template <>
@@ -567,13 +749,29 @@ static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   return a.D == 128 ? attn_launch<T, 128, FL>(a, grid, st) : attn_launch<T, 64, FL>(a, grid, st);
 }
 
+template <int D, bool FL>
+static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_attn_bf16_kernel<D, 1, FL>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_attn_bf16_kernel<D, 2, FL>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_attn_bf16_kernel<D, 4, FL>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_attn_bf16_kernel<D, 8, FL>), grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+template <bool FL>
+static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  return a.D == 128 ? attn_bf16_launch<128, FL>(a, grid, st) : attn_bf16_launch<64, FL>(a, grid, st);
+}
+
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx) {
   dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
   const int kid = from_logits ? K_DEC_ATTN_ANCHOR : K_DEC_ATTN;
   ctx.begin(kid);
-  if (dtype == 1) e = from_logits ? attn_by_d<__bf16, true>(a, grid, ctx.stream)
-                                  : attn_by_d<__bf16, false>(a, grid, ctx.stream);
+  if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx.stream)
+                                  : attn_bf16_by_d<false>(a, grid, ctx.stream);
   else e = from_logits ? attn_by_d<float, true>(a, grid, ctx.stream)
                        : attn_by_d<float, false>(a, grid, ctx.stream);
   if (e != hipSuccess) return e;
