@@ -14,6 +14,8 @@
 //               softmax, split-K partial (o, m, l) per workgroup.
 //  dec_combine  merge of the split-K partials into the output.
 #include "kas_device.hpp"
+#include <stdlib.h>
+
 #include "kas_block.hpp"
 #include "kas_internal.hpp"
 
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
   for (int h = 0; h < G; ++h) { M[h] = s_M[h]; iL[h] = s_iL[h]; }
 
   const float* lg = a.logits + unit * a.N * G;
-  float* P = a.pooled + unit * a.N;
+  float* P = a.pooled + unit * a.pstride;
   const int64_t base = (int64_t)chunk * kSelChunk;
 #pragma unroll 4
   for (int i = 0; i < kSelChunk / 256; ++i) {
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256) void sel_digit_kernel(DecodeArgs a) {
   constexpr int NB = PASS == 2 ? kBins2 : kBins3;
   for (int i = tid; i < NB; i += 256) s_h[i] = 0u;
   __syncthreads();
-  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
   const int64_t base = (int64_t)chunk * kSelChunk;
   const uint32_t pre = PASS == 2 ? (uint32_t)b1 : (((uint32_t)b1 << 11) | (uint32_t)b2);
 #pragma unroll 4
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void sel_count_kernel(DecodeArgs a) {
   block_find_bin(gh + kBins1 + kBins2, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
   const uint32_t tau = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10) | (uint32_t)b3;
   const uint32_t r = k - ab1 - ab2 - ab3;
-  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
   const int64_t base = (int64_t)chunk * kSelChunk;
   uint32_t gt = 0, eq = 0;
 #pragma unroll 4
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   uint32_t gt_before = 0, eq_before = 0;
   const uint32_t* c = a.counts + unit * a.n_sel_chunks * 2;
   for (int x = 0; x < chunk; ++x) { gt_before += c[2 * x]; eq_before += c[2 * x + 1]; }
-  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.N);
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
   // thread owns 16 consecutive keys
   constexpr int PER = kSelChunk / 256;
   const int64_t j0 = (int64_t)chunk * kSelChunk + tid * PER;
@@ -273,6 +275,101 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
       if (e_ex < r && g_ex + e_ex < (uint32_t)a.kk) out[g_ex + e_ex] = (int32_t)(j0 + i);
       ++e_ex;
     }
+  }
+}
+
+// One workgroup of 1024 threads per (b, g): digits 2 and 3 of the radix
+// select (histograms in LDS, the pooled row re-read from L2/HBM), then the
+// stable compaction in index order. Replaces four multi-workgroup launches.
+constexpr int kSelThreads = 1024;
+__global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
+  __shared__ uint32_t s_h[kBins2];
+  __shared__ uint32_t s_tmp[kSelThreads / 64];
+  __shared__ int s_res[2];
+  const int64_t unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t k = (uint32_t)a.kk;
+  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
+  const int64_t N = a.N;
+  int b1, b2, b3;
+  uint32_t ab1, ab2, ab3;
+  block_find_bin_nt<kSelThreads>(a.hist + unit * kHistWords, kBins1, k, s_tmp, s_res, b1, ab1);
+  for (int i = tid; i < kBins2; i += kSelThreads) s_h[i] = 0u;
+  __syncthreads();
+  // Passes read 16 consecutive scores per thread (four 16-byte loads in
+  // flight per thread) so one workgroup keeps enough bytes in flight.
+  auto sweep = [&](auto&& fn) {
+    for (int64_t base = 0; base < N; base += (int64_t)kSelThreads * 16) {
+      const int64_t j0 = base + (int64_t)tid * 16;
+      if (j0 + 16 <= N) {
+        u32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ldg16(P + j0 + 4 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fn(v[q][e]);
+      } else {
+        for (int64_t j = j0; j < N; ++j) fn(P[j]);
+      }
+    }
+  };
+  sweep([&](uint32_t u) {
+    if ((u >> 21) == (uint32_t)b1) atomicAdd(&s_h[(u >> 10) & 0x7ffu], 1u);
+  });
+  __syncthreads();
+  block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+  for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
+  __syncthreads();
+  const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+  sweep([&](uint32_t u) {
+    if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
+  });
+  __syncthreads();
+  block_find_bin_nt<kSelThreads>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  const uint32_t tau = (pre << 10) | (uint32_t)b3;
+  const uint32_t r = k - ab1 - ab2 - ab3;
+  int32_t* out = a.idx_out + unit * a.kk;
+  constexpr int PER = 16;
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int64_t base = 0; base < N; base += (int64_t)kSelThreads * PER) {
+    const int64_t j0 = base + (int64_t)tid * PER;
+    uint32_t u[PER];
+    uint32_t gt = 0, eq = 0;
+    if (j0 + PER <= N) {
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const u32x4 v = ldg16(P + j0 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) u[i] = (j0 + i < N) ? P[j0 + i] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool in = j0 + i < N;
+      gt += in && u[i] > tau;
+      eq += in && u[i] == tau;
+    }
+    uint32_t tg, te;
+    uint32_t g_ex = block_excl_scan<kSelThreads>(gt, s_tmp, &tg) + gt_run;
+    uint32_t e_ex = block_excl_scan<kSelThreads>(eq, s_tmp, &te) + eq_run;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (j0 + i >= N) break;
+      if (u[i] > tau) {
+        const uint32_t pos = g_ex + min(e_ex, r);
+        if (pos < k) out[pos] = (int32_t)(j0 + i);
+        ++g_ex;
+      } else if (u[i] == tau) {
+        if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = (int32_t)(j0 + i);
+        ++e_ex;
+      }
+    }
+    gt_run += tg;
+    eq_run += te;
   }
 }
 
@@ -458,8 +555,11 @@ __device__ __forceinline__ u32x2 dec_lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_i16x4*)(p)));
 }
 
+#ifndef KAS_DEC_PINGPONG
+#define KAS_DEC_PINGPONG 0
+#endif
 template <int D, int G, bool FROM_LOGITS>
-__global__ __launch_bounds__(256, 2) void dec_attn_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
   using QK = QKMfma<__bf16, D>;
   constexpr int NT = D / 16;            // output tiles of 16 dims
   constexpr int VROW = 2 * D + 32;      // bytes per staged V row (transposing reads of 4 rows)
@@ -574,6 +674,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_bf16_kernel(DecodeArgs a) {
   };
 
   const int nblk = (nrows + 15) >> 4;
+#if KAS_DEC_PINGPONG
   Blk bA, bB;
   int blk = wave;
   if (blk < nblk) load_blk(blk, bA);
@@ -586,6 +687,14 @@ __global__ __launch_bounds__(256, 2) void dec_attn_bf16_kernel(DecodeArgs a) {
     process(blk, bB);
     blk += 4;
   }
+#else
+  // no register prefetch: latency is hidden by the other resident waves
+  for (int blk = wave; blk < nblk; blk += 4) {
+    Blk bc;
+    load_blk(blk, bc);
+    process(blk, bc);
+  }
+#endif
 
   // O rows: head 4*(lane/16) + r, dims 16 n + lane%16
 #pragma unroll
@@ -716,6 +825,11 @@ hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
 }
 
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
+  if (getenv("KAS_DECODE_SELECT_MULTI") == nullptr) {
+    ctx.begin(K_SEL_FUSED);
+    KAS_LAUNCH(sel_fused_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx.stream, a);
+    return ctx.end(K_SEL_FUSED);
+  }
   dim3 grid(a.n_sel_chunks, a.B * a.Hkv);
   hipError_t e;
   ctx.begin(K_SEL_DIGIT2);

@@ -13,6 +13,7 @@ enum KernelId {
   K_SEL_DIGIT3,
   K_SEL_COUNT,
   K_SEL_COMPACT,
+  K_SEL_FUSED,
   K_DEC_ATTN,
   K_DEC_ATTN_ANCHOR,
   K_DEC_COMBINE,
@@ -56,7 +57,8 @@ struct DecodeArgs {
   float* logits;                    // [B, Hkv, N, G] base-2 logits
   float* stats;                     // [B, Hkv, n_score_chunks, G, 2]
   int n_score_chunks, score_rows;
-  float* pooled;                    // [B, Hkv, N]
+  float* pooled;                    // [B, Hkv, pstride]
+  int64_t pstride;                  // N rounded up to 4 (16-byte aligned rows)
   uint32_t* hist;                   // [B, Hkv, kHistWords]
   uint32_t* counts;                 // [B, Hkv, n_sel_chunks, 2]
   uint32_t* selstate;               // [B, Hkv, 4]

@@ -36,7 +36,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_digit2", "select_digit3", "select_count",
-    "select_compact", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
+    "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
     "prefill_select", "prefill_attn"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
@@ -214,7 +214,7 @@ static DecodePlan plan_decode(const Shape& s, bool anchor) {
   if (anchor) {
     p.off_logits = take(units * s.N * s.G * sizeof(float));
     p.off_stats = take(units * p.n_score_chunks * s.G * 2 * sizeof(float));
-    p.off_pooled = take(units * s.N * sizeof(float));
+    p.off_pooled = take(units * ((s.N + 3) / 4 * 4) * sizeof(float));
     p.off_hist = take(units * kHistWords * sizeof(uint32_t));
     p.off_counts = take(units * p.n_sel_chunks * 2 * sizeof(uint32_t));
     p.off_selstate = take(units * 4 * sizeof(uint32_t));
@@ -231,6 +231,7 @@ static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, c
   a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.G = s.G; a.N = s.N;
   a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
   a.kk = p.kk;
+  a.pstride = (s.N + 3) / 4 * 4;
   a.score_rows = p.score_rows; a.n_score_chunks = p.n_score_chunks; a.n_sel_chunks = p.n_sel_chunks;
   a.split_rows = p.split_rows; a.nsplit = p.nsplit;
   if (anchor) {

@@ -159,38 +159,67 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   const float cs = a.scale_log2;
   float m0 = kNegInf, l0 = 0.f, m1 = kNegInf, l1 = 0.f;
   KS st;
-  // One staged key block: tile 0 and/or tile 1 (compile-time), each either
-  // a full block or its causal diagonal block.
-  auto step = [&](int kb, auto d0_tag, auto d1_tag, auto m0_tag, auto m1_tag) {
-    constexpr bool DO0 = decltype(d0_tag)::value, DO1 = decltype(d1_tag)::value;
-    constexpr bool DIAG0 = decltype(m0_tag)::value, DIAG1 = decltype(m1_tag)::value;
-    const int buf = kb & 1;
-    if (kb < tl) st.load(kbase, (int64_t)kTile * (kb + 1));
-    const char* sk = s_k[buf];
-    f32x16 acc0 = {}, acc1 = {};
+  // Software pipeline over staged key blocks: the MFMA chain of one tile is
+  // issued next to the softmax VALU work of the other tile's previous chain,
+  // so the MFMA and VALU pipes run side by side inside one wave.
+  auto chain = [&](const u32x4* ka, const u32x4* qb) {
+    f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
-      if (DO0) acc0 = mfma32(ka, qb0[c], acc0);   // S^T[key][query]
-      if (DO1) acc1 = mfma32(ka, qb1[c], acc1);
-    }
-    if (DO0) row_stats_update(acc0, DIAG0, n32, hh, cs, m0, l0);
-    if (DO1) row_stats_update(acc1, DIAG1, n32, hh, cs, m1, l1);
-    if (kb < tl) st.store(s_k[buf ^ 1]);
+    for (int c = 0; c < KC; ++c) acc = mfma32(ka[c], qb[c], acc);   // S^T[key][query]
+    return acc;
+  };
+  auto read_k = [&](int kb, u32x4* ka) {
+    const char* sk = s_k[kb & 1];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+  };
+  // Stage K(kb+1) (already in registers) and start loading K(kb+2).
+  auto advance = [&](int kb) {
+    if (kb + 1 <= tl) st.store(s_k[(kb + 1) & 1]);
+    if (kb + 2 <= tl) st.load(kbase, (int64_t)kTile * (kb + 2));
     __syncthreads();
   };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
   st.load(kbase, 0);
   st.store(s_k[0]);
+  if (tl >= 1) st.load(kbase, kTile);
   __syncthreads();
+  u32x4 ka[KC];
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (has1) {
-    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, T_{}, F_{}, F_{});
-    step(t0, T_{}, T_{}, T_{}, F_{});
-    step(t1, F_{}, T_{}, F_{}, T_{});
+    f32x16 acc1 = {};
+    // FIRST: no previous tile-1 chain; DIAG0: block t0 is tile 0's diagonal
+    auto iter = [&](int kb, auto first_tag, auto diag0_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value, DIAG0 = decltype(diag0_tag)::value;
+      read_k(kb, ka);
+      const f32x16 acc0 = chain(ka, qb0);
+      if (!FIRST) row_stats_update(acc1, false, n32, hh, cs, m1, l1);
+      acc1 = chain(ka, qb1);
+      row_stats_update(acc0, DIAG0, n32, hh, cs, m0, l0);
+      advance(kb);
+    };
+    if (t0 == 0) {
+      iter(0, T_{}, T_{});
+    } else {
+      iter(0, T_{}, F_{});
+      for (int kb = 1; kb < t0; ++kb) iter(kb, F_{}, F_{});
+      iter(t0, F_{}, T_{});
+    }
+    read_k(t1, ka);
+    const f32x16 acc1n = chain(ka, qb1);
+    row_stats_update(acc1, false, n32, hh, cs, m1, l1);
+    row_stats_update(acc1n, true, n32, hh, cs, m1, l1);
   } else {
-    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, F_{}, F_{}, F_{});
-    step(t0, T_{}, F_{}, T_{}, F_{});
+    for (int kb = 0; kb < t0; ++kb) {
+      read_k(kb, ka);
+      const f32x16 acc0 = chain(ka, qb0);
+      row_stats_update(acc0, false, n32, hh, cs, m0, l0);
+      advance(kb);
+    }
+    read_k(t0, ka);
+    const f32x16 acc0 = chain(ka, qb0);
+    row_stats_update(acc0, true, n32, hh, cs, m0, l0);
   }
   auto finish = [&](float m, float l, int t) {
     const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
@@ -213,7 +242,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16;
   using KS = KStage<D, NT>;
   __shared__ __align__(16) char s_k[2][32 * KS::KROW];
-  __shared__ float s_col[2][2][G][32];
+  __shared__ float s_col[2][2][G][64];
   const int pa0 = a.t_begin / 2;
   const int npairs = (a.t_end + 1) / 2 - pa0;
   const int p = pa0 + npairs - 1 - xcd_local_order(blockIdx.x, npairs);
@@ -245,60 +274,80 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
   KS st;
-  auto step = [&](int kb, auto d0_tag, auto d1_tag) {
-    constexpr bool DO0 = decltype(d0_tag)::value, DO1 = decltype(d1_tag)::value;
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) st.load(kbase, (int64_t)kTile * (kb + 1));
-    const char* sk = s_k[buf];
-    f32x16 acc0 = {}, acc1 = {};
+  auto chain = [&](const u32x4* ka, const u32x4* qa) {
+    f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 kbv = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
-      if (DO0) acc0 = mfma32(qa0[c], kbv, acc0);   // S[query][key]
-      if (DO1) acc1 = mfma32(qa1[c], kbv, acc1);
-    }
-    if (DO0) {
-      float col = 0.f;
+    for (int c = 0; c < KC; ++c) acc = mfma32(qa[c], ka[c], acc);   // S[query][key]
+    return acc;
+  };
+  auto read_k = [&](int kb, u32x4* ka) {
+    const char* sk = s_k[kb & 1];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc0[r], cs, -lse0[r]));
-      col += __shfl_xor(col, 32);
-      if (hh == 0) s_col[buf][0][w][n32] = col;
-    }
-    if (DO1) {
-      float col = 0.f;
+    for (int c = 0; c < KC; ++c)
+      ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+  };
+  // Column sums of one tile-block over the wave's 32 query rows; both lane
+  // halves store their (equal) copy, so no lane branch splits the block.
+  auto colsum = [&](const f32x16& acc, const float* lse, float* dst) {
+    float col = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc1[r], cs, -lse1[r]));
-      col += __shfl_xor(col, 32);
-      if (hh == 0) s_col[buf][1][w][n32] = col;
-    }
-    if (kb + 1 < nkb) st.store(s_k[buf ^ 1]);
+    for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc[r], cs, -lse[r]));
+    col += __shfl_xor(col, 32);
+    dst[lane] = col;
+  };
+  auto advance = [&](int kb) {
+    if (kb + 1 < nkb) st.store(s_k[(kb + 1) & 1]);
+    if (kb + 2 < nkb) st.load(kbase, (int64_t)kTile * (kb + 2));
     __syncthreads();
-    // block kb's per-head column sums are complete: one wave per tile adds them
-    if (hh == 0) {
-      if (DO0 && w == 0) {
-        float sum = 0.f;
+  };
+  // Sum the G heads' column sums of (tile, block) and write them out.
+  auto emit = [&](int tile, int kb, int writer_wave) {
+    if (w == writer_wave && hh == 0) {
+      float sum = 0.f;
 #pragma unroll
-        for (int x = 0; x < G; ++x) sum += s_col[buf][0][x][n32];
-        out0[kTile * kb + n32] = sum;
-      }
-      if (DO1 && w == (G > 1 ? 1 : 0)) {
-        float sum = 0.f;
-#pragma unroll
-        for (int x = 0; x < G; ++x) sum += s_col[buf][1][x][n32];
-        out1[kTile * kb + n32] = sum;
-      }
+      for (int x = 0; x < G; ++x) sum += s_col[kb & 1][tile][x][n32];
+      (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
     }
   };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
+  const int w1 = G > 1 ? 1 : 0;
   st.load(kbase, 0);
   st.store(s_k[0]);
+  if (nkb > 1) st.load(kbase, kTile);
   __syncthreads();
+  u32x4 ka[KC];
   if (has1) {
-    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, T_{});
-    step(t0, F_{}, T_{});
+    f32x16 acc1 = {};
+    auto iter = [&](int kb, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      read_k(kb, ka);
+      const f32x16 acc0 = chain(ka, qa0);
+      if (!FIRST) colsum(acc1, lse1, s_col[(kb - 1) & 1][1][w]);
+      acc1 = chain(ka, qa1);
+      colsum(acc0, lse0, s_col[kb & 1][0][w]);
+      advance(kb);
+      emit(0, kb, 0);
+      if (!FIRST) emit(1, kb - 1, w1);
+    };
+    if (t0 > 0) {
+      iter(0, std::true_type{});
+      for (int kb = 1; kb < t0; ++kb) iter(kb, std::false_type{});
+    }
+    // block t0 is a candidate of tile 1 only
+    read_k(t0, ka);
+    const f32x16 acc1n = chain(ka, qa1);
+    if (t0 > 0) colsum(acc1, lse1, s_col[(t0 - 1) & 1][1][w]);
+    colsum(acc1n, lse1, s_col[t0 & 1][1][w]);
+    __syncthreads();
+    if (t0 > 0) emit(1, t0 - 1, w1);
+    emit(1, t0, w1);
   } else {
-    for (int kb = 0; kb < t0; ++kb) step(kb, T_{}, F_{});
+    for (int kb = 0; kb < t0; ++kb) {
+      read_k(kb, ka);
+      const f32x16 acc0 = chain(ka, qa0);
+      colsum(acc0, lse0, s_col[kb & 1][0][w]);
+      advance(kb);
+      emit(0, kb, 0);
+    }
   }
 }
 
@@ -406,6 +455,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   constexpr int NR = (32 * PARTS + NT - 1) / NT;   // 16-byte loads per thread per block, K and V each
   __shared__ __align__(16) char s_k[2][32 * KROW];
   __shared__ __align__(16) char s_v[2][32 * VROW];
+  __shared__ __align__(16) char s_q[G][32 * KROW];
   __shared__ float s_x[G][32];
 
   const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
@@ -422,11 +472,15 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   const int tile_key0 = kTile * t;
 
   const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
-  u32x4 qb[KC];
+  // the wave's 32 query rows stay in LDS (read as the B operand every block)
   {
-    const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
+    const __bf16* qrows = (const __bf16*)a.q + qoff * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) qb[c] = ldg16(qrow + 16 * c + 8 * hh);
+    for (int i = 0; i < 32 * PARTS / 64; ++i) {
+      const int x = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(s_q[w] + (x / PARTS) * KROW + (x % PARTS) * 16) =
+          ldg16(qrows + (x / PARTS) * D + (x % PARTS) * 8);
+    }
   }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
@@ -440,25 +494,31 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
     const int j = S[s];
     return ((unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
   };
-  u32x4 kreg[NR], vreg[NR];
-  auto load_block = [&](int blk) {
+  // Gathered rows travel global -> registers -> LDS. A ring of register sets
+  // keeps the rows of the next RING blocks in flight while one block is
+  // processed (gather latency exceeds one block time).
+  constexpr int RING = 2;
+  u32x4 kreg[RING][NR], vreg[RING][NR];
+  auto load_block = [&](int blk, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int x = tid + i * NT;
       if (x < 32 * PARTS) {
         const int64_t row = (int64_t)key_of(blk, x / PARTS) * D + (x % PARTS) * 8;
-        kreg[i] = ldg16(kbase + row);
-        vreg[i] = ldg16(vbase + row);
+        kreg[SL][i] = ldg16(kbase + row);
+        vreg[SL][i] = ldg16(vbase + row);
       }
     }
   };
-  auto store_block = [&](int buf) {
+  auto store_block = [&](int buf, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int x = tid + i * NT;
       if (x < 32 * PARTS) {
-        *reinterpret_cast<u32x4*>(s_k[buf] + (x / PARTS) * KROW + (x % PARTS) * 16) = kreg[i];
-        *reinterpret_cast<u32x4*>(s_v[buf] + (x / PARTS) * VROW + (x % PARTS) * 16) = vreg[i];
+        *reinterpret_cast<u32x4*>(s_k[buf] + (x / PARTS) * KROW + (x % PARTS) * 16) = kreg[SL][i];
+        *reinterpret_cast<u32x4*>(s_v[buf] + (x / PARTS) * VROW + (x % PARTS) * 16) = vreg[SL][i];
       }
     }
   };
@@ -478,17 +538,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   // selected keys; 1: the last, partial selected block; 2: the causal
   // diagonal block. The next block's rows are loaded into registers before
   // the math and written to the other LDS buffer after it.
-  auto step = [&](int blk, auto mode_tag) {
+  // SLOT = blk % RING: the register set that is free during this block.
+  auto step = [&](int blk, auto mode_tag, auto slot_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int NEXT = (SLOT + 1) % RING;
     const int buf = blk & 1;
-    if (MODE != 2) load_block(blk + 1);
+    if (blk + RING <= nsel) load_block(blk + RING, slot_tag);
     const char* sk = s_k[buf];
     const char* sv = s_v[buf];
+    const char* sq = s_q[w];
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KROW + (16 * c + 8 * hh) * 2);
-      acc = mfma32(ka, qb[c], acc);             // S^T[key slot][query]
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(sq + n32 * KROW + (16 * c + 8 * hh) * 2);
+      acc = mfma32(ka, qv, acc);                // S^T[key slot][query]
     }
     float x[16];
     if (MODE == 0) {
@@ -560,17 +625,29 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
         o[dc] = mfma32(pa, vb, o[dc]);
       }
     }
-    if (MODE != 2) store_block(buf ^ 1);
+    if (MODE != 2) store_block(buf ^ 1, std::integral_constant<int, NEXT>{});
     __syncthreads();
   };
-
-  load_block(0);
-  store_block(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // blocks 0 .. nsel (the last one is the diagonal block)
+  load_block(0, S0{});
+  if (1 <= nsel) load_block(1, S1{});
+  store_block(0, S0{});
   __syncthreads();
   const int nfull = kt / 32;
-  for (int blk = 0; blk < nfull; ++blk) step(blk, std::integral_constant<int, 0>{});
-  if (nsel > nfull) step(nfull, std::integral_constant<int, 1>{});
-  step(nsel, std::integral_constant<int, 2>{});
+  auto step_any = [&](int blk, auto mode_tag) {
+    if (blk % RING == 0) step(blk, mode_tag, S0{});
+    else step(blk, mode_tag, S1{});
+  };
+  int blk = 0;
+  for (; blk + RING <= nfull; blk += RING) {
+    step(blk, std::integral_constant<int, 0>{}, S0{});
+    step(blk + 1, std::integral_constant<int, 0>{}, S1{});
+  }
+  for (; blk < nfull; ++blk) step_any(blk, std::integral_constant<int, 0>{});
+  if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
+  step_any(nsel, std::integral_constant<int, 2>{});
   // normalise: row sums live with the query's lanes, output rows with registers
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (hh == 0) s_x[w][n32] = 1.0f / l_tot;
