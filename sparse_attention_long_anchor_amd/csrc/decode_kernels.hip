@@ -735,6 +735,205 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
   }
 }
 
+// Pipelined bf16 gather attention. Same block math as dec_attn_bf16_kernel
+// (16-row blocks, Q.K^T on 16x16x32 MFMA, per-head online softmax, P.V on
+// 16x16x16 MFMA with V through the transposing LDS load), but each wave keeps
+// the K and V rows of its next two blocks in flight in two register sets, and
+// each lane loads the index of its own row straight from global memory one
+// block before the rows it names (V row indices are then shuffled from the
+// lane that owns the row). Vector memory counters retire in issue order, so
+// the index of block i + 2 is issued before the rows of block i + 1; no
+// load sits behind a divergent branch in the steady-state loop.
+template <int D, int G, bool FROM_LOGITS>
+__global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
+  using QK = QKMfma<__bf16, D>;
+  constexpr int NT = D / 16;            // output tiles of 16 dims
+  constexpr int VROW = 2 * D + 32;      // bytes per staged V row
+  constexpr int VP = D / 8;             // 16-byte parts per V row
+  constexpr int NVL = 16 * VP / 64;     // V 16-byte loads per lane per block
+  __shared__ __align__(16) char s_v[4][16 * VROW];
+  __shared__ __align__(16) uint16_t s_p[4][16 * 16];   // [head][key] bf16; heads >= G stay 0
+  __shared__ float s_o[4][G * D];
+  __shared__ float s_m[4][G], s_l[4][G];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int64_t row0 = (int64_t)split * a.split_rows;
+  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  const int nblk = (nrows + 15) >> 4;
+  const int nb = wave < nblk ? (nblk - wave + 3) >> 2 : 0;   // blocks wave, wave + 4, ...
+  int ga = a.head_map ? a.head_map[g] : g;
+  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+  const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
+
+  const int64_t unit = (int64_t)b * a.Hkv + g;
+  const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const __bf16* vb = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
+  typename QK::QFrag qf;
+  if (!FROM_LOGITS)
+    QK::load_q(qf, (const __bf16*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
+  char* sv = s_v[wave];
+  uint16_t* sp = s_p[wave];
+  reinterpret_cast<uint32_t*>(sp)[lane] = 0u;
+  reinterpret_cast<uint32_t*>(sp)[lane + 64] = 0u;
+
+  f32x4 o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ml[4], ls[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { ml[r] = kNegInf; ls[r] = 0.f; }
+
+  // raw index of this lane's row (c16) in the wave's i-th block; rows past
+  // the split re-read its last index and are masked in the softmax
+  auto load_idx = [&](int i) -> int {
+    const int blk = min(wave + 4 * i, nblk - 1);
+    return idx[min(blk * 16 + c16, nrows - 1)];
+  };
+  struct Blk {
+    QK kq;
+    f32x4 lgt;
+    u32x4 v[NVL];
+  };
+  // Index values are trusted inputs; clamping keeps every access inside the cache.
+  auto load_blk = [&](int jraw, Blk& B_) {
+    const int jk = ((unsigned)jraw < (unsigned)a.N) ? jraw : 0;
+    if (FROM_LOGITS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) B_.lgt[r] = (4 * q4 + r < G) ? lg[(int64_t)jk * G + 4 * q4 + r] : 0.f;
+    } else {
+      B_.kq.load_k(kb + (int64_t)jk * D, q4);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int x = lane + 64 * i;
+      const int jv = __shfl(jk, x / VP);   // lane x / VP (< 16) owns row x / VP
+      B_.v[i] = ldg16(vb + (int64_t)jv * D + (x % VP) * 8);
+    }
+  };
+  // transposing-read source address of this lane: key row 4*(lane/16) + (lane%16)/4,
+  // dims 4*(lane%4) of each 16-dim output tile
+  const char* tr_base = sv + (4 * q4 + (c16 >> 2)) * VROW + 4 * (lane & 3) * 2;
+
+  auto process = [&](int i, const Blk& B_) {
+    const int blk = wave + 4 * i;
+    const f32x4 s = FROM_LOGITS ? B_.lgt : B_.kq.run(qf) * a.scale_log2;
+    const bool kval = blk * 16 + c16 < nrows;
+    float al[4];
+    bool grew = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float t = kval ? s[r] : kNegInf;
+      const float bm = row16_max(t);
+      const float mn = fmaxf(ml[r], bm);
+      al[r] = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
+      grew |= al[r] != 1.f;
+      const float p = exp2_fast(t - mn);   // -inf -> 0
+      ls[r] = ls[r] * al[r] + p;
+      ml[r] = mn;
+      if (4 * q4 + r < G) sp[(4 * q4 + r) * 16 + c16] = f32_to_bf16_rne(p);
+    }
+    if (__any(grew)) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[n][r] *= al[r];
+    }
+#pragma unroll
+    for (int v = 0; v < NVL; ++v) {
+      const int x = lane + 64 * v;
+      *reinterpret_cast<u32x4*>(sv + (x / VP) * VROW + (x % VP) * 16) = B_.v[v];
+    }
+    wave_lds_fence();
+    const u32x2 pa = *reinterpret_cast<const u32x2*>(sp + c16 * 16 + 4 * q4);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x2 vbf = dec_lds_read_tr16(tr_base + 32 * n);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(dec_i16x4, pa),
+                                                       __builtin_bit_cast(dec_i16x4, vbf), o[n], 0, 0, 0);
+    }
+    wave_lds_fence();
+  };
+
+  Blk bA, bB;
+  int i = 0;
+  if (nb >= 4) {
+    // the issue order here matches the loop below, so the loop entry adds no wait
+    const int j0 = load_idx(0);
+    const int j1 = load_idx(1);
+    load_blk(j0, bA);
+    int j2 = load_idx(2);
+    load_blk(j1, bB);
+    int j3 = load_idx(3);
+    // scheduling barriers keep each reload after the math that frees its
+    // registers (hoisting it would need a third register set)
+    for (; i + 3 < nb; i += 2) {
+      process(i, bA);
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk(j2, bA);
+      j2 = load_idx(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      process(i + 1, bB);
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk(j3, bB);
+      j3 = load_idx(i + 5);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // blocks i .. nb - 1 (at most three): i in bA, i + 1 in bB, indices of i + 2 in j2
+    if (i < nb) process(i, bA);
+    if (i + 2 < nb) load_blk(j2, bA);
+    if (i + 1 < nb) process(i + 1, bB);
+    if (i + 2 < nb) process(i + 2, bA);
+  } else if (nb > 0) {
+    load_blk(load_idx(0), bA);
+    if (nb > 1) load_blk(load_idx(1), bB);
+    process(0, bA);
+    if (nb > 2) load_blk(load_idx(2), bA);
+    if (nb > 1) process(1, bB);
+    if (nb > 2) process(2, bA);
+  }
+
+  // O rows: head 4*(lane/16) + r, dims 16 n + lane%16
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lsum = row16_sum(ls[h & 3]);
+    const float M = readlane_f(ml[h & 3], 16 * (h >> 2));
+    const float L = readlane_f(lsum, 16 * (h >> 2));
+    if (lane == 0) { s_m[wave][h] = M; s_l[wave][h] = L; }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * q4 + r;
+    if (h < G) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) s_o[wave][h * D + 16 * n + c16] = o[n][r];
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += 256) {
+    const int h = x / D, d = x % D;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += (s_m[w][h] == kNegInf) ? 0.f : s_o[w][x] * exp2_fast(s_m[w][h] - M);
+    a.part_o[(((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * D + d] = acc;
+  }
+  if (tid < G) {
+    const int h = tid;
+    float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      L += (s_m[w][h] == kNegInf) ? 0.f : s_l[w][h] * exp2_fast(s_m[w][h] - M);
+    float* ml_out = a.part_ml + (((int64_t)b * a.Hq + g * G + h) * a.nsplit + split) * 2;
+    ml_out[0] = M;
+    ml_out[1] = L;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out(T* p, float x);
 template <>
@@ -784,11 +983,10 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ launchers
 
-#define KAS_LAUNCH(kernel, grid, block, stream, arg) \
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, arg)
+#define KAS_LAUNCH(kernel, grid, block, ctx, arg) (ctx).launch(kernel, grid, block, arg)
 
 template <typename T, int D>
-static hipError_t score_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t score_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
     case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1>), grid, dim3(256), st, a); break;
     case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2>), grid, dim3(256), st, a); break;
@@ -803,10 +1001,10 @@ hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   dim3 grid(a.n_score_chunks, a.Hkv, a.B);
   ctx.begin(K_DEC_SCORE);
   hipError_t e;
-  if (dtype == 1) e = (a.D == 128) ? score_launch<__bf16, 128>(a, grid, ctx.stream)
-                                   : score_launch<__bf16, 64>(a, grid, ctx.stream);
-  else e = (a.D == 128) ? score_launch<float, 128>(a, grid, ctx.stream)
-                        : score_launch<float, 64>(a, grid, ctx.stream);
+  if (dtype == 1) e = (a.D == 128) ? score_launch<__bf16, 128>(a, grid, ctx)
+                                   : score_launch<__bf16, 64>(a, grid, ctx);
+  else e = (a.D == 128) ? score_launch<float, 128>(a, grid, ctx)
+                        : score_launch<float, 64>(a, grid, ctx);
   if (e != hipSuccess) return e;
   return ctx.end(K_DEC_SCORE);
 }
@@ -815,10 +1013,10 @@ hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
   dim3 grid(a.n_sel_chunks, a.Hkv, a.B);
   ctx.begin(K_DEC_POOL);
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_pool_kernel<1>), grid, dim3(256), ctx.stream, a); break;
-    case 2: KAS_LAUNCH((dec_pool_kernel<2>), grid, dim3(256), ctx.stream, a); break;
-    case 4: KAS_LAUNCH((dec_pool_kernel<4>), grid, dim3(256), ctx.stream, a); break;
-    case 8: KAS_LAUNCH((dec_pool_kernel<8>), grid, dim3(256), ctx.stream, a); break;
+    case 1: KAS_LAUNCH((dec_pool_kernel<1>), grid, dim3(256), ctx, a); break;
+    case 2: KAS_LAUNCH((dec_pool_kernel<2>), grid, dim3(256), ctx, a); break;
+    case 4: KAS_LAUNCH((dec_pool_kernel<4>), grid, dim3(256), ctx, a); break;
+    case 8: KAS_LAUNCH((dec_pool_kernel<8>), grid, dim3(256), ctx, a); break;
     default: return hipErrorInvalidValue;
   }
   return ctx.end(K_DEC_POOL);
@@ -827,27 +1025,27 @@ hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
   if (getenv("KAS_DECODE_SELECT_MULTI") == nullptr) {
     ctx.begin(K_SEL_FUSED);
-    KAS_LAUNCH(sel_fused_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx.stream, a);
+    KAS_LAUNCH(sel_fused_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx, a);
     return ctx.end(K_SEL_FUSED);
   }
   dim3 grid(a.n_sel_chunks, a.B * a.Hkv);
   hipError_t e;
   ctx.begin(K_SEL_DIGIT2);
-  KAS_LAUNCH((sel_digit_kernel<2>), grid, dim3(256), ctx.stream, a);
+  KAS_LAUNCH((sel_digit_kernel<2>), grid, dim3(256), ctx, a);
   if ((e = ctx.end(K_SEL_DIGIT2)) != hipSuccess) return e;
   ctx.begin(K_SEL_DIGIT3);
-  KAS_LAUNCH((sel_digit_kernel<3>), grid, dim3(256), ctx.stream, a);
+  KAS_LAUNCH((sel_digit_kernel<3>), grid, dim3(256), ctx, a);
   if ((e = ctx.end(K_SEL_DIGIT3)) != hipSuccess) return e;
   ctx.begin(K_SEL_COUNT);
-  KAS_LAUNCH(sel_count_kernel, grid, dim3(256), ctx.stream, a);
+  KAS_LAUNCH(sel_count_kernel, grid, dim3(256), ctx, a);
   if ((e = ctx.end(K_SEL_COUNT)) != hipSuccess) return e;
   ctx.begin(K_SEL_COMPACT);
-  KAS_LAUNCH(sel_compact_kernel, grid, dim3(256), ctx.stream, a);
+  KAS_LAUNCH(sel_compact_kernel, grid, dim3(256), ctx, a);
   return ctx.end(K_SEL_COMPACT);
 }
 
 template <typename T, int D, bool FL>
-static hipError_t attn_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t attn_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
     case 1: KAS_LAUNCH((dec_attn_kernel<T, D, 1, FL>), grid, dim3(256), st, a); break;
     case 2: KAS_LAUNCH((dec_attn_kernel<T, D, 2, FL>), grid, dim3(256), st, a); break;
@@ -859,12 +1057,12 @@ static hipError_t attn_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <typename T, bool FL>
-static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   return a.D == 128 ? attn_launch<T, 128, FL>(a, grid, st) : attn_launch<T, 64, FL>(a, grid, st);
 }
 
 template <int D, bool FL>
-static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
     case 1: KAS_LAUNCH((dec_attn_bf16_kernel<D, 1, FL>), grid, dim3(256), st, a); break;
     case 2: KAS_LAUNCH((dec_attn_bf16_kernel<D, 2, FL>), grid, dim3(256), st, a); break;
@@ -874,8 +1072,21 @@ static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, hipStream_t s
   }
   return hipSuccess;
 }
+template <int D, bool FL>
+static hipError_t gather_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL>), grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
 template <bool FL>
-static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+  if (getenv("KAS_DECODE_GATHER_V1") == nullptr)
+    return a.D == 128 ? gather_launch<128, FL>(a, grid, st) : gather_launch<64, FL>(a, grid, st);
   return a.D == 128 ? attn_bf16_launch<128, FL>(a, grid, st) : attn_bf16_launch<64, FL>(a, grid, st);
 }
 
@@ -884,16 +1095,16 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, 
   hipError_t e;
   const int kid = from_logits ? K_DEC_ATTN_ANCHOR : K_DEC_ATTN;
   ctx.begin(kid);
-  if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx.stream)
-                                  : attn_bf16_by_d<false>(a, grid, ctx.stream);
-  else e = from_logits ? attn_by_d<float, true>(a, grid, ctx.stream)
-                       : attn_by_d<float, false>(a, grid, ctx.stream);
+  if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx)
+                                  : attn_bf16_by_d<false>(a, grid, ctx);
+  else e = from_logits ? attn_by_d<float, true>(a, grid, ctx)
+                       : attn_by_d<float, false>(a, grid, ctx);
   if (e != hipSuccess) return e;
   if ((e = ctx.end(kid)) != hipSuccess) return e;
   ctx.begin(K_DEC_COMBINE);
   dim3 cgrid(a.Hq, a.B);
-  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx.stream, a);
-  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx.stream, a);
+  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx, a);
+  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx, a);
   return ctx.end(K_DEC_COMBINE);
 }
 

@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer and the kernel files.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace kas {
@@ -25,11 +26,21 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
-// Wraps every launch: optional event timing + launch error check.
+// Wraps every launch: optional timing + launch error check. begin() takes a
+// pair of events when profiling is on; launch() then passes them to the
+// dispatch itself (hipExtLaunchKernel stamps the kernel's own start and end,
+// adding no packets to the stream); end() files the pair for readout.
+// Each begin/end bracket holds exactly one launch.
 struct LaunchCtx {
   hipStream_t stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
   void begin(int kid);
   hipError_t end(int kid);
+  template <typename F, typename A>
+  void launch(F kernel, dim3 grid, dim3 block, const A& arg) {
+    if (e0) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0u, arg);
+    else hipLaunchKernelGGL(kernel, grid, block, 0, stream, arg);
+  }
 };
 
 // Radix-select digit layout over the fp32 bit pattern of a non-negative score:

@@ -48,8 +48,6 @@ static std::vector<Record> g_pending;
 static std::vector<hipEvent_t> g_free_events;
 static double g_total_ms[K_COUNT_];
 static int64_t g_launches[K_COUNT_];
-static thread_local hipEvent_t t_open_event = nullptr;
-
 static hipEvent_t take_event() {
   if (!g_free_events.empty()) {
     hipEvent_t e = g_free_events.back();
@@ -63,20 +61,30 @@ static hipEvent_t take_event() {
 
 void LaunchCtx::begin(int kid) {
   (void)kid;
-  t_open_event = nullptr;
+  e0 = e1 = nullptr;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
-  hipEvent_t e = take_event();
-  if (e && hipEventRecord(e, stream) == hipSuccess) t_open_event = e;
+  hipEvent_t a = take_event();
+  hipEvent_t b = a ? take_event() : nullptr;
+  if (a && b) {
+    e0 = a;
+    e1 = b;
+  } else if (a) {
+    g_free_events.push_back(a);
+  }
 }
 
 hipError_t LaunchCtx::end(int kid) {
   hipError_t err = hipGetLastError();
-  if (t_open_event) {
+  if (e0) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    hipEvent_t e1 = take_event();
-    if (e1 && hipEventRecord(e1, stream) == hipSuccess) g_pending.push_back({kid, t_open_event, e1});
-    t_open_event = nullptr;
+    if (err == hipSuccess) {
+      g_pending.push_back({kid, e0, e1});
+    } else {
+      g_free_events.push_back(e0);
+      g_free_events.push_back(e1);
+    }
+    e0 = e1 = nullptr;
   }
   return err;
 }

@@ -486,26 +486,39 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
 
-  // key of row r of block blk; padding rows read row 0 and are masked later
-  auto key_of = [&](int blk, int r) -> int {
-    if (blk == nsel) return tile_key0 + r;
-    const int s = blk * 32 + r;
-    if (s >= kt) return 0;
-    const int j = S[s];
-    return ((unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
-  };
   // Gathered rows travel global -> registers -> LDS. A ring of register sets
   // keeps the rows of the next RING blocks in flight while one block is
-  // processed (gather latency exceeds one block time).
+  // processed (gather latency exceeds one block time). The indices of block
+  // blk + RING + 1 are issued before the rows of block blk + RING: vector
+  // memory counters retire in issue order, so an index load issued after the
+  // prefetched rows would make its consumer wait for those rows as well.
+  // Index loads are unconditional (clamped address) so that no divergent
+  // branch sits between a load and its consumer.
   constexpr int RING = 2;
+  constexpr bool kAllRows = (32 * PARTS) % NT == 0;   // every thread owns NR row chunks
   u32x4 kreg[RING][NR], vreg[RING][NR];
+  int jreg[RING][NR] = {};
+  auto load_index = [&](int blk, auto slot_tag) {
+    constexpr int SL = decltype(slot_tag)::value;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int x = tid + i * NT;
+      if (kAllRows || x < 32 * PARTS) jreg[SL][i] = S[min(blk * 32 + x / PARTS, kt - 1)];
+    }
+  };
+  // Key of each row chunk of block blk; padding rows read row 0 and are
+  // masked in the softmax; the last block is the causal diagonal.
   auto load_block = [&](int blk, auto slot_tag) {
     constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int x = tid + i * NT;
-      if (x < 32 * PARTS) {
-        const int64_t row = (int64_t)key_of(blk, x / PARTS) * D + (x % PARTS) * 8;
+      if (kAllRows || x < 32 * PARTS) {
+        const int r = x / PARTS;
+        const int j = jreg[SL][i];
+        const int sel = (blk * 32 + r < kt && (unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
+        const int key = (blk == nsel) ? tile_key0 + r : sel;
+        const int64_t row = (int64_t)key * D + (x % PARTS) * 8;
         kreg[SL][i] = ldg16(kbase + row);
         vreg[SL][i] = ldg16(vbase + row);
       }
@@ -539,12 +552,16 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   // diagonal block. The next block's rows are loaded into registers before
   // the math and written to the other LDS buffer after it.
   // SLOT = blk % RING: the register set that is free during this block.
-  auto step = [&](int blk, auto mode_tag, auto slot_tag) {
+  // STEADY: both prefetches are known to be due (no branch around them, so
+  // the rows of block blk + RING stay in flight across the next step).
+  auto step = [&](int blk, auto mode_tag, auto slot_tag, auto steady_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;
     constexpr int NEXT = (SLOT + 1) % RING;
     const int buf = blk & 1;
-    if (blk + RING <= nsel) load_block(blk + RING, slot_tag);
+    if (STEADY || blk + RING + 1 < nsel) load_index(blk + RING + 1, std::integral_constant<int, NEXT>{});
+    if (STEADY || blk + RING <= nsel) load_block(blk + RING, slot_tag);
     const char* sk = s_k[buf];
     const char* sv = s_v[buf];
     const char* sq = s_q[w];
@@ -631,19 +648,37 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   // blocks 0 .. nsel (the last one is the diagonal block)
-  load_block(0, S0{});
-  if (1 <= nsel) load_block(1, S1{});
-  store_block(0, S0{});
-  __syncthreads();
   const int nfull = kt / 32;
+  using Tail = std::false_type;
   auto step_any = [&](int blk, auto mode_tag) {
-    if (blk % RING == 0) step(blk, mode_tag, S0{});
-    else step(blk, mode_tag, S1{});
+    if (blk % RING == 0) step(blk, mode_tag, S0{}, Tail{});
+    else step(blk, mode_tag, S1{}, Tail{});
   };
   int blk = 0;
-  for (; blk + RING <= nfull; blk += RING) {
-    step(blk, std::integral_constant<int, 0>{}, S0{});
-    step(blk + 1, std::integral_constant<int, 0>{}, S1{});
+  if (nsel > 4) {
+    // same issue order as the steady state below (indices of block 2 before
+    // the rows of block 1), so that the loop entry needs no extra wait
+    load_index(0, S0{});
+    load_block(0, S0{});
+    load_index(1, S1{});
+    load_index(2, S0{});
+    load_block(1, S1{});
+    store_block(0, S0{});
+    __syncthreads();
+    // steady state: blocks blk, blk + 1 are full and the indices of blk + 4
+    // exist (blk + 4 < nsel also gives blk + 1 < nfull)
+    for (; blk + 4 < nsel; blk += RING) {
+      step(blk, std::integral_constant<int, 0>{}, S0{}, std::true_type{});
+      step(blk + 1, std::integral_constant<int, 0>{}, S1{}, std::true_type{});
+    }
+  } else {
+    if (0 < nsel) load_index(0, S0{});
+    load_block(0, S0{});
+    if (1 < nsel) load_index(1, S1{});
+    if (1 <= nsel) load_block(1, S1{});
+    if (2 < nsel) load_index(2, S0{});
+    store_block(0, S0{});
+    __syncthreads();
   }
   for (; blk < nfull; ++blk) step_any(blk, std::integral_constant<int, 0>{});
   if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
@@ -739,8 +774,7 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   }
 }
 
-#define KAS_LAUNCH_P(kernel, grid, block, stream, arg) \
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, arg)
+#define KAS_LAUNCH_P(kernel, grid, block, ctx, arg) (ctx).launch(kernel, grid, block, arg)
 
 #define KAS_DISPATCH_DG(KERNEL, grid, st, a)                                              \
   do {                                                                                    \
@@ -764,14 +798,14 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   } while (0)
 
 static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
-  KAS_LAUNCH_P(pre_offsets_kernel, dim3(1), dim3(256), ctx.stream, a);
+  KAS_LAUNCH_P(pre_offsets_kernel, dim3(1), dim3(256), ctx, a);
   return hipGetLastError();
 }
 
 static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) {
   ctx.begin(K_PRE_ATTN);
   dim3 grid(a.T, a.Hkv, a.B);
-  KAS_DISPATCH_DG(pre_attn_kernel, grid, ctx.stream, a);
+  KAS_DISPATCH_DG(pre_attn_kernel, grid, ctx, a);
   return ctx.end(K_PRE_ATTN);
 }
 
@@ -781,7 +815,7 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   ctx.begin(K_PRE_STATS);
   {
     dim3 grid((a.T + 1) / 2, a.Hkv, a.B);
-    KAS_DISPATCH_DG(pre_stats_kernel, grid, ctx.stream, a);
+    KAS_DISPATCH_DG(pre_stats_kernel, grid, ctx, a);
   }
   if ((e = ctx.end(K_PRE_STATS)) != hipSuccess) return e;
   const int64_t units = (int64_t)a.B * a.Hkv;
@@ -792,11 +826,11 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
     a.t_end = tb;
     dim3 pgrid((tb + 1) / 2 - ta / 2, a.Hkv, a.B);
     ctx.begin(K_PRE_POOL);
-    KAS_DISPATCH_DG(pre_pool_kernel, pgrid, ctx.stream, a);
+    KAS_DISPATCH_DG(pre_pool_kernel, pgrid, ctx, a);
     if ((e = ctx.end(K_PRE_POOL)) != hipSuccess) return e;
     dim3 grid(tb - ta, a.Hkv, a.B);
     ctx.begin(K_PRE_SELECT);
-    KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx.stream, a);
+    KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx, a);
     if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;
     ta = tb;
   }
