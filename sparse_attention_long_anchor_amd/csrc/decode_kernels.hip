@@ -16,6 +16,8 @@
 #include "kas_device.hpp"
 #include <stdlib.h>
 
+#include <string.h>
+
 #include "kas_block.hpp"
 #include "kas_internal.hpp"
 
@@ -1085,7 +1087,9 @@ static hipError_t gather_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
 }
 template <bool FL>
 static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
-  if (getenv("KAS_DECODE_GATHER_V1") == nullptr)
+  // KAS_DECODE_GATHER=staged selects the LDS-staged-index kernel
+  const char* sel = getenv("KAS_DECODE_GATHER");
+  if (sel == nullptr || strcmp(sel, "staged") != 0)
     return a.D == 128 ? gather_launch<128, FL>(a, grid, st) : gather_launch<64, FL>(a, grid, st);
   return a.D == 128 ? attn_bf16_launch<128, FL>(a, grid, st) : attn_bf16_launch<64, FL>(a, grid, st);
 }

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -181,15 +182,30 @@ static int env_int(const char* name, int dflt) {
   return x > 0 ? x : dflt;
 }
 
-// Rows of the index set per decode attention workgroup: enough workgroups to
-// cover the machine a few times over, at most kMaxSplitRows (LDS staging).
+// Compute units of the current device (cached per device; 256 on MI355X).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Rows of the index set per decode attention workgroup. The gather is bound
+// by bytes in flight, and a workgroup keeps its waves' next blocks in flight,
+// so one wave of workgroups covering every compute unit once is enough:
+// splits per (b, g) = CUs / (B * Hkv), at most kMaxSplitRows rows each.
 static int decode_split_rows(int64_t units, int64_t kk) {
   int r = env_int("KAS_DECODE_SPLIT_ROWS", 0);
   if (r <= 0) {
-    const int64_t target_wgs = 2048;
-    int64_t per = (units * kk + target_wgs - 1) / target_wgs;
+    const int64_t splits = std::max<int64_t>(1, device_cus() / std::max<int64_t>(1, units));
+    int64_t per = (kk + splits - 1) / splits;
     per = (per + 63) / 64 * 64;
-    r = (int)(per < 64 ? 64 : per);
+    r = (int)(per < 64 ? 64 : std::min<int64_t>(per, 1 << 20));
   }
   r = (r + 15) / 16 * 16;
   if (r > 2048) r = 2048;

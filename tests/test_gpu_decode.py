@@ -156,3 +156,52 @@ def test_deterministic_and_strided_cache():
     assert torch.equal(o4, o5)
     # identity reuse over the anchor's own set reproduces the anchor output
     assert max_abs(_np(o4), _np(o1)) <= TOL["bf16"]
+
+
+def test_workspace_contents_do_not_matter():
+    """A workspace full of stale bytes, reused across calls and shapes, gives
+    the same bits as a fresh one."""
+    kas = _kas()
+    B, Hq, Hkv, D, N, pct = 2, 32, 8, 128, 20000, 10
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=31)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx, _ = kas.decode_anchor(q, k, v, pct)
+    d = kas.make_desc(B, Hq, Hkv, D, N, pct, torch.bfloat16)
+    need = kas.workspace_size(d, kas.OP_DECODE_REUSE)
+    hm = torch.arange(Hkv, dtype=torch.int32, device=DEV)
+    ref = kas.decode_reuse(q, k, v, idx, hm, pct, ws=torch.zeros(need, dtype=torch.uint8, device=DEV))
+    ref1 = kas.decode_reuse(q[:1], k[:1], v[:1], idx[:1], hm, pct,
+                            ws=torch.zeros(need, dtype=torch.uint8, device=DEV))
+    for fill in (0xFF, 0x00, 0x5A):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        o1 = kas.decode_reuse(q, k, v, idx, hm, pct, ws=ws)
+        o2 = kas.decode_reuse(q, k, v, idx, hm, pct, ws=ws)
+        # a smaller problem through the same workspace, then the first again
+        o3 = kas.decode_reuse(q[:1], k[:1], v[:1], idx[:1], hm, pct, ws=ws)
+        o4 = kas.decode_reuse(q, k, v, idx, hm, pct, ws=ws)
+        torch.cuda.synchronize()
+        _say(f"    workspace fill 0x{fill:02x}: bitwise equal to a fresh workspace")
+        assert torch.equal(o1, ref) and torch.equal(o2, ref) and torch.equal(o4, ref)
+        assert torch.equal(o3, ref1)
+    err = max_abs(_np(ref), oracle.decode_reuse(_np(q), _np(k), _np(v), idx.cpu().numpy(),
+                                                np.arange(Hkv, dtype=np.int32)))
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("env", [{"KAS_DECODE_SPLIT_ROWS": "16"}, {"KAS_DECODE_SPLIT_ROWS": "16384"},
+                                 {"KAS_DECODE_GATHER": "staged"},
+                                 {"KAS_DECODE_GATHER": "staged", "KAS_DECODE_SPLIT_ROWS": "16"}],
+                         ids=["split16", "split_max", "staged", "staged_split16"])
+def test_split_and_kernel_variants(env, monkeypatch):
+    """Many splits (a merge over hundreds of partials), the largest split, and
+    the LDS-staged gather kernel all match the oracle."""
+    kas = _kas()
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    B, Hq, Hkv, D, N, pct = 1, 32, 8, 128, 30000, 10
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=41)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    label = ",".join(f"{a}={b}" for a, b in env.items())
+    idx, _ = _check_anchor(w, q, k, v, pct, label)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    _check_reuse(w, q2, k2, v2, idx, np.arange(Hkv, dtype=np.int32)[::-1].copy(), pct, label)
