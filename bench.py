@@ -303,11 +303,11 @@ def main():
         out["decode"] = {
             "workload": wd.name, "batch": wd.batch, "seq_len": wd.seq_len, "layers": wd.n_layers,
             "anchors": list(wd.anchors), "topk_pct": wd.topk_pct, "k": kd,
-            "us_per_layer": {"anchor": round(1e3 * sum(anc) / len(anc), 3),
-                             "reuse": round(1e3 * sum(reu) / len(reu), 3),
+            "us_per_layer": {"anchor": round(1e3 * _mean(anc), 3),
+                             "reuse": round(1e3 * _mean(reu), 3),
                              "mean": round(1e3 * step_ms / wd.n_layers, 3)},
-            "GB_per_s": {"anchor": round(anchor_b / (sum(anc) / len(anc) * 1e-3) / 1e9, 2),
-                         "reuse": round(reuse_b / (sum(reu) / len(reu) * 1e-3) / 1e9, 2),
+            "GB_per_s": {"anchor": _rate(anchor_b, _mean(anc) * 1e-3, 1e9),
+                         "reuse": _rate(reuse_b, _mean(reu) * 1e-3, 1e9),
                          "step": round(gbs, 2)},
             "ms_per_step": round(step_ms, 4),
             "tokens_per_s": round(wd.batch / (step_ms * 1e-3), 2),
@@ -329,9 +329,9 @@ def main():
         out["prefill"] = {
             "workload": wp.name, "batch": wp.batch, "seq_len": wp.seq_len, "layers": wp.n_layers,
             "anchors": list(wp.anchors), "topk_pct": wp.topk_pct, "index_entries_per_kv_head": int(off[-1]),
-            "ms_per_layer": {"anchor": round(sum(anc) / len(anc), 4), "reuse": round(sum(reu) / len(reu), 4)},
-            "TFLOP_per_s": {"anchor_layer": round(anc_flops / (sum(anc) / len(anc) * 1e-3) / 1e12, 3),
-                            "reuse_layer": round(work["prefill_attn"] / (sum(reu) / len(reu) * 1e-3) / 1e12, 3)},
+            "ms_per_layer": {"anchor": round(_mean(anc), 4), "reuse": round(_mean(reu), 4)},
+            "TFLOP_per_s": {"anchor_layer": _rate(anc_flops, _mean(anc) * 1e-3, 1e12),
+                            "reuse_layer": _rate(work["prefill_attn"], _mean(reu) * 1e-3, 1e12)},
             "ms_per_step": round(step_ms, 3),
             "tokens_per_s": round(wp.batch * wp.seq_len / (step_ms * 1e-3), 1),
         }
@@ -361,6 +361,14 @@ def main():
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
     print(json.dumps(out), flush=True)
+
+
+def _mean(xs):
+    return sum(xs) / len(xs) if xs else float("nan")
+
+
+def _rate(work, seconds, scale):
+    return round(work / seconds / scale, 3) if seconds == seconds and seconds > 0 else None
 
 
 def _roof_entry(name, bound, total_work, ms_n, peak, unit, scale):

@@ -157,11 +157,16 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
-  float m0 = kNegInf, l0 = 0.f, m1 = kNegInf, l1 = 0.f;
   KS st;
-  // Software pipeline over staged key blocks: the MFMA chain of one tile is
-  // issued next to the softmax VALU work of the other tile's previous chain,
-  // so the MFMA and VALU pipes run side by side inside one wave.
+  // Row sums against a lazy reference: each lane keeps a base-2 offset mr
+  // (the maximum of its first block) and adds exp2(x - mr) of every later
+  // score; the terms stay below 2^64 unless a score exceeds mr by 64, and
+  // only such a block (rare) is redone against its own maximum. Besides the
+  // MFMA, a score costs one FMA, one exponential and one add, and the update
+  // has no branch, so it can share a basic block with the other tile's MFMA
+  // chain.
+  constexpr float kBig = 0x1p64f;
+  float mr0 = 0.f, l0 = 0.f, mr1 = 0.f, l1 = 0.f;
   auto chain = [&](const u32x4* ka, const u32x4* qb) {
     f32x16 acc = {};
 #pragma unroll
@@ -173,6 +178,51 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+  };
+  // masked score (diagonal block: keys after the query row are excluded)
+  auto val = [&](const f32x16& acc, int r, bool diag) -> float {
+    return (diag && mrow(r, hh) > n32) ? kNegInf : acc[r];
+  };
+  auto block_max = [&](const f32x16& acc, bool diag) -> float {
+    float bm = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, val(acc, r, diag));
+    return bm == kNegInf ? 0.f : bm * cs;      // all masked: any finite reference
+  };
+  auto terms = [&](const f32x16& acc, bool diag, float mr) -> float {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(val(acc, r, diag), cs, -mr));
+    return s;
+  };
+  // An MFMA chain with the exponential terms of an earlier, independent block
+  // woven in: 16 / KC terms after each MFMA, pinned by scheduling barriers so
+  // the VALU work fills the matrix unit's dependent-chain latency.
+  auto chain_terms = [&](const u32x4* ka, const u32x4* qb, const f32x16& prev, bool pdiag, float mr,
+                         float& s) {
+    constexpr int TPM = 16 / KC;
+    f32x16 acc = {};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      // terms first: the first group covers the LDS latency of ka[0]
+#pragma unroll
+      for (int e = 0; e < TPM; ++e) s += exp2_fast(fmaf(val(prev, TPM * c + e, pdiag), cs, -mr));
+      acc = mfma32(ka[c], qb[c], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  auto settle = [&](const f32x16& acc, bool diag, float s, float& mr, float& l) {
+    const bool over = !(s <= kBig);
+    if (__builtin_expect(__any(over), 0)) {
+      if (over) {
+        const float mn = fmaxf(mr, block_max(acc, diag));
+        l = l * exp2_fast(mr - mn) + terms(acc, diag, mn);
+        mr = mn;
+        return;
+      }
+    }
+    l += s;
   };
   // Stage K(kb+1) (already in registers) and start loading K(kb+2).
   auto advance = [&](int kb) {
@@ -189,14 +239,24 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   using F_ = std::false_type;
   if (has1) {
     f32x16 acc1 = {};
-    // FIRST: no previous tile-1 chain; DIAG0: block t0 is tile 0's diagonal
+    // One key block for both tiles. Tile 1's update of the previous block
+    // runs beside tile 0's MFMA chain, tile 0's update beside tile 1's chain.
+    // FIRST: block 0 (references set, no previous tile-1 block); DIAG0: block
+    // t0 is tile 0's diagonal.
     auto iter = [&](int kb, auto first_tag, auto diag0_tag) {
       constexpr bool FIRST = decltype(first_tag)::value, DIAG0 = decltype(diag0_tag)::value;
       read_k(kb, ka);
-      const f32x16 acc0 = chain(ka, qb0);
-      if (!FIRST) row_stats_update(acc1, false, n32, hh, cs, m1, l1);
-      acc1 = chain(ka, qb1);
-      row_stats_update(acc0, DIAG0, n32, hh, cs, m0, l0);
+      float s1 = 0.f, s0 = 0.f;
+      const f32x16 acc0 = FIRST ? chain(ka, qb0) : chain_terms(ka, qb0, acc1, false, mr1, s1);
+      if (FIRST) mr0 = block_max(acc0, DIAG0);
+      const f32x16 acc1n = chain_terms(ka, qb1, acc0, DIAG0, mr0, s0);
+      // keep the sums where they are computed (not sunk into the branches below)
+      asm volatile("" : "+v"(s0), "+v"(s1));
+      if (!FIRST) settle(acc1, false, s1, mr1, l1);
+      if (FIRST) l0 = s0;
+      else settle(acc0, DIAG0, s0, mr0, l0);
+      acc1 = acc1n;
+      if (FIRST) mr1 = block_max(acc1, false);
       advance(kb);
     };
     if (t0 == 0) {
@@ -208,27 +268,34 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     }
     read_k(t1, ka);
     const f32x16 acc1n = chain(ka, qb1);
-    row_stats_update(acc1, false, n32, hh, cs, m1, l1);
-    row_stats_update(acc1n, true, n32, hh, cs, m1, l1);
+    const float s1 = terms(acc1, false, mr1);
+    settle(acc1, false, s1, mr1, l1);
+    const float s1n = terms(acc1n, true, mr1);
+    settle(acc1n, true, s1n, mr1, l1);
   } else {
-    for (int kb = 0; kb < t0; ++kb) {
+    for (int kb = 0; kb <= t0; ++kb) {
       read_k(kb, ka);
       const f32x16 acc0 = chain(ka, qb0);
-      row_stats_update(acc0, false, n32, hh, cs, m0, l0);
-      advance(kb);
+      const bool diag = kb == t0;
+      if (kb == 0) {
+        mr0 = block_max(acc0, diag);
+        l0 = terms(acc0, diag, mr0);
+      } else {
+        settle(acc0, diag, terms(acc0, diag, mr0), mr0, l0);
+      }
+      if (kb < t0) advance(kb);
     }
-    read_k(t0, ka);
-    const f32x16 acc0 = chain(ka, qb0);
-    row_stats_update(acc0, true, n32, hh, cs, m0, l0);
   }
+  // merge the two lane halves (different keys of the same query row);
+  // a half whose keys were all masked has l = 0
   auto finish = [&](float m, float l, int t) {
     const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
-    const float M = fmaxf(m, m2);
-    const float L = (m == kNegInf ? 0.f : l * exp2_fast(m - M)) + (m2 == kNegInf ? 0.f : l2 * exp2_fast(m2 - M));
+    const float M = fmaxf(l > 0.f ? m : kNegInf, l2 > 0.f ? m2 : kNegInf);
+    const float L = (l > 0.f ? l * exp2_fast(m - M) : 0.f) + (l2 > 0.f ? l2 * exp2_fast(m2 - M) : 0.f);
     if (hh == 0) a.lse[qoff + kTile * t + n32] = M + log2f(L);
   };
-  finish(m0, l0, t0);
-  if (has1) finish(m1, l1, t1);
+  finish(mr0, l0, t0);
+  if (has1) finish(mr1, l1, t1);
 }
 
 // ------------------------------------------------------------------ pass 2: pooled scores
@@ -295,6 +362,25 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     col += __shfl_xor(col, 32);
     dst[lane] = col;
   };
+  // An MFMA chain with the probability terms of an earlier, independent
+  // block woven in (16 / KC after each MFMA, pinned by scheduling barriers),
+  // then that block's column sums stored.
+  auto chain_cols = [&](const u32x4* ka, const u32x4* qa, const f32x16& prev, const float* lse,
+                        float* dst) {
+    constexpr int TPM = 16 / KC;
+    f32x16 acc = {};
+    float col = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+      for (int e = 0; e < TPM; ++e) col += exp2_fast(fmaf(prev[TPM * c + e], cs, -lse[TPM * c + e]));
+      acc = mfma32(qa[c], ka[c], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    col += __shfl_xor(col, 32);
+    dst[lane] = col;
+    return acc;
+  };
   auto advance = [&](int kb) {
     if (kb + 1 < nkb) st.store(s_k[(kb + 1) & 1]);
     if (kb + 2 < nkb) st.load(kbase, (int64_t)kTile * (kb + 2));
@@ -320,10 +406,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     auto iter = [&](int kb, auto first_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
       read_k(kb, ka);
-      const f32x16 acc0 = chain(ka, qa0);
-      if (!FIRST) colsum(acc1, lse1, s_col[(kb - 1) & 1][1][w]);
-      acc1 = chain(ka, qa1);
-      colsum(acc0, lse0, s_col[kb & 1][0][w]);
+      const f32x16 acc0 = FIRST ? chain(ka, qa0) : chain_cols(ka, qa0, acc1, lse1, s_col[(kb - 1) & 1][1][w]);
+      acc1 = chain_cols(ka, qa1, acc0, lse0, s_col[kb & 1][0][w]);
       advance(kb);
       emit(0, kb, 0);
       if (!FIRST) emit(1, kb - 1, w1);
@@ -451,7 +535,9 @@ template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
   constexpr int KROW = 2 * D + 16;   // bytes per K row in LDS (b128 reads across rows)
-  constexpr int VROW = 2 * D + 32;   // bytes per V row in LDS (transposing b64 reads of 4 rows)
+  // bytes per V row in LDS: a stride of 64 mod 256 bytes puts the four rows and
+  // two column halves of one transposing read phase on distinct banks
+  constexpr int VROW = 2 * D + 64;
   constexpr int NR = (32 * PARTS + NT - 1) / NT;   // 16-byte loads per thread per block, K and V each
   __shared__ __align__(16) char s_k[2][32 * KROW];
   __shared__ __align__(16) char s_v[2][32 * VROW];
@@ -542,6 +628,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   const int tr_row = 4 * hh + (j16 >> 2);
   const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
 
+  // Running max and row sum per query (S^T layout: the lane's query n32);
+  // the softmax scale is folded into the exponent's FMA.
   float m_run = kNegInf, l_run = 0.f;
   f32x16 o[NDC];
 #pragma unroll
@@ -572,24 +660,28 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
       const u32x4 qv = *reinterpret_cast<const u32x4*>(sq + n32 * KROW + (16 * c + 8 * hh) * 2);
       acc = mfma32(ka, qv, acc);                // S^T[key slot][query]
     }
-    float x[16];
-    if (MODE == 0) {
+    // operand reads two MFMAs ahead of their use, not all up front (registers)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = acc[r] * cs;
-    } else {
+    for (int c = 0; c < KC - 2; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (MODE != 0) {
       const int nvalid = kt - blk * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int slot = mrow(r, hh);
         const bool ok = (MODE == 2) ? (slot <= n32) : (slot < nvalid);
-        x[r] = ok ? acc[r] * cs : kNegInf;
+        acc[r] = ok ? acc[r] : kNegInf;
       }
     }
-    float bm = fmaxf(fmaxf(x[0], x[1]), x[2]);
+    float bm = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-    for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, x[r]), x[r + 1]);
-    bm = fmaxf(bm, x[15]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, acc[r]), acc[r + 1]);
+    bm = fmaxf(bm, acc[15]);
+    bm = fmaxf(bm, __shfl_xor(bm, 32)) * cs;   // cs > 0
     // Every row has a valid key in block 0 (the first selected keys, or its
     // own diagonal key), so the running max is set there while O is still
     // zero. Later blocks keep it unless a score exceeds it by 2^8 (lazy
@@ -619,19 +711,17 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
         m_run = m_new;
       }
     }
-    float p[16];
     float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = exp2_fast(x[r] - m_run);       // x = -inf -> 0
-      ps += p[r];
-    }
-    l_run += ps;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       u32x4 pa;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pa[e] = pack_bf16x2(p[8 * c2 + 2 * e], p[8 * c2 + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
+        const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
+        ps += p0 + p1;
+        pa[e] = pack_bf16x2(p0, p1);
+      }
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
         // B[k-slot (hh, e)][d = n32 + 32 dc] = V[key 16 c2 + 8 (e/4) + 4 hh + e%4][d]
@@ -642,6 +732,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
         o[dc] = mfma32(pa, vb, o[dc]);
       }
     }
+    l_run += ps;
     if (MODE != 2) store_block(buf ^ 1, std::integral_constant<int, NEXT>{});
     __syncthreads();
   };

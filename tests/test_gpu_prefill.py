@@ -154,3 +154,21 @@ def test_prefill_deterministic_and_identity_reuse():
     torch.cuda.synchronize()
     assert torch.equal(i1, i2) and torch.equal(o1, o2)
     assert torch.equal(o1, o3)
+
+
+def test_prefill_scores_far_above_first_block():
+    """Row statistics keep a per-lane reference from the first key block; a
+    later key whose score exceeds it by more than 2^64 in probability takes
+    the rescaling path. Plant such a key and compare with the oracle."""
+    kas = _kas()
+    B, Hq, Hkv, D, N, pct = 1, 8, 2, 128, 640, 10
+    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, "bf16", wid=51, sinks=False)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    u = torch.randn(D, generator=torch.Generator().manual_seed(5)).to(DEV)
+    u = u / u.norm()
+    q[:, :, 320:] = (11.0 * u).to(torch.bfloat16)          # same direction for late queries
+    k[:, :, 300] = (70.0 * u).to(torch.bfloat16)           # base-2 score ~ 70*11/sqrt(128)*log2(e) ~ 98
+    _say("[prefill anchor] planted key 300 with a score far above the first block's")
+    gidx, go = kas.prefill_anchor(q, k, v, pct)
+    torch.cuda.synchronize()
+    _check_tiles(w, q, k, v, pct, gidx, go, range(N // 32), "far_scores")
