@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
-  KS st;
+  KS st[2];   // K(j) travels in register set j & 1, loaded two blocks before it is staged
   // Row sums against a lazy reference: each lane keeps a base-2 offset mr
   // (the maximum of its first block) and adds exp2(x - mr) of every later
   // score; the terms stay below 2^64 unless a score exceeds mr by 64, and
@@ -167,29 +167,29 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   // chain.
   constexpr float kBig = 0x1p64f;
   float mr0 = 0.f, l0 = 0.f, mr1 = 0.f, l1 = 0.f;
-  auto chain = [&](const u32x4* ka, const u32x4* qb) {
+  auto chain = [&](const u32x4* ka, const u32x4* qb) __attribute__((always_inline)) {
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) acc = mfma32(ka[c], qb[c], acc);   // S^T[key][query]
     return acc;
   };
-  auto read_k = [&](int kb, u32x4* ka) {
+  auto read_k = [&](int kb, u32x4* ka) __attribute__((always_inline)) {
     const char* sk = s_k[kb & 1];
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
   };
   // masked score (diagonal block: keys after the query row are excluded)
-  auto val = [&](const f32x16& acc, int r, bool diag) -> float {
+  auto val = [&](const f32x16& acc, int r, bool diag) __attribute__((always_inline)) -> float {
     return (diag && mrow(r, hh) > n32) ? kNegInf : acc[r];
   };
-  auto block_max = [&](const f32x16& acc, bool diag) -> float {
+  auto block_max = [&](const f32x16& acc, bool diag) __attribute__((always_inline)) -> float {
     float bm = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bm = fmaxf(bm, val(acc, r, diag));
     return bm == kNegInf ? 0.f : bm * cs;      // all masked: any finite reference
   };
-  auto terms = [&](const f32x16& acc, bool diag, float mr) -> float {
+  auto terms = [&](const f32x16& acc, bool diag, float mr) __attribute__((always_inline)) -> float {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += exp2_fast(fmaf(val(acc, r, diag), cs, -mr));
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   // woven in: 16 / KC terms after each MFMA, pinned by scheduling barriers so
   // the VALU work fills the matrix unit's dependent-chain latency.
   auto chain_terms = [&](const u32x4* ka, const u32x4* qb, const f32x16& prev, bool pdiag, float mr,
-                         float& s) {
+                         float& s) __attribute__((always_inline)) {
     constexpr int TPM = 16 / KC;
     f32x16 acc = {};
 #pragma unroll
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     }
     return acc;
   };
-  auto settle = [&](const f32x16& acc, bool diag, float s, float& mr, float& l) {
+  auto settle = [&](const f32x16& acc, bool diag, float s, float& mr, float& l) __attribute__((always_inline)) {
     const bool over = !(s <= kBig);
     if (__builtin_expect(__any(over), 0)) {
       if (over) {
@@ -224,15 +224,24 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     }
     l += s;
   };
-  // Stage K(kb+1) (already in registers) and start loading K(kb+2).
-  auto advance = [&](int kb) {
-    if (kb + 1 <= tl) st.store(s_k[(kb + 1) & 1]);
-    if (kb + 2 <= tl) st.load(kbase, (int64_t)kTile * (kb + 2));
+  // Stage K(kb+1) (in register set (kb+1) & 1 since two blocks ago) and start
+  // loading K(kb+3) into the same set. SET = (kb+1) & 1 is compile-time so the
+  // two sets keep their registers (a runtime index would force copies, and a
+  // copy of a register with a load in flight waits for the load).
+  auto advance = [&](int kb, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (kb + 1 <= tl) st[SET].store(s_k[(kb + 1) & 1]);
+    if (kb + 3 <= tl) st[SET].load(kbase, (int64_t)kTile * (kb + 3));
     __syncthreads();
   };
-  st.load(kbase, 0);
-  st.store(s_k[0]);
-  if (tl >= 1) st.load(kbase, kTile);
+  auto advance_rt = [&](int kb) __attribute__((always_inline)) {
+    if ((kb + 1) & 1) advance(kb, std::integral_constant<int, 1>{});
+    else advance(kb, std::integral_constant<int, 0>{});
+  };
+  st[0].load(kbase, 0);
+  st[0].store(s_k[0]);
+  if (tl >= 1) st[1].load(kbase, kTile);
+  if (tl >= 2) st[0].load(kbase, 2 * kTile);
   __syncthreads();
   u32x4 ka[KC];
   using T_ = std::true_type;
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     // runs beside tile 0's MFMA chain, tile 0's update beside tile 1's chain.
     // FIRST: block 0 (references set, no previous tile-1 block); DIAG0: block
     // t0 is tile 0's diagonal.
-    auto iter = [&](int kb, auto first_tag, auto diag0_tag) {
+    auto iter = [&](int kb, auto first_tag, auto diag0_tag, auto set_tag) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value, DIAG0 = decltype(diag0_tag)::value;
       read_k(kb, ka);
       float s1 = 0.f, s0 = 0.f;
@@ -257,14 +266,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
       else settle(acc0, DIAG0, s0, mr0, l0);
       acc1 = acc1n;
       if (FIRST) mr1 = block_max(acc1, false);
-      advance(kb);
+      advance(kb, set_tag);
     };
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
     if (t0 == 0) {
-      iter(0, T_{}, T_{});
+      iter(0, T_{}, T_{}, Set1{});
     } else {
-      iter(0, T_{}, F_{});
-      for (int kb = 1; kb < t0; ++kb) iter(kb, F_{}, F_{});
-      iter(t0, F_{}, T_{});
+      iter(0, T_{}, F_{}, Set1{});
+      int kb = 1;
+      for (; kb + 1 < t0; kb += 2) {          // kb odd: set (kb+1)&1 = 0
+        iter(kb, F_{}, F_{}, Set0{});
+        iter(kb + 1, F_{}, F_{}, Set1{});
+      }
+      if (kb < t0) iter(kb, F_{}, F_{}, Set0{});
+      if ((t0 + 1) & 1) iter(t0, F_{}, T_{}, Set1{});
+      else iter(t0, F_{}, T_{}, Set0{});
     }
     read_k(t1, ka);
     const f32x16 acc1n = chain(ka, qb1);
@@ -283,12 +300,12 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
       } else {
         settle(acc0, diag, terms(acc0, diag, mr0), mr0, l0);
       }
-      if (kb < t0) advance(kb);
+      if (kb < t0) advance_rt(kb);
     }
   }
   // merge the two lane halves (different keys of the same query row);
   // a half whose keys were all masked has l = 0
-  auto finish = [&](float m, float l, int t) {
+  auto finish = [&](float m, float l, int t) __attribute__((always_inline)) {
     const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
     const float M = fmaxf(l > 0.f ? m : kNegInf, l2 > 0.f ? m2 : kNegInf);
     const float L = (l > 0.f ? l * exp2_fast(m - M) : 0.f) + (l2 > 0.f ? l2 * exp2_fast(m2 - M) : 0.f);
@@ -340,14 +357,14 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   float* out0 = a.pooled + pool_slot(a, b, g, t0);
   float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
-  KS st;
-  auto chain = [&](const u32x4* ka, const u32x4* qa) {
+  KS st[2];   // K(j) travels in register set j & 1, loaded two blocks before it is staged
+  auto chain = [&](const u32x4* ka, const u32x4* qa) __attribute__((always_inline)) {
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) acc = mfma32(qa[c], ka[c], acc);   // S[query][key]
     return acc;
   };
-  auto read_k = [&](int kb, u32x4* ka) {
+  auto read_k = [&](int kb, u32x4* ka) __attribute__((always_inline)) {
     const char* sk = s_k[kb & 1];
 #pragma unroll
     for (int c = 0; c < KC; ++c)
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   };
   // Column sums of one tile-block over the wave's 32 query rows; both lane
   // halves store their (equal) copy, so no lane branch splits the block.
-  auto colsum = [&](const f32x16& acc, const float* lse, float* dst) {
+  auto colsum = [&](const f32x16& acc, const float* lse, float* dst) __attribute__((always_inline)) {
     float col = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc[r], cs, -lse[r]));
@@ -366,7 +383,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   // block woven in (16 / KC after each MFMA, pinned by scheduling barriers),
   // then that block's column sums stored.
   auto chain_cols = [&](const u32x4* ka, const u32x4* qa, const f32x16& prev, const float* lse,
-                        float* dst) {
+                        float* dst) __attribute__((always_inline)) {
     constexpr int TPM = 16 / KC;
     f32x16 acc = {};
     float col = 0.f;
@@ -381,13 +398,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     dst[lane] = col;
     return acc;
   };
-  auto advance = [&](int kb) {
-    if (kb + 1 < nkb) st.store(s_k[(kb + 1) & 1]);
-    if (kb + 2 < nkb) st.load(kbase, (int64_t)kTile * (kb + 2));
+  // Stage K(kb+1) from register set (kb+1) & 1 and start loading K(kb+3)
+  // into it (compile-time set: see the statistics pass).
+  auto advance = [&](int kb, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (kb + 1 < nkb) st[SET].store(s_k[(kb + 1) & 1]);
+    if (kb + 3 < nkb) st[SET].load(kbase, (int64_t)kTile * (kb + 3));
     __syncthreads();
   };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  auto advance_rt = [&](int kb) __attribute__((always_inline)) {
+    if ((kb + 1) & 1) advance(kb, Set1{});
+    else advance(kb, Set0{});
+  };
   // Sum the G heads' column sums of (tile, block) and write them out.
-  auto emit = [&](int tile, int kb, int writer_wave) {
+  auto emit = [&](int tile, int kb, int writer_wave) __attribute__((always_inline)) {
     if (w == writer_wave && hh == 0) {
       float sum = 0.f;
 #pragma unroll
@@ -396,25 +422,31 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     }
   };
   const int w1 = G > 1 ? 1 : 0;
-  st.load(kbase, 0);
-  st.store(s_k[0]);
-  if (nkb > 1) st.load(kbase, kTile);
+  st[0].load(kbase, 0);
+  st[0].store(s_k[0]);
+  if (nkb > 1) st[1].load(kbase, kTile);
+  if (nkb > 2) st[0].load(kbase, 2 * kTile);
   __syncthreads();
   u32x4 ka[KC];
   if (has1) {
     f32x16 acc1 = {};
-    auto iter = [&](int kb, auto first_tag) {
+    auto iter = [&](int kb, auto first_tag, auto set_tag) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value;
       read_k(kb, ka);
       const f32x16 acc0 = FIRST ? chain(ka, qa0) : chain_cols(ka, qa0, acc1, lse1, s_col[(kb - 1) & 1][1][w]);
       acc1 = chain_cols(ka, qa1, acc0, lse0, s_col[kb & 1][0][w]);
-      advance(kb);
+      advance(kb, set_tag);
       emit(0, kb, 0);
       if (!FIRST) emit(1, kb - 1, w1);
     };
     if (t0 > 0) {
-      iter(0, std::true_type{});
-      for (int kb = 1; kb < t0; ++kb) iter(kb, std::false_type{});
+      iter(0, std::true_type{}, Set1{});
+      int kb = 1;
+      for (; kb + 1 < t0; kb += 2) {          // kb odd: set (kb+1)&1 = 0
+        iter(kb, std::false_type{}, Set0{});
+        iter(kb + 1, std::false_type{}, Set1{});
+      }
+      if (kb < t0) iter(kb, std::false_type{}, Set0{});
     }
     // block t0 is a candidate of tile 1 only
     read_k(t0, ka);
@@ -429,7 +461,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
       read_k(kb, ka);
       const f32x16 acc0 = chain(ka, qa0);
       colsum(acc0, lse0, s_col[kb & 1][0][w]);
-      advance(kb);
+      advance_rt(kb);
       emit(0, kb, 0);
     }
   }
@@ -584,7 +616,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   constexpr bool kAllRows = (32 * PARTS) % NT == 0;   // every thread owns NR row chunks
   u32x4 kreg[RING][NR], vreg[RING][NR];
   int jreg[RING][NR] = {};
-  auto load_index = [&](int blk, auto slot_tag) {
+  auto load_index = [&](int blk, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -594,7 +626,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   };
   // Key of each row chunk of block blk; padding rows read row 0 and are
   // masked in the softmax; the last block is the causal diagonal.
-  auto load_block = [&](int blk, auto slot_tag) {
+  auto load_block = [&](int blk, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -610,7 +642,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
       }
     }
   };
-  auto store_block = [&](int buf, auto slot_tag) {
+  auto store_block = [&](int buf, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -642,7 +674,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   // SLOT = blk % RING: the register set that is free during this block.
   // STEADY: both prefetches are known to be due (no branch around them, so
   // the rows of block blk + RING stay in flight across the next step).
-  auto step = [&](int blk, auto mode_tag, auto slot_tag, auto steady_tag) {
+  auto step = [&](int blk, auto mode_tag, auto slot_tag, auto steady_tag) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int SLOT = decltype(slot_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
@@ -741,7 +773,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
   // blocks 0 .. nsel (the last one is the diagonal block)
   const int nfull = kt / 32;
   using Tail = std::false_type;
-  auto step_any = [&](int blk, auto mode_tag) {
+  auto step_any = [&](int blk, auto mode_tag) __attribute__((always_inline)) {
     if (blk % RING == 0) step(blk, mode_tag, S0{}, Tail{});
     else step(blk, mode_tag, S1{}, Tail{});
   };
@@ -833,7 +865,7 @@ static PrefillPlan plan(int B, int Hq, int Hkv, int64_t N, bool anchor) {
   PrefillPlan p{};
   const int T = (int)(N / kTile);
   size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  auto take = [&](size_t bytes) __attribute__((always_inline)) { size_t o = off; off = align256(off + bytes); return o; };
   p.off_offsets = take((size_t)(T + 1) * sizeof(int32_t));
   if (anchor) {
     p.off_lse = take((size_t)B * Hq * N * sizeof(float));
