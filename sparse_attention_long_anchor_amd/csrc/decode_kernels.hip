@@ -280,64 +280,46 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup of 1024 threads per (b, g): digits 2 and 3 of the radix
-// select (histograms in LDS, the pooled row re-read from L2/HBM), then the
-// stable compaction in index order. Replaces four multi-workgroup launches.
+// One workgroup of 1024 threads per (b, g) finishes the radix select whose
+// first digit (bits 31..21) dec_pool histogrammed:
+//  1. the bin b1 of the k-th largest; its population is known from the
+//     histogram, so if it fits, one sweep of the pooled row collects the bin's
+//     scores into LDS and digits 2 (bits 20..10) and 3 (bits 9..0) are
+//     resolved there; otherwise two more sweeps histogram them in place;
+//  2. tau (the exact bit pattern of the k-th largest) and r (how many scores
+//     equal to tau are kept);
+//  3. a last sweep writes every key with P > tau plus the first r keys equal
+//     to tau, in index order (one packed workgroup scan per step).
+// Sweeps read 16 consecutive scores per thread per step with the next step's
+// loads already in flight (32 scores per thread in registers).
 constexpr int kSelThreads = 1024;
+constexpr int kSelCandCap = 24576;   // LDS candidate list (96 KB)
 __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
   __shared__ uint32_t s_h[kBins2];
+  __shared__ uint32_t s_cand[kSelCandCap];
   __shared__ uint32_t s_tmp[kSelThreads / 64];
   __shared__ int s_res[2];
+  __shared__ uint32_t s_ncand;
   const int64_t unit = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t k = (uint32_t)a.kk;
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
+  const uint32_t* hist1 = a.hist + unit * kHistWords;
   const int64_t N = a.N;
+  constexpr int PER = 16;
+  constexpr int64_t STEP = (int64_t)kSelThreads * PER;
   int b1, b2, b3;
   uint32_t ab1, ab2, ab3;
-  block_find_bin_nt<kSelThreads>(a.hist + unit * kHistWords, kBins1, k, s_tmp, s_res, b1, ab1);
+  block_find_bin_nt<kSelThreads>(hist1, kBins1, k, s_tmp, s_res, b1, ab1);
+  const uint32_t nb1 = hist1[b1];
   for (int i = tid; i < kBins2; i += kSelThreads) s_h[i] = 0u;
+  if (tid == 0) s_ncand = 0u;
   __syncthreads();
-  // Passes read 16 consecutive scores per thread (four 16-byte loads in
-  // flight per thread) so one workgroup keeps enough bytes in flight.
-  auto sweep = [&](auto&& fn) {
-    for (int64_t base = 0; base < N; base += (int64_t)kSelThreads * 16) {
-      const int64_t j0 = base + (int64_t)tid * 16;
-      if (j0 + 16 <= N) {
-        u32x4 v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = ldg16(P + j0 + 4 * q);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fn(v[q][e]);
-      } else {
-        for (int64_t j = j0; j < N; ++j) fn(P[j]);
-      }
-    }
-  };
-  sweep([&](uint32_t u) {
-    if ((u >> 21) == (uint32_t)b1) atomicAdd(&s_h[(u >> 10) & 0x7ffu], 1u);
-  });
-  __syncthreads();
-  block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
-  for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
-  __syncthreads();
-  const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-  sweep([&](uint32_t u) {
-    if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
-  });
-  __syncthreads();
-  block_find_bin_nt<kSelThreads>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
-  const uint32_t tau = (pre << 10) | (uint32_t)b3;
-  const uint32_t r = k - ab1 - ab2 - ab3;
-  int32_t* out = a.idx_out + unit * a.kk;
-  constexpr int PER = 16;
-  uint32_t gt_run = 0, eq_run = 0;
-  for (int64_t base = 0; base < N; base += (int64_t)kSelThreads * PER) {
+
+  // 16 scores of this thread at base + 16 tid (positions >= N read as 0 and
+  // are excluded by the callers through the position test)
+  auto load16 = [&](int64_t base, uint32_t* u) __attribute__((always_inline)) {
     const int64_t j0 = base + (int64_t)tid * PER;
-    uint32_t u[PER];
-    uint32_t gt = 0, eq = 0;
     if (j0 + PER <= N) {
 #pragma unroll
       for (int q = 0; q < PER / 4; ++q) {
@@ -349,30 +331,106 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) u[i] = (j0 + i < N) ? P[j0 + i] : 0u;
     }
+  };
+  // sweep with the next step's loads in flight; fn(base, u) per step
+  auto sweep = [&](auto&& fn) __attribute__((always_inline)) {
+    uint32_t ua[PER], ub[PER];
+    load16(0, ua);
+    for (int64_t base = 0; base < N; base += 2 * STEP) {
+      if (base + STEP < N) load16(base + STEP, ub);
+      fn(base, ua);
+      if (base + 2 * STEP < N) load16(base + 2 * STEP, ua);
+      if (base + STEP < N) fn(base + STEP, ub);
+    }
+  };
+
+  if (nb1 <= (uint32_t)kSelCandCap) {
+    // collect bin b1 into LDS (wave-aggregated appends)
+    sweep([&](int64_t base, const uint32_t* u) __attribute__((always_inline)) {
+      const int64_t j0 = base + (int64_t)tid * PER;
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) c += (j0 + i < N && (u[i] >> 21) == (uint32_t)b1) ? 1u : 0u;
+      const uint32_t inc = wave_incl_scan_u32(c);
+      uint32_t wbase = 0;
+      if (lane == 63 && inc) wbase = atomicAdd(&s_ncand, inc);
+      wbase = __shfl(wbase, 63);
+      uint32_t pos = wbase + inc - c;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (j0 + i < N && (u[i] >> 21) == (uint32_t)b1) {
+          if (pos < (uint32_t)kSelCandCap) s_cand[pos] = u[i];
+          ++pos;
+        }
+      }
+    });
+    __syncthreads();
+    const uint32_t nc = min(s_ncand, (uint32_t)kSelCandCap);
+    for (uint32_t i = tid; i < nc; i += kSelThreads) atomicAdd(&s_h[(s_cand[i] >> 10) & 0x7ffu], 1u);
+    __syncthreads();
+    block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    for (uint32_t i = tid; i < nc; i += kSelThreads)
+      if ((s_cand[i] >> 10) == pre) atomicAdd(&s_h[s_cand[i] & 0x3ffu], 1u);
+    __syncthreads();
+    block_find_bin_nt<kSelThreads>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  } else {
+    sweep([&](int64_t base, const uint32_t* u) __attribute__((always_inline)) {
+      const int64_t j0 = base + (int64_t)tid * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (j0 + i < N && (u[i] >> 21) == (uint32_t)b1) atomicAdd(&s_h[(u[i] >> 10) & 0x7ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    sweep([&](int64_t base, const uint32_t* u) __attribute__((always_inline)) {
+      const int64_t j0 = base + (int64_t)tid * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (j0 + i < N && (u[i] >> 10) == pre) atomicAdd(&s_h[u[i] & 0x3ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin_nt<kSelThreads>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  }
+  const uint32_t tau = (((uint32_t)b1 << 11 | (uint32_t)b2) << 10) | (uint32_t)b3;
+  const uint32_t r = k - ab1 - ab2 - ab3;
+  int32_t* out = a.idx_out + unit * a.kk;
+  // counts above / equal to tau packed in one word (each below 2^16 per step)
+  uint32_t gt_run = 0, eq_run = 0;
+  sweep([&](int64_t base, const uint32_t* u) __attribute__((always_inline)) {
+    const int64_t j0 = base + (int64_t)tid * PER;
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const bool in = j0 + i < N;
-      gt += in && u[i] > tau;
-      eq += in && u[i] == tau;
+      gt += (in && u[i] > tau) ? 1u : 0u;
+      eq += (in && u[i] == tau) ? 1u : 0u;
     }
-    uint32_t tg, te;
-    uint32_t g_ex = block_excl_scan<kSelThreads>(gt, s_tmp, &tg) + gt_run;
-    uint32_t e_ex = block_excl_scan<kSelThreads>(eq, s_tmp, &te) + eq_run;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kSelThreads>((gt << 16) | eq, s_tmp, &tot);
+    uint32_t g_ex = (ex >> 16) + gt_run;
+    uint32_t e_ex = (ex & 0xffffu) + eq_run;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (j0 + i >= N) break;
-      if (u[i] > tau) {
-        const uint32_t pos = g_ex + min(e_ex, r);
-        if (pos < k) out[pos] = (int32_t)(j0 + i);
-        ++g_ex;
-      } else if (u[i] == tau) {
-        if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = (int32_t)(j0 + i);
-        ++e_ex;
+      if (j0 + i < N) {
+        if (u[i] > tau) {
+          const uint32_t pos = g_ex + min(e_ex, r);
+          if (pos < k) out[pos] = (int32_t)(j0 + i);
+          ++g_ex;
+        } else if (u[i] == tau) {
+          if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = (int32_t)(j0 + i);
+          ++e_ex;
+        }
       }
     }
-    gt_run += tg;
-    eq_run += te;
-  }
+    gt_run += tot >> 16;
+    eq_run += tot & 0xffffu;
+  });
 }
 
 // ------------------------------------------------------------------ dec_attn
