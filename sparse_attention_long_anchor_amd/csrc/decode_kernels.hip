@@ -17,6 +17,7 @@
 #include <stdlib.h>
 
 #include <string.h>
+#include <type_traits>
 
 #include "kas_block.hpp"
 #include "kas_internal.hpp"
@@ -52,39 +53,88 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   for (int r = 0; r < 4; ++r) { ml[r] = kNegInf; ls[r] = 0.f; }
 
   const int nblk = (nrows + 15) >> 4;
-  QK cur;
-  if (wave < nblk) {
-    int jr = wave * 16 + c16;
-    cur.load_k(kb + (int64_t)(jr < nrows ? jr : 0) * D, q4);
-  }
-  for (int blk = wave; blk < nblk; blk += 4) {
+  // Wave w takes 16-row blocks w, w+4, ...; the rows of its next two blocks
+  // are in flight in two register sets named at compile time (a runtime
+  // swap would copy registers whose loads are still in flight, which waits
+  // for them).
+  auto load = [&](int blk, QK& dst) __attribute__((always_inline)) {
     const int jr = blk * 16 + c16;
-    const bool val = jr < nrows;
-    QK nxt;
-    if (blk + 4 < nblk) {
-      int jn = jr + 64;
-      nxt.load_k(kb + (int64_t)(jn < nrows ? jn : 0) * D, q4);
-    }
-    f32x4 s = cur.run(qf);
+    dst.load_k(kb + (int64_t)(jr < nrows ? jr : 0) * D, q4);
+  };
+  // STEADY: a full block inside the steady loop (all rows valid); for G = 4
+  // and 8 the logits are transposed across lanes so that the whole wave
+  // writes them with one unconditional contiguous store (a branch around a
+  // store would make the waits before the next block's MFMA drain the loads
+  // in flight: stores count on the same counter).
+  auto process = [&](int blk, const QK& src, auto steady_tag) __attribute__((always_inline)) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int jr = blk * 16 + c16;
+    const bool val = STEADY || jr < nrows;
+    const f32x4 s = src.run(qf);
     float t[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) t[r] = val ? s[r] * a.scale_log2 : kNegInf;
-    if (val) {
+    if (STEADY && G == 4) {
+      // lane l: key l / 4, head l % 4, held by lane l / 4 in reg l % 4
+      const int src_lane = lane >> 2, h = lane & 3;
+      float v0 = __shfl(t[0], src_lane), v1 = __shfl(t[1], src_lane);
+      float v2 = __shfl(t[2], src_lane), v3 = __shfl(t[3], src_lane);
+      asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));   // all four, no branches
+      const float v = (h & 2) ? ((h & 1) ? v3 : v2) : ((h & 1) ? v1 : v0);
+      lg[(int64_t)blk * 16 * G + lane] = v;
+    } else if (STEADY && G == 8) {
+      // lane l: key l / 4, heads 2 (l % 4) and +1, held by lane key + 16 q4
+      const int h0 = 2 * (lane & 3);
+      const int src_lane = (lane >> 2) + 16 * (h0 >> 2);
+      float v0 = __shfl(t[0], src_lane), v1 = __shfl(t[1], src_lane);
+      float v2 = __shfl(t[2], src_lane), v3 = __shfl(t[3], src_lane);
+      asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+      const bool lo = (h0 & 3) == 0;
+      *reinterpret_cast<float2*>(lg + (int64_t)blk * 16 * G + 2 * lane) =
+          lo ? float2{v0, v1} : float2{v2, v3};
+    } else if (val && 4 * q4 < G) {
+      // lane (key jr, quarter q4) holds heads 4 q4 .. 4 q4 + 3
+      float* dst = lg + (int64_t)jr * G + 4 * q4;
+      if (G >= 4) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{t[0], t[1], t[2], t[3]};
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * q4 + r < G) lg[(int64_t)jr * G + 4 * q4 + r] = t[r];
+        for (int r = 0; r < G; ++r) dst[r] = t[r];
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float bm = row16_max(t[r]);
       float mn = fmaxf(ml[r], bm);
       float al = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
-      float p = (t[r] == kNegInf) ? 0.f : exp2_fast(t[r] - mn);
+      float p = (STEADY || t[r] != kNegInf) ? exp2_fast(t[r] - mn) : 0.f;
       ls[r] = ls[r] * al + p;
       ml[r] = mn;
     }
-    cur = nxt;
+  };
+  QK qa, qb;
+  int blk = wave;
+  using Steady = std::true_type;
+  using Edge = std::false_type;
+  if (blk + 12 < nblk) {
+    // steady state without a branch around a load (waits stay partial); the
+    // entry issues the same loads in the same order as the loop's back edge
+    load(blk, qa);
+    load(blk + 4, qb);
+    for (; blk + 12 < nblk; blk += 8) {     // blocks blk .. blk + 12 all full
+      process(blk, qa, Steady{});
+      load(blk + 8, qa);
+      process(blk + 4, qb, Steady{});
+      load(blk + 12, qb);
+    }
+  } else {
+    if (blk < nblk) load(blk, qa);
+    if (blk + 4 < nblk) load(blk + 4, qb);
   }
+  if (blk < nblk) process(blk, qa, Edge{});
+  if (blk + 8 < nblk) load(blk + 8, qa);
+  if (blk + 4 < nblk) process(blk + 4, qb, Edge{});
+  if (blk + 8 < nblk) process(blk + 8, qa, Edge{});
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float lsum = row16_sum(ls[h & 3]);
