@@ -17,6 +17,7 @@
 //               head), gathered K rows and transposed V rows in LDS, S^T and
 //               P.V on MFMA, online softmax over the tile's index set plus
 //               its causal diagonal block.
+#include <string.h>
 #include <type_traits>
 
 #include "kas_block.hpp"
@@ -685,21 +686,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
     const char* sk = s_k[buf];
     const char* sv = s_v[buf];
     const char* sq = s_q[w];
+    // S^T[key slot][query]; operand reads two MFMAs ahead of their use (not
+    // all hoisted: the output accumulators need the registers)
     f32x16 acc = {};
+    u32x4 kf[3], qf[3];
+    auto rd = [&](int c, int slot) __attribute__((always_inline)) {
+      kf[slot] = *reinterpret_cast<const u32x4*>(sk + n32 * KROW + (16 * c + 8 * hh) * 2);
+      qf[slot] = *reinterpret_cast<const u32x4*>(sq + n32 * KROW + (16 * c + 8 * hh) * 2);
+    };
+    rd(0, 0);
+    rd(1, 1);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(sk + n32 * KROW + (16 * c + 8 * hh) * 2);
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(sq + n32 * KROW + (16 * c + 8 * hh) * 2);
-      acc = mfma32(ka, qv, acc);                // S^T[key slot][query]
+      if (c + 2 < KC) rd(c + 2, (c + 2) % 3);
+      acc = mfma32(kf[c % 3], qf[c % 3], acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // operand reads two MFMAs ahead of their use, not all up front (registers)
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int c = 0; c < KC - 2; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     if (MODE != 0) {
       const int nvalid = kt - blk * 32;
 #pragma unroll
@@ -821,6 +823,250 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
       ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = f32_to_bf16_rne(o[dc][r] * inv[r]);
 }
 
+// ------------------------------------------------------------------ tile attention, LDS-DMA gathers
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vector memory only:
+// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) left at max.
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+// 16-byte chunk swizzles of unpadded K and V rows in LDS. K rows are read
+// row-per-lane (8 lanes per LDS phase); V rows by the transposing read (4 rows
+// x 4 chunks per phase); the XOR keeps each phase on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 7) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// Same math as pre_attn_kernel; the gathered K and V rows go from global
+// memory straight into LDS (global_load_lds_dwordx4: each lane names its own
+// row chunk, the data lands at a fixed slot of a 1 KB line) through a ring of
+// three stages, two blocks ahead of the math, so no registers hold rows in
+// flight. Q stays in registers. The stages are distinct arrays selected at
+// compile time (the steady loop is unrolled by three), so the compiler can
+// tell the stage being read from the stages being filled.
+template <int D, int G>
+__global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) {
+  constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
+  constexpr int ROWB = 2 * D;               // bytes per row
+  constexpr int BLKB = 32 * ROWB;           // one block of K (or V) rows
+  constexpr int RPI = 64 / PARTS;           // rows per 1 KB DMA line
+  constexpr int NINS = 32 / RPI;            // lines per block per tensor
+  constexpr int NIW = (NINS + G - 1) / G;   // lines per wave (w, w + G, ...)
+  constexpr bool EVEN = NINS % G == 0;      // every wave issues NIW lines
+  (void)NT;
+  __shared__ __align__(1024) char s_st0[2 * BLKB];
+  __shared__ __align__(1024) char s_st1[2 * BLKB];
+  __shared__ __align__(1024) char s_st2[2 * BLKB];
+
+  const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n32 = lane & 31, hh = lane >> 5;
+  const int h = g * G + w;
+  int ga = a.head_map ? a.head_map[g] : g;
+  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+  const int o0 = a.offsets[t];
+  const int kt = a.offsets[t + 1] - o0;
+  const int32_t* S = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
+  const int nsel = (kt + 31) / 32;
+  const int nfull = kt / 32;
+  const int tile_key0 = kTile * t;
+  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
+  // Q fragments: B operand of S^T (lane: query n32, dims 16 c + 8 hh)
+  u32x4 qf[KC];
+  {
+    const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[c] = ldg16(qrow + 16 * c + 8 * hh);
+  }
+  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const float cs = a.scale_log2;
+  const int lrow = lane / PARTS, lslot = lane % PARTS;   // this lane's row / slot in a DMA line
+
+  // raw indices of this lane's rows in the wave's lines of block blk (set blk % 3)
+  int jr[3][NIW];
+  auto load_index = [&](int blk, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + G * j;
+      if (EVEN || i < NINS) jr[SET][j] = S[min(blk * 32 + RPI * i + lrow, kt - 1)];
+    }
+  };
+  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
+    constexpr int ST = decltype(st_tag)::value;
+    return ST == 0 ? s_st0 : (ST == 1 ? s_st1 : s_st2);
+  };
+  // DMA the K and V rows of block blk into a stage (the causal diagonal block
+  // nsel reads rows tile_key0 ..; padding rows read row 0 and are masked)
+  auto issue = [&](int blk, auto set_tag, char* dst) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + G * j;
+      if (EVEN || i < NINS) {
+        const int r = RPI * i + lrow;
+        const int jj = jr[SET][j];
+        const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
+        const int key = (blk == nsel) ? tile_key0 + r : sel;
+        const __bf16* krow = kbase + (int64_t)key * D;
+        const __bf16* vrow = vbase + (int64_t)key * D;
+        __builtin_amdgcn_global_load_lds((const void*)(krow + 8 * (lslot ^ swz_k<D>(r))),
+                                         (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (lslot ^ swz_v<D>(r))),
+                                         (__attribute__((address_space(3))) void*)(dst + BLKB + 1024 * i), 16,
+                                         0, 0);
+      }
+    }
+  };
+  // P.V operand addressing (transposing read): lane group g16 = lane/16,
+  // member j = lane%16 reads row 4*hh + j/4 (+8 for the upper keys), chunk
+  // 4 dc + 2 (g16 % 2) + (j % 4) / 2, half (j % 4) % 2 of it.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int tr_row = 4 * hh + (j16 >> 2);
+  const int tr_q = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int tr_half = 8 * ((j16 & 3) & 1);
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 o[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x16{};
+
+  // One key block on stage ST (MODE 0: full selected block; 1: the partial
+  // last one; 2: the causal diagonal). Before the math: indices of block
+  // blk + 3 and the DMA of block blk + 2 (into stage (ST + 2) % 3). After it:
+  // block blk + 1's lines complete in every wave, then a barrier.
+  auto step = [&](int blk, auto mode_tag, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr int ST = decltype(st_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    using SetN = std::integral_constant<int, ST>;             // (blk + 3) % 3
+    using St2 = std::integral_constant<int, (ST + 2) % 3>;    // (blk + 2) % 3
+    if (STEADY || blk + 3 < nsel) load_index(blk + 3, SetN{});
+    // the indices of block blk + 2 (loaded a step ago, before block blk + 1's
+    // lines and this step's index loads) have landed; said with the builtin
+    // so the compiler does not wait for everything in flight before using them
+    if (STEADY && EVEN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
+    if (STEADY || blk + 2 <= nsel) issue(blk + 2, St2{}, stage(St2{}));
+    const char* sk = stage(st_tag);
+    const char* sv = sk + BLKB;
+    f32x16 acc = {};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(sk + n32 * ROWB + 16 * ((2 * c + hh) ^ swz_k<D>(n32)));
+      acc = mfma32(kk, qf[c], acc);             // S^T[key slot][query]
+    }
+    if (MODE != 0) {
+      const int nvalid = kt - blk * 32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int slot = mrow(r, hh);
+        const bool ok = (MODE == 2) ? (slot <= n32) : (slot < nvalid);
+        acc[r] = ok ? acc[r] : kNegInf;
+      }
+    }
+    float bm = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) bm = fmaxf(fmaxf(bm, acc[r]), acc[r + 1]);
+    bm = fmaxf(bm, acc[15]);
+    bm = fmaxf(bm, __shfl_xor(bm, 32)) * cs;   // cs > 0
+    // lazy rescale (see pre_attn_kernel); alpha moves from the S^T layout
+    // (lane = query) to the output layout (reg r = query mrow(r, hh)) by shuffles
+    if (blk == 0) {
+      m_run = bm;
+    } else {
+      const bool bump = bm > m_run + 8.f;
+      if (__builtin_expect(__any(bump), 0)) {
+        const float m_new = bump ? bm : m_run;
+        const float alpha = exp2_fast(m_run - m_new);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ar = __shfl(alpha, mrow(r, hh));
+#pragma unroll
+          for (int dc = 0; dc < NDC; ++dc) o[dc][r] *= ar;
+        }
+        l_run *= alpha;
+        m_run = m_new;
+      }
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      u32x4 pa;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
+        const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
+        ps += p0 + p1;
+        pa[e] = pack_bf16x2(p0, p1);
+      }
+      const int R = 16 * c2 + tr_row;
+      const int sw = swz_v<D>(R);                // rows R and R + 8 share it
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const int cofs = 16 * ((4 * dc + tr_q) ^ sw) + tr_half;
+        const u32x2 lo = lds_read_tr16(sv + R * ROWB + cofs);
+        const u32x2 hi = lds_read_tr16(sv + (R + 8) * ROWB + cofs);
+        const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
+        o[dc] = mfma32(pa, vb, o[dc]);
+      }
+    }
+    l_run += ps;
+    // block blk + 1 complete in this wave (steady: only this step's index
+    // loads and DMA lines may still be in flight), then in every wave
+    // (the builtin wait, unlike inline asm, is seen by the compiler's own
+    // wait placement, which then knows these lines have landed)
+    if (STEADY && EVEN) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  using St0 = std::integral_constant<int, 0>;
+  using St1 = std::integral_constant<int, 1>;
+  using St2c = std::integral_constant<int, 2>;
+  using Steady = std::true_type;
+  using Tail = std::false_type;
+  // prologue: indices of blocks 0..2, lines of blocks 0 and 1
+  if (0 < nsel) load_index(0, St0{});
+  if (1 < nsel) load_index(1, St1{});
+  if (2 < nsel) load_index(2, St2c{});
+  issue(0, St0{}, s_st0);
+  if (1 <= nsel) issue(1, St1{}, s_st1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int blk = 0;
+  // steady state: blocks blk .. blk + 2 full, indices of blk + 5 exist
+  for (; blk + 5 < nsel; blk += 3) {
+    step(blk, std::integral_constant<int, 0>{}, St0{}, Steady{});
+    step(blk + 1, std::integral_constant<int, 0>{}, St1{}, Steady{});
+    step(blk + 2, std::integral_constant<int, 0>{}, St2c{}, Steady{});
+  }
+  auto step_any = [&](int bk, auto mode_tag) __attribute__((always_inline)) {
+    const int st = bk % 3;
+    if (st == 0) step(bk, mode_tag, St0{}, Tail{});
+    else if (st == 1) step(bk, mode_tag, St1{}, Tail{});
+    else step(bk, mode_tag, St2c{}, Tail{});
+  };
+  for (; blk < nfull; ++blk) step_any(blk, std::integral_constant<int, 0>{});
+  if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
+  step_any(nsel, std::integral_constant<int, 2>{});
+  // normalise: 1/l of query q lives in lane q; output rows are mrow(r, hh)
+  const float inv_l = 1.0f / (l_run + __shfl_xor(l_run, 32));
+  uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + qoff * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float inv = __shfl(inv_l, mrow(r, hh));
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = f32_to_bf16_rne(o[dc][r] * inv);
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -928,7 +1174,10 @@ static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
 static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) {
   ctx.begin(K_PRE_ATTN);
   dim3 grid(a.T, a.Hkv, a.B);
-  KAS_DISPATCH_DG(pre_attn_kernel, grid, ctx, a);
+  // KAS_PREFILL_ATTN=regring selects the register-staged kernel
+  const char* sel = getenv("KAS_PREFILL_ATTN");
+  if (sel && strcmp(sel, "regring") == 0) KAS_DISPATCH_DG(pre_attn_kernel, grid, ctx, a);
+  else KAS_DISPATCH_DG(pre_attn_dma_kernel, grid, ctx, a);
   return ctx.end(K_PRE_ATTN);
 }
 
