@@ -25,7 +25,10 @@
 
 namespace kas {
 
-constexpr int kPoolBudgetMBDefault = 2048;
+// Pooled-score buffer cap: one pooling launch covers a 128K prompt with 8 KV
+// heads (8.6 GB), which beats chunked launches (fewer launch tails); the
+// buffer is only as large as the prompt needs.
+constexpr int kPoolBudgetMBDefault = 16384;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),

@@ -192,3 +192,17 @@ def test_prefill_register_staged_attention_variant(shape, monkeypatch):
     assert torch.equal(gidx, gidx2)
     assert torch.equal(go, go2)
     _check_tiles(w, q, k, v, pct, gidx2, go2, range(N // 32), label + " regring")
+
+
+def test_prefill_pooling_in_tile_ranges(monkeypatch):
+    """A small pooled-score budget splits pooling and selection into many
+    tile ranges; the index sets and outputs are bit-identical to one range."""
+    kas = _kas()
+    w = inputgen.custom("prefill", 1, 8, 2, 128, 2048, "bf16", wid=61)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    gidx, go = kas.prefill_anchor(q, k, v, 10)
+    monkeypatch.setenv("KAS_PREFILL_POOL_MB", "1")     # ~262K floats per range
+    gidx2, go2 = kas.prefill_anchor(q, k, v, 10)
+    torch.cuda.synchronize()
+    assert torch.equal(gidx, gidx2) and torch.equal(go, go2)
+    _check_tiles(w, q, k, v, 10, gidx2, go2, (1, 17, 40, 63), "pool_ranges")
