@@ -59,6 +59,29 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Combine each lane's value with that of lane l ^ 32 without an LDS round
+// trip. v_permlane32_swap exchanges the upper half-wave of its first operand
+// with the lower half-wave of its second; fed x twice, its two results hold
+// x[l] and x[l ^ 32] (in an order that differs between the halves), so a
+// symmetric combination of them gives the same value in lanes l and l ^ 32.
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Maximum of the 16 accumulator values of a 32x32 MFMA tile held by a lane,
+// as a depth-three tree of three-input maxima.
+template <typename V>
+__device__ __forceinline__ float max16(const V& v) {
+  const float t0 = fmaxf(fmaxf(v[0], v[1]), v[2]), t1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float t2 = fmaxf(fmaxf(v[6], v[7]), v[8]), t3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float t4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), v[15]));
+}
+
 // Full 64-lane reductions through cross-lane permutes.
 __device__ __forceinline__ float wave_sum(float x) {
   x = row16_sum(x);
