@@ -8,8 +8,10 @@
 //               probability (Kascade README "Abstract": exact post-softmax
 //               Top-k, head-aware), first radix digit histogram.
 //  sel_*        anchor: exact k-th largest pooled score by a three-digit
-//               radix select over the fp32 bit pattern, then a stable
-//               compaction of {P > tau} plus the lowest-index ties.
+//               radix select over the fp32 bit pattern (candidates of the
+//               first digit's bin per chunk, digits 2 and 3 resolved per row),
+//               then a stable compaction of {P > tau} plus the lowest-index
+//               ties.
 //  dec_attn     anchor and reuse: index-driven gather of K/V rows, online
 //               softmax, split-K partial (o, m, l) per workgroup.
 //  dec_combine  merge of the split-K partials into the output.
@@ -207,89 +209,60 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ radix select
 
-template <int PASS>
-__global__ __launch_bounds__(256) void sel_digit_kernel(DecodeArgs a) {
-  __shared__ uint32_t s_h[kBins2];
+// Chunked selection, step 1 (one workgroup per 4096-score chunk): the bin b1
+// of the k-th largest from the first-digit histogram; the chunk's count of
+// scores in higher bins (all of them are kept) and its scores of bin b1, in
+// position order, in the chunk's own slot of the candidate area. The chunk's
+// loads are issued before the bin search so the two latencies overlap.
+__global__ __launch_bounds__(256) void sel_cand_kernel(DecodeArgs a) {
   __shared__ uint32_t s_tmp[4];
   __shared__ int s_res[2];
   const int chunk = blockIdx.x;
   const int64_t unit = blockIdx.y;
   const int tid = threadIdx.x;
-  const uint32_t* gh = a.hist + unit * kHistWords;
-  int b1, b2 = 0;
-  uint32_t ab1, ab2;
-  block_find_bin(gh, kBins1, (uint32_t)a.kk, s_tmp, s_res, b1, ab1);
-  if (PASS == 3) block_find_bin(gh + kBins1, kBins2, (uint32_t)a.kk - ab1, s_tmp, s_res, b2, ab2);
-  constexpr int NB = PASS == 2 ? kBins2 : kBins3;
-  for (int i = tid; i < NB; i += 256) s_h[i] = 0u;
-  __syncthreads();
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
-  const int64_t base = (int64_t)chunk * kSelChunk;
-  const uint32_t pre = PASS == 2 ? (uint32_t)b1 : (((uint32_t)b1 << 11) | (uint32_t)b2);
-#pragma unroll 4
-  for (int i = 0; i < kSelChunk / 256; ++i) {
-    const int64_t j = base + i * 256 + tid;
-    if (j < a.N) {
-      uint32_t u = P[j];
-      if (PASS == 2) {
-        if ((u >> 21) == pre) atomicAdd(&s_h[(u >> 10) & 0x7ffu], 1u);
-      } else {
-        if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
-      }
+  constexpr int PER = kSelChunk / 256;
+  const int64_t j0 = (int64_t)chunk * kSelChunk + tid * PER;
+  uint32_t u[PER];
+  if (j0 + PER <= a.N) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 v = ldg16(P + j0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) u[i] = (j0 + i < a.N) ? P[j0 + i] : 0u;
   }
-  __syncthreads();
-  uint32_t* out = a.hist + unit * kHistWords + (PASS == 2 ? kBins1 : kBins1 + kBins2);
-  for (int i = tid; i < NB; i += 256)
-    if (s_h[i]) atomicAdd(&out[i], s_h[i]);
-}
-
-// tau (bit pattern of the k-th largest) and r = ties at tau to keep; per-chunk
-// counts of elements above / equal to tau.
-__global__ __launch_bounds__(256) void sel_count_kernel(DecodeArgs a) {
-  __shared__ uint32_t s_tmp[4];
-  __shared__ int s_res[2];
-  const int chunk = blockIdx.x;
-  const int64_t unit = blockIdx.y;
-  const int tid = threadIdx.x;
-  const uint32_t* gh = a.hist + unit * kHistWords;
-  int b1, b2, b3;
-  uint32_t ab1, ab2, ab3;
-  const uint32_t k = (uint32_t)a.kk;
-  block_find_bin(gh, kBins1, k, s_tmp, s_res, b1, ab1);
-  block_find_bin(gh + kBins1, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
-  block_find_bin(gh + kBins1 + kBins2, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
-  const uint32_t tau = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10) | (uint32_t)b3;
-  const uint32_t r = k - ab1 - ab2 - ab3;
-  const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
-  const int64_t base = (int64_t)chunk * kSelChunk;
-  uint32_t gt = 0, eq = 0;
-#pragma unroll 4
-  for (int i = 0; i < kSelChunk / 256; ++i) {
-    const int64_t j = base + i * 256 + tid;
-    if (j < a.N) {
-      uint32_t u = P[j];
-      gt += u > tau;
-      eq += u == tau;
-    }
+  int b1;
+  uint32_t ab1;
+  block_find_bin(a.hist + unit * kHistWords, kBins1, (uint32_t)a.kk, s_tmp, s_res, b1, ab1);
+  uint32_t gt = 0, nc = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool in = j0 + i < a.N;
+    gt += (in && (u[i] >> 21) > (uint32_t)b1) ? 1u : 0u;
+    nc += (in && (u[i] >> 21) == (uint32_t)b1) ? 1u : 0u;
   }
-  uint32_t tg, te;
-  block_excl_scan_256(gt, s_tmp, &tg);
-  block_excl_scan_256(eq, s_tmp, &te);
+  // both counts fit 16 bits (at most kSelChunk per chunk): one packed scan
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan_256((gt << 16) | nc, s_tmp, &tot);
+  uint32_t pos = ex & 0xffffu;
+  uint32_t* cand = a.cand + (unit * a.n_sel_chunks + chunk) * (int64_t)kSelChunk;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (j0 + i < a.N && (u[i] >> 21) == (uint32_t)b1) cand[pos++] = u[i];
   if (tid == 0) {
     uint32_t* c = a.counts + (unit * a.n_sel_chunks + chunk) * 2;
-    c[0] = tg;
-    c[1] = te;
-    if (chunk == 0) {
-      uint32_t* ss = a.selstate + unit * 4;
-      ss[0] = tau;
-      ss[1] = r;
-    }
+    c[0] = tot >> 16;
+    c[1] = tot & 0xffffu;
   }
 }
 
-// Stable compaction: key j is kept if P_j > tau, or P_j == tau and fewer than
-// r equal keys precede it. Output position = kept keys before j.
+// Chunked selection, step 3: stable compaction. Key j is kept if P_j > tau,
+// or P_j == tau and fewer than r equal keys precede it; output position = kept
+// keys before j (the chunk's prefix counts from step 2 plus a workgroup scan).
 __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   __shared__ uint32_t s_tmp[4];
   const int chunk = blockIdx.x;
@@ -297,9 +270,9 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const uint32_t tau = a.selstate[unit * 4 + 0];
   const uint32_t r = a.selstate[unit * 4 + 1];
-  uint32_t gt_before = 0, eq_before = 0;
-  const uint32_t* c = a.counts + unit * a.n_sel_chunks * 2;
-  for (int x = 0; x < chunk; ++x) { gt_before += c[2 * x]; eq_before += c[2 * x + 1]; }
+  // scores above / equal to tau in the chunks before this one
+  const uint32_t* c = a.counts + (unit * a.n_sel_chunks + chunk) * 2;
+  const uint32_t gt_before = c[0], eq_before = c[1];
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
   // thread owns 16 consecutive keys
   constexpr int PER = kSelChunk / 256;
@@ -481,6 +454,92 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
     gt_run += tot >> 16;
     eq_run += tot & 0xffffu;
   });
+}
+
+// Chunked selection, step 2 (one workgroup of 1024 threads per (b, g)): digits
+// 2 and 3 of the k-th largest from the candidates (bin b1 holds it), so tau
+// and r as in sel_fused_kernel; then per chunk the number of scores above tau
+// (its higher-bin count plus its candidates above tau) and equal to tau, and
+// their exclusive prefixes over the chunks for step 3. Wave w walks chunks
+// w, w + 16, ... (each chunk's candidates are contiguous).
+__global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) {
+  constexpr int NW = kSelThreads / 64;
+  __shared__ uint32_t s_h[kBins2];
+  __shared__ uint32_t s_gt[kMaxSelChunks];
+  __shared__ uint32_t s_eq[kMaxSelChunks];
+  __shared__ uint32_t s_nc[kMaxSelChunks];
+  __shared__ uint32_t s_tmp[NW];
+  __shared__ int s_res[2];
+  const int64_t unit = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t k = (uint32_t)a.kk;
+  const int nch = a.n_sel_chunks;
+  const uint32_t* hist1 = a.hist + unit * kHistWords;
+  const uint32_t* cand = a.cand + unit * nch * (int64_t)kSelChunk;
+  uint32_t* counts = a.counts + unit * nch * 2;
+  for (int c = tid; c < nch; c += kSelThreads) {
+    s_gt[c] = counts[2 * c];
+    s_nc[c] = counts[2 * c + 1];
+  }
+  for (int i = tid; i < kBins2; i += kSelThreads) s_h[i] = 0u;
+  int b1, b2, b3;
+  uint32_t ab1, ab2, ab3;
+  block_find_bin_nt<kSelThreads>(hist1, kBins1, k, s_tmp, s_res, b1, ab1);   // synchronises
+  for (int c = wave; c < nch; c += NW) {
+    const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+    for (uint32_t i = lane; i < s_nc[c]; i += 64) atomicAdd(&s_h[(cc[i] >> 10) & 0x7ffu], 1u);
+  }
+  __syncthreads();
+  block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+  for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
+  __syncthreads();
+  const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+  for (int c = wave; c < nch; c += NW) {
+    const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+    for (uint32_t i = lane; i < s_nc[c]; i += 64) {
+      const uint32_t u = cc[i];
+      if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
+    }
+  }
+  __syncthreads();
+  block_find_bin_nt<kSelThreads>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  const uint32_t tau = (pre << 10) | (uint32_t)b3;
+  const uint32_t r = k - ab1 - ab2 - ab3;
+  for (int c = wave; c < nch; c += NW) {
+    const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = lane; i < s_nc[c]; i += 64) {
+      const uint32_t u = cc[i];
+      gt += u > tau ? 1u : 0u;
+      eq += u == tau ? 1u : 0u;
+    }
+    gt = wave_sum_u32(gt);
+    eq = wave_sum_u32(eq);
+    if (lane == 0) {
+      s_gt[c] += gt;
+      s_eq[c] = eq;
+    }
+  }
+  __syncthreads();
+  // exclusive prefixes over the chunks, kSelThreads chunks at a time
+  uint32_t gt_carry = 0, eq_carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += kSelThreads) {
+    const int c = c0 + tid;
+    const uint32_t g = c < nch ? s_gt[c] : 0u, e = c < nch ? s_eq[c] : 0u;
+    uint32_t gtot, etot;
+    const uint32_t gex = block_excl_scan<kSelThreads>(g, s_tmp, &gtot);
+    const uint32_t eex = block_excl_scan<kSelThreads>(e, s_tmp, &etot);
+    if (c < nch) {
+      counts[2 * c] = gt_carry + gex;
+      counts[2 * c + 1] = eq_carry + eex;
+    }
+    gt_carry += gtot;
+    eq_carry += etot;
+  }
+  if (tid == 0) {
+    a.selstate[unit * 4 + 0] = tau;
+    a.selstate[unit * 4 + 1] = r;
+  }
 }
 
 // ------------------------------------------------------------------ dec_attn
@@ -1133,22 +1192,22 @@ hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
 }
 
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
-  if (getenv("KAS_DECODE_SELECT_MULTI") == nullptr) {
+  // KAS_DECODE_SELECT=fused selects the one-workgroup-per-row kernel (also
+  // used when there are more chunks than the chunked path resolves in LDS)
+  const char* sel = getenv("KAS_DECODE_SELECT");
+  if ((sel && strcmp(sel, "fused") == 0) || a.n_sel_chunks > kMaxSelChunks) {
     ctx.begin(K_SEL_FUSED);
     KAS_LAUNCH(sel_fused_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx, a);
     return ctx.end(K_SEL_FUSED);
   }
   dim3 grid(a.n_sel_chunks, a.B * a.Hkv);
   hipError_t e;
-  ctx.begin(K_SEL_DIGIT2);
-  KAS_LAUNCH((sel_digit_kernel<2>), grid, dim3(256), ctx, a);
-  if ((e = ctx.end(K_SEL_DIGIT2)) != hipSuccess) return e;
-  ctx.begin(K_SEL_DIGIT3);
-  KAS_LAUNCH((sel_digit_kernel<3>), grid, dim3(256), ctx, a);
-  if ((e = ctx.end(K_SEL_DIGIT3)) != hipSuccess) return e;
-  ctx.begin(K_SEL_COUNT);
-  KAS_LAUNCH(sel_count_kernel, grid, dim3(256), ctx, a);
-  if ((e = ctx.end(K_SEL_COUNT)) != hipSuccess) return e;
+  ctx.begin(K_SEL_CAND);
+  KAS_LAUNCH(sel_cand_kernel, grid, dim3(256), ctx, a);
+  if ((e = ctx.end(K_SEL_CAND)) != hipSuccess) return e;
+  ctx.begin(K_SEL_RESOLVE);
+  KAS_LAUNCH(sel_resolve_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx, a);
+  if ((e = ctx.end(K_SEL_RESOLVE)) != hipSuccess) return e;
   ctx.begin(K_SEL_COMPACT);
   KAS_LAUNCH(sel_compact_kernel, grid, dim3(256), ctx, a);
   return ctx.end(K_SEL_COMPACT);

@@ -10,9 +10,8 @@ namespace kas {
 enum KernelId {
   K_DEC_SCORE = 0,
   K_DEC_POOL,
-  K_SEL_DIGIT2,
-  K_SEL_DIGIT3,
-  K_SEL_COUNT,
+  K_SEL_CAND,
+  K_SEL_RESOLVE,
   K_SEL_COMPACT,
   K_SEL_FUSED,
   K_DEC_ATTN,
@@ -48,6 +47,7 @@ struct LaunchCtx {
 constexpr int kBins1 = 2048, kBins2 = 2048, kBins3 = 1024;
 constexpr int kHistWords = kBins1 + kBins2 + kBins3;
 constexpr int kSelChunk = 4096;         // scores per selection workgroup
+constexpr int kMaxSelChunks = 4096;     // chunks the chunked selection resolves in LDS
 
 struct DecodeArgs {
   const void* q;
@@ -72,7 +72,8 @@ struct DecodeArgs {
   int64_t pstride;                  // N rounded up to 4 (16-byte aligned rows)
   uint32_t* hist;                   // [B, Hkv, kHistWords]
   uint32_t* counts;                 // [B, Hkv, n_sel_chunks, 2]
-  uint32_t* selstate;               // [B, Hkv, 4]
+  uint32_t* selstate;               // [B, Hkv, 4]: tau, r
+  uint32_t* cand;                   // [B, Hkv, n_sel_chunks, kSelChunk]: candidate score bits
   int n_sel_chunks;
   float* part_o;                    // [B, Hq, nsplit, D]
   float* part_ml;                   // [B, Hq, nsplit, 2]

@@ -36,7 +36,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 // ------------------------------------------------------------------ timing registry
 
 static const char* const kKernelNames[K_COUNT_] = {
-    "decode_score", "decode_pool", "select_digit2", "select_digit3", "select_count",
+    "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
     "prefill_select", "prefill_attn"};
 
@@ -220,7 +220,7 @@ static int decode_score_rows() {
 struct DecodePlan {
   int64_t kk;
   int score_rows, n_score_chunks, n_sel_chunks, split_rows, nsplit;
-  size_t off_logits, off_stats, off_pooled, off_hist, off_counts, off_selstate, off_part_o,
+  size_t off_logits, off_stats, off_pooled, off_hist, off_counts, off_selstate, off_cand, off_part_o,
       off_part_ml, total;
 };
 
@@ -242,6 +242,7 @@ static DecodePlan plan_decode(const Shape& s, bool anchor) {
     p.off_hist = take(units * kHistWords * sizeof(uint32_t));
     p.off_counts = take(units * p.n_sel_chunks * 2 * sizeof(uint32_t));
     p.off_selstate = take(units * 4 * sizeof(uint32_t));
+    p.off_cand = take(units * p.n_sel_chunks * kSelChunk * sizeof(uint32_t));
   }
   p.off_part_o = take((size_t)s.B * s.Hq * p.nsplit * s.D * sizeof(float));
   p.off_part_ml = take((size_t)s.B * s.Hq * p.nsplit * 2 * sizeof(float));
@@ -265,6 +266,7 @@ static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, c
     a.hist = (uint32_t*)(ws + p.off_hist);
     a.counts = (uint32_t*)(ws + p.off_counts);
     a.selstate = (uint32_t*)(ws + p.off_selstate);
+    a.cand = (uint32_t*)(ws + p.off_cand);
   }
   a.part_o = (float*)(ws + p.off_part_o);
   a.part_ml = (float*)(ws + p.off_part_ml);

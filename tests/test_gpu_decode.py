@@ -134,6 +134,35 @@ def test_exact_ties_take_lowest_indices():
     assert (oidx == np.arange(300, 400)).all()
 
 
+@pytest.mark.parametrize("case", ["random_n40000", "all_tied_n70000"])
+def test_select_paths_agree(case, monkeypatch):
+    """The chunked selection (per-chunk candidates of the first digit's bin,
+    digits 2 and 3 resolved per row) and the one-workgroup-per-row kernel
+    (KAS_DECODE_SELECT=fused) give identical index sets and outputs, equal to
+    the oracle's. With every score tied the first digit's bin holds all N
+    scores, more than the candidate list takes, so the resolve step sweeps the
+    row instead; the kept keys are then the k lowest indices."""
+    kas = _kas()
+    B, Hq, Hkv, D, pct = 1, 8, 2, 128, 10
+    N = 40000 if case.startswith("random") else 70000
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=23)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    if case.startswith("all_tied"):
+        k = torch.zeros_like(k)
+    _say(f"[decode select paths] {case}")
+    idx1, o1 = kas.decode_anchor(q, k, v, pct)
+    monkeypatch.setenv("KAS_DECODE_SELECT", "fused")
+    idx2, o2 = kas.decode_anchor(q, k, v, pct)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2) and torch.equal(o1, o2)
+    oidx, oo, _ = oracle.decode_anchor(_np(q), _np(k), _np(v), pct)
+    np.testing.assert_array_equal(idx1.cpu().numpy(), oidx)
+    assert max_abs(_np(o1), oo) <= TOL["bf16"]
+    if case.startswith("all_tied"):
+        kk = idx1.shape[-1]
+        assert (idx1.cpu().numpy() == np.arange(kk)).all()
+
+
 def test_deterministic_and_strided_cache():
     kas = _kas()
     B, Hq, Hkv, D, N, pct = 2, 32, 8, 128, 3000, 10
