@@ -38,7 +38,9 @@ def build() -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
+    # -z defs: an undefined symbol (say, a kernel whose launch stub the host
+    # pass did not emit) fails the link instead of the first dlopen
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,-z,defs", "-o", tmp, *objs]
     subprocess.check_call(cmd)
     os.replace(tmp, OUT)
     return OUT

@@ -828,6 +828,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
 // vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) left at max.
 __host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
+// Word 3 of a raw (untyped) buffer resource: 32-bit data format, which the
+// buffer unit requires to be non-zero; stride 0, so num_records counts bytes.
+constexpr int kBufWord3 = 0x00020000;
+
 // 16-byte chunk swizzles of unpadded K and V rows in LDS (64 banks of 4 B).
 // K rows are read row-per-lane, 16 lanes (16 rows) per 16-byte read phase; V
 // rows by the transposing read (4 rows x 2 chunks per 16-lane group); the XOR
@@ -860,7 +864,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
 
   const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
   const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS line bases stay scalar
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
   int ga = a.head_map ? a.head_map[g] : g;
@@ -879,8 +884,13 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = ldg16(qrow + 16 * c + 8 * hh);
   }
+  // K and V rows of this (b, g) through buffer resources: 32-bit row offsets,
+  // and the buffer unit returns zeros for any offset past the N rows
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const int nbytes = (int)((int64_t)a.N * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, kBufWord3);
   const float cs = a.scale_log2;
   const int lrow = lane / PARTS, lslot = lane % PARTS;   // this lane's row / slot in a DMA line
 
@@ -900,23 +910,32 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   };
   // DMA the K and V rows of block blk into a stage (the causal diagonal block
   // nsel reads rows tile_key0 ..; padding rows read row 0 and are masked)
-  auto issue = [&](int blk, auto set_tag, char* dst) __attribute__((always_inline)) {
+  // (STEADY: blk is a full selected block, so only the index range check remains)
+  auto issue = [&](int blk, auto set_tag, char* dst, auto steady_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
       const int i = w + G * j;
       if (EVEN || i < NINS) {
         const int r = RPI * i + lrow;
         const int jj = jr[SET][j];
-        const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
-        const int key = (blk == nsel) ? tile_key0 + r : sel;
-        const __bf16* krow = kbase + (int64_t)key * D;
-        const __bf16* vrow = vbase + (int64_t)key * D;
-        __builtin_amdgcn_global_load_lds((const void*)(krow + 8 * (lslot ^ swz_k<D>(r))),
-                                         (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (lslot ^ swz_v<D>(r))),
-                                         (__attribute__((address_space(3))) void*)(dst + BLKB + 1024 * i), 16,
-                                         0, 0);
+        int key;
+        if (STEADY) {
+          key = ((unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
+        } else {
+          const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;
+          key = (blk == nsel) ? tile_key0 + r : sel;
+        }
+        // byte offsets of the row plus this lane's swizzled 16-byte chunk
+        // (computed before the call: a function call inside the builtin's
+        // argument list makes the host pass drop the kernel's launch stub)
+        const int koff = key * ROWB + 16 * (lslot ^ swz_k<D>(r));
+        const int voff = key * ROWB + 16 * (lslot ^ swz_v<D>(r));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
+                                                 koff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dst + BLKB + 1024 * i),
+                                                 16, voff, 0, 0, 0);
       }
     }
   };
@@ -948,7 +967,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
     // lines and this step's index loads) have landed; said with the builtin
     // so the compiler does not wait for everything in flight before using them
     if (STEADY && EVEN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
-    if (STEADY || blk + 2 <= nsel) issue(blk + 2, St2{}, stage(St2{}));
+    if (STEADY || blk + 2 <= nsel) issue(blk + 2, St2{}, stage(St2{}), steady_tag);
     const char* sk = stage(st_tag);
     const char* sv = sk + BLKB;
     f32x16 acc = {};
@@ -1030,8 +1049,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   if (0 < nsel) load_index(0, St0{});
   if (1 < nsel) load_index(1, St1{});
   if (2 < nsel) load_index(2, St2c{});
-  issue(0, St0{}, s_st0);
-  if (1 <= nsel) issue(1, St1{}, s_st1);
+  issue(0, St0{}, s_st0, std::false_type{});
+  if (1 <= nsel) issue(1, St1{}, s_st1, std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
