@@ -752,8 +752,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
         const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
-        ps += p0 + p1;
         pa[e] = pack_bf16x2(p0, p1);
+        ps = add_bf16x2(pa[e], ps);      // the row sum of the bf16 weights P.V uses
       }
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
@@ -894,14 +894,20 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   const float cs = a.scale_log2;
   const int lrow = lane / PARTS, lslot = lane % PARTS;   // this lane's row / slot in a DMA line
 
-  // raw indices of this lane's rows in the wave's lines of block blk (set blk % 3)
+  // raw indices of this lane's rows in the wave's lines of block blk (set blk %
+  // 3), through a buffer resource over the tile's kt indices: positions past
+  // the end read 0 (those rows belong to the partial block and are masked)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)S, (short)0, kt * 4, kBufWord3);
   int jr[3][NIW];
   auto load_index = [&](int blk, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
       const int i = w + G * j;
-      if (EVEN || i < NINS) jr[SET][j] = S[min(blk * 32 + RPI * i + lrow, kt - 1)];
+      if (EVEN || i < NINS) {
+        const int off = 4 * (blk * 32 + RPI * i + lrow);
+        jr[SET][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+      }
     }
   };
   auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
@@ -1013,8 +1019,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
       for (int e = 0; e < 4; ++e) {
         const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
         const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
-        ps += p0 + p1;
         pa[e] = pack_bf16x2(p0, p1);
+        ps = add_bf16x2(pa[e], ps);      // the row sum of the bf16 weights P.V uses
       }
       const int R = 16 * c2 + tr_row;
       const int sw = swz_v<D>(R);                // rows R and R + 8 share it
@@ -1260,8 +1266,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_pipe_kernel(PrefillArgs a)
 #pragma unroll
       for (int k = (8 * j) / NPV; k < (8 * (j + 1)) / NPV; ++k) {
         if (k < 4) {
-          ps += pf[4 * k] + pf[4 * k + 1];
-          ps += pf[4 * k + 2] + pf[4 * k + 3];
+          ps = add_bf16x2(pa[k >> 1][2 * (k & 1)], ps);   // the row sum of the bf16 weights P.V uses
+          ps = add_bf16x2(pa[k >> 1][2 * (k & 1) + 1], ps);
         } else if (!LAST) {
           if (k == 4) {
             if (!STEADY) mask(sn, n + 1);
