@@ -567,261 +567,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(64 * G, 2) void pre_attn_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
-  constexpr int KROW = 2 * D + 16;   // bytes per K row in LDS (b128 reads across rows)
-  // bytes per V row in LDS: a stride of 64 mod 256 bytes puts the four rows and
-  // two column halves of one transposing read phase on distinct banks
-  constexpr int VROW = 2 * D + 64;
-  constexpr int NR = (32 * PARTS + NT - 1) / NT;   // 16-byte loads per thread per block, K and V each
-  __shared__ __align__(16) char s_k[2][32 * KROW];
-  __shared__ __align__(16) char s_v[2][32 * VROW];
-  __shared__ __align__(16) char s_q[G][32 * KROW];
-  __shared__ float s_x[G][32];
-
-  const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n32 = lane & 31, hh = lane >> 5;
-  const int h = g * G + w;
-  int ga = a.head_map ? a.head_map[g] : g;
-  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
-  const int o0 = a.offsets[t];
-  const int kt = a.offsets[t + 1] - o0;
-  const int32_t* S = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
-  const int nsel = (kt + 31) / 32;
-  const int tile_key0 = kTile * t;
-
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
-  // the wave's 32 query rows stay in LDS (read as the B operand every block)
-  {
-    const __bf16* qrows = (const __bf16*)a.q + qoff * D;
-#pragma unroll
-    for (int i = 0; i < 32 * PARTS / 64; ++i) {
-      const int x = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(s_q[w] + (x / PARTS) * KROW + (x % PARTS) * 16) =
-          ldg16(qrows + (x / PARTS) * D + (x % PARTS) * 8);
-    }
-  }
-  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
-  const float cs = a.scale_log2;
-
-  // Gathered rows travel global -> registers -> LDS. A ring of register sets
-  // keeps the rows of the next RING blocks in flight while one block is
-  // processed (gather latency exceeds one block time). The indices of block
-  // blk + RING + 1 are issued before the rows of block blk + RING: vector
-  // memory counters retire in issue order, so an index load issued after the
-  // prefetched rows would make its consumer wait for those rows as well.
-  // Index loads are unconditional (clamped address) so that no divergent
-  // branch sits between a load and its consumer.
-  constexpr int RING = 2;
-  constexpr bool kAllRows = (32 * PARTS) % NT == 0;   // every thread owns NR row chunks
-  u32x4 kreg[RING][NR], vreg[RING][NR];
-  int jreg[RING][NR] = {};
-  auto load_index = [&](int blk, auto slot_tag) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot_tag)::value;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int x = tid + i * NT;
-      if (kAllRows || x < 32 * PARTS) jreg[SL][i] = S[min(blk * 32 + x / PARTS, kt - 1)];
-    }
-  };
-  // Key of each row chunk of block blk; padding rows read row 0 and are
-  // masked in the softmax; the last block is the causal diagonal.
-  auto load_block = [&](int blk, auto slot_tag) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot_tag)::value;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int x = tid + i * NT;
-      if (kAllRows || x < 32 * PARTS) {
-        const int r = x / PARTS;
-        const int j = jreg[SL][i];
-        const int sel = (blk * 32 + r < kt && (unsigned)j < (unsigned)tile_key0) ? j : 0;   // trusted input, kept in bounds
-        const int key = (blk == nsel) ? tile_key0 + r : sel;
-        const int64_t row = (int64_t)key * D + (x % PARTS) * 8;
-        kreg[SL][i] = ldg16(kbase + row);
-        vreg[SL][i] = ldg16(vbase + row);
-      }
-    }
-  };
-  auto store_block = [&](int buf, auto slot_tag) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot_tag)::value;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int x = tid + i * NT;
-      if (x < 32 * PARTS) {
-        *reinterpret_cast<u32x4*>(s_k[buf] + (x / PARTS) * KROW + (x % PARTS) * 16) = kreg[SL][i];
-        *reinterpret_cast<u32x4*>(s_v[buf] + (x / PARTS) * VROW + (x % PARTS) * 16) = vreg[SL][i];
-      }
-    }
-  };
-  // P.V operand addressing: lane group g16 = lane/16 (its half hh = g16/2),
-  // member j = lane%16 supplies row 4*hh + j/4 (+8 for the upper four keys)
-  // and columns 16*(g16%2) + 4*(j%4) of each 32-wide column block.
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int tr_row = 4 * hh + (j16 >> 2);
-  const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
-
-  // Running max and row sum per query (S^T layout: the lane's query n32);
-  // the softmax scale is folded into the exponent's FMA.
-  float m_run = kNegInf, l_run = 0.f;
-  f32x16 o[NDC];
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x16{};
-
-  // One key block: S^T on MFMA, online softmax, P.V on MFMA. MODE 0: 32
-  // selected keys; 1: the last, partial selected block; 2: the causal
-  // diagonal block. The next block's rows are loaded into registers before
-  // the math and written to the other LDS buffer after it.
-  // SLOT = blk % RING: the register set that is free during this block.
-  // STEADY: both prefetches are known to be due (no branch around them, so
-  // the rows of block blk + RING stay in flight across the next step).
-  auto step = [&](int blk, auto mode_tag, auto slot_tag, auto steady_tag) __attribute__((always_inline)) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    constexpr int SLOT = decltype(slot_tag)::value;
-    constexpr bool STEADY = decltype(steady_tag)::value;
-    constexpr int NEXT = (SLOT + 1) % RING;
-    const int buf = blk & 1;
-    if (STEADY || blk + RING + 1 < nsel) load_index(blk + RING + 1, std::integral_constant<int, NEXT>{});
-    if (STEADY || blk + RING <= nsel) load_block(blk + RING, slot_tag);
-    const char* sk = s_k[buf];
-    const char* sv = s_v[buf];
-    const char* sq = s_q[w];
-    // S^T[key slot][query]; operand reads two MFMAs ahead of their use (not
-    // all hoisted: the output accumulators need the registers)
-    f32x16 acc = {};
-    u32x4 kf[3], qf[3];
-    auto rd = [&](int c, int slot) __attribute__((always_inline)) {
-      kf[slot] = *reinterpret_cast<const u32x4*>(sk + n32 * KROW + (16 * c + 8 * hh) * 2);
-      qf[slot] = *reinterpret_cast<const u32x4*>(sq + n32 * KROW + (16 * c + 8 * hh) * 2);
-    };
-    rd(0, 0);
-    rd(1, 1);
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (c + 2 < KC) rd(c + 2, (c + 2) % 3);
-      acc = mfma32(kf[c % 3], qf[c % 3], acc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (MODE != 0) {
-      const int nvalid = kt - blk * 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = mrow(r, hh);
-        const bool ok = (MODE == 2) ? (slot <= n32) : (slot < nvalid);
-        acc[r] = ok ? acc[r] : kNegInf;
-      }
-    }
-    const float bm = xor32_max(max16(acc)) * cs;   // cs > 0
-    // Every row has a valid key in block 0 (the first selected keys, or its
-    // own diagonal key), so the running max is set there while O is still
-    // zero. Later blocks keep it unless a score exceeds it by 2^8 (lazy
-    // rescale: exponentials stay <= 2^8, exact after the final division).
-    if (blk == 0) {
-      m_run = bm;
-    } else {
-      const bool bump = bm > m_run + 8.f;
-      if (__builtin_expect(__any(bump), 0)) {
-        const float m_new = bump ? bm : m_run;
-        const float alpha = exp2_fast(m_run - m_new);
-        if (hh == 0) s_x[w][n32] = alpha;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        float ar[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ar[r] = s_x[w][mrow(r, hh)];
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dc][r] *= ar[r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        l_run *= alpha;
-        m_run = m_new;
-      }
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      u32x4 pa;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
-        const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
-        pa[e] = pack_bf16x2(p0, p1);
-        ps = add_bf16x2(pa[e], ps);      // the row sum of the bf16 weights P.V uses
-      }
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        // B[k-slot (hh, e)][d = n32 + 32 dc] = V[key 16 c2 + 8 (e/4) + 4 hh + e%4][d]
-        const char* vr = sv + (16 * c2 + tr_row) * VROW + (32 * dc + tr_col) * 2;
-        const u32x2 lo = lds_read_tr16(vr);
-        const u32x2 hi = lds_read_tr16(vr + 8 * VROW);
-        const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
-        o[dc] = mfma32(pa, vb, o[dc]);
-      }
-    }
-    l_run += ps;
-    if (MODE != 2) store_block(buf ^ 1, std::integral_constant<int, NEXT>{});
-    __syncthreads();
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  // blocks 0 .. nsel (the last one is the diagonal block)
-  const int nfull = kt / 32;
-  using Tail = std::false_type;
-  auto step_any = [&](int blk, auto mode_tag) __attribute__((always_inline)) {
-    if (blk % RING == 0) step(blk, mode_tag, S0{}, Tail{});
-    else step(blk, mode_tag, S1{}, Tail{});
-  };
-  int blk = 0;
-  if (nsel > 4) {
-    // same issue order as the steady state below (indices of block 2 before
-    // the rows of block 1), so that the loop entry needs no extra wait
-    load_index(0, S0{});
-    load_block(0, S0{});
-    load_index(1, S1{});
-    load_index(2, S0{});
-    load_block(1, S1{});
-    store_block(0, S0{});
-    __syncthreads();
-    // steady state: blocks blk, blk + 1 are full and the indices of blk + 4
-    // exist (blk + 4 < nsel also gives blk + 1 < nfull)
-    for (; blk + 4 < nsel; blk += RING) {
-      step(blk, std::integral_constant<int, 0>{}, S0{}, std::true_type{});
-      step(blk + 1, std::integral_constant<int, 0>{}, S1{}, std::true_type{});
-    }
-  } else {
-    if (0 < nsel) load_index(0, S0{});
-    load_block(0, S0{});
-    if (1 < nsel) load_index(1, S1{});
-    if (1 <= nsel) load_block(1, S1{});
-    if (2 < nsel) load_index(2, S0{});
-    store_block(0, S0{});
-    __syncthreads();
-  }
-  for (; blk < nfull; ++blk) step_any(blk, std::integral_constant<int, 0>{});
-  if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
-  step_any(nsel, std::integral_constant<int, 2>{});
-  // normalise: row sums live with the query's lanes, output rows with registers
-  const float l_tot = xor32_add(l_run);
-  if (hh == 0) s_x[w][n32] = 1.0f / l_tot;
-  __syncthreads();
-  float inv[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) inv[r] = s_x[w][mrow(r, hh)];
-  uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + qoff * D;
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = f32_to_bf16_rne(o[dc][r] * inv[r]);
-}
-
 // ------------------------------------------------------------------ tile attention, LDS-DMA gathers
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vector memory only:
@@ -841,13 +586,20 @@ __device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-// Same math as pre_attn_kernel; the gathered K and V rows go from global
-// memory straight into LDS (global_load_lds_dwordx4: each lane names its own
-// row chunk, the data lands at a fixed slot of a 1 KB line) through a ring of
-// three stages, two blocks ahead of the math, so no registers hold rows in
-// flight. Q stays in registers. The stages are distinct arrays selected at
-// compile time (the steady loop is unrolled by three), so the compiler can
-// tell the stage being read from the stages being filled.
+// Sparse tile attention: one workgroup per (query tile, KV head, batch), one
+// wave per query head of the group (32 query rows each). The tile attends to
+// its selected keys (the anchor's index set for the tile, 32 keys per block)
+// and then to its own 32 keys under the causal mask (the diagonal block).
+// Per block and wave: S^T = K.Q^T on eight 32x32x16 MFMAs (K rows from LDS,
+// Q in registers), an online softmax, O += P.V on eight more MFMAs (V read
+// from LDS by transposing reads); at the end O / l in bf16.
+// The gathered K and V rows go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: each lane names its own row chunk, the data
+// lands at a fixed slot of a 1 KB line) through a ring of three stages, two
+// blocks ahead of the math, so no registers hold rows in flight. The stages
+// are distinct arrays selected at compile time (the steady loop is unrolled
+// by three), so the compiler can tell the stage being read from the stages
+// being filled.
 template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
@@ -857,6 +609,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   constexpr int NINS = 32 / RPI;            // lines per block per tensor
   constexpr int NIW = (NINS + G - 1) / G;   // lines per wave (w, w + G, ...)
   constexpr bool EVEN = NINS % G == 0;      // every wave issues NIW lines
+  constexpr float kBigP = 0x1p64f;          // half-row probability sum that triggers a rescale
   (void)NT;
   __shared__ __align__(1024) char s_st0[2 * BLKB];
   __shared__ __align__(1024) char s_st1[2 * BLKB];
@@ -991,37 +744,49 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
         acc[r] = ok ? acc[r] : kNegInf;
       }
     }
-    const float bm = xor32_max(max16(acc)) * cs;   // cs > 0
-    // lazy rescale (see pre_attn_kernel); alpha moves from the S^T layout
-    // (lane = query) to the output layout (reg r = query mrow(r, hh)) by shuffles
-    if (blk == 0) {
-      m_run = bm;
-    } else {
-      const bool bump = bm > m_run + 8.f;
-      if (__builtin_expect(__any(bump), 0)) {
-        const float m_new = bump ? bm : m_run;
-        const float alpha = exp2_fast(m_run - m_new);
+    // Online softmax with a lazy reference: m_run of a query row is the
+    // maximum of its first block, and later blocks are exponentiated against
+    // it without a maximum of their own. A row whose probabilities grow too
+    // large for the accumulators (its half-row sum above 2^64, or not finite)
+    // takes the rare path: the block maximum over both lane halves of the row,
+    // o and l rescaled by 2^(m_run - m_new), the probabilities recomputed. The
+    // reference cancels in o / l; it only has to keep the exponentials finite.
+    // (alpha moves from the S^T layout, lane = query, to the output layout,
+    // reg r = query mrow(r, hh), by shuffles.)
+    if (blk == 0) m_run = xor32_max(max16(acc)) * cs;   // cs > 0
+    u32x4 pa[2];
+    float ps;
+    auto probs = [&]() __attribute__((always_inline)) {
+      ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float ar = __shfl(alpha, mrow(r, hh));
+      for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-          for (int dc = 0; dc < NDC; ++dc) o[dc][r] *= ar;
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
+          const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
+          pa[c2][e] = pack_bf16x2(p0, p1);
+          ps = add_bf16x2(pa[c2][e], ps);      // the row sum of the bf16 weights P.V uses
         }
-        l_run *= alpha;
-        m_run = m_new;
       }
+    };
+    probs();
+    if (__builtin_expect(__any(!(ps <= kBigP)), 0)) {
+      const float bm = xor32_max(max16(acc)) * cs;
+      const bool bump = bm > m_run + 8.f;
+      const float m_new = bump ? bm : m_run;
+      const float alpha = exp2_fast(m_run - m_new);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ar = __shfl(alpha, mrow(r, hh));
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) o[dc][r] *= ar;
+      }
+      l_run *= alpha;
+      m_run = m_new;
+      probs();
     }
-    float ps = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      u32x4 pa;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
-        const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
-        pa[e] = pack_bf16x2(p0, p1);
-        ps = add_bf16x2(pa[e], ps);      // the row sum of the bf16 weights P.V uses
-      }
       const int R = 16 * c2 + tr_row;
       const int sw = swz_v<D>(R);                // rows R and R + 8 share it
 #pragma unroll
@@ -1030,7 +795,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
         const u32x2 lo = lds_read_tr16(sv + R * ROWB + cofs);
         const u32x2 hi = lds_read_tr16(sv + (R + 8) * ROWB + cofs);
         const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
-        o[dc] = mfma32(pa, vb, o[dc]);
+        o[dc] = mfma32(pa[c2], vb, o[dc]);
       }
     }
     l_run += ps;
@@ -1077,296 +842,6 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
   step_any(nsel, std::integral_constant<int, 2>{});
   // normalise: 1/l of query q lives in lane q; output rows are mrow(r, hh)
-  const float inv_l = 1.0f / xor32_add(l_run);
-  uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + qoff * D;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float inv = __shfl(inv_l, mrow(r, hh));
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = f32_to_bf16_rne(o[dc][r] * inv);
-  }
-}
-
-// ------------------------------------------------------------------ tile attention, software-pipelined
-
-// Same arithmetic as pre_attn_dma_kernel (same running-maximum decisions,
-// same bf16 probabilities, same summation order: the results are identical),
-// scheduled so that each wave always has independent matrix and vector work:
-// step n runs the Q.K^T MFMAs of block n + 1 beside the exponentials of
-// block n, then the P.V MFMAs of block n beside the row sums of block n and
-// the maximum of block n + 1. The DMA ring has four stages (block n's V, block
-// n + 1's K, block n + 2 landing, block n + 3 being issued).
-template <int D, int G>
-__global__ __launch_bounds__(64 * G, 2) void pre_attn_pipe_kernel(PrefillArgs a) {
-  constexpr int KC = D / 16, NDC = D / 32, PARTS = D / 8;
-  constexpr int ROWB = 2 * D;               // bytes per row
-  constexpr int BLKB = 32 * ROWB;           // one block of K (or V) rows
-  constexpr int RPI = 64 / PARTS;           // rows per 1 KB DMA line
-  constexpr int NINS = 32 / RPI;            // lines per block per tensor
-  constexpr int NIW = (NINS + G - 1) / G;   // lines per wave (w, w + G, ...)
-  constexpr bool EVEN = NINS % G == 0;      // every wave issues NIW lines
-  constexpr int TPM = 16 / KC;              // probability terms per Q.K^T MFMA
-  constexpr int NPV = 2 * NDC;              // P.V MFMAs per block
-  constexpr int VPS = NPV / KC;             // P.V operands read per Q.K^T slot
-  static_assert(NPV % KC == 0 && 16 % KC == 0, "slot layout");
-  __shared__ __align__(1024) char s_st0[2 * BLKB];
-  __shared__ __align__(1024) char s_st1[2 * BLKB];
-  __shared__ __align__(1024) char s_st2[2 * BLKB];
-  __shared__ __align__(1024) char s_st3[2 * BLKB];
-
-  const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n32 = lane & 31, hh = lane >> 5;
-  const int h = g * G + w;
-  int ga = a.head_map ? a.head_map[g] : g;
-  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
-  const int o0 = a.offsets[t];
-  const int kt = a.offsets[t + 1] - o0;
-  const int32_t* S = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
-  const int nsel = (kt + 31) / 32;          // selected blocks; block nsel is the causal diagonal
-  const int tile_key0 = kTile * t;
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
-  u32x4 qf[KC];   // B operand of S^T (lane: query n32, dims 16 c + 8 hh)
-  {
-    const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) qf[c] = ldg16(qrow + 16 * c + 8 * hh);
-  }
-  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
-  const float cs = a.scale_log2;
-  const int lrow = lane / PARTS, lslot = lane % PARTS;
-
-  int jr[4][NIW];   // raw indices of this lane's rows of block b in set b % 4
-  auto load_index = [&](int blk, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-#pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-      const int i = w + G * j;
-      if (EVEN || i < NINS) jr[SET][j] = S[min(blk * 32 + RPI * i + lrow, kt - 1)];
-    }
-  };
-  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
-    constexpr int ST = decltype(st_tag)::value;
-    return ST == 0 ? s_st0 : (ST == 1 ? s_st1 : (ST == 2 ? s_st2 : s_st3));
-  };
-  auto issue = [&](int blk, auto set_tag, char* dst) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-#pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-      const int i = w + G * j;
-      if (EVEN || i < NINS) {
-        const int r = RPI * i + lrow;
-        const int jj = jr[SET][j];
-        const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
-        const int key = (blk == nsel) ? tile_key0 + r : sel;
-        const __bf16* krow = kbase + (int64_t)key * D;
-        const __bf16* vrow = vbase + (int64_t)key * D;
-        __builtin_amdgcn_global_load_lds((const void*)(krow + 8 * (lslot ^ swz_k<D>(r))),
-                                         (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vrow + 8 * (lslot ^ swz_v<D>(r))),
-                                         (__attribute__((address_space(3))) void*)(dst + BLKB + 1024 * i), 16,
-                                         0, 0);
-      }
-    }
-  };
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int tr_row = 4 * hh + (j16 >> 2);
-  const int tr_q = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  const int tr_half = 8 * ((j16 & 3) & 1);
-  auto read_k1 = [&](const char* sk, int c, u32x4* kk) __attribute__((always_inline)) {
-    kk[c] = *reinterpret_cast<const u32x4*>(sk + n32 * ROWB + 16 * ((2 * c + hh) ^ swz_k<D>(n32)));
-  };
-  // V operand of P.V MFMA j (c2 = j / NDC, dc = j % NDC): two transposing reads
-  auto read_v = [&](const char* sv, int j, u32x2* lo, u32x2* hi) __attribute__((always_inline)) {
-    const int c2 = j / NDC, dc = j % NDC;
-    const int R = 16 * c2 + tr_row;
-    const int cofs = 16 * ((4 * dc + tr_q) ^ swz_v<D>(R)) + tr_half;   // rows R and R + 8 share the swizzle
-    lo[j] = lds_read_tr16(sv + R * ROWB + cofs);
-    hi[j] = lds_read_tr16(sv + (R + 8) * ROWB + cofs);
-  };
-  // scores of block blk outside the selection (partial block) or after the
-  // query (diagonal block) become -inf
-  auto mask = [&](f32x16& sc, int blk) __attribute__((always_inline)) {
-    const bool diag = blk == nsel;
-    const int nvalid = kt - blk * 32;
-    // the comparisons are made here, not hoisted out of the loop as 32 live
-    // booleans (which would not fit beside the pipeline's registers)
-    int q = n32, half = hh;
-    asm volatile("" : "+v"(q), "+v"(half));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int slot = mrow(r, half);
-      const bool ok = diag ? (slot <= q) : (slot < nvalid);
-      sc[r] = ok ? sc[r] : kNegInf;
-    }
-  };
-
-  float m_run, l_run = 0.f;
-  f32x16 o[NDC];
-#pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x16{};
-  f32x16 sc;   // masked scores of the block being finished
-
-  // Step n (stage ST = n % 4). STEADY: blocks n + 1 .. n + 4 are full selected
-  // blocks (no mask, compile-time waits); LAST: n is the diagonal, nothing follows.
-  auto step = [&](int n, auto st_tag, auto steady_tag, auto last_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
-    constexpr bool STEADY = decltype(steady_tag)::value;
-    constexpr bool LAST = decltype(last_tag)::value;
-    using SetI = std::integral_constant<int, ST>;               // (n + 4) % 4
-    using SetD = std::integral_constant<int, (ST + 3) % 4>;     // (n + 3) % 4
-    using StN = std::integral_constant<int, (ST + 1) % 4>;      // (n + 1) % 4
-    if (!LAST) {
-      if (STEADY || n + 4 < nsel) load_index(n + 4, SetI{});
-      // indices of block n + 3 (loaded a step ago) have landed
-      if (STEADY && EVEN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
-      if (STEADY || n + 3 <= nsel) issue(n + 3, SetD{}, stage(SetD{}));
-    }
-    const char* sk = stage(StN{});
-    const char* sv = stage(st_tag) + BLKB;
-    // operands are read half a chain ahead of their MFMA (KL K chunks, VL V
-    // operands in flight), which bounds the registers they occupy
-    constexpr int KL = KC / 2, VL = NPV / 2;
-    u32x4 kk[KC];
-    u32x2 vlo[NPV], vhi[NPV];
-    if (!LAST) {
-#pragma unroll
-      for (int c = 0; c < KL; ++c) read_k1(sk, c, kk);
-    }
-    // phase 1: Q.K^T of block n + 1 beside block n's exponentials
-    f32x16 sn = {};
-    float pf[16];
-    u32x4 pa[2];
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-#pragma unroll
-      for (int e = 0; e < TPM; ++e) {
-        const int i = TPM * c + e;
-        pf[i] = exp2_fast(fmaf(sc[i], cs, -m_run));            // -inf -> 0
-        if (i & 1) pa[i >> 3][(i & 7) >> 1] = pack_bf16x2(pf[i - 1], pf[i]);
-      }
-      if (!LAST && c + KL < KC) read_k1(sk, c + KL, kk);
-#pragma unroll
-      for (int v = 0; v < VPS; ++v) {
-        const int j = VPS * c + v - (NPV - VL);
-        if (j >= 0) read_v(sv, j, vlo, vhi);
-      }
-      if (!LAST) sn = mfma32(kk[c], qf[c], sn);                 // S^T[key slot][query]
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // phase 2: P.V of block n beside block n's row sums and block n + 1's maximum
-    float ps = 0.f, u = 0.f;
-    float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f, t4 = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      // work item k of 8 runs in slot k * NPV / 8
-#pragma unroll
-      for (int k = (8 * j) / NPV; k < (8 * (j + 1)) / NPV; ++k) {
-        if (k < 4) {
-          ps = add_bf16x2(pa[k >> 1][2 * (k & 1)], ps);   // the row sum of the bf16 weights P.V uses
-          ps = add_bf16x2(pa[k >> 1][2 * (k & 1) + 1], ps);
-        } else if (!LAST) {
-          if (k == 4) {
-            if (!STEADY) mask(sn, n + 1);
-            t0 = fmaxf(fmaxf(sn[0], sn[1]), sn[2]);
-            t1 = fmaxf(fmaxf(sn[3], sn[4]), sn[5]);
-          } else if (k == 5) {
-            t2 = fmaxf(fmaxf(sn[6], sn[7]), sn[8]);
-            t3 = fmaxf(fmaxf(sn[9], sn[10]), sn[11]);
-          } else if (k == 6) {
-            t4 = fmaxf(fmaxf(sn[12], sn[13]), sn[14]);
-            u = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), sn[15]));
-          } else {
-            u = xor32_max(u);
-          }
-        }
-      }
-      if (j + VL < NPV) read_v(sv, j + VL, vlo, vhi);
-      const int c2 = j / NDC, dc = j % NDC;
-      const u32x4 vb = {vlo[j][0], vlo[j][1], vhi[j][0], vhi[j][1]};
-      o[dc] = mfma32(pa[c2], vb, o[dc]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += ps;
-    if (!LAST) {
-      // lazy rescale for block n + 1, applied after block n's P.V (rare)
-      const float bm = u * cs;   // cs > 0
-      const bool bump = bm > m_run + 8.f;
-      if (__builtin_expect(__any(bump), 0)) {
-        const float m_new = bump ? bm : m_run;
-        const float alpha = exp2_fast(m_run - m_new);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float ar = __shfl(alpha, mrow(r, hh));
-#pragma unroll
-          for (int dc = 0; dc < NDC; ++dc) o[dc][r] *= ar;
-        }
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      sc = sn;
-      // block n + 2 complete in this wave, then in every wave
-      if (STEADY && EVEN) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
-  };
-  using St0 = std::integral_constant<int, 0>;
-  using St1 = std::integral_constant<int, 1>;
-  using St2 = std::integral_constant<int, 2>;
-  using St3 = std::integral_constant<int, 3>;
-  using Yes = std::true_type;
-  using No = std::false_type;
-  // prologue: indices of blocks 0..3, lines of blocks 0..2, scores and
-  // reference maximum of block 0
-  if (0 < nsel) load_index(0, St0{});
-  if (1 < nsel) load_index(1, St1{});
-  if (2 < nsel) load_index(2, St2{});
-  if (3 < nsel) load_index(3, St3{});
-  issue(0, St0{}, s_st0);
-  if (1 <= nsel) issue(1, St1{}, s_st1);
-  if (2 <= nsel) issue(2, St2{}, s_st2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  {
-    u32x4 kk[KC];
-#pragma unroll
-    for (int c = 0; c < KC; ++c) read_k1(s_st0, c, kk);
-    sc = f32x16{};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) sc = mfma32(kk[c], qf[c], sc);
-    mask(sc, 0);
-    m_run = xor32_max(max16(sc)) * cs;
-  }
-  int n = 0;
-  for (; n + 7 < nsel; n += 4) {
-    step(n, St0{}, Yes{}, No{});
-    step(n + 1, St1{}, Yes{}, No{});
-    step(n + 2, St2{}, Yes{}, No{});
-    step(n + 3, St3{}, Yes{}, No{});
-  }
-  for (; n < nsel; ++n) {
-    const int st = n & 3;
-    if (st == 0) step(n, St0{}, No{}, No{});
-    else if (st == 1) step(n, St1{}, No{}, No{});
-    else if (st == 2) step(n, St2{}, No{}, No{});
-    else step(n, St3{}, No{}, No{});
-  }
-  {
-    const int st = nsel & 3;
-    if (st == 0) step(nsel, St0{}, No{}, Yes{});
-    else if (st == 1) step(nsel, St1{}, No{}, Yes{});
-    else if (st == 2) step(nsel, St2{}, No{}, Yes{});
-    else step(nsel, St3{}, No{}, Yes{});
-  }
   const float inv_l = 1.0f / xor32_add(l_run);
   uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + qoff * D;
 #pragma unroll
@@ -1485,12 +960,7 @@ static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
 static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) {
   ctx.begin(K_PRE_ATTN);
   dim3 grid(a.T, a.Hkv, a.B);
-  // KAS_PREFILL_ATTN=regring / =pipe select the register-staged and the
-  // software-pipelined kernels (same results as the default)
-  const char* sel = getenv("KAS_PREFILL_ATTN");
-  if (sel && strcmp(sel, "regring") == 0) KAS_DISPATCH_DG(pre_attn_kernel, grid, ctx, a);
-  else if (sel && strcmp(sel, "pipe") == 0) KAS_DISPATCH_DG(pre_attn_pipe_kernel, grid, ctx, a);
-  else KAS_DISPATCH_DG(pre_attn_dma_kernel, grid, ctx, a);
+  KAS_DISPATCH_DG(pre_attn_dma_kernel, grid, ctx, a);
   return ctx.end(K_PRE_ATTN);
 }
 

@@ -174,28 +174,6 @@ def test_prefill_scores_far_above_first_block():
     _check_tiles(w, q, k, v, pct, gidx, go, range(N // 32), "far_scores")
 
 
-@pytest.mark.parametrize("variant", ["regring", "pipe"])
-@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[2], SHAPES[4]], ids=[SHAPES[1][0], SHAPES[2][0], SHAPES[4][0]])
-def test_prefill_attention_kernel_variants(shape, variant, monkeypatch):
-    """The register-staged (KAS_PREFILL_ATTN=regring) and the
-    software-pipelined (=pipe) tile attention kernels against the oracle, and
-    bit-identical to the LDS-DMA default on the same index sets (same
-    arithmetic, different staging and scheduling)."""
-    kas = _kas()
-    label, B, Hq, Hkv, D, N, pct = shape
-    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, "bf16", wid=zlib.crc32(label.encode()) % 1000,
-                        topk_pct=pct)
-    q, k, v = inputgen.layer_inputs(w, 0, DEV)
-    gidx, go = kas.prefill_anchor(q, k, v, pct)
-    monkeypatch.setenv("KAS_PREFILL_ATTN", variant)
-    gidx2, go2 = kas.prefill_anchor(q, k, v, pct)
-    torch.cuda.synchronize()
-    _say(f"[prefill {variant}] {label}: max|o_{variant} - o_default| = {max_abs(_np(go2), _np(go)):.3g}")
-    assert torch.equal(gidx, gidx2)
-    assert torch.equal(go, go2)
-    _check_tiles(w, q, k, v, pct, gidx2, go2, range(N // 32), label + " " + variant)
-
-
 def test_prefill_pooling_in_tile_ranges(monkeypatch):
     """A small pooled-score budget splits pooling and selection into many
     tile ranges; the index sets and outputs are bit-identical to one range."""
