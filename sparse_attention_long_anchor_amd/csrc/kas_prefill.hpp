@@ -31,6 +31,7 @@ struct PrefillArgs {
   float* pooled;                    // pooled rows of the current tile range
   size_t pooled_floats;             // capacity of `pooled`
   int t_begin, t_end;               // tile range of the current pool/select launch
+  int sel_cap;                      // select: largest first-digit bin resolved in LDS
 };
 
 size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);

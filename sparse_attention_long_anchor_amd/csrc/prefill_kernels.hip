@@ -18,6 +18,8 @@
 //               P.V on MFMA, online softmax over the tile's index set plus
 //               its causal diagonal block.
 #include <string.h>
+
+#include <algorithm>
 #include <type_traits>
 
 #include "kas_block.hpp"
@@ -473,14 +475,27 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------------ Top-k per tile
 
+// One workgroup per (tile, KV head): an exact radix select over the tile's
+// pooled row (n = 32 t scores, rows 128-byte aligned, so every access is a
+// whole 16-byte load): the first digit (bits 31..21) histogrammed over the
+// row; the scores of the k-th largest's bin collected into LDS in a second
+// pass, digits 2 (bits 20..10) and 3 (bits 9..0) resolved there (a bin too
+// large for LDS is histogrammed in two more passes over the row instead); a
+// last pass writes the kept keys in index order (P > tau, then the first r
+// keys equal to tau) through workgroup scans. Passes keep four 16-byte loads
+// per thread in flight (indices past the row re-read its last vector and are
+// not counted).
+constexpr int kPreSelCap = 8192;   // LDS candidates of the k-th largest's first-digit bin
 __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   __shared__ uint32_t s_h[kBins1];
+  __shared__ uint32_t s_cand[kPreSelCap];
   __shared__ uint32_t s_tmp[4];
   __shared__ int s_res[2];
+  __shared__ uint32_t s_nc;
   const int t = a.t_end - 1 - xcd_local_order(blockIdx.x, a.t_end - a.t_begin);
   const int g = blockIdx.y, b = blockIdx.z;
   if (t < 1) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = kTile * t;
   const int o0 = a.offsets[t];
   const uint32_t k = (uint32_t)(a.offsets[t + 1] - o0);
@@ -491,66 +506,124 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
     return;
   }
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + pool_slot(a, b, g, t));
-  // digit 1
+  const int n4 = n / 4;
+  // fn(v, valid) on the 16-byte vectors g0 + tid + 256 q (q < 4) of each
+  // group; every thread runs every group (the candidate appends use wave-wide
+  // scans and shuffles), and indices past the row are loaded clamped and
+  // passed as invalid
+  auto pass = [&](auto&& fn) __attribute__((always_inline)) {
+    for (int g0 = 0; g0 < n4; g0 += 4 * 256) {
+      const int i0 = g0 + tid;
+      u32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = ldg16(P + 4 * min(i0 + 256 * q, n4 - 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fn(v[q], i0 + 256 * q < n4);
+    }
+  };
   for (int i = tid; i < kBins1; i += 256) s_h[i] = 0u;
+  if (tid == 0) s_nc = 0u;
   __syncthreads();
-  for (int j = tid; j < n; j += 256) atomicAdd(&s_h[P[j] >> 21], 1u);
+  pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+    if (ok) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&s_h[v[e] >> 21], 1u);
+    }
+  });
   __syncthreads();
   int b1, b2, b3;
   uint32_t ab1, ab2, ab3;
   block_find_bin(s_h, kBins1, k, s_tmp, s_res, b1, ab1);
-  // digit 2
+  const uint32_t nb1 = s_h[b1];
+  __syncthreads();
   for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
   __syncthreads();
-  for (int j = tid; j < n; j += 256) {
-    const uint32_t u = P[j];
-    if ((u >> 21) == (uint32_t)b1) atomicAdd(&s_h[(u >> 10) & 0x7ffu], 1u);
+  if (nb1 <= (uint32_t)a.sel_cap) {
+    // the bin's scores into LDS (wave-aggregated appends), digits 2 and 3 there
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += (ok && (v[e] >> 21) == (uint32_t)b1) ? 1u : 0u;
+      const uint32_t inc = wave_incl_scan_u32(c);
+      uint32_t wbase = 0;
+      if (lane == 63 && inc) wbase = atomicAdd(&s_nc, inc);
+      wbase = __shfl(wbase, 63);
+      uint32_t pos = wbase + inc - c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 21) == (uint32_t)b1) s_cand[pos++] = v[e];
+    });
+    __syncthreads();
+    for (uint32_t i = tid; i < nb1; i += 256) atomicAdd(&s_h[(s_cand[i] >> 10) & 0x7ffu], 1u);
+    __syncthreads();
+    block_find_bin(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += 256) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    for (uint32_t i = tid; i < nb1; i += 256)
+      if ((s_cand[i] >> 10) == pre) atomicAdd(&s_h[s_cand[i] & 0x3ffu], 1u);
+    __syncthreads();
+    block_find_bin(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  } else {
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 21) == (uint32_t)b1) atomicAdd(&s_h[(v[e] >> 10) & 0x7ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += 256) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 10) == pre) atomicAdd(&s_h[v[e] & 0x3ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
   }
-  __syncthreads();
-  block_find_bin(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
-  // digit 3
-  for (int i = tid; i < kBins3; i += 256) s_h[i] = 0u;
-  __syncthreads();
-  const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-  for (int j = tid; j < n; j += 256) {
-    const uint32_t u = P[j];
-    if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
-  }
-  __syncthreads();
-  block_find_bin(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
-  const uint32_t tau = (pre << 10) | (uint32_t)b3;
+  const uint32_t tau = (((uint32_t)b1 << 11 | (uint32_t)b2) << 10) | (uint32_t)b3;
   const uint32_t r = k - ab1 - ab2 - ab3;
   // stable compaction, 16 consecutive keys per thread per 4096-key chunk
+  // (n is a multiple of 32, so a thread's 16 keys are all in or all out)
   constexpr int PER = 16;
   uint32_t gt_run = 0, eq_run = 0;
   for (int base = 0; base < n; base += 256 * PER) {
     const int j0 = base + tid * PER;
+    const bool in = j0 < n;
     uint32_t u[PER];
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 v = ldg16(P + min(j0, n - PER) + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+    }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const bool in = j0 + i < n;
-      u[i] = in ? P[j0 + i] : 0u;
-      gt += in && u[i] > tau;
-      eq += in && u[i] == tau;
+      gt += (in && u[i] > tau) ? 1u : 0u;
+      eq += (in && u[i] == tau) ? 1u : 0u;
     }
-    uint32_t tg, te;
-    uint32_t g_ex = block_excl_scan_256(gt, s_tmp, &tg) + gt_run;
-    uint32_t e_ex = block_excl_scan_256(eq, s_tmp, &te) + eq_run;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan_256((gt << 16) | eq, s_tmp, &tot);   // both below 2^16 per chunk
+    uint32_t g_ex = (ex >> 16) + gt_run;
+    uint32_t e_ex = (ex & 0xffffu) + eq_run;
+    if (in) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (j0 + i >= n) break;
-      if (u[i] > tau) {
-        const uint32_t pos = g_ex + min(e_ex, r);
-        if (pos < k) out[pos] = j0 + i;
-        ++g_ex;
-      } else if (u[i] == tau) {
-        if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = j0 + i;
-        ++e_ex;
+      for (int i = 0; i < PER; ++i) {
+        if (u[i] > tau) {
+          const uint32_t pos = g_ex + min(e_ex, r);
+          if (pos < k) out[pos] = j0 + i;
+          ++g_ex;
+        } else if (u[i] == tau) {
+          if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = j0 + i;
+          ++e_ex;
+        }
       }
     }
-    gt_run += tg;
-    eq_run += te;
+    gt_run += tot >> 16;
+    eq_run += tot & 0xffffu;
   }
 }
 
@@ -921,6 +994,10 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.kv_bstride = kv_bs; a.kv_hstride = kv_hs;
   PrefillPlan p = plan(B, Hq, Hkv, N, anchor);
+  // KAS_PREFILL_SELECT_CAP lowers the LDS candidate cap of the select (0 sends
+  // every tile through the in-place histogram passes)
+  const char* cap = getenv("KAS_PREFILL_SELECT_CAP");
+  a.sel_cap = cap ? std::min(std::max(atoi(cap), 0), kPreSelCap) : kPreSelCap;
   a.offsets = (int32_t*)(ws + p.off_offsets);
   if (anchor) {
     a.lse = (float*)(ws + p.off_lse);
