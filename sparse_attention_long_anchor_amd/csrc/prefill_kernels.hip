@@ -85,6 +85,24 @@ __device__ __forceinline__ int xcd_local_order(int j, int n) {
 
 // ------------------------------------------------------------------ K block staging
 
+// s_waitcnt immediate (gfx9 encoding) waiting for vector memory only:
+// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) left at max.
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+// Word 3 of a raw (untyped) buffer resource: 32-bit data format, which the
+// buffer unit requires to be non-zero; stride 0, so num_records counts bytes.
+constexpr int kBufWord3 = 0x00020000;
+
+// 16-byte chunk swizzles of unpadded K and V rows in LDS (64 banks of 4 B).
+// K rows are read row-per-lane, 16 lanes (16 rows) per 16-byte read phase; V
+// rows by the transposing read (4 rows x 2 chunks per 16-lane group); the XOR
+// keeps each phase on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+
 // 32 consecutive K rows: global -> registers (issued early), registers -> LDS.
 template <int D, int NT>
 struct KStage {
@@ -105,6 +123,45 @@ struct KStage {
       const int x = threadIdx.x + i * NT;
       if (x < 32 * PARTS) *reinterpret_cast<u32x4*>(s_k + (x / PARTS) * KROW + (x % PARTS) * 16) = r[i];
     }
+  }
+};
+
+// 32 consecutive K rows of one (b, g) straight into an LDS stage by DMA
+// (buffer_load_dwordx4 ... lds through a buffer resource over the slice, so
+// row offsets are 32-bit), unpadded with the 16-byte chunks swizzled per row
+// by swz_k: LDS slot (row, s) holds global chunk s ^ swz_k(row), and a reader
+// wanting chunk c of row r reads slot c ^ swz_k(r). A block is NINS 1 KB
+// lines; wave w issues lines w, w + G, ... (NIW per wave, all waves equally
+// many when EVEN).
+template <int D, int G>
+struct KDma {
+  static constexpr int ROWB = 2 * D, BLKB = 32 * ROWB, PARTS = D / 8, RPI = 64 / PARTS;
+  static constexpr int NINS = 32 / RPI, NIW = (NINS + G - 1) / G;
+  static constexpr bool EVEN = NINS % G == 0;
+  __amdgpu_buffer_rsrc_t rk;
+  int w, lrow, lslot;
+  __device__ __forceinline__ void init(const __bf16* kbase, int64_t nrows) {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)(nrows * ROWB), kBufWord3);
+    w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    lrow = lane / PARTS;
+    lslot = lane % PARTS;
+  }
+  __device__ __forceinline__ void issue(int row0, char* dst) const {
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + G * j;
+      if (EVEN || i < NINS) {
+        const int r = RPI * i + lrow;
+        const int off = (row0 + r) * ROWB + 16 * (lslot ^ swz_k<D>(r));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+  }
+  // chunk c (16 bytes) of row `row` of a staged block
+  __device__ __forceinline__ static const u32x4& read(const char* stage, int row, int c) {
+    return *reinterpret_cast<const u32x4*>(stage + row * ROWB + 16 * (c ^ swz_k<D>(row)));
   }
 };
 
@@ -141,9 +198,13 @@ __device__ __forceinline__ void row_stats_update(const f32x16& acc, bool diag, i
 // wave w = query head g*G + w; each staged K block feeds both tiles.
 template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16;
-  using KS = KStage<D, NT>;
-  __shared__ __align__(16) char s_k[2][32 * KS::KROW];
+  constexpr int KC = D / 16;
+  using KD = KDma<D, G>;
+  // three K stages, filled two blocks ahead (distinct arrays, so the
+  // compiler tells the stage being read from the stage being filled)
+  __shared__ __align__(1024) char s_k0[KD::BLKB];
+  __shared__ __align__(1024) char s_k1[KD::BLKB];
+  __shared__ __align__(1024) char s_k2[KD::BLKB];
   const int npairs = (a.T + 1) / 2;
   const int p = npairs - 1 - xcd_local_order(blockIdx.x, npairs);
   const int t0 = 2 * p, t1 = 2 * p + 1;
@@ -163,7 +224,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   }
   const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
-  KS st[2];   // K(j) travels in register set j & 1, loaded two blocks before it is staged
+  KD kd;
+  kd.init(kbase, a.N);
   // Row sums against a lazy reference: each lane keeps a base-2 offset mr
   // (the maximum of its first block) and adds exp2(x - mr) of every later
   // score; the terms stay below 2^64 unless a score exceeds mr by 64, and
@@ -179,11 +241,14 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     for (int c = 0; c < KC; ++c) acc = mfma32(ka[c], qb[c], acc);   // S^T[key][query]
     return acc;
   };
-  auto read_k = [&](int kb, u32x4* ka) __attribute__((always_inline)) {
-    const char* sk = s_k[kb & 1];
+  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
+    constexpr int ST = decltype(st_tag)::value;
+    return ST == 0 ? s_k0 : (ST == 1 ? s_k1 : s_k2);
+  };
+  auto read_k = [&](auto st_tag, u32x4* ka) __attribute__((always_inline)) {
+    const char* sk = stage(st_tag);
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+    for (int c = 0; c < KC; ++c) ka[c] = KD::read(sk, n32, 2 * c + hh);
   };
   // masked score (diagonal block: keys after the query row are excluded)
   auto val = [&](const f32x16& acc, int r, bool diag) __attribute__((always_inline)) -> float {
@@ -230,25 +295,38 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     }
     l += s;
   };
-  // Stage K(kb+1) (in register set (kb+1) & 1 since two blocks ago) and start
-  // loading K(kb+3) into the same set. SET = (kb+1) & 1 is compile-time so the
-  // two sets keep their registers (a runtime index would force copies, and a
-  // copy of a register with a load in flight waits for the load).
-  auto advance = [&](int kb, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (kb + 1 <= tl) st[SET].store(s_k[(kb + 1) & 1]);
-    if (kb + 3 <= tl) st[SET].load(kbase, (int64_t)kTile * (kb + 3));
-    __syncthreads();
+  // Block kb is in stage kb % 3 (ST). Before its math: the DMA of block
+  // kb + 2 into stage (ST + 2) % 3 (block kb - 1's, released by the last
+  // barrier). After it: block kb + 1 has landed in this wave (only the lines
+  // just issued may still be in flight; said with the builtin wait, which the
+  // compiler's own wait placement sees), then a barrier without a fence (the
+  // block's LDS reads were consumed by its MFMAs).
+  // (STEADY: block kb + 2 exists, so the DMA and the partial wait need no test)
+  auto begin = [&](int kb, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
+    using S2 = std::integral_constant<int, (decltype(st_tag)::value + 2) % 3>;
+    if (decltype(steady_tag)::value || kb + 2 <= tl) kd.issue(kTile * (kb + 2), stage(S2{}));
   };
-  auto advance_rt = [&](int kb) __attribute__((always_inline)) {
-    if ((kb + 1) & 1) advance(kb, std::integral_constant<int, 1>{});
-    else advance(kb, std::integral_constant<int, 0>{});
+  auto end = [&](int kb, auto steady_tag) __attribute__((always_inline)) {
+    if (KD::EVEN && (decltype(steady_tag)::value || kb + 2 <= tl)) __builtin_amdgcn_s_waitcnt(vmcnt_imm(KD::NIW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
-  st[0].load(kbase, 0);
-  st[0].store(s_k[0]);
-  if (tl >= 1) st[1].load(kbase, kTile);
-  if (tl >= 2) st[0].load(kbase, 2 * kTile);
-  __syncthreads();
+  using St0 = std::integral_constant<int, 0>;
+  using St1 = std::integral_constant<int, 1>;
+  using St2 = std::integral_constant<int, 2>;
+  // fn(st_tag) with the stage of block kb named at compile time
+  auto on_stage = [&](int kb, auto&& fn) __attribute__((always_inline)) {
+    const int st = kb % 3;
+    if (st == 0) fn(St0{});
+    else if (st == 1) fn(St1{});
+    else fn(St2{});
+  };
+  kd.issue(0, s_k0);
+  if (tl >= 1) kd.issue(kTile, s_k1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   u32x4 ka[KC];
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -258,9 +336,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     // runs beside tile 0's MFMA chain, tile 0's update beside tile 1's chain.
     // FIRST: block 0 (references set, no previous tile-1 block); DIAG0: block
     // t0 is tile 0's diagonal.
-    auto iter = [&](int kb, auto first_tag, auto diag0_tag, auto set_tag) __attribute__((always_inline)) {
+    auto iter = [&](int kb, auto first_tag, auto diag0_tag, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value, DIAG0 = decltype(diag0_tag)::value;
-      read_k(kb, ka);
+      begin(kb, st_tag, steady_tag);
+      read_k(st_tag, ka);
       float s1 = 0.f, s0 = 0.f;
       const f32x16 acc0 = FIRST ? chain(ka, qb0) : chain_terms(ka, qb0, acc1, false, mr1, s1);
       if (FIRST) mr0 = block_max(acc0, DIAG0);
@@ -272,24 +351,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
       else settle(acc0, DIAG0, s0, mr0, l0);
       acc1 = acc1n;
       if (FIRST) mr1 = block_max(acc1, false);
-      advance(kb, set_tag);
+      end(kb, steady_tag);
     };
-    using Set0 = std::integral_constant<int, 0>;
-    using Set1 = std::integral_constant<int, 1>;
     if (t0 == 0) {
-      iter(0, T_{}, T_{}, Set1{});
+      iter(0, T_{}, T_{}, St0{}, F_{});
     } else {
-      iter(0, T_{}, F_{}, Set1{});
+      iter(0, T_{}, F_{}, St0{}, F_{});
       int kb = 1;
-      for (; kb + 1 < t0; kb += 2) {          // kb odd: set (kb+1)&1 = 0
-        iter(kb, F_{}, F_{}, Set0{});
-        iter(kb + 1, F_{}, F_{}, Set1{});
+      for (; kb + 2 < t0; kb += 3) {          // kb = 1 (mod 3); blocks up to kb + 4 <= t1 exist
+        iter(kb, F_{}, F_{}, St1{}, T_{});
+        iter(kb + 1, F_{}, F_{}, St2{}, T_{});
+        iter(kb + 2, F_{}, F_{}, St0{}, T_{});
       }
-      if (kb < t0) iter(kb, F_{}, F_{}, Set0{});
-      if ((t0 + 1) & 1) iter(t0, F_{}, T_{}, Set1{});
-      else iter(t0, F_{}, T_{}, Set0{});
+      for (; kb < t0; ++kb) on_stage(kb, [&](auto st) __attribute__((always_inline)) { iter(kb, F_{}, F_{}, st, F_{}); });
+      on_stage(t0, [&](auto st) __attribute__((always_inline)) { iter(t0, F_{}, T_{}, st, F_{}); });
     }
-    read_k(t1, ka);
+    on_stage(t1, [&](auto st) __attribute__((always_inline)) { read_k(st, ka); });
     const f32x16 acc1n = chain(ka, qb1);
     const float s1 = terms(acc1, false, mr1);
     settle(acc1, false, s1, mr1, l1);
@@ -297,7 +374,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     settle(acc1n, true, s1n, mr1, l1);
   } else {
     for (int kb = 0; kb <= t0; ++kb) {
-      read_k(kb, ka);
+      on_stage(kb, [&](auto st) __attribute__((always_inline)) {
+        begin(kb, st, F_{});
+        read_k(st, ka);
+      });
       const f32x16 acc0 = chain(ka, qb0);
       const bool diag = kb == t0;
       if (kb == 0) {
@@ -306,7 +386,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
       } else {
         settle(acc0, diag, terms(acc0, diag, mr0), mr0, l0);
       }
-      if (kb < t0) advance_rt(kb);
+      if (kb < t0) end(kb, F_{});
     }
   }
   // merge the two lane halves (different keys of the same query row);
@@ -642,22 +722,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 
 // ------------------------------------------------------------------ tile attention, LDS-DMA gathers
 
-// s_waitcnt immediate (gfx9 encoding) waiting for vector memory only:
-// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) left at max.
-__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
-
-// Word 3 of a raw (untyped) buffer resource: 32-bit data format, which the
-// buffer unit requires to be non-zero; stride 0, so num_records counts bytes.
-constexpr int kBufWord3 = 0x00020000;
-
-// 16-byte chunk swizzles of unpadded K and V rows in LDS (64 banks of 4 B).
-// K rows are read row-per-lane, 16 lanes (16 rows) per 16-byte read phase; V
-// rows by the transposing read (4 rows x 2 chunks per 16-lane group); the XOR
-// keeps each phase on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 // Sparse tile attention: one workgroup per (query tile, KV head, batch), one
 // wave per query head of the group (32 query rows each). The tile attends to
