@@ -88,6 +88,8 @@ __device__ __forceinline__ int xcd_local_order(int j, int n) {
 // s_waitcnt immediate (gfx9 encoding) waiting for vector memory only:
 // vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) left at max.
 __host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+// the same with lgkmcnt 0 as well (LDS stores done)
+__host__ __device__ constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~0x0F00; }
 
 // Word 3 of a raw (untyped) buffer resource: 32-bit data format, which the
 // buffer unit requires to be non-zero; stride 0, so num_records counts bytes.
@@ -102,29 +104,6 @@ __device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-
-// 32 consecutive K rows: global -> registers (issued early), registers -> LDS.
-template <int D, int NT>
-struct KStage {
-  static constexpr int PARTS = D / 8;
-  static constexpr int KROW = 2 * D + 16;   // padded LDS row (bytes)
-  static constexpr int NK = (32 * PARTS + NT - 1) / NT;
-  u32x4 r[NK];
-  __device__ __forceinline__ void load(const __bf16* kbase, int64_t row0) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int x = threadIdx.x + i * NT;
-      if (x < 32 * PARTS) r[i] = ldg16(kbase + (row0 + x / PARTS) * D + (x % PARTS) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(char* s_k) const {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int x = threadIdx.x + i * NT;
-      if (x < 32 * PARTS) *reinterpret_cast<u32x4*>(s_k + (x / PARTS) * KROW + (x % PARTS) * 16) = r[i];
-    }
-  }
-};
 
 // 32 consecutive K rows of one (b, g) straight into an LDS stage by DMA
 // (buffer_load_dwordx4 ... lds through a buffer resource over the slice, so
@@ -409,9 +388,12 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 // waves' sums are added through LDS (double-buffered, one barrier per block).
 template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * G, KC = D / 16;
-  using KS = KStage<D, NT>;
-  __shared__ __align__(16) char s_k[2][32 * KS::KROW];
+  constexpr int KC = D / 16;
+  using KD = KDma<D, G>;
+  // three K stages, filled two blocks ahead (as in the statistics pass)
+  __shared__ __align__(1024) char s_k0[KD::BLKB];
+  __shared__ __align__(1024) char s_k1[KD::BLKB];
+  __shared__ __align__(1024) char s_k2[KD::BLKB];
   __shared__ float s_col[2][2][G][64];
   const int pa0 = a.t_begin / 2;
   const int npairs = (a.t_end + 1) / 2 - pa0;
@@ -443,18 +425,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   float* out0 = a.pooled + pool_slot(a, b, g, t0);
   float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
-  KS st[2];   // K(j) travels in register set j & 1, loaded two blocks before it is staged
+  KD kd;
+  kd.init(kbase, a.N);
   auto chain = [&](const u32x4* ka, const u32x4* qa) __attribute__((always_inline)) {
     f32x16 acc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c) acc = mfma32(qa[c], ka[c], acc);   // S[query][key]
     return acc;
   };
-  auto read_k = [&](int kb, u32x4* ka) __attribute__((always_inline)) {
-    const char* sk = s_k[kb & 1];
+  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
+    constexpr int ST = decltype(st_tag)::value;
+    return ST == 0 ? s_k0 : (ST == 1 ? s_k1 : s_k2);
+  };
+  auto read_k = [&](auto st_tag, u32x4* ka) __attribute__((always_inline)) {
+    const char* sk = stage(st_tag);
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      ka[c] = *reinterpret_cast<const u32x4*>(sk + n32 * KS::KROW + (16 * c + 8 * hh) * 2);
+    for (int c = 0; c < KC; ++c) ka[c] = KD::read(sk, n32, 2 * c + hh);
   };
   // Column sums of one tile-block over the wave's 32 query rows; both lane
   // halves store their (equal) copy, so no lane branch splits the block.
@@ -484,19 +470,29 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     dst[lane] = col;
     return acc;
   };
-  // Stage K(kb+1) from register set (kb+1) & 1 and start loading K(kb+3)
-  // into it (compile-time set: see the statistics pass).
-  auto advance = [&](int kb, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (kb + 1 < nkb) st[SET].store(s_k[(kb + 1) & 1]);
-    if (kb + 3 < nkb) st[SET].load(kbase, (int64_t)kTile * (kb + 3));
-    __syncthreads();
+  // Block kb is in stage kb % 3 (ST): the DMA of block kb + 2 before its
+  // math, and after it block kb + 1 landed and the column sums in LDS, then
+  // a barrier without a fence (STEADY: block kb + 2 exists).
+  auto begin = [&](int kb, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
+    using S2 = std::integral_constant<int, (decltype(st_tag)::value + 2) % 3>;
+    if (decltype(steady_tag)::value || kb + 2 < nkb) kd.issue(kTile * (kb + 2), stage(S2{}));
   };
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  auto advance_rt = [&](int kb) __attribute__((always_inline)) {
-    if ((kb + 1) & 1) advance(kb, Set1{});
-    else advance(kb, Set0{});
+  auto end = [&](int kb, auto steady_tag) __attribute__((always_inline)) {
+    if (KD::EVEN && (decltype(steady_tag)::value || kb + 2 < nkb))
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(KD::NIW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  using St0 = std::integral_constant<int, 0>;
+  using St1 = std::integral_constant<int, 1>;
+  using St2 = std::integral_constant<int, 2>;
+  auto on_stage = [&](int kb, auto&& fn) __attribute__((always_inline)) {
+    const int st = kb % 3;
+    if (st == 0) fn(St0{});
+    else if (st == 1) fn(St1{});
+    else fn(St2{});
   };
   // Sum the G heads' column sums of (tile, block) and write them out.
   auto emit = [&](int tile, int kb, int writer_wave) __attribute__((always_inline)) {
@@ -508,34 +504,38 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     }
   };
   const int w1 = G > 1 ? 1 : 0;
-  st[0].load(kbase, 0);
-  st[0].store(s_k[0]);
-  if (nkb > 1) st[1].load(kbase, kTile);
-  if (nkb > 2) st[0].load(kbase, 2 * kTile);
-  __syncthreads();
+  kd.issue(0, s_k0);
+  if (nkb > 1) kd.issue(kTile, s_k1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   u32x4 ka[KC];
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (has1) {
     f32x16 acc1 = {};
-    auto iter = [&](int kb, auto first_tag, auto set_tag) __attribute__((always_inline)) {
+    auto iter = [&](int kb, auto first_tag, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      read_k(kb, ka);
+      begin(kb, st_tag, steady_tag);
+      read_k(st_tag, ka);
       const f32x16 acc0 = FIRST ? chain(ka, qa0) : chain_cols(ka, qa0, acc1, lse1, s_col[(kb - 1) & 1][1][w]);
       acc1 = chain_cols(ka, qa1, acc0, lse0, s_col[kb & 1][0][w]);
-      advance(kb, set_tag);
+      end(kb, steady_tag);
       emit(0, kb, 0);
       if (!FIRST) emit(1, kb - 1, w1);
     };
     if (t0 > 0) {
-      iter(0, std::true_type{}, Set1{});
+      iter(0, T_{}, St0{}, F_{});
       int kb = 1;
-      for (; kb + 1 < t0; kb += 2) {          // kb odd: set (kb+1)&1 = 0
-        iter(kb, std::false_type{}, Set0{});
-        iter(kb + 1, std::false_type{}, Set1{});
+      for (; kb + 3 < t0; kb += 3) {          // kb = 1 (mod 3); blocks up to kb + 4 <= t0 exist
+        iter(kb, F_{}, St1{}, T_{});
+        iter(kb + 1, F_{}, St2{}, T_{});
+        iter(kb + 2, F_{}, St0{}, T_{});
       }
-      if (kb < t0) iter(kb, std::false_type{}, Set0{});
+      for (; kb < t0; ++kb) on_stage(kb, [&](auto st) __attribute__((always_inline)) { iter(kb, F_{}, st, F_{}); });
     }
     // block t0 is a candidate of tile 1 only
-    read_k(t0, ka);
+    on_stage(t0, [&](auto st) __attribute__((always_inline)) { read_k(st, ka); });
     const f32x16 acc1n = chain(ka, qa1);
     if (t0 > 0) colsum(acc1, lse1, s_col[(t0 - 1) & 1][1][w]);
     colsum(acc1n, lse1, s_col[t0 & 1][1][w]);
@@ -544,10 +544,13 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     emit(1, t0, w1);
   } else {
     for (int kb = 0; kb < t0; ++kb) {
-      read_k(kb, ka);
+      on_stage(kb, [&](auto st) __attribute__((always_inline)) {
+        begin(kb, st, F_{});
+        read_k(st, ka);
+      });
       const f32x16 acc0 = chain(ka, qa0);
       colsum(acc0, lse0, s_col[kb & 1][0][w]);
-      advance_rt(kb);
+      end(kb, F_{});
       emit(0, kb, 0);
     }
   }
