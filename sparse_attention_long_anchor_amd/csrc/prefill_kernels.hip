@@ -735,10 +735,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // from LDS by transposing reads); at the end O / l in bf16.
 // The gathered K and V rows go from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane names its own row chunk, the data
-// lands at a fixed slot of a 1 KB line) through a ring of three stages, two
+// lands at a fixed slot of a 1 KB line) through a ring of four stages, three
 // blocks ahead of the math, so no registers hold rows in flight. The stages
 // are distinct arrays selected at compile time (the steady loop is unrolled
-// by three), so the compiler can tell the stage being read from the stages
+// by four), so the compiler can tell the stage being read from the stages
 // being filled.
 template <int D, int G>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) {
@@ -754,6 +754,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   __shared__ __align__(1024) char s_st0[2 * BLKB];
   __shared__ __align__(1024) char s_st1[2 * BLKB];
   __shared__ __align__(1024) char s_st2[2 * BLKB];
+  __shared__ __align__(1024) char s_st3[2 * BLKB];
 
   const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
   const int g = blockIdx.y, b = blockIdx.z;
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   // 3), through a buffer resource over the tile's kt indices: positions past
   // the end read 0 (those rows belong to the partial block and are masked)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)S, (short)0, kt * 4, kBufWord3);
-  int jr[3][NIW];
+  int jr[4][NIW];
   auto load_index = [&](int blk, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
 #pragma unroll
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   };
   auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
     constexpr int ST = decltype(st_tag)::value;
-    return ST == 0 ? s_st0 : (ST == 1 ? s_st1 : s_st2);
+    return ST == 0 ? s_st0 : (ST == 1 ? s_st1 : (ST == 2 ? s_st2 : s_st3));
   };
   // DMA the K and V rows of block blk into a stage (the causal diagonal block
   // nsel reads rows tile_key0 ..; padding rows read row 0 and are masked)
@@ -851,22 +852,24 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
 #pragma unroll
   for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x16{};
 
-  // One key block on stage ST (MODE 0: full selected block; 1: the partial
-  // last one; 2: the causal diagonal). Before the math: indices of block
-  // blk + 3 and the DMA of block blk + 2 (into stage (ST + 2) % 3). After it:
-  // block blk + 1's lines complete in every wave, then a barrier.
+  // One key block on stage ST = blk % 4 (MODE 0: full selected block; 1: the
+  // partial last one; 2: the causal diagonal). Before the math: indices of
+  // block blk + 4 (into set ST, free since block blk's lines were issued) and
+  // the DMA of block blk + 3 (into stage (ST + 3) % 4, block blk - 1's,
+  // released by the last barrier). After it: block blk + 1's lines complete in
+  // every wave, then a barrier.
   auto step = [&](int blk, auto mode_tag, auto st_tag, auto steady_tag) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
-    using SetN = std::integral_constant<int, ST>;             // (blk + 3) % 3
-    using St2 = std::integral_constant<int, (ST + 2) % 3>;    // (blk + 2) % 3
-    if (STEADY || blk + 3 < nsel) load_index(blk + 3, SetN{});
-    // the indices of block blk + 2 (loaded a step ago, before block blk + 1's
+    using SetN = std::integral_constant<int, ST>;             // (blk + 4) % 4
+    using St2 = std::integral_constant<int, (ST + 3) % 4>;    // (blk + 3) % 4
+    if (STEADY || blk + 4 < nsel) load_index(blk + 4, SetN{});
+    // the indices of block blk + 3 (loaded a step ago, before block blk + 2's
     // lines and this step's index loads) have landed; said with the builtin
     // so the compiler does not wait for everything in flight before using them
     if (STEADY && EVEN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
-    if (STEADY || blk + 2 <= nsel) issue(blk + 2, St2{}, stage(St2{}), steady_tag);
+    if (STEADY || blk + 3 <= nsel) issue(blk + 3, St2{}, stage(St2{}), steady_tag);
     const char* sk = stage(st_tag);
     const char* sv = sk + BLKB;
     f32x16 acc = {};
@@ -939,12 +942,13 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
       }
     }
     l_run += ps;
-    // block blk + 1 complete in this wave (steady: only this step's index
-    // loads and DMA lines may still be in flight), then in every wave
+    // block blk + 1 complete in this wave (steady: only the index loads and
+    // DMA lines of this step and the last one may still be in flight), then
+    // in every wave
     // (the builtin wait, unlike inline asm, is seen by the compiler's own
     // wait placement, which then knows these lines have landed)
     if (STEADY && EVEN) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * NIW));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -954,29 +958,34 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
   using St2c = std::integral_constant<int, 2>;
+  using St3c = std::integral_constant<int, 3>;
   using Steady = std::true_type;
   using Tail = std::false_type;
-  // prologue: indices of blocks 0..2, lines of blocks 0 and 1
+  // prologue: indices of blocks 0..3, lines of blocks 0..2
   if (0 < nsel) load_index(0, St0{});
   if (1 < nsel) load_index(1, St1{});
   if (2 < nsel) load_index(2, St2c{});
+  if (3 < nsel) load_index(3, St3c{});
   issue(0, St0{}, s_st0, std::false_type{});
   if (1 <= nsel) issue(1, St1{}, s_st1, std::false_type{});
+  if (2 <= nsel) issue(2, St2c{}, s_st2, std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   int blk = 0;
-  // steady state: blocks blk .. blk + 2 full, indices of blk + 5 exist
-  for (; blk + 5 < nsel; blk += 3) {
+  // steady state: blocks blk .. blk + 3 full, indices of blk + 7 exist
+  for (; blk + 7 < nsel; blk += 4) {
     step(blk, std::integral_constant<int, 0>{}, St0{}, Steady{});
     step(blk + 1, std::integral_constant<int, 0>{}, St1{}, Steady{});
     step(blk + 2, std::integral_constant<int, 0>{}, St2c{}, Steady{});
+    step(blk + 3, std::integral_constant<int, 0>{}, St3c{}, Steady{});
   }
   auto step_any = [&](int bk, auto mode_tag) __attribute__((always_inline)) {
-    const int st = bk % 3;
+    const int st = bk & 3;
     if (st == 0) step(bk, mode_tag, St0{}, Tail{});
     else if (st == 1) step(bk, mode_tag, St1{}, Tail{});
-    else step(bk, mode_tag, St2c{}, Tail{});
+    else if (st == 2) step(bk, mode_tag, St2c{}, Tail{});
+    else step(bk, mode_tag, St3c{}, Tail{});
   };
   for (; blk < nfull; ++blk) step_any(blk, std::integral_constant<int, 0>{});
   if (nsel > nfull) step_any(nfull, std::integral_constant<int, 1>{});
