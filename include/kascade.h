@@ -118,7 +118,9 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
  * are summed over the tile's rows and the group's heads; the exact Top-k_t
  * is tile t's set. Row i of tile t then attends over that set plus its causal
  * diagonal keys [tile*t, i]. idx_out: [B, Hkv, total] CSR; o: [B, Hq, N, D].
- * bf16 only. */
+ * bf16 only. KAS_ERR_UNSUPPORTED when the index set of one KV head would
+ * exceed 2^31 - 1 entries (total; about N > 1.17M at 10 %) or a KV head's
+ * slice of k or v reaches 2^31 bytes (N * D * 2). */
 kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k,
                                 const void* v, int32_t* idx_out, void* o,
                                 void* ws, size_t ws_bytes, void* stream);
@@ -127,7 +129,8 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
  * tile t for anchor KV head head_map[g] plus the causal diagonal keys.
  * anchor_idx: [B, anchor_kv_heads, total] CSR from kas_prefill_anchor with the
  * same N, tile and pct; every index of tile t must be < tile*t (trusted on
- * the device). head_map as in kas_decode_reuse. bf16 only. */
+ * the device). head_map as in kas_decode_reuse. bf16 only. The size limits
+ * of kas_prefill_anchor apply. */
 kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void* k,
                                const void* v, const int32_t* anchor_idx,
                                int32_t anchor_kv_heads, const int32_t* head_map, void* o,

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -280,6 +281,18 @@ static kas_status_t check_ws(void* ws, size_t ws_bytes, size_t need) {
   return KAS_OK;
 }
 
+// The prefill kernels keep CSR offsets and index positions in 32 bits and
+// address a KV head's rows through 32-bit byte offsets.
+static kas_status_t check_prefill_limits(const Shape& s, int64_t total) {
+  if (total > INT32_MAX)
+    return fail(KAS_ERR_UNSUPPORTED, "prefill index set of %lld entries per KV head exceeds 2^31 - 1",
+                (long long)total);
+  if (s.N * 2 * s.D > INT32_MAX)
+    return fail(KAS_ERR_UNSUPPORTED, "prefill KV head slice of %lld bytes reaches 2^31",
+                (long long)(s.N * 2 * s.D));
+  return KAS_OK;
+}
+
 static kas_status_t hip_fail(hipError_t e, const char* where) {
   return fail(KAS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
@@ -388,6 +401,7 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
   if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
   int64_t total = 0;
   if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
+  if ((st = check_prefill_limits(s, total))) return st;
   size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, true);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   PrefillArgs a;
@@ -416,6 +430,7 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
     return fail(KAS_ERR_INVALID_ARGUMENT, "identity head map needs anchor_kv_heads == n_kv_heads");
   int64_t total = 0;
   if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
+  if ((st = check_prefill_limits(s, total))) return st;
   size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, false);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   PrefillArgs a;

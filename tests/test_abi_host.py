@@ -97,6 +97,13 @@ def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
     assert r == 1 and b"identity head map" in L.kas_last_error()
     r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, None, 2, None, fake, fake, 1 << 30, None)
     assert r == 1
+    # prefill sizes past the 32-bit CSR offsets / row offsets: rejected
+    # before anything is launched
+    dbig = b.make_desc(1, 8, 2, 128, 2_000_000, 10, torch.bfloat16)
+    r = L.kas_prefill_anchor(ctypes.byref(dbig), fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert r == 2 and b"2^31" in L.kas_last_error()
+    r = L.kas_prefill_reuse(ctypes.byref(dbig), fake, fake, fake, fake, 2, None, fake, fake, 1 << 40, None)
+    assert r == 2
     dp = b.make_desc(1, 8, 2, 64, 96, 10, torch.float32)
     r = L.kas_prefill_anchor(ctypes.byref(dp), fake, fake, fake, fake, fake, fake, 1 << 30, None)
     assert r == 2
