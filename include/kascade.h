@@ -55,13 +55,15 @@ typedef enum {
   KAS_OP_DECODE_ANCHOR = 0,
   KAS_OP_DECODE_REUSE = 1,
   KAS_OP_PREFILL_ANCHOR = 2,
-  KAS_OP_PREFILL_REUSE = 3
+  KAS_OP_PREFILL_REUSE = 3,
+  KAS_OP_DECODE_DENSE = 4,
+  KAS_OP_PREFILL_DENSE = 5
 } kas_op_t;
 
 /* Problem description shared by all calls of one layer. */
 typedef struct kas_desc {
   int32_t batch;        /* B >= 1 */
-  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads, Hq / Hkv <= 16 */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads; Hq / Hkv in {1, 2, 4, 8} */
   int32_t n_kv_heads;   /* Hkv >= 1 */
   int32_t head_dim;     /* D in {64, 128} */
   int64_t seq_len;      /* decode: keys in the cache (the new token's key
@@ -135,6 +137,28 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
                                const void* v, const int32_t* anchor_idx,
                                int32_t anchor_kv_heads, const int32_t* head_map, void* o,
                                void* ws, size_t ws_bytes, void* stream);
+
+/* Dense baselines. The pages state Kascade's speed-ups against dense
+ * attention (README "Abstract": a FlashAttention-3 baseline; its benchmarks
+ * run FlashAttention-3 code). These calls compute that dense attention with
+ * this library's own kernels, for comparison at the same shapes: the textbook
+ * softmax(Q K^T * scale) V ("I/O complexity of attention" abstract).
+ * topk_pct is not used (it must still be in range); head_map and index sets
+ * do not exist here.
+ *
+ * Decode: o[b, h] = attention of query head h over all N keys of KV head
+ * h / G (split-K over the cache, then a merge of the splits). Layouts as in
+ * kas_decode_anchor; F32 or BF16; workspace from
+ * kas_workspace_size(KAS_OP_DECODE_DENSE). */
+kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                              void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill: causal attention, row i over keys [0, i]. Layouts as in
+ * kas_prefill_anchor; bf16 only; N a multiple of the tile (32). Needs no
+ * workspace (ws may be NULL; kas_workspace_size(KAS_OP_PREFILL_DENSE) is 0).
+ * KAS_ERR_UNSUPPORTED when a KV head's slice of k or v reaches 2^31 bytes. */
+kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                               void* o, void* ws, size_t ws_bytes, void* stream);
 
 const char* kas_status_string(kas_status_t status);
 /* Text of the last failure on the calling thread ("" if none). */

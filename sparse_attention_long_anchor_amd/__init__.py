@@ -9,11 +9,13 @@ raises.
 from .binding import (  # noqa: F401
     KasError,
     decode_anchor,
+    decode_dense,
     decode_k,
     decode_reuse,
     lib_path,
     make_desc,
     prefill_anchor,
+    prefill_dense,
     prefill_offsets,
     prefill_reuse,
     profile_enable,
@@ -26,6 +28,8 @@ from .binding import (  # noqa: F401
     OP_DECODE_REUSE,
     OP_PREFILL_ANCHOR,
     OP_PREFILL_REUSE,
+    OP_DECODE_DENSE,
+    OP_PREFILL_DENSE,
 )
 from .binding import _load as _load_library
 

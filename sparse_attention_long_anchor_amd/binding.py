@@ -1,7 +1,8 @@
 """ctypes binding of libkascade_mi355x.so (argument marshalling only).
 
 Names follow the C ABI (include/kascade.h): decode_anchor, decode_reuse,
-prefill_anchor, prefill_reuse, topk_count, prefill_offsets, workspace_size.
+prefill_anchor, prefill_reuse, decode_dense, prefill_dense, topk_count,
+prefill_offsets, workspace_size.
 Tensors must already live on the GPU in the documented layouts; outputs may be
 passed in (preallocated) or are allocated with torch.empty on the inputs'
 device. Work is enqueued on torch's current stream of that device.
@@ -19,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libkascade_mi355x.so")
 
 OP_DECODE_ANCHOR, OP_DECODE_REUSE, OP_PREFILL_ANCHOR, OP_PREFILL_REUSE = 0, 1, 2, 3
+OP_DECODE_DENSE, OP_PREFILL_DENSE = 4, 5
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 
@@ -69,6 +71,8 @@ def _load():
         L.kas_decode_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.kas_prefill_anchor.argtypes = [dp, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_prefill_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+        L.kas_decode_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_status_string.argtypes = [st]
         L.kas_status_string.restype = ctypes.c_char_p
         L.kas_last_error.restype = ctypes.c_char_p
@@ -78,6 +82,7 @@ def _load():
         L.kas_profile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         for n in ("kas_prefill_index_offsets", "kas_workspace_size", "kas_decode_anchor",
                   "kas_decode_reuse", "kas_prefill_anchor", "kas_prefill_reuse",
+                  "kas_decode_dense", "kas_prefill_dense",
                   "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
                   "kas_profile_names"):
             getattr(L, n).restype = st
@@ -218,6 +223,31 @@ def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o
     _check(_load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
                                      anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws),
                                      ws.numel(), _stream(q)), "prefill_reuse")
+    return o
+
+
+def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None) -> torch.Tensor:
+    """Dense decode attention over all N keys: q [B,Hq,D], k/v [B,Hkv,N,D] -> o [B,Hq,D]."""
+    desc = _desc_from(q, k, 100, False, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "decode_dense", "k and v must share strides")
+    if o is None:
+        o = torch.empty_like(q)
+    ws = _ws(desc, OP_DECODE_DENSE, ws, q.device)
+    _check(_load().kas_decode_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
+                                    ws.numel(), _stream(q)), "decode_dense")
+    return o
+
+
+def prefill_dense(q, k, v, scale: float = 0.0, o=None) -> torch.Tensor:
+    """Dense causal attention: q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> o [B,Hq,N,D]."""
+    desc = _desc_from(q, k, 100, True, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "prefill_dense", "k and v must share strides")
+    if o is None:
+        o = torch.empty_like(q)
+    _check(_load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0,
+                                     _stream(q)), "prefill_dense")
     return o
 
 

@@ -545,10 +545,11 @@ __global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) 
 // ------------------------------------------------------------------ dec_attn
 
 // One workgroup = one split of one (b, g): rows [split*split_rows, ...) of the
-// index set. Wave w takes 16-row blocks w, w+4, ...; per block: Q.K^T on a
-// 16x16 MFMA tile (or the anchor's stored logits), online softmax with
-// wave-uniform running max per head, P.V on the VALU with 16 lanes per V row.
-template <typename T, int D, int G, bool FROM_LOGITS>
+// index set (DENSE: of the whole cache, row i being key i). Wave w takes
+// 16-row blocks w, w+4, ...; per block: Q.K^T on a 16x16 MFMA tile (or the
+// anchor's stored logits), online softmax with wave-uniform running max per
+// head, P.V on the VALU with 16 lanes per V row.
+template <typename T, int D, int G, bool FROM_LOGITS, bool DENSE = false>
 __global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
   using QK = QKMfma<T, D>;
   constexpr int EPL = D / 16;
@@ -564,12 +565,16 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
   const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
   // Index values and the head map are trusted inputs; clamping keeps every
   // access inside the cache even if they are not.
-  int ga = a.head_map ? a.head_map[g] : g;
-  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
-  const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
-  for (int i = tid; i < nrows; i += 256) {
-    const int32_t j = idx[i];
-    s_idx[i] = ((uint32_t)j < (uint32_t)a.N) ? j : 0;
+  if (DENSE) {
+    for (int i = tid; i < nrows; i += 256) s_idx[i] = (int32_t)(row0 + i);
+  } else {
+    int ga = a.head_map ? a.head_map[g] : g;
+    ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+    const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
+    for (int i = tid; i < nrows; i += 256) {
+      const int32_t j = idx[i];
+      s_idx[i] = ((uint32_t)j < (uint32_t)a.N) ? j : 0;
+    }
   }
   __syncthreads();
 
@@ -913,7 +918,9 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
 // lane that owns the row). Vector memory counters retire in issue order, so
 // the index of block i + 2 is issued before the rows of block i + 1; no
 // load sits behind a divergent branch in the steady-state loop.
-template <int D, int G, bool FROM_LOGITS>
+// DENSE: the split covers keys [row0, row0 + nrows) of the cache and a row's
+// key is its position (no index loads); otherwise the same kernel.
+template <int D, int G, bool FROM_LOGITS, bool DENSE = false>
 __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   using QK = QKMfma<__bf16, D>;
   constexpr int NT = D / 16;            // output tiles of 16 dims
@@ -932,9 +939,9 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
   const int nblk = (nrows + 15) >> 4;
   const int nb = wave < nblk ? (nblk - wave + 3) >> 2 : 0;   // blocks wave, wave + 4, ...
-  int ga = a.head_map ? a.head_map[g] : g;
+  int ga = (!DENSE && a.head_map) ? a.head_map[g] : g;
   ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
-  const int32_t* idx = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
+  const int32_t* idx = DENSE ? nullptr : a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
   const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
@@ -959,7 +966,9 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   // the split re-read its last index and are masked in the softmax
   auto load_idx = [&](int i) -> int {
     const int blk = min(wave + 4 * i, nblk - 1);
-    return idx[min(blk * 16 + c16, nrows - 1)];
+    const int r = min(blk * 16 + c16, nrows - 1);
+    if constexpr (DENSE) return (int)row0 + r;
+    else return idx[r];
   };
   struct Blk {
     QK kq;
@@ -1213,21 +1222,21 @@ hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
   return ctx.end(K_SEL_COMPACT);
 }
 
-template <typename T, int D, bool FL>
+template <typename T, int D, bool FL, bool DENSE = false>
 static hipError_t attn_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_attn_kernel<T, D, 1, FL>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_attn_kernel<T, D, 2, FL>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_attn_kernel<T, D, 4, FL>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_attn_kernel<T, D, 8, FL>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_attn_kernel<T, D, 1, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_attn_kernel<T, D, 2, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_attn_kernel<T, D, 4, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_attn_kernel<T, D, 8, FL, DENSE>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
 }
 
-template <typename T, bool FL>
+template <typename T, bool FL, bool DENSE = false>
 static hipError_t attn_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
-  return a.D == 128 ? attn_launch<T, 128, FL>(a, grid, st) : attn_launch<T, 64, FL>(a, grid, st);
+  return a.D == 128 ? attn_launch<T, 128, FL, DENSE>(a, grid, st) : attn_launch<T, 64, FL, DENSE>(a, grid, st);
 }
 
 template <int D, bool FL>
@@ -1241,13 +1250,13 @@ static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st
   }
   return hipSuccess;
 }
-template <int D, bool FL>
+template <int D, bool FL, bool DENSE = false>
 static hipError_t gather_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL, DENSE>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -1261,6 +1270,15 @@ static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) 
   return a.D == 128 ? attn_bf16_launch<128, FL>(a, grid, st) : attn_bf16_launch<64, FL>(a, grid, st);
 }
 
+// merge of the split partials into o
+static hipError_t launch_combine(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
+  ctx.begin(K_DEC_COMBINE);
+  dim3 cgrid(a.Hq, a.B);
+  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx, a);
+  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx, a);
+  return ctx.end(K_DEC_COMBINE);
+}
+
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx) {
   dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
@@ -1272,11 +1290,20 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, 
                        : attn_by_d<float, false>(a, grid, ctx);
   if (e != hipSuccess) return e;
   if ((e = ctx.end(kid)) != hipSuccess) return e;
-  ctx.begin(K_DEC_COMBINE);
-  dim3 cgrid(a.Hq, a.B);
-  if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx, a);
-  else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx, a);
-  return ctx.end(K_DEC_COMBINE);
+  return launch_combine(a, dtype, ctx);
+}
+
+hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
+  dim3 grid(a.nsplit, a.Hkv, a.B);
+  hipError_t e;
+  ctx.begin(K_DEC_DENSE);
+  if (dtype == 1)
+    e = a.D == 128 ? gather_launch<128, false, true>(a, grid, ctx) : gather_launch<64, false, true>(a, grid, ctx);
+  else
+    e = attn_by_d<float, false, true>(a, grid, ctx);
+  if (e != hipSuccess) return e;
+  if ((e = ctx.end(K_DEC_DENSE)) != hipSuccess) return e;
+  return launch_combine(a, dtype, ctx);
 }
 
 }  // namespace kas

@@ -21,6 +21,8 @@ enum KernelId {
   K_PRE_POOL,
   K_PRE_SELECT,
   K_PRE_ATTN,
+  K_DEC_DENSE,
+  K_PRE_DENSE,
   K_COUNT_
 };
 const char* kernel_name(int id);
@@ -59,7 +61,7 @@ struct DecodeArgs {
   int64_t N;
   float scale_log2;                 // softmax scale * log2(e)
   // index sets
-  const int32_t* idx;               // [B, Hkv_a, kk]
+  const int32_t* idx;               // [B, Hkv_a, kk]; unused by the dense kernels
   int64_t kk;
   int Hkv_a;
   const int32_t* head_map;          // [Hkv] or null
@@ -84,5 +86,8 @@ hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
 hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx);
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx);
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx);
+// Dense decode attention over all N keys: the split kernels with row i of a
+// split standing for key split_rows * split + i (idx unused, kk = N).
+hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
 
 }  // namespace kas

@@ -39,5 +39,8 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
                        int64_t kv_bs, int64_t kv_hs, char* ws, bool anchor);
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx);
 hipError_t launch_prefill_reuse(PrefillArgs& a, LaunchCtx& ctx);
+// Dense causal attention: tile t attends to keys [0, 32 t] block by block
+// (idx, offsets and head_map unused).
+hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx);
 
 }  // namespace kas

@@ -39,7 +39,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
-    "prefill_select", "prefill_attn"};
+    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
 
@@ -225,9 +225,11 @@ struct DecodePlan {
       off_part_ml, total;
 };
 
-static DecodePlan plan_decode(const Shape& s, bool anchor) {
+// dense: the split rows cover the whole cache (kk = N) and only the split
+// partials are needed
+static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false) {
   DecodePlan p{};
-  p.kk = decode_k(s.N, s.pct);
+  p.kk = dense ? s.N : decode_k(s.N, s.pct);
   p.score_rows = decode_score_rows();
   p.n_score_chunks = (int)((s.N + p.score_rows - 1) / p.score_rows);
   p.n_sel_chunks = (int)((s.N + kSelChunk - 1) / kSelChunk);
@@ -327,12 +329,14 @@ kas_status_t kas_prefill_index_offsets(const kas_desc_t* desc, int64_t* offsets,
 kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* bytes) {
   if (!bytes) return fail(KAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
   Shape s;
-  const bool prefill = op == KAS_OP_PREFILL_ANCHOR || op == KAS_OP_PREFILL_REUSE;
-  if (op < 0 || op > 3) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown op %d", op);
+  const bool prefill = op == KAS_OP_PREFILL_ANCHOR || op == KAS_OP_PREFILL_REUSE || op == KAS_OP_PREFILL_DENSE;
+  if (op < KAS_OP_DECODE_ANCHOR || op > KAS_OP_PREFILL_DENSE) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   kas_status_t st = check_desc(desc, prefill, s);
   if (st != KAS_OK) return st;
-  if (!prefill) {
-    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR).total;
+  if (op == KAS_OP_PREFILL_DENSE) {
+    *bytes = 0;
+  } else if (!prefill) {
+    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE).total;
   } else {
     *bytes = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, op == KAS_OP_PREFILL_ANCHOR);
   }
@@ -440,6 +444,46 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e = launch_prefill_reuse(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_reuse");
+  return KAS_OK;
+}
+
+kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v, void* o,
+                              void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  kas_status_t st = check_desc(desc, false, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  DecodePlan p = plan_decode(s, false, true);
+  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  DecodeArgs a;
+  fill_decode_args(s, p, false, (char*)ws, a);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e;
+  if ((e = launch_decode_dense(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_dense");
+  return KAS_OK;
+}
+
+kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v, void* o,
+                               void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  Shape s;
+  kas_status_t st = check_desc(desc, true, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if ((st = check_prefill_limits(s, 0))) return st;
+  PrefillArgs a;
+  fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, nullptr, false);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.offsets = nullptr; a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = 0;
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e = launch_prefill_dense(a, ctx);
+  if (e != hipSuccess) return hip_fail(e, "prefill_dense");
   return KAS_OK;
 }
 

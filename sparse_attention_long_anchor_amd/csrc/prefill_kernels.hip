@@ -740,7 +740,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // are distinct arrays selected at compile time (the steady loop is unrolled
 // by four), so the compiler can tell the stage being read from the stages
 // being filled.
-template <int D, int G>
+// DENSE: dense causal attention with the same block math; block blk holds
+// keys [32 blk, 32 blk + 32) for every blk <= t (block t is the diagonal), so
+// there are no index loads and the tile's key list is [0, 32 t).
+template <int D, int G, bool DENSE = false>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
   constexpr int ROWB = 2 * D;               // bytes per row
@@ -762,11 +765,11 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS line bases stay scalar
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
-  int ga = a.head_map ? a.head_map[g] : g;
+  int ga = (!DENSE && a.head_map) ? a.head_map[g] : g;
   ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
-  const int o0 = a.offsets[t];
-  const int kt = a.offsets[t + 1] - o0;
-  const int32_t* S = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
+  const int o0 = DENSE ? 0 : a.offsets[t];
+  const int kt = DENSE ? kTile * t : a.offsets[t + 1] - o0;
+  const int32_t* S = DENSE ? nullptr : a.idx + ((int64_t)b * a.Hkv_a + ga) * a.total + o0;
   const int nsel = (kt + 31) / 32;
   const int nfull = kt / 32;
   const int tile_key0 = kTile * t;
@@ -795,6 +798,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   int jr[4][NIW];
   auto load_index = [&](int blk, auto set_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
+    if constexpr (DENSE) return;
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
       const int i = w + G * j;
@@ -819,13 +823,17 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
       const int i = w + G * j;
       if (EVEN || i < NINS) {
         const int r = RPI * i + lrow;
-        const int jj = jr[SET][j];
         int key;
-        if (STEADY) {
-          key = ((unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
+        if constexpr (DENSE) {
+          key = blk * 32 + r;                                    // blk <= t: inside the prompt
         } else {
-          const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;
-          key = (blk == nsel) ? tile_key0 + r : sel;
+          const int jj = jr[SET][j];
+          if (STEADY) {
+            key = ((unsigned)jj < (unsigned)tile_key0) ? jj : 0;   // trusted input, kept in bounds
+          } else {
+            const int sel = (blk * 32 + r < kt && (unsigned)jj < (unsigned)tile_key0) ? jj : 0;
+            key = (blk == nsel) ? tile_key0 + r : sel;
+          }
         }
         // byte offsets of the row plus this lane's swizzled 16-byte chunk
         // (computed before the call: a function call inside the builtin's
@@ -868,7 +876,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
     // the indices of block blk + 3 (loaded a step ago, before block blk + 2's
     // lines and this step's index loads) have landed; said with the builtin
     // so the compiler does not wait for everything in flight before using them
-    if (STEADY && EVEN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
+    if (STEADY && EVEN && !DENSE) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NIW));
     if (STEADY || blk + 3 <= nsel) issue(blk + 3, St2{}, stage(St2{}), steady_tag);
     const char* sk = stage(st_tag);
     const char* sv = sk + BLKB;
@@ -946,9 +954,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
     // DMA lines of this step and the last one may still be in flight), then
     // in every wave
     // (the builtin wait, unlike inline asm, is seen by the compiler's own
-    // wait placement, which then knows these lines have landed)
+    // wait placement, which then knows these lines have landed; DENSE has no
+    // index loads in flight, only the lines of blocks blk + 2 and blk + 3)
     if (STEADY && EVEN) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * NIW));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(DENSE ? 4 * NIW : 6 * NIW));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
@@ -1074,6 +1083,7 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   // every tile through the in-place histogram passes)
   const char* cap = getenv("KAS_PREFILL_SELECT_CAP");
   a.sel_cap = cap ? std::min(std::max(atoi(cap), 0), kPreSelCap) : kPreSelCap;
+  if (!ws) return;                  // dense attention: no workspace
   a.offsets = (int32_t*)(ws + p.off_offsets);
   if (anchor) {
     a.lse = (float*)(ws + p.off_lse);
@@ -1105,6 +1115,28 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
     }                                                                                     \
   } while (0)
 
+// KERNEL<D, G, X> over the supported (D, G)
+#define KAS_DISPATCH_DGX(KERNEL, X, grid, st, a)                                          \
+  do {                                                                                    \
+    if (a.D == 128) {                                                                     \
+      switch (a.G) {                                                                      \
+        case 1: KAS_LAUNCH_P((KERNEL<128, 1, X>), grid, dim3(64), st, a); break;          \
+        case 2: KAS_LAUNCH_P((KERNEL<128, 2, X>), grid, dim3(128), st, a); break;         \
+        case 4: KAS_LAUNCH_P((KERNEL<128, 4, X>), grid, dim3(256), st, a); break;         \
+        case 8: KAS_LAUNCH_P((KERNEL<128, 8, X>), grid, dim3(512), st, a); break;         \
+        default: return hipErrorInvalidValue;                                             \
+      }                                                                                   \
+    } else {                                                                              \
+      switch (a.G) {                                                                      \
+        case 1: KAS_LAUNCH_P((KERNEL<64, 1, X>), grid, dim3(64), st, a); break;           \
+        case 2: KAS_LAUNCH_P((KERNEL<64, 2, X>), grid, dim3(128), st, a); break;          \
+        case 4: KAS_LAUNCH_P((KERNEL<64, 4, X>), grid, dim3(256), st, a); break;          \
+        case 8: KAS_LAUNCH_P((KERNEL<64, 8, X>), grid, dim3(512), st, a); break;          \
+        default: return hipErrorInvalidValue;                                             \
+      }                                                                                   \
+    }                                                                                     \
+  } while (0)
+
 static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
   KAS_LAUNCH_P(pre_offsets_kernel, dim3(1), dim3(256), ctx, a);
   return hipGetLastError();
@@ -1113,8 +1145,15 @@ static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
 static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) {
   ctx.begin(K_PRE_ATTN);
   dim3 grid(a.T, a.Hkv, a.B);
-  KAS_DISPATCH_DG(pre_attn_dma_kernel, grid, ctx, a);
+  KAS_DISPATCH_DGX(pre_attn_dma_kernel, false, grid, ctx, a);
   return ctx.end(K_PRE_ATTN);
+}
+
+hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) {
+  ctx.begin(K_PRE_DENSE);
+  dim3 grid(a.T, a.Hkv, a.B);
+  KAS_DISPATCH_DGX(pre_attn_dma_kernel, true, grid, ctx, a);
+  return ctx.end(K_PRE_DENSE);
 }
 
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {

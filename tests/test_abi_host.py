@@ -58,6 +58,10 @@ def test_descriptor_validation():
     ok = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16)
     assert b.workspace_size(ok, b.OP_DECODE_ANCHOR) > b.workspace_size(ok, b.OP_DECODE_REUSE) > 0
     assert b.workspace_size(ok, b.OP_PREFILL_REUSE) >= 0
+    # dense decode keeps split partials only; dense prefill needs no workspace
+    assert b.workspace_size(ok, b.OP_DECODE_REUSE) < b.workspace_size(ok, b.OP_DECODE_DENSE) \
+        < b.workspace_size(ok, b.OP_DECODE_ANCHOR)
+    assert b.workspace_size(ok, b.OP_PREFILL_DENSE) == 0
     bad = [
         (b.make_desc(1, 12, 4, 128, 64, 10, torch.bfloat16), b.OP_DECODE_REUSE, 2),    # G = 3
         (b.make_desc(1, 32, 8, 96, 64, 10, torch.bfloat16), b.OP_DECODE_REUSE, 2),     # head_dim
@@ -76,7 +80,8 @@ def test_descriptor_validation():
     L = b._load()
     n = ctypes.c_size_t(0)
     assert L.kas_workspace_size(None, 0, ctypes.byref(n)) == 1
-    assert L.kas_workspace_size(ctypes.byref(ok), 7, ctypes.byref(n)) == 1
+    assert L.kas_workspace_size(ctypes.byref(ok), 6, ctypes.byref(n)) == 1
+    assert L.kas_workspace_size(ctypes.byref(ok), -1, ctypes.byref(n)) == 1
 
 
 def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
@@ -107,13 +112,27 @@ def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
     dp = b.make_desc(1, 8, 2, 64, 96, 10, torch.float32)
     r = L.kas_prefill_anchor(ctypes.byref(dp), fake, fake, fake, fake, fake, fake, 1 << 30, None)
     assert r == 2
+    # dense baselines: the same checks
+    need_dense = b.workspace_size(d, b.OP_DECODE_DENSE)
+    r = L.kas_decode_dense(ctypes.byref(d), fake, None, fake, fake, fake, need_dense, None)
+    assert r == 1 and b"k is NULL" in L.kas_last_error()
+    r = L.kas_decode_dense(ctypes.byref(d), fake, fake, fake, fake, fake, need_dense - 1, None)
+    assert r == 3
+    r = L.kas_prefill_dense(ctypes.byref(dp), fake, fake, fake, fake, None, 0, None)
+    assert r == 2                              # prefill is bf16 only
+    dhuge = b.make_desc(1, 8, 2, 128, 9_000_000, 10, torch.bfloat16)
+    r = L.kas_prefill_dense(ctypes.byref(dhuge), fake, fake, fake, fake, None, 0, None)
+    assert r == 2 and b"2^31" in L.kas_last_error()
+    r = L.kas_prefill_dense(ctypes.byref(dbig), fake, fake, fake, None, None, 0, None)
+    assert r == 1 and b"o is NULL" in L.kas_last_error()
     assert L.kas_status_string(3) == b"workspace too small"
 
 
 def test_profile_names():
     b = _kas()
     names = b.profile_names()
-    for n in ["decode_score", "decode_pool", "decode_attn", "decode_combine", "select_compact"]:
+    for n in ["decode_score", "decode_pool", "decode_attn", "decode_combine", "select_compact",
+              "decode_dense", "prefill_dense"]:
         assert n in names
     with pytest.raises(b.KasError):
         b.profile_query("no_such_kernel")
