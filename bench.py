@@ -12,7 +12,10 @@ Prints one JSON line. `value` is the decode step's algorithmic HBM throughput
 (GB/s over all layers); per-layer microseconds, prefill TFLOP/s, the roofline
 of the dominant kernel (device time from HIP events recorded by the library
 around each launch during the timed steps) and the CPU oracle baseline are
-reported alongside.
+reported alongside. After the timed steps, the same layers run through the
+library's dense attention (every key; causal in prefill), the comparison the
+pages state their speed-ups against, and the speed-up of the Kascade step over
+the dense step is reported as well (outside the timed region).
 """
 import argparse
 import json
@@ -47,6 +50,15 @@ def decode_work(w, k):
         "decode_score": B * Hkv * N * D * s + B * Hq * D * s,
     }
     return reuse, anchor, kern
+
+
+def dense_work(wd, wp):
+    """Algorithmic work of one dense layer: decode bytes (all of K and V, Q,
+    O), prefill flops (causal Q.K^T and P.V)."""
+    s = 2 if wd.dtype == "bf16" else 4
+    dec = wd.batch * wd.n_kv_heads * wd.seq_len * 2 * wd.head_dim * s + 2 * wd.batch * wd.n_q_heads * wd.head_dim * s
+    pre = 2 * wp.head_dim * wp.n_q_heads * wp.batch * wp.seq_len * (wp.seq_len + 1)
+    return dec, pre
 
 
 def prefill_work(w, offsets):
@@ -189,6 +201,7 @@ def main():
     ap.add_argument("--prefill-workload", default="llama8b_prefill_128k")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -357,10 +370,69 @@ def main():
                                                 "traffic": _traffic("decode_attn")}
         out["roofline_all"] = [{k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac", "avg_us")}
                                for r in roof]
+    if not args.no_dense:
+        out["dense_baseline"], out["roofline_dense"] = dense_baseline(
+            args, wd, dec_state, wp, pre_state, out, torch, kas, dev)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
     print(json.dumps(out), flush=True)
+
+
+def dense_baseline(args, wd, dec_state, wp, pre_state, out, torch, kas, dev):
+    """Every layer of the same resident workloads through the dense calls: one
+    pass with per-layer events, one with the library's per-launch timing."""
+    dec_b, pre_f = dense_work(wd, wp)
+    res, roof = {}, []
+    runs = []
+    if dec_state is not None:
+        layers, _, o, *_ = dec_state
+        d = kas.make_desc(wd.batch, wd.n_q_heads, wd.n_kv_heads, wd.head_dim, wd.seq_len, wd.topk_pct,
+                          wd.torch_dtype)
+        ws = torch.empty(kas.workspace_size(d, kas.OP_DECODE_DENSE), dtype=torch.uint8, device=dev)
+        runs.append(("decode", layers, lambda q, k, v, o=o, ws=ws: kas.decode_dense(q, k, v, o=o, ws=ws)))
+    if pre_state is not None:
+        layers, _, o, *_ = pre_state
+        runs.append(("prefill", layers, lambda q, k, v, o=o: kas.prefill_dense(q, k, v, o=o)))
+    for phase, layers, call in runs:
+        q, k, v, _ = layers[0]
+        call(q, k, v)                                  # warm-up
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+        torch.cuda.synchronize()
+        for l, (q, k, v, _) in enumerate(layers):
+            ev[l][0].record()
+            call(q, k, v)
+            ev[l][1].record()
+        torch.cuda.synchronize()
+        per_layer = [a.elapsed_time(b) for a, b in ev]
+        kas.profile_reset()
+        kas.profile_enable(True)
+        for q, k, v, _ in layers:
+            call(q, k, v)
+        torch.cuda.synchronize()
+        kas.profile_enable(False)
+        step_ms = sum(per_layer)
+        name = phase + "_dense"
+        kms = kas.profile_query(name)
+        if phase == "decode":
+            sparse_ms = out["decode"]["ms_per_step"] if "decode" in out else None
+            res[phase] = {"workload": wd.name, "us_per_layer": round(1e3 * _mean(per_layer), 3),
+                          "GB_per_s": _rate(dec_b, _mean(per_layer) * 1e-3, 1e9),
+                          "ms_per_step": round(step_ms, 4)}
+            roof.append(_roof_entry(name, "hbm", dec_b * kms[1], kms, HBM_PEAK_GBS, "GB/s", 1e9))
+        else:
+            sparse_ms = out["prefill"]["ms_per_step"] if "prefill" in out else None
+            res[phase] = {"workload": wp.name, "ms_per_layer": round(_mean(per_layer), 4),
+                          "TFLOP_per_s": _rate(pre_f, _mean(per_layer) * 1e-3, 1e12),
+                          "ms_per_step": round(step_ms, 3)}
+            roof.append(_roof_entry(name, "mfma", pre_f * kms[1], kms, BF16_PEAK_TFLOPS, "TFLOP/s", 1e12))
+        if sparse_ms:
+            res[phase]["speedup_kascade_step"] = round(step_ms / sparse_ms, 3)
+        log(f"[bench] dense {phase}: {step_ms:.3f} ms per {len(layers)}-layer step")
+    for r in roof:
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+    return res, [dict({k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "avg_us")},
+                      traffic=_traffic(r["kernel"])) for r in roof]
 
 
 def _mean(xs):
