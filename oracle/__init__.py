@@ -59,8 +59,15 @@ def lib():
                                          _dbl, _i64, _i64, _ip, _dp]
         L.orc_prefill_reuse.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                         _dbl, _i64, _i64, _ip, _i32, _ip, _dp]
+        L.orc_decode_anchor_v.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _dbl,
+                                          _i32, _i32, _ip, _dp, _dp]
+        L.orc_prefill_pooled_v.argtypes = [_fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _dbl,
+                                           _i64, _i64, _i32, _i32, _i64, _i64, _i64, _dp]
+        L.orc_prefill_anchor_v.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                           _dbl, _i64, _i64, _i32, _i32, _ip, _dp]
         for name in ("orc_dense_attention", "orc_decode_anchor", "orc_decode_reuse",
-                     "orc_prefill_pooled", "orc_prefill_anchor", "orc_prefill_reuse"):
+                     "orc_prefill_pooled", "orc_prefill_anchor", "orc_prefill_reuse",
+                     "orc_decode_anchor_v", "orc_prefill_pooled_v", "orc_prefill_anchor_v"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -112,19 +119,30 @@ def dense_attention(q, k, v, causal: bool, scale: float = 0.0) -> np.ndarray:
     return o
 
 
-def decode_anchor(q, k, v, pct: int, scale: float = 0.0, want_pooled: bool = False
+def decode_anchor(q, k, v, pct: int, scale: float = 0.0, want_pooled: bool = False,
+                  pool_scope: int = 0, pool_op: int = 0
                   ) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
-    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hkv,kk], o [B,Hq,D], pooled [B,Hkv,N])."""
+    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hs,kk], o [B,Hq,D], pooled [B,Hs,N]).
+
+    pool_scope 0: one set per KV head (its group's heads pooled), Hs = Hkv;
+    1: one set per batch row pooled over all heads, Hs = 1. pool_op 0: sum,
+    1: maximum."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, Hq, D = q.shape
     Hkv, N = k.shape[1], k.shape[2]
+    Hs = 1 if pool_scope else Hkv
     kk = decode_k(N, pct)
-    idx = np.zeros((B, Hkv, kk), dtype=np.int32)
+    idx = np.zeros((B, Hs, kk), dtype=np.int32)
     o = np.zeros((B, Hq, D), dtype=np.float64)
-    pooled = np.zeros((B, Hkv, N), dtype=np.float64) if want_pooled else None
-    _check(lib().orc_decode_anchor(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
-                                   pct, scale, _ptr(idx, _ip), _ptr(o, _dp),
-                                   _ptr(pooled, _dp) if want_pooled else None), "decode_anchor")
+    pooled = np.zeros((B, Hs, N), dtype=np.float64) if want_pooled else None
+    pp = _ptr(pooled, _dp) if want_pooled else None
+    if pool_scope == 0 and pool_op == 0:
+        rc = lib().orc_decode_anchor(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
+                                     pct, scale, _ptr(idx, _ip), _ptr(o, _dp), pp)
+    else:
+        rc = lib().orc_decode_anchor_v(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
+                                       pct, scale, pool_scope, pool_op, _ptr(idx, _ip), _ptr(o, _dp), pp)
+    _check(rc, "decode_anchor")
     return idx, o, pooled
 
 
@@ -142,35 +160,50 @@ def decode_reuse(q, k, v, anchor_idx, head_map, scale: float = 0.0) -> np.ndarra
 
 
 def prefill_anchor(q_rows, k, v, pct: int, tile: int = 32, t0: int = 0, t1: Optional[int] = None,
-                   scale: float = 0.0) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: float = 0.0, pool_scope: int = 0, pool_op: int = 0
+                   ) -> Tuple[np.ndarray, np.ndarray]:
     """q_rows [B,Hq,R,D] = query rows of tiles [t0,t1); k/v [B,Hkv,N,D].
 
-    Returns (idx int32 [B,Hkv,off[t1]-off[t0]], o float64 [B,Hq,R,D])."""
+    Returns (idx int32 [B,Hs,off[t1]-off[t0]], o float64 [B,Hq,R,D]); Hs and
+    the pooling variants as in decode_anchor."""
     q_rows, k, v = _f32(q_rows), _f32(k), _f32(v)
     B, Hq, R, D = q_rows.shape
     Hkv, N = k.shape[1], k.shape[2]
+    Hs = 1 if pool_scope else Hkv
     T = (N + tile - 1) // tile
     t1 = T if t1 is None else t1
     off = prefill_offsets(N, tile, pct)
     assert R == min(N, tile * t1) - tile * t0, "q_rows must hold exactly the tile range"
-    idx = np.zeros((B, Hkv, int(off[t1] - off[t0])), dtype=np.int32)
+    idx = np.zeros((B, Hs, int(off[t1] - off[t0])), dtype=np.int32)
     o = np.zeros((B, Hq, R, D), dtype=np.float64)
-    _check(lib().orc_prefill_anchor(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
-                                    D, tile, pct, scale, t0, t1, _ptr(idx, _ip), _ptr(o, _dp)),
-           "prefill_anchor")
+    if pool_scope == 0 and pool_op == 0:
+        rc = lib().orc_prefill_anchor(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
+                                      D, tile, pct, scale, t0, t1, _ptr(idx, _ip), _ptr(o, _dp))
+    else:
+        rc = lib().orc_prefill_anchor_v(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
+                                        D, tile, pct, scale, t0, t1, pool_scope, pool_op,
+                                        _ptr(idx, _ip), _ptr(o, _dp))
+    _check(rc, "prefill_anchor")
     return idx, o
 
 
 def prefill_pooled(q_rows, k, b: int, t: int, g: int, tile: int = 32, t0: int = 0,
-                   t1: Optional[int] = None, scale: float = 0.0) -> np.ndarray:
+                   t1: Optional[int] = None, scale: float = 0.0, pool_scope: int = 0,
+                   pool_op: int = 0) -> np.ndarray:
+    """Pooled scores of set g of tile t (g = 0 when pool_scope is 1)."""
     q_rows, k = _f32(q_rows), _f32(k)
     B, Hq, R, D = q_rows.shape
     Hkv, N = k.shape[1], k.shape[2]
     T = (N + tile - 1) // tile
     t1 = T if t1 is None else t1
     P = np.zeros(min(N, tile * (t + 1)), dtype=np.float64)
-    _check(lib().orc_prefill_pooled(_ptr(q_rows, _fp), _ptr(k, _fp), B, Hq, Hkv, N, D, tile,
-                                    scale, t0, t1, b, t, g, _ptr(P, _dp)), "prefill_pooled")
+    if pool_scope == 0 and pool_op == 0:
+        rc = lib().orc_prefill_pooled(_ptr(q_rows, _fp), _ptr(k, _fp), B, Hq, Hkv, N, D, tile,
+                                      scale, t0, t1, b, t, g, _ptr(P, _dp))
+    else:
+        rc = lib().orc_prefill_pooled_v(_ptr(q_rows, _fp), _ptr(k, _fp), B, Hq, Hkv, N, D, tile,
+                                        scale, t0, t1, pool_scope, pool_op, b, t, g, _ptr(P, _dp))
+    _check(rc, "prefill_pooled")
     return P
 
 

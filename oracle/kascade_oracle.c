@@ -36,6 +36,12 @@
  *   - the output of a selected set is attention renormalised over that set
  *     (prefill: the set plus the causal diagonal keys of the row);
  *   - query head h uses KV head h / G.
+ * Selection variants (the README's "Reproducibility" commands name
+ * strategies that pool per KV-head group or over all heads; max-pooling is a
+ * further variant of the pooling operator): the _v entry points take a
+ * pooling scope (0: the G heads sharing a KV head, one set per KV head;
+ * 1: all query heads, one set shared by every KV head) and operator (0: sum,
+ * 1: maximum); the plain entry points are scope 0 with the sum.
  *
  * Arithmetic is IEEE double throughout (inputs arrive as float, which holds
  * bf16 values exactly). Work units are independent and each is computed by
@@ -206,27 +212,37 @@ int orc_dense_attention(const float *q, const float *k, const float *v, double *
 /* decode                                                              */
 /* ------------------------------------------------------------------ */
 
-/* Anchor layer, one new token per sequence.
- * q [B,Hq,D]; k/v [B,Hkv,N,D]; idx_out [B,Hkv,kk] (kk = decode k);
- * o_out [B,Hq,D]; pooled_out [B,Hkv,N] or NULL.
- * For each (b, g): every query head of the group gets its softmax over all N
- * keys; the probabilities are summed over the group; the Top-k of that pooled
- * score is the index set; each head's output is attention over the set. */
-int orc_decode_anchor(const float *q, const float *k, const float *v,
-                      int B, int Hq, int Hkv, int64_t N, int D, int32_t pct, double scale,
-                      int32_t *idx_out, double *o_out, double *pooled_out)
+/* Anchor layer, one new token per sequence, with the pooling variants the
+ * README names among its strategies ("Reproducibility": post-softmax pooling
+ * per KV-head group, pooling over all heads) plus max-pooling:
+ *   scope 0: one set per (b, KV head g), pooled over the G query heads that
+ *            share g (the method's head-aware selection);
+ *   scope 1: one set per b, pooled over all Hq query heads and shared by
+ *            every KV head;
+ *   op 0:    pooled score = sum of the heads' probabilities;
+ *   op 1:    pooled score = their maximum.
+ * q [B,Hq,D]; k/v [B,Hkv,N,D]; with Hs = (scope ? 1 : Hkv):
+ * idx_out [B,Hs,kk] (kk = decode k); o_out [B,Hq,D]; pooled_out [B,Hs,N] or
+ * NULL. Each query head's output is attention over its set. */
+int orc_decode_anchor_v(const float *q, const float *k, const float *v,
+                        int B, int Hq, int Hkv, int64_t N, int D, int32_t pct, double scale,
+                        int scope, int op, int32_t *idx_out, double *o_out, double *pooled_out)
 {
     if (check_shape(B, Hq, Hkv, N, D) || pct < 1 || pct > 100) return ORC_BAD_ARG;
+    if ((scope != 0 && scope != 1) || (op != 0 && op != 1)) return ORC_BAD_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     const int G = Hq / Hkv;
+    const int Hs = scope ? 1 : Hkv;       /* sets per batch row */
+    const int ng = scope ? Hkv : 1;       /* KV heads pooled into one set */
+    const int nh = ng * G;                /* query heads pooled into one set */
     const int64_t kk = decode_k(N, pct);
     int status = ORC_OK;
 #pragma omp parallel
     {
-        double *s = (double *)malloc((size_t)G * N * sizeof(double));
+        double *s = (double *)malloc((size_t)nh * N * sizeof(double));
         double *P = (double *)malloc((size_t)N * sizeof(double));
-        double *mrow = (double *)malloc((size_t)G * sizeof(double));
-        double *lrow = (double *)malloc((size_t)G * sizeof(double));
+        double *mrow = (double *)malloc((size_t)nh * sizeof(double));
+        double *lrow = (double *)malloc((size_t)nh * sizeof(double));
         double *sel = (double *)malloc((size_t)kk * sizeof(double));
         int64_t *keys = (int64_t *)malloc((size_t)kk * sizeof(int64_t));
         if (!s || !P || !mrow || !lrow || !sel || !keys) {
@@ -234,27 +250,31 @@ int orc_decode_anchor(const float *q, const float *k, const float *v,
             status = ORC_NOMEM;
         } else {
 #pragma omp for schedule(dynamic)
-            for (int64_t u = 0; u < (int64_t)B * Hkv; ++u) {
-                int64_t b = u / Hkv, g = u % Hkv;
-                const float *kb = k + (b * Hkv + g) * N * D;
-                const float *vb = v + (b * Hkv + g) * N * D;
-                /* 1. per-head logits and softmax statistics over all keys */
-                for (int r = 0; r < G; ++r) {
-                    const float *qh = q + (b * Hq + g * G + r) * D;
+            for (int64_t u = 0; u < (int64_t)B * Hs; ++u) {
+                int64_t b = u / Hs, g0 = scope ? 0 : u % Hs;
+                /* 1. per-head logits and softmax statistics over all keys;
+                 *    head x of the unit is query head (g0 + x / G) * G + x % G */
+                for (int x = 0; x < nh; ++x) {
+                    const int64_t g = g0 + x / G;
+                    const float *kb = k + (b * Hkv + g) * N * D;
+                    const float *qh = q + (b * Hq + g * G + x % G) * D;
                     double m = -INFINITY;
                     for (int64_t j = 0; j < N; ++j) {
-                        s[r * N + j] = dot_scaled(qh, kb + j * D, D, scale);
-                        if (s[r * N + j] > m) m = s[r * N + j];
+                        s[x * N + j] = dot_scaled(qh, kb + j * D, D, scale);
+                        if (s[x * N + j] > m) m = s[x * N + j];
                     }
                     double l = 0.0;
-                    for (int64_t j = 0; j < N; ++j) l += exp(s[r * N + j] - m);
-                    mrow[r] = m;
-                    lrow[r] = l;
+                    for (int64_t j = 0; j < N; ++j) l += exp(s[x * N + j] - m);
+                    mrow[x] = m;
+                    lrow[x] = l;
                 }
-                /* 2. pool the post-softmax probabilities over the group */
+                /* 2. pool the post-softmax probabilities over the unit's heads */
                 for (int64_t j = 0; j < N; ++j) {
                     double acc = 0.0;
-                    for (int r = 0; r < G; ++r) acc += exp(s[r * N + j] - mrow[r]) / lrow[r];
+                    for (int x = 0; x < nh; ++x) {
+                        const double p = exp(s[x * N + j] - mrow[x]) / lrow[x];
+                        acc = op ? (p > acc ? p : acc) : acc + p;
+                    }
                     P[j] = acc;
                 }
                 if (pooled_out) memcpy(pooled_out + u * N, P, (size_t)N * sizeof(double));
@@ -267,15 +287,25 @@ int orc_decode_anchor(const float *q, const float *k, const float *v,
                 }
                 /* 4. attention over the selected keys, per head */
                 for (int64_t a = 0; a < kk; ++a) keys[a] = S[a];
-                for (int r = 0; r < G; ++r) {
-                    for (int64_t a = 0; a < kk; ++a) sel[a] = s[r * N + S[a]];
-                    weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + g * G + r) * D);
+                for (int x = 0; x < nh; ++x) {
+                    const int64_t g = g0 + x / G;
+                    const float *vb = v + (b * Hkv + g) * N * D;
+                    for (int64_t a = 0; a < kk; ++a) sel[a] = s[x * N + S[a]];
+                    weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + g * G + x % G) * D);
                 }
             }
         }
         free(s); free(P); free(mrow); free(lrow); free(sel); free(keys);
     }
     return status;
+}
+
+/* The method's own anchor layer: scope 0 (per KV-head group), sum pooling. */
+int orc_decode_anchor(const float *q, const float *k, const float *v,
+                      int B, int Hq, int Hkv, int64_t N, int D, int32_t pct, double scale,
+                      int32_t *idx_out, double *o_out, double *pooled_out)
+{
+    return orc_decode_anchor_v(q, k, v, B, Hq, Hkv, N, D, pct, scale, 0, 0, idx_out, o_out, pooled_out);
 }
 
 /* Reuse layer: attention over the anchor's index set of the mapped KV head.
@@ -340,33 +370,38 @@ static int64_t range_rows(int64_t N, int32_t tile, int64_t t0, int64_t t1)
     return end - t0 * tile;
 }
 
-/* Pooled score of one (b, t, g) unit over keys [0, min(N, tile*(t+1))):
- * P[j] = sum over the group's heads and the tile's rows i >= j of the row's
- * softmax probability of key j (softmax over the causal row j' <= i).
- * `rowbuf` holds at least N doubles. */
+/* Pooled score of one unit over keys [0, min(N, tile*(t+1))): over the query
+ * heads of KV heads [g0, g0 + ng) and the tile's rows i >= j, the sum (op 0)
+ * or the maximum (op 1) of the row's softmax probability of key j (softmax
+ * over the causal row j' <= i). `rowbuf` holds at least N doubles. */
 static void prefill_pool_unit(const float *q, const float *k, int B, int Hq, int Hkv,
                               int64_t N, int D, int32_t tile, double scale,
-                              int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g,
-                              double *P, double *rowbuf)
+                              int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g0, int ng,
+                              int op, double *P, double *rowbuf)
 {
     (void)B;
     const int G = Hq / Hkv;
     const int64_t i0 = t * tile;
     const int64_t i1 = (i0 + tile < N) ? i0 + tile : N;
-    const float *kb = k + (b * Hkv + g) * N * D;
     for (int64_t j = 0; j < i1; ++j) P[j] = 0.0;
-    for (int r = 0; r < G; ++r) {
-        const int64_t h = g * G + r;
-        for (int64_t i = i0; i < i1; ++i) {
-            const float *qi = q + ((b * Hq + h) * R + (i - t0 * tile)) * D;
-            double m = -INFINITY;
-            for (int64_t j = 0; j <= i; ++j) {
-                rowbuf[j] = dot_scaled(qi, kb + j * D, D, scale);
-                if (rowbuf[j] > m) m = rowbuf[j];
+    for (int64_t g = g0; g < g0 + ng; ++g) {
+        const float *kb = k + (b * Hkv + g) * N * D;
+        for (int r = 0; r < G; ++r) {
+            const int64_t h = g * G + r;
+            for (int64_t i = i0; i < i1; ++i) {
+                const float *qi = q + ((b * Hq + h) * R + (i - t0 * tile)) * D;
+                double m = -INFINITY;
+                for (int64_t j = 0; j <= i; ++j) {
+                    rowbuf[j] = dot_scaled(qi, kb + j * D, D, scale);
+                    if (rowbuf[j] > m) m = rowbuf[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j <= i; ++j) l += exp(rowbuf[j] - m);
+                for (int64_t j = 0; j <= i; ++j) {
+                    const double p = exp(rowbuf[j] - m) / l;
+                    P[j] = op ? (p > P[j] ? p : P[j]) : P[j] + p;
+                }
             }
-            double l = 0.0;
-            for (int64_t j = 0; j <= i; ++j) l += exp(rowbuf[j] - m);
-            for (int64_t j = 0; j <= i; ++j) P[j] += exp(rowbuf[j] - m) / l;
         }
     }
 }
@@ -398,32 +433,50 @@ static void prefill_output_unit(const float *q, const float *k, const float *v,
 }
 
 /* Pooled scores of a single unit, for checking: P_out has
- * min(N, tile*(t+1)) entries (selection candidates are the first tile*t). */
-int orc_prefill_pooled(const float *q, const float *k, int B, int Hq, int Hkv, int64_t N,
-                       int D, int32_t tile, double scale, int64_t t0, int64_t t1,
-                       int64_t b, int64_t t, int64_t g, double *P_out)
+ * min(N, tile*(t+1)) entries (selection candidates are the first tile*t).
+ * Unit (b, t, gs): scope 0 pools KV head gs's group, scope 1 all heads
+ * (gs = 0); op as in prefill_pool_unit. */
+int orc_prefill_pooled_v(const float *q, const float *k, int B, int Hq, int Hkv, int64_t N,
+                         int D, int32_t tile, double scale, int64_t t0, int64_t t1,
+                         int scope, int op, int64_t b, int64_t t, int64_t gs, double *P_out)
 {
     if (check_shape(B, Hq, Hkv, N, D) || tile <= 0) return ORC_BAD_ARG;
+    if ((scope != 0 && scope != 1) || (op != 0 && op != 1)) return ORC_BAD_ARG;
+    const int Hs = scope ? 1 : Hkv;
     int64_t T = (N + tile - 1) / tile;
-    if (t0 < 0 || t1 > T || t0 >= t1 || t < t0 || t >= t1 || b < 0 || b >= B || g < 0 || g >= Hkv)
+    if (t0 < 0 || t1 > T || t0 >= t1 || t < t0 || t >= t1 || b < 0 || b >= B || gs < 0 || gs >= Hs)
         return ORC_BAD_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     double *rowbuf = (double *)malloc((size_t)N * sizeof(double));
     if (!rowbuf) return ORC_NOMEM;
     prefill_pool_unit(q, k, B, Hq, Hkv, N, D, tile, scale, t0, range_rows(N, tile, t0, t1),
-                      b, t, g, P_out, rowbuf);
+                      b, t, scope ? 0 : gs, scope ? Hkv : 1, op, P_out, rowbuf);
     free(rowbuf);
     return ORC_OK;
 }
 
+int orc_prefill_pooled(const float *q, const float *k, int B, int Hq, int Hkv, int64_t N,
+                       int D, int32_t tile, double scale, int64_t t0, int64_t t1,
+                       int64_t b, int64_t t, int64_t g, double *P_out)
+{
+    return orc_prefill_pooled_v(q, k, B, Hq, Hkv, N, D, tile, scale, t0, t1, 0, 0, b, t, g, P_out);
+}
+
 /* Prefill anchor layer over tiles [t0, t1): pooled tile scores, exact Top-k_t
- * per (b, t, g), and the output rows. */
-int orc_prefill_anchor(const float *q, const float *k, const float *v,
-                       int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
-                       double scale, int64_t t0, int64_t t1,
-                       int32_t *idx_out, double *o_out)
+ * per (b, t, set), and the output rows. Pooling variants as in
+ * orc_decode_anchor_v: scope 0 gives one set per (b, t, KV head), scope 1 one
+ * set per (b, t) pooled over all query heads and shared by every KV head
+ * (idx_out [B, Hs, off[t1] - off[t0]], Hs = scope ? 1 : Hkv); op 0 sums,
+ * op 1 takes the maximum over the pooled heads and rows. */
+int orc_prefill_anchor_v(const float *q, const float *k, const float *v,
+                         int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                         double scale, int64_t t0, int64_t t1, int scope, int op,
+                         int32_t *idx_out, double *o_out)
 {
     if (check_shape(B, Hq, Hkv, N, D) || tile <= 0 || pct < 1 || pct > 100) return ORC_BAD_ARG;
+    if ((scope != 0 && scope != 1) || (op != 0 && op != 1)) return ORC_BAD_ARG;
+    const int Hs = scope ? 1 : Hkv;
+    const int ng = scope ? Hkv : 1;
     const int64_t T = (N + tile - 1) / tile;
     if (t0 < 0 || t1 > T || t0 >= t1) return ORC_BAD_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
@@ -432,7 +485,7 @@ int orc_prefill_anchor(const float *q, const float *k, const float *v,
     orc_prefill_offsets(N, tile, pct, off);
     const int64_t R = range_rows(N, tile, t0, t1);
     const int64_t tot = off[t1] - off[t0];
-    const int64_t n_units = (int64_t)B * (t1 - t0) * Hkv;
+    const int64_t n_units = (int64_t)B * (t1 - t0) * Hs;
     int status = ORC_OK;
 #pragma omp parallel
     {
@@ -446,25 +499,37 @@ int orc_prefill_anchor(const float *q, const float *k, const float *v,
             /* big tiles first: better balance */
 #pragma omp for schedule(dynamic)
             for (int64_t u = 0; u < n_units; ++u) {
-                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hkv));
-                int64_t rem = u % ((int64_t)B * Hkv);
-                int64_t b = rem / Hkv, g = rem % Hkv;
+                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hs));
+                int64_t rem = u % ((int64_t)B * Hs);
+                int64_t b = rem / Hs, gs = rem % Hs;
                 int64_t kt = off[tt + 1] - off[tt];
-                int32_t *S = idx_out + (b * Hkv + g) * tot + (off[tt] - off[t0]);
-                prefill_pool_unit(q, k, B, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g, P, rowbuf);
+                int32_t *S = idx_out + (b * Hs + gs) * tot + (off[tt] - off[t0]);
+                prefill_pool_unit(q, k, B, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, gs * ng, ng, op,
+                                  P, rowbuf);
                 if (select_topk(P, tt * (int64_t)tile, kt, S) != ORC_OK) {
 #pragma omp atomic write
                     status = ORC_NOMEM;
                     continue;
                 }
-                prefill_output_unit(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g,
-                                    S, kt, o_out, rowbuf, keys);
+                for (int64_t g = gs * ng; g < gs * ng + ng; ++g)
+                    prefill_output_unit(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g,
+                                        S, kt, o_out, rowbuf, keys);
             }
         }
         free(P); free(rowbuf); free(keys);
     }
     free(off);
     return status;
+}
+
+/* The method's own prefill anchor layer: per KV-head group, sum pooling. */
+int orc_prefill_anchor(const float *q, const float *k, const float *v,
+                       int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                       double scale, int64_t t0, int64_t t1,
+                       int32_t *idx_out, double *o_out)
+{
+    return orc_prefill_anchor_v(q, k, v, B, Hq, Hkv, N, D, tile, pct, scale, t0, t1, 0, 0,
+                                idx_out, o_out);
 }
 
 /* Prefill reuse layer over tiles [t0, t1): tile t of KV head g attends over

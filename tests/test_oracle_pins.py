@@ -355,3 +355,144 @@ def test_prefill_tile_range_matches_full():
     idx_r, o_r = oracle.prefill_anchor(q[:, :, 64:128], k, v, pct=10, t0=2, t1=4)
     np.testing.assert_array_equal(idx_r, idx[..., off[2]:off[4]])
     np.testing.assert_array_equal(o_r, o[:, :, 64:128])
+
+
+# ---------------------------------------------------------------- pooling variants
+# Pooling scope (the README's strategies: post-softmax pooling per KV-head
+# group, or over all heads) and operator (sum, or max-pooling).
+
+def _two_head_logits():
+    """Probabilities of three live keys for two heads, chosen so that sum and
+    max pooling disagree: A = [0.6, 0.35, 0.05], B = [~0, 0.45, 0.55].
+    sum = [0.6, 0.8, 0.6] -> key 1 first; max = [0.6, 0.45, 0.55] -> key 0."""
+    pa = np.log([0.6, 0.35, 0.05])
+    pb = np.array([-40.0, math.log(0.45), math.log(0.55)])   # e^-40 / (1 + e^-40) ~ 4e-18
+    return pa, pb
+
+
+def test_decode_pool_variants_worked_example():
+    pa, pb = _two_head_logits()      # rounded to float32 on input: values to ~1e-7
+    D = 3
+    k1 = np.eye(3, dtype=np.float32).reshape(1, 1, 3, 3)               # key j = e_j
+    v1 = (np.arange(1, 4, dtype=np.float32)[:, None] * np.array([1, 10, 100], np.float32)).reshape(1, 1, 3, 3)
+    q = (np.stack([pa, pb]) * math.sqrt(D)).astype(np.float32)[None]   # logits = q . e_j / sqrt(3)
+    # one KV head with both query heads: group scope = all heads scope
+    for scope in (0, 1):
+        idx, o, P = oracle.decode_anchor(q, k1, v1, pct=33, want_pooled=True, pool_scope=scope)
+        assert idx.tolist() == [[[1]]]
+        np.testing.assert_allclose(P[0, 0], [0.6, 0.8, 0.6], rtol=1e-6)
+        np.testing.assert_allclose(o[0, :], np.repeat(v1[0, 0, 1][None], 2, 0), rtol=1e-6)
+        idx, o, P = oracle.decode_anchor(q, k1, v1, pct=33, want_pooled=True, pool_scope=scope, pool_op=1)
+        assert idx.tolist() == [[[0]]]
+        np.testing.assert_allclose(P[0, 0], [0.6, 0.45, 0.55], rtol=1e-6)
+        np.testing.assert_allclose(o[0, :], np.repeat(v1[0, 0, 0][None], 2, 0), rtol=1e-6)
+    # two KV heads with one query head each: per-head sets differ from the shared one
+    k2 = np.repeat(k1, 2, axis=1)
+    v2 = np.concatenate([v1, 2 * v1], axis=1)
+    idx, o, _ = oracle.decode_anchor(q, k2, v2, pct=33)
+    assert idx.tolist() == [[[0], [2]]]
+    np.testing.assert_allclose(o[0], [v2[0, 0, 0], v2[0, 1, 2]], rtol=1e-6)
+    idx, o, P = oracle.decode_anchor(q, k2, v2, pct=33, want_pooled=True, pool_scope=1)
+    assert idx.tolist() == [[[1]]]
+    np.testing.assert_allclose(P[0, 0], [0.6, 0.8, 0.6], rtol=1e-6)
+    np.testing.assert_allclose(o[0], [v2[0, 0, 1], v2[0, 1, 1]], rtol=1e-6)
+    idx, _, _ = oracle.decode_anchor(q, k2, v2, pct=33, pool_scope=1, pool_op=1)
+    assert idx.tolist() == [[[0]]]
+
+
+def test_decode_pool_variant_invariants():
+    q, k, v = _decode_case(B=2, Hq=8, Hkv=2, N=257)
+    Hq = q.shape[1]
+    _, _, Pg = oracle.decode_anchor(q, k, v, pct=10, want_pooled=True)
+    _, _, Pa = oracle.decode_anchor(q, k, v, pct=10, want_pooled=True, pool_scope=1)
+    _, _, Pm = oracle.decode_anchor(q, k, v, pct=10, want_pooled=True, pool_scope=1, pool_op=1)
+    _, _, Pgm = oracle.decode_anchor(q, k, v, pct=10, want_pooled=True, pool_op=1)
+    assert Pa.shape == (2, 1, 257) and Pgm.shape == Pg.shape
+    np.testing.assert_allclose(Pa.sum(-1), np.full((2, 1), float(Hq)), rtol=1e-12)
+    # all-heads sum = sum of the group sums; max lies between sum / heads and sum
+    np.testing.assert_allclose(Pa[:, 0], Pg.sum(1), rtol=1e-12)
+    assert (Pm <= Pa * (1 + 1e-12)).all() and (Pm * Hq >= Pa * (1 - 1e-12)).all()
+    assert (Pgm <= Pg * (1 + 1e-12)).all() and (Pgm * 4 >= Pg * (1 - 1e-12)).all()
+    assert (Pm <= 1.0).all() and (Pm[:, 0] >= Pgm.max(1) * (1 - 1e-12)).all()
+
+
+def test_decode_pool_variants_brute_force_tiny():
+    """Softmax per head (torch, float64), pooled, then a full stable sort."""
+    for seed, (Hq, Hkv, N) in enumerate([(4, 2, 40), (8, 4, 65), (2, 1, 33)]):
+        q, k, v = _decode_case(B=1, Hq=Hq, Hkv=Hkv, N=N, seed=seed + 11)
+        G = Hq // Hkv
+        qt, kt = torch.from_numpy(q).double(), torch.from_numpy(k).double()
+        kr = kt.repeat_interleave(G, dim=1)
+        p = torch.softmax(torch.einsum("bhd,bhnd->bhn", qt, kr) / math.sqrt(q.shape[-1]), -1)[0].numpy()
+        for scope, op in itertools.product((0, 1), (0, 1)):
+            groups = [list(range(Hq))] if scope else [list(range(g * G, g * G + G)) for g in range(Hkv)]
+            idx, _, _ = oracle.decode_anchor(q, k, v, pct=25, pool_scope=scope, pool_op=op)
+            kk = oracle.decode_k(N, 25)
+            for s, heads in enumerate(groups):
+                P = p[heads].max(0) if op else p[heads].sum(0)
+                order = sorted(range(N), key=lambda j: (-np.float32(P[j]), j))
+                assert idx[0, s].tolist() == sorted(order[:kk]), (seed, scope, op, s)
+
+
+def test_prefill_pool_variants_worked_example():
+    """Tile 1 of a 64-row prompt (k_1 = 1 at 4 %): every row of both heads
+    sees keys 0..2 with the probabilities of _two_head_logits; every other
+    key gets logit -50. sum over rows and heads = 32 * [0.6, 0.8, 0.6] -> key
+    1; max = [0.6, 0.45, 0.55] -> key 0."""
+    pa, pb = _two_head_logits()
+    N, D = 64, 4
+    k = np.zeros((1, 1, N, D), np.float32)
+    k[0, 0, :3, :3] = np.eye(3)
+    k[0, 0, 3:, 3] = -1.0                               # dead keys
+    q = np.zeros((1, 2, N, D), np.float32)
+    q[0, 0, :, :3] = 2 * pa                             # scale 1/sqrt(4) = 1/2
+    q[0, 1, :, :3] = 2 * pb
+    q[0, :, :, 3] = 100.0                               # dead keys: logit -50
+    v = np.arange(N * D, dtype=np.float32).reshape(1, 1, N, D)
+    assert oracle.topk_count(32, 4) == 1
+    for scope in (0, 1):
+        idx, _ = oracle.prefill_anchor(q, k, v, pct=4, pool_scope=scope)
+        assert idx.tolist() == [[[1]]]
+        P = oracle.prefill_pooled(q, k, 0, 1, 0, pool_scope=scope)
+        np.testing.assert_allclose(P[:3], [19.2, 25.6, 19.2], rtol=1e-6)
+        idx, _ = oracle.prefill_anchor(q, k, v, pct=4, pool_scope=scope, pool_op=1)
+        assert idx.tolist() == [[[0]]]
+        P = oracle.prefill_pooled(q, k, 0, 1, 0, pool_scope=scope, pool_op=1)
+        np.testing.assert_allclose(P[:3], [0.6, 0.45, 0.55], rtol=1e-6)
+    # two KV heads, one query head each
+    k2 = np.repeat(k, 2, axis=1)
+    v2 = np.repeat(v, 2, axis=1)
+    idx, _ = oracle.prefill_anchor(q, k2, v2, pct=4)
+    assert idx.tolist() == [[[0], [2]]]
+    idx, o = oracle.prefill_anchor(q, k2, v2, pct=4, pool_scope=1)
+    assert idx.tolist() == [[[1]]]
+    # row 40 of head 1 attends over {1} + [32, 40]: the dead keys vanish, only key 1 counts
+    np.testing.assert_allclose(o[0, 1, 40], v2[0, 1, 1], rtol=1e-6)
+
+
+def test_prefill_pool_variant_invariants():
+    q, k, v = _prefill_case(B=1, Hq=8, Hkv=2, N=128)
+    Hq = 8
+    for t in range(4):
+        Pa = oracle.prefill_pooled(q, k, 0, t, 0, pool_scope=1)
+        Pg = sum(oracle.prefill_pooled(q, k, 0, t, g) for g in range(2))
+        np.testing.assert_allclose(Pa.sum(), 32.0 * Hq, rtol=1e-12)
+        np.testing.assert_allclose(Pa, Pg, rtol=1e-12, atol=1e-15)
+        Pm = oracle.prefill_pooled(q, k, 0, t, 0, pool_scope=1, pool_op=1)
+        assert (Pm <= Pa * (1 + 1e-12) + 1e-300).all()
+        assert (Pm * 32 * Hq >= Pa * (1 - 1e-12)).all() and (Pm <= 1.0).all()
+    # one KV head: all-heads scope is the group scope
+    q1, k1, v1 = _prefill_case(B=1, Hq=4, Hkv=1, N=96, seed=3)
+    for op in (0, 1):
+        a = oracle.prefill_anchor(q1, k1, v1, pct=10, pool_op=op)
+        b = oracle.prefill_anchor(q1, k1, v1, pct=10, pool_op=op, pool_scope=1)
+        assert (a[0] == b[0]).all() and np.array_equal(a[1], b[1])
+
+
+def test_prefill_shared_set_output_matches_reuse():
+    """The all-heads anchor's output equals a reuse pass over its shared set."""
+    q, k, v = _prefill_case(B=1, Hq=4, Hkv=2, N=128, seed=5)
+    for op in (0, 1):
+        idx, o = oracle.prefill_anchor(q, k, v, pct=10, pool_scope=1, pool_op=op)
+        o2 = oracle.prefill_reuse(q, k, v, idx, np.zeros(2, np.int32), pct=10)
+        np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
