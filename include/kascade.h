@@ -25,9 +25,10 @@
  *       prefill: q, o [B, Hq, N, D];     k, v [B, Hkv, N, D] (strides below)
  *     Query head h uses KV head h / (Hq / Hkv).
  *   - Index sets are int32 key positions in ascending order.
- *       decode : [B, Hkv, kd]     kd = max(1, kas_topk_count(N, pct))
- *       prefill: [B, Hkv, total]  CSR over query tiles; tile t's set is
+ *       decode : [B, Hs, kd]      kd = max(1, kas_topk_count(N, pct))
+ *       prefill: [B, Hs, total]   CSR over query tiles; tile t's set is
  *                [offsets[t], offsets[t+1]) of kas_prefill_index_offsets.
+ *     Hs = Hkv, or 1 when desc->pool_scope is 1 (one shared set).
  *   - Selection is exact: the k largest pooled scores, ties to the lower key
  *     index, scores compared as fp32.
  */
@@ -76,6 +77,17 @@ typedef struct kas_desc {
   float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
   int64_t kv_batch_stride;  /* elements between batches of k/v; 0 = Hkv*N*D */
   int64_t kv_head_stride;   /* elements between KV heads of k/v; 0 = N*D */
+  /* Anchor selection variants (README "Reproducibility": strategies that pool
+   * post-softmax scores per KV-head group or over all heads). Zero is the
+   * method's own selection. */
+  int32_t pool_scope;   /* 0: one index set per KV head, pooled over the
+                           Hq/Hkv query heads sharing it (sets [B, Hkv, ..]);
+                           1: one set per batch row (decode) or tile
+                           (prefill), pooled over all Hq query heads and shared
+                           by every KV head (sets [B, 1, ..]); Hq <= 256 */
+  int32_t pool_op;      /* 0: pooled score = sum of the heads' (and, in
+                           prefill, the tile rows') probabilities; 1: their
+                           maximum */
 } kas_desc_t;
 
 /* round-half-up(pct * n / 100) clamped to [0, n]; 0 for n <= 0 or pct <= 0.
@@ -97,7 +109,9 @@ kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* byte
  * N keys, each head's softmax, the probabilities summed over the G heads
  * (head-aware pooling), the exact Top-kd of that pooled score written to
  * idx_out[b, g, :] ascending, and o[b, h] = attention of head h renormalised
- * over the selected keys. idx_out: [B, Hkv, kd] int32; o: [B, Hq, D]. */
+ * over the selected keys. idx_out: [B, Hkv, kd] int32; o: [B, Hq, D].
+ * pool_scope 1 pools all Hq heads into one set idx_out[b, 0, :] that every
+ * head attends over; pool_op 1 pools by maximum instead of sum. */
 kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void* k,
                                const void* v, int32_t* idx_out, void* o,
                                void* ws, size_t ws_bytes, void* stream);
@@ -108,7 +122,8 @@ kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void
  * same N and pct) using this layer's own q, k, v.
  * anchor_idx: [B, anchor_kv_heads, kd]; head_map: device int32 [Hkv] with
  * values in [0, anchor_kv_heads) (trusted on the device; NULL = identity,
- * which needs anchor_kv_heads == Hkv). o: [B, Hq, D]. */
+ * which needs anchor_kv_heads == Hkv, or every KV head reading set 0 when
+ * anchor_kv_heads == 1, as for an anchor with pool_scope 1). o: [B, Hq, D]. */
 kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void* k,
                               const void* v, const int32_t* anchor_idx,
                               int32_t anchor_kv_heads, const int32_t* head_map, void* o,
@@ -120,6 +135,8 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
  * are summed over the tile's rows and the group's heads; the exact Top-k_t
  * is tile t's set. Row i of tile t then attends over that set plus its causal
  * diagonal keys [tile*t, i]. idx_out: [B, Hkv, total] CSR; o: [B, Hq, N, D].
+ * pool_scope 1 pools the tile's rows of all Hq heads into one set per tile
+ * (idx_out [B, 1, total]); pool_op 1 pools by maximum.
  * bf16 only. KAS_ERR_UNSUPPORTED when the index set of one KV head would
  * exceed 2^31 - 1 entries (total; about N > 1.17M at 10 %) or a KV head's
  * slice of k or v reaches 2^31 bytes (N * D * 2). */

@@ -43,6 +43,8 @@ class KasDesc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("kv_batch_stride", ctypes.c_int64),
         ("kv_head_stride", ctypes.c_int64),
+        ("pool_scope", ctypes.c_int32),
+        ("pool_op", ctypes.c_int32),
     ]
 
 
@@ -98,7 +100,8 @@ def _check(rc: int, where: str) -> None:
 
 def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
               topk_pct: int, dtype: torch.dtype, tile: int = 32, softmax_scale: float = 0.0,
-              kv_batch_stride: int = 0, kv_head_stride: int = 0) -> KasDesc:
+              kv_batch_stride: int = 0, kv_head_stride: int = 0, pool_scope: int = 0,
+              pool_op: int = 0) -> KasDesc:
     if dtype == torch.bfloat16:
         dt = DTYPE_BF16
     elif dtype == torch.float32:
@@ -106,7 +109,7 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
     else:
         raise KasError(2, "make_desc", f"dtype {dtype} not supported")
     return KasDesc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, topk_pct, tile, dt,
-                   softmax_scale, kv_batch_stride, kv_head_stride)
+                   softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op)
 
 
 def topk_count(n: int, pct: int) -> int:
@@ -149,7 +152,7 @@ def _ws(desc: KasDesc, op: int, ws: Optional[torch.Tensor], device) -> torch.Ten
 
 
 def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale: float,
-               tile: int = 32) -> KasDesc:
+               tile: int = 32, pool_scope: int = 0, pool_op: int = 0) -> KasDesc:
     if prefill:
         B, Hq, N, D = q.shape
     else:
@@ -159,18 +162,21 @@ def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale:
     if k.stride(3) != 1 or k.stride(2) != D:
         raise KasError(1, "desc", "k/v rows must be contiguous [.., N, D]")
     return make_desc(B, Hq, Hkv, D, N, pct, q.dtype, tile=tile, softmax_scale=scale,
-                     kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1))
+                     kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1),
+                     pool_scope=pool_scope, pool_op=pool_op)
 
 
-def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None
-                  ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hkv,kd], o [B,Hq,D])."""
-    desc = _desc_from(q, k, pct, False, scale)
+def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
+                  pool_scope: int = 0, pool_op: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hs,kd], o [B,Hq,D]); Hs = Hkv, or 1
+    with pool_scope=1 (one set pooled over all heads)."""
+    desc = _desc_from(q, k, pct, False, scale, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "decode_anchor", "k and v must share strides")
     kd = decode_k(desc.seq_len, pct)
     if idx_out is None:
-        idx_out = torch.empty((desc.batch, desc.n_kv_heads, kd), dtype=torch.int32, device=q.device)
+        hs = 1 if pool_scope else desc.n_kv_heads
+        idx_out = torch.empty((desc.batch, hs, kd), dtype=torch.int32, device=q.device)
     if o is None:
         o = torch.empty_like(q)
     ws = _ws(desc, OP_DECODE_ANCHOR, ws, q.device)
@@ -194,15 +200,17 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
     return o
 
 
-def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None
-                   ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> (idx int32 [B,Hkv,total] CSR, o [B,Hq,N,D])."""
-    desc = _desc_from(q, k, pct, True, scale)
+def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
+                   pool_scope: int = 0, pool_op: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> (idx int32 [B,Hs,total] CSR, o [B,Hq,N,D]);
+    Hs as in decode_anchor."""
+    desc = _desc_from(q, k, pct, True, scale, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_anchor", "k and v must share strides")
     total = int(prefill_offsets(desc)[-1])
     if idx_out is None:
-        idx_out = torch.empty((desc.batch, desc.n_kv_heads, max(total, 1)), dtype=torch.int32,
+        hs = 1 if pool_scope else desc.n_kv_heads
+        idx_out = torch.empty((desc.batch, hs, max(total, 1)), dtype=torch.int32,
                               device=q.device)
     if o is None:
         o = torch.empty_like(q)

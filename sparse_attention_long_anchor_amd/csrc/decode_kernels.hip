@@ -159,18 +159,29 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ dec_pool
 
-template <int G>
+// One workgroup per (4096-key chunk, set): each head's softmax statistics
+// from the score pass's per-chunk (max, sum) pairs, then per key the heads'
+// probabilities pooled (OP 0: sum, OP 1: max) and the first-digit histogram
+// of the pooled scores. A set is one (b, KV head) over its G query heads, or
+// (ALL) one b over all Hkv * G heads.
+template <int G, int OP, bool ALL>
 __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
+  constexpr int NS = ALL ? kMaxPoolHeads : G;
   __shared__ uint32_t s_hist[kBins1];
   __shared__ float s_tmp[4];
-  __shared__ float s_M[G], s_iL[G];
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ float s_M[NS], s_iL[NS];
+  const int chunk = blockIdx.x, b = blockIdx.z;
+  const int g0 = ALL ? 0 : blockIdx.y;
+  const int nh = ALL ? a.Hkv * G : G;                         // heads pooled into the set
+  const int64_t unit = ALL ? b : (int64_t)b * a.Hkv + g0;     // set: pooled row, histogram
   const int tid = threadIdx.x;
-  const int64_t unit = (int64_t)b * a.Hkv + g;
   for (int i = tid; i < kBins1; i += 256) s_hist[i] = 0u;
 
-  const float* st = a.stats + unit * a.n_score_chunks * G * 2;
-  for (int h = 0; h < G; ++h) {
+  // head x of the set is query head r = x % G of KV head g0 + x / G
+  for (int x = 0; x < nh; ++x) {
+    const int64_t ug = (int64_t)b * a.Hkv + g0 + x / G;
+    const int h = x % G;
+    const float* st = a.stats + ug * a.n_score_chunks * G * 2;
     float m = kNegInf;
     for (int c = tid; c < a.n_score_chunks; c += 256) m = fmaxf(m, st[(c * G + h) * 2]);
     const float M = block_max_256(m, s_tmp);
@@ -180,25 +191,45 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
       l += (mc == kNegInf) ? 0.f : st[(c * G + h) * 2 + 1] * exp2_fast(mc - M);
     }
     const float L = block_sum_256(l, s_tmp);
-    if (tid == 0) { s_M[h] = M; s_iL[h] = 1.0f / L; }
+    if (tid == 0) { s_M[x] = M; s_iL[x] = 1.0f / L; }
   }
   __syncthreads();
-  float M[G], iL[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { M[h] = s_M[h]; iL[h] = s_iL[h]; }
+  auto pool = [](float acc, float p) __attribute__((always_inline)) { return OP ? fmaxf(acc, p) : acc + p; };
 
-  const float* lg = a.logits + unit * a.N * G;
   float* P = a.pooled + unit * a.pstride;
   const int64_t base = (int64_t)chunk * kSelChunk;
-#pragma unroll 4
-  for (int i = 0; i < kSelChunk / 256; ++i) {
-    const int64_t j = base + i * 256 + tid;
-    if (j < a.N) {
-      float acc = 0.f;
+  if (!ALL) {
+    float M[G], iL[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc += exp2_fast(lg[j * G + h] - M[h]) * iL[h];
-      P[j] = acc;
-      atomicAdd(&s_hist[__float_as_uint(acc) >> 21], 1u);
+    for (int h = 0; h < G; ++h) { M[h] = s_M[h]; iL[h] = s_iL[h]; }
+    const float* lg = a.logits + unit * a.N * G;
+#pragma unroll 4
+    for (int i = 0; i < kSelChunk / 256; ++i) {
+      const int64_t j = base + i * 256 + tid;
+      if (j < a.N) {
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc = pool(acc, exp2_fast(lg[j * G + h] - M[h]) * iL[h]);
+        P[j] = acc;
+        atomicAdd(&s_hist[__float_as_uint(acc) >> 21], 1u);
+      }
+    }
+  } else {
+    // heads in KV-head order, each KV head's G logits of a key contiguous
+    const int64_t gstride = a.N * G;
+    const float* lg0 = a.logits + (int64_t)b * a.Hkv * gstride;
+    for (int i = 0; i < kSelChunk / 256; ++i) {
+      const int64_t j = base + i * 256 + tid;
+      if (j < a.N) {
+        float acc = 0.f;
+        for (int g = 0; g < a.Hkv; ++g) {
+          const float* lg = lg0 + g * gstride + j * G;
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc = pool(acc, exp2_fast(lg[h] - s_M[g * G + h]) * s_iL[g * G + h]);
+        }
+        P[j] = acc;
+        atomicAdd(&s_hist[__float_as_uint(acc) >> 21], 1u);
+      }
     }
   }
   __syncthreads();
@@ -1187,16 +1218,25 @@ hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   return ctx.end(K_DEC_SCORE);
 }
 
-hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
-  dim3 grid(a.n_sel_chunks, a.Hkv, a.B);
-  ctx.begin(K_DEC_POOL);
+template <int OP, bool ALL>
+static hipError_t pool_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& ctx) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_pool_kernel<1>), grid, dim3(256), ctx, a); break;
-    case 2: KAS_LAUNCH((dec_pool_kernel<2>), grid, dim3(256), ctx, a); break;
-    case 4: KAS_LAUNCH((dec_pool_kernel<4>), grid, dim3(256), ctx, a); break;
-    case 8: KAS_LAUNCH((dec_pool_kernel<8>), grid, dim3(256), ctx, a); break;
+    case 1: KAS_LAUNCH((dec_pool_kernel<1, OP, ALL>), grid, dim3(256), ctx, a); break;
+    case 2: KAS_LAUNCH((dec_pool_kernel<2, OP, ALL>), grid, dim3(256), ctx, a); break;
+    case 4: KAS_LAUNCH((dec_pool_kernel<4, OP, ALL>), grid, dim3(256), ctx, a); break;
+    case 8: KAS_LAUNCH((dec_pool_kernel<8, OP, ALL>), grid, dim3(256), ctx, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipSuccess;
+}
+
+hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
+  dim3 grid(a.n_sel_chunks, a.pool_all ? 1 : a.Hkv, a.B);
+  ctx.begin(K_DEC_POOL);
+  hipError_t e;
+  if (a.pool_all) e = a.pool_op ? pool_launch<1, true>(a, grid, ctx) : pool_launch<0, true>(a, grid, ctx);
+  else e = a.pool_op ? pool_launch<1, false>(a, grid, ctx) : pool_launch<0, false>(a, grid, ctx);
+  if (e != hipSuccess) return e;
   return ctx.end(K_DEC_POOL);
 }
 
@@ -1206,16 +1246,16 @@ hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
   const char* sel = getenv("KAS_DECODE_SELECT");
   if ((sel && strcmp(sel, "fused") == 0) || a.n_sel_chunks > kMaxSelChunks) {
     ctx.begin(K_SEL_FUSED);
-    KAS_LAUNCH(sel_fused_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx, a);
+    KAS_LAUNCH(sel_fused_kernel, dim3((unsigned)a.sel_units), dim3(kSelThreads), ctx, a);
     return ctx.end(K_SEL_FUSED);
   }
-  dim3 grid(a.n_sel_chunks, a.B * a.Hkv);
+  dim3 grid(a.n_sel_chunks, (unsigned)a.sel_units);
   hipError_t e;
   ctx.begin(K_SEL_CAND);
   KAS_LAUNCH(sel_cand_kernel, grid, dim3(256), ctx, a);
   if ((e = ctx.end(K_SEL_CAND)) != hipSuccess) return e;
   ctx.begin(K_SEL_RESOLVE);
-  KAS_LAUNCH(sel_resolve_kernel, dim3(a.B * a.Hkv), dim3(kSelThreads), ctx, a);
+  KAS_LAUNCH(sel_resolve_kernel, dim3((unsigned)a.sel_units), dim3(kSelThreads), ctx, a);
   if ((e = ctx.end(K_SEL_RESOLVE)) != hipSuccess) return e;
   ctx.begin(K_SEL_COMPACT);
   KAS_LAUNCH(sel_compact_kernel, grid, dim3(256), ctx, a);

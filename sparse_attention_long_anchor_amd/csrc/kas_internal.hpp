@@ -23,6 +23,7 @@ enum KernelId {
   K_PRE_ATTN,
   K_DEC_DENSE,
   K_PRE_DENSE,
+  K_PRE_POOL_HEADS,
   K_COUNT_
 };
 const char* kernel_name(int id);
@@ -50,6 +51,7 @@ constexpr int kBins1 = 2048, kBins2 = 2048, kBins3 = 1024;
 constexpr int kHistWords = kBins1 + kBins2 + kBins3;
 constexpr int kSelChunk = 4096;         // scores per selection workgroup
 constexpr int kMaxSelChunks = 4096;     // chunks the chunked selection resolves in LDS
+constexpr int kMaxPoolHeads = 256;      // query heads one all-heads pooled set may cover
 
 struct DecodeArgs {
   const void* q;
@@ -80,6 +82,10 @@ struct DecodeArgs {
   float* part_o;                    // [B, Hq, nsplit, D]
   float* part_ml;                   // [B, Hq, nsplit, 2]
   int nsplit, split_rows;
+  // selection variants: pooled score = sum (0) or max (1) of the heads'
+  // probabilities; pool_all: one set per batch row over all heads
+  int pool_op, pool_all;
+  int64_t sel_units;                // index sets selected: B * Hkv, or B with pool_all
 };
 
 hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);

@@ -32,6 +32,10 @@ struct PrefillArgs {
   size_t pooled_floats;             // capacity of `pooled`
   int t_begin, t_end;               // tile range of the current pool/select launch
   int sel_cap;                      // select: largest first-digit bin resolved in LDS
+  // selection variants: pooled score = sum (0) or max (1) over the tile's rows
+  // and the heads; pool_all: one set per tile over all heads, Hsel sets per
+  // (b, tile) in idx_out (Hkv, or 1 with pool_all)
+  int pool_op, pool_all, Hsel;
 };
 
 size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);

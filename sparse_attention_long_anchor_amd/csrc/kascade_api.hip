@@ -39,7 +39,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
-    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense"};
+    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
 
@@ -110,6 +110,7 @@ struct Shape {
   int B, Hq, Hkv, D, G;
   int64_t N;
   int pct, tile, dtype;
+  int scope, op;                    // anchor pooling variant (kas_desc_t.pool_scope / pool_op)
   float scale;
   int64_t kv_hs, kv_bs;
   size_t esize;
@@ -145,6 +146,10 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
     return fail(KAS_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
   if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
     return fail(KAS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if ((d->pool_scope != 0 && d->pool_scope != 1) || (d->pool_op != 0 && d->pool_op != 1))
+    return fail(KAS_ERR_INVALID_ARGUMENT, "pool_scope and pool_op must be 0 or 1");
+  if (d->pool_scope == 1 && d->n_q_heads > kMaxPoolHeads)
+    return fail(KAS_ERR_UNSUPPORTED, "pooling over all heads supports at most %d query heads", kMaxPoolHeads);
   if (prefill) {
     if (d->dtype != KAS_DTYPE_BF16) return fail(KAS_ERR_UNSUPPORTED, "prefill supports bf16 only");
     if (d->tile != 32) return fail(KAS_ERR_UNSUPPORTED, "prefill tile must be 32 (got %d)", d->tile);
@@ -152,6 +157,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   }
   s.B = d->batch; s.Hq = d->n_q_heads; s.Hkv = d->n_kv_heads; s.D = d->head_dim; s.G = G;
   s.N = d->seq_len; s.pct = d->topk_pct; s.tile = d->tile; s.dtype = d->dtype;
+  s.scope = d->pool_scope; s.op = d->pool_op;
   s.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
   s.esize = d->dtype == KAS_DTYPE_BF16 ? 2 : 4;
   s.kv_hs = d->kv_head_stride ? d->kv_head_stride : s.N * s.D;
@@ -262,6 +268,8 @@ static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, c
   a.pstride = (s.N + 3) / 4 * 4;
   a.score_rows = p.score_rows; a.n_score_chunks = p.n_score_chunks; a.n_sel_chunks = p.n_sel_chunks;
   a.split_rows = p.split_rows; a.nsplit = p.nsplit;
+  a.pool_op = s.op; a.pool_all = s.scope;
+  a.sel_units = (int64_t)s.B * (s.scope ? 1 : s.Hkv);
   if (anchor) {
     a.logits = (float*)(ws + p.off_logits);
     a.stats = (float*)(ws + p.off_stats);
@@ -358,7 +366,8 @@ kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void
   fill_decode_args(s, p, true, (char*)ws, a);
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx_out = idx_out;
-  a.idx = idx_out; a.Hkv_a = s.Hkv; a.head_map = nullptr;
+  // the output reads the selected sets back: one per KV head, or one shared
+  a.idx = idx_out; a.Hkv_a = s.scope ? 1 : s.Hkv; a.head_map = nullptr;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
   if ((e = launch_decode_score(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
@@ -380,8 +389,9 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
     return st;
   if (!anchor_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_idx is NULL");
   if (anchor_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_kv_heads must be >= 1");
-  if (!head_map && anchor_kv_heads != s.Hkv)
-    return fail(KAS_ERR_INVALID_ARGUMENT, "identity head map needs anchor_kv_heads == n_kv_heads");
+  if (!head_map && anchor_kv_heads != s.Hkv && anchor_kv_heads != 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT,
+                "without a head map, anchor_kv_heads must be n_kv_heads (identity) or 1 (shared set)");
   DecodePlan p = plan_decode(s, false);
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a;
@@ -411,7 +421,8 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, true);
   a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
-  a.idx = idx_out; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = total;
+  a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
+  a.idx = idx_out; a.Hkv_a = a.Hsel; a.head_map = nullptr; a.total = total;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e = launch_prefill_anchor(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_anchor");
@@ -430,8 +441,9 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
     return st;
   if (!anchor_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_idx is NULL");
   if (anchor_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_kv_heads must be >= 1");
-  if (!head_map && anchor_kv_heads != s.Hkv)
-    return fail(KAS_ERR_INVALID_ARGUMENT, "identity head map needs anchor_kv_heads == n_kv_heads");
+  if (!head_map && anchor_kv_heads != s.Hkv && anchor_kv_heads != 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT,
+                "without a head map, anchor_kv_heads must be n_kv_heads (identity) or 1 (shared set)");
   int64_t total = 0;
   if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
   if ((st = check_prefill_limits(s, total))) return st;

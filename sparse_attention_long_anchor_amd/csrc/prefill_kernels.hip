@@ -386,7 +386,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 // key block before a tile, each wave (query head) forms S = Q.K^T, the
 // probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
 // waves' sums are added through LDS (double-buffered, one barrier per block).
-template <int D, int G>
+template <int D, int G, int OP = 0>
 __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   constexpr int KC = D / 16;
   using KD = KDma<D, G>;
@@ -442,13 +442,16 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) ka[c] = KD::read(sk, n32, 2 * c + hh);
   };
-  // Column sums of one tile-block over the wave's 32 query rows; both lane
-  // halves store their (equal) copy, so no lane branch splits the block.
+  // Column sums (OP 1: maxima) of one tile-block over the wave's 32 query
+  // rows; both lane halves store their (equal) copy, so no lane branch splits
+  // the block.
+  auto pool = [](float x, float p) __attribute__((always_inline)) { return OP ? fmaxf(x, p) : x + p; };
+  auto pool_halves = [](float x) __attribute__((always_inline)) { return OP ? xor32_max(x) : xor32_add(x); };
   auto colsum = [&](const f32x16& acc, const float* lse, float* dst) __attribute__((always_inline)) {
     float col = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) col += exp2_fast(fmaf(acc[r], cs, -lse[r]));
-    col = xor32_add(col);
+    for (int r = 0; r < 16; ++r) col = pool(col, exp2_fast(fmaf(acc[r], cs, -lse[r])));
+    col = pool_halves(col);
     dst[lane] = col;
   };
   // An MFMA chain with the probability terms of an earlier, independent
@@ -462,11 +465,11 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
 #pragma unroll
-      for (int e = 0; e < TPM; ++e) col += exp2_fast(fmaf(prev[TPM * c + e], cs, -lse[TPM * c + e]));
+      for (int e = 0; e < TPM; ++e) col = pool(col, exp2_fast(fmaf(prev[TPM * c + e], cs, -lse[TPM * c + e])));
       acc = mfma32(qa[c], ka[c], acc);
       __builtin_amdgcn_sched_barrier(0);
     }
-    col = xor32_add(col);
+    col = pool_halves(col);
     dst[lane] = col;
     return acc;
   };
@@ -494,12 +497,12 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     else if (st == 1) fn(St1{});
     else fn(St2{});
   };
-  // Sum the G heads' column sums of (tile, block) and write them out.
+  // Pool the G heads' column sums (maxima) of (tile, block) and write them out.
   auto emit = [&](int tile, int kb, int writer_wave) __attribute__((always_inline)) {
     if (w == writer_wave && hh == 0) {
       float sum = 0.f;
 #pragma unroll
-      for (int x = 0; x < G; ++x) sum += s_col[kb & 1][tile][x][n32];
+      for (int x = 0; x < G; ++x) sum = pool(sum, s_col[kb & 1][tile][x][n32]);
       (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
     }
   };
@@ -556,6 +559,29 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ pooling over all heads
+
+// For one set per tile over all heads: the KV heads' pooled rows of (b, t)
+// summed (OP 1: max) in KV-head order into KV head 0's row, in place. One
+// workgroup per (tile, b); 16-byte accesses (rows are 128-byte aligned and
+// 32 t long).
+template <int OP>
+__global__ __launch_bounds__(256) void pre_pool_heads_kernel(PrefillArgs a) {
+  const int t = a.t_begin + blockIdx.x, b = blockIdx.y;
+  if (t < 1) return;
+  const int n4 = kTile * t / 4;
+  f32x4* dst = reinterpret_cast<f32x4*>(a.pooled + pool_slot(a, b, 0, t));
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    f32x4 acc = dst[i];
+    for (int g = 1; g < a.Hkv; ++g) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(a.pooled + pool_slot(a, b, g, t))[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = OP ? fmaxf(acc[e], x[e]) : acc[e] + x[e];
+    }
+    dst[i] = acc;
+  }
+}
+
 // ------------------------------------------------------------------ Top-k per tile
 
 // One workgroup per (tile, KV head): an exact radix select over the tile's
@@ -583,7 +609,7 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   const int o0 = a.offsets[t];
   const uint32_t k = (uint32_t)(a.offsets[t + 1] - o0);
   if (k == 0) return;
-  int32_t* out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.total + o0;
+  int32_t* out = a.idx_out + ((int64_t)b * a.Hsel + g) * a.total + o0;   // g < Hsel
   if (k >= (uint32_t)n) {
     for (int j = tid; j < n; j += 256) out[j] = j;
     return;
@@ -1078,6 +1104,7 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   a.T = (int)(N / kTile);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.kv_bstride = kv_bs; a.kv_hstride = kv_hs;
+  a.Hsel = Hkv;
   PrefillPlan p = plan(B, Hq, Hkv, N, anchor);
   // KAS_PREFILL_SELECT_CAP lowers the LDS candidate cap of the select (0 sends
   // every tile through the in-place histogram passes)
@@ -1173,9 +1200,16 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
     a.t_end = tb;
     dim3 pgrid((tb + 1) / 2 - ta / 2, a.Hkv, a.B);
     ctx.begin(K_PRE_POOL);
-    KAS_DISPATCH_DG(pre_pool_kernel, pgrid, ctx, a);
+    if (a.pool_op) KAS_DISPATCH_DGX(pre_pool_kernel, 1, pgrid, ctx, a);
+    else KAS_DISPATCH_DGX(pre_pool_kernel, 0, pgrid, ctx, a);
     if ((e = ctx.end(K_PRE_POOL)) != hipSuccess) return e;
-    dim3 grid(tb - ta, a.Hkv, a.B);
+    if (a.pool_all) {
+      ctx.begin(K_PRE_POOL_HEADS);
+      if (a.pool_op) KAS_LAUNCH_P(pre_pool_heads_kernel<1>, dim3(tb - ta, a.B), dim3(256), ctx, a);
+      else KAS_LAUNCH_P(pre_pool_heads_kernel<0>, dim3(tb - ta, a.B), dim3(256), ctx, a);
+      if ((e = ctx.end(K_PRE_POOL_HEADS)) != hipSuccess) return e;
+    }
+    dim3 grid(tb - ta, a.Hsel, a.B);
     ctx.begin(K_PRE_SELECT);
     KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx, a);
     if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;

@@ -74,7 +74,15 @@ def test_descriptor_validation():
         (b.make_desc(0, 32, 8, 128, 64, 10, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),   # batch
         (b.make_desc(1, 32, 8, 128, 0, 10, torch.bfloat16), b.OP_DECODE_ANCHOR, 1),    # seq_len
         (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, kv_head_stride=64), b.OP_DECODE_ANCHOR, 1),
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, pool_scope=2), b.OP_DECODE_ANCHOR, 1),
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, pool_op=-1), b.OP_PREFILL_ANCHOR, 1),
+        (b.make_desc(1, 512, 64, 128, 64, 10, torch.bfloat16, pool_scope=1), b.OP_DECODE_ANCHOR, 2),
     ]
+    # the variants keep the workspace of the default selection
+    for scope, op in [(0, 1), (1, 0), (1, 1)]:
+        dv = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16, pool_scope=scope, pool_op=op)
+        assert b.workspace_size(dv, b.OP_DECODE_ANCHOR) == b.workspace_size(ok, b.OP_DECODE_ANCHOR)
+        assert b.workspace_size(dv, b.OP_PREFILL_ANCHOR) == b.workspace_size(ok, b.OP_PREFILL_ANCHOR)
     for d, op, want in bad:
         assert _status(lambda: b.workspace_size(d, op)) == want
     L = b._load()
@@ -99,7 +107,7 @@ def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
     r = L.kas_decode_anchor(ctypes.byref(d), fake, fake, fake, fake, fake, fake, need - 1, None)
     assert r == 3
     r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, fake, 3, None, fake, fake, 1 << 30, None)
-    assert r == 1 and b"identity head map" in L.kas_last_error()
+    assert r == 1 and b"without a head map" in L.kas_last_error()
     r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, None, 2, None, fake, fake, 1 << 30, None)
     assert r == 1
     # prefill sizes past the 32-bit CSR offsets / row offsets: rejected

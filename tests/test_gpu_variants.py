@@ -1,0 +1,180 @@
+"""GPU parity of the anchor selection variants against the oracle, through
+the C ABI: pooling over all query heads (one set shared by every KV head, the
+README's all-heads-pooled strategy) and max-pooling instead of the sum, in
+decode and prefill, with reuse layers reading the shared sets.
+
+Index sets must match the oracle's exactly except inside the near-tie band
+(relative 1e-4 of the oracle's k-th pooled score, using the oracle's pooled
+scores of the same variant); outputs within 2e-2 (bf16) / 1e-4 (fp32).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import oracle
+from parity_util import TOL, assert_index_set, max_abs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+VARIANTS = [(0, 1), (1, 0), (1, 1)]          # (pool_scope, pool_op); (0, 0) is the default path
+VIDS = ["group_max", "all_sum", "all_max"]
+
+
+def _kas():
+    import sparse_attention_long_anchor_amd as kas
+    return kas
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_decode(w, q, k, v, pct, scope, op, label):
+    kas = _kas()
+    _say(f"[decode anchor {VIDS[VARIANTS.index((scope, op))]}] {label}: B={w.batch} Hq={w.n_q_heads} "
+         f"Hkv={w.n_kv_heads} N={w.seq_len} {w.dtype}")
+    idx, o = kas.decode_anchor(q, k, v, pct, pool_scope=scope, pool_op=op)
+    torch.cuda.synchronize()
+    Hs = 1 if scope else w.n_kv_heads
+    assert tuple(idx.shape) == (w.batch, Hs, oracle.decode_k(w.seq_len, pct))
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    oidx, oo, pooled = oracle.decode_anchor(qn, kn, vn, pct, want_pooled=True, pool_scope=scope, pool_op=op)
+    kk = oracle.decode_k(w.seq_len, pct)
+    gidx = idx.cpu().numpy()
+    swaps = 0
+    for b in range(w.batch):
+        for s in range(Hs):
+            swaps += assert_index_set(gidx[b, s], oidx[b, s], pooled[b, s], kk, where=f"{label} b{b} s{s}")
+    hm = np.zeros(w.n_kv_heads, np.int32) if scope else np.arange(w.n_kv_heads, dtype=np.int32)
+    o_same = oracle.decode_reuse(qn, kn, vn, gidx, hm)
+    err_same, err_e2e = max_abs(_np(o), o_same), max_abs(_np(o), oo)
+    tol = TOL[w.dtype]
+    _say(f"    near-tie swaps={swaps} max|o-o_oracle(same set)|={err_same:.3g} max|o-o_oracle|={err_e2e:.3g}")
+    assert err_same <= tol and err_e2e <= tol
+    return idx
+
+
+DECODE_SHAPES = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct)
+    ("f32_d64_g4", 1, 8, 2, 64, 2048, "f32", 10),
+    ("bf16_d128_g4_ragged", 2, 32, 8, 128, 5037, "bf16", 10),
+    ("bf16_d64_g1", 2, 4, 4, 64, 3001, "bf16", 10),
+    ("bf16_d128_g8", 1, 16, 2, 128, 4099, "bf16", 10),
+    ("bf16_n17", 1, 8, 2, 128, 17, "bf16", 30),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[s[0] for s in DECODE_SHAPES])
+def test_decode_variant_anchor_then_reuse(shape, variant):
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct = shape
+    scope, op = variant
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx = _check_decode(w, q, k, v, pct, scope, op, label)
+    # a reuse layer reads the shared set (no head map) or a mapped per-head set
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    if scope:
+        o2 = kas.decode_reuse(q2, k2, v2, idx, None, pct)
+        hm = np.zeros(Hkv, np.int32)
+    else:
+        hm = np.random.default_rng(2).integers(0, Hkv, Hkv).astype(np.int32)
+        o2 = kas.decode_reuse(q2, k2, v2, idx, torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    ref = oracle.decode_reuse(_np(q2), _np(k2), _np(v2), idx.cpu().numpy(), hm)
+    err = max_abs(_np(o2), ref)
+    _say(f"    reuse max|o-o_oracle|={err:.3g}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (0, 1)], ids=["all_sum", "group_max"])
+def test_decode_variant_full_size(variant):
+    w = inputgen.WORKLOADS["llama8b_decode_128k"]
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    _check_decode(w, q, k, v, w.topk_pct, variant[0], variant[1], w.name)
+
+
+def _check_prefill_tiles(w, q, k, v, pct, scope, op, gidx, go, tiles, label):
+    N, B, Hkv = w.seq_len, w.batch, w.n_kv_heads
+    Hs = 1 if scope else Hkv
+    off = oracle.prefill_offsets(N, 32, pct)
+    kn, vn = _np(k), _np(v)
+    gi = gidx.cpu().numpy()
+    assert gi.shape[1] == Hs
+    hm = np.zeros(Hkv, np.int32) if scope else np.arange(Hkv, dtype=np.int32)
+    worst_set, worst_e2e, swaps = 0.0, 0.0, 0
+    for t in tiles:
+        qr = _np(q[:, :, 32 * t: 32 * t + 32])
+        oidx, oo = oracle.prefill_anchor(qr, kn, vn, pct, t0=t, t1=t + 1, pool_scope=scope, pool_op=op)
+        kt = int(off[t + 1] - off[t])
+        for b in range(B):
+            for s in range(Hs):
+                gs = gi[b, s, off[t]:off[t + 1]]
+                if not np.array_equal(gs, oidx[b, s]):
+                    P = oracle.prefill_pooled(qr, kn, b, t, s, t0=t, t1=t + 1, pool_scope=scope,
+                                              pool_op=op)[: 32 * t]
+                    swaps += assert_index_set(gs, oidx[b, s], P, kt, where=f"{label} b{b} t{t} s{s}")
+        o_same = oracle.prefill_reuse(qr, kn, vn, gi, hm, pct, t0=t, t1=t + 1)
+        gor = _np(go[:, :, 32 * t: 32 * t + 32])
+        worst_set = max(worst_set, max_abs(gor, o_same))
+        worst_e2e = max(worst_e2e, max_abs(gor, oo))
+    _say(f"    tiles={list(tiles)[:8]}{'...' if len(tiles) > 8 else ''} near-tie swaps={swaps} "
+         f"max|o-o_oracle(same set)|={worst_set:.3g} max|o-o_oracle|={worst_e2e:.3g}")
+    assert worst_set <= TOL["bf16"] and worst_e2e <= TOL["bf16"]
+
+
+PREFILL_SHAPES = [
+    # (label, B, Hq, Hkv, D, N, pct)
+    ("d128_g4_n256", 1, 8, 2, 128, 256, 10),
+    ("d128_g4_b2_n1184", 2, 8, 2, 128, 1184, 10),
+    ("d64_g1_n640", 1, 2, 2, 64, 640, 10),
+    ("d128_g8_n384_pct25", 1, 16, 2, 128, 384, 25),
+    ("d128_g4_n32_single_tile", 1, 8, 2, 128, 32, 10),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VIDS)
+@pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
+def test_prefill_variant_anchor_then_reuse(shape, variant):
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, pct = shape
+    scope, op = variant
+    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, "bf16", wid=zlib.crc32(label.encode()) % 1000,
+                        topk_pct=pct)
+    _say(f"[prefill anchor {VIDS[VARIANTS.index(variant)]}] {label}: B={B} Hq={Hq} Hkv={Hkv} D={D} N={N}")
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    gidx, go = kas.prefill_anchor(q, k, v, pct, pool_scope=scope, pool_op=op)
+    torch.cuda.synchronize()
+    _check_prefill_tiles(w, q, k, v, pct, scope, op, gidx, go, range(N // 32), label)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.zeros(Hkv, np.int32)
+    o2 = kas.prefill_reuse(q2, k2, v2, gidx, None if scope else torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_reuse(_np(q2), _np(k2), _np(v2), gidx.cpu().numpy(), hm, pct)
+    err = max_abs(_np(o2), ref)
+    _say(f"    reuse max|o-o_oracle|={err:.3g}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (0, 1)], ids=["all_sum", "group_max"])
+def test_prefill_variant_full_size_sampled_tiles(variant):
+    kas = _kas()
+    w = inputgen.WORKLOADS["qwen8b_prefill_32k"]
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    _say(f"[prefill anchor {variant}] {w.name}: N={w.seq_len}")
+    gidx, go = kas.prefill_anchor(q, k, v, w.topk_pct, pool_scope=variant[0], pool_op=variant[1])
+    torch.cuda.synchronize()
+    _check_prefill_tiles(w, q, k, v, w.topk_pct, variant[0], variant[1], gidx, go, (1, 37, 500, 1023), w.name)
