@@ -202,6 +202,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
+    ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -373,6 +374,8 @@ def main():
     if not args.no_dense:
         out["dense_baseline"], out["roofline_dense"] = dense_baseline(
             args, wd, dec_state, wp, pre_state, out, torch, kas, dev)
+    if not args.no_variants:
+        out["selection_variants"] = variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
@@ -433,6 +436,60 @@ def dense_baseline(args, wd, dec_state, wp, pre_state, out, torch, kas, dev):
         r["frac"] = round(r["achieved"] / r["peak"], 4)
     return res, [dict({k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "avg_us")},
                       traffic=_traffic(r["kernel"])) for r in roof]
+
+
+VARIANTS = {"group_sum": (0, 0), "group_max": (0, 1), "all_sum": (1, 0), "all_max": (1, 1)}
+
+
+def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev):
+    """Anchor-layer time of each selection variant (pooling scope: the KV
+    head's group or all heads; operator: sum or max) on layer 0's resident
+    inputs, median of repeated calls; plus the schedule in which every layer is
+    an anchor, derived from the measured anchor-layer time."""
+    res = {}
+
+    def timed(call, reps):
+        call()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    if dec_state is not None:
+        (q, k, v, _), o, ws = dec_state[0][0], dec_state[2], dec_state[3]
+        kd = dec_state[5]
+        r = {}
+        for name, (sc, op) in VARIANTS.items():
+            idx = torch.empty((wd.batch, 1 if sc else wd.n_kv_heads, kd), dtype=torch.int32, device=dev)
+            ms = timed(lambda: kas.decode_anchor(q, k, v, wd.topk_pct, idx_out=idx, o=o, ws=ws,
+                                                 pool_scope=sc, pool_op=op), 5)
+            r[name] = round(1e3 * ms, 3)
+        res["decode_anchor_us"] = r
+        if "decode" in out:
+            res["decode_every_layer_anchor_ms_per_step"] = {
+                "value": round(wd.n_layers * out["decode"]["us_per_layer"]["anchor"] / 1e3, 4),
+                "derived": "layers x measured anchor layer"}
+    if pre_state is not None:
+        (q, k, v, _), o, ws = pre_state[0][0], pre_state[2], pre_state[3]
+        total = int(pre_state[5][-1])
+        r = {}
+        for name, (sc, op) in VARIANTS.items():
+            idx = torch.empty((wp.batch, 1 if sc else wp.n_kv_heads, total), dtype=torch.int32, device=dev)
+            ms = timed(lambda: kas.prefill_anchor(q, k, v, wp.topk_pct, idx_out=idx, o=o, ws=ws,
+                                                  pool_scope=sc, pool_op=op), 2)
+            r[name] = round(ms, 3)
+        res["prefill_anchor_ms"] = r
+        if "prefill" in out:
+            res["prefill_every_layer_anchor_ms_per_step"] = {
+                "value": round(wp.n_layers * out["prefill"]["ms_per_layer"]["anchor"], 3),
+                "derived": "layers x measured anchor layer"}
+    log(f"[bench] selection variants: {res}")
+    return res
 
 
 def _mean(xs):
