@@ -50,7 +50,11 @@ typedef enum {
   KAS_ERR_HIP = 4                 /* a HIP launch/runtime call failed */
 } kas_status_t;
 
-typedef enum { KAS_DTYPE_F32 = 0, KAS_DTYPE_BF16 = 1 } kas_dtype_t;
+/* Element type of q, k, v and o. The README's own kernels run fp16 only
+ * (README notes); bf16 and fp16 take the same paths here, with 16-bit MFMA of
+ * that type, fp32 accumulation and softmax, and probabilities rounded to the
+ * element type for P.V. fp32 is decode only. */
+typedef enum { KAS_DTYPE_F32 = 0, KAS_DTYPE_BF16 = 1, KAS_DTYPE_F16 = 2 } kas_dtype_t;
 
 typedef enum {
   KAS_OP_DECODE_ANCHOR = 0,
@@ -73,7 +77,7 @@ typedef struct kas_desc {
   int32_t topk_pct;     /* 1..100: k is this percentage of the candidates
                            (README: "k=10", "--topk 10") */
   int32_t tile;         /* prefill query tile; must be 32 (README notes) */
-  int32_t dtype;        /* kas_dtype_t. decode: F32 or BF16; prefill: BF16 */
+  int32_t dtype;        /* kas_dtype_t. decode: F32, BF16 or F16; prefill: BF16 or F16 */
   float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
   int64_t kv_batch_stride;  /* elements between batches of k/v; 0 = Hkv*N*D */
   int64_t kv_head_stride;   /* elements between KV heads of k/v; 0 = N*D */
@@ -137,7 +141,7 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
  * diagonal keys [tile*t, i]. idx_out: [B, Hkv, total] CSR; o: [B, Hq, N, D].
  * pool_scope 1 pools the tile's rows of all Hq heads into one set per tile
  * (idx_out [B, 1, total]); pool_op 1 pools by maximum.
- * bf16 only. KAS_ERR_UNSUPPORTED when the index set of one KV head would
+ * bf16 or fp16. KAS_ERR_UNSUPPORTED when the index set of one KV head would
  * exceed 2^31 - 1 entries (total; about N > 1.17M at 10 %) or a KV head's
  * slice of k or v reaches 2^31 bytes (N * D * 2). */
 kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k,
@@ -148,7 +152,7 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
  * tile t for anchor KV head head_map[g] plus the causal diagonal keys.
  * anchor_idx: [B, anchor_kv_heads, total] CSR from kas_prefill_anchor with the
  * same N, tile and pct; every index of tile t must be < tile*t (trusted on
- * the device). head_map as in kas_decode_reuse. bf16 only. The size limits
+ * the device). head_map as in kas_decode_reuse. bf16 or fp16. The size limits
  * of kas_prefill_anchor apply. */
 kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void* k,
                                const void* v, const int32_t* anchor_idx,
@@ -165,13 +169,13 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
  *
  * Decode: o[b, h] = attention of query head h over all N keys of KV head
  * h / G (split-K over the cache, then a merge of the splits). Layouts as in
- * kas_decode_anchor; F32 or BF16; workspace from
+ * kas_decode_anchor; any dtype; workspace from
  * kas_workspace_size(KAS_OP_DECODE_DENSE). */
 kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                               void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill: causal attention, row i over keys [0, i]. Layouts as in
- * kas_prefill_anchor; bf16 only; N a multiple of the tile (32). Needs no
+ * kas_prefill_anchor; bf16 or fp16; N a multiple of the tile (32). Needs no
  * workspace (ws may be NULL; kas_workspace_size(KAS_OP_PREFILL_DENSE) is 0).
  * KAS_ERR_UNSUPPORTED when a KV head's slice of k or v reaches 2^31 bytes. */
 kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,

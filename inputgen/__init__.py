@@ -50,7 +50,7 @@ class Workload:
     n_kv_heads: int
     head_dim: int
     seq_len: int
-    dtype: str               # "f32" or "bf16"
+    dtype: str               # "f32", "bf16" or "f16"
     topk_pct: int = 10
     tile: int = 32
     n_heavy: int = 0         # per (batch, KV head, layer)
@@ -65,7 +65,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
 
 WORKLOADS: Dict[str, Workload] = {

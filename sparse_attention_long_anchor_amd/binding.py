@@ -21,7 +21,7 @@ _LIB = os.path.join(_HERE, "libkascade_mi355x.so")
 
 OP_DECODE_ANCHOR, OP_DECODE_REUSE, OP_PREFILL_ANCHOR, OP_PREFILL_REUSE = 0, 1, 2, 3
 OP_DECODE_DENSE, OP_PREFILL_DENSE = 4, 5
-DTYPE_F32, DTYPE_BF16 = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 
 
 class KasError(RuntimeError):
@@ -104,6 +104,8 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
               pool_op: int = 0) -> KasDesc:
     if dtype == torch.bfloat16:
         dt = DTYPE_BF16
+    elif dtype == torch.float16:
+        dt = DTYPE_F16
     elif dtype == torch.float32:
         dt = DTYPE_F32
     else:

@@ -951,9 +951,9 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
 // load sits behind a divergent branch in the steady-state loop.
 // DENSE: the split covers keys [row0, row0 + nrows) of the cache and a row's
 // key is its position (no index loads); otherwise the same kernel.
-template <int D, int G, bool FROM_LOGITS, bool DENSE = false>
+template <int D, int G, bool FROM_LOGITS, bool DENSE = false, typename E = __bf16>
 __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
-  using QK = QKMfma<__bf16, D>;
+  using QK = QKMfma<E, D>;
   constexpr int NT = D / 16;            // output tiles of 16 dims
   constexpr int VROW = 2 * D + 32;      // bytes per staged V row
   constexpr int VP = D / 8;             // 16-byte parts per V row
@@ -975,12 +975,12 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   const int32_t* idx = DENSE ? nullptr : a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
-  const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const __bf16* vb = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kb = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const E* vb = (const E*)a.v + b * a.kv_bstride + g * a.kv_hstride;
   const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
   typename QK::QFrag qf;
   if (!FROM_LOGITS)
-    QK::load_q(qf, (const __bf16*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
+    QK::load_q(qf, (const E*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
   char* sv = s_v[wave];
   uint16_t* sp = s_p[wave];
   reinterpret_cast<uint32_t*>(sp)[lane] = 0u;
@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
       const float p = exp2_fast(t - mn);   // -inf -> 0
       ls[r] = ls[r] * al[r] + p;
       ml[r] = mn;
-      if (4 * q4 + r < G) sp[(4 * q4 + r) * 16 + c16] = f32_to_bf16_rne(p);
+      if (4 * q4 + r < G) sp[(4 * q4 + r) * 16 + c16] = Ew<E>::bits(p);
     }
     if (__any(grew)) {
 #pragma unroll
@@ -1060,8 +1060,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const u32x2 vbf = dec_lds_read_tr16(tr_base + 32 * n);
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(dec_i16x4, pa),
-                                                       __builtin_bit_cast(dec_i16x4, vbf), o[n], 0, 0, 0);
+      o[n] = Ew<E>::mfma16k16(pa, vbf, o[n]);
     }
     wave_lds_fence();
   };
@@ -1151,6 +1150,10 @@ template <>
 __device__ __forceinline__ void store_out<__bf16>(__bf16* p, float x) {
   *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_rne(x);
 }
+template <>
+__device__ __forceinline__ void store_out<_Float16>(_Float16* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = Ew<_Float16>::bits(x);
+}
 
 // Merge of the split-K partials of one (b, query head): weights
 // exp2(m_s - M) staged in LDS, 256 threads = (256 / D) interleaved split
@@ -1212,6 +1215,8 @@ hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   hipError_t e;
   if (dtype == 1) e = (a.D == 128) ? score_launch<__bf16, 128>(a, grid, ctx)
                                    : score_launch<__bf16, 64>(a, grid, ctx);
+  else if (dtype == 2) e = (a.D == 128) ? score_launch<_Float16, 128>(a, grid, ctx)
+                                        : score_launch<_Float16, 64>(a, grid, ctx);
   else e = (a.D == 128) ? score_launch<float, 128>(a, grid, ctx)
                         : score_launch<float, 64>(a, grid, ctx);
   if (e != hipSuccess) return e;
@@ -1290,13 +1295,13 @@ static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st
   }
   return hipSuccess;
 }
-template <int D, bool FL, bool DENSE = false>
+template <int D, bool FL, bool DENSE = false, typename E = __bf16>
 static hipError_t gather_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL, DENSE>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL, DENSE>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL, DENSE>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL, DENSE>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL, DENSE, E>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL, DENSE, E>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL, DENSE, E>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL, DENSE, E>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -1315,6 +1320,7 @@ static hipError_t launch_combine(const DecodeArgs& a, int dtype, LaunchCtx& ctx)
   ctx.begin(K_DEC_COMBINE);
   dim3 cgrid(a.Hq, a.B);
   if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx, a);
+  else if (dtype == 2) KAS_LAUNCH((dec_combine_kernel<_Float16>), cgrid, dim3(256), ctx, a);
   else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx, a);
   return ctx.end(K_DEC_COMBINE);
 }
@@ -1326,6 +1332,11 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, 
   ctx.begin(kid);
   if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx)
                                   : attn_bf16_by_d<false>(a, grid, ctx);
+  else if (dtype == 2)   // fp16: the pipelined gather (the staged variant is bf16 only)
+    e = from_logits ? (a.D == 128 ? gather_launch<128, true, false, _Float16>(a, grid, ctx)
+                                  : gather_launch<64, true, false, _Float16>(a, grid, ctx))
+                    : (a.D == 128 ? gather_launch<128, false, false, _Float16>(a, grid, ctx)
+                                  : gather_launch<64, false, false, _Float16>(a, grid, ctx));
   else e = from_logits ? attn_by_d<float, true>(a, grid, ctx)
                        : attn_by_d<float, false>(a, grid, ctx);
   if (e != hipSuccess) return e;
@@ -1339,6 +1350,9 @@ hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   ctx.begin(K_DEC_DENSE);
   if (dtype == 1)
     e = a.D == 128 ? gather_launch<128, false, true>(a, grid, ctx) : gather_launch<64, false, true>(a, grid, ctx);
+  else if (dtype == 2)
+    e = a.D == 128 ? gather_launch<128, false, true, _Float16>(a, grid, ctx)
+                   : gather_launch<64, false, true, _Float16>(a, grid, ctx);
   else
     e = attn_by_d<float, false, true>(a, grid, ctx);
   if (e != hipSuccess) return e;

@@ -37,6 +37,67 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+
+// The two 16-bit element types of the matrix paths (bf16, fp16): their MFMA
+// instructions (operands as raw dwords, 8 or 4 elements per lane), the
+// round-to-nearest-even packing of two fp32 values, the exact fp32 sum of a
+// packed pair (a dot product with (1, 1)), the rounding store, and the
+// largest half-row probability sum the lazy softmax lets grow before it
+// rescales (bf16 shares fp32's exponent range; fp16 ends at 65504).
+template <typename E>
+struct Ew;
+
+template <>
+struct Ew<__bf16> {
+  static constexpr float kBigP = 0x1p64f;
+  __device__ static __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4v, a), __builtin_bit_cast(i16x4v, b),
+                                                     c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static __forceinline__ float add2(uint32_t pair, float acc) { return add_bf16x2(pair, acc); }
+  __device__ static __forceinline__ uint16_t bits(float f) { return f32_to_bf16_rne(f); }
+};
+
+template <>
+struct Ew<_Float16> {
+  static constexpr float kBigP = 0x1p14f;
+  __device__ static __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b),
+                                                 c, 0, 0, 0);
+  }
+  // v_cvt_pk_f16_f32 (round to nearest even)
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float add2(uint32_t pair, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
+  __device__ static __forceinline__ uint16_t bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+};
+
 // ---------------------------------------------------------------- DPP
 // Reductions inside each row of 16 lanes; afterwards every lane of the row
 // holds the row's result.
@@ -178,31 +239,33 @@ struct RowFrag<float, 8> {
 template <typename T, int D>
 struct QKMfma;
 
-// bf16: v_mfma_f32_16x16x32_bf16; instruction c covers dims [32c, 32c+32),
-// lane quarter q = l/16 supplies dims 32c + 8q .. +8.
-template <int D>
-struct QKMfma<__bf16, D> {
+// 16-bit elements (bf16, fp16): v_mfma_f32_16x16x32_{bf16,f16}; instruction
+// c covers dims [32c, 32c+32), lane quarter q = l/16 supplies dims 32c + 8q .. +8.
+template <typename E, int D>
+struct QKMfma16 {
   static constexpr int NI = D / 32;
   u32x4 kf[NI];
   __device__ __forceinline__ static int dim_of(int c, int q) { return 32 * c + 8 * q; }
-  __device__ __forceinline__ void load_k(const __bf16* row, int q) {
+  __device__ __forceinline__ void load_k(const E* row, int q) {
 #pragma unroll
     for (int c = 0; c < NI; ++c) kf[c] = ldg16(row + dim_of(c, q));
   }
   struct QFrag { u32x4 a[NI]; };
-  __device__ __forceinline__ static void load_q(QFrag& f, const __bf16* qrow, bool valid, int q) {
+  __device__ __forceinline__ static void load_q(QFrag& f, const E* qrow, bool valid, int q) {
 #pragma unroll
     for (int c = 0; c < NI; ++c) f.a[c] = valid ? ldg16(qrow + dim_of(c, q)) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ f32x4 run(const QFrag& f) const {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NI; ++c)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[c]),
-                                                    __builtin_bit_cast(bf16x8, kf[c]), acc, 0, 0, 0);
+    for (int c = 0; c < NI; ++c) acc = Ew<E>::mfma16k32(f.a[c], kf[c], acc);
     return acc;
   }
 };
+template <int D>
+struct QKMfma<__bf16, D> : QKMfma16<__bf16, D> {};
+template <int D>
+struct QKMfma<_Float16, D> : QKMfma16<_Float16, D> {};
 
 // fp32: v_mfma_f32_16x16x4_f32; lane quarter q owns dims [q*D/4, (q+1)*D/4)
 // (contiguous, loaded 16 B at a time) and instruction c uses its c-th dim.

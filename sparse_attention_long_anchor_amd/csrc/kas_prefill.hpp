@@ -36,6 +36,7 @@ struct PrefillArgs {
   // and the heads; pool_all: one set per tile over all heads, Hsel sets per
   // (b, tile) in idx_out (Hkv, or 1 with pool_all)
   int pool_op, pool_all, Hsel;
+  int dtype;                        // element type of q, k, v, o: 1 bf16, 2 fp16
 };
 
 size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);

@@ -142,7 +142,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
     return fail(KAS_ERR_INVALID_ARGUMENT, "seq_len must be in [1, 2^31)");
   if (d->topk_pct < 1 || d->topk_pct > 100)
     return fail(KAS_ERR_INVALID_ARGUMENT, "topk_pct must be in [1, 100]");
-  if (d->dtype != KAS_DTYPE_F32 && d->dtype != KAS_DTYPE_BF16)
+  if (d->dtype != KAS_DTYPE_F32 && d->dtype != KAS_DTYPE_BF16 && d->dtype != KAS_DTYPE_F16)
     return fail(KAS_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
   if (!(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
     return fail(KAS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
@@ -151,7 +151,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   if (d->pool_scope == 1 && d->n_q_heads > kMaxPoolHeads)
     return fail(KAS_ERR_UNSUPPORTED, "pooling over all heads supports at most %d query heads", kMaxPoolHeads);
   if (prefill) {
-    if (d->dtype != KAS_DTYPE_BF16) return fail(KAS_ERR_UNSUPPORTED, "prefill supports bf16 only");
+    if (d->dtype == KAS_DTYPE_F32) return fail(KAS_ERR_UNSUPPORTED, "prefill supports bf16 and fp16 only");
     if (d->tile != 32) return fail(KAS_ERR_UNSUPPORTED, "prefill tile must be 32 (got %d)", d->tile);
     if (d->seq_len % 32) return fail(KAS_ERR_UNSUPPORTED, "prefill seq_len must be a multiple of 32");
   }
@@ -159,7 +159,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   s.N = d->seq_len; s.pct = d->topk_pct; s.tile = d->tile; s.dtype = d->dtype;
   s.scope = d->pool_scope; s.op = d->pool_op;
   s.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
-  s.esize = d->dtype == KAS_DTYPE_BF16 ? 2 : 4;
+  s.esize = d->dtype == KAS_DTYPE_F32 ? 4 : 2;
   s.kv_hs = d->kv_head_stride ? d->kv_head_stride : s.N * s.D;
   s.kv_bs = d->kv_batch_stride ? d->kv_batch_stride : s.Hkv * s.kv_hs;
   if (s.kv_hs < s.N * s.D || s.kv_bs < (s.Hkv - 1) * s.kv_hs + s.N * s.D)
@@ -420,6 +420,7 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, true);
+  a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
   a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
   a.idx = idx_out; a.Hkv_a = a.Hsel; a.head_map = nullptr; a.total = total;
@@ -451,6 +452,7 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, false);
+  a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map; a.total = total;
   LaunchCtx ctx{(hipStream_t)stream};
@@ -491,6 +493,7 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
   if ((st = check_prefill_limits(s, 0))) return st;
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, nullptr, false);
+  a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.offsets = nullptr; a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = 0;
   LaunchCtx ctx{(hipStream_t)stream};

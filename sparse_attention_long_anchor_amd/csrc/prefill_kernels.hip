@@ -1,5 +1,6 @@
-// Prefill-phase kernels for gfx950: query tiles of 32 rows, bf16 inputs,
-// 32x32x16 bf16 MFMA tiles, fp32 softmax.
+// Prefill-phase kernels for gfx950: query tiles of 32 rows, 16-bit inputs
+// (bf16 or fp16, the element type E of the matrix kernels), 32x32x16 MFMA
+// tiles of that type, fp32 softmax.
 //
 //  pre_offsets  CSR offsets of the per-tile index sets.
 //  pre_stats    pass 1 of the anchor: for every query row its base-2
@@ -31,11 +32,6 @@ namespace kas {
 // heads (8.6 GB), which beats chunked launches (fewer launch tails); the
 // buffer is only as large as the prompt needs.
 constexpr int kPoolBudgetMBDefault = 16384;
-
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                 c, 0, 0, 0);
-}
 
 // Row (query or key) of the 32x32 MFMA output held by lane half hh in reg r.
 __device__ __forceinline__ int mrow(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
@@ -119,7 +115,7 @@ struct KDma {
   static constexpr bool EVEN = NINS % G == 0;
   __amdgpu_buffer_rsrc_t rk;
   int w, lrow, lslot;
-  __device__ __forceinline__ void init(const __bf16* kbase, int64_t nrows) {
+  __device__ __forceinline__ void init(const void* kbase, int64_t nrows) {
     rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)(nrows * ROWB), kBufWord3);
     w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -175,7 +171,7 @@ __device__ __forceinline__ void row_stats_update(const f32x16& acc, bool diag, i
 
 // One workgroup = two consecutive tiles (t0 = 2p, t1 = 2p+1) of one KV head;
 // wave w = query head g*G + w; each staged K block feeds both tiles.
-template <int D, int G>
+template <int D, int G, typename E = __bf16>
 __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   constexpr int KC = D / 16;
   using KD = KDma<D, G>;
@@ -196,12 +192,12 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N;
   u32x4 qb0[KC], qb1[KC];
   {
-    const __bf16* q0 = (const __bf16*)a.q + (qoff + kTile * t0 + n32) * D;
-    const __bf16* q1 = (const __bf16*)a.q + (qoff + kTile * (has1 ? t1 : t0) + n32) * D;
+    const E* q0 = (const E*)a.q + (qoff + kTile * t0 + n32) * D;
+    const E* q1 = (const E*)a.q + (qoff + kTile * (has1 ? t1 : t0) + n32) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) { qb0[c] = ldg16(q0 + 16 * c + 8 * hh); qb1[c] = ldg16(q1 + 16 * c + 8 * hh); }
   }
-  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kbase = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   const float cs = a.scale_log2;
   KD kd;
   kd.init(kbase, a.N);
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   auto chain = [&](const u32x4* ka, const u32x4* qb) __attribute__((always_inline)) {
     f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) acc = mfma32(ka[c], qb[c], acc);   // S^T[key][query]
+    for (int c = 0; c < KC; ++c) acc = Ew<E>::mfma32(ka[c], qb[c], acc);   // S^T[key][query]
     return acc;
   };
   auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
@@ -257,7 +253,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
       // terms first: the first group covers the LDS latency of ka[0]
 #pragma unroll
       for (int e = 0; e < TPM; ++e) s += exp2_fast(fmaf(val(prev, TPM * c + e, pdiag), cs, -mr));
-      acc = mfma32(ka[c], qb[c], acc);
+      acc = Ew<E>::mfma32(ka[c], qb[c], acc);
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
@@ -386,7 +382,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 // key block before a tile, each wave (query head) forms S = Q.K^T, the
 // probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
 // waves' sums are added through LDS (double-buffered, one barrier per block).
-template <int D, int G, int OP = 0>
+template <int D, int G, int OP = 0, typename E = __bf16>
 __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   constexpr int KC = D / 16;
   using KD = KDma<D, G>;
@@ -411,8 +407,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   float lse0[16], lse1[16];
   {
     const int tq1 = has1 ? t1 : t0;
-    const __bf16* q0 = (const __bf16*)a.q + (qoff + kTile * t0 + n32) * D;
-    const __bf16* q1 = (const __bf16*)a.q + (qoff + kTile * tq1 + n32) * D;
+    const E* q0 = (const E*)a.q + (qoff + kTile * t0 + n32) * D;
+    const E* q1 = (const E*)a.q + (qoff + kTile * tq1 + n32) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) { qa0[c] = ldg16(q0 + 16 * c + 8 * hh); qa1[c] = ldg16(q1 + 16 * c + 8 * hh); }
 #pragma unroll
@@ -421,7 +417,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
       lse1[r] = a.lse[qoff + kTile * tq1 + mrow(r, hh)];
     }
   }
-  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kbase = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
   float* out0 = a.pooled + pool_slot(a, b, g, t0);
   float* out1 = has1 ? a.pooled + pool_slot(a, b, g, t1) : out0;
   const float cs = a.scale_log2;
@@ -430,7 +426,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   auto chain = [&](const u32x4* ka, const u32x4* qa) __attribute__((always_inline)) {
     f32x16 acc = {};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) acc = mfma32(qa[c], ka[c], acc);   // S[query][key]
+    for (int c = 0; c < KC; ++c) acc = Ew<E>::mfma32(qa[c], ka[c], acc);   // S[query][key]
     return acc;
   };
   auto stage = [&](auto st_tag) __attribute__((always_inline)) -> char* {
@@ -466,7 +462,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     for (int c = 0; c < KC; ++c) {
 #pragma unroll
       for (int e = 0; e < TPM; ++e) col = pool(col, exp2_fast(fmaf(prev[TPM * c + e], cs, -lse[TPM * c + e])));
-      acc = mfma32(qa[c], ka[c], acc);
+      acc = Ew<E>::mfma32(qa[c], ka[c], acc);
       __builtin_amdgcn_sched_barrier(0);
     }
     col = pool_halves(col);
@@ -758,7 +754,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // and then to its own 32 keys under the causal mask (the diagonal block).
 // Per block and wave: S^T = K.Q^T on eight 32x32x16 MFMAs (K rows from LDS,
 // Q in registers), an online softmax, O += P.V on eight more MFMAs (V read
-// from LDS by transposing reads); at the end O / l in bf16.
+// from LDS by transposing reads); at the end O / l in the element type.
 // The gathered K and V rows go from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane names its own row chunk, the data
 // lands at a fixed slot of a 1 KB line) through a ring of four stages, three
@@ -769,7 +765,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // DENSE: dense causal attention with the same block math; block blk holds
 // keys [32 blk, 32 blk + 32) for every blk <= t (block t is the diagonal), so
 // there are no index loads and the tile's key list is [0, 32 t).
-template <int D, int G, bool DENSE = false>
+template <int D, int G, bool DENSE = false, typename E = __bf16>
 __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) {
   constexpr int NT = 64 * G, KC = D / 16, NDC = D / 32, PARTS = D / 8;
   constexpr int ROWB = 2 * D;               // bytes per row
@@ -778,7 +774,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   constexpr int NINS = 32 / RPI;            // lines per block per tensor
   constexpr int NIW = (NINS + G - 1) / G;   // lines per wave (w, w + G, ...)
   constexpr bool EVEN = NINS % G == 0;      // every wave issues NIW lines
-  constexpr float kBigP = 0x1p64f;          // half-row probability sum that triggers a rescale
+  constexpr float kBigP = Ew<E>::kBigP;     // half-row probability sum that triggers a rescale
   (void)NT;
   __shared__ __align__(1024) char s_st0[2 * BLKB];
   __shared__ __align__(1024) char s_st1[2 * BLKB];
@@ -803,14 +799,14 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   // Q fragments: B operand of S^T (lane: query n32, dims 16 c + 8 hh)
   u32x4 qf[KC];
   {
-    const __bf16* qrow = (const __bf16*)a.q + (qoff + n32) * D;
+    const E* qrow = (const E*)a.q + (qoff + n32) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = ldg16(qrow + 16 * c + 8 * hh);
   }
   // K and V rows of this (b, g) through buffer resources: 32-bit row offsets,
   // and the buffer unit returns zeros for any offset past the N rows
-  const __bf16* kbase = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const __bf16* vbase = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kbase = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+  const E* vbase = (const E*)a.v + b * a.kv_bstride + g * a.kv_hstride;
   const int nbytes = (int)((int64_t)a.N * ROWB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, kBufWord3);
@@ -910,7 +906,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 kk = *reinterpret_cast<const u32x4*>(sk + n32 * ROWB + 16 * ((2 * c + hh) ^ swz_k<D>(n32)));
-      acc = mfma32(kk, qf[c], acc);             // S^T[key slot][query]
+      acc = Ew<E>::mfma32(kk, qf[c], acc);             // S^T[key slot][query]
     }
     if (MODE != 0) {
       const int nvalid = kt - blk * 32;
@@ -941,8 +937,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
         for (int e = 0; e < 4; ++e) {
           const float p0 = exp2_fast(fmaf(acc[8 * c2 + 2 * e], cs, -m_run));       // -inf -> 0
           const float p1 = exp2_fast(fmaf(acc[8 * c2 + 2 * e + 1], cs, -m_run));
-          pa[c2][e] = pack_bf16x2(p0, p1);
-          ps = add_bf16x2(pa[c2][e], ps);      // the row sum of the bf16 weights P.V uses
+          pa[c2][e] = Ew<E>::pack2(p0, p1);
+          ps = Ew<E>::add2(pa[c2][e], ps);     // the row sum of the 16-bit weights P.V uses
         }
       }
     };
@@ -972,7 +968,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
         const u32x2 lo = lds_read_tr16(sv + R * ROWB + cofs);
         const u32x2 hi = lds_read_tr16(sv + (R + 8) * ROWB + cofs);
         const u32x4 vb = {lo[0], lo[1], hi[0], hi[1]};
-        o[dc] = mfma32(pa[c2], vb, o[dc]);
+        o[dc] = Ew<E>::mfma32(pa[c2], vb, o[dc]);
       }
     }
     l_run += ps;
@@ -1033,7 +1029,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
     const float inv = __shfl(inv_l, mrow(r, hh));
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
-      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = f32_to_bf16_rne(o[dc][r] * inv);
+      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = Ew<E>::bits(o[dc][r] * inv);
   }
 }
 
@@ -1121,75 +1117,61 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
 
 #define KAS_LAUNCH_P(kernel, grid, block, ctx, arg) (ctx).launch(kernel, grid, block, arg)
 
-#define KAS_DISPATCH_DG(KERNEL, grid, st, a)                                              \
-  do {                                                                                    \
-    if (a.D == 128) {                                                                     \
-      switch (a.G) {                                                                      \
-        case 1: KAS_LAUNCH_P((KERNEL<128, 1>), grid, dim3(64), st, a); break;             \
-        case 2: KAS_LAUNCH_P((KERNEL<128, 2>), grid, dim3(128), st, a); break;            \
-        case 4: KAS_LAUNCH_P((KERNEL<128, 4>), grid, dim3(256), st, a); break;            \
-        case 8: KAS_LAUNCH_P((KERNEL<128, 8>), grid, dim3(512), st, a); break;            \
-        default: return hipErrorInvalidValue;                                             \
-      }                                                                                   \
-    } else {                                                                              \
-      switch (a.G) {                                                                      \
-        case 1: KAS_LAUNCH_P((KERNEL<64, 1>), grid, dim3(64), st, a); break;              \
-        case 2: KAS_LAUNCH_P((KERNEL<64, 2>), grid, dim3(128), st, a); break;             \
-        case 4: KAS_LAUNCH_P((KERNEL<64, 4>), grid, dim3(256), st, a); break;             \
-        case 8: KAS_LAUNCH_P((KERNEL<64, 8>), grid, dim3(512), st, a); break;             \
-        default: return hipErrorInvalidValue;                                             \
-      }                                                                                   \
-    }                                                                                     \
-  } while (0)
-
-// KERNEL<D, G, X> over the supported (D, G)
-#define KAS_DISPATCH_DGX(KERNEL, X, grid, st, a)                                          \
-  do {                                                                                    \
-    if (a.D == 128) {                                                                     \
-      switch (a.G) {                                                                      \
-        case 1: KAS_LAUNCH_P((KERNEL<128, 1, X>), grid, dim3(64), st, a); break;          \
-        case 2: KAS_LAUNCH_P((KERNEL<128, 2, X>), grid, dim3(128), st, a); break;         \
-        case 4: KAS_LAUNCH_P((KERNEL<128, 4, X>), grid, dim3(256), st, a); break;         \
-        case 8: KAS_LAUNCH_P((KERNEL<128, 8, X>), grid, dim3(512), st, a); break;         \
-        default: return hipErrorInvalidValue;                                             \
-      }                                                                                   \
-    } else {                                                                              \
-      switch (a.G) {                                                                      \
-        case 1: KAS_LAUNCH_P((KERNEL<64, 1, X>), grid, dim3(64), st, a); break;           \
-        case 2: KAS_LAUNCH_P((KERNEL<64, 2, X>), grid, dim3(128), st, a); break;          \
-        case 4: KAS_LAUNCH_P((KERNEL<64, 4, X>), grid, dim3(256), st, a); break;          \
-        case 8: KAS_LAUNCH_P((KERNEL<64, 8, X>), grid, dim3(512), st, a); break;          \
-        default: return hipErrorInvalidValue;                                             \
-      }                                                                                   \
-    }                                                                                     \
-  } while (0)
+// fn(D, G, E) with head_dim D, group size G and element type E (tags whose
+// ::value / type name them at compile time) for the supported shapes.
+template <typename E>
+struct ETag { using type = E; };
+template <typename F>
+static hipError_t for_dge(const PrefillArgs& a, F&& fn) {
+  auto by_g = [&](auto dc, auto et) -> hipError_t {
+    switch (a.G) {
+      case 1: fn(dc, std::integral_constant<int, 1>{}, et); return hipSuccess;
+      case 2: fn(dc, std::integral_constant<int, 2>{}, et); return hipSuccess;
+      case 4: fn(dc, std::integral_constant<int, 4>{}, et); return hipSuccess;
+      case 8: fn(dc, std::integral_constant<int, 8>{}, et); return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  };
+  auto by_d = [&](auto et) -> hipError_t {
+    return a.D == 128 ? by_g(std::integral_constant<int, 128>{}, et) : by_g(std::integral_constant<int, 64>{}, et);
+  };
+  return a.dtype == 2 ? by_d(ETag<_Float16>{}) : by_d(ETag<__bf16>{});
+}
+#define KAS_DGE(dc, gc, et) \
+  constexpr int D = decltype(dc)::value, G = decltype(gc)::value; using E = typename decltype(et)::type
 
 static hipError_t launch_offsets(PrefillArgs& a, LaunchCtx& ctx) {
   KAS_LAUNCH_P(pre_offsets_kernel, dim3(1), dim3(256), ctx, a);
   return hipGetLastError();
 }
 
-static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) {
-  ctx.begin(K_PRE_ATTN);
-  dim3 grid(a.T, a.Hkv, a.B);
-  KAS_DISPATCH_DGX(pre_attn_dma_kernel, false, grid, ctx, a);
-  return ctx.end(K_PRE_ATTN);
+template <bool DENSE>
+static hipError_t launch_tile_attn(PrefillArgs& a, LaunchCtx& ctx, int kid) {
+  ctx.begin(kid);
+  const dim3 grid(a.T, a.Hkv, a.B);
+  hipError_t e = for_dge(a, [&](auto dc, auto gc, auto et) {
+    KAS_DGE(dc, gc, et);
+    ctx.launch(pre_attn_dma_kernel<D, G, DENSE, E>, grid, dim3(64 * G), a);
+  });
+  if (e != hipSuccess) return e;
+  return ctx.end(kid);
 }
 
-hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) {
-  ctx.begin(K_PRE_DENSE);
-  dim3 grid(a.T, a.Hkv, a.B);
-  KAS_DISPATCH_DGX(pre_attn_dma_kernel, true, grid, ctx, a);
-  return ctx.end(K_PRE_DENSE);
-}
+static hipError_t launch_attn(PrefillArgs& a, LaunchCtx& ctx) { return launch_tile_attn<false>(a, ctx, K_PRE_ATTN); }
+
+hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) { return launch_tile_attn<true>(a, ctx, K_PRE_DENSE); }
 
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   hipError_t e;
   if ((e = launch_offsets(a, ctx)) != hipSuccess) return e;
   ctx.begin(K_PRE_STATS);
   {
-    dim3 grid((a.T + 1) / 2, a.Hkv, a.B);
-    KAS_DISPATCH_DG(pre_stats_kernel, grid, ctx, a);
+    const dim3 grid((a.T + 1) / 2, a.Hkv, a.B);
+    e = for_dge(a, [&](auto dc, auto gc, auto et) {
+      KAS_DGE(dc, gc, et);
+      ctx.launch(pre_stats_kernel<D, G, E>, grid, dim3(64 * G), a);
+    });
+    if (e != hipSuccess) return e;
   }
   if ((e = ctx.end(K_PRE_STATS)) != hipSuccess) return e;
   const int64_t units = (int64_t)a.B * a.Hkv;
@@ -1198,10 +1180,14 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
     const int tb = next_chunk_end(ta, a.T, units, budget);
     a.t_begin = ta;
     a.t_end = tb;
-    dim3 pgrid((tb + 1) / 2 - ta / 2, a.Hkv, a.B);
+    const dim3 pgrid((tb + 1) / 2 - ta / 2, a.Hkv, a.B);
     ctx.begin(K_PRE_POOL);
-    if (a.pool_op) KAS_DISPATCH_DGX(pre_pool_kernel, 1, pgrid, ctx, a);
-    else KAS_DISPATCH_DGX(pre_pool_kernel, 0, pgrid, ctx, a);
+    e = for_dge(a, [&](auto dc, auto gc, auto et) {
+      KAS_DGE(dc, gc, et);
+      if (a.pool_op) ctx.launch(pre_pool_kernel<D, G, 1, E>, pgrid, dim3(64 * G), a);
+      else ctx.launch(pre_pool_kernel<D, G, 0, E>, pgrid, dim3(64 * G), a);
+    });
+    if (e != hipSuccess) return e;
     if ((e = ctx.end(K_PRE_POOL)) != hipSuccess) return e;
     if (a.pool_all) {
       ctx.begin(K_PRE_POOL_HEADS);

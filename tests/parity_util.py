@@ -3,12 +3,15 @@
 Tolerances (see the design doc for the derivation):
   - index sets: exact, except that a key may be swapped for another only if
     both pooled scores lie within a relative 1e-4 of the oracle's k-th score;
-  - outputs: max-abs 2e-2 for bf16 storage (fp32 accumulation), 1e-4 for fp32.
+  - outputs: max-abs 2e-2 for bf16 storage (fp32 accumulation), 1e-4 for fp32,
+    5e-3 for fp16 storage: outputs here stay below ~4 in magnitude, and the
+    fp16 rounding of the output and of the probabilities used for P.V each
+    contribute at most about 4 * 2^-11 = 2e-3.
 """
 import numpy as np
 
 NEAR_TIE_REL = 1e-4
-TOL = {"bf16": 2e-2, "f32": 1e-4}
+TOL = {"bf16": 2e-2, "f32": 1e-4, "f16": 5e-3}
 
 
 def assert_index_set(gpu, orc, pooled, k, rel=NEAR_TIE_REL, where=""):

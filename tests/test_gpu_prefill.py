@@ -59,8 +59,8 @@ def _check_tiles(w, q, k, v, pct, gidx, go, tiles, label):
         worst_e2e = max(worst_e2e, max_abs(gor, oo))
     _say(f"    tiles={list(tiles)} near-tie swaps={swaps} max|o-o_oracle(same set)|={worst_set:.3g} "
          f"max|o-o_oracle|={worst_e2e:.3g}")
-    assert worst_set <= TOL["bf16"]
-    assert worst_e2e <= TOL["bf16"]
+    assert worst_set <= TOL[w.dtype]
+    assert worst_e2e <= TOL[w.dtype]
 
 
 def _check_reuse_tiles(w, q, k, v, pct, anchor_idx, head_map, go, tiles, label):
@@ -72,7 +72,7 @@ def _check_reuse_tiles(w, q, k, v, pct, anchor_idx, head_map, go, tiles, label):
         ref = oracle.prefill_reuse(qr, kn, vn, aidx, head_map, pct, t0=t, t1=t + 1)
         worst = max(worst, max_abs(_np(go[:, :, 32 * t: 32 * t + 32]), ref))
     _say(f"    reuse head_map={list(head_map)} tiles={list(tiles)} max|o-o_oracle|={worst:.3g}")
-    assert worst <= TOL["bf16"]
+    assert worst <= TOL[w.dtype]
 
 
 SHAPES = [
