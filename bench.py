@@ -203,6 +203,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 layer timings")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -376,6 +377,9 @@ def main():
             args, wd, dec_state, wp, pre_state, out, torch, kas, dev)
     if not args.no_variants:
         out["selection_variants"] = variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev)
+    if not args.no_fp16:
+        out["fp16"] = fp16_timings(wd if do_dec else None, wp if do_pre else None, dec_state, pre_state, dev,
+                                   torch, inputgen, kas)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
@@ -489,6 +493,72 @@ def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev):
                 "value": round(wp.n_layers * out["prefill"]["ms_per_layer"]["anchor"], 3),
                 "derived": "layers x measured anchor layer"}
     log(f"[bench] selection variants: {res}")
+    return res
+
+
+def fp16_timings(wd, wp, dec_state, pre_state, dev, torch, inputgen, kas):
+    """Anchor and reuse layer times with fp16 I/O (the element type of the
+    pages' own kernels) beside bf16, same protocol for both: layers 0 (anchor)
+    and 1 (reuse) of the workload, calls enqueued back to back as anchor,
+    reuse, anchor, ... (each reuse finds its rows evicted by the anchor's full
+    K stream), per-call events, medians. bf16 uses the resident layers."""
+    import dataclasses
+    res = {}
+
+    def alternate(anchor, reuse, reps):
+        anchor()
+        reuse()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            anchor()
+            e[1].record()
+            reuse()
+            e[2].record()
+        torch.cuda.synchronize()
+        ta = sorted(e[0].elapsed_time(e[1]) for e in ev)
+        tr = sorted(e[1].elapsed_time(e[2]) for e in ev)
+        return ta[reps // 2], tr[reps // 2]
+
+    for phase, w0, st in (("decode", wd, dec_state), ("prefill", wp, pre_state)):
+        if w0 is None:
+            continue
+        dec = phase == "decode"
+        reps, scale, unit = (7, 1e3, "us") if dec else (3, 1.0, "ms")
+        out = {"workload": w0.name, "unit": unit}
+        for dt in ("bf16", "f16"):
+            w = dataclasses.replace(w0, dtype=dt)
+            hm = torch.as_tensor(inputgen.head_maps(w)[1], device=dev)
+            if dt == w0.dtype:
+                (qa, ka, va, _), (qr, kr, vr, _) = st[0][0], st[0][1]
+            else:
+                pos = inputgen.heavy_positions(w)
+                qa, ka, va = inputgen.layer_inputs(w, 0, dev, pos)
+                qr, kr, vr = inputgen.layer_inputs(w, 1, dev, pos)
+            d = kas.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.topk_pct, w.torch_dtype)
+            o = torch.empty_like(qa)
+            if dec:
+                ws_a = torch.empty(kas.workspace_size(d, kas.OP_DECODE_ANCHOR), dtype=torch.uint8, device=dev)
+                ws_r = torch.empty(kas.workspace_size(d, kas.OP_DECODE_REUSE), dtype=torch.uint8, device=dev)
+                idx = torch.empty((w.batch, w.n_kv_heads, kas.decode_k(w.seq_len, w.topk_pct)),
+                                  dtype=torch.int32, device=dev)
+                anchor = lambda: kas.decode_anchor(qa, ka, va, w.topk_pct, idx_out=idx, o=o, ws=ws_a)
+                reuse = lambda: kas.decode_reuse(qr, kr, vr, idx, hm, w.topk_pct, o=o, ws=ws_r)
+            else:
+                ws_a = torch.empty(kas.workspace_size(d, kas.OP_PREFILL_ANCHOR), dtype=torch.uint8, device=dev)
+                ws_r = torch.empty(max(256, kas.workspace_size(d, kas.OP_PREFILL_REUSE)), dtype=torch.uint8,
+                                   device=dev)
+                idx = torch.empty((w.batch, w.n_kv_heads, int(kas.prefill_offsets(d)[-1])), dtype=torch.int32,
+                                  device=dev)
+                anchor = lambda: kas.prefill_anchor(qa, ka, va, w.topk_pct, idx_out=idx, o=o, ws=ws_a)
+                reuse = lambda: kas.prefill_reuse(qr, kr, vr, idx, hm, w.topk_pct, o=o, ws=ws_r)
+            ta, tr = alternate(anchor, reuse, reps)
+            out[dt] = {"anchor": round(scale * ta, 3), "reuse": round(scale * tr, 3)}
+            del qa, ka, va, qr, kr, vr, o, ws_a, ws_r, idx
+            torch.cuda.empty_cache()
+        res[phase] = out
+    log(f"[bench] bf16 / fp16 layers: {res}")
     return res
 
 
