@@ -65,7 +65,10 @@ def lib():
                                            _i64, _i64, _i32, _i32, _i64, _i64, _i64, _dp]
         L.orc_prefill_anchor_v.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                            _dbl, _i64, _i64, _i32, _i32, _ip, _dp]
-        for name in ("orc_dense_attention", "orc_decode_anchor", "orc_decode_reuse",
+        L.orc_decode_reuse_q.argtypes = L.orc_decode_reuse.argtypes
+        L.orc_prefill_reuse_q.argtypes = L.orc_prefill_reuse.argtypes
+        for name in ("orc_decode_reuse_q", "orc_prefill_reuse_q",
+                     "orc_dense_attention", "orc_decode_anchor", "orc_decode_reuse",
                      "orc_prefill_pooled", "orc_prefill_anchor", "orc_prefill_reuse",
                      "orc_decode_anchor_v", "orc_prefill_pooled_v", "orc_prefill_anchor_v"):
             getattr(L, name).restype = ctypes.c_int
@@ -146,16 +149,20 @@ def decode_anchor(q, k, v, pct: int, scale: float = 0.0, want_pooled: bool = Fal
     return idx, o, pooled
 
 
-def decode_reuse(q, k, v, anchor_idx, head_map, scale: float = 0.0) -> np.ndarray:
+def decode_reuse(q, k, v, anchor_idx, head_map, scale: float = 0.0,
+                 query_head_map: bool = False) -> np.ndarray:
+    """head_map: [Hkv] anchor set per KV head, or [Hq] per query head with
+    query_head_map=True."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     anchor_idx, head_map = _i32a(anchor_idx), _i32a(head_map)
     B, Hq, D = q.shape
     Hkv, N = k.shape[1], k.shape[2]
     Hkv_a, kk = anchor_idx.shape[1], anchor_idx.shape[2]
+    assert head_map.shape == ((Hq,) if query_head_map else (Hkv,))
     o = np.zeros((B, Hq, D), dtype=np.float64)
-    _check(lib().orc_decode_reuse(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D,
-                                  scale, _ptr(anchor_idx, _ip), Hkv_a, kk, _ptr(head_map, _ip),
-                                  _ptr(o, _dp)), "decode_reuse")
+    fn = lib().orc_decode_reuse_q if query_head_map else lib().orc_decode_reuse
+    _check(fn(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D, scale, _ptr(anchor_idx, _ip),
+              Hkv_a, kk, _ptr(head_map, _ip), _ptr(o, _dp)), "decode_reuse")
     return o
 
 
@@ -208,17 +215,18 @@ def prefill_pooled(q_rows, k, b: int, t: int, g: int, tile: int = 32, t0: int = 
 
 
 def prefill_reuse(q_rows, k, v, anchor_idx, head_map, pct: int, tile: int = 32, t0: int = 0,
-                  t1: Optional[int] = None, scale: float = 0.0) -> np.ndarray:
-    """anchor_idx: the anchor's FULL CSR array [B, Hkv_a, total]."""
+                  t1: Optional[int] = None, scale: float = 0.0, query_head_map: bool = False) -> np.ndarray:
+    """anchor_idx: the anchor's FULL CSR array [B, Hkv_a, total]; head_map as in decode_reuse."""
     q_rows, k, v = _f32(q_rows), _f32(k), _f32(v)
     anchor_idx, head_map = _i32a(anchor_idx), _i32a(head_map)
     B, Hq, R, D = q_rows.shape
     Hkv, N = k.shape[1], k.shape[2]
+    assert head_map.shape == ((Hq,) if query_head_map else (Hkv,))
     T = (N + tile - 1) // tile
     t1 = T if t1 is None else t1
     o = np.zeros((B, Hq, R, D), dtype=np.float64)
-    _check(lib().orc_prefill_reuse(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N,
-                                   D, tile, pct, scale, t0, t1, _ptr(anchor_idx, _ip),
-                                   anchor_idx.shape[1], _ptr(head_map, _ip), _ptr(o, _dp)),
+    fn = lib().orc_prefill_reuse_q if query_head_map else lib().orc_prefill_reuse
+    _check(fn(_ptr(q_rows, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D, tile, pct, scale, t0, t1,
+              _ptr(anchor_idx, _ip), anchor_idx.shape[1], _ptr(head_map, _ip), _ptr(o, _dp)),
            "prefill_reuse")
     return o

@@ -308,17 +308,20 @@ int orc_decode_anchor(const float *q, const float *k, const float *v,
     return orc_decode_anchor_v(q, k, v, B, Hq, Hkv, N, D, pct, scale, 0, 0, idx_out, o_out, pooled_out);
 }
 
-/* Reuse layer: attention over the anchor's index set of the mapped KV head.
- * anchor_idx [B, Hkv_a, kk]; head_map [Hkv] with values in [0, Hkv_a). */
-int orc_decode_reuse(const float *q, const float *k, const float *v,
-                     int B, int Hq, int Hkv, int64_t N, int D, double scale,
-                     const int32_t *anchor_idx, int Hkv_a, int64_t kk,
-                     const int32_t *head_map, double *o_out)
+/* Reuse layer with one anchor set per query head: query head h attends over
+ * anchor_idx[b, qmap[h], :] (qmap [Hq], values in [0, Hkv_a)) with its own
+ * KV head's K and V. The README stores head mappings per model ("Running
+ * Evaluations"); mapping per query head is the finer of the two
+ * granularities a GQA model allows. */
+int orc_decode_reuse_q(const float *q, const float *k, const float *v,
+                       int B, int Hq, int Hkv, int64_t N, int D, double scale,
+                       const int32_t *anchor_idx, int Hkv_a, int64_t kk,
+                       const int32_t *qmap, double *o_out)
 {
     if (check_shape(B, Hq, Hkv, N, D) || Hkv_a <= 0 || kk <= 0) return ORC_BAD_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
-    for (int g = 0; g < Hkv; ++g)
-        if (head_map[g] < 0 || head_map[g] >= Hkv_a) return ORC_BAD_ARG;
+    for (int h = 0; h < Hq; ++h)
+        if (qmap[h] < 0 || qmap[h] >= Hkv_a) return ORC_BAD_ARG;
     for (int64_t i = 0; i < (int64_t)B * Hkv_a * kk; ++i)
         if (anchor_idx[i] < 0 || anchor_idx[i] >= N) return ORC_BAD_INDEX;
     const int G = Hq / Hkv;
@@ -332,22 +335,38 @@ int orc_decode_reuse(const float *q, const float *k, const float *v,
             status = ORC_NOMEM;
         } else {
 #pragma omp for schedule(dynamic)
-            for (int64_t u = 0; u < (int64_t)B * Hkv; ++u) {
-                int64_t b = u / Hkv, g = u % Hkv;
-                const int32_t *S = anchor_idx + (b * Hkv_a + head_map[g]) * kk;
+            for (int64_t u = 0; u < (int64_t)B * Hq; ++u) {
+                int64_t b = u / Hq, h = u % Hq, g = h / G;
+                const int32_t *S = anchor_idx + (b * Hkv_a + qmap[h]) * kk;
                 const float *kb = k + (b * Hkv + g) * N * D;
                 const float *vb = v + (b * Hkv + g) * N * D;
+                const float *qh = q + (b * Hq + h) * D;
                 for (int64_t a = 0; a < kk; ++a) keys[a] = S[a];
-                for (int r = 0; r < G; ++r) {
-                    const float *qh = q + (b * Hq + g * G + r) * D;
-                    for (int64_t a = 0; a < kk; ++a) sel[a] = dot_scaled(qh, kb + keys[a] * D, D, scale);
-                    weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + g * G + r) * D);
-                }
+                for (int64_t a = 0; a < kk; ++a) sel[a] = dot_scaled(qh, kb + keys[a] * D, D, scale);
+                weighted_rows(sel, keys, kk, vb, D, o_out + (b * Hq + h) * D);
             }
         }
         free(sel); free(keys);
     }
     return status;
+}
+
+/* Reuse layer: attention over the anchor's index set of the mapped KV head.
+ * anchor_idx [B, Hkv_a, kk]; head_map [Hkv] with values in [0, Hkv_a): every
+ * query head of KV head g reads set head_map[g]. */
+int orc_decode_reuse(const float *q, const float *k, const float *v,
+                     int B, int Hq, int Hkv, int64_t N, int D, double scale,
+                     const int32_t *anchor_idx, int Hkv_a, int64_t kk,
+                     const int32_t *head_map, double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D)) return ORC_BAD_ARG;
+    const int G = Hq / Hkv;
+    int32_t *qmap = (int32_t *)malloc((size_t)Hq * sizeof(int32_t));
+    if (!qmap) return ORC_NOMEM;
+    for (int h = 0; h < Hq; ++h) qmap[h] = head_map[h / G];
+    int st = orc_decode_reuse_q(q, k, v, B, Hq, Hkv, N, D, scale, anchor_idx, Hkv_a, kk, qmap, o_out);
+    free(qmap);
+    return st;
 }
 
 /* ------------------------------------------------------------------ */
@@ -406,21 +425,22 @@ static void prefill_pool_unit(const float *q, const float *k, int B, int Hq, int
     }
 }
 
-/* Output rows of one (b, t, g) unit: each row attends over the index set S
- * (n_sel keys, all before the tile) plus its causal diagonal keys [i0, i]. */
-static void prefill_output_unit(const float *q, const float *k, const float *v,
+/* Output rows of query head h of tile t: each row attends over the index set
+ * S (n_sel keys, all before the tile) plus its causal diagonal keys [i0, i],
+ * with the K and V of h's KV head. */
+static void prefill_output_head(const float *q, const float *k, const float *v,
                                 int Hq, int Hkv, int64_t N, int D, int32_t tile, double scale,
-                                int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g,
+                                int64_t t0, int64_t R, int64_t b, int64_t t, int64_t h,
                                 const int32_t *S, int64_t n_sel,
                                 double *o_out, double *logit, int64_t *keys)
 {
     const int G = Hq / Hkv;
+    const int64_t g = h / G;
     const int64_t i0 = t * tile;
     const int64_t i1 = (i0 + tile < N) ? i0 + tile : N;
     const float *kb = k + (b * Hkv + g) * N * D;
     const float *vb = v + (b * Hkv + g) * N * D;
-    for (int r = 0; r < G; ++r) {
-        const int64_t h = g * G + r;
+    {
         for (int64_t i = i0; i < i1; ++i) {
             const float *qi = q + ((b * Hq + h) * R + (i - t0 * tile)) * D;
             int64_t n = 0;
@@ -430,6 +450,19 @@ static void prefill_output_unit(const float *q, const float *k, const float *v,
             weighted_rows(logit, keys, n, vb, D, o_out + ((b * Hq + h) * R + (i - t0 * tile)) * D);
         }
     }
+}
+
+/* Output rows of one (b, t, g) unit: every query head of KV head g over S. */
+static void prefill_output_unit(const float *q, const float *k, const float *v,
+                                int Hq, int Hkv, int64_t N, int D, int32_t tile, double scale,
+                                int64_t t0, int64_t R, int64_t b, int64_t t, int64_t g,
+                                const int32_t *S, int64_t n_sel,
+                                double *o_out, double *logit, int64_t *keys)
+{
+    const int G = Hq / Hkv;
+    for (int r = 0; r < G; ++r)
+        prefill_output_head(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, t, g * G + r, S, n_sel,
+                            o_out, logit, keys);
 }
 
 /* Pooled scores of a single unit, for checking: P_out has
@@ -532,21 +565,22 @@ int orc_prefill_anchor(const float *q, const float *k, const float *v,
                                 idx_out, o_out);
 }
 
-/* Prefill reuse layer over tiles [t0, t1): tile t of KV head g attends over
- * the anchor's set of tile t for anchor KV head head_map[g] plus the causal
- * diagonal. anchor_idx is the anchor's full CSR array [B, Hkv_a, total]. */
-int orc_prefill_reuse(const float *q, const float *k, const float *v,
-                      int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
-                      double scale, int64_t t0, int64_t t1,
-                      const int32_t *anchor_idx, int Hkv_a, const int32_t *head_map,
-                      double *o_out)
+/* Prefill reuse layer over tiles [t0, t1) with one anchor set per query head:
+ * tile t of query head h attends over the anchor's set of tile t for anchor
+ * KV head qmap[h] (qmap [Hq]) plus the causal diagonal. anchor_idx is the
+ * anchor's full CSR array [B, Hkv_a, total]. */
+int orc_prefill_reuse_q(const float *q, const float *k, const float *v,
+                        int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                        double scale, int64_t t0, int64_t t1,
+                        const int32_t *anchor_idx, int Hkv_a, const int32_t *qmap,
+                        double *o_out)
 {
     if (check_shape(B, Hq, Hkv, N, D) || tile <= 0 || pct < 1 || pct > 100 || Hkv_a <= 0)
         return ORC_BAD_ARG;
     const int64_t T = (N + tile - 1) / tile;
     if (t0 < 0 || t1 > T || t0 >= t1) return ORC_BAD_ARG;
-    for (int g = 0; g < Hkv; ++g)
-        if (head_map[g] < 0 || head_map[g] >= Hkv_a) return ORC_BAD_ARG;
+    for (int h = 0; h < Hq; ++h)
+        if (qmap[h] < 0 || qmap[h] >= Hkv_a) return ORC_BAD_ARG;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
     int64_t *off = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
     if (!off) return ORC_NOMEM;
@@ -560,7 +594,7 @@ int orc_prefill_reuse(const float *q, const float *k, const float *v,
                     if (j < 0 || j >= t * tile) { free(off); return ORC_BAD_INDEX; }
                 }
     const int64_t R = range_rows(N, tile, t0, t1);
-    const int64_t n_units = (int64_t)B * (t1 - t0) * Hkv;
+    const int64_t n_units = (int64_t)B * (t1 - t0) * Hq;
     int status = ORC_OK;
 #pragma omp parallel
     {
@@ -572,11 +606,11 @@ int orc_prefill_reuse(const float *q, const float *k, const float *v,
         } else {
 #pragma omp for schedule(dynamic)
             for (int64_t u = 0; u < n_units; ++u) {
-                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hkv));
-                int64_t rem = u % ((int64_t)B * Hkv);
-                int64_t b = rem / Hkv, g = rem % Hkv;
-                const int32_t *S = anchor_idx + (b * Hkv_a + head_map[g]) * total + off[tt];
-                prefill_output_unit(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, g,
+                int64_t tt = (t1 - 1) - (u / ((int64_t)B * Hq));
+                int64_t rem = u % ((int64_t)B * Hq);
+                int64_t b = rem / Hq, h = rem % Hq;
+                const int32_t *S = anchor_idx + (b * Hkv_a + qmap[h]) * total + off[tt];
+                prefill_output_head(q, k, v, Hq, Hkv, N, D, tile, scale, t0, R, b, tt, h,
                                     S, off[tt + 1] - off[tt], o_out, rowbuf, keys);
             }
         }
@@ -584,4 +618,24 @@ int orc_prefill_reuse(const float *q, const float *k, const float *v,
     }
     free(off);
     return status;
+}
+
+/* Prefill reuse layer over tiles [t0, t1): tile t of KV head g attends over
+ * the anchor's set of tile t for anchor KV head head_map[g] plus the causal
+ * diagonal. anchor_idx is the anchor's full CSR array [B, Hkv_a, total]. */
+int orc_prefill_reuse(const float *q, const float *k, const float *v,
+                      int B, int Hq, int Hkv, int64_t N, int D, int32_t tile, int32_t pct,
+                      double scale, int64_t t0, int64_t t1,
+                      const int32_t *anchor_idx, int Hkv_a, const int32_t *head_map,
+                      double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D)) return ORC_BAD_ARG;
+    const int G = Hq / Hkv;
+    int32_t *qmap = (int32_t *)malloc((size_t)Hq * sizeof(int32_t));
+    if (!qmap) return ORC_NOMEM;
+    for (int h = 0; h < Hq; ++h) qmap[h] = head_map[h / G];
+    int st = orc_prefill_reuse_q(q, k, v, B, Hq, Hkv, N, D, tile, pct, scale, t0, t1,
+                                 anchor_idx, Hkv_a, qmap, o_out);
+    free(qmap);
+    return st;
 }

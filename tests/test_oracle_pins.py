@@ -496,3 +496,47 @@ def test_prefill_shared_set_output_matches_reuse():
         idx, o = oracle.prefill_anchor(q, k, v, pct=10, pool_scope=1, pool_op=op)
         o2 = oracle.prefill_reuse(q, k, v, idx, np.zeros(2, np.int32), pct=10)
         np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- per-query-head maps
+
+def test_query_head_map_worked_example():
+    """Two query heads sharing one KV head read different single-key sets:
+    each output is exactly that key's V row (a softmax over one key)."""
+    q, k, v = _decode_case(B=1, Hq=2, Hkv=1, N=50, seed=9)
+    sets = np.array([[[7], [31]]], np.int32)                 # anchor sets of 2 anchor KV heads
+    o = oracle.decode_reuse(q, k, v, sets, np.array([1, 0], np.int32), query_head_map=True)
+    np.testing.assert_allclose(o[0], [v[0, 0, 31], v[0, 0, 7]], rtol=0, atol=1e-15)
+    # prefill: tile 1 rows of head 0 over {3} + diagonal, head 1 over {20} + diagonal
+    qp, kp, vp = _prefill_case(B=1, Hq=2, Hkv=1, N=64, seed=9)
+    off = oracle.prefill_offsets(64, 32, 4)                  # k_1 = 1
+    psets = np.array([[[3], [20]]], np.int32)
+    assert off[-1] == 1
+    op = oracle.prefill_reuse(qp, kp, vp, psets, np.array([0, 1], np.int32), pct=4, query_head_map=True)
+    for h, j in ((0, 3), (1, 20)):
+        keys = [j] + list(range(32, 33))                     # row 32: set + diagonal key 32
+        qd, kd, vd = (x.astype(np.float64) for x in (qp[0, h, 32], kp[0, 0], vp[0, 0]))
+        s_ = np.array([qd @ kd[x] for x in keys]) / math.sqrt(qp.shape[-1])
+        w_ = np.exp(s_ - s_.max())
+        np.testing.assert_allclose(op[0, h, 32], (w_[:, None] * vd[keys]).sum(0) / w_.sum(), rtol=1e-12)
+
+
+def test_query_head_map_reduces_to_kv_head_map():
+    q, k, v = _decode_case(B=2, Hq=8, Hkv=2, N=300, seed=4)
+    idx, _, _ = oracle.decode_anchor(q, k, v, pct=10)
+    hm = np.array([1, 0], np.int32)
+    a = oracle.decode_reuse(q, k, v, idx, hm)
+    b = oracle.decode_reuse(q, k, v, idx, np.repeat(hm, 4), query_head_map=True)
+    assert np.array_equal(a, b)
+    qp, kp, vp = _prefill_case(B=1, Hq=4, Hkv=2, N=128, seed=4)
+    pidx, _ = oracle.prefill_anchor(qp, kp, vp, pct=10)
+    a = oracle.prefill_reuse(qp, kp, vp, pidx, hm, pct=10)
+    b = oracle.prefill_reuse(qp, kp, vp, pidx, np.repeat(hm, 2), pct=10, query_head_map=True)
+    assert np.array_equal(a, b)
+    # a query head reading another head's set: its output is the KV-head-map
+    # output of a layer whose map sends its KV head to that set
+    qm = np.array([0, 1, 1, 1, 0, 0, 1, 0], np.int32)
+    c = oracle.decode_reuse(q, k, v, idx, qm, query_head_map=True)
+    for h in range(8):
+        ref = oracle.decode_reuse(q, k, v, idx, np.full(2, qm[h], np.int32))
+        np.testing.assert_array_equal(c[:, h], ref[:, h])
