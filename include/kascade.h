@@ -92,6 +92,13 @@ typedef struct kas_desc {
   int32_t pool_op;      /* 0: pooled score = sum of the heads' (and, in
                            prefill, the tile rows') probabilities; 1: their
                            maximum */
+  int32_t query_head_map;  /* reuse calls: 0: head_map has one entry per KV
+                              head (all its query heads read that set); 1:
+                              one entry per query head (n_q_heads entries,
+                              required), each query head gathering its own
+                              set's rows (G times the rows of the KV-head
+                              map). The README stores head mappings per model
+                              ("Running Evaluations"). */
 } kas_desc_t;
 
 /* round-half-up(pct * n / 100) clamped to [0, n]; 0 for n <= 0 or pct <= 0.

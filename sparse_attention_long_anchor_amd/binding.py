@@ -45,6 +45,7 @@ class KasDesc(ctypes.Structure):
         ("kv_head_stride", ctypes.c_int64),
         ("pool_scope", ctypes.c_int32),
         ("pool_op", ctypes.c_int32),
+        ("query_head_map", ctypes.c_int32),
     ]
 
 
@@ -101,7 +102,7 @@ def _check(rc: int, where: str) -> None:
 def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
               topk_pct: int, dtype: torch.dtype, tile: int = 32, softmax_scale: float = 0.0,
               kv_batch_stride: int = 0, kv_head_stride: int = 0, pool_scope: int = 0,
-              pool_op: int = 0) -> KasDesc:
+              pool_op: int = 0, query_head_map: int = 0) -> KasDesc:
     if dtype == torch.bfloat16:
         dt = DTYPE_BF16
     elif dtype == torch.float16:
@@ -111,7 +112,7 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
     else:
         raise KasError(2, "make_desc", f"dtype {dtype} not supported")
     return KasDesc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, topk_pct, tile, dt,
-                   softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op)
+                   softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op, query_head_map)
 
 
 def topk_count(n: int, pct: int) -> int:
@@ -154,7 +155,7 @@ def _ws(desc: KasDesc, op: int, ws: Optional[torch.Tensor], device) -> torch.Ten
 
 
 def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale: float,
-               tile: int = 32, pool_scope: int = 0, pool_op: int = 0) -> KasDesc:
+               tile: int = 32, pool_scope: int = 0, pool_op: int = 0, query_head_map: int = 0) -> KasDesc:
     if prefill:
         B, Hq, N, D = q.shape
     else:
@@ -165,7 +166,7 @@ def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale:
         raise KasError(1, "desc", "k/v rows must be contiguous [.., N, D]")
     return make_desc(B, Hq, Hkv, D, N, pct, q.dtype, tile=tile, softmax_scale=scale,
                      kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1),
-                     pool_scope=pool_scope, pool_op=pool_op)
+                     pool_scope=pool_scope, pool_op=pool_op, query_head_map=query_head_map)
 
 
 def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
@@ -187,10 +188,11 @@ def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, w
     return idx_out, o
 
 
-def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None
-                 ) -> torch.Tensor:
-    """anchor_idx [B,Hkv_a,kd] int32 (device), head_map int32 [Hkv] (device) or None."""
-    desc = _desc_from(q, k, pct, False, scale)
+def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
+                 query_head_map: bool = False) -> torch.Tensor:
+    """anchor_idx [B,Hkv_a,kd] int32 (device), head_map int32 [Hkv] (device) or None;
+    with query_head_map, head_map holds one entry per query head [Hq]."""
+    desc = _desc_from(q, k, pct, False, scale, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "decode_reuse", "k and v must share strides")
     if o is None:
@@ -222,9 +224,10 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
     return idx_out, o
 
 
-def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None
-                  ) -> torch.Tensor:
-    desc = _desc_from(q, k, pct, True, scale)
+def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
+                  query_head_map: bool = False) -> torch.Tensor:
+    """head_map as in decode_reuse."""
+    desc = _desc_from(q, k, pct, True, scale, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "prefill_reuse", "k and v must share strides")
     if o is None:

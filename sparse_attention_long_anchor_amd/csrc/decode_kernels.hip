@@ -28,6 +28,11 @@ namespace kas {
 
 constexpr int kMaxSplitRows = 2048;
 
+// KV head of workgroup head index g: g itself, or with one anchor set per
+// query head (the reuse kernels then run one query head per "KV head", G = 1)
+// the query head's KV head g / kvdiv.
+__device__ __forceinline__ int kv_head(const DecodeArgs& a, int g) { return a.kvdiv > 1 ? g / a.kvdiv : g; }
+
 // ------------------------------------------------------------------ dec_score
 
 template <typename T, int D, int G>
@@ -610,8 +615,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
-  const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const T* vb = (const T*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const T* kb = (const T*)a.k + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const T* vb = (const T*)a.v + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
   const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
 
   typename QK::QFrag qf;
@@ -794,8 +799,8 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
-  const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const __bf16* vb = (const __bf16*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const __bf16* kb = (const __bf16*)a.k + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const __bf16* vb = (const __bf16*)a.v + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
   const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
   typename QK::QFrag qf;
   if (!FROM_LOGITS)
@@ -975,8 +980,8 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   const int32_t* idx = DENSE ? nullptr : a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
-  const E* kb = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const E* vb = (const E*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kb = (const E*)a.k + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const E* vb = (const E*)a.v + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
   const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
   typename QK::QFrag qf;
   if (!FROM_LOGITS)

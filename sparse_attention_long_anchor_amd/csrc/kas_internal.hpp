@@ -86,6 +86,9 @@ struct DecodeArgs {
   // probabilities; pool_all: one set per batch row over all heads
   int pool_op, pool_all;
   int64_t sel_units;                // index sets selected: B * Hkv, or B with pool_all
+  // reuse with one anchor set per query head: Hkv and G describe query heads
+  // (Hkv = Hq, G = 1) and KV head = head / kvdiv; 1 otherwise
+  int kvdiv;
 };
 
 hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);

@@ -37,6 +37,7 @@ struct PrefillArgs {
   // (b, tile) in idx_out (Hkv, or 1 with pool_all)
   int pool_op, pool_all, Hsel;
   int dtype;                        // element type of q, k, v, o: 1 bf16, 2 fp16
+  int kvdiv;                        // reuse per query head: Hkv = Hq, G = 1, KV head = head / kvdiv
 };
 
 size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);

@@ -111,6 +111,7 @@ struct Shape {
   int64_t N;
   int pct, tile, dtype;
   int scope, op;                    // anchor pooling variant (kas_desc_t.pool_scope / pool_op)
+  int qmap;                         // reuse: head_map per query head (kas_desc_t.query_head_map)
   float scale;
   int64_t kv_hs, kv_bs;
   size_t esize;
@@ -148,6 +149,8 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
     return fail(KAS_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if ((d->pool_scope != 0 && d->pool_scope != 1) || (d->pool_op != 0 && d->pool_op != 1))
     return fail(KAS_ERR_INVALID_ARGUMENT, "pool_scope and pool_op must be 0 or 1");
+  if (d->query_head_map != 0 && d->query_head_map != 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map must be 0 or 1");
   if (d->pool_scope == 1 && d->n_q_heads > kMaxPoolHeads)
     return fail(KAS_ERR_UNSUPPORTED, "pooling over all heads supports at most %d query heads", kMaxPoolHeads);
   if (prefill) {
@@ -157,7 +160,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   }
   s.B = d->batch; s.Hq = d->n_q_heads; s.Hkv = d->n_kv_heads; s.D = d->head_dim; s.G = G;
   s.N = d->seq_len; s.pct = d->topk_pct; s.tile = d->tile; s.dtype = d->dtype;
-  s.scope = d->pool_scope; s.op = d->pool_op;
+  s.scope = d->pool_scope; s.op = d->pool_op; s.qmap = d->query_head_map;
   s.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
   s.esize = d->dtype == KAS_DTYPE_F32 ? 4 : 2;
   s.kv_hs = d->kv_head_stride ? d->kv_head_stride : s.N * s.D;
@@ -259,8 +262,19 @@ static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false) {
   return p;
 }
 
+// The reuse shape with one anchor set per query head: the gather kernels run
+// every query head as its own group of one (Hkv = Hq, G = 1) and address K and
+// V through head / G.
+static Shape per_query_head(const Shape& s) {
+  Shape q = s;
+  q.Hkv = s.Hq;
+  q.G = 1;
+  return q;
+}
+
 static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, char* ws, DecodeArgs& a) {
   memset(&a, 0, sizeof(a));
+  a.kvdiv = 1;
   a.kv_bstride = s.kv_bs; a.kv_hstride = s.kv_hs;
   a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.G = s.G; a.N = s.N;
   a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
@@ -343,6 +357,8 @@ kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* byte
   if (st != KAS_OK) return st;
   if (op == KAS_OP_PREFILL_DENSE) {
     *bytes = 0;
+  } else if (op == KAS_OP_DECODE_REUSE && s.qmap) {
+    *bytes = plan_decode(per_query_head(s), false).total;
   } else if (!prefill) {
     *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE).total;
   } else {
@@ -392,10 +408,13 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
   if (!head_map && anchor_kv_heads != s.Hkv && anchor_kv_heads != 1)
     return fail(KAS_ERR_INVALID_ARGUMENT,
                 "without a head map, anchor_kv_heads must be n_kv_heads (identity) or 1 (shared set)");
-  DecodePlan p = plan_decode(s, false);
+  if (s.qmap && !head_map) return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map needs a head_map of n_q_heads entries");
+  const Shape sr = s.qmap ? per_query_head(s) : s;
+  DecodePlan p = plan_decode(sr, false);
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a;
-  fill_decode_args(s, p, false, (char*)ws, a);
+  fill_decode_args(sr, p, false, (char*)ws, a);
+  a.kvdiv = s.qmap ? s.G : 1;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map;
   LaunchCtx ctx{(hipStream_t)stream};
@@ -448,11 +467,14 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
   int64_t total = 0;
   if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
   if ((st = check_prefill_limits(s, total))) return st;
-  size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, false);
+  if (s.qmap && !head_map) return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map needs a head_map of n_q_heads entries");
+  const Shape sr = s.qmap ? per_query_head(s) : s;
+  size_t need = prefill_workspace_bytes(sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, false);
   if ((st = check_ws(ws, ws_bytes, need))) return st;
   PrefillArgs a;
-  fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, false);
+  fill_prefill_args(a, sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, sr.scale, sr.kv_bs, sr.kv_hs, (char*)ws, false);
   a.dtype = s.dtype;
+  a.kvdiv = s.qmap ? s.G : 1;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map; a.total = total;
   LaunchCtx ctx{(hipStream_t)stream};

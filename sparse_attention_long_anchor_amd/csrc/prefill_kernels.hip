@@ -805,8 +805,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   }
   // K and V rows of this (b, g) through buffer resources: 32-bit row offsets,
   // and the buffer unit returns zeros for any offset past the N rows
-  const E* kbase = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
-  const E* vbase = (const E*)a.v + b * a.kv_bstride + g * a.kv_hstride;
+  const E* kbase = (const E*)a.k + b * a.kv_bstride + (a.kvdiv > 1 ? g / a.kvdiv : g) * a.kv_hstride;
+  const E* vbase = (const E*)a.v + b * a.kv_bstride + (a.kvdiv > 1 ? g / a.kvdiv : g) * a.kv_hstride;
   const int nbytes = (int)((int64_t)a.N * ROWB);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, kBufWord3);
@@ -1101,6 +1101,7 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.kv_bstride = kv_bs; a.kv_hstride = kv_hs;
   a.Hsel = Hkv;
+  a.kvdiv = 1;
   PrefillPlan p = plan(B, Hq, Hkv, N, anchor);
   // KAS_PREFILL_SELECT_CAP lowers the LDS candidate cap of the select (0 sends
   // every tile through the in-place histogram passes)

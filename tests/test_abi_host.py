@@ -77,7 +77,11 @@ def test_descriptor_validation():
         (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, pool_scope=2), b.OP_DECODE_ANCHOR, 1),
         (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, pool_op=-1), b.OP_PREFILL_ANCHOR, 1),
         (b.make_desc(1, 512, 64, 128, 64, 10, torch.bfloat16, pool_scope=1), b.OP_DECODE_ANCHOR, 2),
+        (b.make_desc(1, 32, 8, 128, 64, 10, torch.bfloat16, query_head_map=2), b.OP_DECODE_REUSE, 1),
     ]
+    # a map per query head gathers per query head: more split partials
+    dq = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16, query_head_map=1)
+    assert b.workspace_size(dq, b.OP_DECODE_REUSE) >= b.workspace_size(ok, b.OP_DECODE_REUSE)
     # the variants keep the workspace of the default selection
     for scope, op in [(0, 1), (1, 0), (1, 1)]:
         dv = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16, pool_scope=scope, pool_op=op)
@@ -110,6 +114,9 @@ def test_calls_reject_bad_pointers_and_small_workspace_without_gpu():
     assert r == 1 and b"without a head map" in L.kas_last_error()
     r = L.kas_decode_reuse(ctypes.byref(d), fake, fake, fake, None, 2, None, fake, fake, 1 << 30, None)
     assert r == 1
+    dq = b.make_desc(1, 8, 2, 64, 2048, 10, torch.float32, query_head_map=1)
+    r = L.kas_decode_reuse(ctypes.byref(dq), fake, fake, fake, fake, 2, None, fake, fake, 1 << 30, None)
+    assert r == 1 and b"query_head_map" in L.kas_last_error()
     # prefill sizes past the 32-bit CSR offsets / row offsets: rejected
     # before anything is launched
     dbig = b.make_desc(1, 8, 2, 128, 2_000_000, 10, torch.bfloat16)

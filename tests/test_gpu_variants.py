@@ -1,7 +1,8 @@
 """GPU parity of the anchor selection variants against the oracle, through
 the C ABI: pooling over all query heads (one set shared by every KV head, the
 README's all-heads-pooled strategy) and max-pooling instead of the sum, in
-decode and prefill, with reuse layers reading the shared sets.
+decode and prefill, with reuse layers reading the shared sets; and reuse
+layers whose head map has one entry per query head.
 
 Index sets must match the oracle's exactly except inside the near-tie band
 (relative 1e-4 of the oracle's k-th pooled score, using the oracle's pooled
@@ -178,3 +179,91 @@ def test_prefill_variant_full_size_sampled_tiles(variant):
     gidx, go = kas.prefill_anchor(q, k, v, w.topk_pct, pool_scope=variant[0], pool_op=variant[1])
     torch.cuda.synchronize()
     _check_prefill_tiles(w, q, k, v, w.topk_pct, variant[0], variant[1], gidx, go, (1, 37, 500, 1023), w.name)
+
+
+# ---------------------------------------------------------------- per-query-head maps
+
+QMAP_DECODE = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct)
+    ("f32_d64_g4", 1, 8, 2, 64, 2048, "f32", 10),
+    ("bf16_d128_g4_ragged", 2, 32, 8, 128, 5037, "bf16", 10),
+    ("bf16_d128_g8", 1, 16, 2, 128, 4099, "bf16", 10),
+    ("f16_d64_g2", 2, 8, 4, 64, 3001, "f16", 25),
+]
+
+
+@pytest.mark.parametrize("shape", QMAP_DECODE, ids=[s[0] for s in QMAP_DECODE])
+def test_decode_reuse_query_head_map(shape):
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct = shape
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx, _ = kas.decode_anchor(q, k, v, pct)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    qm = np.random.default_rng(7).integers(0, Hkv, Hq).astype(np.int32)
+    o = kas.decode_reuse(q2, k2, v2, idx, torch.as_tensor(qm, device=DEV), pct, query_head_map=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode_reuse(_np(q2), _np(k2), _np(v2), idx.cpu().numpy(), qm, query_head_map=True)
+    err = max_abs(_np(o), ref)
+    _say(f"[decode reuse, map per query head] {label}: qmap={qm.tolist()} max|o-o_oracle|={err:.3g}")
+    assert err <= TOL[dt]
+
+
+QMAP_PREFILL = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct)
+    ("bf16_d128_g4_n256", 1, 8, 2, 128, 256, "bf16", 10),
+    ("bf16_d128_g4_b2_n1184", 2, 8, 2, 128, 1184, "bf16", 10),
+    ("bf16_d64_g2_n640", 1, 4, 2, 64, 640, "bf16", 25),
+    ("f16_d128_g8_n384", 1, 16, 2, 128, 384, "f16", 10),
+]
+
+
+@pytest.mark.parametrize("shape", QMAP_PREFILL, ids=[s[0] for s in QMAP_PREFILL])
+def test_prefill_reuse_query_head_map(shape):
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct = shape
+    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx, _ = kas.prefill_anchor(q, k, v, pct)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    qm = np.random.default_rng(8).integers(0, Hkv, Hq).astype(np.int32)
+    o = kas.prefill_reuse(q2, k2, v2, idx, torch.as_tensor(qm, device=DEV), pct, query_head_map=True)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_reuse(_np(q2), _np(k2), _np(v2), idx.cpu().numpy(), qm, pct, query_head_map=True)
+    err = max_abs(_np(o), ref)
+    _say(f"[prefill reuse, map per query head] {label}: max|o-o_oracle|={err:.3g}")
+    assert err <= TOL[dt]
+
+
+def test_reuse_query_head_map_full_size():
+    kas = _kas()
+    w = inputgen.WORKLOADS["llama8b_decode_128k"]
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    idx, _ = kas.decode_anchor(q, k, v, w.topk_pct)
+    del q, k, v
+    q, k, v = inputgen.layer_inputs(w, 1, DEV, pos)
+    qm = np.random.default_rng(9).integers(0, w.n_kv_heads, w.n_q_heads).astype(np.int32)
+    o = kas.decode_reuse(q, k, v, idx, torch.as_tensor(qm, device=DEV), w.topk_pct, query_head_map=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode_reuse(_np(q), _np(k), _np(v), idx.cpu().numpy(), qm, query_head_map=True)
+    err = max_abs(_np(o), ref)
+    _say(f"[decode reuse, map per query head] {w.name}: max|o-o_oracle|={err:.3g}")
+    assert err <= TOL["bf16"]
+    del q, k, v
+    wp = inputgen.WORKLOADS["qwen8b_prefill_32k"]
+    posp = inputgen.heavy_positions(wp)
+    q, k, v = inputgen.layer_inputs(wp, 0, DEV, posp)
+    pidx, _ = kas.prefill_anchor(q, k, v, wp.topk_pct)
+    q, k, v = inputgen.layer_inputs(wp, 1, DEV, posp)
+    qm = np.random.default_rng(10).integers(0, wp.n_kv_heads, wp.n_q_heads).astype(np.int32)
+    o = kas.prefill_reuse(q, k, v, pidx, torch.as_tensor(qm, device=DEV), wp.topk_pct, query_head_map=True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for t in (1, 500, 1023):
+        qr = _np(q[:, :, 32 * t: 32 * t + 32])
+        ref = oracle.prefill_reuse(qr, _np(k), _np(v), pidx.cpu().numpy(), qm, wp.topk_pct, t0=t, t1=t + 1,
+                                   query_head_map=True)
+        worst = max(worst, max_abs(_np(o[:, :, 32 * t: 32 * t + 32]), ref))
+    _say(f"[prefill reuse, map per query head] {wp.name}: tiles (1, 500, 1023) max|o-o_oracle|={worst:.3g}")
+    assert worst <= TOL["bf16"]
