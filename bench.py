@@ -376,7 +376,7 @@ def main():
         out["dense_baseline"], out["roofline_dense"] = dense_baseline(
             args, wd, dec_state, wp, pre_state, out, torch, kas, dev)
     if not args.no_variants:
-        out["selection_variants"] = variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev)
+        out["selection_variants"] = variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev, inputgen)
     if not args.no_fp16:
         out["fp16"] = fp16_timings(wd if do_dec else None, wp if do_pre else None, dec_state, pre_state, dev,
                                    torch, inputgen, kas)
@@ -445,7 +445,7 @@ def dense_baseline(args, wd, dec_state, wp, pre_state, out, torch, kas, dev):
 VARIANTS = {"group_sum": (0, 0), "group_max": (0, 1), "all_sum": (1, 0), "all_max": (1, 1)}
 
 
-def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev):
+def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev, inputgen):
     """Anchor-layer time of each selection variant (pooling scope: the KV
     head's group or all heads; operator: sum or max) on layer 0's resident
     inputs, median of repeated calls; plus the schedule in which every layer is
@@ -474,6 +474,19 @@ def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev):
                                                  pool_scope=sc, pool_op=op), 5)
             r[name] = round(1e3 * ms, 3)
         res["decode_anchor_us"] = r
+        # reuse layer 1 with a head map per KV head vs one per query head
+        (q1, k1, v1, _), ws_r = dec_state[0][1], dec_state[4]
+        idx = torch.empty((wd.batch, wd.n_kv_heads, kd), dtype=torch.int32, device=dev)
+        anchor = lambda: kas.decode_anchor(q, k, v, wd.topk_pct, idx_out=idx, o=o, ws=ws)
+        hm = torch.as_tensor(inputgen.head_maps(wd)[1], device=dev)
+        qm = hm.repeat_interleave(wd.group)
+        d_q = kas.make_desc(wd.batch, wd.n_q_heads, wd.n_kv_heads, wd.head_dim, wd.seq_len, wd.topk_pct,
+                            wd.torch_dtype, query_head_map=1)
+        ws_q = torch.empty(kas.workspace_size(d_q, kas.OP_DECODE_REUSE), dtype=torch.uint8, device=dev)
+        _, t_kv = _alternate(torch, anchor, lambda: kas.decode_reuse(q1, k1, v1, idx, hm, wd.topk_pct, o=o, ws=ws_r), 7)
+        _, t_q = _alternate(torch, anchor, lambda: kas.decode_reuse(q1, k1, v1, idx, qm, wd.topk_pct, o=o, ws=ws_q,
+                                                                    query_head_map=True), 7)
+        res["decode_reuse_us"] = {"map_per_kv_head": round(1e3 * t_kv, 3), "map_per_query_head": round(1e3 * t_q, 3)}
         if "decode" in out:
             res["decode_every_layer_anchor_ms_per_step"] = {
                 "value": round(wd.n_layers * out["decode"]["us_per_layer"]["anchor"] / 1e3, 4),
@@ -488,12 +501,41 @@ def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev):
                                                   pool_scope=sc, pool_op=op), 2)
             r[name] = round(ms, 3)
         res["prefill_anchor_ms"] = r
+        (q1, k1, v1, _), ws_r = pre_state[0][1], pre_state[4]
+        idx = torch.empty((wp.batch, wp.n_kv_heads, total), dtype=torch.int32, device=dev)
+        anchor = lambda: kas.prefill_anchor(q, k, v, wp.topk_pct, idx_out=idx, o=o, ws=ws)
+        hm = torch.as_tensor(inputgen.head_maps(wp)[1], device=dev)
+        qm = hm.repeat_interleave(wp.group)
+        _, t_kv = _alternate(torch, anchor, lambda: kas.prefill_reuse(q1, k1, v1, idx, hm, wp.topk_pct, o=o, ws=ws_r), 2)
+        _, t_q = _alternate(torch, anchor, lambda: kas.prefill_reuse(q1, k1, v1, idx, qm, wp.topk_pct, o=o, ws=ws_r,
+                                                                     query_head_map=True), 2)
+        res["prefill_reuse_ms"] = {"map_per_kv_head": round(t_kv, 3), "map_per_query_head": round(t_q, 3)}
         if "prefill" in out:
             res["prefill_every_layer_anchor_ms_per_step"] = {
                 "value": round(wp.n_layers * out["prefill"]["ms_per_layer"]["anchor"], 3),
                 "derived": "layers x measured anchor layer"}
     log(f"[bench] selection variants: {res}")
     return res
+
+
+def _alternate(torch, anchor, reuse, reps):
+    """Median device times of anchor() and reuse() enqueued back to back as
+    anchor, reuse, anchor, ... (each reuse finds its rows evicted by the
+    anchor's K stream)."""
+    anchor()
+    reuse()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        anchor()
+        e[1].record()
+        reuse()
+        e[2].record()
+    torch.cuda.synchronize()
+    ta = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    tr = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    return ta[reps // 2], tr[reps // 2]
 
 
 def fp16_timings(wd, wp, dec_state, pre_state, dev, torch, inputgen, kas):
@@ -504,22 +546,7 @@ def fp16_timings(wd, wp, dec_state, pre_state, dev, torch, inputgen, kas):
     K stream), per-call events, medians. bf16 uses the resident layers."""
     import dataclasses
     res = {}
-
-    def alternate(anchor, reuse, reps):
-        anchor()
-        reuse()
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
-        for e in ev:
-            e[0].record()
-            anchor()
-            e[1].record()
-            reuse()
-            e[2].record()
-        torch.cuda.synchronize()
-        ta = sorted(e[0].elapsed_time(e[1]) for e in ev)
-        tr = sorted(e[1].elapsed_time(e[2]) for e in ev)
-        return ta[reps // 2], tr[reps // 2]
+    alternate = lambda anchor, reuse, reps: _alternate(torch, anchor, reuse, reps)
 
     for phase, w0, st in (("decode", wd, dec_state), ("prefill", wp, pre_state)):
         if w0 is None:
