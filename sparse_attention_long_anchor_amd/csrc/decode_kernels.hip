@@ -35,6 +35,8 @@ __device__ __forceinline__ int kv_head(const DecodeArgs& a, int g) { return a.kv
 
 // ------------------------------------------------------------------ dec_score
 
+constexpr float kBigSum = 0x1p64f;   // lazy-reference term that forces the exact update
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   using QK = QKMfma<T, D>;
@@ -109,15 +111,29 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
         for (int r = 0; r < G; ++r) dst[r] = t[r];
       }
     }
+    // Row sums against a lazy per-lane reference: ml is the lane's running
+    // offset, and a score is added as exp2(t - ml) without a block maximum.
+    // Only a term that is not finite or above 2^64 (the lane's first value,
+    // or a score 64 above the reference) sends the wave through the exact
+    // update, which moves the reference to the larger of the two.
+    float p[4];
+    bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float bm = row16_max(t[r]);
-      float mn = fmaxf(ml[r], bm);
-      float al = (mn == ml[r]) ? 1.f : exp2_fast(ml[r] - mn);
-      float p = (STEADY || t[r] != kNegInf) ? exp2_fast(t[r] - mn) : 0.f;
-      ls[r] = ls[r] * al + p;
-      ml[r] = mn;
+      p[r] = exp2_fast(t[r] - ml[r]);
+      over |= !(p[r] <= kBigSum);
     }
+    if (__builtin_expect(__any(over), 0)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mn = fmaxf(ml[r], t[r]);
+        ls[r] = (ml[r] == kNegInf) ? 0.f : ls[r] * exp2_fast(ml[r] - mn);
+        p[r] = (t[r] == kNegInf) ? 0.f : exp2_fast(t[r] - mn);
+        ml[r] = mn;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] += p[r];
   };
   QK qa, qb;
   int blk = wave;
@@ -142,10 +158,14 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   if (blk + 8 < nblk) load(blk + 8, qa);
   if (blk + 4 < nblk) process(blk + 4, qb, Edge{});
   if (blk + 8 < nblk) process(blk + 8, qa, Edge{});
+  // merge the lanes' (reference, sum) pairs of each head: lanes 16 (h / 4) ..
+  // + 15 hold head h in register h % 4
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float lsum = row16_sum(ls[h & 3]);
-    float M = readlane_f(ml[h & 3], 16 * (h >> 2));
+    const float m = ml[h & 3];
+    const float rowmax = row16_max(m);
+    const float lsum = row16_sum(m == kNegInf ? 0.f : ls[h & 3] * exp2_fast(m - rowmax));
+    float M = readlane_f(rowmax, 16 * (h >> 2));
     float L = readlane_f(lsum, 16 * (h >> 2));
     if (lane == 0) { s_m[wave][h] = M; s_l[wave][h] = L; }
   }
