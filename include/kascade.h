@@ -188,6 +188,49 @@ kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void*
 kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                void* o, void* ws, size_t ws_bytes, void* stream);
 
+/* Decode KV caches whose sequences have different lengths and/or whose rows
+ * live in pages (README notes: paged and varlen kernels are announced for
+ * the pages' own kernels). Passed to the *_kv decode calls; NULL there means
+ * the dense [B, Hkv, N, D] cache of kas_desc_t with every sequence N keys
+ * long, exactly the calls without _kv.
+ *   - seq_lens (device [B] or NULL): keys of sequence b, in [1, desc->seq_len]
+ *     (values outside are clamped into it on the device); the new token's key
+ *     is the sequence's last. Sequence b's sets hold max(1,
+ *     kas_topk_count(seq_lens[b], pct)) keys; index arrays keep the shape
+ *     that desc->seq_len gives, entries past a sequence's count are
+ *     unspecified.
+ *   - block_table (device [B, max_pages] or NULL for the contiguous cache of
+ *     desc): the page holding keys [P i, P i + P) of sequence b. Page ids are
+ *     trusted (ids outside [0, num_pages) read page 0). k and v are then page
+ *     pools, [num_pages, Hkv, P, D] with the default strides; desc's
+ *     kv_*_stride are not used. Paged caches hold bf16 or fp16.
+ * KAS_ERR_UNSUPPORTED: a paged fp32 cache, or a pool of 2^31 rows or more
+ * (num_pages * page_stride / head_dim). */
+typedef struct kas_kv_cache {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t page_size;         /* P: a power of two in [16, 2^20] */
+  int32_t max_pages;         /* entries per block_table row, >= ceil(seq_len / P) */
+  int64_t num_pages;         /* pages in each of the k and v pools */
+  int64_t page_stride;       /* elements between pages, a multiple of head_dim (0 = Hkv * P * D) */
+  int64_t page_head_stride;  /* elements between KV heads in a page (0 = P * D) */
+} kas_kv_cache_t;
+
+/* Workspace of a *_kv call (op: KAS_OP_DECODE_*). */
+kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int32_t op,
+                                   size_t* bytes);
+/* kas_decode_anchor / kas_decode_reuse / kas_decode_dense over such a cache. */
+kas_status_t kas_decode_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
+                                  size_t ws_bytes, void* stream);
+kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                 const void* k, const void* v, const int32_t* anchor_idx,
+                                 int32_t anchor_kv_heads, const int32_t* head_map, void* o, void* ws,
+                                 size_t ws_bytes, void* stream);
+kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                 const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 const char* kas_status_string(kas_status_t status);
 /* Text of the last failure on the calling thread ("" if none). */
 const char* kas_last_error(void);

@@ -49,6 +49,18 @@ class KasDesc(ctypes.Structure):
     ]
 
 
+class KasKvCache(ctypes.Structure):
+    _fields_ = [
+        ("seq_lens", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("page_head_stride", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -75,6 +87,11 @@ def _load():
         L.kas_prefill_anchor.argtypes = [dp, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_prefill_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
+        cp = ctypes.POINTER(KasKvCache)
+        L.kas_workspace_size_kv.argtypes = [dp, cp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kas_decode_anchor_kv.argtypes = [dp, cp, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_decode_reuse_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+        L.kas_decode_dense_kv.argtypes = [dp, cp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_status_string.argtypes = [st]
         L.kas_status_string.restype = ctypes.c_char_p
@@ -85,7 +102,8 @@ def _load():
         L.kas_profile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         for n in ("kas_prefill_index_offsets", "kas_workspace_size", "kas_decode_anchor",
                   "kas_decode_reuse", "kas_prefill_anchor", "kas_prefill_reuse",
-                  "kas_decode_dense", "kas_prefill_dense",
+                  "kas_decode_dense", "kas_prefill_dense", "kas_workspace_size_kv",
+                  "kas_decode_anchor_kv", "kas_decode_reuse_kv", "kas_decode_dense_kv",
                   "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
                   "kas_profile_names"):
             getattr(L, n).restype = st
@@ -169,11 +187,54 @@ def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale:
                      pool_scope=pool_scope, pool_op=pool_op, query_head_map=query_head_map)
 
 
+def _cache(q, k, seq_lens, block_table, seq_len):
+    """(descriptor overrides, KasKvCache or None) of a varlen / paged decode cache.
+    Paged: k, v are page pools [num_pages, Hkv, P, D]; block_table [B, max_pages];
+    seq_len is the longest sequence the call may see."""
+    if seq_lens is None and block_table is None:
+        return None, None
+    c = KasKvCache(None if seq_lens is None else seq_lens.data_ptr(),
+                   None if block_table is None else block_table.data_ptr(), 0, 0, 0, 0, 0)
+    over = None
+    if block_table is not None:
+        if seq_len is None:
+            raise KasError(1, "cache", "a paged cache needs seq_len (the longest sequence)")
+        if k.stride(3) != 1 or k.stride(2) != k.shape[3]:
+            raise KasError(1, "cache", "page rows must be contiguous [.., P, D]")
+        c.page_size, c.max_pages, c.num_pages = k.shape[2], block_table.shape[1], k.shape[0]
+        c.page_stride, c.page_head_stride = k.stride(0), k.stride(1)
+        over = dict(seq_len=int(seq_len), n_kv_heads=k.shape[1], head_dim=k.shape[3])
+    return over, c
+
+
+def _decode_desc(q, k, pct, scale, over, **kw) -> KasDesc:
+    if over is None:
+        return _desc_from(q, k, pct, False, scale, **kw)
+    B, Hq, D = q.shape
+    return make_desc(B, Hq, over["n_kv_heads"], over["head_dim"], over["seq_len"], pct, q.dtype,
+                     softmax_scale=scale, **kw)
+
+
+def _ws_kv(desc, cache, op, ws, device):
+    if cache is None:
+        return _ws(desc, op, ws, device)
+    n = ctypes.c_size_t(0)
+    _check(_load().kas_workspace_size_kv(ctypes.byref(desc), ctypes.byref(cache), op, ctypes.byref(n)),
+           "workspace_size")
+    if ws is None:
+        ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device)
+    return ws
+
+
 def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
-                  pool_scope: int = 0, pool_op: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                  pool_scope: int = 0, pool_op: int = 0, seq_lens=None, block_table=None,
+                  seq_len=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hs,kd], o [B,Hq,D]); Hs = Hkv, or 1
-    with pool_scope=1 (one set pooled over all heads)."""
-    desc = _desc_from(q, k, pct, False, scale, pool_scope=pool_scope, pool_op=pool_op)
+    with pool_scope=1 (one set pooled over all heads). seq_lens (device int32 [B])
+    gives each sequence's length; block_table (device int32 [B, max_pages]) makes
+    k, v page pools [num_pages, Hkv, P, D] (then seq_len = the longest sequence)."""
+    over, cache = _cache(q, k, seq_lens, block_table, seq_len)
+    desc = _decode_desc(q, k, pct, scale, over, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "decode_anchor", "k and v must share strides")
     kd = decode_k(desc.seq_len, pct)
@@ -182,25 +243,38 @@ def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, w
         idx_out = torch.empty((desc.batch, hs, kd), dtype=torch.int32, device=q.device)
     if o is None:
         o = torch.empty_like(q)
-    ws = _ws(desc, OP_DECODE_ANCHOR, ws, q.device)
-    _check(_load().kas_decode_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
-                                     _ptr(o), _ptr(ws), ws.numel(), _stream(q)), "decode_anchor")
+    ws = _ws_kv(desc, cache, OP_DECODE_ANCHOR, ws, q.device)
+    if cache is None:
+        rc = _load().kas_decode_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
+                                       _ptr(o), _ptr(ws), ws.numel(), _stream(q))
+    else:
+        rc = _load().kas_decode_anchor_kv(ctypes.byref(desc), ctypes.byref(cache), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(idx_out), _ptr(o), _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "decode_anchor")
     return idx_out, o
 
 
 def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
-                 query_head_map: bool = False) -> torch.Tensor:
+                 query_head_map: bool = False, seq_lens=None, block_table=None, seq_len=None) -> torch.Tensor:
     """anchor_idx [B,Hkv_a,kd] int32 (device), head_map int32 [Hkv] (device) or None;
-    with query_head_map, head_map holds one entry per query head [Hq]."""
-    desc = _desc_from(q, k, pct, False, scale, query_head_map=int(query_head_map))
+    with query_head_map, head_map holds one entry per query head [Hq]. Cache
+    arguments as in decode_anchor."""
+    over, cache = _cache(q, k, seq_lens, block_table, seq_len)
+    desc = _decode_desc(q, k, pct, scale, over, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "decode_reuse", "k and v must share strides")
     if o is None:
         o = torch.empty_like(q)
-    ws = _ws(desc, OP_DECODE_REUSE, ws, q.device)
-    _check(_load().kas_decode_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
-                                    anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws),
-                                    ws.numel(), _stream(q)), "decode_reuse")
+    ws = _ws_kv(desc, cache, OP_DECODE_REUSE, ws, q.device)
+    if cache is None:
+        rc = _load().kas_decode_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
+                                      anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws), ws.numel(),
+                                      _stream(q))
+    else:
+        rc = _load().kas_decode_reuse_kv(ctypes.byref(desc), ctypes.byref(cache), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(anchor_idx), anchor_idx.shape[1], _ptr(head_map), _ptr(o),
+                                         _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "decode_reuse")
     return o
 
 
@@ -239,16 +313,24 @@ def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o
     return o
 
 
-def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None) -> torch.Tensor:
-    """Dense decode attention over all N keys: q [B,Hq,D], k/v [B,Hkv,N,D] -> o [B,Hq,D]."""
-    desc = _desc_from(q, k, 100, False, scale)
+def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None, seq_lens=None, block_table=None,
+                 seq_len=None) -> torch.Tensor:
+    """Dense decode attention over all keys: q [B,Hq,D], k/v [B,Hkv,N,D] -> o [B,Hq,D].
+    Cache arguments as in decode_anchor."""
+    over, cache = _cache(q, k, seq_lens, block_table, seq_len)
+    desc = _decode_desc(q, k, 100, scale, over)
     if k.stride() != v.stride():
         raise KasError(1, "decode_dense", "k and v must share strides")
     if o is None:
         o = torch.empty_like(q)
-    ws = _ws(desc, OP_DECODE_DENSE, ws, q.device)
-    _check(_load().kas_decode_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
-                                    ws.numel(), _stream(q)), "decode_dense")
+    ws = _ws_kv(desc, cache, OP_DECODE_DENSE, ws, q.device)
+    if cache is None:
+        rc = _load().kas_decode_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
+                                      ws.numel(), _stream(q))
+    else:
+        rc = _load().kas_decode_dense_kv(ctypes.byref(desc), ctypes.byref(cache), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(o), _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "decode_dense")
     return o
 
 

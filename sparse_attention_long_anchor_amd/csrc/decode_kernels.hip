@@ -33,19 +33,48 @@ constexpr int kMaxSplitRows = 2048;
 // the query head's KV head g / kvdiv.
 __device__ __forceinline__ int kv_head(const DecodeArgs& a, int g) { return a.kvdiv > 1 ? g / a.kvdiv : g; }
 
+// Keys of sequence b (all sequences have N unless lengths are given).
+// (lengths are trusted inputs, clamped to [1, N])
+__device__ __forceinline__ int64_t seq_n(const DecodeArgs& a, int b) {
+  if (!a.seq_lens) return a.N;
+  const int64_t n = a.seq_lens[b];
+  return n < 1 ? 1 : (n > a.N ? a.N : n);
+}
+// Rows of sequence b's sets in a gather: its k, or (dense) all its keys.
+__device__ __forceinline__ int64_t set_rows(const DecodeArgs& a, int b) {
+  if (!a.seq_lens) return a.kk;
+  const int64_t n = seq_n(a, b);
+  return a.rows_are_keys ? n : decode_k_of(n, a.pct);
+}
+// Keys the selection keeps for one of its units (sets).
+__device__ __forceinline__ uint32_t unit_k(const DecodeArgs& a, int64_t unit) {
+  if (!a.seq_lens) return (uint32_t)a.kk;
+  const int64_t per_b = a.sel_units / a.B;
+  return (uint32_t)decode_k_of(seq_n(a, (int)(unit / per_b)), a.pct);
+}
+// A page id from the block table (trusted input, clamped to the pool).
+__device__ __forceinline__ int64_t page_id(const DecodeArgs& a, int32_t p) {
+  return ((uint64_t)p < (uint64_t)a.num_pages) ? p : 0;
+}
+
+constexpr int kScorePages = kScoreMaxRows / 16 + 1;  // pages a scoring chunk can touch
+
 // ------------------------------------------------------------------ dec_score
 
 constexpr float kBigSum = 0x1p64f;   // lazy-reference term that forces the exact update
 
-template <typename T, int D, int G>
+// PG: a paged cache; the chunk's page ids are read into LDS once, and a
+// 16-key block (pages hold a power-of-two multiple of 16 keys) lies in one page.
+template <typename T, int D, int G, bool PG = false>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   using QK = QKMfma<T, D>;
   __shared__ float s_m[4][G], s_l[4][G];
+  __shared__ int32_t s_pg[PG ? kScorePages : 1];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int64_t row0 = (int64_t)chunk * a.score_rows;
-  const int nrows = (int)min((int64_t)a.score_rows, a.N - row0);
+  const int nrows = (int)min((int64_t)a.score_rows, seq_n(a, b) - row0);   // <= 0: nothing to score
   const int64_t unit = (int64_t)b * a.Hkv + g;
 
   if (chunk == 0) {
@@ -53,6 +82,12 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
     for (int i = tid; i < kHistWords; i += 256) h[i] = 0u;
   }
   const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + row0 * D;
+  const int64_t p0 = row0 >> a.page_shift;
+  if (PG) {
+    const int np = nrows > 0 ? (int)(((row0 + nrows - 1) >> a.page_shift) - p0 + 1) : 0;
+    for (int i = tid; i < np; i += 256) s_pg[i] = a.block_table[(int64_t)b * a.max_pages + p0 + i];
+    __syncthreads();
+  }
   typename QK::QFrag qf;
   QK::load_q(qf, (const T*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
   float* lg = a.logits + (unit * a.N + row0) * G;
@@ -68,7 +103,13 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   // for them).
   auto load = [&](int blk, QK& dst) __attribute__((always_inline)) {
     const int jr = blk * 16 + c16;
-    dst.load_k(kb + (int64_t)(jr < nrows ? jr : 0) * D, q4);
+    if (PG) {
+      const int64_t j = row0 + (jr < nrows ? jr : 0);
+      const int64_t pg = page_id(a, s_pg[(j >> a.page_shift) - p0]);
+      dst.load_k((const T*)a.k + pg * a.page_stride + g * a.page_hstride + (j & ((1 << a.page_shift) - 1)) * D, q4);
+    } else {
+      dst.load_k(kb + (int64_t)(jr < nrows ? jr : 0) * D, q4);
+    }
   };
   // STEADY: a full block inside the steady loop (all rows valid); for G = 4
   // and 8 the logits are transposed across lanes so that the whole wave
@@ -223,6 +264,7 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
 
   float* P = a.pooled + unit * a.pstride;
   const int64_t base = (int64_t)chunk * kSelChunk;
+  const int64_t Nb = seq_n(a, b);       // keys past the sequence's end pool to 0
   if (!ALL) {
     float M[G], iL[G];
 #pragma unroll
@@ -233,8 +275,10 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
       const int64_t j = base + i * 256 + tid;
       if (j < a.N) {
         float acc = 0.f;
+        if (j < Nb) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc = pool(acc, exp2_fast(lg[j * G + h] - M[h]) * iL[h]);
+          for (int h = 0; h < G; ++h) acc = pool(acc, exp2_fast(lg[j * G + h] - M[h]) * iL[h]);
+        }
         P[j] = acc;
         atomicAdd(&s_hist[__float_as_uint(acc) >> 21], 1u);
       }
@@ -247,7 +291,7 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
       const int64_t j = base + i * 256 + tid;
       if (j < a.N) {
         float acc = 0.f;
-        for (int g = 0; g < a.Hkv; ++g) {
+        for (int g = 0; g < (j < Nb ? a.Hkv : 0); ++g) {
           const float* lg = lg0 + g * gstride + j * G;
 #pragma unroll
           for (int h = 0; h < G; ++h) acc = pool(acc, exp2_fast(lg[h] - s_M[g * G + h]) * s_iL[g * G + h]);
@@ -293,7 +337,7 @@ __global__ __launch_bounds__(256) void sel_cand_kernel(DecodeArgs a) {
   }
   int b1;
   uint32_t ab1;
-  block_find_bin(a.hist + unit * kHistWords, kBins1, (uint32_t)a.kk, s_tmp, s_res, b1, ab1);
+  block_find_bin(a.hist + unit * kHistWords, kBins1, unit_k(a, unit), s_tmp, s_res, b1, ab1);
   uint32_t gt = 0, nc = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -345,15 +389,16 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   uint32_t g_ex = block_excl_scan_256(gt, s_tmp, nullptr) + gt_before;
   uint32_t e_ex = block_excl_scan_256(eq, s_tmp, nullptr) + eq_before;
   int32_t* out = a.idx_out + unit * a.kk;
+  const uint32_t ku = unit_k(a, unit);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (j0 + i >= a.N) break;
     if (u[i] > tau) {
       const uint32_t pos = g_ex + min(e_ex, r);
-      if (pos < (uint32_t)a.kk) out[pos] = (int32_t)(j0 + i);
+      if (pos < ku) out[pos] = (int32_t)(j0 + i);
       ++g_ex;
     } else if (u[i] == tau) {
-      if (e_ex < r && g_ex + e_ex < (uint32_t)a.kk) out[g_ex + e_ex] = (int32_t)(j0 + i);
+      if (e_ex < r && g_ex + e_ex < ku) out[g_ex + e_ex] = (int32_t)(j0 + i);
       ++e_ex;
     }
   }
@@ -381,7 +426,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
   __shared__ uint32_t s_ncand;
   const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
-  const uint32_t k = (uint32_t)a.kk;
+  const uint32_t k = unit_k(a, unit);
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
   const uint32_t* hist1 = a.hist + unit * kHistWords;
   const int64_t N = a.N;
@@ -528,7 +573,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) 
   __shared__ int s_res[2];
   const int64_t unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t k = (uint32_t)a.kk;
+  const uint32_t k = unit_k(a, unit);
   const int nch = a.n_sel_chunks;
   const uint32_t* hist1 = a.hist + unit * kHistWords;
   const uint32_t* cand = a.cand + unit * nch * (int64_t)kSelChunk;
@@ -618,7 +663,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int64_t row0 = (int64_t)split * a.split_rows;
-  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  const int nrows = (int)min((int64_t)a.split_rows, set_rows(a, b) - row0);
   // Index values and the head map are trusted inputs; clamping keeps every
   // access inside the cache even if they are not.
   if (DENSE) {
@@ -805,7 +850,7 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int64_t row0 = (int64_t)split * a.split_rows;
-  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  const int nrows = (int)min((int64_t)a.split_rows, set_rows(a, b) - row0);
   // Index values and the head map are trusted inputs; clamping keeps every
   // access inside the cache even if they are not.
   int ga = a.head_map ? a.head_map[g] : g;
@@ -976,7 +1021,9 @@ __global__ __launch_bounds__(256, 4) void dec_attn_bf16_kernel(DecodeArgs a) {
 // load sits behind a divergent branch in the steady-state loop.
 // DENSE: the split covers keys [row0, row0 + nrows) of the cache and a row's
 // key is its position (no index loads); otherwise the same kernel.
-template <int D, int G, bool FROM_LOGITS, bool DENSE = false, typename E = __bf16>
+// PG: a paged cache; the index sets hold physical rows (translated by
+// dec_page_rows), addressed from k + g * page_hstride.
+template <int D, int G, bool FROM_LOGITS, bool DENSE = false, typename E = __bf16, bool PG = false>
 __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   using QK = QKMfma<E, D>;
   constexpr int NT = D / 16;            // output tiles of 16 dims
@@ -992,7 +1039,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
   const int64_t row0 = (int64_t)split * a.split_rows;
-  const int nrows = (int)min((int64_t)a.split_rows, a.kk - row0);
+  const int nrows = (int)min((int64_t)a.split_rows, set_rows(a, b) - row0);
   const int nblk = (nrows + 15) >> 4;
   const int nb = wave < nblk ? (nblk - wave + 3) >> 2 : 0;   // blocks wave, wave + 4, ...
   int ga = (!DENSE && a.head_map) ? a.head_map[g] : g;
@@ -1000,8 +1047,11 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   const int32_t* idx = DENSE ? nullptr : a.idx + ((int64_t)b * a.Hkv_a + ga) * a.kk + row0;
 
   const int64_t unit = (int64_t)b * a.Hkv + g;
-  const E* kb = (const E*)a.k + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
-  const E* vb = (const E*)a.v + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const E* kb = PG ? (const E*)a.k + kv_head(a, g) * a.page_hstride
+                  : (const E*)a.k + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const E* vb = PG ? (const E*)a.v + kv_head(a, g) * a.page_hstride
+                  : (const E*)a.v + b * a.kv_bstride + kv_head(a, g) * a.kv_hstride;
+  const uint32_t nkeys = PG ? (uint32_t)a.pool_rows : (uint32_t)a.N;   // rows an index may name
   const float* lg = FROM_LOGITS ? a.logits + unit * a.N * G : nullptr;
   typename QK::QFrag qf;
   if (!FROM_LOGITS)
@@ -1033,7 +1083,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   };
   // Index values are trusted inputs; clamping keeps every access inside the cache.
   auto load_blk = [&](int jraw, Blk& B_) {
-    const int jk = ((unsigned)jraw < (unsigned)a.N) ? jraw : 0;
+    const int jk = ((unsigned)jraw < nkeys) ? jraw : 0;
     if (FROM_LOGITS) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) B_.lgt[r] = (4 * q4 + r < G) ? lg[(int64_t)jk * G + 4 * q4 + r] : 0.f;
@@ -1222,16 +1272,22 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
 
 #define KAS_LAUNCH(kernel, grid, block, ctx, arg) (ctx).launch(kernel, grid, block, arg)
 
-template <typename T, int D>
-static hipError_t score_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+template <typename T, int D, bool PG>
+static hipError_t score_launch_pg(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1, PG>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2, PG>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4, PG>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8, PG>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
+}
+template <typename T, int D>
+static hipError_t score_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+  // paged caches hold 16-bit elements only (checked on the host)
+  if (sizeof(T) == 2 && a.block_table) return score_launch_pg<T, D, true>(a, grid, st);
+  return score_launch_pg<T, D, false>(a, grid, st);
 }
 
 hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
@@ -1320,13 +1376,13 @@ static hipError_t attn_bf16_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st
   }
   return hipSuccess;
 }
-template <int D, bool FL, bool DENSE = false, typename E = __bf16>
+template <int D, bool FL, bool DENSE = false, typename E = __bf16, bool PG = false>
 static hipError_t gather_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL, DENSE, E>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL, DENSE, E>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL, DENSE, E>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL, DENSE, E>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_gather_kernel<D, 1, FL, DENSE, E, PG>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_gather_kernel<D, 2, FL, DENSE, E, PG>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_gather_kernel<D, 4, FL, DENSE, E, PG>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_gather_kernel<D, 8, FL, DENSE, E, PG>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -1350,12 +1406,25 @@ static hipError_t launch_combine(const DecodeArgs& a, int dtype, LaunchCtx& ctx)
   return ctx.end(K_DEC_COMBINE);
 }
 
+// Paged caches: the gather over translated physical rows (from_logits is
+// not used: the rows' own K is read again).
+static hipError_t gather_paged(const DecodeArgs& a, int dtype, dim3 grid, LaunchCtx& ctx) {
+  if (dtype == 1)
+    return a.D == 128 ? gather_launch<128, false, false, __bf16, true>(a, grid, ctx)
+                      : gather_launch<64, false, false, __bf16, true>(a, grid, ctx);
+  if (dtype == 2)
+    return a.D == 128 ? gather_launch<128, false, false, _Float16, true>(a, grid, ctx)
+                      : gather_launch<64, false, false, _Float16, true>(a, grid, ctx);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx) {
   dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
   const int kid = from_logits ? K_DEC_ATTN_ANCHOR : K_DEC_ATTN;
   ctx.begin(kid);
-  if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx)
+  if (a.block_table) e = gather_paged(a, dtype, grid, ctx);
+  else if (dtype == 1) e = from_logits ? attn_bf16_by_d<true>(a, grid, ctx)
                                   : attn_bf16_by_d<false>(a, grid, ctx);
   else if (dtype == 2)   // fp16: the pipelined gather (the staged variant is bf16 only)
     e = from_logits ? (a.D == 128 ? gather_launch<128, true, false, _Float16>(a, grid, ctx)
@@ -1373,7 +1442,9 @@ hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   dim3 grid(a.nsplit, a.Hkv, a.B);
   hipError_t e;
   ctx.begin(K_DEC_DENSE);
-  if (dtype == 1)
+  if (a.block_table)   // the sets are the translated rows of keys 0 .. seq_len - 1
+    e = gather_paged(a, dtype, grid, ctx);
+  else if (dtype == 1)
     e = a.D == 128 ? gather_launch<128, false, true>(a, grid, ctx) : gather_launch<64, false, true>(a, grid, ctx);
   else if (dtype == 2)
     e = a.D == 128 ? gather_launch<128, false, true, _Float16>(a, grid, ctx)
@@ -1383,6 +1454,39 @@ hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   if (e != hipSuccess) return e;
   if ((e = ctx.end(K_DEC_DENSE)) != hipSuccess) return e;
   return launch_combine(a, dtype, ctx);
+}
+
+// ------------------------------------------------------------------ paged caches
+
+// Physical row of every key in this call's sets: key j of sequence b sits in
+// page block_table[b][j >> page_shift] at row j & (P - 1); rows are counted
+// in D elements from k + g * page_hstride, so a page starts at row
+// page * page_stride / D. One workgroup per (chunk of the set, set, b); set s
+// reads source set head_map[s] (or s, clamped to the source's sets), or the
+// keys themselves when there is no source.
+__global__ __launch_bounds__(256) void dec_page_rows_kernel(DecodeArgs a) {
+  const int s = blockIdx.y, b = blockIdx.z;
+  const int64_t rows = set_rows(a, b), n = seq_n(a, b);
+  int ga = (a.page_src && a.head_map) ? a.head_map[s] : s;
+  ga = ((unsigned)ga < (unsigned)a.page_src_sets) ? ga : 0;
+  const int32_t* in = a.page_src ? a.page_src + ((int64_t)b * a.page_src_sets + ga) * a.kk : nullptr;
+  uint32_t* out = a.prow + ((int64_t)b * gridDim.y + s) * a.kk;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int64_t page_rows = a.page_stride / a.D;
+  const int64_t mask = (int64_t(1) << a.page_shift) - 1;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows; i += (int64_t)gridDim.x * 256) {
+    int64_t j = in ? (int64_t)in[i] : i;
+    j = ((uint64_t)j < (uint64_t)n) ? j : 0;            // trusted input, kept in the sequence
+    out[i] = (uint32_t)(page_id(a, bt[j >> a.page_shift]) * page_rows + (j & mask));
+  }
+}
+
+hipError_t launch_page_rows(const DecodeArgs& a, int nsets, LaunchCtx& ctx) {
+  ctx.begin(K_DEC_PAGE_ROWS);
+  const int64_t chunks = (a.kk + 255) / 256;
+  dim3 grid((unsigned)(chunks < 64 ? chunks : 64), nsets, a.B);
+  KAS_LAUNCH(dec_page_rows_kernel, grid, dim3(256), ctx, a);
+  return ctx.end(K_DEC_PAGE_ROWS);
 }
 
 }  // namespace kas

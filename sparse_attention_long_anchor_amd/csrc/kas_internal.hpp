@@ -24,6 +24,7 @@ enum KernelId {
   K_DEC_DENSE,
   K_PRE_DENSE,
   K_PRE_POOL_HEADS,
+  K_DEC_PAGE_ROWS,
   K_COUNT_
 };
 const char* kernel_name(int id);
@@ -52,6 +53,7 @@ constexpr int kHistWords = kBins1 + kBins2 + kBins3;
 constexpr int kSelChunk = 4096;         // scores per selection workgroup
 constexpr int kMaxSelChunks = 4096;     // chunks the chunked selection resolves in LDS
 constexpr int kMaxPoolHeads = 256;      // query heads one all-heads pooled set may cover
+constexpr int kScoreMaxRows = 4096;     // keys per scoring workgroup (at most)
 
 struct DecodeArgs {
   const void* q;
@@ -89,7 +91,27 @@ struct DecodeArgs {
   // reuse with one anchor set per query head: Hkv and G describe query heads
   // (Hkv = Hq, G = 1) and KV head = head / kvdiv; 1 otherwise
   int kvdiv;
+  // sequences of different lengths and paged caches
+  const int32_t* seq_lens;          // [B] keys of sequence b (<= N), or null: all N
+  int pct;                          // a sequence's set holds decode_k(seq_lens[b], pct) keys
+  int rows_are_keys;                // gathers over whole sequences (dense): seq_lens[b] rows
+  const int32_t* block_table;       // [B, max_pages] page of keys [P i, P i + P), or null
+  int page_shift, max_pages;        // P = 1 << page_shift
+  int64_t page_stride, page_hstride;  // elements between pages / between KV heads in a page
+  int64_t pool_rows;                // paged: rows addressable from k + g * page_hstride
+  int64_t num_pages;                // paged: pages in the pools (page ids are clamped to it)
+  uint32_t* prow;                   // paged: physical rows of the sets this call gathers
+  const int32_t* page_src;          // page-row translation: source sets, or null (keys 0..)
+  int page_src_sets;                // sets per batch row in page_src
 };
+
+// Decode k of n keys: round-half-up(pct * n / 100) clamped to [1, n].
+__host__ __device__ inline int64_t decode_k_of(int64_t n, int pct) {
+  if (n <= 0 || pct <= 0) return n > 0 ? 1 : 0;
+  int64_t k = ((int64_t)pct * n + 50) / 100;
+  k = k > n ? n : k;
+  return k < 1 ? 1 : k;
+}
 
 hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
 hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx);
@@ -98,5 +120,9 @@ hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, 
 // Dense decode attention over all N keys: the split kernels with row i of a
 // split standing for key split_rows * split + i (idx unused, kk = N).
 hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
+// Paged caches: physical rows of this call's sets into a.prow ([B, nsets,
+// a.kk]); set s reads source set head_map[s] (or s, clamped) of a.page_src,
+// or, with a.page_src null, the keys 0 .. seq_len - 1 themselves.
+hipError_t launch_page_rows(const DecodeArgs& a, int nsets, LaunchCtx& ctx);
 
 }  // namespace kas

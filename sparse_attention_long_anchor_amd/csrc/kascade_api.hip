@@ -39,7 +39,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
-    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads"};
+    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
 
@@ -224,19 +224,21 @@ static int decode_split_rows(int64_t units, int64_t kk) {
 }
 static int decode_score_rows() {
   int r = env_int("KAS_DECODE_SCORE_ROWS", 1024);
-  return (r + 63) / 64 * 64;
+  r = (r + 63) / 64 * 64;
+  return r > kScoreMaxRows ? kScoreMaxRows : r;
 }
 
 struct DecodePlan {
   int64_t kk;
   int score_rows, n_score_chunks, n_sel_chunks, split_rows, nsplit;
   size_t off_logits, off_stats, off_pooled, off_hist, off_counts, off_selstate, off_cand, off_part_o,
-      off_part_ml, total;
+      off_part_ml, off_prow, total;
 };
 
 // dense: the split rows cover the whole cache (kk = N) and only the split
-// partials are needed
-static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false) {
+// partials are needed. paged: room for the physical rows of the call's sets
+// (Hkv sets of kk rows per batch row; dense: one set of all N keys).
+static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false, bool paged = false) {
   DecodePlan p{};
   p.kk = dense ? s.N : decode_k(s.N, s.pct);
   p.score_rows = decode_score_rows();
@@ -258,8 +260,64 @@ static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false) {
   }
   p.off_part_o = take((size_t)s.B * s.Hq * p.nsplit * s.D * sizeof(float));
   p.off_part_ml = take((size_t)s.B * s.Hq * p.nsplit * 2 * sizeof(float));
+  if (paged) p.off_prow = take((size_t)s.B * (dense ? 1 : s.Hkv) * p.kk * sizeof(uint32_t));
   p.total = off;
   return p;
+}
+
+// A checked kas_kv_cache_t (all zero: the dense cache of the descriptor).
+struct CacheView {
+  const int32_t* seq_lens = nullptr;
+  const int32_t* block_table = nullptr;
+  int shift = 0, max_pages = 0;
+  int64_t num_pages = 0, page_stride = 0, page_hstride = 0, pool_rows = 0;
+  bool paged() const { return block_table != nullptr; }
+};
+
+static kas_status_t check_cache(const kas_kv_cache_t* c, const Shape& s, CacheView& v) {
+  v = CacheView{};
+  if (!c) return KAS_OK;
+  v.seq_lens = c->seq_lens;
+  if (!c->block_table) return KAS_OK;
+  if (s.dtype == KAS_DTYPE_F32) return fail(KAS_ERR_UNSUPPORTED, "paged caches hold bf16 or fp16");
+  const int64_t P = c->page_size;
+  if (P < 16 || P > (1 << 20) || (P & (P - 1)))
+    return fail(KAS_ERR_INVALID_ARGUMENT, "page_size must be a power of two in [16, 2^20] (got %lld)", (long long)P);
+  if (c->max_pages < (s.N + P - 1) / P)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "max_pages (%d) does not cover seq_len %lld", c->max_pages, (long long)s.N);
+  if (c->num_pages < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  const int64_t phs = c->page_head_stride ? c->page_head_stride : P * s.D;
+  const int64_t ps = c->page_stride ? c->page_stride : s.Hkv * P * s.D;
+  if (phs < P * s.D || ps < (s.Hkv - 1) * phs + P * s.D)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "page strides overlap the [P, D] rows of a head");
+  const int64_t vec = 16 / (int64_t)s.esize;
+  if (ps % vec || phs % vec) return fail(KAS_ERR_INVALID_ARGUMENT, "page strides must be multiples of 16 bytes");
+  if (ps % s.D) return fail(KAS_ERR_INVALID_ARGUMENT, "page_stride must be a multiple of head_dim");
+  const int64_t rows = c->num_pages * (ps / s.D);
+  if (rows >= (int64_t(1) << 31) || c->num_pages >= (int64_t(1) << 31))
+    return fail(KAS_ERR_UNSUPPORTED, "page pool of %lld rows: 2^31 or more", (long long)rows);
+  v.block_table = c->block_table;
+  int shift = 0;
+  while ((int64_t(1) << shift) < P) ++shift;
+  v.shift = shift;
+  v.max_pages = c->max_pages;
+  v.num_pages = c->num_pages;
+  v.page_stride = ps;
+  v.page_hstride = phs;
+  v.pool_rows = rows;
+  return KAS_OK;
+}
+
+static void fill_cache(DecodeArgs& a, const CacheView& v, const Shape& s) {
+  a.seq_lens = v.seq_lens;
+  a.pct = s.pct;
+  a.block_table = v.block_table;
+  a.page_shift = v.shift;
+  a.max_pages = v.max_pages;
+  a.num_pages = v.num_pages;
+  a.page_stride = v.page_stride;
+  a.page_hstride = v.page_hstride;
+  a.pool_rows = v.pool_rows;
 }
 
 // The reuse shape with one anchor set per query head: the gather kernels run
@@ -295,6 +353,7 @@ static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, c
   }
   a.part_o = (float*)(ws + p.off_part_o);
   a.part_ml = (float*)(ws + p.off_part_ml);
+  a.prow = p.off_prow ? (uint32_t*)(ws + p.off_prow) : nullptr;
 }
 
 static kas_status_t check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -349,18 +408,25 @@ kas_status_t kas_prefill_index_offsets(const kas_desc_t* desc, int64_t* offsets,
 }
 
 kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* bytes) {
+  return kas_workspace_size_kv(desc, nullptr, op, bytes);
+}
+
+kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int32_t op, size_t* bytes) {
   if (!bytes) return fail(KAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
   Shape s;
   const bool prefill = op == KAS_OP_PREFILL_ANCHOR || op == KAS_OP_PREFILL_REUSE || op == KAS_OP_PREFILL_DENSE;
   if (op < KAS_OP_DECODE_ANCHOR || op > KAS_OP_PREFILL_DENSE) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   kas_status_t st = check_desc(desc, prefill, s);
   if (st != KAS_OK) return st;
+  CacheView cv;
+  if (cache && prefill) return fail(KAS_ERR_UNSUPPORTED, "varlen / paged caches are decode only");
+  if ((st = check_cache(cache, s, cv))) return st;
   if (op == KAS_OP_PREFILL_DENSE) {
     *bytes = 0;
   } else if (op == KAS_OP_DECODE_REUSE && s.qmap) {
-    *bytes = plan_decode(per_query_head(s), false).total;
+    *bytes = plan_decode(per_query_head(s), false, false, cv.paged()).total;
   } else if (!prefill) {
-    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE).total;
+    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE, cv.paged()).total;
   } else {
     *bytes = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, op == KAS_OP_PREFILL_ANCHOR);
   }
@@ -369,17 +435,26 @@ kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* byte
 
 kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return kas_decode_anchor_kv(desc, nullptr, q, k, v, idx_out, o, ws, ws_bytes, stream);
+}
+
+kas_status_t kas_decode_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
+                                  size_t ws_bytes, void* stream) {
   Shape s;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
   if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
-  DecodePlan p = plan_decode(s, true);
+  DecodePlan p = plan_decode(s, true, false, cv.paged());
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a;
   fill_decode_args(s, p, true, (char*)ws, a);
+  fill_cache(a, cv, s);
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx_out = idx_out;
   // the output reads the selected sets back: one per KV head, or one shared
@@ -389,6 +464,13 @@ kas_status_t kas_decode_anchor(const kas_desc_t* desc, const void* q, const void
   if ((e = launch_decode_score(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
   if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
   if ((e = launch_decode_select(a, ctx)) != hipSuccess) return hip_fail(e, "decode_select");
+  if (cv.paged()) {
+    // physical rows of every KV head's set, then the output from them
+    a.page_src = idx_out;
+    a.page_src_sets = a.Hkv_a;
+    if ((e = launch_page_rows(a, s.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    a.idx = (const int32_t*)a.prow; a.Hkv_a = s.Hkv;
+  }
   if ((e = launch_decode_attn(a, s.dtype, true, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
   return KAS_OK;
 }
@@ -397,9 +479,19 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
                               const int32_t* anchor_idx, int32_t anchor_kv_heads,
                               const int32_t* head_map, void* o, void* ws, size_t ws_bytes,
                               void* stream) {
+  return kas_decode_reuse_kv(desc, nullptr, q, k, v, anchor_idx, anchor_kv_heads, head_map, o, ws, ws_bytes,
+                             stream);
+}
+
+kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                 const void* k, const void* v, const int32_t* anchor_idx,
+                                 int32_t anchor_kv_heads, const int32_t* head_map, void* o, void* ws,
+                                 size_t ws_bytes, void* stream) {
   Shape s;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -410,15 +502,23 @@ kas_status_t kas_decode_reuse(const kas_desc_t* desc, const void* q, const void*
                 "without a head map, anchor_kv_heads must be n_kv_heads (identity) or 1 (shared set)");
   if (s.qmap && !head_map) return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map needs a head_map of n_q_heads entries");
   const Shape sr = s.qmap ? per_query_head(s) : s;
-  DecodePlan p = plan_decode(sr, false);
+  DecodePlan p = plan_decode(sr, false, false, cv.paged());
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a;
   fill_decode_args(sr, p, false, (char*)ws, a);
+  fill_cache(a, cv, s);
   a.kvdiv = s.qmap ? s.G : 1;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
+  if (cv.paged()) {
+    // this layer's sets (head map applied) as physical rows
+    a.page_src = anchor_idx;
+    a.page_src_sets = anchor_kv_heads;
+    if ((e = launch_page_rows(a, sr.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    a.idx = (const int32_t*)a.prow; a.Hkv_a = sr.Hkv; a.head_map = nullptr;
+  }
   if ((e = launch_decode_attn(a, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
   return KAS_OK;
 }
@@ -485,20 +585,36 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
 
 kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v, void* o,
                               void* ws, size_t ws_bytes, void* stream) {
+  return kas_decode_dense_kv(desc, nullptr, q, k, v, o, ws, ws_bytes, stream);
+}
+
+kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                 const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                                 void* stream) {
   Shape s;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
-  DecodePlan p = plan_decode(s, false, true);
+  DecodePlan p = plan_decode(s, false, true, cv.paged());
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
   DecodeArgs a;
   fill_decode_args(s, p, false, (char*)ws, a);
+  fill_cache(a, cv, s);
+  a.rows_are_keys = 1;       // a sequence's "set" is all its keys
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
+  if (cv.paged()) {
+    a.page_src = nullptr;
+    a.page_src_sets = 1;
+    if ((e = launch_page_rows(a, 1, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    a.idx = (const int32_t*)a.prow; a.Hkv_a = 1;
+  }
   if ((e = launch_decode_dense(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_dense");
   return KAS_OK;
 }

@@ -153,3 +153,39 @@ def test_profile_names():
         assert n in names
     with pytest.raises(b.KasError):
         b.profile_query("no_such_kernel")
+
+
+def test_kv_cache_layout_checks_without_gpu():
+    import torch
+    b = _kas()
+    L = b._load()
+    fake = ctypes.c_void_p(1 << 20)
+    d = b.make_desc(2, 8, 2, 128, 4096, 10, torch.bfloat16)
+    n = ctypes.c_size_t(0)
+
+    def ws(c, op=b.OP_DECODE_ANCHOR, desc=d):
+        return L.kas_workspace_size_kv(ctypes.byref(desc), ctypes.byref(c) if c is not None else None, op,
+                                       ctypes.byref(n))
+    assert ws(None) == 0 and n.value == b.workspace_size(d, b.OP_DECODE_ANCHOR)
+    varlen = b.KasKvCache(1 << 20, None, 0, 0, 0, 0, 0)
+    assert ws(varlen) == 0 and n.value == b.workspace_size(d, b.OP_DECODE_ANCHOR)
+    paged = b.KasKvCache(None, 1 << 20, 64, 64, 100, 0, 0)
+    assert ws(paged) == 0 and n.value > b.workspace_size(d, b.OP_DECODE_ANCHOR)   # physical rows
+    assert ws(paged, b.OP_DECODE_DENSE) == 0
+    bad = [
+        (b.KasKvCache(None, 1 << 20, 48, 100, 100, 0, 0), 1),            # page size not a power of two
+        (b.KasKvCache(None, 1 << 20, 8, 600, 100, 0, 0), 1),             # page size below 16
+        (b.KasKvCache(None, 1 << 20, 64, 63, 100, 0, 0), 1),             # max_pages short of 4096 keys
+        (b.KasKvCache(None, 1 << 20, 64, 64, 0, 0, 0), 1),               # no pages
+        (b.KasKvCache(None, 1 << 20, 64, 64, 100, 64 * 128, 0), 1),      # page stride overlaps heads
+        (b.KasKvCache(None, 1 << 20, 64, 64, 1 << 40, 0, 0), 2),         # pool of 2^31 rows or more
+    ]
+    for c, want in bad:
+        assert ws(c) == want, (c.page_size, c.max_pages, c.num_pages, L.kas_last_error())
+    df = b.make_desc(2, 8, 2, 64, 2048, 10, torch.float32)
+    assert ws(paged, desc=df) == 2 and b"bf16 or fp16" in L.kas_last_error()
+    dp = b.make_desc(1, 8, 2, 128, 256, 10, torch.bfloat16)
+    assert ws(varlen, b.OP_PREFILL_ANCHOR, dp) == 2                      # decode only
+    r = L.kas_decode_anchor_kv(ctypes.byref(d), ctypes.byref(bad[0][0]), fake, fake, fake, fake, fake, fake,
+                               1 << 30, None)
+    assert r == 1 and b"power of two" in L.kas_last_error()

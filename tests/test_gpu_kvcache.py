@@ -1,0 +1,161 @@
+"""GPU parity of decode over varlen and paged KV caches (the README announces
+paged and varlen kernels), through the C ABI.
+
+Each sequence b of a varlen batch is checked against the oracle run on its
+own contiguous keys [0, seq_lens[b]); keys past a sequence's end hold random
+values that must not matter. A paged cache holds the same rows scattered over
+a shuffled page pool; its index sets, reuse and dense outputs must equal the
+contiguous varlen results bit for bit (the same kernels over the same rows),
+and its anchor output (which reads K again instead of stored logits) must
+match the oracle.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import oracle
+from parity_util import TOL, assert_index_set, max_abs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _kas():
+    import sparse_attention_long_anchor_amd as kas
+    return kas
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _paged(k, v, P, seed):
+    """Scatter contiguous k, v [B, Hkv, N, D] into page pools [num_pages, Hkv, P, D]
+    (shuffled page ids, spare pages filled with noise) and a block table."""
+    B, Hkv, N, D = k.shape
+    per = (N + P - 1) // P
+    npages = B * per + 3
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(npages)[: B * per].reshape(B, per).astype(np.int32)
+    kp = torch.randn((npages, Hkv, P, D), device=DEV).to(k.dtype)
+    vp = torch.randn((npages, Hkv, P, D), device=DEV).to(v.dtype)
+    for b in range(B):
+        for i in range(per):
+            n = min(P, N - i * P)
+            kp[ids[b, i], :, :n] = k[b, :, i * P: i * P + n]
+            vp[ids[b, i], :, :n] = v[b, :, i * P: i * P + n]
+    return kp, vp, torch.as_tensor(ids, device=DEV)
+
+
+def _lens(B, N, seed, must=()):
+    rng = np.random.default_rng(seed)
+    L = rng.integers(1, N + 1, B)
+    for i, x in enumerate(must):
+        L[i] = x
+    return L.astype(np.int32)
+
+
+def _check_varlen(w, q, k, v, lens, pct, label, P=None):
+    kas = _kas()
+    B, Hkv = w.batch, w.n_kv_heads
+    tl = torch.as_tensor(lens, device=DEV)
+    _say(f"[decode varlen{' paged P=%d' % P if P else ''}] {label}: lens={lens.tolist()} pct={pct}")
+    idx, o = kas.decode_anchor(q, k, v, pct, seq_lens=tl)
+    o_dense = kas.decode_dense(q, k, v, seq_lens=tl)
+    q2 = torch.flip(q, dims=[1]).contiguous()                 # a reuse layer: other queries, same cache
+    hm = np.random.default_rng(3).integers(0, Hkv, Hkv).astype(np.int32)
+    o_reuse = kas.decode_reuse(q2, k, v, idx, torch.as_tensor(hm, device=DEV), pct, seq_lens=tl)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    q2n = _np(q2)
+    tol = TOL[w.dtype]
+    worst = [0.0, 0.0, 0.0]
+    swaps = 0
+    for b in range(B):
+        n = int(lens[b])
+        kk = oracle.decode_k(n, pct)
+        sl = (slice(b, b + 1), slice(None), slice(0, n))
+        oidx, oo, pooled = oracle.decode_anchor(qn[b:b + 1], kn[sl], vn[sl], pct, want_pooled=True)
+        for g in range(Hkv):
+            swaps += assert_index_set(gi[b, g, :kk], oidx[0, g], pooled[0, g], kk, where=f"{label} b{b} g{g}")
+        own = gi[b:b + 1, :, :kk]
+        o_same = oracle.decode_reuse(qn[b:b + 1], kn[sl], vn[sl], own, np.arange(Hkv, dtype=np.int32))
+        worst[0] = max(worst[0], max_abs(_np(o[b:b + 1]), o_same), max_abs(_np(o[b:b + 1]), oo))
+        ref_r = oracle.decode_reuse(q2n[b:b + 1], kn[sl], vn[sl], own, hm)
+        worst[1] = max(worst[1], max_abs(_np(o_reuse[b:b + 1]), ref_r))
+        ref_d = oracle.dense_attention(qn[b:b + 1, :, None, :], kn[sl], vn[sl], causal=False)[:, :, 0, :]
+        worst[2] = max(worst[2], max_abs(_np(o_dense[b:b + 1]), ref_d))
+    _say(f"    near-tie swaps={swaps} max|o-o_oracle| anchor={worst[0]:.3g} reuse={worst[1]:.3g} "
+         f"dense={worst[2]:.3g} tol={tol}")
+    assert max(worst) <= tol
+    if P is None:
+        return idx, o, o_reuse, o_dense
+    # the same calls on a paged copy of the cache
+    kp, vp, bt = _paged(k, v, P, seed=P + B)
+    idx_p, o_p = kas.decode_anchor(q, kp, vp, pct, seq_lens=tl, block_table=bt, seq_len=w.seq_len)
+    od_p = kas.decode_dense(q, kp, vp, seq_lens=tl, block_table=bt, seq_len=w.seq_len)
+    or_p = kas.decode_reuse(q2, kp, vp, idx, torch.as_tensor(hm, device=DEV), pct, seq_lens=tl,
+                            block_table=bt, seq_len=w.seq_len)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kk = oracle.decode_k(int(lens[b]), pct)
+        assert torch.equal(idx_p[b, :, :kk], idx[b, :, :kk]), f"paged index sets differ (b{b})"
+    assert torch.equal(or_p, o_reuse), "paged reuse differs from the contiguous cache"
+    assert torch.equal(od_p, o_dense), "paged dense differs from the contiguous cache"
+    err = max_abs(_np(o_p), _np(o))
+    _say(f"    paged: sets, reuse and dense bit-identical; anchor output vs contiguous {err:.3g}")
+    assert err <= tol
+    return idx, o, o_reuse, o_dense
+
+
+VARLEN = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, forced lengths, page size)
+    ("bf16_d128_g4", 4, 32, 8, 128, 5037, "bf16", 10, (5037, 1, 16), 64),
+    ("bf16_d64_g1", 3, 4, 4, 64, 3001, "bf16", 10, (17,), 16),
+    ("f16_d128_g8", 2, 16, 2, 128, 4099, "f16", 25, (4099,), 1024),
+    ("f32_d64_g4", 3, 8, 2, 64, 2048, "f32", 10, (2048, 300), None),
+    ("bf16_many_splits", 2, 8, 2, 128, 40000, "bf16", 50, (40000, 23457), 32),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_decode_varlen_and_paged(case):
+    label, B, Hq, Hkv, D, N, dt, pct, must, P = case
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    _check_varlen(w, q, k, v, _lens(B, N, 5, must), pct, label, P)
+
+
+def test_decode_paged_full_length_equals_dense_cache():
+    """All sequences full length: the paged calls give the contiguous calls' results."""
+    kas = _kas()
+    w = inputgen.custom("decode", 2, 8, 2, 128, 3000, "bf16", wid=55)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx, o = kas.decode_anchor(q, k, v, 10)
+    kp, vp, bt = _paged(k, v, 128, seed=9)
+    idx_p, o_p = kas.decode_anchor(q, kp, vp, 10, block_table=bt, seq_len=3000)
+    od = kas.decode_dense(q, k, v)
+    od_p = kas.decode_dense(q, kp, vp, block_table=bt, seq_len=3000)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_p)
+    assert torch.equal(od, od_p)
+    assert max_abs(_np(o), _np(o_p)) <= TOL["bf16"]
+
+
+def test_decode_varlen_paged_full_size():
+    w = inputgen.WORKLOADS["llama8b_decode_128k"]
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    lens = np.array([131072, 100000, 65536, 4097], np.int32)
+    _check_varlen(w, q, k, v, lens, w.topk_pct, w.name, P=256)
