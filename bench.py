@@ -204,6 +204,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 layer timings")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode timings")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -380,6 +381,8 @@ def main():
     if not args.no_fp16:
         out["fp16"] = fp16_timings(wd if do_dec else None, wp if do_pre else None, dec_state, pre_state, dev,
                                    torch, inputgen, kas)
+    if not args.no_paged and do_dec:
+        out["paged_decode"] = paged_timings(wd, dec_state, dev, torch, inputgen, kas)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
@@ -536,6 +539,46 @@ def _alternate(torch, anchor, reuse, reps):
     ta = sorted(e[0].elapsed_time(e[1]) for e in ev)
     tr = sorted(e[1].elapsed_time(e[2]) for e in ev)
     return ta[reps // 2], tr[reps // 2]
+
+
+def paged_timings(wd, dec_state, dev, torch, inputgen, kas):
+    """Decode anchor and reuse layer times on the contiguous cache and on page
+    pools (pages of P keys, [pages, Hkv, P, D], shuffled page ids) holding
+    the same layers 0 and 1; same alternating protocol as the dtype timings."""
+    (q0, k0, v0, _), (q1, k1, v1, _) = dec_state[0][0], dec_state[0][1]
+    o, ws_a, ws_r, kd = dec_state[2], dec_state[3], dec_state[4], dec_state[5]
+    B, Hkv, N, D = k0.shape
+    hm = torch.as_tensor(inputgen.head_maps(wd)[1], device=dev)
+    idx = torch.empty((B, Hkv, kd), dtype=torch.int32, device=dev)
+    res = {"workload": wd.name, "unit": "us"}
+    ta, tr = _alternate(torch, lambda: kas.decode_anchor(q0, k0, v0, wd.topk_pct, idx_out=idx, o=o, ws=ws_a),
+                        lambda: kas.decode_reuse(q1, k1, v1, idx, hm, wd.topk_pct, o=o, ws=ws_r), 7)
+    res["contiguous"] = {"anchor": round(1e3 * ta, 3), "reuse": round(1e3 * tr, 3)}
+    for P in (16, 64):
+        per = N // P
+        g = torch.Generator(device="cpu").manual_seed(P)
+        ids = torch.randperm(B * per, generator=g).to(torch.int32).view(B, per).to(dev)
+
+        def pool(x):
+            pg = torch.empty((B * per, Hkv, P, D), dtype=x.dtype, device=dev)
+            pg[ids.view(-1).long()] = x.view(B, Hkv, per, P, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, P, D)
+            return pg
+        kp0, vp0, kp1, vp1 = pool(k0), pool(v0), pool(k1), pool(v1)
+        kw = dict(block_table=ids, seq_len=N)
+        wsa = kas.binding._ws_kv(*_kv_desc(kas, q0, kp0, ids, N, wd), kas.OP_DECODE_ANCHOR, None, dev)
+        wsr = kas.binding._ws_kv(*_kv_desc(kas, q0, kp0, ids, N, wd), kas.OP_DECODE_REUSE, None, dev)
+        ta, tr = _alternate(torch, lambda: kas.decode_anchor(q0, kp0, vp0, wd.topk_pct, idx_out=idx, o=o, ws=wsa, **kw),
+                            lambda: kas.decode_reuse(q1, kp1, vp1, idx, hm, wd.topk_pct, o=o, ws=wsr, **kw), 7)
+        res[f"paged_P{P}"] = {"anchor": round(1e3 * ta, 3), "reuse": round(1e3 * tr, 3)}
+        del kp0, vp0, kp1, vp1, wsa, wsr
+        torch.cuda.empty_cache()
+    log(f"[bench] paged decode: {res}")
+    return res
+
+
+def _kv_desc(kas, q, kp, ids, N, w):
+    over, cache = kas.binding._cache(q, kp, None, ids, N)
+    return kas.binding._decode_desc(q, kp, w.topk_pct, 0.0, over), cache
 
 
 def fp16_timings(wd, wp, dec_state, pre_state, dev, torch, inputgen, kas):
