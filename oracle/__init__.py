@@ -66,6 +66,9 @@ def lib():
         L.orc_prefill_anchor_v.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                            _dbl, _i64, _i64, _i32, _i32, _ip, _dp]
         L.orc_decode_reuse_q.argtypes = L.orc_decode_reuse.argtypes
+        L.orc_decode_refine.argtypes = [_fp, _fp, _fp, _i32, _i32, _i32, _i64, _i32, _dbl,
+                                        _ip, _i32, _i64, _ip, _i64, _ip, _dp]
+        L.orc_decode_refine.restype = ctypes.c_int
         L.orc_prefill_reuse_q.argtypes = L.orc_prefill_reuse.argtypes
         for name in ("orc_decode_reuse_q", "orc_prefill_reuse_q",
                      "orc_dense_attention", "orc_decode_anchor", "orc_decode_reuse",
@@ -164,6 +167,22 @@ def decode_reuse(q, k, v, anchor_idx, head_map, scale: float = 0.0,
     _check(fn(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D, scale, _ptr(anchor_idx, _ip),
               Hkv_a, kk, _ptr(head_map, _ip), _ptr(o, _dp)), "decode_reuse")
     return o
+
+
+def decode_refine(q, k, v, pool_idx, head_map, kappa: int, scale: float = 0.0
+                  ) -> Tuple[np.ndarray, np.ndarray]:
+    """Refined layer of proposal-refined reuse: pool_idx [B, Hkv_p, n_pool] (ascending
+    keys), head_map [Hkv] -> (idx int32 [B, Hkv, kappa], o [B, Hq, D])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    pool_idx, head_map = _i32a(pool_idx), _i32a(head_map)
+    B, Hq, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    idx = np.zeros((B, Hkv, kappa), dtype=np.int32)
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    _check(lib().orc_decode_refine(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), B, Hq, Hkv, N, D, scale,
+                                   _ptr(pool_idx, _ip), pool_idx.shape[1], pool_idx.shape[2],
+                                   _ptr(head_map, _ip), kappa, _ptr(idx, _ip), _ptr(o, _dp)), "decode_refine")
+    return idx, o
 
 
 def prefill_anchor(q_rows, k, v, pct: int, tile: int = 32, t0: int = 0, t1: Optional[int] = None,

@@ -639,3 +639,83 @@ int orc_prefill_reuse(const float *q, const float *k, const float *v,
     free(qmap);
     return st;
 }
+
+/* ------------------------------------------------------------------ */
+/* proposal-refined reuse (decode)                                     */
+/* ------------------------------------------------------------------ */
+
+/* Refined layer of proposal-refined reuse (the Prism Attention page,
+ * thelatestinai.com/papers/2610.22985: a proposal layer exports a pool of
+ * rho * kappa candidate keys; each refined layer selects its own kappa keys
+ * within the pool). Reading taken here: KV head g's pool is
+ * pool_idx[b, head_map[g], :] (n_pool keys, ascending); each query head of
+ * the group gets its softmax over the pool's keys with this layer's q and K;
+ * the probabilities are summed over the group; the exact Top-kappa within the
+ * pool (ties to the lower key) is the refined set, written to idx_out[b, g, :]
+ * ascending; each head attends over it. pool_idx [B, Hkv_p, n_pool];
+ * idx_out [B, Hkv, kappa]; o_out [B, Hq, D]. */
+int orc_decode_refine(const float *q, const float *k, const float *v,
+                      int B, int Hq, int Hkv, int64_t N, int D, double scale,
+                      const int32_t *pool_idx, int Hkv_p, int64_t n_pool,
+                      const int32_t *head_map, int64_t kappa, int32_t *idx_out, double *o_out)
+{
+    if (check_shape(B, Hq, Hkv, N, D) || Hkv_p <= 0 || n_pool <= 0 || kappa <= 0 || kappa > n_pool)
+        return ORC_BAD_ARG;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int g = 0; g < Hkv; ++g)
+        if (head_map[g] < 0 || head_map[g] >= Hkv_p) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < (int64_t)B * Hkv_p * n_pool; ++i)
+        if (pool_idx[i] < 0 || pool_idx[i] >= N) return ORC_BAD_INDEX;
+    const int G = Hq / Hkv;
+    int status = ORC_OK;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)G * n_pool * sizeof(double));
+        double *P = (double *)malloc((size_t)n_pool * sizeof(double));
+        int32_t *pos = (int32_t *)malloc((size_t)kappa * sizeof(int32_t));
+        double *sel = (double *)malloc((size_t)kappa * sizeof(double));
+        int64_t *keys = (int64_t *)malloc((size_t)kappa * sizeof(int64_t));
+        if (!s || !P || !pos || !sel || !keys) {
+#pragma omp atomic write
+            status = ORC_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic)
+            for (int64_t u = 0; u < (int64_t)B * Hkv; ++u) {
+                int64_t b = u / Hkv, g = u % Hkv;
+                const int32_t *pool = pool_idx + (b * Hkv_p + head_map[g]) * n_pool;
+                const float *kb = k + (b * Hkv + g) * N * D;
+                const float *vb = v + (b * Hkv + g) * N * D;
+                /* 1. each head's softmax over the pool's keys */
+                for (int64_t a = 0; a < n_pool; ++a) P[a] = 0.0;
+                for (int r = 0; r < G; ++r) {
+                    const float *qh = q + (b * Hq + g * G + r) * D;
+                    double m = -INFINITY;
+                    for (int64_t a = 0; a < n_pool; ++a) {
+                        s[r * n_pool + a] = dot_scaled(qh, kb + (int64_t)pool[a] * D, D, scale);
+                        if (s[r * n_pool + a] > m) m = s[r * n_pool + a];
+                    }
+                    double l = 0.0;
+                    for (int64_t a = 0; a < n_pool; ++a) l += exp(s[r * n_pool + a] - m);
+                    /* 2. summed over the group's heads */
+                    for (int64_t a = 0; a < n_pool; ++a) P[a] += exp(s[r * n_pool + a] - m) / l;
+                }
+                /* 3. exact Top-kappa within the pool: positions in the pool are
+                 *    in key order, so the lower position is the lower key */
+                if (select_topk(P, n_pool, kappa, pos) != ORC_OK) {
+#pragma omp atomic write
+                    status = ORC_NOMEM;
+                    continue;
+                }
+                int32_t *S = idx_out + u * kappa;
+                for (int64_t a = 0; a < kappa; ++a) { S[a] = pool[pos[a]]; keys[a] = S[a]; }
+                /* 4. attention over the refined set, per head */
+                for (int r = 0; r < G; ++r) {
+                    for (int64_t a = 0; a < kappa; ++a) sel[a] = s[r * n_pool + pos[a]];
+                    weighted_rows(sel, keys, kappa, vb, D, o_out + (b * Hq + g * G + r) * D);
+                }
+            }
+        }
+        free(s); free(P); free(pos); free(sel); free(keys);
+    }
+    return status;
+}

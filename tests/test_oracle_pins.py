@@ -540,3 +540,59 @@ def test_query_head_map_reduces_to_kv_head_map():
     for h in range(8):
         ref = oracle.decode_reuse(q, k, v, idx, np.full(2, qm[h], np.int32))
         np.testing.assert_array_equal(c[:, h], ref[:, h])
+
+
+# ---------------------------------------------------------------- proposal-refined reuse
+
+def test_refine_worked_example():
+    """Pool {0, 1, 2} of 4 keys; key 3 (outside the pool) has a huge logit for
+    head A, which must not enter the pool's softmax. Within the pool the heads'
+    probabilities are A = [0.6, 0.35, 0.05], B = [~0, 0.45, 0.55]; summed,
+    key 1 wins (kappa 1) and both heads then attend over key 1 alone."""
+    pa, pb = _two_head_logits()
+    D = 4
+    k = np.zeros((1, 1, 4, D), np.float32)
+    k[0, 0, :3, :3] = np.eye(3)
+    k[0, 0, 3, 3] = 1.0
+    q = np.zeros((1, 2, D), np.float32)
+    q[0, 0, :3], q[0, 1, :3] = 2 * pa, 2 * pb          # scale 1/sqrt(4)
+    q[0, 0, 3] = 60.0                                   # head A: key 3 dominates the full row
+    v = np.arange(4 * D, dtype=np.float32).reshape(1, 1, 4, D)
+    idx, o = oracle.decode_refine(q, k, v, np.array([[[0, 1, 2]]], np.int32), np.zeros(1, np.int32), 1)
+    assert idx.tolist() == [[[1]]]
+    np.testing.assert_allclose(o[0], np.repeat(v[0, 0, 1][None], 2, 0), rtol=0, atol=1e-12)
+
+
+def test_refine_reduces_to_reuse_and_anchor():
+    q, k, v = _decode_case(B=2, Hq=8, Hkv=2, N=300, seed=12)
+    N = 300
+    pool, _, _ = oracle.decode_anchor(q, k, v, pct=40)
+    hm = np.array([1, 0], np.int32)
+    n_pool = pool.shape[-1]
+    # kappa = whole pool: the refined set is the pool, the output a reuse over it
+    idx, o = oracle.decode_refine(q, k, v, pool, hm, n_pool)
+    assert np.array_equal(idx, pool[:, hm])
+    np.testing.assert_array_equal(o, oracle.decode_reuse(q, k, v, pool, hm))
+    # pool = every key: the refined set is this layer's own anchor selection
+    every = np.broadcast_to(np.arange(N, dtype=np.int32), (2, 2, N)).copy()
+    kk = oracle.decode_k(N, 10)
+    idx, o = oracle.decode_refine(q, k, v, every, np.arange(2, dtype=np.int32), kk)
+    aidx, ao, _ = oracle.decode_anchor(q, k, v, pct=10)
+    assert np.array_equal(idx, aidx)
+    np.testing.assert_allclose(o, ao, rtol=0, atol=1e-14)
+
+
+def test_refine_brute_force_tiny():
+    for seed, (Hq, Hkv, N, pct_pool, kappa) in enumerate([(4, 2, 60, 50, 7), (8, 2, 97, 30, 5), (2, 1, 40, 75, 11)]):
+        q, k, v = _decode_case(B=1, Hq=Hq, Hkv=Hkv, N=N, seed=seed + 31)
+        G = Hq // Hkv
+        pool, _, _ = oracle.decode_anchor(q, k, v, pct=pct_pool)
+        hm = np.random.default_rng(seed).integers(0, Hkv, Hkv).astype(np.int32)
+        idx, _ = oracle.decode_refine(q, k, v, pool, hm, kappa)
+        qt, kt = torch.from_numpy(q).double(), torch.from_numpy(k).double()
+        for g in range(Hkv):
+            keys = pool[0, hm[g]]
+            s = qt[0, g * G:(g + 1) * G] @ kt[0, g, keys].T / math.sqrt(q.shape[-1])
+            P = torch.softmax(s, -1).sum(0).numpy()
+            order = sorted(range(len(keys)), key=lambda a: (-np.float32(P[a]), a))
+            assert idx[0, g].tolist() == sorted(keys[order[:kappa]].tolist()), (seed, g)
