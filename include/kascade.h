@@ -231,6 +231,26 @@ kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
                                  const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Refined layer of proposal-refined reuse (decode). The Prism Attention page
+ * (thelatestinai.com/papers/2610.22985, "Proposal-Refined" sharing) has a
+ * proposal layer export a pool of rho * kappa candidate keys and every
+ * refined layer select its own kappa keys within that pool; here the pool is
+ * an anchor call's index set at a larger percentage (rho times the layer's)
+ * and kappa is this layer's own max(1, kas_topk_count(N, pct)). For each
+ * (b, KV head g): pool = pool_idx[b, head_map[g], :pool_size] (ascending
+ * keys); each query head's softmax over the pool's keys with this layer's
+ * q and K, summed over the group's heads; the exact Top-kappa within the pool
+ * (ties to the lower key) written to idx_out[b, g, :kappa] ascending; each
+ * head attends over it. pool_idx [B, pool_kv_heads, pool_size], kappa <=
+ * pool_size <= N; head_map as in kas_decode_reuse (values in [0,
+ * pool_kv_heads)); idx_out [B, Hkv, kappa]; o [B, Hq, D]. pool_scope,
+ * pool_op and query_head_map must be 0. */
+kas_status_t kas_workspace_size_refine(const kas_desc_t* desc, int64_t pool_size, size_t* bytes);
+kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                               const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
+                               const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
+                               size_t ws_bytes, void* stream);
+
 const char* kas_status_string(kas_status_t status);
 /* Text of the last failure on the calling thread ("" if none). */
 const char* kas_last_error(void);

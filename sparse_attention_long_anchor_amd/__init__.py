@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     decode_anchor,
     decode_dense,
     decode_k,
+    decode_refine,
     decode_reuse,
     lib_path,
     make_desc,

@@ -92,6 +92,9 @@ def _load():
         L.kas_decode_anchor_kv.argtypes = [dp, cp, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_reuse_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_dense_kv.argtypes = [dp, cp, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_workspace_size_refine.argtypes = [dp, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+        L.kas_decode_refine.argtypes = [dp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
+                                        ctypes.c_size_t, P]
         L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_status_string.argtypes = [st]
         L.kas_status_string.restype = ctypes.c_char_p
@@ -104,6 +107,7 @@ def _load():
                   "kas_decode_reuse", "kas_prefill_anchor", "kas_prefill_reuse",
                   "kas_decode_dense", "kas_prefill_dense", "kas_workspace_size_kv",
                   "kas_decode_anchor_kv", "kas_decode_reuse_kv", "kas_decode_dense_kv",
+                  "kas_workspace_size_refine", "kas_decode_refine",
                   "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
                   "kas_profile_names"):
             getattr(L, n).restype = st
@@ -344,6 +348,31 @@ def prefill_dense(q, k, v, scale: float = 0.0, o=None) -> torch.Tensor:
     _check(_load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0,
                                      _stream(q)), "prefill_dense")
     return o
+
+
+def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx_out=None, o=None,
+                  ws=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Refined layer of proposal-refined reuse: pool_idx [B, Hkv_p, n_pool] int32 (an anchor
+    set at a larger percentage), head_map [Hkv] or None -> (idx int32 [B, Hkv, kappa],
+    o [B, Hq, D]) with kappa this layer's own k for pct."""
+    desc = _desc_from(q, k, pct, False, scale)
+    if k.stride() != v.stride():
+        raise KasError(1, "decode_refine", "k and v must share strides")
+    n_pool = pool_idx.shape[2]
+    kappa = decode_k(desc.seq_len, pct)
+    if idx_out is None:
+        idx_out = torch.empty((desc.batch, desc.n_kv_heads, kappa), dtype=torch.int32, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    L = _load()
+    if ws is None:
+        n = ctypes.c_size_t(0)
+        _check(L.kas_workspace_size_refine(ctypes.byref(desc), n_pool, ctypes.byref(n)), "workspace_size")
+        ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=q.device)
+    _check(L.kas_decode_refine(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(pool_idx), pool_idx.shape[1],
+                               n_pool, _ptr(head_map), _ptr(idx_out), _ptr(o), _ptr(ws), ws.numel(), _stream(q)),
+           "decode_refine")
+    return idx_out, o
 
 
 def profile_enable(on: bool = True) -> None:

@@ -65,11 +65,13 @@ constexpr float kBigSum = 0x1p64f;   // lazy-reference term that forces the exac
 
 // PG: a paged cache; the chunk's page ids are read into LDS once, and a
 // 16-key block (pages hold a power-of-two multiple of 16 keys) lies in one page.
-template <typename T, int D, int G, bool PG = false>
+// IX: rows are the keys of a pool (a.idx through the head map, a.N = pool
+// size); the chunk's keys are read into LDS once.
+template <typename T, int D, int G, bool PG = false, bool IX = false>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   using QK = QKMfma<T, D>;
   __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ int32_t s_pg[PG ? kScorePages : 1];
+  __shared__ int32_t s_pg[PG ? kScorePages : (IX ? kScoreMaxRows : 1)];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
@@ -88,6 +90,16 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
     for (int i = tid; i < np; i += 256) s_pg[i] = a.block_table[(int64_t)b * a.max_pages + p0 + i];
     __syncthreads();
   }
+  if (IX) {
+    int ga = a.head_map ? a.head_map[g] : g;
+    ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+    const int32_t* pool = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.N + row0;
+    for (int i = tid; i < nrows; i += 256) {
+      const int32_t j = pool[i];
+      s_pg[i] = ((uint32_t)j < (uint64_t)a.n_keys) ? j : 0;     // trusted input, kept in the cache
+    }
+    __syncthreads();
+  }
   typename QK::QFrag qf;
   QK::load_q(qf, (const T*)a.q + ((int64_t)b * a.Hq + g * G + min(c16, G - 1)) * D, c16 < G, q4);
   float* lg = a.logits + (unit * a.N + row0) * G;
@@ -103,7 +115,10 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   // for them).
   auto load = [&](int blk, QK& dst) __attribute__((always_inline)) {
     const int jr = blk * 16 + c16;
-    if (PG) {
+    if (IX) {
+      const int64_t key = s_pg[jr < nrows ? jr : 0];
+      dst.load_k((const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + key * D, q4);
+    } else if (PG) {
       const int64_t j = row0 + (jr < nrows ? jr : 0);
       const int64_t pg = page_id(a, s_pg[(j >> a.page_shift) - p0]);
       dst.load_k((const T*)a.k + pg * a.page_stride + g * a.page_hstride + (j & ((1 << a.page_shift) - 1)) * D, q4);
@@ -1284,6 +1299,29 @@ static hipError_t score_launch_pg(const DecodeArgs& a, dim3 grid, LaunchCtx& st)
   return hipSuccess;
 }
 template <typename T, int D>
+static hipError_t score_launch_ix(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+  switch (a.G) {
+    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1, false, true>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2, false, true>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4, false, true>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8, false, true>), grid, dim3(256), st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_decode_score_pool_rows(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
+  dim3 grid(a.n_score_chunks, a.Hkv, a.B);
+  ctx.begin(K_DEC_SCORE);
+  hipError_t e;
+  if (dtype == 1) e = a.D == 128 ? score_launch_ix<__bf16, 128>(a, grid, ctx) : score_launch_ix<__bf16, 64>(a, grid, ctx);
+  else if (dtype == 2) e = a.D == 128 ? score_launch_ix<_Float16, 128>(a, grid, ctx) : score_launch_ix<_Float16, 64>(a, grid, ctx);
+  else e = a.D == 128 ? score_launch_ix<float, 128>(a, grid, ctx) : score_launch_ix<float, 64>(a, grid, ctx);
+  if (e != hipSuccess) return e;
+  return ctx.end(K_DEC_SCORE);
+}
+
+template <typename T, int D>
 static hipError_t score_launch(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   // paged caches hold 16-bit elements only (checked on the host)
   if (sizeof(T) == 2 && a.block_table) return score_launch_pg<T, D, true>(a, grid, st);
@@ -1479,6 +1517,28 @@ __global__ __launch_bounds__(256) void dec_page_rows_kernel(DecodeArgs a) {
     j = ((uint64_t)j < (uint64_t)n) ? j : 0;            // trusted input, kept in the sequence
     out[i] = (uint32_t)(page_id(a, bt[j >> a.page_shift]) * page_rows + (j & mask));
   }
+}
+
+// Refined layer: the selected positions in each (b, g)'s pool, in ascending
+// order, mapped to the pool's keys (also ascending, so the set stays sorted).
+__global__ __launch_bounds__(256) void dec_pool_keys_kernel(DecodeArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  int ga = a.head_map ? a.head_map[g] : g;
+  ga = ((unsigned)ga < (unsigned)a.Hkv_a) ? ga : 0;
+  const int32_t* pool = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.N;
+  const int32_t* pos = a.pos + ((int64_t)b * a.Hkv + g) * a.kk;
+  int32_t* out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.kk;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.kk; i += (int64_t)gridDim.x * 256) {
+    const int32_t p = pos[i];
+    out[i] = pool[((uint32_t)p < (uint64_t)a.N) ? p : 0];
+  }
+}
+
+hipError_t launch_pool_positions_to_keys(const DecodeArgs& a, LaunchCtx& ctx) {
+  ctx.begin(K_DEC_REFINE_MAP);
+  const int64_t chunks = (a.kk + 255) / 256;
+  KAS_LAUNCH(dec_pool_keys_kernel, dim3((unsigned)(chunks < 16 ? chunks : 16), a.Hkv, a.B), dim3(256), ctx, a);
+  return ctx.end(K_DEC_REFINE_MAP);
 }
 
 hipError_t launch_page_rows(const DecodeArgs& a, int nsets, LaunchCtx& ctx) {

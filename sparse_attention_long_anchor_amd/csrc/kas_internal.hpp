@@ -25,6 +25,7 @@ enum KernelId {
   K_PRE_DENSE,
   K_PRE_POOL_HEADS,
   K_DEC_PAGE_ROWS,
+  K_DEC_REFINE_MAP,
   K_COUNT_
 };
 const char* kernel_name(int id);
@@ -103,6 +104,10 @@ struct DecodeArgs {
   uint32_t* prow;                   // paged: physical rows of the sets this call gathers
   const int32_t* page_src;          // page-row translation: source sets, or null (keys 0..)
   int page_src_sets;                // sets per batch row in page_src
+  // refined layer: scoring over a pool of keys (rows of a.idx through the
+  // head map) instead of the cache; n_keys = rows of the cache
+  int64_t n_keys;
+  const int32_t* pos;               // selected positions in the pool [B, Hkv, kk]
 };
 
 // Decode k of n keys: round-half-up(pct * n / 100) clamped to [1, n].
@@ -124,5 +129,9 @@ hipError_t launch_decode_dense(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
 // a.kk]); set s reads source set head_map[s] (or s, clamped) of a.page_src,
 // or, with a.page_src null, the keys 0 .. seq_len - 1 themselves.
 hipError_t launch_page_rows(const DecodeArgs& a, int nsets, LaunchCtx& ctx);
+// Refined layer: Q.K^T and statistics over the pool rows (a.N = pool size);
+// then the selected pool positions (a.pos) mapped to keys into a.idx_out.
+hipError_t launch_decode_score_pool_rows(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
+hipError_t launch_pool_positions_to_keys(const DecodeArgs& a, LaunchCtx& ctx);
 
 }  // namespace kas

@@ -39,7 +39,7 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 static const char* const kKernelNames[K_COUNT_] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
-    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows"};
+    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows", "decode_refine_map"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
 
@@ -232,15 +232,18 @@ struct DecodePlan {
   int64_t kk;
   int score_rows, n_score_chunks, n_sel_chunks, split_rows, nsplit;
   size_t off_logits, off_stats, off_pooled, off_hist, off_counts, off_selstate, off_cand, off_part_o,
-      off_part_ml, off_prow, total;
+      off_part_ml, off_prow, off_pos, total;
 };
 
 // dense: the split rows cover the whole cache (kk = N) and only the split
 // partials are needed. paged: room for the physical rows of the call's sets
 // (Hkv sets of kk rows per batch row; dense: one set of all N keys).
-static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false, bool paged = false) {
+// kk_fixed > 0: the sets hold that many keys (a refined layer's kappa; s.N is
+// then the pool size) and room for the selected pool positions is added.
+static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false, bool paged = false,
+                              int64_t kk_fixed = 0) {
   DecodePlan p{};
-  p.kk = dense ? s.N : decode_k(s.N, s.pct);
+  p.kk = kk_fixed > 0 ? kk_fixed : (dense ? s.N : decode_k(s.N, s.pct));
   p.score_rows = decode_score_rows();
   p.n_score_chunks = (int)((s.N + p.score_rows - 1) / p.score_rows);
   p.n_sel_chunks = (int)((s.N + kSelChunk - 1) / kSelChunk);
@@ -261,6 +264,7 @@ static DecodePlan plan_decode(const Shape& s, bool anchor, bool dense = false, b
   p.off_part_o = take((size_t)s.B * s.Hq * p.nsplit * s.D * sizeof(float));
   p.off_part_ml = take((size_t)s.B * s.Hq * p.nsplit * 2 * sizeof(float));
   if (paged) p.off_prow = take((size_t)s.B * (dense ? 1 : s.Hkv) * p.kk * sizeof(uint32_t));
+  if (kk_fixed > 0) p.off_pos = take((size_t)s.B * s.Hkv * p.kk * sizeof(int32_t));
   p.total = off;
   return p;
 }
@@ -637,6 +641,73 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e = launch_prefill_dense(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_dense");
+  return KAS_OK;
+}
+
+// Refined layer of proposal-refined reuse: the pool-sized plan (scores,
+// pooled values and selection over the pool; gather splits over kappa).
+static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, DecodePlan& p) {
+  const int64_t kappa = decode_k(s.N, s.pct);
+  if (pool_size < kappa || pool_size > s.N)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "pool_size %lld must lie in [kappa = %lld, seq_len = %lld]",
+                (long long)pool_size, (long long)kappa, (long long)s.N);
+  if (s.scope || s.op || s.qmap)
+    return fail(KAS_ERR_UNSUPPORTED, "refined layers pool by sum per KV head with a KV-head map");
+  sp = s;
+  sp.N = pool_size;
+  p = plan_decode(sp, true, false, false, kappa);
+  return KAS_OK;
+}
+
+kas_status_t kas_workspace_size_refine(const kas_desc_t* desc, int64_t pool_size, size_t* bytes) {
+  if (!bytes) return fail(KAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Shape s, sp;
+  DecodePlan p;
+  kas_status_t st = check_desc(desc, false, s);
+  if (st != KAS_OK) return st;
+  if ((st = refine_plan(s, pool_size, sp, p))) return st;
+  *bytes = p.total;
+  return KAS_OK;
+}
+
+kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                               const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
+                               const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Shape s, sp;
+  DecodePlan p;
+  kas_status_t st = check_desc(desc, false, s);
+  if (st != KAS_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!pool_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "pool_idx is NULL");
+  if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
+  if (pool_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "pool_kv_heads must be >= 1");
+  if (!head_map && pool_kv_heads != s.Hkv && pool_kv_heads != 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT,
+                "without a head map, pool_kv_heads must be n_kv_heads (identity) or 1 (shared pool)");
+  if ((st = refine_plan(s, pool_size, sp, p))) return st;
+  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  // scoring, pooling and selection over the pool's keys: positions in the pool
+  DecodeArgs a;
+  fill_decode_args(sp, p, true, (char*)ws, a);
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = pool_idx; a.Hkv_a = pool_kv_heads; a.head_map = head_map; a.n_keys = s.N;
+  a.idx_out = (int32_t*)((char*)ws + p.off_pos);
+  LaunchCtx ctx{(hipStream_t)stream};
+  hipError_t e;
+  if ((e = launch_decode_score_pool_rows(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
+  if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
+  if ((e = launch_decode_select(a, ctx)) != hipSuccess) return hip_fail(e, "decode_select");
+  // positions -> keys, then attention over the refined keys of the cache
+  a.pos = a.idx_out;
+  a.idx_out = idx_out;
+  if ((e = launch_pool_positions_to_keys(a, ctx)) != hipSuccess) return hip_fail(e, "decode_refine_map");
+  DecodeArgs ga = a;
+  ga.N = s.N;
+  ga.idx = idx_out; ga.Hkv_a = s.Hkv; ga.head_map = nullptr;
+  if ((e = launch_decode_attn(ga, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
   return KAS_OK;
 }
 

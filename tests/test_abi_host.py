@@ -189,3 +189,22 @@ def test_kv_cache_layout_checks_without_gpu():
     r = L.kas_decode_anchor_kv(ctypes.byref(d), ctypes.byref(bad[0][0]), fake, fake, fake, fake, fake, fake,
                                1 << 30, None)
     assert r == 1 and b"power of two" in L.kas_last_error()
+
+
+def test_refine_checks_without_gpu():
+    import torch
+    b = _kas()
+    L = b._load()
+    fake = ctypes.c_void_p(1 << 20)
+    d = b.make_desc(2, 8, 2, 128, 4096, 10, torch.bfloat16)
+    n = ctypes.c_size_t(0)
+    kappa = b.decode_k(4096, 10)
+    assert L.kas_workspace_size_refine(ctypes.byref(d), 4 * kappa, ctypes.byref(n)) == 0
+    assert n.value > b.workspace_size(d, b.OP_DECODE_REUSE)
+    assert L.kas_workspace_size_refine(ctypes.byref(d), kappa - 1, ctypes.byref(n)) == 1   # pool < kappa
+    assert L.kas_workspace_size_refine(ctypes.byref(d), 4097, ctypes.byref(n)) == 1        # pool > N
+    dv = b.make_desc(2, 8, 2, 128, 4096, 10, torch.bfloat16, pool_op=1)
+    assert L.kas_workspace_size_refine(ctypes.byref(dv), 4 * kappa, ctypes.byref(n)) == 2
+    r = L.kas_decode_refine(ctypes.byref(d), fake, fake, fake, None, 2, 4 * kappa, None, fake, fake, fake,
+                            1 << 30, None)
+    assert r == 1 and b"pool_idx" in L.kas_last_error()

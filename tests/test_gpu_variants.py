@@ -267,3 +267,74 @@ def test_reuse_query_head_map_full_size():
         worst = max(worst, max_abs(_np(o[:, :, 32 * t: 32 * t + 32]), ref))
     _say(f"[prefill reuse, map per query head] {wp.name}: tiles (1, 500, 1023) max|o-o_oracle|={worst:.3g}")
     assert worst <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- proposal-refined reuse
+
+REFINE = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, pool pct)
+    ("bf16_d128_g4_ragged", 2, 32, 8, 128, 5037, "bf16", 10, 40),
+    ("f32_d64_g4", 1, 8, 2, 64, 2048, "f32", 10, 40),
+    ("f16_d128_g8", 1, 16, 2, 128, 4099, "f16", 10, 20),
+    ("bf16_d64_g1_small", 2, 4, 4, 64, 300, "bf16", 5, 100),
+]
+
+
+def _check_refine(w, q2, k2, v2, pool, hm, pct, label):
+    kas = _kas()
+    idx, o = kas.decode_refine(q2, k2, v2, pool, torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    qn, kn, vn = _np(q2), _np(k2), _np(v2)
+    pn = pool.cpu().numpy()
+    kappa = oracle.decode_k(w.seq_len, pct)
+    oidx, oo = oracle.decode_refine(qn, kn, vn, pn, hm, kappa)
+    gi = idx.cpu().numpy()
+    G = w.n_q_heads // w.n_kv_heads
+    swaps = 0
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            if np.array_equal(gi[b, g], oidx[b, g]):
+                continue
+            # near ties: the pool-restricted pooled scores (float64, torch), indexed by key
+            keys = pn[b, hm[g]]
+            s = torch.from_numpy(qn[b, g * G:(g + 1) * G]).double() @ torch.from_numpy(kn[b, g, keys]).double().T
+            P = torch.softmax(s / np.sqrt(w.head_dim), -1).sum(0).numpy()
+            full = np.zeros(w.seq_len)
+            full[keys] = P
+            swaps += assert_index_set(gi[b, g], oidx[b, g], full, kappa, where=f"{label} b{b} g{g}")
+    o_same = oracle.decode_reuse(qn, kn, vn, gi, np.arange(w.n_kv_heads, dtype=np.int32))
+    err_same, err = max_abs(_np(o), o_same), max_abs(_np(o), oo)
+    _say(f"[decode refine] {label}: pool {pn.shape[-1]} -> kappa {kappa}, near-tie swaps={swaps} "
+         f"max|o-o_oracle(same set)|={err_same:.3g} max|o-o_oracle|={err:.3g}")
+    assert err_same <= TOL[w.dtype] and err <= TOL[w.dtype]
+    return idx, o
+
+
+@pytest.mark.parametrize("case", REFINE, ids=[c[0] for c in REFINE])
+def test_decode_refine(case):
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct, ppct = case
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    pool, _ = kas.decode_anchor(q, k, v, ppct)                      # the proposal layer
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(6).integers(0, Hkv, Hkv).astype(np.int32)
+    idx, o = _check_refine(w, q2, k2, v2, pool, hm, pct, label)
+    if ppct == 100:
+        # the pool is every key: the refined layer selects what an anchor on it selects
+        aidx, _ = kas.decode_anchor(q2, k2, v2, pct)
+        ident = np.arange(Hkv, dtype=np.int32)
+        idx2, _ = kas.decode_refine(q2, k2, v2, pool, torch.as_tensor(ident, device=DEV), pct)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, aidx)
+
+
+def test_decode_refine_full_size():
+    kas = _kas()
+    w = inputgen.WORKLOADS["llama8b_decode_128k"]
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    pool, _ = kas.decode_anchor(q, k, v, 4 * w.topk_pct)
+    del q, k, v
+    q, k, v = inputgen.layer_inputs(w, 1, DEV, pos)
+    _check_refine(w, q, k, v, pool, inputgen.head_maps(w)[1], w.topk_pct, w.name)
