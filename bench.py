@@ -490,6 +490,20 @@ def variant_timings(wd, dec_state, wp, pre_state, out, torch, kas, dev, inputgen
         _, t_q = _alternate(torch, anchor, lambda: kas.decode_reuse(q1, k1, v1, idx, qm, wd.topk_pct, o=o, ws=ws_q,
                                                                     query_head_map=True), 7)
         res["decode_reuse_us"] = {"map_per_kv_head": round(1e3 * t_kv, 3), "map_per_query_head": round(1e3 * t_q, 3)}
+        # proposal-refined reuse: a proposal anchor at 4x the percentage, the
+        # refined layer selecting its own k within that pool
+        rho = 4
+        pool = torch.empty((wd.batch, wd.n_kv_heads, kas.decode_k(wd.seq_len, rho * wd.topk_pct)), dtype=torch.int32,
+                           device=dev)
+        d_p = kas.make_desc(wd.batch, wd.n_q_heads, wd.n_kv_heads, wd.head_dim, wd.seq_len, rho * wd.topk_pct,
+                            wd.torch_dtype)
+        ws_p = torch.empty(kas.workspace_size(d_p, kas.OP_DECODE_ANCHOR), dtype=torch.uint8, device=dev)
+        ridx = torch.empty((wd.batch, wd.n_kv_heads, kd), dtype=torch.int32, device=dev)
+        t_pa, t_rf = _alternate(torch, lambda: kas.decode_anchor(q, k, v, rho * wd.topk_pct, idx_out=pool, o=o, ws=ws_p),
+                                lambda: kas.decode_refine(q1, k1, v1, pool, hm, wd.topk_pct, idx_out=ridx, o=o), 7)
+        res["decode_proposal_refined_us"] = {"rho": rho, "proposal_anchor": round(1e3 * t_pa, 3),
+                                             "refined_layer": round(1e3 * t_rf, 3)}
+        del pool, ws_p, ridx
         if "decode" in out:
             res["decode_every_layer_anchor_ms_per_step"] = {
                 "value": round(wd.n_layers * out["decode"]["us_per_layer"]["anchor"] / 1e3, 4),
