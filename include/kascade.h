@@ -205,7 +205,8 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
  *     pools, [num_pages, Hkv, P, D] with the default strides; desc's
  *     kv_*_stride are not used. Paged caches hold bf16 or fp16.
  * KAS_ERR_UNSUPPORTED: a paged fp32 cache, or a pool of 2^31 rows or more
- * (num_pages * page_stride / head_dim). */
+ * (num_pages * page_stride / head_dim). The prefill *_kv calls take seq_lens
+ * only (see below). */
 typedef struct kas_kv_cache {
   const int32_t* seq_lens;
   const int32_t* block_table;
@@ -230,6 +231,23 @@ kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
 kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
                                  const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* The prefill calls over sequences of different lengths: cache->seq_lens
+ * (device [B]) gives each prompt's length, taken in whole tiles of 32 rows
+ * (clamped to [32, desc->seq_len]); tiles past a prompt are not computed and
+ * their rows of o and their index sets are left unspecified. The CSR layout
+ * is that of desc->seq_len (a tile's set size depends only on the tile).
+ * block_table must be NULL (KAS_ERR_UNSUPPORTED). */
+kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                   const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
+                                   size_t ws_bytes, void* stream);
+kas_status_t kas_prefill_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, const int32_t* anchor_idx,
+                                  int32_t anchor_kv_heads, const int32_t* head_map, void* o, void* ws,
+                                  size_t ws_bytes, void* stream);
+kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Refined layer of proposal-refined reuse (decode). The Prism Attention page
  * (thelatestinai.com/papers/2610.22985, "Proposal-Refined" sharing) has a

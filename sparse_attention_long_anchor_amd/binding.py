@@ -92,6 +92,9 @@ def _load():
         L.kas_decode_anchor_kv.argtypes = [dp, cp, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_reuse_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_dense_kv.argtypes = [dp, cp, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_anchor_kv.argtypes = [dp, cp, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_reuse_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
+        L.kas_prefill_dense_kv.argtypes = [dp, cp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_workspace_size_refine.argtypes = [dp, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
         L.kas_decode_refine.argtypes = [dp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
                                         ctypes.c_size_t, P]
@@ -107,7 +110,8 @@ def _load():
                   "kas_decode_reuse", "kas_prefill_anchor", "kas_prefill_reuse",
                   "kas_decode_dense", "kas_prefill_dense", "kas_workspace_size_kv",
                   "kas_decode_anchor_kv", "kas_decode_reuse_kv", "kas_decode_dense_kv",
-                  "kas_workspace_size_refine", "kas_decode_refine",
+                  "kas_workspace_size_refine", "kas_decode_refine", "kas_prefill_anchor_kv",
+                  "kas_prefill_reuse_kv", "kas_prefill_dense_kv",
                   "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
                   "kas_profile_names"):
             getattr(L, n).restype = st
@@ -282,8 +286,12 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
     return o
 
 
+def _lens_cache(seq_lens):
+    return None if seq_lens is None else KasKvCache(seq_lens.data_ptr(), None, 0, 0, 0, 0, 0)
+
+
 def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
-                   pool_scope: int = 0, pool_op: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                   pool_scope: int = 0, pool_op: int = 0, seq_lens=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> (idx int32 [B,Hs,total] CSR, o [B,Hq,N,D]);
     Hs as in decode_anchor."""
     desc = _desc_from(q, k, pct, True, scale, pool_scope=pool_scope, pool_op=pool_op)
@@ -297,13 +305,19 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
     if o is None:
         o = torch.empty_like(q)
     ws = _ws(desc, OP_PREFILL_ANCHOR, ws, q.device)
-    _check(_load().kas_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
-                                      _ptr(o), _ptr(ws), ws.numel(), _stream(q)), "prefill_anchor")
+    c = _lens_cache(seq_lens)
+    if c is None:
+        rc = _load().kas_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
+                                        _ptr(o), _ptr(ws), ws.numel(), _stream(q))
+    else:
+        rc = _load().kas_prefill_anchor_kv(ctypes.byref(desc), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(idx_out), _ptr(o), _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "prefill_anchor")
     return idx_out, o
 
 
 def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
-                  query_head_map: bool = False) -> torch.Tensor:
+                  query_head_map: bool = False, seq_lens=None) -> torch.Tensor:
     """head_map as in decode_reuse."""
     desc = _desc_from(q, k, pct, True, scale, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
@@ -311,9 +325,16 @@ def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o
     if o is None:
         o = torch.empty_like(q)
     ws = _ws(desc, OP_PREFILL_REUSE, ws, q.device)
-    _check(_load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
-                                     anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws),
-                                     ws.numel(), _stream(q)), "prefill_reuse")
+    c = _lens_cache(seq_lens)
+    if c is None:
+        rc = _load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
+                                       anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws), ws.numel(),
+                                       _stream(q))
+    else:
+        rc = _load().kas_prefill_reuse_kv(ctypes.byref(desc), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(anchor_idx), anchor_idx.shape[1], _ptr(head_map), _ptr(o),
+                                          _ptr(ws), ws.numel(), _stream(q))
+    _check(rc, "prefill_reuse")
     return o
 
 
@@ -338,15 +359,20 @@ def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None, seq_lens=None, bl
     return o
 
 
-def prefill_dense(q, k, v, scale: float = 0.0, o=None) -> torch.Tensor:
+def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None) -> torch.Tensor:
     """Dense causal attention: q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> o [B,Hq,N,D]."""
     desc = _desc_from(q, k, 100, True, scale)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_dense", "k and v must share strides")
     if o is None:
         o = torch.empty_like(q)
-    _check(_load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0,
-                                     _stream(q)), "prefill_dense")
+    c = _lens_cache(seq_lens)
+    if c is None:
+        rc = _load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0, _stream(q))
+    else:
+        rc = _load().kas_prefill_dense_kv(ctypes.byref(desc), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          None, 0, _stream(q))
+    _check(rc, "prefill_dense")
     return o
 
 

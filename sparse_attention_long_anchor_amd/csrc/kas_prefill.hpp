@@ -38,6 +38,7 @@ struct PrefillArgs {
   int pool_op, pool_all, Hsel;
   int dtype;                        // element type of q, k, v, o: 1 bf16, 2 fp16
   int kvdiv;                        // reuse per query head: Hkv = Hq, G = 1, KV head = head / kvdiv
+  const int32_t* seq_lens;          // [B] prompt length of sequence b (tiles past it are skipped), or null
 };
 
 size_t prefill_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t N, int pct, bool anchor);

@@ -423,7 +423,7 @@ kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t*
   kas_status_t st = check_desc(desc, prefill, s);
   if (st != KAS_OK) return st;
   CacheView cv;
-  if (cache && prefill) return fail(KAS_ERR_UNSUPPORTED, "varlen / paged caches are decode only");
+  if (cache && prefill && cache->block_table) return fail(KAS_ERR_UNSUPPORTED, "paged caches are decode only");
   if ((st = check_cache(cache, s, cv))) return st;
   if (op == KAS_OP_PREFILL_DENSE) {
     *bytes = 0;
@@ -527,11 +527,29 @@ kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
   return KAS_OK;
 }
 
+// Prefill calls over sequences of different lengths take only seq_lens of a
+// kas_kv_cache_t (prefill caches are contiguous).
+static kas_status_t prefill_lens(const kas_kv_cache_t* cache, const int32_t** lens) {
+  *lens = nullptr;
+  if (!cache) return KAS_OK;
+  if (cache->block_table) return fail(KAS_ERR_UNSUPPORTED, "paged caches are decode only");
+  *lens = cache->seq_lens;
+  return KAS_OK;
+}
+
 kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                 int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return kas_prefill_anchor_kv(desc, nullptr, q, k, v, idx_out, o, ws, ws_bytes, stream);
+}
+
+kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                   const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
+                                   size_t ws_bytes, void* stream) {
   Shape s;
+  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
+  if ((st = prefill_lens(cache, &lens))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -547,6 +565,7 @@ kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const voi
   a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
   a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
   a.idx = idx_out; a.Hkv_a = a.Hsel; a.head_map = nullptr; a.total = total;
+  a.seq_lens = lens;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e = launch_prefill_anchor(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_anchor");
@@ -557,9 +576,19 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
                                const int32_t* anchor_idx, int32_t anchor_kv_heads,
                                const int32_t* head_map, void* o, void* ws, size_t ws_bytes,
                                void* stream) {
+  return kas_prefill_reuse_kv(desc, nullptr, q, k, v, anchor_idx, anchor_kv_heads, head_map, o, ws, ws_bytes,
+                              stream);
+}
+
+kas_status_t kas_prefill_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, const int32_t* anchor_idx,
+                                  int32_t anchor_kv_heads, const int32_t* head_map, void* o, void* ws,
+                                  size_t ws_bytes, void* stream) {
   Shape s;
+  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
+  if ((st = prefill_lens(cache, &lens))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -579,6 +608,7 @@ kas_status_t kas_prefill_reuse(const kas_desc_t* desc, const void* q, const void
   fill_prefill_args(a, sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, sr.scale, sr.kv_bs, sr.kv_hs, (char*)ws, false);
   a.dtype = s.dtype;
   a.kvdiv = s.qmap ? s.G : 1;
+  a.seq_lens = lens;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map; a.total = total;
   LaunchCtx ctx{(hipStream_t)stream};
@@ -625,10 +655,18 @@ kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
 
 kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v, void* o,
                                void* ws, size_t ws_bytes, void* stream) {
+  return kas_prefill_dense_kv(desc, nullptr, q, k, v, o, ws, ws_bytes, stream);
+}
+
+kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                                  void* stream) {
   (void)ws; (void)ws_bytes;
   Shape s;
+  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
+  if ((st = prefill_lens(cache, &lens))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -638,6 +676,7 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
   a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.offsets = nullptr; a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = 0;
+  a.seq_lens = lens;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e = launch_prefill_dense(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_dense");

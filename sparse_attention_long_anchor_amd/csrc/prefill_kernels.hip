@@ -33,6 +33,16 @@ namespace kas {
 // buffer is only as large as the prompt needs.
 constexpr int kPoolBudgetMBDefault = 16384;
 
+// Tiles of sequence b: all T, or its own length's (a trusted input, clamped
+// to [1 tile, N] and taken in whole tiles). Tiles past it are not computed:
+// causality keeps every earlier tile's work inside the sequence.
+__device__ __forceinline__ int tiles_of(const PrefillArgs& a, int b) {
+  if (!a.seq_lens) return a.T;
+  int64_t n = a.seq_lens[b];
+  n = n < kTile ? kTile : (n > a.N ? a.N : n);
+  return (int)(n / kTile);
+}
+
 // Row (query or key) of the 32x32 MFMA output held by lane half hh in reg r.
 __device__ __forceinline__ int mrow(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
@@ -183,7 +193,9 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   const int npairs = (a.T + 1) / 2;
   const int p = npairs - 1 - xcd_local_order(blockIdx.x, npairs);
   const int t0 = 2 * p, t1 = 2 * p + 1;
-  const bool has1 = t1 < a.T;
+  const int Tb = tiles_of(a, blockIdx.z);
+  if (t0 >= Tb) return;                           // past the sequence (whole workgroup)
+  const bool has1 = t1 < Tb;
   const int tl = has1 ? t1 : t0;
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -395,7 +407,9 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   const int npairs = (a.t_end + 1) / 2 - pa0;
   const int p = pa0 + npairs - 1 - xcd_local_order(blockIdx.x, npairs);
   const int t0 = 2 * p, t1 = 2 * p + 1;
-  const bool has1 = t1 < a.T;
+  const int Tb = tiles_of(a, blockIdx.z);
+  if (t0 >= Tb) return;                           // past the sequence (whole workgroup)
+  const bool has1 = t1 < Tb;
   const int nkb = has1 ? t1 : t0;              // key blocks before the later tile
   if (nkb == 0) return;
   const int g = blockIdx.y, b = blockIdx.z;
@@ -564,7 +578,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 template <int OP>
 __global__ __launch_bounds__(256) void pre_pool_heads_kernel(PrefillArgs a) {
   const int t = a.t_begin + blockIdx.x, b = blockIdx.y;
-  if (t < 1) return;
+  if (t < 1 || t >= tiles_of(a, b)) return;
   const int n4 = kTile * t / 4;
   f32x4* dst = reinterpret_cast<f32x4*>(a.pooled + pool_slot(a, b, 0, t));
   for (int i = threadIdx.x; i < n4; i += 256) {
@@ -599,7 +613,7 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   __shared__ uint32_t s_nc;
   const int t = a.t_end - 1 - xcd_local_order(blockIdx.x, a.t_end - a.t_begin);
   const int g = blockIdx.y, b = blockIdx.z;
-  if (t < 1) return;
+  if (t < 1 || t >= tiles_of(a, b)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = kTile * t;
   const int o0 = a.offsets[t];
@@ -783,6 +797,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
 
   const int t = a.T - 1 - xcd_local_order(blockIdx.x, a.T);
   const int g = blockIdx.y, b = blockIdx.z;
+  if (t >= tiles_of(a, b)) return;                          // past the sequence (whole workgroup)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS line bases stay scalar
   const int n32 = lane & 31, hh = lane >> 5;

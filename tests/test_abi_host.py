@@ -185,7 +185,8 @@ def test_kv_cache_layout_checks_without_gpu():
     df = b.make_desc(2, 8, 2, 64, 2048, 10, torch.float32)
     assert ws(paged, desc=df) == 2 and b"bf16 or fp16" in L.kas_last_error()
     dp = b.make_desc(1, 8, 2, 128, 256, 10, torch.bfloat16)
-    assert ws(varlen, b.OP_PREFILL_ANCHOR, dp) == 2                      # decode only
+    assert ws(varlen, b.OP_PREFILL_ANCHOR, dp) == 0                      # prefill takes lengths
+    assert ws(paged, b.OP_PREFILL_ANCHOR, dp) == 2                       # but no pages
     r = L.kas_decode_anchor_kv(ctypes.byref(d), ctypes.byref(bad[0][0]), fake, fake, fake, fake, fake, fake,
                                1 << 30, None)
     assert r == 1 and b"power of two" in L.kas_last_error()

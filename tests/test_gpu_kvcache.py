@@ -159,3 +159,71 @@ def test_decode_varlen_paged_full_size():
     q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
     lens = np.array([131072, 100000, 65536, 4097], np.int32)
     _check_varlen(w, q, k, v, lens, w.topk_pct, w.name, P=256)
+
+
+# ---------------------------------------------------------------- varlen prefill
+
+def _check_prefill_varlen(w, q, k, v, lens, pct, label, tiles=None):
+    kas = _kas()
+    B, Hkv = w.batch, w.n_kv_heads
+    tl = torch.as_tensor(lens, device=DEV)
+    _say(f"[prefill varlen] {label}: lens={lens.tolist()} pct={pct}")
+    idx, o = kas.prefill_anchor(q, k, v, pct, seq_lens=tl)
+    hm = np.random.default_rng(2).integers(0, Hkv, Hkv).astype(np.int32)
+    q2 = torch.flip(q, dims=[1]).contiguous()
+    o_r = kas.prefill_reuse(q2, k, v, idx, torch.as_tensor(hm, device=DEV), pct, seq_lens=tl)
+    o_d = kas.prefill_dense(q, k, v, seq_lens=tl)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    tol = TOL[w.dtype]
+    worst = [0.0, 0.0, 0.0]
+    swaps = 0
+    for b in range(B):
+        n = int(lens[b])
+        T = n // 32
+        off = oracle.prefill_offsets(n, 32, pct)
+        kb, vb = _np(k[b:b + 1, :, :n]), _np(v[b:b + 1, :, :n])
+        for t in (range(T) if tiles is None else [x for x in tiles if x < T]):
+            qr = _np(q[b:b + 1, :, 32 * t: 32 * t + 32])
+            oidx, oo = oracle.prefill_anchor(qr, kb, vb, pct, t0=t, t1=t + 1)
+            for g in range(Hkv):
+                gs = gi[b, g, off[t]:off[t + 1]]
+                if not np.array_equal(gs, oidx[0, g]):
+                    P = oracle.prefill_pooled(qr, kb, 0, t, g, t0=t, t1=t + 1)[: 32 * t]
+                    swaps += assert_index_set(gs, oidx[0, g], P, int(off[t + 1] - off[t]), where=f"{label} b{b} t{t}")
+            worst[0] = max(worst[0], max_abs(_np(o[b:b + 1, :, 32 * t: 32 * t + 32]), oo))
+            q2r = _np(q2[b:b + 1, :, 32 * t: 32 * t + 32])
+            own = np.ascontiguousarray(gi[b:b + 1, :, : off[-1]])   # this sequence's tiles' sets
+            ref = oracle.prefill_reuse(q2r, kb, vb, own, hm, pct, t0=t, t1=t + 1)
+            worst[1] = max(worst[1], max_abs(_np(o_r[b:b + 1, :, 32 * t: 32 * t + 32]), ref))
+            refd = oracle.dense_attention(qr, _np(k[b:b + 1, :, :32 * t + 32]), _np(v[b:b + 1, :, :32 * t + 32]),
+                                          causal=True)
+            worst[2] = max(worst[2], max_abs(_np(o_d[b:b + 1, :, 32 * t: 32 * t + 32]), refd))
+    _say(f"    near-tie swaps={swaps} max|o-o_oracle| anchor={worst[0]:.3g} reuse={worst[1]:.3g} "
+         f"dense={worst[2]:.3g} tol={tol}")
+    assert max(worst) <= tol
+
+
+PREFILL_VARLEN = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, lens)
+    ("bf16_d128_g4", 3, 8, 2, 128, 640, "bf16", 10, (640, 96, 32)),
+    ("f16_d64_g2", 2, 4, 2, 64, 1184, "f16", 25, (1184, 608)),
+    ("bf16_d128_g8_anchor_pairs", 2, 16, 2, 128, 384, "bf16", 10, (352, 64)),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_VARLEN, ids=[c[0] for c in PREFILL_VARLEN])
+def test_prefill_varlen(case):
+    label, B, Hq, Hkv, D, N, dt, pct, lens = case
+    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    _check_prefill_varlen(w, q, k, v, np.array(lens, np.int32), pct, label)
+
+
+def test_prefill_varlen_full_size_sampled_tiles():
+    import dataclasses
+    w = dataclasses.replace(inputgen.WORKLOADS["qwen8b_prefill_32k"], batch=2)
+    pos = inputgen.heavy_positions(w)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
+    _check_prefill_varlen(w, q, k, v, np.array([32768, 8192], np.int32), w.topk_pct, w.name,
+                          tiles=(1, 37, 255, 500, 1023))
