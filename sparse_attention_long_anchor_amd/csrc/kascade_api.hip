@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -36,10 +37,11 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 
 // ------------------------------------------------------------------ timing registry
 
-static const char* const kKernelNames[K_COUNT_] = {
+static const char* const kKernelNames[] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
     "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows", "decode_refine_map"};
+static_assert(sizeof(kKernelNames) / sizeof(kKernelNames[0]) == K_COUNT_, "one timing name per kernel id");
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
 
@@ -193,16 +195,18 @@ static int env_int(const char* name, int dflt) {
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
+// Calls from several threads may query the same device at once: the cache
+// entries are atomics, and concurrent first queries store the same value.
 static int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Rows of the index set per decode attention workgroup. The gather is bound
