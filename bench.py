@@ -204,7 +204,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention comparison")
     ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 layer timings")
-    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode timings")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache timings")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -383,6 +383,8 @@ def main():
                                    torch, inputgen, kas)
     if not args.no_paged and do_dec:
         out["paged_decode"] = paged_timings(wd, dec_state, dev, torch, inputgen, kas)
+    if not args.no_paged and do_pre:
+        out["paged_prefill"] = paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
@@ -573,11 +575,7 @@ def paged_timings(wd, dec_state, dev, torch, inputgen, kas):
         g = torch.Generator(device="cpu").manual_seed(P)
         ids = torch.randperm(B * per, generator=g).to(torch.int32).view(B, per).to(dev)
 
-        def pool(x):
-            pg = torch.empty((B * per, Hkv, P, D), dtype=x.dtype, device=dev)
-            pg[ids.view(-1).long()] = x.view(B, Hkv, per, P, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, P, D)
-            return pg
-        kp0, vp0, kp1, vp1 = pool(k0), pool(v0), pool(k1), pool(v1)
+        kp0, vp0, kp1, vp1 = (_page_pool(torch, x, ids, P) for x in (k0, v0, k1, v1))
         kw = dict(block_table=ids, seq_len=N)
         wsa = kas.binding._ws_kv(*_kv_desc(kas, q0, kp0, ids, N, wd), kas.OP_DECODE_ANCHOR, None, dev)
         wsr = kas.binding._ws_kv(*_kv_desc(kas, q0, kp0, ids, N, wd), kas.OP_DECODE_REUSE, None, dev)
@@ -587,6 +585,58 @@ def paged_timings(wd, dec_state, dev, torch, inputgen, kas):
         del kp0, vp0, kp1, vp1, wsa, wsr
         torch.cuda.empty_cache()
     log(f"[bench] paged decode: {res}")
+    return res
+
+
+def _page_pool(torch, x, ids, P):
+    """Page pool [pages, Hkv, P, D] holding x [B, Hkv, N, D] at the page ids
+    ids [B, N / P] (shuffled, so the pages of a sequence are scattered)."""
+    B, Hkv, N, D = x.shape
+    per = N // P
+    pg = torch.empty((B * per, Hkv, P, D), dtype=x.dtype, device=x.device)
+    pg[ids.view(-1).long()] = x.view(B, Hkv, per, P, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, P, D)
+    return pg
+
+
+def paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas):
+    """Prefill anchor and reuse layer times on the contiguous cache and on page
+    pools holding the same layers 0 and 1 (alternating protocol); the paged
+    calls include their page copy, also timed on its own."""
+    (q0, k0, v0, _), (q1, k1, v1, _) = pre_state[0][0], pre_state[0][1]
+    o, ws_a, ws_r = pre_state[2], pre_state[3], pre_state[4]
+    total = int(pre_state[5][-1])
+    B, Hkv, N, D = k0.shape
+    hm = torch.as_tensor(inputgen.head_maps(wp)[1], device=dev)
+    idx = torch.empty((B, Hkv, total), dtype=torch.int32, device=dev)
+    res = {"workload": wp.name, "unit": "ms"}
+    ta, tr = _alternate(torch, lambda: kas.prefill_anchor(q0, k0, v0, wp.topk_pct, idx_out=idx, o=o, ws=ws_a),
+                        lambda: kas.prefill_reuse(q1, k1, v1, idx, hm, wp.topk_pct, o=o, ws=ws_r), 3)
+    res["contiguous"] = {"anchor": round(ta, 3), "reuse": round(tr, 3)}
+    for P in (16, 256):
+        g = torch.Generator(device="cpu").manual_seed(P)
+        ids = torch.randperm(B * (N // P), generator=g).to(torch.int32).view(B, N // P).to(dev)
+        kp0, vp0, kp1, vp1 = (_page_pool(torch, x, ids, P) for x in (k0, v0, k1, v1))
+        kw = dict(block_table=ids)
+        wsa = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids),
+                                 kas.OP_PREFILL_ANCHOR, None, dev)
+        wsr = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids),
+                                 kas.OP_PREFILL_REUSE, None, dev)
+        ta, tr = _alternate(torch,
+                            lambda: kas.prefill_anchor(q0, kp0, vp0, wp.topk_pct, idx_out=idx, o=o, ws=wsa, **kw),
+                            lambda: kas.prefill_reuse(q1, kp1, vp1, idx, hm, wp.topk_pct, o=o, ws=wsr, **kw), 3)
+        kas.profile_reset()
+        kas.profile_enable(True)
+        for _ in range(3):
+            kas.prefill_reuse(q1, kp1, vp1, idx, hm, wp.topk_pct, o=o, ws=wsr, **kw)
+        torch.cuda.synchronize()
+        kas.profile_enable(False)
+        ms, n = kas.profile_query("prefill_page_copy")
+        res[f"paged_P{P}"] = {"anchor": round(ta, 3), "reuse": round(tr, 3),
+                              "page_copy": round(ms / max(n, 1), 4)}
+        del kp0, vp0, kp1, vp1, wsa, wsr
+        torch.cuda.empty_cache()
+    res["page_copy_bytes"] = 2 * 2 * k0.numel() * k0.element_size()   # K and V, read and written
+    log(f"[bench] paged prefill: {res}")
     return res
 
 

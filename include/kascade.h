@@ -188,9 +188,9 @@ kas_status_t kas_decode_dense(const kas_desc_t* desc, const void* q, const void*
 kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                void* o, void* ws, size_t ws_bytes, void* stream);
 
-/* Decode KV caches whose sequences have different lengths and/or whose rows
- * live in pages (README notes: paged and varlen kernels are announced for
- * the pages' own kernels). Passed to the *_kv decode calls; NULL there means
+/* KV caches whose sequences have different lengths and/or whose rows live in
+ * pages (README notes: paged and varlen kernels are announced for the pages'
+ * own kernels). Passed to the *_kv decode and prefill calls; NULL there means
  * the dense [B, Hkv, N, D] cache of kas_desc_t with every sequence N keys
  * long, exactly the calls without _kv.
  *   - seq_lens (device [B] or NULL): keys of sequence b, in [1, desc->seq_len]
@@ -205,8 +205,8 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
  *     pools, [num_pages, Hkv, P, D] with the default strides; desc's
  *     kv_*_stride are not used. Paged caches hold bf16 or fp16.
  * KAS_ERR_UNSUPPORTED: a paged fp32 cache, or a pool of 2^31 rows or more
- * (num_pages * page_stride / head_dim). The prefill *_kv calls take seq_lens
- * only (see below). */
+ * (num_pages * page_stride / head_dim). The prefill *_kv calls read lengths
+ * in whole tiles (see below). */
 typedef struct kas_kv_cache {
   const int32_t* seq_lens;
   const int32_t* block_table;
@@ -217,7 +217,9 @@ typedef struct kas_kv_cache {
   int64_t page_head_stride;  /* elements between KV heads in a page (0 = P * D) */
 } kas_kv_cache_t;
 
-/* Workspace of a *_kv call (op: KAS_OP_DECODE_*). */
+/* Workspace of a *_kv call (any KAS_OP_*): a paged prefill call needs room
+ * for contiguous copies of its K and V (2 * B * Hkv * seq_len * head_dim
+ * elements) beyond the workspace of the same call without pages. */
 kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int32_t op,
                                    size_t* bytes);
 /* kas_decode_anchor / kas_decode_reuse / kas_decode_dense over such a cache. */
@@ -237,7 +239,11 @@ kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
  * (clamped to [32, desc->seq_len]); tiles past a prompt are not computed and
  * their rows of o and their index sets are left unspecified. The CSR layout
  * is that of desc->seq_len (a tile's set size depends only on the tile).
- * block_table must be NULL (KAS_ERR_UNSUPPORTED). */
+ * With block_table, k and v are page pools as for decode (P >= 16, desc->
+ * seq_len the longest prompt): the call first copies the K and V rows of
+ * every prompt's whole tiles, page by page, into its workspace as a
+ * contiguous [B, Hkv, seq_len, D] cache and then runs as over a contiguous
+ * one, so its results equal those of the same call on that cache. */
 kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
                                    const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
                                    size_t ws_bytes, void* stream);

@@ -286,15 +286,28 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
     return o
 
 
-def _lens_cache(seq_lens):
-    return None if seq_lens is None else KasKvCache(seq_lens.data_ptr(), None, 0, 0, 0, 0, 0)
+def _prefill_desc(q, k, pct, scale, seq_lens, block_table, **kw):
+    """(descriptor, KasKvCache or None) of a prefill call. With block_table
+    (device int32 [B, max_pages]), k and v are page pools [num_pages, Hkv, P, D]
+    and the prompt length N comes from q [B, Hq, N, D]."""
+    if block_table is None:
+        desc = _desc_from(q, k, pct, True, scale, **kw)
+        cache = None if seq_lens is None else KasKvCache(seq_lens.data_ptr(), None, 0, 0, 0, 0, 0)
+        return desc, cache
+    over, cache = _cache(q, k, seq_lens, block_table, q.shape[2])
+    B, Hq, N, D = q.shape
+    desc = make_desc(B, Hq, over["n_kv_heads"], over["head_dim"], N, pct, q.dtype, softmax_scale=scale, **kw)
+    return desc, cache
 
 
 def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
-                   pool_scope: int = 0, pool_op: int = 0, seq_lens=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> (idx int32 [B,Hs,total] CSR, o [B,Hq,N,D]);
-    Hs as in decode_anchor."""
-    desc = _desc_from(q, k, pct, True, scale, pool_scope=pool_scope, pool_op=pool_op)
+                   pool_scope: int = 0, pool_op: int = 0, seq_lens=None,
+                   block_table=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 or fp16 -> (idx int32 [B,Hs,total] CSR,
+    o [B,Hq,N,D]); Hs as in decode_anchor. seq_lens (device int32 [B]) gives each
+    prompt's length; block_table (device int32 [B, max_pages]) makes k, v page
+    pools [num_pages, Hkv, P, D]."""
+    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_anchor", "k and v must share strides")
     total = int(prefill_offsets(desc)[-1])
@@ -304,8 +317,7 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
                               device=q.device)
     if o is None:
         o = torch.empty_like(q)
-    ws = _ws(desc, OP_PREFILL_ANCHOR, ws, q.device)
-    c = _lens_cache(seq_lens)
+    ws = _ws_kv(desc, c, OP_PREFILL_ANCHOR, ws, q.device)
     if c is None:
         rc = _load().kas_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
                                         _ptr(o), _ptr(ws), ws.numel(), _stream(q))
@@ -317,15 +329,14 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
 
 
 def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
-                  query_head_map: bool = False, seq_lens=None) -> torch.Tensor:
-    """head_map as in decode_reuse."""
-    desc = _desc_from(q, k, pct, True, scale, query_head_map=int(query_head_map))
+                  query_head_map: bool = False, seq_lens=None, block_table=None) -> torch.Tensor:
+    """head_map as in decode_reuse; cache arguments as in prefill_anchor."""
+    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "prefill_reuse", "k and v must share strides")
     if o is None:
         o = torch.empty_like(q)
-    ws = _ws(desc, OP_PREFILL_REUSE, ws, q.device)
-    c = _lens_cache(seq_lens)
+    ws = _ws_kv(desc, c, OP_PREFILL_REUSE, ws, q.device)
     if c is None:
         rc = _load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
                                        anchor_idx.shape[1], _ptr(head_map), _ptr(o), _ptr(ws), ws.numel(),
@@ -359,19 +370,22 @@ def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None, seq_lens=None, bl
     return o
 
 
-def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None) -> torch.Tensor:
-    """Dense causal attention: q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 -> o [B,Hq,N,D]."""
-    desc = _desc_from(q, k, 100, True, scale)
+def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None, block_table=None,
+                  ws=None) -> torch.Tensor:
+    """Dense causal attention: q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 or fp16 -> o [B,Hq,N,D].
+    Cache arguments as in prefill_anchor (only a paged call needs a workspace)."""
+    desc, c = _prefill_desc(q, k, 100, scale, seq_lens, block_table)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_dense", "k and v must share strides")
     if o is None:
         o = torch.empty_like(q)
-    c = _lens_cache(seq_lens)
     if c is None:
         rc = _load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0, _stream(q))
     else:
+        if block_table is not None:
+            ws = _ws_kv(desc, c, OP_PREFILL_DENSE, ws, q.device)
         rc = _load().kas_prefill_dense_kv(ctypes.byref(desc), ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                          None, 0, _stream(q))
+                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
     _check(rc, "prefill_dense")
     return o
 

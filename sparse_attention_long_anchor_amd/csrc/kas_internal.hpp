@@ -26,6 +26,7 @@ enum KernelId {
   K_PRE_POOL_HEADS,
   K_DEC_PAGE_ROWS,
   K_DEC_REFINE_MAP,
+  K_PRE_PAGE_COPY,
   K_COUNT_
 };
 const char* kernel_name(int id);

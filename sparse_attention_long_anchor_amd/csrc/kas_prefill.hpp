@@ -50,4 +50,20 @@ hipError_t launch_prefill_reuse(PrefillArgs& a, LaunchCtx& ctx);
 // (idx, offsets and head_map unused).
 hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx);
 
+// Prefill over a paged cache: the K and V rows of pools [pages, Hkv, P, D],
+// read through a block table, into contiguous [B, Hkv, N, D] copies that the
+// tile kernels above then read like any contiguous cache.
+struct PageCopyArgs {
+  const void* k;
+  const void* v;                    // page pools
+  void* kc;
+  void* vc;                         // contiguous copies [B, Hkv, N, D]
+  const int32_t* seq_lens;          // [B] or null: tiles past a prompt are not copied
+  const int32_t* block_table;       // [B, max_pages] page ids (clamped to [0, num_pages))
+  int64_t page_stride, page_hstride, num_pages;   // elements per page and per head in a page; pages
+  int64_t N;
+  int B, Hkv, D, T, shift, max_pages;             // shift = log2 of the page size
+};
+hipError_t launch_prefill_page_copy(const PageCopyArgs& c, LaunchCtx& ctx);
+
 }  // namespace kas

@@ -40,7 +40,8 @@ static kas_status_t fail(kas_status_t st, const char* fmt, ...) {
 static const char* const kKernelNames[] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
-    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows", "decode_refine_map"};
+    "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows", "decode_refine_map",
+    "prefill_page_copy"};
 static_assert(sizeof(kKernelNames) / sizeof(kKernelNames[0]) == K_COUNT_, "one timing name per kernel id");
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
@@ -384,6 +385,38 @@ static kas_status_t check_prefill_limits(const Shape& s, int64_t total) {
   return KAS_OK;
 }
 
+// Prefill calls take a kas_kv_cache_t for prompts of different lengths and
+// for paged pools. A paged call first copies its prompts' K and V rows, page
+// by page, into contiguous [B, Hkv, N, D] copies placed after the call's own
+// workspace, and the tile kernels read those: the tile kernels are bound by
+// their matrix products, so one more pass over K and V costs little, and their
+// DMA pipelines keep plain row offsets.
+static size_t paged_copy_bytes(const Shape& s) {
+  return align_up((size_t)s.B * s.Hkv * (size_t)s.N * s.D * s.esize, 256);
+}
+
+static size_t prefill_need(size_t base, const Shape& s, const CacheView& cv) {
+  return cv.paged() ? align_up(base, 256) + 2 * paged_copy_bytes(s) : base;
+}
+
+// Copies a paged call's K and V (s: the call's own shape, with its KV heads)
+// and points the tile kernels' arguments at the copies.
+static hipError_t prefill_paged_kv(const CacheView& cv, const Shape& s, const void* k, const void* v, char* ws,
+                                   size_t base, PrefillArgs& a, LaunchCtx& ctx) {
+  PageCopyArgs c{};
+  c.k = k; c.v = v;
+  c.kc = ws + align_up(base, 256);
+  c.vc = (char*)c.kc + paged_copy_bytes(s);
+  c.seq_lens = cv.seq_lens; c.block_table = cv.block_table;
+  c.page_stride = cv.page_stride; c.page_hstride = cv.page_hstride; c.num_pages = cv.num_pages;
+  c.N = s.N; c.B = s.B; c.Hkv = s.Hkv; c.D = s.D; c.T = (int)(s.N / 32);
+  c.shift = cv.shift; c.max_pages = cv.max_pages;
+  a.k = c.kc; a.v = c.vc;
+  a.kv_hstride = s.N * s.D;
+  a.kv_bstride = (int64_t)s.Hkv * s.N * s.D;
+  return launch_prefill_page_copy(c, ctx);
+}
+
 static kas_status_t hip_fail(hipError_t e, const char* where) {
   return fail(KAS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
@@ -427,16 +460,17 @@ kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t*
   kas_status_t st = check_desc(desc, prefill, s);
   if (st != KAS_OK) return st;
   CacheView cv;
-  if (cache && prefill && cache->block_table) return fail(KAS_ERR_UNSUPPORTED, "paged caches are decode only");
   if ((st = check_cache(cache, s, cv))) return st;
   if (op == KAS_OP_PREFILL_DENSE) {
-    *bytes = 0;
+    *bytes = prefill_need(0, s, cv);
   } else if (op == KAS_OP_DECODE_REUSE && s.qmap) {
     *bytes = plan_decode(per_query_head(s), false, false, cv.paged()).total;
   } else if (!prefill) {
     *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE, cv.paged()).total;
   } else {
-    *bytes = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, op == KAS_OP_PREFILL_ANCHOR);
+    const Shape sr = (op == KAS_OP_PREFILL_REUSE && s.qmap) ? per_query_head(s) : s;
+    *bytes = prefill_need(prefill_workspace_bytes(sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, op == KAS_OP_PREFILL_ANCHOR),
+                          s, cv);
   }
   return KAS_OK;
 }
@@ -531,16 +565,6 @@ kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
   return KAS_OK;
 }
 
-// Prefill calls over sequences of different lengths take only seq_lens of a
-// kas_kv_cache_t (prefill caches are contiguous).
-static kas_status_t prefill_lens(const kas_kv_cache_t* cache, const int32_t** lens) {
-  *lens = nullptr;
-  if (!cache) return KAS_OK;
-  if (cache->block_table) return fail(KAS_ERR_UNSUPPORTED, "paged caches are decode only");
-  *lens = cache->seq_lens;
-  return KAS_OK;
-}
-
 kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                 int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
   return kas_prefill_anchor_kv(desc, nullptr, q, k, v, idx_out, o, ws, ws_bytes, stream);
@@ -550,10 +574,10 @@ kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t*
                                    const void* k, const void* v, int32_t* idx_out, void* o, void* ws,
                                    size_t ws_bytes, void* stream) {
   Shape s;
-  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
-  if ((st = prefill_lens(cache, &lens))) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -561,17 +585,20 @@ kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t*
   int64_t total = 0;
   if ((st = kas_prefill_index_offsets(desc, nullptr, &total))) return st;
   if ((st = check_prefill_limits(s, total))) return st;
-  size_t need = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, true);
-  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  const size_t base = prefill_workspace_bytes(s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, true);
+  if ((st = check_ws(ws, ws_bytes, prefill_need(base, s, cv)))) return st;
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, true);
   a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
   a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
   a.idx = idx_out; a.Hkv_a = a.Hsel; a.head_map = nullptr; a.total = total;
-  a.seq_lens = lens;
+  a.seq_lens = cv.seq_lens;
   LaunchCtx ctx{(hipStream_t)stream};
-  hipError_t e = launch_prefill_anchor(a, ctx);
+  hipError_t e;
+  if (cv.paged() && (e = prefill_paged_kv(cv, s, k, v, (char*)ws, base, a, ctx)) != hipSuccess)
+    return hip_fail(e, "prefill_page_copy");
+  e = launch_prefill_anchor(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_anchor");
   return KAS_OK;
 }
@@ -589,10 +616,10 @@ kas_status_t kas_prefill_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
                                   int32_t anchor_kv_heads, const int32_t* head_map, void* o, void* ws,
                                   size_t ws_bytes, void* stream) {
   Shape s;
-  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
-  if ((st = prefill_lens(cache, &lens))) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -606,17 +633,20 @@ kas_status_t kas_prefill_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   if ((st = check_prefill_limits(s, total))) return st;
   if (s.qmap && !head_map) return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map needs a head_map of n_q_heads entries");
   const Shape sr = s.qmap ? per_query_head(s) : s;
-  size_t need = prefill_workspace_bytes(sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, false);
-  if ((st = check_ws(ws, ws_bytes, need))) return st;
+  const size_t base = prefill_workspace_bytes(sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, false);
+  if ((st = check_ws(ws, ws_bytes, prefill_need(base, s, cv)))) return st;
   PrefillArgs a;
   fill_prefill_args(a, sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, sr.scale, sr.kv_bs, sr.kv_hs, (char*)ws, false);
   a.dtype = s.dtype;
   a.kvdiv = s.qmap ? s.G : 1;
-  a.seq_lens = lens;
+  a.seq_lens = cv.seq_lens;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.idx = anchor_idx; a.Hkv_a = anchor_kv_heads; a.head_map = head_map; a.total = total;
   LaunchCtx ctx{(hipStream_t)stream};
-  hipError_t e = launch_prefill_reuse(a, ctx);
+  hipError_t e;
+  if (cv.paged() && (e = prefill_paged_kv(cv, s, k, v, (char*)ws, base, a, ctx)) != hipSuccess)
+    return hip_fail(e, "prefill_page_copy");
+  e = launch_prefill_reuse(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_reuse");
   return KAS_OK;
 }
@@ -665,24 +695,27 @@ kas_status_t kas_prefill_dense(const kas_desc_t* desc, const void* q, const void
 kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
                                   const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                                   void* stream) {
-  (void)ws; (void)ws_bytes;
   Shape s;
-  const int32_t* lens;
   kas_status_t st = check_desc(desc, true, s);
   if (st != KAS_OK) return st;
-  if ((st = prefill_lens(cache, &lens))) return st;
+  CacheView cv;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
   if ((st = check_prefill_limits(s, 0))) return st;
+  if ((st = check_ws(ws, ws_bytes, prefill_need(0, s, cv)))) return st;   // 0 bytes unless paged
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, nullptr, false);
   a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.offsets = nullptr; a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = 0;
-  a.seq_lens = lens;
+  a.seq_lens = cv.seq_lens;
   LaunchCtx ctx{(hipStream_t)stream};
-  hipError_t e = launch_prefill_dense(a, ctx);
+  hipError_t e;
+  if (cv.paged() && (e = prefill_paged_kv(cv, s, k, v, (char*)ws, 0, a, ctx)) != hipSuccess)
+    return hip_fail(e, "prefill_page_copy");
+  e = launch_prefill_dense(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "prefill_dense");
   return KAS_OK;
 }

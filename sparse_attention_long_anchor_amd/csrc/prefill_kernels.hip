@@ -36,12 +36,13 @@ constexpr int kPoolBudgetMBDefault = 16384;
 // Tiles of sequence b: all T, or its own length's (a trusted input, clamped
 // to [1 tile, N] and taken in whole tiles). Tiles past it are not computed:
 // causality keeps every earlier tile's work inside the sequence.
-__device__ __forceinline__ int tiles_of(const PrefillArgs& a, int b) {
-  if (!a.seq_lens) return a.T;
-  int64_t n = a.seq_lens[b];
-  n = n < kTile ? kTile : (n > a.N ? a.N : n);
+__device__ __forceinline__ int tiles_in(const int32_t* lens, int b, int64_t N, int T) {
+  if (!lens) return T;
+  int64_t n = lens[b];
+  n = n < kTile ? kTile : (n > N ? N : n);
   return (int)(n / kTile);
 }
+__device__ __forceinline__ int tiles_of(const PrefillArgs& a, int b) { return tiles_in(a.seq_lens, b, a.N, a.T); }
 
 // Row (query or key) of the 32x32 MFMA output held by lane half hh in reg r.
 __device__ __forceinline__ int mrow(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
@@ -1048,6 +1049,43 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   }
 }
 
+// ------------------------------------------------------------------ paged caches
+
+// One workgroup per (32-row tile, KV head, sequence): the tile's K and V rows,
+// each found through the block table (page = id of entry row / P, row % P
+// inside it), into the contiguous copies. Tiles past the prompt are skipped:
+// the tile kernels read no key row at or past the prompt's last whole tile.
+// 16 bytes per lane per load; D / 64 loads of K and as many of V in flight.
+template <int D>
+__global__ __launch_bounds__(256) void pre_page_copy_kernel(PageCopyArgs c) {
+  constexpr int PARTS = D / 8;                    // 16-byte chunks per row
+  constexpr int PER = kTile * PARTS / 256;        // chunks per lane per tensor
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (t >= tiles_in(c.seq_lens, b, c.N, c.T)) return;
+  const int32_t* bt = c.block_table + (int64_t)b * c.max_pages;
+  const int64_t pmask = (int64_t(1) << c.shift) - 1;
+  const uint16_t* ks = (const uint16_t*)c.k;
+  const uint16_t* vs = (const uint16_t*)c.v;
+  const int64_t dst0 = (((int64_t)b * c.Hkv + g) * c.N + (int64_t)t * kTile) * D;
+  u32x4 kx[PER], vx[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i, r = e / PARTS, part = e % PARTS;
+    const int64_t row = (int64_t)t * kTile + r;       // < N, so row / P < max_pages
+    int64_t page = bt[row >> c.shift];
+    page = page < 0 ? 0 : (page >= c.num_pages ? c.num_pages - 1 : page);
+    const int64_t src = page * c.page_stride + g * c.page_hstride + (row & pmask) * D + 8 * part;
+    kx[i] = ldg16(ks + src);
+    vx[i] = ldg16(vs + src);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t dst = dst0 + (int64_t)(threadIdx.x + 256 * i) * 8;
+    *reinterpret_cast<u32x4*>((uint16_t*)c.kc + dst) = kx[i];
+    *reinterpret_cast<u32x4*>((uint16_t*)c.vc + dst) = vx[i];
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1218,6 +1256,14 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
     ta = tb;
   }
   return launch_attn(a, ctx);
+}
+
+hipError_t launch_prefill_page_copy(const PageCopyArgs& c, LaunchCtx& ctx) {
+  ctx.begin(K_PRE_PAGE_COPY);
+  const dim3 grid(c.T, c.Hkv, c.B);
+  if (c.D == 128) ctx.launch(pre_page_copy_kernel<128>, grid, dim3(256), c);
+  else ctx.launch(pre_page_copy_kernel<64>, grid, dim3(256), c);
+  return ctx.end(K_PRE_PAGE_COPY);
 }
 
 hipError_t launch_prefill_reuse(PrefillArgs& a, LaunchCtx& ctx) {

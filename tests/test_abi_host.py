@@ -186,7 +186,16 @@ def test_kv_cache_layout_checks_without_gpu():
     assert ws(paged, desc=df) == 2 and b"bf16 or fp16" in L.kas_last_error()
     dp = b.make_desc(1, 8, 2, 128, 256, 10, torch.bfloat16)
     assert ws(varlen, b.OP_PREFILL_ANCHOR, dp) == 0                      # prefill takes lengths
-    assert ws(paged, b.OP_PREFILL_ANCHOR, dp) == 2                       # but no pages
+    # and pages: room for contiguous K and V copies (B Hkv N D elements each)
+    # after the call's own workspace
+    kv = 1 * 2 * 256 * 128 * 2
+    for op in (b.OP_PREFILL_ANCHOR, b.OP_PREFILL_REUSE):
+        base = b.workspace_size(dp, op)
+        assert ws(paged, op, dp) == 0 and n.value == (base + 255) // 256 * 256 + 2 * kv
+    assert ws(paged, b.OP_PREFILL_DENSE, dp) == 0 and n.value == 2 * kv
+    assert b.workspace_size(dp, b.OP_PREFILL_DENSE) == 0
+    r = L.kas_prefill_dense_kv(ctypes.byref(dp), ctypes.byref(paged), fake, fake, fake, fake, None, 0, None)
+    assert r != 0 and b"workspace" in L.kas_last_error()
     r = L.kas_decode_anchor_kv(ctypes.byref(d), ctypes.byref(bad[0][0]), fake, fake, fake, fake, fake, fake,
                                1 << 30, None)
     assert r == 1 and b"power of two" in L.kas_last_error()

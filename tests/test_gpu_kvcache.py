@@ -1,5 +1,5 @@
-"""GPU parity of decode over varlen and paged KV caches (the README announces
-paged and varlen kernels), through the C ABI.
+"""GPU parity of decode and prefill over varlen and paged KV caches (the
+README announces paged and varlen kernels), through the C ABI.
 
 Each sequence b of a varlen batch is checked against the oracle run on its
 own contiguous keys [0, seq_lens[b]); keys past a sequence's end hold random
@@ -7,7 +7,9 @@ values that must not matter. A paged cache holds the same rows scattered over
 a shuffled page pool; its index sets, reuse and dense outputs must equal the
 contiguous varlen results bit for bit (the same kernels over the same rows),
 and its anchor output (which reads K again instead of stored logits) must
-match the oracle.
+match the oracle. Prefill over a paged cache copies the pages into a
+contiguous cache first, so all of its results must equal the contiguous
+ones bit for bit.
 """
 import sys
 import zlib
@@ -202,6 +204,35 @@ def _check_prefill_varlen(w, q, k, v, lens, pct, label, tiles=None):
     _say(f"    near-tie swaps={swaps} max|o-o_oracle| anchor={worst[0]:.3g} reuse={worst[1]:.3g} "
          f"dense={worst[2]:.3g} tol={tol}")
     assert max(worst) <= tol
+    return idx, o, o_r, o_d, q2, hm
+
+
+def _check_prefill_paged(w, q, k, v, lens, pct, P, ref):
+    """The prefill calls on a paged copy of the cache equal the contiguous ones
+    (ref = their results) bit for bit on every tile inside the prompts. Block
+    table entries of pages past a prompt's last whole tile hold ids far out of
+    range: the calls must not need them."""
+    kas = _kas()
+    idx, o, o_r, o_d, q2, hm = ref
+    B, Hkv = w.batch, w.n_kv_heads
+    kp, vp, bt = _paged(k, v, P, seed=P + 7 * B)
+    tl = None if lens is None else torch.as_tensor(lens, device=DEV)
+    tiles = [w.seq_len // 32] * B if lens is None else [max(int(n), 32) // 32 for n in lens]
+    for b in range(B):
+        bt[b, (32 * tiles[b] + P - 1) // P:] = 1 << 30
+    _say(f"[prefill paged P={P}] {w.name}: lens={None if lens is None else lens.tolist()} "
+         f"pool={tuple(kp.shape)}")
+    idx_p, o_p = kas.prefill_anchor(q, kp, vp, pct, seq_lens=tl, block_table=bt)
+    or_p = kas.prefill_reuse(q2, kp, vp, idx, torch.as_tensor(hm, device=DEV), pct, seq_lens=tl, block_table=bt)
+    od_p = kas.prefill_dense(q, kp, vp, seq_lens=tl, block_table=bt)
+    torch.cuda.synchronize()
+    off = oracle.prefill_offsets(w.seq_len, 32, pct)
+    for b in range(B):
+        rows, sets = 32 * tiles[b], int(off[tiles[b]])
+        assert torch.equal(idx_p[b, :, :sets], idx[b, :, :sets]), f"paged index sets differ (b{b})"
+        for name, x, y in (("anchor", o_p, o), ("reuse", or_p, o_r), ("dense", od_p, o_d)):
+            assert torch.equal(x[b, :, :rows], y[b, :, :rows]), f"paged {name} output differs (b{b})"
+    _say("    paged: sets, anchor, reuse and dense outputs bit-identical to the contiguous cache")
 
 
 PREFILL_VARLEN = [
@@ -220,10 +251,38 @@ def test_prefill_varlen(case):
     _check_prefill_varlen(w, q, k, v, np.array(lens, np.int32), pct, label)
 
 
+PREFILL_PAGED = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, lens or None, page size)
+    ("bf16_d128_g4_P16_varlen", 3, 8, 2, 128, 640, "bf16", 10, (640, 96, 32), 16),
+    ("f16_d64_g2_P64_varlen", 2, 4, 2, 64, 1184, "f16", 25, (1184, 608), 64),
+    ("bf16_d128_g8_P32", 2, 16, 2, 128, 384, "bf16", 10, None, 32),
+    ("bf16_d64_g1_P1024", 1, 4, 4, 64, 2080, "bf16", 10, None, 1024),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_PAGED, ids=[c[0] for c in PREFILL_PAGED])
+def test_prefill_paged(case):
+    """Paged prefill: every prompt against the oracle (through the contiguous
+    calls) and the paged calls bit-identical to the contiguous ones."""
+    label, B, Hq, Hkv, D, N, dt, pct, lens, P = case
+    w = inputgen.custom("prefill", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    L = np.array(lens if lens else [N] * B, np.int32)
+    ref = _check_prefill_varlen(w, q, k, v, L, pct, label)
+    if lens is None:      # full-length prompts: also the calls without lengths
+        kas = _kas()
+        idx, o = kas.prefill_anchor(q, k, v, pct)
+        assert torch.equal(idx, ref[0]) and torch.equal(o, ref[1])
+        ref = (idx, o, kas.prefill_reuse(ref[4], k, v, idx, torch.as_tensor(ref[5], device=DEV), pct),
+               kas.prefill_dense(q, k, v), ref[4], ref[5])
+    _check_prefill_paged(w, q, k, v, None if lens is None else L, pct, P, ref)
+
+
 def test_prefill_varlen_full_size_sampled_tiles():
     import dataclasses
     w = dataclasses.replace(inputgen.WORKLOADS["qwen8b_prefill_32k"], batch=2)
     pos = inputgen.heavy_positions(w)
     q, k, v = inputgen.layer_inputs(w, 0, DEV, pos)
-    _check_prefill_varlen(w, q, k, v, np.array([32768, 8192], np.int32), w.topk_pct, w.name,
-                          tiles=(1, 37, 255, 500, 1023))
+    lens = np.array([32768, 8192], np.int32)
+    ref = _check_prefill_varlen(w, q, k, v, lens, w.topk_pct, w.name, tiles=(1, 37, 255, 500, 1023))
+    _check_prefill_paged(w, q, k, v, lens, w.topk_pct, 256, ref)
