@@ -256,25 +256,41 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
 
-    # Pass 1 (the timed region of the step): per-layer events on the stream,
-    # library launch timing off. Pass 2: the same steps again with the
-    # library's per-launch events on (hipExtLaunchKernel start/stop stamps),
-    # for per-kernel device times; those stamps add host and device time per
-    # launch, so layer figures come from pass 1 only.
-    dec_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(wd.n_layers)] for _ in range(args.steps)] if do_dec else None
-    pre_ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(wp.n_layers)] for _ in range(args.steps)] if do_pre else None
+    # Pass 1 (the timed region): events only around each phase of a step, so
+    # that nothing is enqueued between layers. Pass 2: the same steps again
+    # with events between layers, for the anchor / reuse layer breakdown (an
+    # event record between two layers adds a few microseconds of device
+    # time, so step figures come from pass 1). Pass 3: the library's
+    # per-launch events on (hipExtLaunchKernel start/stop stamps), for
+    # per-kernel device times.
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dec_ev = [ev_pair() for _ in range(args.steps)] if do_dec else None
+    pre_ev = [ev_pair() for _ in range(args.steps)] if do_pre else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         if do_dec:
-            run_decode_step(wd, dec_state, inputgen, kas, dec_ev[s])
+            dec_ev[s][0].record()
+            run_decode_step(wd, dec_state, inputgen, kas)
+            dec_ev[s][1].record()
         if do_pre:
-            run_prefill_step(wp, pre_state, inputgen, kas, pre_ev[s])
+            pre_ev[s][0].record()
+            run_prefill_step(wp, pre_state, inputgen, kas)
+            pre_ev[s][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.3f} s")
+
+    dec_lay = [[ev_pair() for _ in range(wd.n_layers)] for _ in range(args.steps)] if do_dec else None
+    pre_lay = [[ev_pair() for _ in range(wp.n_layers)] for _ in range(args.steps)] if do_pre else None
+    for s in range(args.steps):
+        if do_dec:
+            run_decode_step(wd, dec_state, inputgen, kas, dec_lay[s])
+        if do_pre:
+            run_prefill_step(wp, pre_state, inputgen, kas, pre_lay[s])
+    torch.cuda.synchronize()
+    log(f"[bench] per-layer pass: {args.steps} steps")
 
     kas.profile_reset()
     kas.profile_enable(True)
@@ -308,11 +324,11 @@ def main():
     if do_dec:
         kd = dec_state[5]
         reuse_b, anchor_b, kern_b = decode_work(wd, kd)
-        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in dec_ev]
+        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in dec_lay]
         per_layer = [sum(x[l] for x in lay_ms) / args.steps for l in range(wd.n_layers)]
         anc = [per_layer[l] for l in range(wd.n_layers) if l in wd.anchors]
         reu = [per_layer[l] for l in range(wd.n_layers) if l not in wd.anchors]
-        step_ms = sum(per_layer)
+        step_ms = _mean([a.elapsed_time(b) for a, b in dec_ev])
         step_bytes = len(anc) * anchor_b + len(reu) * reuse_b
         gbs = step_bytes / (step_ms * 1e-3) / 1e9
         out["value"] = round(gbs, 3)
@@ -321,7 +337,8 @@ def main():
             "anchors": list(wd.anchors), "topk_pct": wd.topk_pct, "k": kd,
             "us_per_layer": {"anchor": round(1e3 * _mean(anc), 3),
                              "reuse": round(1e3 * _mean(reu), 3),
-                             "mean": round(1e3 * step_ms / wd.n_layers, 3)},
+                             "mean": round(1e3 * step_ms / wd.n_layers, 3),
+                             "timing": "anchor, reuse: events between layers; mean: the step's own events"},
             "GB_per_s": {"anchor": _rate(anchor_b, _mean(anc) * 1e-3, 1e9),
                          "reuse": _rate(reuse_b, _mean(reu) * 1e-3, 1e9),
                          "step": round(gbs, 2)},
@@ -336,11 +353,11 @@ def main():
     if do_pre:
         off = pre_state[5]
         work = prefill_work(wp, off)
-        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in pre_ev]
+        lay_ms = [[a.elapsed_time(b) for (a, b) in step] for step in pre_lay]
         per_layer = [sum(x[l] for x in lay_ms) / args.steps for l in range(wp.n_layers)]
         anc = [per_layer[l] for l in range(wp.n_layers) if l in wp.anchors]
         reu = [per_layer[l] for l in range(wp.n_layers) if l not in wp.anchors]
-        step_ms = sum(per_layer)
+        step_ms = _mean([a.elapsed_time(b) for a, b in pre_ev])
         anc_flops = work["prefill_stats"] + work["prefill_pool"] + work["prefill_attn"]
         out["prefill"] = {
             "workload": wp.name, "batch": wp.batch, "seq_len": wp.seq_len, "layers": wp.n_layers,
@@ -409,14 +426,14 @@ def dense_baseline(args, wd, dec_state, wp, pre_state, out, torch, kas, dev):
     for phase, layers, call in runs:
         q, k, v, _ = layers[0]
         call(q, k, v)                                  # warm-up
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         torch.cuda.synchronize()
-        for l, (q, k, v, _) in enumerate(layers):
-            ev[l][0].record()
+        ev[0].record()                                 # events around the step, as for the sparse step
+        for q, k, v, _ in layers:
             call(q, k, v)
-            ev[l][1].record()
+        ev[1].record()
         torch.cuda.synchronize()
-        per_layer = [a.elapsed_time(b) for a, b in ev]
+        per_layer = [ev[0].elapsed_time(ev[1]) / len(layers)] * len(layers)
         kas.profile_reset()
         kas.profile_enable(True)
         for q, k, v, _ in layers:
