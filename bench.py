@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 layer timings")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache timings")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the reference ceilings (a large bf16 GEMM, a device copy)")
     ap.add_argument("--layers", type=int, default=0,
                     help="profiling runs only: keep the first N layers of each schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -402,6 +404,8 @@ def main():
         out["paged_decode"] = paged_timings(wd, dec_state, dev, torch, inputgen, kas)
     if not args.no_paged and do_pre:
         out["paged_prefill"] = paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas)
+    if not args.no_ceilings:
+        out["ceilings"] = ceilings(torch, dev)
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
@@ -613,6 +617,44 @@ def _page_pool(torch, x, ids, P):
     pg = torch.empty((B * per, Hkv, P, D), dtype=x.dtype, device=x.device)
     pg[ids.view(-1).long()] = x.view(B, Hkv, per, P, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, P, D)
     return pg
+
+
+def ceilings(torch, dev):
+    """What this GPU reaches on plain work, beside the published peaks the
+    rooflines use: a 16384^3 bf16 GEMM through torch (the vendor BLAS) and a
+    2 GiB device-to-device copy (read + written bytes)."""
+    res = {}
+    n = 16384
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    res["gemm_bf16_16384"] = {"TFLOP_per_s": round(2 * n ** 3 / ms / 1e9, 1),
+                              "frac_of_peak": round(2 * n ** 3 / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    del a, b, c
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    gbs = 2 * src.numel() * 2 / (ms * 1e-3) / 1e9
+    res["copy_2GiB"] = {"GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"[bench] ceilings: {res}")
+    return res
 
 
 def paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas):
