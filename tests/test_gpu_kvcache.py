@@ -225,14 +225,19 @@ def _check_prefill_paged(w, q, k, v, lens, pct, P, ref):
     idx_p, o_p = kas.prefill_anchor(q, kp, vp, pct, seq_lens=tl, block_table=bt)
     or_p = kas.prefill_reuse(q2, kp, vp, idx, torch.as_tensor(hm, device=DEV), pct, seq_lens=tl, block_table=bt)
     od_p = kas.prefill_dense(q, kp, vp, seq_lens=tl, block_table=bt)
+    # a head map per query head (each query head reads its KV head's rows)
+    qm = torch.as_tensor(np.repeat(hm, w.n_q_heads // Hkv), device=DEV)
+    oq = kas.prefill_reuse(q2, k, v, idx, qm, pct, query_head_map=True, seq_lens=tl)
+    oq_p = kas.prefill_reuse(q2, kp, vp, idx, qm, pct, query_head_map=True, seq_lens=tl, block_table=bt)
     torch.cuda.synchronize()
     off = oracle.prefill_offsets(w.seq_len, 32, pct)
     for b in range(B):
         rows, sets = 32 * tiles[b], int(off[tiles[b]])
         assert torch.equal(idx_p[b, :, :sets], idx[b, :, :sets]), f"paged index sets differ (b{b})"
-        for name, x, y in (("anchor", o_p, o), ("reuse", or_p, o_r), ("dense", od_p, o_d)):
+        for name, x, y in (("anchor", o_p, o), ("reuse", or_p, o_r), ("dense", od_p, o_d),
+                           ("reuse, query-head map", oq_p, oq)):
             assert torch.equal(x[b, :, :rows], y[b, :, :rows]), f"paged {name} output differs (b{b})"
-    _say("    paged: sets, anchor, reuse and dense outputs bit-identical to the contiguous cache")
+    _say("    paged: sets, anchor, reuse (both map kinds) and dense outputs bit-identical to the contiguous cache")
 
 
 PREFILL_VARLEN = [
