@@ -274,6 +274,18 @@ kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void
                                const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
                                const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
                                size_t ws_bytes, void* stream);
+/* The same over a paged cache (cache->block_table as for kas_decode_*_kv;
+ * NULL cache: exactly kas_decode_refine). Every sequence holds
+ * desc->seq_len keys: seq_lens must be NULL (KAS_ERR_UNSUPPORTED). The
+ * pool's keys are translated to rows of the page pools before scoring, and
+ * the refined keys again before the attention; the results equal those of
+ * kas_decode_refine on the same keys in a contiguous cache. */
+kas_status_t kas_workspace_size_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int64_t pool_size,
+                                          size_t* bytes);
+kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, const int32_t* pool_idx, int32_t pool_kv_heads,
+                                  int64_t pool_size, const int32_t* head_map, int32_t* idx_out, void* o,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 const char* kas_status_string(kas_status_t status);
 /* Text of the last failure on the calling thread ("" if none). */

@@ -98,6 +98,9 @@ def _load():
         L.kas_workspace_size_refine.argtypes = [dp, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
         L.kas_decode_refine.argtypes = [dp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
                                         ctypes.c_size_t, P]
+        L.kas_workspace_size_refine_kv.argtypes = [dp, cp, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+        L.kas_decode_refine_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
+                                           ctypes.c_size_t, P]
         L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_status_string.argtypes = [st]
         L.kas_status_string.restype = ctypes.c_char_p
@@ -111,8 +114,8 @@ def _load():
                   "kas_decode_dense", "kas_prefill_dense", "kas_workspace_size_kv",
                   "kas_decode_anchor_kv", "kas_decode_reuse_kv", "kas_decode_dense_kv",
                   "kas_workspace_size_refine", "kas_decode_refine", "kas_prefill_anchor_kv",
-                  "kas_prefill_reuse_kv", "kas_prefill_dense_kv",
-                  "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
+                  "kas_prefill_reuse_kv", "kas_prefill_dense_kv", "kas_workspace_size_refine_kv",
+                  "kas_decode_refine_kv", "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
                   "kas_profile_names"):
             getattr(L, n).restype = st
         _lib = L
@@ -391,11 +394,13 @@ def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None, block_tabl
 
 
 def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx_out=None, o=None,
-                  ws=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  ws=None, block_table=None, seq_len=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Refined layer of proposal-refined reuse: pool_idx [B, Hkv_p, n_pool] int32 (an anchor
     set at a larger percentage), head_map [Hkv] or None -> (idx int32 [B, Hkv, kappa],
-    o [B, Hq, D]) with kappa this layer's own k for pct."""
-    desc = _desc_from(q, k, pct, False, scale)
+    o [B, Hq, D]) with kappa this layer's own k for pct. With block_table, k and v are
+    page pools as in decode_anchor (seq_len = the sequences' common length)."""
+    over, cache = _cache(q, k, None, block_table, seq_len)
+    desc = _decode_desc(q, k, pct, scale, over)
     if k.stride() != v.stride():
         raise KasError(1, "decode_refine", "k and v must share strides")
     n_pool = pool_idx.shape[2]
@@ -405,12 +410,14 @@ def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx
     if o is None:
         o = torch.empty_like(q)
     L = _load()
+    cref = None if cache is None else ctypes.byref(cache)
     if ws is None:
         n = ctypes.c_size_t(0)
-        _check(L.kas_workspace_size_refine(ctypes.byref(desc), n_pool, ctypes.byref(n)), "workspace_size")
+        _check(L.kas_workspace_size_refine_kv(ctypes.byref(desc), cref, n_pool, ctypes.byref(n)), "workspace_size")
         ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=q.device)
-    _check(L.kas_decode_refine(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(pool_idx), pool_idx.shape[1],
-                               n_pool, _ptr(head_map), _ptr(idx_out), _ptr(o), _ptr(ws), ws.numel(), _stream(q)),
+    _check(L.kas_decode_refine_kv(ctypes.byref(desc), cref, _ptr(q), _ptr(k), _ptr(v), _ptr(pool_idx),
+                                  pool_idx.shape[1], n_pool, _ptr(head_map), _ptr(idx_out), _ptr(o), _ptr(ws),
+                                  ws.numel(), _stream(q)),
            "decode_refine")
     return idx_out, o
 

@@ -66,12 +66,14 @@ constexpr float kBigSum = 0x1p64f;   // lazy-reference term that forces the exac
 // PG: a paged cache; the chunk's page ids are read into LDS once, and a
 // 16-key block (pages hold a power-of-two multiple of 16 keys) lies in one page.
 // IX: rows are the keys of a pool (a.idx through the head map, a.N = pool
-// size); the chunk's keys are read into LDS once.
+// size); the chunk's keys are read into LDS once. IX with PG: the pool's keys
+// are physical rows of a page pool (translated beforehand), counted in D
+// elements from k + g * page_hstride.
 template <typename T, int D, int G, bool PG = false, bool IX = false>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   using QK = QKMfma<T, D>;
   __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ int32_t s_pg[PG ? kScorePages : (IX ? kScoreMaxRows : 1)];
+  __shared__ int32_t s_pg[IX ? kScoreMaxRows : (PG ? kScorePages : 1)];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c16 = lane & 15;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
   }
   const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + row0 * D;
   const int64_t p0 = row0 >> a.page_shift;
-  if (PG) {
+  if (PG && !IX) {
     const int np = nrows > 0 ? (int)(((row0 + nrows - 1) >> a.page_shift) - p0 + 1) : 0;
     for (int i = tid; i < np; i += 256) s_pg[i] = a.block_table[(int64_t)b * a.max_pages + p0 + i];
     __syncthreads();
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecodeArgs a) {
     const int jr = blk * 16 + c16;
     if (IX) {
       const int64_t key = s_pg[jr < nrows ? jr : 0];
-      dst.load_k((const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + key * D, q4);
+      const T* base = PG ? (const T*)a.k + g * a.page_hstride : (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+      dst.load_k(base + key * D, q4);
     } else if (PG) {
       const int64_t j = row0 + (jr < nrows ? jr : 0);
       const int64_t pg = page_id(a, s_pg[(j >> a.page_shift) - p0]);
@@ -1298,16 +1301,21 @@ static hipError_t score_launch_pg(const DecodeArgs& a, dim3 grid, LaunchCtx& st)
   }
   return hipSuccess;
 }
-template <typename T, int D>
-static hipError_t score_launch_ix(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+template <typename T, int D, bool PG>
+static hipError_t score_launch_ix_pg(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
   switch (a.G) {
-    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1, false, true>), grid, dim3(256), st, a); break;
-    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2, false, true>), grid, dim3(256), st, a); break;
-    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4, false, true>), grid, dim3(256), st, a); break;
-    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8, false, true>), grid, dim3(256), st, a); break;
+    case 1: KAS_LAUNCH((dec_score_kernel<T, D, 1, PG, true>), grid, dim3(256), st, a); break;
+    case 2: KAS_LAUNCH((dec_score_kernel<T, D, 2, PG, true>), grid, dim3(256), st, a); break;
+    case 4: KAS_LAUNCH((dec_score_kernel<T, D, 4, PG, true>), grid, dim3(256), st, a); break;
+    case 8: KAS_LAUNCH((dec_score_kernel<T, D, 8, PG, true>), grid, dim3(256), st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
+}
+template <typename T, int D>
+static hipError_t score_launch_ix(const DecodeArgs& a, dim3 grid, LaunchCtx& st) {
+  if (sizeof(T) == 2 && a.block_table) return score_launch_ix_pg<T, D, true>(a, grid, st);
+  return score_launch_ix_pg<T, D, false>(a, grid, st);
 }
 
 hipError_t launch_decode_score_pool_rows(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {

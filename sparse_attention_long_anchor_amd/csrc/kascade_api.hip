@@ -721,8 +721,10 @@ kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
 }
 
 // Refined layer of proposal-refined reuse: the pool-sized plan (scores,
-// pooled values and selection over the pool; gather splits over kappa).
-static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, DecodePlan& p) {
+// pooled values and selection over the pool; gather splits over kappa). A
+// paged cache adds the pool's physical rows (B * Hkv * pool_size) after it.
+static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, DecodePlan& p,
+                                bool paged = false, size_t* off_pool_rows = nullptr) {
   const int64_t kappa = decode_k(s.N, s.pct);
   if (pool_size < kappa || pool_size > s.N)
     return fail(KAS_ERR_INVALID_ARGUMENT, "pool_size %lld must lie in [kappa = %lld, seq_len = %lld]",
@@ -731,17 +733,36 @@ static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, De
     return fail(KAS_ERR_UNSUPPORTED, "refined layers pool by sum per KV head with a KV-head map");
   sp = s;
   sp.N = pool_size;
-  p = plan_decode(sp, true, false, false, kappa);
+  p = plan_decode(sp, true, false, paged, kappa);
+  if (paged) {
+    if (off_pool_rows) *off_pool_rows = p.total;
+    p.total = align_up(p.total + (size_t)s.B * s.Hkv * pool_size * sizeof(uint32_t), 256);
+  }
+  return KAS_OK;
+}
+
+// Refined layers read lengths from no cache: every sequence holds seq_len keys.
+static kas_status_t refine_cache(const kas_kv_cache_t* cache, const Shape& s, CacheView& cv) {
+  kas_status_t st = check_cache(cache, s, cv);
+  if (st != KAS_OK) return st;
+  if (cv.seq_lens) return fail(KAS_ERR_UNSUPPORTED, "refined layers take no sequence lengths");
   return KAS_OK;
 }
 
 kas_status_t kas_workspace_size_refine(const kas_desc_t* desc, int64_t pool_size, size_t* bytes) {
+  return kas_workspace_size_refine_kv(desc, nullptr, pool_size, bytes);
+}
+
+kas_status_t kas_workspace_size_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int64_t pool_size,
+                                          size_t* bytes) {
   if (!bytes) return fail(KAS_ERR_INVALID_ARGUMENT, "bytes is NULL");
   Shape s, sp;
   DecodePlan p;
+  CacheView cv;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
-  if ((st = refine_plan(s, pool_size, sp, p))) return st;
+  if ((st = refine_cache(cache, s, cv))) return st;
+  if ((st = refine_plan(s, pool_size, sp, p, cv.paged()))) return st;
   *bytes = p.total;
   return KAS_OK;
 }
@@ -750,10 +771,21 @@ kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void
                                const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
                                const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
                                size_t ws_bytes, void* stream) {
+  return kas_decode_refine_kv(desc, nullptr, q, k, v, pool_idx, pool_kv_heads, pool_size, head_map, idx_out, o, ws,
+                              ws_bytes, stream);
+}
+
+kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
+                                  const void* k, const void* v, const int32_t* pool_idx, int32_t pool_kv_heads,
+                                  int64_t pool_size, const int32_t* head_map, int32_t* idx_out, void* o,
+                                  void* ws, size_t ws_bytes, void* stream) {
   Shape s, sp;
   DecodePlan p;
+  CacheView cv;
+  size_t off_pool_rows = 0;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
+  if ((st = refine_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
@@ -763,26 +795,43 @@ kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void
   if (!head_map && pool_kv_heads != s.Hkv && pool_kv_heads != 1)
     return fail(KAS_ERR_INVALID_ARGUMENT,
                 "without a head map, pool_kv_heads must be n_kv_heads (identity) or 1 (shared pool)");
-  if ((st = refine_plan(s, pool_size, sp, p))) return st;
+  if ((st = refine_plan(s, pool_size, sp, p, cv.paged(), &off_pool_rows))) return st;
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
-  // scoring, pooling and selection over the pool's keys: positions in the pool
   DecodeArgs a;
   fill_decode_args(sp, p, true, (char*)ws, a);
+  fill_cache(a, cv, s);
   a.q = q; a.k = k; a.v = v; a.o = o;
-  a.idx = pool_idx; a.Hkv_a = pool_kv_heads; a.head_map = head_map; a.n_keys = s.N;
-  a.idx_out = (int32_t*)((char*)ws + p.off_pos);
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
+  if (cv.paged()) {
+    // the pools' keys (head map applied) as physical rows, scored from there
+    DecodeArgs t = a;
+    t.N = s.N; t.kk = pool_size;
+    t.prow = (uint32_t*)((char*)ws + off_pool_rows);
+    t.page_src = pool_idx; t.page_src_sets = pool_kv_heads; t.head_map = head_map;
+    if ((e = launch_page_rows(t, s.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    a.idx = (const int32_t*)t.prow; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.n_keys = cv.pool_rows;
+  } else {
+    a.idx = pool_idx; a.Hkv_a = pool_kv_heads; a.head_map = head_map; a.n_keys = s.N;
+  }
+  // scoring, pooling and selection over the pool's keys: positions in the pool
+  a.idx_out = (int32_t*)((char*)ws + p.off_pos);
   if ((e = launch_decode_score_pool_rows(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
   if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
   if ((e = launch_decode_select(a, ctx)) != hipSuccess) return hip_fail(e, "decode_select");
   // positions -> keys, then attention over the refined keys of the cache
   a.pos = a.idx_out;
   a.idx_out = idx_out;
+  a.idx = pool_idx; a.Hkv_a = pool_kv_heads; a.head_map = head_map;
   if ((e = launch_pool_positions_to_keys(a, ctx)) != hipSuccess) return hip_fail(e, "decode_refine_map");
   DecodeArgs ga = a;
   ga.N = s.N;
   ga.idx = idx_out; ga.Hkv_a = s.Hkv; ga.head_map = nullptr;
+  if (cv.paged()) {
+    ga.page_src = idx_out; ga.page_src_sets = s.Hkv;
+    if ((e = launch_page_rows(ga, s.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    ga.idx = (const int32_t*)ga.prow;
+  }
   if ((e = launch_decode_attn(ga, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
   return KAS_OK;
 }

@@ -218,3 +218,15 @@ def test_refine_checks_without_gpu():
     r = L.kas_decode_refine(ctypes.byref(d), fake, fake, fake, None, 2, 4 * kappa, None, fake, fake, fake,
                             1 << 30, None)
     assert r == 1 and b"pool_idx" in L.kas_last_error()
+    # over a paged cache: room for the pool's physical rows (B Hkv pool_size
+    # uint32) and the refined set's; sequence lengths are not taken
+    base = ctypes.c_size_t(0)
+    assert L.kas_workspace_size_refine(ctypes.byref(d), 4 * kappa, ctypes.byref(base)) == 0
+    paged = b.KasKvCache(None, 1 << 20, 64, 64, 200, 0, 0)
+    assert L.kas_workspace_size_refine_kv(ctypes.byref(d), ctypes.byref(paged), 4 * kappa, ctypes.byref(n)) == 0
+    assert n.value >= base.value + 2 * 2 * (4 * kappa) * 4 + 2 * 2 * kappa * 4
+    assert L.kas_workspace_size_refine_kv(ctypes.byref(d), None, 4 * kappa, ctypes.byref(n)) == 0
+    assert n.value == base.value
+    varlen = b.KasKvCache(1 << 20, None, 0, 0, 0, 0, 0)
+    assert L.kas_workspace_size_refine_kv(ctypes.byref(d), ctypes.byref(varlen), 4 * kappa, ctypes.byref(n)) == 2
+    assert b"sequence lengths" in L.kas_last_error()

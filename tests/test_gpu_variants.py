@@ -320,6 +320,8 @@ def test_decode_refine(case):
     q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
     hm = np.random.default_rng(6).integers(0, Hkv, Hkv).astype(np.int32)
     idx, o = _check_refine(w, q2, k2, v2, pool, hm, pct, label)
+    if dt != "f32":
+        _check_refine_paged(w, q2, k2, v2, pool, hm, pct, idx, o, P=64 if N > 1000 else 16)
     if ppct == 100:
         # the pool is every key: the refined layer selects what an anchor on it selects
         aidx, _ = kas.decode_anchor(q2, k2, v2, pct)
@@ -327,6 +329,20 @@ def test_decode_refine(case):
         idx2, _ = kas.decode_refine(q2, k2, v2, pool, torch.as_tensor(ident, device=DEV), pct)
         torch.cuda.synchronize()
         assert torch.equal(idx2, aidx)
+
+
+def _check_refine_paged(w, q2, k2, v2, pool, hm, pct, idx, o, P):
+    """The refined layer over a paged copy of the cache: the same sets and
+    the same output, bit for bit."""
+    kas = _kas()
+    from test_gpu_kvcache import _paged
+    kp, vp, bt = _paged(k2, v2, P, seed=P)
+    idx_p, o_p = kas.decode_refine(q2, kp, vp, pool, torch.as_tensor(hm, device=DEV), pct, block_table=bt,
+                                   seq_len=w.seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx), "paged refined sets differ from the contiguous cache's"
+    assert torch.equal(o_p, o), "paged refined output differs from the contiguous cache's"
+    _say(f"    paged (P = {P}): sets and output bit-identical to the contiguous cache")
 
 
 def test_decode_refine_full_size():
@@ -337,4 +353,6 @@ def test_decode_refine_full_size():
     pool, _ = kas.decode_anchor(q, k, v, 4 * w.topk_pct)
     del q, k, v
     q, k, v = inputgen.layer_inputs(w, 1, DEV, pos)
-    _check_refine(w, q, k, v, pool, inputgen.head_maps(w)[1], w.topk_pct, w.name)
+    hm = inputgen.head_maps(w)[1]
+    idx, o = _check_refine(w, q, k, v, pool, hm, w.topk_pct, w.name)
+    _check_refine_paged(w, q, k, v, pool, hm, w.topk_pct, idx, o, P=256)
