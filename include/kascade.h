@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   KAS_OK = 0,
   KAS_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad shape, bad value */
-  KAS_ERR_UNSUPPORTED = 2,        /* valid request this build does not run */
+  KAS_ERR_UNSUPPORTED = 2,        /* valid request the library does not run */
   KAS_ERR_WORKSPACE_TOO_SMALL = 3,
   KAS_ERR_HIP = 4                 /* a HIP launch/runtime call failed */
 } kas_status_t;
