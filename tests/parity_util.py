@@ -8,8 +8,9 @@ Tolerances:
   - outputs: max-abs 2e-2 for bf16 storage (fp32 accumulation), 1e-4 for fp32,
     5e-3 for fp16 storage. Outputs here stay below ~4 in magnitude, and the
     16-bit rounding of the output and of the probabilities used for P.V each
-    contribute at most about 4 * 2^-8 = 1.6e-2 (bf16) or 4 * 2^-11 = 2e-3
-    (fp16); fp32 I/O leaves only accumulation-order differences.
+    contribute at most about 4 * 2^-9 = 7.8e-3 (bf16) or 4 * 2^-11 = 2e-3
+    (fp16), together below the bound; fp32 I/O leaves only accumulation-order
+    differences.
 """
 import numpy as np
 
