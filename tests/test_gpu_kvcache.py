@@ -262,6 +262,7 @@ PREFILL_PAGED = [
     ("f16_d64_g2_P64_varlen", 2, 4, 2, 64, 1184, "f16", 25, (1184, 608), 64),
     ("bf16_d128_g8_P32", 2, 16, 2, 128, 384, "bf16", 10, None, 32),
     ("bf16_d64_g1_P1024", 1, 4, 4, 64, 2080, "bf16", 10, None, 1024),
+    ("f16_d128_g2_P128_varlen", 3, 8, 4, 128, 800, "f16", 20, (800, 33, 500), 128),
 ]
 
 

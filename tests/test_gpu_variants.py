@@ -277,6 +277,7 @@ REFINE = [
     ("f32_d64_g4", 1, 8, 2, 64, 2048, "f32", 10, 40),
     ("f16_d128_g8", 1, 16, 2, 128, 4099, "f16", 10, 20),
     ("bf16_d64_g1_small", 2, 4, 4, 64, 300, "bf16", 5, 100),
+    ("f16_d64_g2_b3", 3, 8, 4, 64, 7001, "f16", 10, 30),
 ]
 
 
