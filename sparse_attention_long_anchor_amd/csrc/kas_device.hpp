@@ -184,6 +184,10 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// 16 bytes with the non-temporal hint (the line is not kept in the caches)
+__device__ __forceinline__ u32x4 ldg16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ u32x2 ldg8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
@@ -249,6 +253,11 @@ struct QKMfma16 {
   __device__ __forceinline__ void load_k(const E* row, int q) {
 #pragma unroll
     for (int c = 0; c < NI; ++c) kf[c] = ldg16(row + dim_of(c, q));
+  }
+  // the same with non-temporal loads (rows read once per call)
+  __device__ __forceinline__ void load_k_nt(const E* row, int q) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) kf[c] = ldg16_nt(row + dim_of(c, q));
   }
   struct QFrag { u32x4 a[NI]; };
   __device__ __forceinline__ static void load_q(QFrag& f, const E* qrow, bool valid, int q) {
