@@ -303,6 +303,53 @@ def test_prefill_pooled_group_mass():
         np.testing.assert_allclose(P.sum(), 32 * 4, rtol=1e-12)
 
 
+def _torch_tile_pooled(q, k, b, t, heads, op, tile=32):
+    """Pooled scores of tile t from torch (float64): each query head's causal
+    softmax, with query head h reading KV head h // G (the KV heads expanded by
+    repeat_interleave, as Hugging Face's repeat_kv does), then summed (op 0) or
+    maxed (op 1) over the tile's rows and the given heads."""
+    D, N = q.shape[-1], k.shape[2]
+    G = q.shape[1] // k.shape[1]
+    kx = torch.from_numpy(k).double().repeat_interleave(G, dim=1)
+    i0, i1 = tile * t, min(N, tile * (t + 1))
+    rows = torch.arange(i0, i1)
+    mask = torch.arange(i1)[None, :] > rows[:, None]
+    acc = None
+    for h in heads:
+        s = torch.from_numpy(q[b, h, i0:i1]).double() @ kx[b, h, :i1].T / math.sqrt(D)
+        p = torch.softmax(s.masked_fill(mask, float("-inf")), dim=-1)
+        p = p.max(0).values if op else p.sum(0)
+        acc = p if acc is None else (torch.maximum(acc, p) if op else acc + p)
+    return acc.numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 4), (6, 3)])
+def test_prefill_pooled_grouped_heads_match_torch(Hq, Hkv):
+    """Pooling across several KV heads with G > 1: KV head g pools query heads
+    g*G .. g*G + G - 1 (consecutive heads share a KV head), over every row of
+    the tile, for both scopes and both operators; the sets are the stable Top-k
+    of the torch-pooled scores, compared in float32."""
+    N, B = 101, 2
+    q, k, v = _prefill_case(B=B, Hq=Hq, Hkv=Hkv, N=N, seed=31 + Hkv)
+    G = Hq // Hkv
+    T = (N + 31) // 32
+    off = oracle.prefill_offsets(N, 32, 25)
+    for scope, op in itertools.product((0, 1), (0, 1)):
+        groups = [list(range(Hq))] if scope else [list(range(g * G, g * G + G)) for g in range(Hkv)]
+        idx, _ = oracle.prefill_anchor(q, k, v, pct=25, pool_scope=scope, pool_op=op)
+        for b in range(B):
+            for t in range(T):
+                for s, heads in enumerate(groups):
+                    ref = _torch_tile_pooled(q, k, b, t, heads, op)
+                    P = oracle.prefill_pooled(q, k, b, t, s, pool_scope=scope, pool_op=op)
+                    np.testing.assert_allclose(P, ref, rtol=1e-12, atol=1e-15,
+                                               err_msg=f"scope {scope} op {op} b {b} t {t} set {s}")
+                    kt = int(off[t + 1] - off[t])
+                    cand = ref[: 32 * t]
+                    order = sorted(range(32 * t), key=lambda j: (-np.float32(cand[j]), j))
+                    assert idx[b, s, off[t]:off[t + 1]].tolist() == sorted(order[:kt]), (scope, op, b, t, s)
+
+
 def test_prefill_selection_is_topk():
     q, k, v = _prefill_case(B=2, Hq=4, Hkv=2, N=192)
     k[:, :, 40:48] = k[:, :, 7:8]       # exact ties among candidates
