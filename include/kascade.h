@@ -19,10 +19,13 @@
  *     on failure nothing is enqueued and the status says why
  *     (kas_last_error() gives text, per calling thread).
  *   - Calls are thread-safe and keep no state between calls, except the
- *     optional kernel-timing registry (kas_profile_*).
+ *     optional kernel-timing registry (kas_profile_*) and the tuning options
+ *     (kas_set_option).
  *   - Layouts are row-major with head_dim contiguous:
- *       decode : q, o [B, Hq, D];        k, v [B, Hkv, N, D] (strides below)
- *       prefill: q, o [B, Hq, N, D];     k, v [B, Hkv, N, D] (strides below)
+ *       decode : q, o [B, Hq, D];        k, v [B, Hkv, N, D]
+ *       prefill: q, o [B, Hq, N, D];     k, v [B, Hkv, N, D]
+ *     with the batch and head strides of q, o, k, v and the token strides of
+ *     q and o given in kas_desc_t; the k and v rows of one head are adjacent.
  *     Query head h uses KV head h / (Hq / Hkv).
  *   - Index sets are int32 key positions in ascending order.
  *       decode : [B, Hs, kd]      kd = max(1, kas_topk_count(N, pct))
@@ -99,6 +102,15 @@ typedef struct kas_desc {
                               set's rows (G times the rows of the KV-head
                               map). The README stores head mappings per model
                               ("Running Evaluations"). */
+  /* Element strides of q and o (head_dim stays contiguous), so that views
+   * such as a [B, N, Hq, D] projection output can be passed without a copy.
+   * 0 = the contiguous default: batch Hq*D (decode) or Hq*N*D (prefill), head
+   * D (decode) or N*D (prefill), token D (prefill; decode has one token and
+   * ignores it). Given values must be positive multiples of 16 bytes; q may
+   * alias itself (it is only read), o must not: its rows (b, h, token) may not
+   * overlap (KAS_ERR_INVALID_ARGUMENT). */
+  int64_t q_batch_stride, q_head_stride, q_token_stride;
+  int64_t o_batch_stride, o_head_stride, o_token_stride;
 } kas_desc_t;
 
 /* round-half-up(pct * n / 100) clamped to [0, n]; 0 for n <= 0 or pct <= 0.
@@ -287,7 +299,30 @@ kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
                                   int64_t pool_size, const int32_t* head_map, int32_t* idx_out, void* o,
                                   void* ws, size_t ws_bytes, void* stream);
 
-const char* kas_status_string(kas_status_t status);
+/* Process-wide tuning options. They select alternative but equivalent code
+ * paths (every setting gives the same results) and the sizes of internal
+ * buffers; tests use them to reach the alternative paths, benchmarks to
+ * compare them. Settings apply to calls (and workspace-size queries) made
+ * after them, in any thread; a value of -1 restores the default. Not meant
+ * to change while another thread is between kas_workspace_size and the call
+ * it sized. */
+typedef enum {
+  KAS_OPT_DECODE_SPLIT_ROWS = 0,    /* index-set rows per decode gather workgroup, 16..2048
+                                       (default -1: sized so one wave of workgroups covers the chip) */
+  KAS_OPT_DECODE_SELECT_ONE_PASS = 1, /* 1: decode Top-k by one workgroup per index set; 0 (default):
+                                         spread over the chip in three launches */
+  KAS_OPT_PREFILL_POOL_MB = 2,      /* cap of the prefill pooled-score buffer, MiB (default 16384);
+                                       longer prompts run their pooling and selection in tile ranges */
+  KAS_OPT_PREFILL_SELECT_CAP = 3,   /* 0..8192 (default 8192): the largest first-digit bin the prefill
+                                       Top-k resolves in LDS; larger bins take in-place passes */
+  KAS_OPT_COUNT_ = 4
+} kas_option_t;
+/* KAS_ERR_INVALID_ARGUMENT for an unknown option or a value out of range. */
+kas_status_t kas_set_option(int32_t option, int64_t value);
+kas_status_t kas_get_option(int32_t option, int64_t* value);
+
+/* Text of a status code; any int (also values outside kas_status_t) is accepted. */
+const char* kas_status_string(int32_t status);
 /* Text of the last failure on the calling thread ("" if none). */
 const char* kas_last_error(void);
 

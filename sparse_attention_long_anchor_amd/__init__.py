@@ -25,6 +25,12 @@ from .binding import (  # noqa: F401
     profile_reset,
     topk_count,
     workspace_size,
+    set_option,
+    get_option,
+    OPT_DECODE_SPLIT_ROWS,
+    OPT_DECODE_SELECT_ONE_PASS,
+    OPT_PREFILL_POOL_MB,
+    OPT_PREFILL_SELECT_CAP,
     OP_DECODE_ANCHOR,
     OP_DECODE_REUSE,
     OP_PREFILL_ANCHOR,

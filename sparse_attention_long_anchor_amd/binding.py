@@ -46,6 +46,12 @@ class KasDesc(ctypes.Structure):
         ("pool_scope", ctypes.c_int32),
         ("pool_op", ctypes.c_int32),
         ("query_head_map", ctypes.c_int32),
+        ("q_batch_stride", ctypes.c_int64),
+        ("q_head_stride", ctypes.c_int64),
+        ("q_token_stride", ctypes.c_int64),
+        ("o_batch_stride", ctypes.c_int64),
+        ("o_head_stride", ctypes.c_int64),
+        ("o_token_stride", ctypes.c_int64),
     ]
 
 
@@ -102,6 +108,8 @@ def _load():
         L.kas_decode_refine_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
                                            ctypes.c_size_t, P]
         L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_set_option.argtypes = [ctypes.c_int32, ctypes.c_int64]
+        L.kas_get_option.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
         L.kas_status_string.argtypes = [st]
         L.kas_status_string.restype = ctypes.c_char_p
         L.kas_last_error.restype = ctypes.c_char_p
@@ -116,7 +124,7 @@ def _load():
                   "kas_workspace_size_refine", "kas_decode_refine", "kas_prefill_anchor_kv",
                   "kas_prefill_reuse_kv", "kas_prefill_dense_kv", "kas_workspace_size_refine_kv",
                   "kas_decode_refine_kv", "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
-                  "kas_profile_names"):
+                  "kas_profile_names", "kas_set_option", "kas_get_option"):
             getattr(L, n).restype = st
         _lib = L
     return _lib
@@ -128,10 +136,25 @@ def _check(rc: int, where: str) -> None:
         raise KasError(rc, where, L.kas_last_error().decode())
 
 
+OPT_DECODE_SPLIT_ROWS, OPT_DECODE_SELECT_ONE_PASS, OPT_PREFILL_POOL_MB, OPT_PREFILL_SELECT_CAP = 0, 1, 2, 3
+
+
+def set_option(option: int, value: int) -> None:
+    """Process-wide tuning option (kas_set_option); -1 restores the default."""
+    _check(_load().kas_set_option(option, value), "set_option")
+
+
+def get_option(option: int) -> int:
+    v = ctypes.c_int64(0)
+    _check(_load().kas_get_option(option, ctypes.byref(v)), "get_option")
+    return int(v.value)
+
+
 def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_len: int,
               topk_pct: int, dtype: torch.dtype, tile: int = 32, softmax_scale: float = 0.0,
               kv_batch_stride: int = 0, kv_head_stride: int = 0, pool_scope: int = 0,
-              pool_op: int = 0, query_head_map: int = 0) -> KasDesc:
+              pool_op: int = 0, query_head_map: int = 0, q_strides=(0, 0, 0),
+              o_strides=(0, 0, 0)) -> KasDesc:
     if dtype == torch.bfloat16:
         dt = DTYPE_BF16
     elif dtype == torch.float16:
@@ -141,7 +164,8 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
     else:
         raise KasError(2, "make_desc", f"dtype {dtype} not supported")
     return KasDesc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, topk_pct, tile, dt,
-                   softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op, query_head_map)
+                   softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op, query_head_map,
+                   *q_strides, *o_strides)
 
 
 def topk_count(n: int, pct: int) -> int:
@@ -183,8 +207,41 @@ def _ws(desc: KasDesc, op: int, ws: Optional[torch.Tensor], device) -> torch.Ten
     return ws
 
 
+def _row_strides(t: torch.Tensor, name: str):
+    """(batch, head, token) element strides of q or o ([B, H, D] or [B, H, N, D],
+    head_dim contiguous); a dimension of size 1 passes 0 (its stride is unused)."""
+    if t.stride(-1) != 1:
+        raise KasError(1, name, f"{name} must have a contiguous last (head_dim) dimension")
+    dims = list(zip(t.shape[:-1], t.stride()[:-1])) + ([] if t.dim() == 4 else [(1, 0)])
+    return tuple(0 if n == 1 else st for n, st in dims)
+
+
+def _check_tensors(where: str, q, k, v, o=None, **ints) -> None:
+    """q, k, v (and o) share dtype and device; index-like arguments are
+    contiguous int32 tensors on that device."""
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if t is None:
+            continue
+        if t.dtype != q.dtype:
+            raise KasError(1, where, f"{name} has dtype {t.dtype}, q has {q.dtype}")
+        if t.device != q.device:
+            raise KasError(1, where, f"{name} is on {t.device}, q on {q.device}")
+    for name, t in ints.items():
+        if t is None:
+            continue
+        if t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous():
+            raise KasError(1, where, f"{name} must be a contiguous int32 tensor on {q.device}")
+    if q.device.type != "cuda":
+        raise KasError(1, where, "tensors must live on the GPU")
+
+
+def _new_out(q: torch.Tensor) -> torch.Tensor:
+    return torch.empty(q.shape, dtype=q.dtype, device=q.device)
+
+
 def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale: float,
-               tile: int = 32, pool_scope: int = 0, pool_op: int = 0, query_head_map: int = 0) -> KasDesc:
+               tile: int = 32, pool_scope: int = 0, pool_op: int = 0, query_head_map: int = 0,
+               o: Optional[torch.Tensor] = None) -> KasDesc:
     if prefill:
         B, Hq, N, D = q.shape
     else:
@@ -195,7 +252,8 @@ def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale:
         raise KasError(1, "desc", "k/v rows must be contiguous [.., N, D]")
     return make_desc(B, Hq, Hkv, D, N, pct, q.dtype, tile=tile, softmax_scale=scale,
                      kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1),
-                     pool_scope=pool_scope, pool_op=pool_op, query_head_map=query_head_map)
+                     pool_scope=pool_scope, pool_op=pool_op, query_head_map=query_head_map,
+                     q_strides=_row_strides(q, "q"), o_strides=_row_strides(q if o is None else o, "o"))
 
 
 def _cache(q, k, seq_lens, block_table, seq_len):
@@ -218,12 +276,12 @@ def _cache(q, k, seq_lens, block_table, seq_len):
     return over, c
 
 
-def _decode_desc(q, k, pct, scale, over, **kw) -> KasDesc:
+def _decode_desc(q, k, pct, scale, over, o, **kw) -> KasDesc:
     if over is None:
-        return _desc_from(q, k, pct, False, scale, **kw)
+        return _desc_from(q, k, pct, False, scale, o=o, **kw)
     B, Hq, D = q.shape
     return make_desc(B, Hq, over["n_kv_heads"], over["head_dim"], over["seq_len"], pct, q.dtype,
-                     softmax_scale=scale, **kw)
+                     softmax_scale=scale, q_strides=_row_strides(q, "q"), o_strides=_row_strides(o, "o"), **kw)
 
 
 def _ws_kv(desc, cache, op, ws, device):
@@ -243,17 +301,18 @@ def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, w
     """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hs,kd], o [B,Hq,D]); Hs = Hkv, or 1
     with pool_scope=1 (one set pooled over all heads). seq_lens (device int32 [B])
     gives each sequence's length; block_table (device int32 [B, max_pages]) makes
-    k, v page pools [num_pages, Hkv, P, D] (then seq_len = the longest sequence)."""
+    k, v page pools [num_pages, Hkv, P, D] (then seq_len = the longest sequence).
+    q and o may be strided views with a contiguous head_dim."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("decode_anchor", q, k, v, o, idx_out=idx_out, seq_lens=seq_lens, block_table=block_table)
     over, cache = _cache(q, k, seq_lens, block_table, seq_len)
-    desc = _decode_desc(q, k, pct, scale, over, pool_scope=pool_scope, pool_op=pool_op)
+    desc = _decode_desc(q, k, pct, scale, over, o, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "decode_anchor", "k and v must share strides")
     kd = decode_k(desc.seq_len, pct)
     if idx_out is None:
         hs = 1 if pool_scope else desc.n_kv_heads
         idx_out = torch.empty((desc.batch, hs, kd), dtype=torch.int32, device=q.device)
-    if o is None:
-        o = torch.empty_like(q)
     ws = _ws_kv(desc, cache, OP_DECODE_ANCHOR, ws, q.device)
     if cache is None:
         rc = _load().kas_decode_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
@@ -270,12 +329,13 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
     """anchor_idx [B,Hkv_a,kd] int32 (device), head_map int32 [Hkv] (device) or None;
     with query_head_map, head_map holds one entry per query head [Hq]. Cache
     arguments as in decode_anchor."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("decode_reuse", q, k, v, o, anchor_idx=anchor_idx, head_map=head_map, seq_lens=seq_lens,
+                   block_table=block_table)
     over, cache = _cache(q, k, seq_lens, block_table, seq_len)
-    desc = _decode_desc(q, k, pct, scale, over, query_head_map=int(query_head_map))
+    desc = _decode_desc(q, k, pct, scale, over, o, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "decode_reuse", "k and v must share strides")
-    if o is None:
-        o = torch.empty_like(q)
     ws = _ws_kv(desc, cache, OP_DECODE_REUSE, ws, q.device)
     if cache is None:
         rc = _load().kas_decode_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
@@ -289,17 +349,18 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
     return o
 
 
-def _prefill_desc(q, k, pct, scale, seq_lens, block_table, **kw):
+def _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, **kw):
     """(descriptor, KasKvCache or None) of a prefill call. With block_table
     (device int32 [B, max_pages]), k and v are page pools [num_pages, Hkv, P, D]
     and the prompt length N comes from q [B, Hq, N, D]."""
     if block_table is None:
-        desc = _desc_from(q, k, pct, True, scale, **kw)
+        desc = _desc_from(q, k, pct, True, scale, o=o, **kw)
         cache = None if seq_lens is None else KasKvCache(seq_lens.data_ptr(), None, 0, 0, 0, 0, 0)
         return desc, cache
     over, cache = _cache(q, k, seq_lens, block_table, q.shape[2])
     B, Hq, N, D = q.shape
-    desc = make_desc(B, Hq, over["n_kv_heads"], over["head_dim"], N, pct, q.dtype, softmax_scale=scale, **kw)
+    desc = make_desc(B, Hq, over["n_kv_heads"], over["head_dim"], N, pct, q.dtype, softmax_scale=scale,
+                     q_strides=_row_strides(q, "q"), o_strides=_row_strides(o, "o"), **kw)
     return desc, cache
 
 
@@ -309,8 +370,11 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
     """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 or fp16 -> (idx int32 [B,Hs,total] CSR,
     o [B,Hq,N,D]); Hs as in decode_anchor. seq_lens (device int32 [B]) gives each
     prompt's length; block_table (device int32 [B, max_pages]) makes k, v page
-    pools [num_pages, Hkv, P, D]."""
-    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, pool_scope=pool_scope, pool_op=pool_op)
+    pools [num_pages, Hkv, P, D]. q and o may be strided views (for example the
+    [B,N,Hq,D] projection output transposed) with a contiguous head_dim."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("prefill_anchor", q, k, v, o, idx_out=idx_out, seq_lens=seq_lens, block_table=block_table)
+    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, pool_scope=pool_scope, pool_op=pool_op)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_anchor", "k and v must share strides")
     total = int(prefill_offsets(desc)[-1])
@@ -318,8 +382,6 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
         hs = 1 if pool_scope else desc.n_kv_heads
         idx_out = torch.empty((desc.batch, hs, max(total, 1)), dtype=torch.int32,
                               device=q.device)
-    if o is None:
-        o = torch.empty_like(q)
     ws = _ws_kv(desc, c, OP_PREFILL_ANCHOR, ws, q.device)
     if c is None:
         rc = _load().kas_prefill_anchor(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out),
@@ -333,12 +395,13 @@ def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, 
 
 def prefill_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None, ws=None,
                   query_head_map: bool = False, seq_lens=None, block_table=None) -> torch.Tensor:
-    """head_map as in decode_reuse; cache arguments as in prefill_anchor."""
-    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, query_head_map=int(query_head_map))
+    """head_map as in decode_reuse; cache arguments and strides as in prefill_anchor."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("prefill_reuse", q, k, v, o, anchor_idx=anchor_idx, head_map=head_map, seq_lens=seq_lens,
+                   block_table=block_table)
+    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "prefill_reuse", "k and v must share strides")
-    if o is None:
-        o = torch.empty_like(q)
     ws = _ws_kv(desc, c, OP_PREFILL_REUSE, ws, q.device)
     if c is None:
         rc = _load().kas_prefill_reuse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
@@ -356,12 +419,12 @@ def decode_dense(q, k, v, scale: float = 0.0, o=None, ws=None, seq_lens=None, bl
                  seq_len=None) -> torch.Tensor:
     """Dense decode attention over all keys: q [B,Hq,D], k/v [B,Hkv,N,D] -> o [B,Hq,D].
     Cache arguments as in decode_anchor."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("decode_dense", q, k, v, o, seq_lens=seq_lens, block_table=block_table)
     over, cache = _cache(q, k, seq_lens, block_table, seq_len)
-    desc = _decode_desc(q, k, 100, scale, over)
+    desc = _decode_desc(q, k, 100, scale, over, o)
     if k.stride() != v.stride():
         raise KasError(1, "decode_dense", "k and v must share strides")
-    if o is None:
-        o = torch.empty_like(q)
     ws = _ws_kv(desc, cache, OP_DECODE_DENSE, ws, q.device)
     if cache is None:
         rc = _load().kas_decode_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws),
@@ -377,11 +440,11 @@ def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None, block_tabl
                   ws=None) -> torch.Tensor:
     """Dense causal attention: q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 or fp16 -> o [B,Hq,N,D].
     Cache arguments as in prefill_anchor (only a paged call needs a workspace)."""
-    desc, c = _prefill_desc(q, k, 100, scale, seq_lens, block_table)
+    o = _new_out(q) if o is None else o
+    _check_tensors("prefill_dense", q, k, v, o, seq_lens=seq_lens, block_table=block_table)
+    desc, c = _prefill_desc(q, k, 100, scale, seq_lens, block_table, o)
     if k.stride() != v.stride():
         raise KasError(1, "prefill_dense", "k and v must share strides")
-    if o is None:
-        o = torch.empty_like(q)
     if c is None:
         rc = _load().kas_prefill_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), None, 0, _stream(q))
     else:
@@ -399,16 +462,17 @@ def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx
     set at a larger percentage), head_map [Hkv] or None -> (idx int32 [B, Hkv, kappa],
     o [B, Hq, D]) with kappa this layer's own k for pct. With block_table, k and v are
     page pools as in decode_anchor (seq_len = the sequences' common length)."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("decode_refine", q, k, v, o, pool_idx=pool_idx, head_map=head_map, idx_out=idx_out,
+                   block_table=block_table)
     over, cache = _cache(q, k, None, block_table, seq_len)
-    desc = _decode_desc(q, k, pct, scale, over)
+    desc = _decode_desc(q, k, pct, scale, over, o)
     if k.stride() != v.stride():
         raise KasError(1, "decode_refine", "k and v must share strides")
     n_pool = pool_idx.shape[2]
     kappa = decode_k(desc.seq_len, pct)
     if idx_out is None:
         idx_out = torch.empty((desc.batch, desc.n_kv_heads, kappa), dtype=torch.int32, device=q.device)
-    if o is None:
-        o = torch.empty_like(q)
     L = _load()
     cref = None if cache is None else ctypes.byref(cache)
     if ws is None:

@@ -4,6 +4,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "../../include/kascade.h"
+
 namespace kas {
 
 // Names under which kernel timings are reported (kas_profile_query).
@@ -30,6 +32,9 @@ enum KernelId {
   K_COUNT_
 };
 const char* kernel_name(int id);
+
+// Current value of a tuning option (kas_option_t), -1 when it is at its default.
+int64_t option_value(int id);
 
 // Wraps every launch: optional timing + launch error check. begin() takes a
 // pair of events when profiling is on; launch() then passes them to the
@@ -63,6 +68,8 @@ struct DecodeArgs {
   const void* v;
   void* o;
   int64_t kv_bstride, kv_hstride;   // elements
+  int64_t q_bstride, q_hstride;     // elements between batch rows / query heads of q
+  int64_t o_bstride, o_hstride;     // the same for o
   int B, Hq, Hkv, D, G;
   int64_t N;
   float scale_log2;                 // softmax scale * log2(e)

@@ -16,6 +16,8 @@ struct PrefillArgs {
   const void* v;
   void* o;
   int64_t kv_bstride, kv_hstride;   // elements
+  int64_t q_bstride, q_hstride, q_tstride;   // elements between batch rows / query heads / tokens of q
+  int64_t o_bstride, o_hstride, o_tstride;   // the same for o
   int B, Hq, Hkv, D, G, T, pct;
   int64_t N;
   float scale_log2;

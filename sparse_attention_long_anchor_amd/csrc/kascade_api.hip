@@ -117,6 +117,7 @@ struct Shape {
   int qmap;                         // reuse: head_map per query head (kas_desc_t.query_head_map)
   float scale;
   int64_t kv_hs, kv_bs;
+  int64_t q_bs, q_hs, q_ts, o_bs, o_hs, o_ts;   // element strides of q and o
   size_t esize;
 };
 
@@ -173,6 +174,31 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   const int64_t vec = 16 / (int64_t)s.esize;
   if (s.kv_hs % vec || s.kv_bs % vec)
     return fail(KAS_ERR_INVALID_ARGUMENT, "kv strides must be multiples of 16 bytes");
+  // q and o: [B, Hq, (N,) D] by default; given strides replace the defaults
+  const int64_t rows = prefill ? s.N : 1;
+  const int64_t dflt[3] = {(int64_t)s.Hq * rows * s.D, rows * s.D, s.D};
+  const int64_t qs[3] = {d->q_batch_stride, d->q_head_stride, d->q_token_stride};
+  const int64_t os[3] = {d->o_batch_stride, d->o_head_stride, d->o_token_stride};
+  int64_t* qdst[3] = {&s.q_bs, &s.q_hs, &s.q_ts};
+  int64_t* odst[3] = {&s.o_bs, &s.o_hs, &s.o_ts};
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || os[i] < 0 || qs[i] % vec || os[i] % vec)
+      return fail(KAS_ERR_INVALID_ARGUMENT, "q/o strides must be 0 or positive multiples of 16 bytes");
+    *qdst[i] = qs[i] ? qs[i] : dflt[i];
+    *odst[i] = os[i] ? os[i] : dflt[i];
+  }
+  // o rows must not overlap: with the dimensions of more than one entry in
+  // ascending stride order, each stride must clear the span of the smaller ones
+  {
+    struct Dim { int64_t stride, size; } dims[3] = {{s.o_bs, s.B}, {s.o_hs, s.Hq}, {s.o_ts, rows}};
+    std::sort(dims, dims + 3, [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
+    int64_t span = s.D;
+    for (const Dim& dm : dims) {
+      if (dm.size <= 1) continue;
+      if (dm.stride < span) return fail(KAS_ERR_INVALID_ARGUMENT, "o strides make output rows overlap");
+      span = dm.stride * (dm.size - 1) + span;
+    }
+  }
   return KAS_OK;
 }
 
@@ -188,11 +214,12 @@ static kas_status_t check_ptr(const void* p, const char* name) {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  int x = atoi(v);
-  return x > 0 ? x : dflt;
+// ------------------------------------------------------------------ tuning options
+
+static std::atomic<int64_t> g_options[KAS_OPT_COUNT_] = {{-1}, {-1}, {-1}, {-1}};
+
+int64_t option_value(int id) {
+  return (id >= 0 && id < KAS_OPT_COUNT_) ? g_options[id].load(std::memory_order_relaxed) : -1;
 }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
@@ -215,7 +242,7 @@ static int device_cus() {
 // so one wave of workgroups covering every compute unit once is enough:
 // splits per (b, g) = CUs / (B * Hkv), at most kMaxSplitRows rows each.
 static int decode_split_rows(int64_t units, int64_t kk) {
-  int r = env_int("KAS_DECODE_SPLIT_ROWS", 0);
+  int r = (int)option_value(KAS_OPT_DECODE_SPLIT_ROWS);
   if (r <= 0) {
     const int64_t splits = std::max<int64_t>(1, device_cus() / std::max<int64_t>(1, units));
     int64_t per = (kk + splits - 1) / splits;
@@ -227,11 +254,8 @@ static int decode_split_rows(int64_t units, int64_t kk) {
   if (r < 16) r = 16;
   return r;
 }
-static int decode_score_rows() {
-  int r = env_int("KAS_DECODE_SCORE_ROWS", 1024);
-  r = (r + 63) / 64 * 64;
-  return r > kScoreMaxRows ? kScoreMaxRows : r;
-}
+// Keys per scoring workgroup (512, 2048 and 4096 measured slower at 128K).
+static int decode_score_rows() { return 1024; }
 
 struct DecodePlan {
   int64_t kk;
@@ -343,6 +367,8 @@ static void fill_decode_args(const Shape& s, const DecodePlan& p, bool anchor, c
   memset(&a, 0, sizeof(a));
   a.kvdiv = 1;
   a.kv_bstride = s.kv_bs; a.kv_hstride = s.kv_hs;
+  a.q_bstride = s.q_bs; a.q_hstride = s.q_hs;
+  a.o_bstride = s.o_bs; a.o_hstride = s.o_hs;
   a.B = s.B; a.Hq = s.Hq; a.Hkv = s.Hkv; a.D = s.D; a.G = s.G; a.N = s.N;
   a.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
   a.kk = p.kk;
@@ -415,6 +441,11 @@ static hipError_t prefill_paged_kv(const CacheView& cv, const Shape& s, const vo
   a.kv_hstride = s.N * s.D;
   a.kv_bstride = (int64_t)s.Hkv * s.N * s.D;
   return launch_prefill_page_copy(c, ctx);
+}
+
+static void set_qo_strides(PrefillArgs& a, const Shape& s) {
+  a.q_bstride = s.q_bs; a.q_hstride = s.q_hs; a.q_tstride = s.q_ts;
+  a.o_bstride = s.o_bs; a.o_hstride = s.o_hs; a.o_tstride = s.o_ts;
 }
 
 static kas_status_t hip_fail(hipError_t e, const char* where) {
@@ -589,6 +620,7 @@ kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t*
   if ((st = check_ws(ws, ws_bytes, prefill_need(base, s, cv)))) return st;
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, (char*)ws, true);
+  set_qo_strides(a, s);
   a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o; a.idx_out = idx_out;
   a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
@@ -637,6 +669,7 @@ kas_status_t kas_prefill_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   if ((st = check_ws(ws, ws_bytes, prefill_need(base, s, cv)))) return st;
   PrefillArgs a;
   fill_prefill_args(a, sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, sr.scale, sr.kv_bs, sr.kv_hs, (char*)ws, false);
+  set_qo_strides(a, sr);
   a.dtype = s.dtype;
   a.kvdiv = s.qmap ? s.G : 1;
   a.seq_lens = cv.seq_lens;
@@ -707,6 +740,7 @@ kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   if ((st = check_ws(ws, ws_bytes, prefill_need(0, s, cv)))) return st;   // 0 bytes unless paged
   PrefillArgs a;
   fill_prefill_args(a, s.B, s.Hq, s.Hkv, s.D, s.N, s.pct, s.scale, s.kv_bs, s.kv_hs, nullptr, false);
+  set_qo_strides(a, s);
   a.dtype = s.dtype;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.offsets = nullptr; a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.total = 0;
@@ -836,7 +870,7 @@ kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   return KAS_OK;
 }
 
-const char* kas_status_string(kas_status_t status) {
+const char* kas_status_string(int32_t status) {
   switch (status) {
     case KAS_OK: return "ok";
     case KAS_ERR_INVALID_ARGUMENT: return "invalid argument";
@@ -848,6 +882,29 @@ const char* kas_status_string(kas_status_t status) {
 }
 
 const char* kas_last_error(void) { return kas::t_last_error.c_str(); }
+
+kas_status_t kas_set_option(int32_t option, int64_t value) {
+  if (option < 0 || option >= KAS_OPT_COUNT_) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
+  if (value != -1) {
+    bool ok = true;
+    switch (option) {
+      case KAS_OPT_DECODE_SPLIT_ROWS: ok = value >= 16 && value <= 2048; break;
+      case KAS_OPT_DECODE_SELECT_ONE_PASS: ok = value == 0 || value == 1; break;
+      case KAS_OPT_PREFILL_POOL_MB: ok = value >= 1 && value <= (int64_t(1) << 30); break;
+      case KAS_OPT_PREFILL_SELECT_CAP: ok = value >= 0 && value <= 8192; break;
+    }
+    if (!ok) return fail(KAS_ERR_INVALID_ARGUMENT, "value %lld out of range for option %d", (long long)value, option);
+  }
+  kas::g_options[option].store(value, std::memory_order_relaxed);
+  return KAS_OK;
+}
+
+kas_status_t kas_get_option(int32_t option, int64_t* value) {
+  if (option < 0 || option >= KAS_OPT_COUNT_) return fail(KAS_ERR_INVALID_ARGUMENT, "unknown option %d", option);
+  if (!value) return fail(KAS_ERR_INVALID_ARGUMENT, "value is NULL");
+  *value = kas::g_options[option].load(std::memory_order_relaxed);
+  return KAS_OK;
+}
 
 kas_status_t kas_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -202,11 +202,12 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N;
+  const int64_t lse_off = ((int64_t)b * a.Hq + h) * a.N;   // row statistics of this head
   u32x4 qb0[KC], qb1[KC];
   {
-    const E* q0 = (const E*)a.q + (qoff + kTile * t0 + n32) * D;
-    const E* q1 = (const E*)a.q + (qoff + kTile * (has1 ? t1 : t0) + n32) * D;
+    const E* qh = (const E*)a.q + b * a.q_bstride + h * a.q_hstride;
+    const E* q0 = qh + (int64_t)(kTile * t0 + n32) * a.q_tstride;
+    const E* q1 = qh + (int64_t)(kTile * (has1 ? t1 : t0) + n32) * a.q_tstride;
 #pragma unroll
     for (int c = 0; c < KC; ++c) { qb0[c] = ldg16(q0 + 16 * c + 8 * hh); qb1[c] = ldg16(q1 + 16 * c + 8 * hh); }
   }
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
     const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
     const float M = fmaxf(l > 0.f ? m : kNegInf, l2 > 0.f ? m2 : kNegInf);
     const float L = (l > 0.f ? l * exp2_fast(m - M) : 0.f) + (l2 > 0.f ? l2 * exp2_fast(m2 - M) : 0.f);
-    if (hh == 0) a.lse[qoff + kTile * t + n32] = M + log2f(L);
+    if (hh == 0) a.lse[lse_off + kTile * t + n32] = M + log2f(L);
   };
   finish(mr0, l0, t0);
   if (has1) finish(mr1, l1, t1);
@@ -417,19 +418,20 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N;
+  const int64_t lse_off = ((int64_t)b * a.Hq + h) * a.N;   // row statistics of this head
   u32x4 qa0[KC], qa1[KC];
   float lse0[16], lse1[16];
   {
     const int tq1 = has1 ? t1 : t0;
-    const E* q0 = (const E*)a.q + (qoff + kTile * t0 + n32) * D;
-    const E* q1 = (const E*)a.q + (qoff + kTile * tq1 + n32) * D;
+    const E* qh = (const E*)a.q + b * a.q_bstride + h * a.q_hstride;
+    const E* q0 = qh + (int64_t)(kTile * t0 + n32) * a.q_tstride;
+    const E* q1 = qh + (int64_t)(kTile * tq1 + n32) * a.q_tstride;
 #pragma unroll
     for (int c = 0; c < KC; ++c) { qa0[c] = ldg16(q0 + 16 * c + 8 * hh); qa1[c] = ldg16(q1 + 16 * c + 8 * hh); }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      lse0[r] = a.lse[qoff + kTile * t0 + mrow(r, hh)];
-      lse1[r] = a.lse[qoff + kTile * tq1 + mrow(r, hh)];
+      lse0[r] = a.lse[lse_off + kTile * t0 + mrow(r, hh)];
+      lse1[r] = a.lse[lse_off + kTile * tq1 + mrow(r, hh)];
     }
   }
   const E* kbase = (const E*)a.k + b * a.kv_bstride + g * a.kv_hstride;
@@ -811,11 +813,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   const int nsel = (kt + 31) / 32;
   const int nfull = kt / 32;
   const int tile_key0 = kTile * t;
-  const int64_t qoff = ((int64_t)b * a.Hq + h) * a.N + tile_key0;
   // Q fragments: B operand of S^T (lane: query n32, dims 16 c + 8 hh)
   u32x4 qf[KC];
   {
-    const E* qrow = (const E*)a.q + (qoff + n32) * D;
+    const E* qrow = (const E*)a.q + b * a.q_bstride + h * a.q_hstride + (int64_t)(tile_key0 + n32) * a.q_tstride;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = ldg16(qrow + 16 * c + 8 * hh);
   }
@@ -1039,13 +1040,13 @@ __global__ __launch_bounds__(64 * G, 2) void pre_attn_dma_kernel(PrefillArgs a) 
   step_any(nsel, std::integral_constant<int, 2>{});
   // normalise: 1/l of query q lives in lane q; output rows are mrow(r, hh)
   const float inv_l = 1.0f / xor32_add(l_run);
-  uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + qoff * D;
+  uint16_t* ob = reinterpret_cast<uint16_t*>(a.o) + b * a.o_bstride + h * a.o_hstride + (int64_t)tile_key0 * a.o_tstride;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float inv = __shfl(inv_l, mrow(r, hh));
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
-      ob[(int64_t)mrow(r, hh) * D + n32 + 32 * dc] = Ew<E>::bits(o[dc][r] * inv);
+      ob[(int64_t)mrow(r, hh) * a.o_tstride + n32 + 32 * dc] = Ew<E>::bits(o[dc][r] * inv);
   }
 }
 
@@ -1091,8 +1092,8 @@ __global__ __launch_bounds__(256) void pre_page_copy_kernel(PageCopyArgs c) {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 static int64_t pool_budget_floats() {
-  const char* v = getenv("KAS_PREFILL_POOL_MB");
-  int64_t mb = (v && atoll(v) > 0) ? atoll(v) : kPoolBudgetMBDefault;
+  const int64_t v = option_value(KAS_OPT_PREFILL_POOL_MB);
+  const int64_t mb = v > 0 ? v : kPoolBudgetMBDefault;
   return mb * (1 << 20) / 4;
 }
 
@@ -1156,10 +1157,10 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
   a.Hsel = Hkv;
   a.kvdiv = 1;
   PrefillPlan p = plan(B, Hq, Hkv, N, anchor);
-  // KAS_PREFILL_SELECT_CAP lowers the LDS candidate cap of the select (0 sends
+  // the tuning option lowers the LDS candidate cap of the select (0 sends
   // every tile through the in-place histogram passes)
-  const char* cap = getenv("KAS_PREFILL_SELECT_CAP");
-  a.sel_cap = cap ? std::min(std::max(atoi(cap), 0), kPreSelCap) : kPreSelCap;
+  const int64_t cap = option_value(KAS_OPT_PREFILL_SELECT_CAP);
+  a.sel_cap = cap >= 0 ? (int)std::min<int64_t>(cap, kPreSelCap) : kPreSelCap;
   if (!ws) return;                  // dense attention: no workspace
   a.offsets = (int32_t*)(ws + p.off_offsets);
   if (anchor) {

@@ -11,3 +11,19 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture
+def kas_options():
+    """Set library tuning options for one test; every option touched is put
+    back to its default afterwards."""
+    import sparse_attention_long_anchor_amd as kas
+    touched = []
+
+    def setter(option, value):
+        touched.append(option)
+        kas.set_option(option, value)
+
+    yield setter
+    for option in touched:
+        kas.set_option(option, -1)

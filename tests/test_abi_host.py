@@ -230,3 +230,88 @@ def test_refine_checks_without_gpu():
     varlen = b.KasKvCache(1 << 20, None, 0, 0, 0, 0, 0)
     assert L.kas_workspace_size_refine_kv(ctypes.byref(d), ctypes.byref(varlen), 4 * kappa, ctypes.byref(n)) == 2
     assert b"sequence lengths" in L.kas_last_error()
+
+
+def test_qo_stride_validation_without_gpu():
+    """q/o strides: 0 keeps the contiguous default, given strides must be
+    positive multiples of 16 bytes, and o's rows must not overlap (q may)."""
+    import torch
+    b = _kas()
+    L = b._load()
+    fake = ctypes.c_void_p(1 << 20)
+    B, Hq, Hkv, D, N = 2, 8, 2, 128, 64
+    base = b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16)
+    need = b.workspace_size(base, b.OP_PREFILL_REUSE)
+    # [B, N, Hq, D] transposed to [B, Hq, N, D]: batch N*Hq*D, head D, token Hq*D
+    tr = (N * Hq * D, D, Hq * D)
+    good = [b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, q_strides=tr, o_strides=tr),
+            b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, q_strides=(0, 0, 2 * D)),
+            # q may alias: every batch row reads the same queries
+            b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, q_strides=(0, N * D, D))]
+    for d in good:
+        assert b.workspace_size(d, b.OP_PREFILL_REUSE) == need
+    bad = [((-8, 0, 0), (0, 0, 0)), ((0, 0, 4), (0, 0, 0)), ((0, 0, 0), (0, 0, 12)),
+           ((0, 0, 0), (0, N * D, 64)),                      # o tokens overlap
+           ((0, 0, 0), (N * D, N * D, D)),                   # o batch rows land on head rows
+           ((0, 0, 0), (0, D, D))]                           # o heads and tokens collide
+    for qs, os_ in bad:
+        d = b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, q_strides=qs, o_strides=os_)
+        assert _status(lambda: b.workspace_size(d, b.OP_PREFILL_ANCHOR)) == 1, (qs, os_)
+        r = L.kas_prefill_reuse(ctypes.byref(d), fake, fake, fake, fake, Hkv, None, fake, fake, 1 << 30, None)
+        assert r == 1 and (b"stride" in L.kas_last_error() or b"overlap" in L.kas_last_error())
+    # decode has one token: its token stride is ignored, heads may sit far apart
+    dd = b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, q_strides=(Hq * 4 * D, 4 * D, 7 * 8),
+                     o_strides=(Hq * 2 * D, 2 * D, 0))
+    assert b.workspace_size(dd, b.OP_DECODE_REUSE) > 0
+    dd = b.make_desc(B, Hq, Hkv, D, N, 10, torch.bfloat16, o_strides=(0, 64, 0))   # o heads overlap
+    assert _status(lambda: b.workspace_size(dd, b.OP_DECODE_REUSE)) == 1
+
+
+def test_tuning_options_without_gpu():
+    b = _kas()
+    for opt in range(4):
+        assert b.get_option(opt) == -1
+    b.set_option(b.OPT_DECODE_SPLIT_ROWS, 64)
+    try:
+        assert b.get_option(b.OPT_DECODE_SPLIT_ROWS) == 64
+    finally:
+        b.set_option(b.OPT_DECODE_SPLIT_ROWS, -1)
+    assert b.get_option(b.OPT_DECODE_SPLIT_ROWS) == -1
+    for opt, val in [(b.OPT_DECODE_SPLIT_ROWS, 8), (b.OPT_DECODE_SPLIT_ROWS, 4096),
+                     (b.OPT_DECODE_SELECT_ONE_PASS, 2), (b.OPT_PREFILL_POOL_MB, 0),
+                     (b.OPT_PREFILL_SELECT_CAP, 8193), (4, 1), (-1, 1)]:
+        assert _status(lambda: b.set_option(opt, val)) == 1, (opt, val)
+    # a smaller pooled-score cap shrinks the prefill anchor workspace
+    import torch
+    d = b.make_desc(1, 32, 8, 128, 32768, 10, torch.bfloat16)
+    full = b.workspace_size(d, b.OP_PREFILL_ANCHOR)
+    b.set_option(b.OPT_PREFILL_POOL_MB, 64)
+    try:
+        assert b.workspace_size(d, b.OP_PREFILL_ANCHOR) < full
+    finally:
+        b.set_option(b.OPT_PREFILL_POOL_MB, -1)
+    assert b.workspace_size(d, b.OP_PREFILL_ANCHOR) == full
+
+
+def test_binding_rejects_mismatched_tensors_without_gpu():
+    """The binding checks dtypes, a contiguous head_dim and index dtypes
+    before any call reaches the library (CPU tensors: nothing is launched)."""
+    import torch
+    b = _kas()
+    q = torch.zeros(1, 8, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    with pytest.raises(b.KasError, match="dtype"):
+        b.prefill_dense(q, k.half(), v)
+    with pytest.raises(b.KasError, match="dtype"):
+        b.prefill_dense(q, k, v, o=torch.zeros(1, 8, 64, 128, dtype=torch.float16))
+    with pytest.raises(b.KasError, match="int32"):
+        b.prefill_reuse(q, k, v, torch.zeros(1, 2, 10, dtype=torch.int64), None, 10)
+    with pytest.raises(b.KasError):
+        b.prefill_dense(q, k, v)                       # CPU tensors
+    qt = torch.zeros(1, 8, 128, 64, dtype=torch.bfloat16).transpose(2, 3)   # head_dim strided
+    # [B, N, Hq, D] storage seen as [B, Hq, N, D] (batch 1: its stride is not used)
+    assert b._row_strides(q.transpose(1, 2).contiguous().transpose(1, 2), "q") == (0, 128, 8 * 128)
+    with pytest.raises(b.KasError, match="contiguous"):
+        b._row_strides(qt, "q")
+    assert b._row_strides(torch.zeros(1, 8, 128), "q") == (0, 128, 0)

@@ -135,10 +135,10 @@ def test_exact_ties_take_lowest_indices():
 
 
 @pytest.mark.parametrize("case", ["random_n40000", "all_tied_n70000"])
-def test_select_paths_agree(case, monkeypatch):
+def test_select_paths_agree(case, kas_options):
     """The chunked selection (per-chunk candidates of the first digit's bin,
     digits 2 and 3 resolved per row) and the one-workgroup-per-row kernel
-    (KAS_DECODE_SELECT=fused) give identical index sets and outputs, equal to
+    (option KAS_OPT_DECODE_SELECT_ONE_PASS) give identical index sets and outputs, equal to
     the oracle's. With every score tied the first digit's bin holds all N
     scores, more than the candidate list takes, so the resolve step sweeps the
     row instead; the kept keys are then the k lowest indices."""
@@ -151,7 +151,7 @@ def test_select_paths_agree(case, monkeypatch):
         k = torch.zeros_like(k)
     _say(f"[decode select paths] {case}")
     idx1, o1 = kas.decode_anchor(q, k, v, pct)
-    monkeypatch.setenv("KAS_DECODE_SELECT", "fused")
+    kas_options(kas.OPT_DECODE_SELECT_ONE_PASS, 1)
     idx2, o2 = kas.decode_anchor(q, k, v, pct)
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2) and torch.equal(o1, o2)
@@ -217,16 +217,13 @@ def test_workspace_contents_do_not_matter():
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("env", [{"KAS_DECODE_SPLIT_ROWS": "16"}, {"KAS_DECODE_SPLIT_ROWS": "16384"},
-                                 {"KAS_DECODE_GATHER": "staged"},
-                                 {"KAS_DECODE_GATHER": "staged", "KAS_DECODE_SPLIT_ROWS": "16"}],
-                         ids=["split16", "split_max", "staged", "staged_split16"])
-def test_split_and_kernel_variants(env, monkeypatch):
-    """Many splits (a merge over hundreds of partials), the largest split, and
-    the LDS-staged gather kernel all match the oracle."""
+@pytest.mark.parametrize("rows", [16, 2048], ids=["split16", "split_max"])
+def test_split_variants(rows, kas_options):
+    """Many splits (a merge over hundreds of partials) and the largest split
+    both match the oracle."""
     kas = _kas()
-    for key, val in env.items():
-        monkeypatch.setenv(key, val)
+    kas_options(kas.OPT_DECODE_SPLIT_ROWS, rows)
+    env = {"split_rows": rows}
     B, Hq, Hkv, D, N, pct = 1, 32, 8, 128, 30000, 10
     w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=41)
     q, k, v = inputgen.layer_inputs(w, 0, DEV)

@@ -174,29 +174,29 @@ def test_prefill_scores_far_above_first_block():
     _check_tiles(w, q, k, v, pct, gidx, go, range(N // 32), "far_scores")
 
 
-def test_prefill_select_without_lds_candidates(monkeypatch):
-    """KAS_PREFILL_SELECT_CAP=0 sends every tile's selection through the
+def test_prefill_select_without_lds_candidates(kas_options):
+    """A select cap of 0 (KAS_OPT_PREFILL_SELECT_CAP) sends every tile's selection through the
     in-place histogram passes over the pooled row (the path a first-digit bin
     too large for LDS takes); the index sets and outputs are bit-identical."""
     kas = _kas()
     w = inputgen.custom("prefill", 1, 8, 2, 128, 2048, "bf16", wid=62)
     q, k, v = inputgen.layer_inputs(w, 0, DEV)
     gidx, go = kas.prefill_anchor(q, k, v, 10)
-    monkeypatch.setenv("KAS_PREFILL_SELECT_CAP", "0")
+    kas_options(kas.OPT_PREFILL_SELECT_CAP, 0)
     gidx2, go2 = kas.prefill_anchor(q, k, v, 10)
     torch.cuda.synchronize()
     assert torch.equal(gidx, gidx2) and torch.equal(go, go2)
     _check_tiles(w, q, k, v, 10, gidx2, go2, (1, 17, 40, 63), "select_in_place")
 
 
-def test_prefill_pooling_in_tile_ranges(monkeypatch):
+def test_prefill_pooling_in_tile_ranges(kas_options):
     """A small pooled-score budget splits pooling and selection into many
     tile ranges; the index sets and outputs are bit-identical to one range."""
     kas = _kas()
     w = inputgen.custom("prefill", 1, 8, 2, 128, 2048, "bf16", wid=61)
     q, k, v = inputgen.layer_inputs(w, 0, DEV)
     gidx, go = kas.prefill_anchor(q, k, v, 10)
-    monkeypatch.setenv("KAS_PREFILL_POOL_MB", "1")     # ~262K floats per range
+    kas_options(kas.OPT_PREFILL_POOL_MB, 1)            # ~262K floats per range
     gidx2, go2 = kas.prefill_anchor(q, k, v, 10)
     torch.cuda.synchronize()
     assert torch.equal(gidx, gidx2) and torch.equal(go, go2)
