@@ -676,9 +676,9 @@ def paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas):
         ids = torch.randperm(B * (N // P), generator=g).to(torch.int32).view(B, N // P).to(dev)
         kp0, vp0, kp1, vp1 = (_page_pool(torch, x, ids, P) for x in (k0, v0, k1, v1))
         kw = dict(block_table=ids)
-        wsa = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids),
+        wsa = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids, q0),
                                  kas.OP_PREFILL_ANCHOR, None, dev)
-        wsr = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids),
+        wsr = kas.binding._ws_kv(*kas.binding._prefill_desc(q0, kp0, wp.topk_pct, 0.0, None, ids, q0),
                                  kas.OP_PREFILL_REUSE, None, dev)
         ta, tr = _alternate(torch,
                             lambda: kas.prefill_anchor(q0, kp0, vp0, wp.topk_pct, idx_out=idx, o=o, ws=wsa, **kw),
@@ -701,7 +701,7 @@ def paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas):
 
 def _kv_desc(kas, q, kp, ids, N, w):
     over, cache = kas.binding._cache(q, kp, None, ids, N)
-    return kas.binding._decode_desc(q, kp, w.topk_pct, 0.0, over), cache
+    return kas.binding._decode_desc(q, kp, w.topk_pct, 0.0, over, q), cache
 
 
 def fp16_timings(wd, wp, dec_state, pre_state, dev, torch, inputgen, kas):

@@ -132,7 +132,7 @@ def test_paged_calls_in_a_graph():
     idx = torch.empty((wd.batch, wd.n_kv_heads, kd), dtype=torch.int32, device=DEV)
     o, orr = torch.empty_like(q), torch.empty_like(q)
     over, cache = kas.binding._cache(q, kp, lens, bt, wd.seq_len)
-    dd = kas.binding._decode_desc(q, kp, wd.topk_pct, 0.0, over)
+    dd = kas.binding._decode_desc(q, kp, wd.topk_pct, 0.0, over, o)
     ws_a = kas.binding._ws_kv(dd, cache, kas.OP_DECODE_ANCHOR, None, DEV)
     ws_r = kas.binding._ws_kv(dd, cache, kas.OP_DECODE_REUSE, None, DEV)
     hm = torch.as_tensor(np.array([1, 0], np.int32), device=DEV)
@@ -141,7 +141,7 @@ def test_paged_calls_in_a_graph():
     pkp, pvp, pbt = _paged(pk, pv, 32, seed=6)
     plens = torch.as_tensor(np.array([512, 320], np.int32), device=DEV)
     po = torch.empty_like(pq)
-    pdesc, pcache = kas.binding._prefill_desc(pq, pkp, 100, 0.0, plens, pbt)
+    pdesc, pcache = kas.binding._prefill_desc(pq, pkp, 100, 0.0, plens, pbt, pq)
     ws_p = kas.binding._ws_kv(pdesc, pcache, kas.OP_PREFILL_DENSE, None, DEV)
     _say("[graph paged] decode anchor + reuse (P 64), prefill dense (P 32), varlen")
 
