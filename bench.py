@@ -136,57 +136,209 @@ def run_prefill_step(w, st, inputgen, kas, events=None):
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(wd, dec_state, wp, pre_state, budget_s, inputgen):
-    """Time the (untuned) oracle on a bounded sample of the same workloads."""
-    import numpy as np
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads():
+    return int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+
+
+def cpu_decode_sample(w, st, budget_s, inputgen):
+    """The (untuned) oracle over the first layers of a decode schedule (full
+    B, Hkv, N per layer) until the budget is spent: algorithmic GB/s."""
     import oracle
-    layers, idx, *_ = dec_state
-    reuse_b, anchor_b, _ = decode_work(wd, oracle.decode_k(wd.seq_len, wd.topk_pct))
-    maps = inputgen.head_maps(wd)
+    layers = st[0]
+    reuse_b, anchor_b, _ = decode_work(w, oracle.decode_k(w.seq_len, w.topk_pct))
+    maps = inputgen.head_maps(w)
     f = lambda t: t.float().cpu().numpy()
-    done_bytes, spent, n_layers = 0, 0.0, 0
-    cur_idx = None
+    done, spent, n, cur = 0, 0.0, 0, None
     for l, (q, k, v, _) in enumerate(layers):
-        if spent > budget_s and n_layers >= 2:
+        if n >= 2 and spent > budget_s:
             break
         qn, kn, vn = f(q), f(k), f(v)
         t0 = time.perf_counter()
-        if l in wd.anchors:
-            cur_idx, _, _ = oracle.decode_anchor(qn, kn, vn, wd.topk_pct)
-            done_bytes += anchor_b
+        if l in w.anchors:
+            cur, _, _ = oracle.decode_anchor(qn, kn, vn, w.topk_pct)
+            done += anchor_b
         else:
-            oracle.decode_reuse(qn, kn, vn, cur_idx, maps[l])
-            done_bytes += reuse_b
+            oracle.decode_reuse(qn, kn, vn, cur, maps[l])
+            done += reuse_b
         spent += time.perf_counter() - t0
-        n_layers += 1
-        del qn, kn, vn
-    dec_gbs = done_bytes / spent / 1e9
-    # prefill: anchor layer 0 on the last tile and on one mid tile
-    pl = pre_state[0][0]
-    q, k, v, _ = pl
-    kn, vn = f(k), f(v)
+        n += 1
+    return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "layers": n, "seconds": round(spent, 2),
+            "sample": f"{w.name}: first {n} of {w.n_layers} layers (full B, Hkv, N each)"}
+
+
+def cpu_prefill_sample(w, st, tiles, inputgen):
+    """The oracle on a few tiles of the schedule's first anchor layer and of
+    the first reuse layer after it (all KV heads): measured TFLOP/s, and the
+    full layer's time extrapolated linearly in flops (labelled as such)."""
+    import oracle
+    layers, idx = st[0], st[1]
+    f = lambda t: t.float().cpu().numpy()
+    D, rows = w.head_dim, w.batch * w.n_q_heads * 32
+    T = w.seq_len // 32
+    off = oracle.prefill_offsets(w.seq_len, 32, w.topk_pct)
+    work = prefill_work(w, off)
+    res = {}
+    a0 = min(w.anchors)
+    r0 = next(l for l in range(w.n_layers) if l not in w.anchors)
+    maps = inputgen.head_maps(w)
+    anc_idx = idx[a0].cpu().numpy()
+    for kind, layer in (("anchor_layer", a0), ("reuse_layer", r0)):
+        q, k, v, _ = layers[layer]
+        kn, vn = f(k), f(v)
+        flops, spent = 0.0, 0.0
+        for t in tiles:
+            qr = f(q[:, :, 32 * t: 32 * t + 32])
+            kt = int(off[t + 1] - off[t])
+            t0 = time.perf_counter()
+            if kind == "anchor_layer":
+                oracle.prefill_anchor(qr, kn, vn, w.topk_pct, t0=t, t1=t + 1)
+                flops += 2 * D * rows * (32 * t + 16.5) + 2 * D * rows * 32 * t + 4 * D * rows * (kt + 16.5)
+            else:
+                oracle.prefill_reuse(qr, kn, vn, anc_idx, maps[layer], w.topk_pct, t0=t, t1=t + 1)
+                flops += 4 * D * rows * (kt + 16.5)
+            spent += time.perf_counter() - t0
+        full = (work["prefill_stats"] + work["prefill_pool"] + work["prefill_attn"]) if kind == "anchor_layer" \
+            else work["prefill_attn"]
+        rate = flops / spent
+        res[kind] = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "tiles": list(tiles), "of_tiles": T,
+                     "seconds": round(spent, 2),
+                     "extrapolated_full_layer_s": {"value": round(full / rate, 1),
+                                                   "note": "linear in flops from the measured tiles, not measured"}}
+    return res
+
+
+def cpu_baseline(wd, dec_state, wp, pre_state, budget_s, inputgen, extra):
+    """The oracle (plain fp64 C with OpenMP, never tuned) on bounded samples of
+    the same resident workloads, on this host's cores; `value` is the 128K
+    decode schedule's algorithmic GB/s (the metric), the rest are per config."""
+    dec = cpu_decode_sample(wd, dec_state, budget_s * 0.4, inputgen)
     T = wp.seq_len // 32
-    tiles = [T - 1, T // 2]
-    flops, tp = 0, 0.0
-    D, G = wp.head_dim, wp.group
-    for t in tiles:
-        qr = f(q[:, :, 32 * t: 32 * t + 32])
-        t0 = time.perf_counter()
-        oracle.prefill_anchor(qr, kn, vn, wp.topk_pct, t0=t, t1=t + 1)
-        tp += time.perf_counter() - t0
-        kt = oracle.topk_count(32 * t, wp.topk_pct)
-        rows = wp.batch * wp.n_q_heads * 32
-        flops += 2 * D * rows * (32 * t + 16.5)      # row statistics (causal)
-        flops += 2 * D * rows * 32 * t               # pooled scores
-        flops += 4 * D * rows * (kt + 16.5)          # output over set + diagonal
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    pre = cpu_prefill_sample(wp, pre_state, (T - 1, T // 2), inputgen)
+    per = dict(extra)
+    per[wd.name] = dec
+    per[wp.name] = pre
     return {
-        "value": round(dec_gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"{wd.name}: first {n_layers} layers of the schedule (full B,Hkv,N per layer); "
-                  f"oracle fp64 C with OpenMP; {spent:.1f} s",
-        "prefill": {"value": round(flops / tp / 1e12, 6), "unit": "TFLOP/s",
-                    "sample": f"{wp.name} anchor layer 0, tiles {tiles} (all KV heads); {tp:.1f} s"},
+        "value": dec["value"], "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "sample": f"{dec['sample']}; oracle fp64 C with OpenMP; {dec['seconds']} s",
+        "prefill": {"value": pre["anchor_layer"]["value"], "unit": "TFLOP/s",
+                    "sample": f"{wp.name} anchor layer {min(wp.anchors)}, tiles {pre['anchor_layer']['tiles']} "
+                              f"(all KV heads)"},
+        "per_config": per,
     }
+
+
+# ---------------------------------------------------------------- the other workloads
+
+OTHER_CONFIGS = ("tiny_decode_2k", "llama8b_decode_32k", "qwen8b_prefill_32k")
+
+
+def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
+    """One workload's own schedule (every layer resident): `warmup` untimed
+    steps, `steps` steps with events around each step, the same steps with an
+    event pair around every layer (anchor / reuse layer times), and one pass
+    with the library's per-launch timing for the kernels' rooflines. The
+    oracle is timed on a sample of the same layers when cpu_budget > 0."""
+    w = inputgen.WORKLOADS[name]
+    dec = w.phase == "decode"
+    log(f"[bench] config {name}: generating {w.n_layers} layers")
+    st = (build_decode if dec else build_prefill)(w, dev, torch, inputgen, kas)
+    run = run_decode_step if dec else run_prefill_step
+    for _ in range(warmup):
+        run(w, st, inputgen, kas)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        run(w, st, inputgen, kas)
+        e[1].record()
+    torch.cuda.synchronize()
+    step_ms = _mean([a.elapsed_time(b) for a, b in ev])
+    lay = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(w.n_layers)] for _ in range(steps)]
+    for s_ in range(steps):
+        run(w, st, inputgen, kas, lay[s_])
+    torch.cuda.synchronize()
+    per_layer = [_mean([lay[s_][l][0].elapsed_time(lay[s_][l][1]) for s_ in range(steps)]) for l in range(w.n_layers)]
+    anc = [per_layer[l] for l in range(w.n_layers) if l in w.anchors]
+    reu = [per_layer[l] for l in range(w.n_layers) if l not in w.anchors]
+    kas.profile_reset()
+    kas.profile_enable(True)
+    run(w, st, inputgen, kas)
+    torch.cuda.synchronize()
+    kas.profile_enable(False)
+    kern = {}
+    for kname in kas.profile_names():
+        ms, n = kas.profile_query(kname)
+        if n:
+            kern[kname] = (ms, n)
+    rec = {"workload": name, "batch": w.batch, "seq_len": w.seq_len, "layers": w.n_layers,
+           "anchors": list(w.anchors), "topk_pct": w.topk_pct, "dtype": w.dtype, "steps": steps}
+    roof = []
+    if dec:
+        kd = st[5]
+        reuse_b, anchor_b, kern_b = decode_work(w, kd)
+        step_b = len(anc) * anchor_b + len(reu) * reuse_b
+        rec.update({
+            "k": kd,
+            "us_per_layer": {"anchor": round(1e3 * _mean(anc), 3), "reuse": round(1e3 * _mean(reu), 3),
+                             "schedule_mean": round(1e3 * step_ms / w.n_layers, 3)},
+            "GB_per_s": {"anchor": _rate(anchor_b, _mean(anc) * 1e-3, 1e9),
+                         "reuse": _rate(reuse_b, _mean(reu) * 1e-3, 1e9),
+                         "step": _rate(step_b, step_ms * 1e-3, 1e9)},
+            "ms_per_step": round(step_ms, 4),
+            "tokens_per_s": round(w.batch / (step_ms * 1e-3), 2)})
+        ops = {"decode_attn": len(reu), "decode_attn_anchor": len(anc), "decode_score": len(anc)}
+        for kname, b in kern_b.items():
+            if kname in kern:
+                roof.append(_roof_entry(kname, "hbm", b * ops[kname], kern[kname], HBM_PEAK_GBS, "GB/s", 1e9))
+    else:
+        off = st[5]
+        work = prefill_work(w, off)
+        anc_flops = work["prefill_stats"] + work["prefill_pool"] + work["prefill_attn"]
+        rec.update({
+            "index_entries_per_kv_head": int(off[-1]),
+            "ms_per_layer": {"anchor": round(_mean(anc), 4), "reuse": round(_mean(reu), 4),
+                             "schedule_mean": round(step_ms / w.n_layers, 4)},
+            "TFLOP_per_s": {"anchor_layer": _rate(anc_flops, _mean(anc) * 1e-3, 1e12),
+                            "reuse_layer": _rate(work["prefill_attn"], _mean(reu) * 1e-3, 1e12)},
+            "ms_per_step": round(step_ms, 3),
+            "tokens_per_s": round(w.batch * w.seq_len / (step_ms * 1e-3), 1)})
+        ops = {"prefill_stats": len(anc), "prefill_pool": len(anc), "prefill_attn": w.n_layers}
+        for kname, fl in work.items():
+            if kname in kern:
+                roof.append(_roof_entry(kname, "mfma", fl * ops[kname], kern[kname], BF16_PEAK_TFLOPS,
+                                        "TFLOP/s", 1e12))
+    for r in roof:
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+    rec["roofline"] = [{k: r[k] for k in ("kernel", "bound", "achieved", "unit", "frac", "avg_us")} for r in roof]
+    if not dec:
+        qk = [r for r in roof if r["kernel"] in ("prefill_stats", "prefill_pool")]
+        rec["qkt_passes_vs_half_peak"] = {r["kernel"]: {"ms": round(r["avg_us"] / 1e3, 3), "frac": r["frac"],
+                                                        "meets_0.5": r["frac"] >= 0.5} for r in qk}
+    rec["kernels"] = {n_: {"total_ms": round(ms, 3), "launches": c, "avg_us": round(1e3 * ms / c, 3)}
+                      for n_, (ms, c) in sorted(kern.items(), key=lambda x: -x[1][0])}
+    cpu = None
+    if cpu_budget > 0:
+        if dec:
+            cpu = cpu_decode_sample(w, st, cpu_budget, inputgen)
+        else:
+            T = w.seq_len // 32
+            cpu = cpu_prefill_sample(w, st, (T - 1, T // 2), inputgen)
+    log(f"[bench] config {name}: step {step_ms:.3f} ms")
+    del st
+    torch.cuda.empty_cache()
+    return rec, cpu
 
 
 # ---------------------------------------------------------------- main
@@ -205,6 +357,9 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 layer timings")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config records of the other workloads (tiny 2K decode, 32K decode, "
+                         "32K Qwen prefill)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the reference ceilings (a large bf16 GEMM, a device copy)")
     ap.add_argument("--layers", type=int, default=0,
@@ -406,9 +561,21 @@ def main():
         out["paged_prefill"] = paged_prefill_timings(wp, pre_state, dev, torch, inputgen, kas)
     if not args.no_ceilings:
         out["ceilings"] = ceilings(torch, dev)
+    cpu_extra = {}
+    if not args.no_configs and not args.layers:
+        out["configs"] = {}
+        for name in OTHER_CONFIGS:
+            w = inputgen.WORKLOADS[name]
+            if (w.phase == "decode" and not do_dec) or (w.phase == "prefill" and not do_pre):
+                continue
+            budget = 0.0 if args.no_cpu_baseline else args.cpu_budget * 0.15
+            rec, cpu = config_record(name, args.steps, max(1, args.warmup), dev, torch, inputgen, kas, budget)
+            out["configs"][name] = rec
+            if cpu is not None:
+                cpu_extra[name] = cpu
     if not args.no_cpu_baseline and do_dec and do_pre:
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen)
+        out["cpu_baseline"] = cpu_baseline(wd, dec_state, wp, pre_state, args.cpu_budget, inputgen, cpu_extra)
     print(json.dumps(out), flush=True)
 
 

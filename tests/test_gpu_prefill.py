@@ -113,9 +113,13 @@ def test_prefill_anchor_then_reuse(shape):
     _check_reuse_tiles(w, q2, k2, v2, pct, gidx, hm, o2, range(T), label)
 
 
+# Oracle-checked tiles: first and last tiles, both members of several tile
+# pairs (2p, 2p+1) of the statistics and pooling kernels, and tiles that land
+# on different XCDs and in different groups of 64 workgroups of the
+# XCD-local order (the attention kernel takes tile T - 1 - order(j)).
 @pytest.mark.parametrize("name,tiles", [
-    ("qwen8b_prefill_32k", (1, 2, 37, 500, 1023)),
-    ("llama8b_prefill_128k", (1, 1500, 4095)),
+    ("qwen8b_prefill_32k", (1, 2, 3, 37, 64, 65, 500, 511, 700, 1022, 1023)),
+    ("llama8b_prefill_128k", (1, 2, 3, 63, 64, 776, 777, 1500, 2048, 2049, 3001, 4094, 4095)),
 ])
 def test_full_size_prefill_sampled_tiles(name, tiles):
     kas = _kas()
