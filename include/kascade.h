@@ -267,6 +267,21 @@ kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
                                   const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* kas_decode_reuse for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call and results, with the split-K partials in a static device
+ * buffer of the library (KAS_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends) instead of a caller workspace. Calls needing more scratch
+ * than that (kas_workspace_size(KAS_OP_DECODE_REUSE) of the same descriptor)
+ * return KAS_ERR_UNSUPPORTED and enqueue nothing. The current device must be
+ * the stream's device. Every call on one GPU shares that GPU's buffer: calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * must be serialised by the caller. Nothing in it needs to start at zero. */
+#define KAS_NOALLOC_SCRATCH_BYTES (16u << 20)
+kas_status_t kas_decode_reuse_noalloc(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                                      const int32_t* anchor_idx, int32_t anchor_kv_heads, const int32_t* head_map,
+                                      void* o, void* stream);
+
 /* Refined layer of proposal-refined reuse (decode). The Prism Attention page
  * (thelatestinai.com/papers/2610.22985, "Proposal-Refined" sharing) has a
  * proposal layer export a pool of rho * kappa candidate keys and every

@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     decode_k,
     decode_refine,
     decode_reuse,
+    decode_reuse_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     lib_path,
     make_desc,
     prefill_anchor,

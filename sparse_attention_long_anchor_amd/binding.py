@@ -93,6 +93,7 @@ def _load():
         L.kas_prefill_anchor.argtypes = [dp, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_prefill_reuse.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P, ctypes.c_size_t, P]
         L.kas_decode_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kas_decode_reuse_noalloc.argtypes = [dp, P, P, P, P, ctypes.c_int32, P, P, P]
         cp = ctypes.POINTER(KasKvCache)
         L.kas_workspace_size_kv.argtypes = [dp, cp, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
         L.kas_decode_anchor_kv.argtypes = [dp, cp, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -124,7 +125,7 @@ def _load():
                   "kas_workspace_size_refine", "kas_decode_refine", "kas_prefill_anchor_kv",
                   "kas_prefill_reuse_kv", "kas_prefill_dense_kv", "kas_workspace_size_refine_kv",
                   "kas_decode_refine_kv", "kas_profile_enable", "kas_profile_reset", "kas_profile_query",
-                  "kas_profile_names", "kas_set_option", "kas_get_option"):
+                  "kas_profile_names", "kas_set_option", "kas_get_option", "kas_decode_reuse_noalloc"):
             getattr(L, n).restype = st
         _lib = L
     return _lib
@@ -346,6 +347,23 @@ def decode_reuse(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=
                                          _ptr(anchor_idx), anchor_idx.shape[1], _ptr(head_map), _ptr(o),
                                          _ptr(ws), ws.numel(), _stream(q))
     _check(rc, "decode_reuse")
+    return o
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_reuse_noalloc(q, k, v, anchor_idx, head_map, pct: int, scale: float = 0.0, o=None) -> torch.Tensor:
+    """decode_reuse without a workspace (kas_decode_reuse_noalloc: the library's
+    static per-GPU scratch buffer; pass o to allocate nothing at all)."""
+    o = _new_out(q) if o is None else o
+    _check_tensors("decode_reuse_noalloc", q, k, v, o, anchor_idx=anchor_idx, head_map=head_map)
+    desc = _desc_from(q, k, pct, False, scale, o=o)
+    if k.stride() != v.stride():
+        raise KasError(1, "decode_reuse_noalloc", "k and v must share strides")
+    _check(_load().kas_decode_reuse_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(anchor_idx),
+                                            anchor_idx.shape[1], _ptr(head_map), _ptr(o), _stream(q)),
+           "decode_reuse_noalloc")
     return o
 
 

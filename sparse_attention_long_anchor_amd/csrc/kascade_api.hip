@@ -452,6 +452,34 @@ static kas_status_t hip_fail(hipError_t e, const char* where) {
   return fail(KAS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// ------------------------------------------------------------------ static scratch
+
+// The buffer of kas_decode_reuse_noalloc. In host code `scratch` names a
+// host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device is passed on.
+static __device__ __align__(256) char scratch[KAS_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+// This device's copy of the static buffer, looked up once per device.
+static kas_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KAS_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & 255u)) return fail(KAS_ERR_HIP, "static scratch buffer has no aligned address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KAS_OK;
+}
+
 }  // namespace kas
 
 using namespace kas;
@@ -594,6 +622,27 @@ kas_status_t kas_decode_reuse_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
   }
   if ((e = launch_decode_attn(a, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");
   return KAS_OK;
+}
+
+kas_status_t kas_decode_reuse_noalloc(const kas_desc_t* desc, const void* q, const void* k, const void* v,
+                                      const int32_t* anchor_idx, int32_t anchor_kv_heads, const int32_t* head_map,
+                                      void* o, void* stream) {
+  size_t need = 0;
+  kas_status_t st = kas_workspace_size(desc, KAS_OP_DECODE_REUSE, &need);
+  if (st != KAS_OK) return st;
+  // the argument checks of kas_decode_reuse come first, before any device query
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")))
+    return st;
+  if (!anchor_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_idx is NULL");
+  if (anchor_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_kv_heads must be >= 1");
+  if (need > KAS_NOALLOC_SCRATCH_BYTES)
+    return fail(KAS_ERR_UNSUPPORTED, "decode reuse needs %zu bytes of scratch; the static buffer holds %u",
+                need, (unsigned)KAS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != KAS_OK) return st;
+  return kas_decode_reuse_kv(desc, nullptr, q, k, v, anchor_idx, anchor_kv_heads, head_map, o, ws,
+                             KAS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kas_status_t kas_prefill_anchor(const kas_desc_t* desc, const void* q, const void* k, const void* v,

@@ -130,6 +130,15 @@ int main() {
   c.max_pages = 2;          // does not cover seq_len
   CHECK(kas_decode_reuse_kv(&d, &c, fake, fake, fake, (int32_t*)fake, 8, nullptr, fake, fake, need, nullptr) ==
         KAS_ERR_INVALID_ARGUMENT);
+  // the no-allocation reuse call: checked before any device query
+  kas_desc_t nb = base_desc();
+  nb.batch = 1024; nb.n_q_heads = 64; nb.seq_len = 64;
+  CHECK(kas_decode_reuse_noalloc(&nb, fake, fake, fake, (int32_t*)fake, 8, nullptr, fake, nullptr) ==
+        KAS_ERR_UNSUPPORTED);
+  CHECK(kas_decode_reuse_noalloc(&d, nullptr, fake, fake, (int32_t*)fake, 8, nullptr, fake, nullptr) ==
+        KAS_ERR_INVALID_ARGUMENT);
+  CHECK(kas_decode_reuse_noalloc(nullptr, fake, fake, fake, (int32_t*)fake, 8, nullptr, fake, nullptr) ==
+        KAS_ERR_INVALID_ARGUMENT);
   // options
   int64_t v = 0;
   CHECK(kas_get_option(KAS_OPT_DECODE_SPLIT_ROWS, &v) == KAS_OK && v == -1);

@@ -315,3 +315,21 @@ def test_binding_rejects_mismatched_tensors_without_gpu():
     with pytest.raises(b.KasError, match="contiguous"):
         b._row_strides(qt, "q")
     assert b._row_strides(torch.zeros(1, 8, 128), "q") == (0, 128, 0)
+
+
+def test_noalloc_reuse_checks_without_gpu():
+    """kas_decode_reuse_noalloc validates like kas_decode_reuse and rejects a
+    call whose partials exceed its static buffer before touching a device."""
+    import torch
+    b = _kas()
+    L = b._load()
+    fake = ctypes.c_void_p(1 << 20)
+    big = b.make_desc(1024, 64, 8, 128, 64, 10, torch.bfloat16)
+    assert b.workspace_size(big, b.OP_DECODE_REUSE) > b.NOALLOC_SCRATCH_BYTES
+    r = L.kas_decode_reuse_noalloc(ctypes.byref(big), fake, fake, fake, fake, 8, None, fake, None)
+    assert r == 2 and b"static buffer" in L.kas_last_error()
+    ok = b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16)
+    assert b.workspace_size(ok, b.OP_DECODE_REUSE) <= b.NOALLOC_SCRATCH_BYTES
+    r = L.kas_decode_reuse_noalloc(ctypes.byref(ok), None, fake, fake, fake, 8, None, fake, None)
+    assert r == 1 and b"q is NULL" in L.kas_last_error()
+    assert L.kas_decode_reuse_noalloc(None, fake, fake, fake, fake, 8, None, fake, None) == 1
