@@ -907,7 +907,9 @@ __device__ __forceinline__ u32x2 dec_lds_read_tr16(const char* p) {
 // tile (or the anchor's stored logits), an online softmax with a running max
 // per head shared by the 16 lanes of each lane row, P (16-bit) and the
 // gathered V rows staged in the wave's own LDS slice, and O += P.V on 16x16x16
-// MFMA with V through the transposing LDS load. Each wave keeps
+// MFMA with V through the transposing LDS load. K and V rows are both loaded
+// whole (16 lanes per 256-byte row) and K re-laid out into the MFMA operand
+// through LDS, as in the scoring pass. Each wave keeps
 // the K and V rows of its next two blocks in flight in two register sets, and
 // each lane loads the index of its own row straight from global memory one
 // block before the rows it names (V row indices are then shuffled from the
@@ -926,6 +928,9 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
   constexpr int VP = D / 8;             // 16-byte parts per V row
   constexpr int NVL = 16 * VP / 64;     // V 16-byte loads per lane per block
   __shared__ __align__(16) char s_v[4][16 * VROW];
+  // K rows of the wave's block (16-byte chunks XOR-swizzled by row), re-laid
+  // out from whole-row loads into the MFMA operand
+  __shared__ __align__(16) char s_k[FROM_LOGITS ? 1 : 4][FROM_LOGITS ? 16 : 16 * 2 * D];
   __shared__ __align__(16) uint16_t s_p[4][16 * 16];   // [head][key] bf16; heads >= G stay 0
   __shared__ float s_o[4][G * D];
   __shared__ float s_m[4][G], s_l[4][G];
@@ -972,7 +977,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
     else return idx[r];
   };
   struct Blk {
-    QK kq;
+    u32x4 k[FROM_LOGITS ? 1 : NVL];   // whole K rows, in the layout of v
     f32x4 lgt;
     u32x4 v[NVL];
   };
@@ -993,16 +998,34 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) B_.lgt[r] = (4 * q4 + r < G) ? lg[(int64_t)jk * G + 4 * q4 + r] : 0.f;
       }
-    } else {
-      if constexpr (STREAM) B_.kq.load_k_nt(kb + (int64_t)jk * D, q4);
-      else B_.kq.load_k(kb + (int64_t)jk * D, q4);
     }
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int x = lane + 64 * i;
       const int jv = __shfl(jk, x / VP);   // lane x / VP (< 16) owns row x / VP
+      if constexpr (!FROM_LOGITS)
+        B_.k[i] = STREAM ? ldg16_nt(kb + (int64_t)jv * D + (x % VP) * 8) : ldg16(kb + (int64_t)jv * D + (x % VP) * 8);
       B_.v[i] = STREAM ? ldg16_nt(vb + (int64_t)jv * D + (x % VP) * 8) : ldg16(vb + (int64_t)jv * D + (x % VP) * 8);
     }
+  };
+  // Whole K rows -> the Q.K^T operand (chunk 4 c + q4 of row c16 for
+  // instruction c) through the wave's LDS slot; a wave's LDS accesses execute
+  // in order, so one slot serves every block.
+  auto k_operand = [&](const Blk& B_) __attribute__((always_inline)) -> QK {
+    QK kq;
+    if constexpr (!FROM_LOGITS) {
+      char* sk = s_k[wave];
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) {
+        const int x = lane + 64 * i, row = x / VP, ch = x % VP;
+        *reinterpret_cast<u32x4*>(sk + row * 2 * D + 16 * (ch ^ (row & (VP - 1)))) = B_.k[i];
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int c = 0; c < QK::NI; ++c)
+        kq.kf[c] = *reinterpret_cast<const u32x4*>(sk + c16 * 2 * D + 16 * ((4 * c + q4) ^ (c16 & (VP - 1))));
+    }
+    return kq;
   };
   // transposing-read source address of this lane: key row 4*(lane/16) + (lane%16)/4,
   // dims 4*(lane%4) of each 16-dim output tile
@@ -1010,7 +1033,7 @@ __global__ __launch_bounds__(256, 2) void dec_gather_kernel(DecodeArgs a) {
 
   auto process = [&](int i, const Blk& B_) {
     const int blk = wave + 4 * i;
-    const f32x4 s = FROM_LOGITS ? B_.lgt : B_.kq.run(qf) * a.scale_log2;
+    const f32x4 s = FROM_LOGITS ? B_.lgt : k_operand(B_).run(qf) * a.scale_log2;
     const bool kval = blk * 16 + c16 < nrows;
     float al[4];
     bool grew = false;
