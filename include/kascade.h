@@ -294,25 +294,36 @@ kas_status_t kas_decode_reuse_noalloc(const kas_desc_t* desc, const void* q, con
  * (ties to the lower key) written to idx_out[b, g, :kappa] ascending; each
  * head attends over it. pool_idx [B, pool_kv_heads, pool_size], kappa <=
  * pool_size <= N; head_map as in kas_decode_reuse (values in [0,
- * pool_kv_heads)); idx_out [B, Hkv, kappa]; o [B, Hq, D]. pool_scope,
- * pool_op and query_head_map must be 0. */
+ * pool_kv_heads)); idx_out [B, Hkv, kappa]; o [B, Hq, D]. pool_scope and
+ * pool_op must be 0 (KAS_ERR_UNSUPPORTED). With query_head_map = 1 every
+ * query head h is a set of its own: its pool is pool_idx[b, head_map[h], :]
+ * (head_map of Hq entries, required), it selects its Top-kappa by its own
+ * softmax over the pool, and idx_out is [B, Hq, kappa]. */
 kas_status_t kas_workspace_size_refine(const kas_desc_t* desc, int64_t pool_size, size_t* bytes);
 kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void* k, const void* v,
                                const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
                                const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
                                size_t ws_bytes, void* stream);
-/* The same over a paged cache (cache->block_table as for kas_decode_*_kv;
- * NULL cache: exactly kas_decode_refine). Every sequence holds
- * desc->seq_len keys: seq_lens must be NULL (KAS_ERR_UNSUPPORTED). The
+/* The same over a cache described by a kas_kv_cache_t; a NULL cache and NULL
+ * pool_lens give exactly kas_decode_refine. With cache->block_table the
  * pool's keys are translated to rows of the page pools before scoring, and
- * the refined keys again before the attention; the results equal those of
- * kas_decode_refine on the same keys in a contiguous cache. */
+ * the refined keys again before the attention; the results equal those of a
+ * contiguous cache. Sequences of different lengths (cache->seq_lens, L_b
+ * clamped to [1, seq_len]) and pools of different sizes (pool_lens: device
+ * [B] or NULL, the valid entries of sequence b's pool rows, e.g. max(1,
+ * kas_topk_count(L_b, pct_pool)) after an anchor call over the same cache):
+ * sequence b refines within its first pool_b = clamp(pool_lens[b] (or
+ * pool_size), 1, min(pool_size, L_b)) pool entries and keeps kappa_b =
+ * min(max(1, kas_topk_count(L_b, pct)), pool_b) keys, which is what the call
+ * on that sequence alone (seq_len L_b, pool_size pool_b) computes. Entries of
+ * idx_out past kappa_b are unspecified. Pool entries are trusted to be keys
+ * of the sequence (keys outside [0, seq_len) read key 0). */
 kas_status_t kas_workspace_size_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, int64_t pool_size,
                                           size_t* bytes);
 kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
                                   const void* k, const void* v, const int32_t* pool_idx, int32_t pool_kv_heads,
-                                  int64_t pool_size, const int32_t* head_map, int32_t* idx_out, void* o,
-                                  void* ws, size_t ws_bytes, void* stream);
+                                  int64_t pool_size, const int32_t* pool_lens, const int32_t* head_map,
+                                  int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Process-wide tuning options. They select alternative but equivalent code
  * paths (every setting gives the same results) and the sizes of internal

@@ -106,7 +106,7 @@ def _load():
         L.kas_decode_refine.argtypes = [dp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
                                         ctypes.c_size_t, P]
         L.kas_workspace_size_refine_kv.argtypes = [dp, cp, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
-        L.kas_decode_refine_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P,
+        L.kas_decode_refine_kv.argtypes = [dp, cp, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P,
                                            ctypes.c_size_t, P]
         L.kas_prefill_dense.argtypes = [dp, P, P, P, P, P, ctypes.c_size_t, P]
         L.kas_set_option.argtypes = [ctypes.c_int32, ctypes.c_int64]
@@ -475,22 +475,25 @@ def prefill_dense(q, k, v, scale: float = 0.0, o=None, seq_lens=None, block_tabl
 
 
 def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx_out=None, o=None,
-                  ws=None, block_table=None, seq_len=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  ws=None, query_head_map: bool = False, seq_lens=None, pool_lens=None, block_table=None,
+                  seq_len=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Refined layer of proposal-refined reuse: pool_idx [B, Hkv_p, n_pool] int32 (an anchor
-    set at a larger percentage), head_map [Hkv] or None -> (idx int32 [B, Hkv, kappa],
-    o [B, Hq, D]) with kappa this layer's own k for pct. With block_table, k and v are
-    page pools as in decode_anchor (seq_len = the sequences' common length)."""
+    set at a larger percentage), head_map [Hkv] or None -> (idx int32 [B, Hs, kappa],
+    o [B, Hq, D]) with kappa this layer's own k for pct and Hs = Hkv (Hq with
+    query_head_map, head_map then [Hq]). seq_lens / block_table as in decode_anchor;
+    pool_lens [B] int32: valid entries of each sequence's pool rows."""
     o = _new_out(q) if o is None else o
     _check_tensors("decode_refine", q, k, v, o, pool_idx=pool_idx, head_map=head_map, idx_out=idx_out,
-                   block_table=block_table)
-    over, cache = _cache(q, k, None, block_table, seq_len)
-    desc = _decode_desc(q, k, pct, scale, over, o)
+                   seq_lens=seq_lens, pool_lens=pool_lens, block_table=block_table)
+    over, cache = _cache(q, k, seq_lens, block_table, seq_len)
+    desc = _decode_desc(q, k, pct, scale, over, o, query_head_map=int(query_head_map))
     if k.stride() != v.stride():
         raise KasError(1, "decode_refine", "k and v must share strides")
     n_pool = pool_idx.shape[2]
     kappa = decode_k(desc.seq_len, pct)
+    sets = desc.n_q_heads if query_head_map else desc.n_kv_heads
     if idx_out is None:
-        idx_out = torch.empty((desc.batch, desc.n_kv_heads, kappa), dtype=torch.int32, device=q.device)
+        idx_out = torch.empty((desc.batch, sets, kappa), dtype=torch.int32, device=q.device)
     L = _load()
     cref = None if cache is None else ctypes.byref(cache)
     if ws is None:
@@ -498,8 +501,8 @@ def decode_refine(q, k, v, pool_idx, head_map, pct: int, scale: float = 0.0, idx
         _check(L.kas_workspace_size_refine_kv(ctypes.byref(desc), cref, n_pool, ctypes.byref(n)), "workspace_size")
         ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=q.device)
     _check(L.kas_decode_refine_kv(ctypes.byref(desc), cref, _ptr(q), _ptr(k), _ptr(v), _ptr(pool_idx),
-                                  pool_idx.shape[1], n_pool, _ptr(head_map), _ptr(idx_out), _ptr(o), _ptr(ws),
-                                  ws.numel(), _stream(q)),
+                                  pool_idx.shape[1], n_pool, _ptr(pool_lens), _ptr(head_map), _ptr(idx_out),
+                                  _ptr(o), _ptr(ws), ws.numel(), _stream(q)),
            "decode_refine")
     return idx_out, o
 

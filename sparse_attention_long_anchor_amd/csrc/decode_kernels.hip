@@ -42,14 +42,16 @@ __device__ __forceinline__ int64_t seq_n(const DecodeArgs& a, int b) {
 }
 // Rows of sequence b's sets in a gather: its k, or (dense) all its keys.
 __device__ __forceinline__ int64_t set_rows(const DecodeArgs& a, int b) {
+  if (a.set_lens) return a.set_lens[b];
   if (!a.seq_lens) return a.kk;
   const int64_t n = seq_n(a, b);
   return a.rows_are_keys ? n : decode_k_of(n, a.pct);
 }
 // Keys the selection keeps for one of its units (sets).
 __device__ __forceinline__ uint32_t unit_k(const DecodeArgs& a, int64_t unit) {
-  if (!a.seq_lens) return (uint32_t)a.kk;
   const int64_t per_b = a.sel_units / a.B;
+  if (a.set_lens) return (uint32_t)a.set_lens[unit / per_b];
+  if (!a.seq_lens) return (uint32_t)a.kk;
   return (uint32_t)decode_k_of(seq_n(a, (int)(unit / per_b)), a.pct);
 }
 // A page id from the block table (trusted input, clamped to the pool).
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(256, 4) void dec_score_kernel(DecodeArgs a) {
     uint32_t* h = a.hist + unit * kHistWords;
     for (int i = tid; i < kHistWords; i += 256) h[i] = 0u;
   }
-  const T* kb = (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride + row0 * D;
+  const int gk = kv_head(a, g);     // K head of the set (a query head's with one set per query head)
+  const T* kb = (const T*)a.k + b * a.kv_bstride + gk * a.kv_hstride + row0 * D;
   const int64_t p0 = row0 >> a.page_shift;
   if (PG && !IX) {
     const int np = nrows > 0 ? (int)(((row0 + nrows - 1) >> a.page_shift) - p0 + 1) : 0;
@@ -133,12 +136,12 @@ __global__ __launch_bounds__(256, 4) void dec_score_kernel(DecodeArgs a) {
   auto row_ptr = [&](int jr) __attribute__((always_inline)) -> const T* {
     if (IX) {
       const int64_t key = s_pg[jr < nrows ? jr : 0];
-      const T* base = PG ? (const T*)a.k + g * a.page_hstride : (const T*)a.k + b * a.kv_bstride + g * a.kv_hstride;
+      const T* base = PG ? (const T*)a.k + gk * a.page_hstride : (const T*)a.k + b * a.kv_bstride + gk * a.kv_hstride;
       return base + key * D;
     } else if (PG) {
       const int64_t j = row0 + (jr < nrows ? jr : 0);
       const int64_t pg = page_id(a, s_pg[(j >> a.page_shift) - p0]);
-      return (const T*)a.k + pg * a.page_stride + g * a.page_hstride + (j & ((1 << a.page_shift) - 1)) * D;
+      return (const T*)a.k + pg * a.page_stride + gk * a.page_hstride + (j & ((1 << a.page_shift) - 1)) * D;
     } else {
       return kb + (int64_t)(jr < nrows ? jr : 0) * D;
     }
@@ -1447,7 +1450,8 @@ __global__ __launch_bounds__(256) void dec_pool_keys_kernel(DecodeArgs a) {
   const int32_t* pool = a.idx + ((int64_t)b * a.Hkv_a + ga) * a.N;
   const int32_t* pos = a.pos + ((int64_t)b * a.Hkv + g) * a.kk;
   int32_t* out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.kk;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.kk; i += (int64_t)gridDim.x * 256) {
+  const int64_t rows = set_rows(a, b);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows; i += (int64_t)gridDim.x * 256) {
     const int32_t p = pos[i];
     out[i] = pool[((uint32_t)p < (uint64_t)a.N) ? p : 0];
   }
@@ -1458,6 +1462,36 @@ hipError_t launch_pool_positions_to_keys(const DecodeArgs& a, LaunchCtx& ctx) {
   const int64_t chunks = (a.kk + 255) / 256;
   KAS_LAUNCH(dec_pool_keys_kernel, dim3((unsigned)(chunks < 16 ? chunks : 16), a.Hkv, a.B), dim3(256), ctx, a);
   return ctx.end(K_DEC_REFINE_MAP);
+}
+
+struct RefineLens {
+  const int32_t* seq_lens;
+  const int32_t* pool_lens;
+  int B, pct;
+  int64_t N, pool_size;
+  int32_t* pool_out;
+  int32_t* kappa_out;
+};
+
+__global__ __launch_bounds__(256) void dec_refine_lens_kernel(RefineLens r) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= r.B) return;
+  int64_t L = r.seq_lens ? (int64_t)r.seq_lens[b] : r.N;
+  L = L < 1 ? 1 : (L > r.N ? r.N : L);
+  const int64_t cap = r.pool_size < L ? r.pool_size : L;
+  int64_t n = r.pool_lens ? (int64_t)r.pool_lens[b] : r.pool_size;
+  n = n < 1 ? 1 : (n > cap ? cap : n);
+  const int64_t k = decode_k_of(L, r.pct);
+  r.pool_out[b] = (int32_t)n;
+  r.kappa_out[b] = (int32_t)(k < n ? k : n);
+}
+
+hipError_t launch_refine_lens(const int32_t* seq_lens, const int32_t* pool_lens, int B, int64_t N,
+                              int64_t pool_size, int pct, int32_t* pool_out, int32_t* kappa_out, LaunchCtx& ctx) {
+  ctx.begin(K_DEC_REFINE_LENS);
+  const RefineLens r{seq_lens, pool_lens, B, pct, N, pool_size, pool_out, kappa_out};
+  KAS_LAUNCH(dec_refine_lens_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), ctx, r);
+  return ctx.end(K_DEC_REFINE_LENS);
 }
 
 hipError_t launch_page_rows(const DecodeArgs& a, int nsets, LaunchCtx& ctx) {

@@ -28,6 +28,7 @@ enum KernelId {
   K_PRE_POOL_HEADS,
   K_DEC_PAGE_ROWS,
   K_DEC_REFINE_MAP,
+  K_DEC_REFINE_LENS,
   K_PRE_PAGE_COPY,
   K_COUNT_
 };
@@ -116,6 +117,9 @@ struct DecodeArgs {
   // head map) instead of the cache; n_keys = rows of the cache
   int64_t n_keys;
   const int32_t* pos;               // selected positions in the pool [B, Hkv, kk]
+  // refined layers over sequences of different lengths or pools: keys in
+  // sequence b's sets (its kappa), or null: kk, or decode_k(seq_lens[b], pct)
+  const int32_t* set_lens;
 };
 
 // Decode k of n keys: round-half-up(pct * n / 100) clamped to [1, n].
@@ -127,6 +131,12 @@ __host__ __device__ inline int64_t decode_k_of(int64_t n, int pct) {
 }
 
 hipError_t launch_decode_score(const DecodeArgs& a, int dtype, LaunchCtx& ctx);
+// Refined layer over sequences of different lengths or pools: for each b,
+// pool_out[b] = pool_lens[b] (or pool_size) clamped to [1, min(pool_size,
+// L_b)] and kappa_out[b] = min(decode_k(L_b, pct), pool_out[b]), with L_b =
+// seq_lens[b] (or N) clamped to [1, N].
+hipError_t launch_refine_lens(const int32_t* seq_lens, const int32_t* pool_lens, int B, int64_t N,
+                              int64_t pool_size, int pct, int32_t* pool_out, int32_t* kappa_out, LaunchCtx& ctx);
 hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx);
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx);
 hipError_t launch_decode_attn(const DecodeArgs& a, int dtype, bool from_logits, LaunchCtx& ctx);

@@ -41,7 +41,7 @@ static const char* const kKernelNames[] = {
     "decode_score", "decode_pool", "select_cand", "select_resolve",
     "select_compact", "select_fused", "decode_attn", "decode_attn_anchor", "decode_combine", "prefill_stats", "prefill_pool",
     "prefill_select", "prefill_attn", "decode_dense", "prefill_dense", "prefill_pool_heads", "decode_page_rows", "decode_refine_map",
-    "prefill_page_copy"};
+    "decode_refine_lens", "prefill_page_copy"};
 static_assert(sizeof(kKernelNames) / sizeof(kKernelNames[0]) == K_COUNT_, "one timing name per kernel id");
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_COUNT_) ? kKernelNames[id] : "?"; }
@@ -804,31 +804,28 @@ kas_status_t kas_prefill_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
 }
 
 // Refined layer of proposal-refined reuse: the pool-sized plan (scores,
-// pooled values and selection over the pool; gather splits over kappa). A
-// paged cache adds the pool's physical rows (B * Hkv * pool_size) after it.
-static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, DecodePlan& p,
-                                bool paged = false, size_t* off_pool_rows = nullptr) {
+// pooled values and selection over the pool; gather splits over kappa). With
+// one set per query head the plan is that of the per-query-head shape. A
+// paged cache adds the pool's physical rows (B * sets * pool_size) after it;
+// every plan ends with room for the per-sequence pool sizes and kappas.
+static kas_status_t refine_plan(const Shape& s, int64_t pool_size, Shape& sp, DecodePlan& p, bool paged,
+                                size_t* off_pool_rows = nullptr, size_t* off_lens = nullptr) {
   const int64_t kappa = decode_k(s.N, s.pct);
   if (pool_size < kappa || pool_size > s.N)
     return fail(KAS_ERR_INVALID_ARGUMENT, "pool_size %lld must lie in [kappa = %lld, seq_len = %lld]",
                 (long long)pool_size, (long long)kappa, (long long)s.N);
-  if (s.scope || s.op || s.qmap)
-    return fail(KAS_ERR_UNSUPPORTED, "refined layers pool by sum per KV head with a KV-head map");
-  sp = s;
+  if (s.scope || s.op)
+    return fail(KAS_ERR_UNSUPPORTED, "refined layers pool by sum within each set (pool_scope and pool_op 0)");
+  sp = s.qmap ? per_query_head(s) : s;
   sp.N = pool_size;
   p = plan_decode(sp, true, false, paged, kappa);
+  size_t off = p.total;
   if (paged) {
-    if (off_pool_rows) *off_pool_rows = p.total;
-    p.total = align_up(p.total + (size_t)s.B * s.Hkv * pool_size * sizeof(uint32_t), 256);
+    if (off_pool_rows) *off_pool_rows = off;
+    off = align_up(off + (size_t)s.B * sp.Hkv * pool_size * sizeof(uint32_t), 256);
   }
-  return KAS_OK;
-}
-
-// Refined layers read lengths from no cache: every sequence holds seq_len keys.
-static kas_status_t refine_cache(const kas_kv_cache_t* cache, const Shape& s, CacheView& cv) {
-  kas_status_t st = check_cache(cache, s, cv);
-  if (st != KAS_OK) return st;
-  if (cv.seq_lens) return fail(KAS_ERR_UNSUPPORTED, "refined layers take no sequence lengths");
+  if (off_lens) *off_lens = off;
+  p.total = align_up(off + (size_t)2 * s.B * sizeof(int32_t), 256);
   return KAS_OK;
 }
 
@@ -844,7 +841,7 @@ kas_status_t kas_workspace_size_refine_kv(const kas_desc_t* desc, const kas_kv_c
   CacheView cv;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
-  if ((st = refine_cache(cache, s, cv))) return st;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = refine_plan(s, pool_size, sp, p, cv.paged()))) return st;
   *bytes = p.total;
   return KAS_OK;
@@ -854,50 +851,65 @@ kas_status_t kas_decode_refine(const kas_desc_t* desc, const void* q, const void
                                const int32_t* pool_idx, int32_t pool_kv_heads, int64_t pool_size,
                                const int32_t* head_map, int32_t* idx_out, void* o, void* ws,
                                size_t ws_bytes, void* stream) {
-  return kas_decode_refine_kv(desc, nullptr, q, k, v, pool_idx, pool_kv_heads, pool_size, head_map, idx_out, o, ws,
-                              ws_bytes, stream);
+  return kas_decode_refine_kv(desc, nullptr, q, k, v, pool_idx, pool_kv_heads, pool_size, nullptr, head_map,
+                              idx_out, o, ws, ws_bytes, stream);
 }
 
 kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* cache, const void* q,
                                   const void* k, const void* v, const int32_t* pool_idx, int32_t pool_kv_heads,
-                                  int64_t pool_size, const int32_t* head_map, int32_t* idx_out, void* o,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  int64_t pool_size, const int32_t* pool_lens, const int32_t* head_map,
+                                  int32_t* idx_out, void* o, void* ws, size_t ws_bytes, void* stream) {
   Shape s, sp;
   DecodePlan p;
   CacheView cv;
-  size_t off_pool_rows = 0;
+  size_t off_pool_rows = 0, off_lens = 0;
   kas_status_t st = check_desc(desc, false, s);
   if (st != KAS_OK) return st;
-  if ((st = refine_cache(cache, s, cv))) return st;
+  if ((st = check_cache(cache, s, cv))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
   if (!pool_idx) return fail(KAS_ERR_INVALID_ARGUMENT, "pool_idx is NULL");
   if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
   if (pool_kv_heads < 1) return fail(KAS_ERR_INVALID_ARGUMENT, "pool_kv_heads must be >= 1");
+  if (s.qmap && !head_map) return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map needs a head_map of n_q_heads entries");
   if (!head_map && pool_kv_heads != s.Hkv && pool_kv_heads != 1)
     return fail(KAS_ERR_INVALID_ARGUMENT,
                 "without a head map, pool_kv_heads must be n_kv_heads (identity) or 1 (shared pool)");
-  if ((st = refine_plan(s, pool_size, sp, p, cv.paged(), &off_pool_rows))) return st;
+  if ((st = refine_plan(s, pool_size, sp, p, cv.paged(), &off_pool_rows, &off_lens))) return st;
   if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  const int sets = sp.Hkv;     // Hkv, or Hq with one set per query head
   DecodeArgs a;
   fill_decode_args(sp, p, true, (char*)ws, a);
   fill_cache(a, cv, s);
+  a.kvdiv = s.qmap ? s.G : 1;
   a.q = q; a.k = k; a.v = v; a.o = o;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
+  // sequences of different lengths or pools: sequence b's pool size and kappa
+  const bool varlen = cv.seq_lens || pool_lens;
+  int32_t* lens_pool = (int32_t*)((char*)ws + off_lens);
+  int32_t* lens_kappa = lens_pool + s.B;
+  if (varlen && (e = launch_refine_lens(cv.seq_lens, pool_lens, s.B, s.N, pool_size, s.pct, lens_pool, lens_kappa,
+                                        ctx)) != hipSuccess)
+    return hip_fail(e, "decode_refine_lens");
+  const int32_t* set_lens = varlen ? lens_kappa : nullptr;
   if (cv.paged()) {
     // the pools' keys (head map applied) as physical rows, scored from there
     DecodeArgs t = a;
     t.N = s.N; t.kk = pool_size;
+    t.seq_lens = cv.seq_lens; t.set_lens = varlen ? lens_pool : nullptr;
     t.prow = (uint32_t*)((char*)ws + off_pool_rows);
     t.page_src = pool_idx; t.page_src_sets = pool_kv_heads; t.head_map = head_map;
-    if ((e = launch_page_rows(t, s.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
-    a.idx = (const int32_t*)t.prow; a.Hkv_a = s.Hkv; a.head_map = nullptr; a.n_keys = cv.pool_rows;
+    if ((e = launch_page_rows(t, sets, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    a.idx = (const int32_t*)t.prow; a.Hkv_a = sets; a.head_map = nullptr; a.n_keys = cv.pool_rows;
   } else {
     a.idx = pool_idx; a.Hkv_a = pool_kv_heads; a.head_map = head_map; a.n_keys = s.N;
   }
-  // scoring, pooling and selection over the pool's keys: positions in the pool
+  // scoring, pooling and selection over the pool's keys: positions in the
+  // pool (sequence b: its first pool_b positions, kappa_b kept)
+  a.seq_lens = varlen ? lens_pool : nullptr;
+  a.set_lens = set_lens;
   a.idx_out = (int32_t*)((char*)ws + p.off_pos);
   if ((e = launch_decode_score_pool_rows(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
   if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
@@ -909,10 +921,11 @@ kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   if ((e = launch_pool_positions_to_keys(a, ctx)) != hipSuccess) return hip_fail(e, "decode_refine_map");
   DecodeArgs ga = a;
   ga.N = s.N;
-  ga.idx = idx_out; ga.Hkv_a = s.Hkv; ga.head_map = nullptr;
+  ga.seq_lens = cv.seq_lens; ga.set_lens = set_lens;
+  ga.idx = idx_out; ga.Hkv_a = sets; ga.head_map = nullptr;
   if (cv.paged()) {
-    ga.page_src = idx_out; ga.page_src_sets = s.Hkv;
-    if ((e = launch_page_rows(ga, s.Hkv, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
+    ga.page_src = idx_out; ga.page_src_sets = sets;
+    if ((e = launch_page_rows(ga, sets, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
     ga.idx = (const int32_t*)ga.prow;
   }
   if ((e = launch_decode_attn(ga, s.dtype, false, ctx)) != hipSuccess) return hip_fail(e, "decode_attn");

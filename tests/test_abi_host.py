@@ -219,7 +219,7 @@ def test_refine_checks_without_gpu():
                             1 << 30, None)
     assert r == 1 and b"pool_idx" in L.kas_last_error()
     # over a paged cache: room for the pool's physical rows (B Hkv pool_size
-    # uint32) and the refined set's; sequence lengths are not taken
+    # uint32) and the refined set's
     base = ctypes.c_size_t(0)
     assert L.kas_workspace_size_refine(ctypes.byref(d), 4 * kappa, ctypes.byref(base)) == 0
     paged = b.KasKvCache(None, 1 << 20, 64, 64, 200, 0, 0)
@@ -227,9 +227,22 @@ def test_refine_checks_without_gpu():
     assert n.value >= base.value + 2 * 2 * (4 * kappa) * 4 + 2 * 2 * kappa * 4
     assert L.kas_workspace_size_refine_kv(ctypes.byref(d), None, 4 * kappa, ctypes.byref(n)) == 0
     assert n.value == base.value
+    # sequence lengths need no more room: every plan holds the per-sequence
+    # pool sizes and kappas
     varlen = b.KasKvCache(1 << 20, None, 0, 0, 0, 0, 0)
-    assert L.kas_workspace_size_refine_kv(ctypes.byref(d), ctypes.byref(varlen), 4 * kappa, ctypes.byref(n)) == 2
-    assert b"sequence lengths" in L.kas_last_error()
+    assert L.kas_workspace_size_refine_kv(ctypes.byref(d), ctypes.byref(varlen), 4 * kappa, ctypes.byref(n)) == 0
+    assert n.value == base.value
+    # one set per query head: the plan of the per-query-head shape (larger),
+    # and the call needs a head map
+    dq = b.make_desc(2, 8, 2, 128, 4096, 10, torch.bfloat16, query_head_map=1)
+    assert L.kas_workspace_size_refine(ctypes.byref(dq), 4 * kappa, ctypes.byref(n)) == 0
+    assert n.value > base.value
+    r = L.kas_decode_refine_kv(ctypes.byref(dq), None, fake, fake, fake, fake, 2, 4 * kappa, None, None, fake, fake,
+                               fake, 1 << 30, None)
+    assert r == 1 and b"head_map" in L.kas_last_error()
+    r = L.kas_decode_refine_kv(ctypes.byref(d), None, fake, fake, fake, fake, 3, 4 * kappa, None, None, fake, fake,
+                               fake, 1 << 30, None)
+    assert r == 1 and b"pool_kv_heads" in L.kas_last_error()
 
 
 def test_qo_stride_validation_without_gpu():

@@ -357,3 +357,137 @@ def test_decode_refine_full_size():
     hm = inputgen.head_maps(w)[1]
     idx, o = _check_refine(w, q, k, v, pool, hm, w.topk_pct, w.name)
     _check_refine_paged(w, q, k, v, pool, hm, w.topk_pct, idx, o, P=256)
+
+
+REFINE_QMAP = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, pool pct)
+    ("bf16_d128_g4", 2, 16, 4, 128, 3001, "bf16", 10, 40),
+    ("f16_d64_g2", 1, 8, 4, 64, 1500, "f16", 5, 25),
+]
+
+
+@pytest.mark.parametrize("case", REFINE_QMAP, ids=[c[0] for c in REFINE_QMAP])
+def test_decode_refine_query_head_map(case):
+    """One refined set per query head: query head h refines within pool
+    head_map[h] by its own softmax. The oracle's refined layer over K and V
+    expanded to one head per query head (groups of one) defines it."""
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct, ppct = case
+    G = Hq // Hkv
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000 + 7, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    pool, _ = kas.decode_anchor(q, k, v, ppct)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(8).integers(0, Hkv, Hq).astype(np.int32)
+    hmt = torch.as_tensor(hm, device=DEV)
+    idx, o = kas.decode_refine(q2, k2, v2, pool, hmt, pct, query_head_map=True)
+    torch.cuda.synchronize()
+    assert idx.shape == (B, Hq, oracle.decode_k(N, pct))
+    qn, kn, vn, pn = _np(q2), _np(k2), _np(v2), pool.cpu().numpy()
+    ke, ve = np.repeat(kn, G, axis=1), np.repeat(vn, G, axis=1)
+    kappa = oracle.decode_k(N, pct)
+    oidx, oo = oracle.decode_refine(qn, ke, ve, pn, hm, kappa)
+    gi = idx.cpu().numpy()
+    swaps = 0
+    for b in range(B):
+        for h in range(Hq):
+            if np.array_equal(gi[b, h], oidx[b, h]):
+                continue
+            keys = pn[b, hm[h]]
+            s = torch.from_numpy(qn[b, h]).double() @ torch.from_numpy(kn[b, h // G, keys]).double().T
+            full = np.zeros(N)
+            full[keys] = torch.softmax(s / np.sqrt(D), -1).numpy()
+            swaps += assert_index_set(gi[b, h], oidx[b, h], full, kappa, where=f"{label} b{b} h{h}")
+    o_same = oracle.decode_reuse(qn, ke, ve, gi, np.arange(Hq, dtype=np.int32))
+    err_same, err = max_abs(_np(o), o_same), max_abs(_np(o), oo)
+    _say(f"[decode refine, per query head] {label}: near-tie swaps={swaps} "
+         f"max|o-o_oracle(same set)|={err_same:.3g} max|o-o_oracle|={err:.3g}")
+    assert err_same <= TOL[dt] and err <= TOL[dt]
+    from test_gpu_kvcache import _paged
+    kp, vp, bt = _paged(k2, v2, 64, seed=9)
+    idx_p, o_p = kas.decode_refine(q2, kp, vp, pool, hmt, pct, query_head_map=True, block_table=bt, seq_len=N)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx) and torch.equal(o_p, o)
+
+
+REFINE_VARLEN = [
+    # (label, B, Hq, Hkv, D, N, dtype, pct, pool pct, lengths)
+    ("bf16_d128_g4", 3, 8, 2, 128, 4099, "bf16", 10, 40, (4099, 1777, 300)),
+    ("f16_d64_g2_short", 4, 8, 4, 64, 2048, "f16", 5, 20, (2048, 1, 33, 1200)),
+]
+
+
+@pytest.mark.parametrize("case", REFINE_VARLEN, ids=[c[0] for c in REFINE_VARLEN])
+def test_decode_refine_varlen(case):
+    """Sequences of different lengths, with pools from a varlen anchor call:
+    sequence b refines within its pool_b valid pool entries and keeps
+    kappa_b = min(k(L_b), pool_b) keys, as the oracle's refined layer on that
+    sequence alone. A paged copy gives the same bits."""
+    kas = _kas()
+    label, B, Hq, Hkv, D, N, dt, pct, ppct, lens = case
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000 + 11, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    L = np.array(lens, dtype=np.int32)
+    tl = torch.as_tensor(L, device=DEV)
+    pool, _ = kas.decode_anchor(q, k, v, ppct, seq_lens=tl)
+    plen = np.array([oracle.decode_k(int(x), ppct) for x in L], dtype=np.int32)
+    tp = torch.as_tensor(plen, device=DEV)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(12).integers(0, Hkv, Hkv).astype(np.int32)
+    hmt = torch.as_tensor(hm, device=DEV)
+    idx, o = kas.decode_refine(q2, k2, v2, pool, hmt, pct, seq_lens=tl, pool_lens=tp)
+    torch.cuda.synchronize()
+    qn, kn, vn, pn, gi = _np(q2), _np(k2), _np(v2), pool.cpu().numpy(), idx.cpu().numpy()
+    G = Hq // Hkv
+    worst_same, worst, swaps = 0.0, 0.0, 0
+    for b in range(B):
+        n, pb = int(L[b]), int(plen[b])
+        kappa = min(oracle.decode_k(n, pct), pb)
+        kb, vb = kn[b:b + 1, :, :n], vn[b:b + 1, :, :n]
+        pool_b = np.ascontiguousarray(pn[b:b + 1, :, :pb])
+        oidx, oo = oracle.decode_refine(qn[b:b + 1], kb, vb, pool_b, hm, kappa)
+        for g in range(Hkv):
+            got = gi[b, g, :kappa]
+            if np.array_equal(got, oidx[0, g]):
+                continue
+            keys = pool_b[0, hm[g]]
+            s = torch.from_numpy(qn[b, g * G:(g + 1) * G]).double() @ torch.from_numpy(kn[b, g, keys]).double().T
+            full = np.zeros(n)
+            full[keys] = torch.softmax(s / np.sqrt(D), -1).sum(0).numpy()
+            swaps += assert_index_set(got, oidx[0, g], full, kappa, where=f"{label} b{b} g{g}")
+        o_same = oracle.decode_reuse(qn[b:b + 1], kb, vb, np.ascontiguousarray(gi[b:b + 1, :, :kappa]),
+                                     np.arange(Hkv, dtype=np.int32))
+        worst_same = max(worst_same, max_abs(_np(o[b:b + 1]), o_same))
+        worst = max(worst, max_abs(_np(o[b:b + 1]), oo))
+    _say(f"[decode refine, varlen] {label}: lengths {list(L)} pools {list(plen)} near-tie swaps={swaps} "
+         f"max|o-o_oracle(same set)|={worst_same:.3g} max|o-o_oracle|={worst:.3g}")
+    assert worst_same <= TOL[dt] and worst <= TOL[dt]
+    from test_gpu_kvcache import _paged
+    kp, vp, bt = _paged(k2, v2, 16, seed=13)
+    idx_p, o_p = kas.decode_refine(q2, kp, vp, pool, hmt, pct, seq_lens=tl, pool_lens=tp, block_table=bt,
+                                   seq_len=N)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kappa = min(oracle.decode_k(int(L[b]), pct), int(plen[b]))
+        assert torch.equal(idx_p[b, :, :kappa], idx[b, :, :kappa])
+    assert torch.equal(o_p, o)
+
+
+def test_decode_refine_full_lengths_equal_plain_call():
+    """Lengths of N for every sequence and full pools take the per-sequence
+    path; the sets and outputs are those of the plain call, bit for bit."""
+    kas = _kas()
+    B, Hq, Hkv, D, N, pct = 2, 32, 8, 128, 5000, 10
+    w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=314, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    pool, _ = kas.decode_anchor(q, k, v, 4 * pct)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = torch.as_tensor(np.random.default_rng(15).integers(0, Hkv, Hkv).astype(np.int32), device=DEV)
+    idx, o = kas.decode_refine(q2, k2, v2, pool, hm, pct)
+    tl = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    tp = torch.full((B,), pool.shape[2], dtype=torch.int32, device=DEV)
+    idx_v, o_v = kas.decode_refine(q2, k2, v2, pool, hm, pct, seq_lens=tl, pool_lens=tp)
+    idx_l, o_l = kas.decode_refine(q2, k2, v2, pool, hm, pct, pool_lens=tp)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_v) and torch.equal(o, o_v)
+    assert torch.equal(idx, idx_l) and torch.equal(o, o_l)
