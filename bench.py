@@ -229,7 +229,7 @@ def cpu_baseline(wd, dec_state, wp, pre_state, budget_s, inputgen, extra):
     per[wp.name] = pre
     return {
         "value": dec["value"], "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
-        "cpu_model": _cpu_model(),
+        "precision": "fp64", "cpu_model": _cpu_model(),
         "sample": f"{dec['sample']}; oracle fp64 C with OpenMP; {dec['seconds']} s",
         "prefill": {"value": pre["anchor_layer"]["value"], "unit": "TFLOP/s",
                     "sample": f"{wp.name} anchor layer {min(wp.anchors)}, tiles {pre['anchor_layer']['tiles']} "
