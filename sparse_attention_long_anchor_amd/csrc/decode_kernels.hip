@@ -1179,54 +1179,42 @@ __device__ __forceinline__ void store_out<_Float16>(_Float16* p, float x) {
   *reinterpret_cast<uint16_t*>(p) = Ew<_Float16>::bits(x);
 }
 
-// Merge of the split-K partials: one wave per (b, query head). The wave takes
-// the maximum and the rescaled sum of the splits' (m, l), then each lane
-// accumulates its D / 64 output dims (D is 64 or 128) over the splits with
-// weights exp2(m_s - M) and writes o = acc / L. The partial rows of the first
-// kPre splits are loaded before the (m, l) reduction so that both loads are in
-// flight together: with a few splits the merge is two memory latencies long,
-// not three. (Every sequence has at least one key, so some split of it is
-// non-empty and M is finite; empty splits carry m = -inf, l = 0 and weigh 0.)
+// Merge of the split-K partials of one (b, query head): weights
+// exp2(m_s - M) staged in LDS, 256 threads = (256 / D) interleaved split
+// streams per output dim.
 template <typename T>
 __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
-  constexpr int kPre = 8;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
-  if (bh >= (int64_t)a.B * a.Hq) return;
-  const int b = (int)(bh / a.Hq), h = (int)(bh % a.Hq);
+  constexpr int WCH = 1024;
+  __shared__ float s_w[WCH];
+  __shared__ float s_tmp[4];
+  __shared__ float s_acc[256];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int64_t bh = (int64_t)b * a.Hq + h;
   const float* ml = a.part_ml + bh * a.nsplit * 2;
   const float* po = a.part_o + bh * a.nsplit * a.D;
-  const int nd = a.D >> 6;
-  float pre[kPre][2];
-#pragma unroll
-  for (int s = 0; s < kPre; ++s)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      pre[s][j] = (s < a.nsplit && j < nd) ? po[(int64_t)s * a.D + 64 * j + lane] : 0.f;
   float m = kNegInf;
-  for (int s = lane; s < a.nsplit; s += 64) m = fmaxf(m, ml[2 * s]);
-  const float M = wave_max(m);
+  for (int s = tid; s < a.nsplit; s += 256) m = fmaxf(m, ml[2 * s]);
+  const float M = block_max_256(m, s_tmp);
   float l = 0.f;
-  for (int s = lane; s < a.nsplit; s += 64) l += ml[2 * s + 1] * exp2_fast(ml[2 * s] - M);
-  const float L = wave_sum(l);
-  const float w_lane = lane < a.nsplit ? exp2_fast(ml[2 * lane] - M) : 0.f;
-  float acc[2] = {0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < kPre; ++s) {
-    const float w = __shfl(w_lane, s);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[j] += pre[s][j] * w;
+  for (int s = tid; s < a.nsplit; s += 256) l += ml[2 * s + 1] * exp2_fast(ml[2 * s] - M);
+  const float L = block_sum_256(l, s_tmp);
+  const int D = a.D, nparts = 256 / D, d = tid % D, part = tid / D;
+  float acc = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += WCH) {
+    const int n = min(WCH, a.nsplit - s0);
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) s_w[i] = exp2_fast(ml[2 * (s0 + i)] - M);
+    __syncthreads();
+#pragma unroll 4
+    for (int i = part; i < n; i += nparts) acc += po[(int64_t)(s0 + i) * D + d] * s_w[i];
   }
-  for (int s = kPre; s < a.nsplit; ++s) {
-    const float w = exp2_fast(ml[2 * s] - M);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (j < nd) acc[j] += po[(int64_t)s * a.D + 64 * j + lane] * w;
+  s_acc[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float tot = 0.f;
+    for (int x = 0; x < nparts; ++x) tot += s_acc[x * D + d];
+    store_out<T>((T*)a.o + b * a.o_bstride + (int64_t)h * a.o_hstride + d, tot / L);
   }
-  T* out = (T*)a.o + b * a.o_bstride + (int64_t)h * a.o_hstride;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (j < nd) store_out<T>(out + 64 * j + lane, acc[j] / L);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1375,7 +1363,7 @@ static hipError_t attn_bf16_by_d(const DecodeArgs& a, dim3 grid, LaunchCtx& st) 
 // merge of the split partials into o
 static hipError_t launch_combine(const DecodeArgs& a, int dtype, LaunchCtx& ctx) {
   ctx.begin(K_DEC_COMBINE);
-  dim3 cgrid((unsigned)(((int64_t)a.B * a.Hq + 3) / 4));
+  dim3 cgrid(a.Hq, a.B);
   if (dtype == 1) KAS_LAUNCH((dec_combine_kernel<__bf16>), cgrid, dim3(256), ctx, a);
   else if (dtype == 2) KAS_LAUNCH((dec_combine_kernel<_Float16>), cgrid, dim3(256), ctx, a);
   else KAS_LAUNCH((dec_combine_kernel<float>), cgrid, dim3(256), ctx, a);
