@@ -456,20 +456,32 @@ __global__ __launch_bounds__(256) void sel_compact_kernel(DecodeArgs a) {
   const uint32_t* c = a.counts + (unit * a.n_sel_chunks + chunk) * 2;
   const uint32_t gt_before = c[0], eq_before = c[1];
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + unit * a.pstride);
-  // thread owns 16 consecutive keys
+  // thread owns 16 consecutive keys (16-byte loads inside the row)
   constexpr int PER = kSelChunk / 256;
   const int64_t j0 = (int64_t)chunk * kSelChunk + tid * PER;
   uint32_t u[PER];
+  if (j0 + PER <= a.N) {
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 v = ldg16(P + j0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) u[i] = (j0 + i < a.N) ? P[j0 + i] : 0u;
+  }
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    u[i] = (j0 + i < a.N) ? P[j0 + i] : 0u;
-    bool in = j0 + i < a.N;
-    gt += in && u[i] > tau;
-    eq += in && u[i] == tau;
+    const bool in = j0 + i < a.N;
+    gt += (in && u[i] > tau) ? 1u : 0u;
+    eq += (in && u[i] == tau) ? 1u : 0u;
   }
-  uint32_t g_ex = block_excl_scan_256(gt, s_tmp, nullptr) + gt_before;
-  uint32_t e_ex = block_excl_scan_256(eq, s_tmp, nullptr) + eq_before;
+  // both counts fit 16 bits (at most kSelChunk per chunk): one packed scan
+  const uint32_t ex = block_excl_scan_256((gt << 16) | eq, s_tmp, nullptr);
+  uint32_t g_ex = (ex >> 16) + gt_before;
+  uint32_t e_ex = (ex & 0xffffu) + eq_before;
   int32_t* out = a.idx_out + unit * a.kk;
   const uint32_t ku = unit_k(a, unit);
 #pragma unroll
@@ -643,14 +655,20 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(DecodeArgs a) {
 // 2 and 3 of the k-th largest from the candidates (bin b1 holds it), so tau
 // and r as in sel_fused_kernel; then per chunk the number of scores above tau
 // (its higher-bin count plus its candidates above tau) and equal to tau, and
-// their exclusive prefixes over the chunks for step 3. Wave w walks chunks
-// w, w + 16, ... (each chunk's candidates are contiguous).
+// their exclusive prefixes over the chunks for step 3. The candidates (the
+// chunks' lists, each contiguous) are copied into LDS once, wave w taking
+// chunks w, w + 16, ... with a chunk's loads issued together, and the three
+// passes run there; a bin too large for LDS is read from the lists in every
+// pass instead.
+constexpr int kResolveCap = 16384;   // LDS candidate list of one (b, g) (64 KB)
 __global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) {
   constexpr int NW = kSelThreads / 64;
   __shared__ uint32_t s_h[kBins2];
   __shared__ uint32_t s_gt[kMaxSelChunks];
   __shared__ uint32_t s_eq[kMaxSelChunks];
   __shared__ uint32_t s_nc[kMaxSelChunks];
+  __shared__ uint32_t s_off[kMaxSelChunks];
+  __shared__ uint32_t s_cand[kResolveCap];
   __shared__ uint32_t s_tmp[NW];
   __shared__ int s_res[2];
   const int64_t unit = blockIdx.x;
@@ -668,20 +686,55 @@ __global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) 
   int b1, b2, b3;
   uint32_t ab1, ab2, ab3;
   block_find_bin_nt<kSelThreads>(hist1, kBins1, k, s_tmp, s_res, b1, ab1);   // synchronises
-  for (int c = wave; c < nch; c += NW) {
-    const uint32_t* cc = cand + (int64_t)c * kSelChunk;
-    for (uint32_t i = lane; i < s_nc[c]; i += 64) atomicAdd(&s_h[(cc[i] >> 10) & 0x7ffu], 1u);
+  // offsets of the chunks' candidates in the LDS list
+  uint32_t ncand = 0;
+  for (int c0 = 0; c0 < nch; c0 += kSelThreads) {
+    const int c = c0 + tid;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kSelThreads>(c < nch ? s_nc[c] : 0u, s_tmp, &tot);
+    if (c < nch) s_off[c] = ncand + ex;
+    ncand += tot;
+  }
+  __syncthreads();
+  const bool staged = ncand <= (uint32_t)kResolveCap;
+  if (staged) {
+    for (int c = wave; c < nch; c += NW) {
+      const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+      const uint32_t n = s_nc[c], off = s_off[c];
+      for (uint32_t i0 = lane; i0 < n; i0 += 256) {
+        uint32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (i0 + 64 * q < n) ? cc[i0 + 64 * q] : 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (i0 + 64 * q < n) s_cand[off + i0 + 64 * q] = v[q];
+      }
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < ncand; i += kSelThreads) atomicAdd(&s_h[(s_cand[i] >> 10) & 0x7ffu], 1u);
+  } else {
+    for (int c = wave; c < nch; c += NW) {
+      const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+      for (uint32_t i = lane; i < s_nc[c]; i += 64) atomicAdd(&s_h[(cc[i] >> 10) & 0x7ffu], 1u);
+    }
   }
   __syncthreads();
   block_find_bin_nt<kSelThreads>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
   for (int i = tid; i < kBins3; i += kSelThreads) s_h[i] = 0u;
   __syncthreads();
   const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-  for (int c = wave; c < nch; c += NW) {
-    const uint32_t* cc = cand + (int64_t)c * kSelChunk;
-    for (uint32_t i = lane; i < s_nc[c]; i += 64) {
-      const uint32_t u = cc[i];
+  if (staged) {
+    for (uint32_t i = tid; i < ncand; i += kSelThreads) {
+      const uint32_t u = s_cand[i];
       if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
+    }
+  } else {
+    for (int c = wave; c < nch; c += NW) {
+      const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+      for (uint32_t i = lane; i < s_nc[c]; i += 64) {
+        const uint32_t u = cc[i];
+        if ((u >> 10) == pre) atomicAdd(&s_h[u & 0x3ffu], 1u);
+      }
     }
   }
   __syncthreads();
@@ -689,10 +742,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_resolve_kernel(DecodeArgs a) 
   const uint32_t tau = (pre << 10) | (uint32_t)b3;
   const uint32_t r = k - ab1 - ab2 - ab3;
   for (int c = wave; c < nch; c += NW) {
+    const uint32_t n = s_nc[c];
     const uint32_t* cc = cand + (int64_t)c * kSelChunk;
+    const uint32_t* lc = s_cand + s_off[c];
     uint32_t gt = 0, eq = 0;
-    for (uint32_t i = lane; i < s_nc[c]; i += 64) {
-      const uint32_t u = cc[i];
+    for (uint32_t i = lane; i < n; i += 64) {
+      const uint32_t u = staged ? lc[i] : cc[i];
       gt += u > tau ? 1u : 0u;
       eq += u == tau ? 1u : 0u;
     }

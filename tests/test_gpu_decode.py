@@ -140,8 +140,10 @@ def test_select_paths_agree(case, kas_options):
     digits 2 and 3 resolved per row) and the one-workgroup-per-row kernel
     (option KAS_OPT_DECODE_SELECT_ONE_PASS) give identical index sets and outputs, equal to
     the oracle's. With every score tied the first digit's bin holds all N
-    scores, more than the candidate list takes, so the resolve step sweeps the
-    row instead; the kept keys are then the k lowest indices."""
+    scores, more than either kernel's LDS candidate list takes: the one-pass
+    kernel then sweeps the row in every pass, the chunked resolve step reads
+    the chunks' lists in every pass (a random row takes the LDS paths); the
+    kept keys are then the k lowest indices."""
     kas = _kas()
     B, Hq, Hkv, D, pct = 1, 8, 2, 128, 10
     N = 40000 if case.startswith("random") else 70000
