@@ -312,24 +312,66 @@ __global__ __launch_bounds__(256) void dec_pool_kernel(DecodeArgs a) {
   const int g0 = ALL ? 0 : blockIdx.y;
   const int nh = ALL ? a.Hkv * G : G;                         // heads pooled into the set
   const int64_t unit = ALL ? b : (int64_t)b * a.Hkv + g0;     // set: pooled row, histogram
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kBins1; i += 256) s_hist[i] = 0u;
 
-  // head x of the set is query head r = x % G of KV head g0 + x / G
-  for (int x = 0; x < nh; ++x) {
-    const int64_t ug = (int64_t)b * a.Hkv + g0 + x / G;
-    const int h = x % G;
-    const float* st = a.stats + ug * a.n_score_chunks * G * 2;
-    float m = kNegInf;
-    for (int c = tid; c < a.n_score_chunks; c += 256) m = fmaxf(m, st[(c * G + h) * 2]);
-    const float M = block_max_256(m, s_tmp);
-    float l = 0.f;
-    for (int c = tid; c < a.n_score_chunks; c += 256) {
-      float mc = st[(c * G + h) * 2];
-      l += (mc == kNegInf) ? 0.f : st[(c * G + h) * 2 + 1] * exp2_fast(mc - M);
+  if (!ALL) {
+    // the G heads' statistics in one sweep over the chunks (per head the same
+    // arithmetic and reduction order as block_max_256 / block_sum_256)
+    __shared__ float s_red[4][G];
+    const float* st = a.stats + unit * a.n_score_chunks * G * 2;
+    float m[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) m[h] = kNegInf;
+    for (int c = tid; c < a.n_score_chunks; c += 256)
+#pragma unroll
+      for (int h = 0; h < G; ++h) m[h] = fmaxf(m[h], st[(c * G + h) * 2]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = wave_max(m[h]);
+      if (lane == 0) s_red[wave][h] = m[h];
     }
-    const float L = block_sum_256(l, s_tmp);
-    if (tid == 0) { s_M[x] = M; s_iL[x] = 1.0f / L; }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) m[h] = fmaxf(fmaxf(s_red[0][h], s_red[1][h]), fmaxf(s_red[2][h], s_red[3][h]));
+    float l[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) l[h] = 0.f;
+    for (int c = tid; c < a.n_score_chunks; c += 256)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mc = st[(c * G + h) * 2];
+        l[h] += (mc == kNegInf) ? 0.f : st[(c * G + h) * 2 + 1] * exp2_fast(mc - m[h]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      l[h] = wave_sum(l[h]);
+      if (lane == 0) s_red[wave][h] = l[h];
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int h = tid;
+      s_M[h] = m[h];
+      s_iL[h] = 1.0f / ((s_red[0][h] + s_red[1][h]) + (s_red[2][h] + s_red[3][h]));
+    }
+  } else {
+    // head x of the set is query head r = x % G of KV head g0 + x / G
+    for (int x = 0; x < nh; ++x) {
+      const int64_t ug = (int64_t)b * a.Hkv + g0 + x / G;
+      const int h = x % G;
+      const float* st = a.stats + ug * a.n_score_chunks * G * 2;
+      float m = kNegInf;
+      for (int c = tid; c < a.n_score_chunks; c += 256) m = fmaxf(m, st[(c * G + h) * 2]);
+      const float M = block_max_256(m, s_tmp);
+      float l = 0.f;
+      for (int c = tid; c < a.n_score_chunks; c += 256) {
+        float mc = st[(c * G + h) * 2];
+        l += (mc == kNegInf) ? 0.f : st[(c * G + h) * 2 + 1] * exp2_fast(mc - M);
+      }
+      const float L = block_sum_256(l, s_tmp);
+      if (tid == 0) { s_M[x] = M; s_iL[x] = 1.0f / L; }
+    }
   }
   __syncthreads();
   auto pool = [](float acc, float p) __attribute__((always_inline)) { return OP ? fmaxf(acc, p) : acc + p; };
