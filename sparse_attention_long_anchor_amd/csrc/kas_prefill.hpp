@@ -33,6 +33,11 @@ struct PrefillArgs {
   float* pooled;                    // pooled rows of the current tile range
   size_t pooled_floats;             // capacity of `pooled`
   int t_begin, t_end;               // tile range of the current pool/select launch
+  // per (b, KV head, tile): the first-digit bin of the k-th largest pooled
+  // score, the count above it and the bin's size (int4), found by the pooling
+  // pass; null when the rows change after pooling (pool_all), then the select
+  // histograms the rows itself
+  int32_t* sel_pre;
   int sel_cap;                      // select: largest first-digit bin resolved in LDS
   // selection variants: pooled score = sum (0) or max (1) over the tile's rows
   // and the heads; pool_all: one set per tile over all heads, Hsel sets per

@@ -12,8 +12,9 @@
 //               README "Abstract": tile-level, head-aware post-softmax
 //               pooling). Each lane owns one key of the block.
 //  pre_select   exact Top-k_t of each tile's pooled row (radix select over
-//               the fp32 bit pattern, ties to the lower index), written as
-//               ascending CSR indices.
+//               the fp32 bit pattern, ties to the lower index; the first
+//               digit's bin comes from pre_pool), written as ascending CSR
+//               indices.
 //  pre_attn     anchor output and reuse layers: one workgroup per (tile, KV
 //               head), gathered K rows and transposed V rows in LDS, S^T and
 //               P.V on MFMA, online softmax over the tile's index set plus
@@ -429,6 +430,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 // key block before a tile, each wave (query head) forms S = Q.K^T, the
 // probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
 // waves' sums are added through LDS (double-buffered, one barrier per block).
+// Unless the rows change afterwards (pooling over all heads), the writer
+// lanes also histogram the first digit (bits 31..21) of every pooled score
+// they write, and at the end the workgroup finds each tile's bin of the k-th
+// largest for the select (sel_pre), which then skips its histogram pass.
 template <int D, int G, int OP = 0, typename E = __bf16>
 __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   constexpr int KC = D / 16;
@@ -438,6 +443,9 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   __shared__ __align__(1024) char s_k1[KD::BLKB];
   __shared__ __align__(1024) char s_k2[KD::BLKB];
   __shared__ float s_col[2][2][G][64];
+  __shared__ uint32_t s_h1[2][kBins1];     // first-digit histograms of the two tiles' pooled rows
+  __shared__ uint32_t s_tmp[G];
+  __shared__ int s_res[2];
   const int pa0 = a.t_begin / 2;
   const int npairs = (a.t_end + 1) / 2 - pa0;
   const WorkItem it = work_item(blockIdx.x, npairs, a.Hkv, a.Hkv * a.B, true);
@@ -453,6 +461,11 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   const int n32 = lane & 31, hh = lane >> 5;
   const int h = g * G + w;
   const int64_t lse_off = ((int64_t)b * a.Hq + h) * a.N;   // row statistics of this head
+  // cleared before the first block's end barrier, whose wait covers LDS stores;
+  // every histogram update comes after that barrier
+  const bool hist = a.sel_pre != nullptr;
+  if (hist)
+    for (int i = threadIdx.x; i < 2 * kBins1; i += 64 * G) (&s_h1[0][0])[i] = 0u;
   u32x4 qa0[KC], qa1[KC];
   float lse0[16], lse1[16];
   {
@@ -551,6 +564,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < G; ++x) sum = pool(sum, s_col[kb & 1][tile][x][n32]);
       (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
+      if (hist) atomicAdd(&s_h1[tile][__float_as_uint(sum) >> 21], 1u);
     }
   };
   const int w1 = G > 1 ? 1 : 0;
@@ -604,6 +618,22 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
       emit(0, kb, 0);
     }
   }
+  // each tile's first-digit bin of the k-th largest pooled score, for the select
+  if (hist) {
+    __syncthreads();
+    for (int tile = 0; tile < (has1 ? 2 : 1); ++tile) {
+      const int t = tile ? t1 : t0;
+      const uint32_t kt = (uint32_t)(a.offsets[t + 1] - a.offsets[t]);
+      if (t >= 1 && kt > 0 && kt < (uint32_t)(kTile * t)) {   // uniform over the workgroup
+        int b1;
+        uint32_t ab1;
+        block_find_bin_nt<64 * G>(s_h1[tile], kBins1, kt, s_tmp, s_res, b1, ab1);
+        if (threadIdx.x == 0)
+          reinterpret_cast<int4*>(a.sel_pre)[((int64_t)b * a.Hkv + g) * a.T + t] =
+              int4{b1, (int)ab1, (int)s_h1[tile][b1], 0};
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ pooling over all heads
@@ -633,9 +663,9 @@ __global__ __launch_bounds__(256) void pre_pool_heads_kernel(PrefillArgs a) {
 
 // One workgroup per (tile, KV head): an exact radix select over the tile's
 // pooled row (n = 32 t scores, rows 128-byte aligned, so every access is a
-// whole 16-byte load): the first digit (bits 31..21) histogrammed over the
-// row; the scores of the k-th largest's bin collected into LDS in a second
-// pass, digits 2 (bits 20..10) and 3 (bits 9..0) resolved there (a bin too
+// whole 16-byte load): the bin of the k-th largest's first digit (bits
+// 31..21), from the pooling pass (sel_pre) or a histogram pass over the row;
+// the scores of that bin collected into LDS in a pass over the row, digits 2 (bits 20..10) and 3 (bits 9..0) resolved there (a bin too
 // large for LDS is histogrammed in two more passes over the row instead); a
 // last pass writes the kept keys in index order (P > tau, then the first r
 // keys equal to tau) through workgroup scans. Passes keep four 16-byte loads
@@ -678,23 +708,34 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
       for (int q = 0; q < 4; ++q) fn(v[q], i0 + 256 * q < n4);
     }
   };
-  for (int i = tid; i < kBins1; i += 256) s_h[i] = 0u;
-  if (tid == 0) s_nc = 0u;
-  __syncthreads();
-  pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
-    if (ok) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&s_h[v[e] >> 21], 1u);
-    }
-  });
-  __syncthreads();
   int b1, b2, b3;
-  uint32_t ab1, ab2, ab3;
-  block_find_bin(s_h, kBins1, k, s_tmp, s_res, b1, ab1);
-  const uint32_t nb1 = s_h[b1];
-  __syncthreads();
-  for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
-  __syncthreads();
+  uint32_t ab1, ab2, ab3, nb1;
+  if (a.sel_pre) {
+    // the pooling pass histogrammed the row's first digit and found its bin
+    const int4 pre = reinterpret_cast<const int4*>(a.sel_pre)[((int64_t)b * a.Hsel + g) * a.T + t];
+    b1 = pre.x;
+    ab1 = (uint32_t)pre.y;
+    nb1 = (uint32_t)pre.z;
+    for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
+    if (tid == 0) s_nc = 0u;
+    __syncthreads();
+  } else {
+    for (int i = tid; i < kBins1; i += 256) s_h[i] = 0u;
+    if (tid == 0) s_nc = 0u;
+    __syncthreads();
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&s_h[v[e] >> 21], 1u);
+      }
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins1, k, s_tmp, s_res, b1, ab1);
+    nb1 = s_h[b1];
+    __syncthreads();
+    for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
+    __syncthreads();
+  }
   if (nb1 <= (uint32_t)a.sel_cap) {
     // the bin's scores into LDS (wave-aggregated appends), digits 2 and 3 there
     pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
@@ -1161,7 +1202,7 @@ static int64_t max_chunk_floats(int T, int64_t units, int64_t budget) {
 }
 
 struct PrefillPlan {
-  size_t off_offsets, off_lse, off_pooled, total;
+  size_t off_offsets, off_lse, off_pooled, off_sel_pre, total;
   int64_t pooled_floats;
 };
 
@@ -1175,6 +1216,7 @@ static PrefillPlan plan(int B, int Hq, int Hkv, int64_t N, bool anchor) {
     p.off_lse = take((size_t)B * Hq * N * sizeof(float));
     p.pooled_floats = max_chunk_floats(T, (int64_t)B * Hkv, pool_budget_floats());
     p.off_pooled = take((size_t)(p.pooled_floats > 0 ? p.pooled_floats : 1) * sizeof(float));
+    p.off_sel_pre = take((size_t)B * Hkv * T * 4 * sizeof(int32_t));
   }
   p.total = off;
   return p;
@@ -1205,6 +1247,7 @@ void fill_prefill_args(PrefillArgs& a, int B, int Hq, int Hkv, int D, int64_t N,
     a.lse = (float*)(ws + p.off_lse);
     a.pooled = (float*)(ws + p.off_pooled);
     a.pooled_floats = (size_t)p.pooled_floats;
+    a.sel_pre = (int32_t*)(ws + p.off_sel_pre);
   }
 }
 
@@ -1260,6 +1303,7 @@ hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) { return launch_
 
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   hipError_t e;
+  if (a.pool_all) a.sel_pre = nullptr;   // the heads' rows are summed after pooling
   if ((e = launch_offsets(a, ctx)) != hipSuccess) return e;
   if (!grid_fits((int64_t)((a.T + 1) / 2) * a.Hkv * a.B)) return hipErrorInvalidConfiguration;
   ctx.begin(K_PRE_STATS);
