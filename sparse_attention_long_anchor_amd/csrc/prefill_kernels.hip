@@ -665,8 +665,9 @@ __global__ __launch_bounds__(256) void pre_pool_heads_kernel(PrefillArgs a) {
 // pooled row (n = 32 t scores, rows 128-byte aligned, so every access is a
 // whole 16-byte load): the bin of the k-th largest's first digit (bits
 // 31..21), from the pooling pass (sel_pre) or a histogram pass over the row;
-// the scores of that bin collected into LDS in a pass over the row, digits 2 (bits 20..10) and 3 (bits 9..0) resolved there (a bin too
-// large for LDS is histogrammed in two more passes over the row instead); a
+// the scores of that bin collected into LDS in a pass over the row, digits 2
+// (bits 20..10) and 3 (bits 9..0) resolved there (a bin too large for LDS is
+// histogrammed in two more passes over the row instead); a
 // last pass writes the kept keys in index order (P > tau, then the first r
 // keys equal to tau) through workgroup scans. Passes keep four 16-byte loads
 // per thread in flight (indices past the row re-read its last vector and are
