@@ -335,8 +335,9 @@ kas_status_t kas_decode_refine_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
 typedef enum {
   KAS_OPT_DECODE_SPLIT_ROWS = 0,    /* index-set rows per decode gather workgroup, 16..2048
                                        (default -1: sized so one wave of workgroups covers the chip) */
-  KAS_OPT_DECODE_SELECT_ONE_PASS = 1, /* 1: decode Top-k by one workgroup per index set; 0 (default):
-                                         spread over the chip in three launches */
+  KAS_OPT_DECODE_SELECT_ONE_PASS = 1, /* 1: decode Top-k by one workgroup per index set (one launch);
+                                         0: spread over the chip in three launches; default -1: one
+                                         workgroup per set for sets of at most 8192 keys, else spread */
   KAS_OPT_PREFILL_POOL_MB = 2,      /* cap of the prefill pooled-score buffer, MiB (default 16384);
                                        longer prompts run their pooling and selection in tile ranges */
   KAS_OPT_PREFILL_SELECT_CAP = 3,   /* 0..8192 (default 8192): the largest first-digit bin the prefill

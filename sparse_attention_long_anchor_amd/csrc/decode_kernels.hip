@@ -1401,9 +1401,12 @@ hipError_t launch_decode_pool(const DecodeArgs& a, LaunchCtx& ctx) {
 }
 
 hipError_t launch_decode_select(const DecodeArgs& a, LaunchCtx& ctx) {
-  // the one-workgroup-per-set kernel: when selected by the tuning option, and
-  // when there are more chunks than the chunked path resolves in LDS
-  if (option_value(KAS_OPT_DECODE_SELECT_ONE_PASS) == 1 || a.n_sel_chunks > kMaxSelChunks) {
+  // the one-workgroup-per-set kernel: when selected by the tuning option, by
+  // default for sets of at most two chunks (one launch instead of three:
+  // 58 against 63 us for a 2K anchor layer, even at 32K, 26 us slower at
+  // 128K), and when there are more chunks than the chunked path resolves in LDS
+  const int64_t one = option_value(KAS_OPT_DECODE_SELECT_ONE_PASS);
+  if (one == 1 || (one == -1 && a.n_sel_chunks <= 2) || a.n_sel_chunks > kMaxSelChunks) {
     ctx.begin(K_SEL_FUSED);
     KAS_LAUNCH(sel_fused_kernel, dim3((unsigned)a.sel_units), dim3(kSelThreads), ctx, a);
     return ctx.end(K_SEL_FUSED);

@@ -134,29 +134,33 @@ def test_exact_ties_take_lowest_indices():
     assert (oidx == np.arange(300, 400)).all()
 
 
-@pytest.mark.parametrize("case", ["random_n40000", "all_tied_n70000"])
+@pytest.mark.parametrize("case", ["random_n3000", "random_n40000", "all_tied_n70000"])
 def test_select_paths_agree(case, kas_options):
     """The chunked selection (per-chunk candidates of the first digit's bin,
     digits 2 and 3 resolved per row) and the one-workgroup-per-row kernel
-    (option KAS_OPT_DECODE_SELECT_ONE_PASS) give identical index sets and outputs, equal to
-    the oracle's. With every score tied the first digit's bin holds all N
-    scores, more than either kernel's LDS candidate list takes: the one-pass
-    kernel then sweeps the row in every pass, the chunked resolve step reads
-    the chunks' lists in every pass (a random row takes the LDS paths); the
-    kept keys are then the k lowest indices."""
+    (KAS_OPT_DECODE_SELECT_ONE_PASS 0 and 1; the default takes the one-pass
+    kernel for rows of at most 8192 keys) give identical index sets and
+    outputs, equal to the oracle's. With every score tied the first digit's
+    bin holds all N scores, more than either kernel's LDS candidate list
+    takes: the one-pass kernel then sweeps the row in every pass, the chunked
+    resolve step reads the chunks' lists in every pass (a random row takes the
+    LDS paths); the kept keys are then the k lowest indices."""
     kas = _kas()
     B, Hq, Hkv, D, pct = 1, 8, 2, 128, 10
-    N = 40000 if case.startswith("random") else 70000
+    N = int(case.split("_n")[1])
     w = inputgen.custom("decode", B, Hq, Hkv, D, N, "bf16", wid=23)
     q, k, v = inputgen.layer_inputs(w, 0, DEV)
     if case.startswith("all_tied"):
         k = torch.zeros_like(k)
     _say(f"[decode select paths] {case}")
+    idx0, o0 = kas.decode_anchor(q, k, v, pct)
+    kas_options(kas.OPT_DECODE_SELECT_ONE_PASS, 0)
     idx1, o1 = kas.decode_anchor(q, k, v, pct)
     kas_options(kas.OPT_DECODE_SELECT_ONE_PASS, 1)
     idx2, o2 = kas.decode_anchor(q, k, v, pct)
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2) and torch.equal(o1, o2)
+    assert torch.equal(idx0, idx1) and torch.equal(o0, o1)
     oidx, oo, _ = oracle.decode_anchor(_np(q), _np(k), _np(v), pct)
     np.testing.assert_array_equal(idx1.cpu().numpy(), oidx)
     assert max_abs(_np(o1), oo) <= TOL["bf16"]
