@@ -18,6 +18,7 @@ pages state their speed-ups against, and the speed-up of the Kascade step over
 the dense step is reported as well (outside the timed region).
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -243,6 +244,33 @@ def cpu_baseline(wd, dec_state, wp, pre_state, budget_s, inputgen, extra):
 OTHER_CONFIGS = ("tiny_decode_2k", "llama8b_decode_32k", "qwen8b_prefill_32k")
 
 
+def graph_step_ms(w, st, run, steps, torch, inputgen, kas):
+    """Mean device time of one step captured in a HIP graph and replayed (the
+    step's calls only enqueue kernels on the current stream, so they capture
+    as they are); small decode steps are bound by host launch work otherwise."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(w, st, inputgen, kas)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(w, st, inputgen, kas)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(max(steps, 3))]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = _mean([a.elapsed_time(b) for a, b in ev])
+    del g
+    return ms
+
+
 def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
     """One workload's own schedule (every layer resident): `warmup` untimed
     steps, `steps` steps with events around each step, the same steps with an
@@ -254,6 +282,7 @@ def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
     log(f"[bench] config {name}: generating {w.n_layers} layers")
     st = (build_decode if dec else build_prefill)(w, dev, torch, inputgen, kas)
     run = run_decode_step if dec else run_prefill_step
+    gc.collect()
     for _ in range(warmup):
         run(w, st, inputgen, kas)
     torch.cuda.synchronize()
@@ -264,6 +293,8 @@ def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
         e[1].record()
     torch.cuda.synchronize()
     step_ms = _mean([a.elapsed_time(b) for a, b in ev])
+    log(f"[bench] config {name}: eager steps (ms) {[round(a.elapsed_time(b), 3) for a, b in ev]}")
+    graph_ms = graph_step_ms(w, st, run, steps, torch, inputgen, kas) if dec else None
     lay = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(w.n_layers)] for _ in range(steps)]
     for s_ in range(steps):
@@ -297,7 +328,10 @@ def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
                          "reuse": _rate(reuse_b, _mean(reu) * 1e-3, 1e9),
                          "step": _rate(step_b, step_ms * 1e-3, 1e9)},
             "ms_per_step": round(step_ms, 4),
-            "tokens_per_s": round(w.batch / (step_ms * 1e-3), 2)})
+            "tokens_per_s": round(w.batch / (step_ms * 1e-3), 2),
+            "graph": {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(w.batch / (graph_ms * 1e-3), 2),
+                      "GB_per_s": _rate(step_b, graph_ms * 1e-3, 1e9),
+                      "note": "the whole step captured once in a HIP graph and replayed: no host launch work"}})
         ops = {"decode_attn": len(reu), "decode_attn_anchor": len(anc), "decode_score": len(anc)}
         for kname, b in kern_b.items():
             if kname in kern:
@@ -344,6 +378,7 @@ def config_record(name, steps, warmup, dev, torch, inputgen, kas, cpu_budget):
 # ---------------------------------------------------------------- main
 
 def main():
+    gc.disable()   # collected explicitly between measurements
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
@@ -404,6 +439,9 @@ def main():
         log(f"[bench] generating {wp.name} ({wp.n_layers} layers)")
         pre_state = build_prefill(wp, dev, torch, inputgen, kas)
     torch.cuda.synchronize()
+    # the collector runs only between measurements: a collection inside a timed
+    # host-bound step would leave the GPU idle for milliseconds
+    gc.collect()
 
     for i in range(args.warmup):
         if do_dec:
