@@ -111,6 +111,14 @@ typedef struct kas_desc {
    * overlap (KAS_ERR_INVALID_ARGUMENT). */
   int64_t q_batch_stride, q_head_stride, q_token_stride;
   int64_t o_batch_stride, o_head_stride, o_token_stride;
+  /* Anchor calls only (others ignore it). 0: the layer's output attends over
+   * its own selected set, as a reuse layer with the identity map would (the
+   * reading this library takes; the README "Abstract" leaves it open); 1: the
+   * output is dense attention over all keys (causal in prefill), computed as
+   * kas_decode_dense / kas_prefill_dense compute it, with the sets selected
+   * exactly as with 0. For comparisons against schedules whose anchor layers
+   * attend densely. */
+  int32_t anchor_dense_output;
 } kas_desc_t;
 
 /* round-half-up(pct * n / 100) clamped to [0, n]; 0 for n <= 0 or pct <= 0.

@@ -52,6 +52,7 @@ class KasDesc(ctypes.Structure):
         ("o_batch_stride", ctypes.c_int64),
         ("o_head_stride", ctypes.c_int64),
         ("o_token_stride", ctypes.c_int64),
+        ("anchor_dense_output", ctypes.c_int32),
     ]
 
 
@@ -155,7 +156,7 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
               topk_pct: int, dtype: torch.dtype, tile: int = 32, softmax_scale: float = 0.0,
               kv_batch_stride: int = 0, kv_head_stride: int = 0, pool_scope: int = 0,
               pool_op: int = 0, query_head_map: int = 0, q_strides=(0, 0, 0),
-              o_strides=(0, 0, 0)) -> KasDesc:
+              o_strides=(0, 0, 0), anchor_dense_output: int = 0) -> KasDesc:
     if dtype == torch.bfloat16:
         dt = DTYPE_BF16
     elif dtype == torch.float16:
@@ -166,7 +167,7 @@ def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, seq_le
         raise KasError(2, "make_desc", f"dtype {dtype} not supported")
     return KasDesc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, topk_pct, tile, dt,
                    softmax_scale, kv_batch_stride, kv_head_stride, pool_scope, pool_op, query_head_map,
-                   *q_strides, *o_strides)
+                   *q_strides, *o_strides, anchor_dense_output)
 
 
 def topk_count(n: int, pct: int) -> int:
@@ -242,7 +243,7 @@ def _new_out(q: torch.Tensor) -> torch.Tensor:
 
 def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale: float,
                tile: int = 32, pool_scope: int = 0, pool_op: int = 0, query_head_map: int = 0,
-               o: Optional[torch.Tensor] = None) -> KasDesc:
+               o: Optional[torch.Tensor] = None, anchor_dense_output: int = 0) -> KasDesc:
     if prefill:
         B, Hq, N, D = q.shape
     else:
@@ -254,7 +255,8 @@ def _desc_from(q: torch.Tensor, k: torch.Tensor, pct: int, prefill: bool, scale:
     return make_desc(B, Hq, Hkv, D, N, pct, q.dtype, tile=tile, softmax_scale=scale,
                      kv_batch_stride=k.stride(0), kv_head_stride=k.stride(1),
                      pool_scope=pool_scope, pool_op=pool_op, query_head_map=query_head_map,
-                     q_strides=_row_strides(q, "q"), o_strides=_row_strides(q if o is None else o, "o"))
+                     q_strides=_row_strides(q, "q"), o_strides=_row_strides(q if o is None else o, "o"),
+                     anchor_dense_output=anchor_dense_output)
 
 
 def _cache(q, k, seq_lens, block_table, seq_len):
@@ -298,16 +300,18 @@ def _ws_kv(desc, cache, op, ws, device):
 
 def decode_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
                   pool_scope: int = 0, pool_op: int = 0, seq_lens=None, block_table=None,
-                  seq_len=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  seq_len=None, dense_output: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """q [B,Hq,D], k/v [B,Hkv,N,D] -> (idx int32 [B,Hs,kd], o [B,Hq,D]); Hs = Hkv, or 1
     with pool_scope=1 (one set pooled over all heads). seq_lens (device int32 [B])
     gives each sequence's length; block_table (device int32 [B, max_pages]) makes
     k, v page pools [num_pages, Hkv, P, D] (then seq_len = the longest sequence).
-    q and o may be strided views with a contiguous head_dim."""
+    q and o may be strided views with a contiguous head_dim. dense_output: o is
+    dense attention over all keys (the sets are selected as usual)."""
     o = _new_out(q) if o is None else o
     _check_tensors("decode_anchor", q, k, v, o, idx_out=idx_out, seq_lens=seq_lens, block_table=block_table)
     over, cache = _cache(q, k, seq_lens, block_table, seq_len)
-    desc = _decode_desc(q, k, pct, scale, over, o, pool_scope=pool_scope, pool_op=pool_op)
+    desc = _decode_desc(q, k, pct, scale, over, o, pool_scope=pool_scope, pool_op=pool_op,
+                        anchor_dense_output=int(dense_output))
     if k.stride() != v.stride():
         raise KasError(1, "decode_anchor", "k and v must share strides")
     kd = decode_k(desc.seq_len, pct)
@@ -384,15 +388,17 @@ def _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, **kw):
 
 def prefill_anchor(q, k, v, pct: int, scale: float = 0.0, idx_out=None, o=None, ws=None,
                    pool_scope: int = 0, pool_op: int = 0, seq_lens=None,
-                   block_table=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   block_table=None, dense_output: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 or fp16 -> (idx int32 [B,Hs,total] CSR,
     o [B,Hq,N,D]); Hs as in decode_anchor. seq_lens (device int32 [B]) gives each
     prompt's length; block_table (device int32 [B, max_pages]) makes k, v page
     pools [num_pages, Hkv, P, D]. q and o may be strided views (for example the
-    [B,N,Hq,D] projection output transposed) with a contiguous head_dim."""
+    [B,N,Hq,D] projection output transposed) with a contiguous head_dim.
+    dense_output: o is dense causal attention (the sets are selected as usual)."""
     o = _new_out(q) if o is None else o
     _check_tensors("prefill_anchor", q, k, v, o, idx_out=idx_out, seq_lens=seq_lens, block_table=block_table)
-    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, pool_scope=pool_scope, pool_op=pool_op)
+    desc, c = _prefill_desc(q, k, pct, scale, seq_lens, block_table, o, pool_scope=pool_scope, pool_op=pool_op,
+                            anchor_dense_output=int(dense_output))
     if k.stride() != v.stride():
         raise KasError(1, "prefill_anchor", "k and v must share strides")
     total = int(prefill_offsets(desc)[-1])

@@ -115,6 +115,7 @@ struct Shape {
   int pct, tile, dtype;
   int scope, op;                    // anchor pooling variant (kas_desc_t.pool_scope / pool_op)
   int qmap;                         // reuse: head_map per query head (kas_desc_t.query_head_map)
+  int dense_out;                    // anchor: dense output (kas_desc_t.anchor_dense_output)
   float scale;
   int64_t kv_hs, kv_bs;
   int64_t q_bs, q_hs, q_ts, o_bs, o_hs, o_ts;   // element strides of q and o
@@ -155,6 +156,8 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
     return fail(KAS_ERR_INVALID_ARGUMENT, "pool_scope and pool_op must be 0 or 1");
   if (d->query_head_map != 0 && d->query_head_map != 1)
     return fail(KAS_ERR_INVALID_ARGUMENT, "query_head_map must be 0 or 1");
+  if (d->anchor_dense_output != 0 && d->anchor_dense_output != 1)
+    return fail(KAS_ERR_INVALID_ARGUMENT, "anchor_dense_output must be 0 or 1");
   if (d->pool_scope == 1 && d->n_q_heads > kMaxPoolHeads)
     return fail(KAS_ERR_UNSUPPORTED, "pooling over all heads supports at most %d query heads", kMaxPoolHeads);
   if (prefill) {
@@ -164,7 +167,7 @@ static kas_status_t check_desc(const kas_desc_t* d, bool prefill, Shape& s) {
   }
   s.B = d->batch; s.Hq = d->n_q_heads; s.Hkv = d->n_kv_heads; s.D = d->head_dim; s.G = G;
   s.N = d->seq_len; s.pct = d->topk_pct; s.tile = d->tile; s.dtype = d->dtype;
-  s.scope = d->pool_scope; s.op = d->pool_op; s.qmap = d->query_head_map;
+  s.scope = d->pool_scope; s.op = d->pool_op; s.qmap = d->query_head_map; s.dense_out = d->anchor_dense_output;
   s.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
   s.esize = d->dtype == KAS_DTYPE_F32 ? 4 : 2;
   s.kv_hs = d->kv_head_stride ? d->kv_head_stride : s.N * s.D;
@@ -507,6 +510,38 @@ kas_status_t kas_prefill_index_offsets(const kas_desc_t* desc, int64_t* offsets,
   return KAS_OK;
 }
 
+// An anchor call's workspace: its own plan, or with a dense output the larger
+// of that and the dense plan (the dense output runs after the selection and
+// reuses the workspace from its start).
+static size_t decode_anchor_need(const Shape& s, bool paged) {
+  size_t need = plan_decode(s, true, false, paged).total;
+  if (s.dense_out) need = std::max(need, plan_decode(s, false, true, paged).total);
+  return need;
+}
+
+// Dense decode attention over every key of each sequence: split-K gather
+// over the keys (paged: their physical rows first) and the merge.
+static hipError_t run_decode_dense(const Shape& s, const CacheView& cv, const void* q, const void* k, const void* v,
+                                   void* o, char* ws, LaunchCtx& ctx, const char** where) {
+  const DecodePlan p = plan_decode(s, false, true, cv.paged());
+  DecodeArgs a;
+  fill_decode_args(s, p, false, ws, a);
+  fill_cache(a, cv, s);
+  a.rows_are_keys = 1;       // a sequence's "set" is all its keys
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr;
+  hipError_t e;
+  if (cv.paged()) {
+    a.page_src = nullptr;
+    a.page_src_sets = 1;
+    *where = "decode_page_rows";
+    if ((e = launch_page_rows(a, 1, ctx)) != hipSuccess) return e;
+    a.idx = (const int32_t*)a.prow; a.Hkv_a = 1;
+  }
+  *where = "decode_dense";
+  return launch_decode_dense(a, s.dtype, ctx);
+}
+
 kas_status_t kas_workspace_size(const kas_desc_t* desc, int32_t op, size_t* bytes) {
   return kas_workspace_size_kv(desc, nullptr, op, bytes);
 }
@@ -524,8 +559,10 @@ kas_status_t kas_workspace_size_kv(const kas_desc_t* desc, const kas_kv_cache_t*
     *bytes = prefill_need(0, s, cv);
   } else if (op == KAS_OP_DECODE_REUSE && s.qmap) {
     *bytes = plan_decode(per_query_head(s), false, false, cv.paged()).total;
+  } else if (op == KAS_OP_DECODE_ANCHOR) {
+    *bytes = decode_anchor_need(s, cv.paged());
   } else if (!prefill) {
-    *bytes = plan_decode(s, op == KAS_OP_DECODE_ANCHOR, op == KAS_OP_DECODE_DENSE, cv.paged()).total;
+    *bytes = plan_decode(s, false, op == KAS_OP_DECODE_DENSE, cv.paged()).total;
   } else {
     const Shape sr = (op == KAS_OP_PREFILL_REUSE && s.qmap) ? per_query_head(s) : s;
     *bytes = prefill_need(prefill_workspace_bytes(sr.B, sr.Hq, sr.Hkv, sr.D, sr.N, sr.pct, op == KAS_OP_PREFILL_ANCHOR),
@@ -552,7 +589,7 @@ kas_status_t kas_decode_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
     return st;
   if (!idx_out) return fail(KAS_ERR_INVALID_ARGUMENT, "idx_out is NULL");
   DecodePlan p = plan_decode(s, true, false, cv.paged());
-  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
+  if ((st = check_ws(ws, ws_bytes, decode_anchor_need(s, cv.paged())))) return st;
   DecodeArgs a;
   fill_decode_args(s, p, true, (char*)ws, a);
   fill_cache(a, cv, s);
@@ -565,6 +602,11 @@ kas_status_t kas_decode_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t* 
   if ((e = launch_decode_score(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_score");
   if ((e = launch_decode_pool(a, ctx)) != hipSuccess) return hip_fail(e, "decode_pool");
   if ((e = launch_decode_select(a, ctx)) != hipSuccess) return hip_fail(e, "decode_select");
+  if (s.dense_out) {
+    const char* where = "decode_dense";
+    if ((e = run_decode_dense(s, cv, q, k, v, o, (char*)ws, ctx, &where)) != hipSuccess) return hip_fail(e, where);
+    return KAS_OK;
+  }
   if (cv.paged()) {
     // physical rows of every KV head's set, then the output from them
     a.page_src = idx_out;
@@ -675,6 +717,7 @@ kas_status_t kas_prefill_anchor_kv(const kas_desc_t* desc, const kas_kv_cache_t*
   a.pool_op = s.op; a.pool_all = s.scope; a.Hsel = s.scope ? 1 : s.Hkv;
   a.idx = idx_out; a.Hkv_a = a.Hsel; a.head_map = nullptr; a.total = total;
   a.seq_lens = cv.seq_lens;
+  a.dense_out = s.dense_out;
   LaunchCtx ctx{(hipStream_t)stream};
   hipError_t e;
   if (cv.paged() && (e = prefill_paged_kv(cv, s, k, v, (char*)ws, base, a, ctx)) != hipSuccess)
@@ -749,23 +792,11 @@ kas_status_t kas_decode_dense_kv(const kas_desc_t* desc, const kas_kv_cache_t* c
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")))
     return st;
-  DecodePlan p = plan_decode(s, false, true, cv.paged());
-  if ((st = check_ws(ws, ws_bytes, p.total))) return st;
-  DecodeArgs a;
-  fill_decode_args(s, p, false, (char*)ws, a);
-  fill_cache(a, cv, s);
-  a.rows_are_keys = 1;       // a sequence's "set" is all its keys
-  a.q = q; a.k = k; a.v = v; a.o = o;
-  a.idx = nullptr; a.Hkv_a = s.Hkv; a.head_map = nullptr;
+  if ((st = check_ws(ws, ws_bytes, plan_decode(s, false, true, cv.paged()).total))) return st;
   LaunchCtx ctx{(hipStream_t)stream};
-  hipError_t e;
-  if (cv.paged()) {
-    a.page_src = nullptr;
-    a.page_src_sets = 1;
-    if ((e = launch_page_rows(a, 1, ctx)) != hipSuccess) return hip_fail(e, "decode_page_rows");
-    a.idx = (const int32_t*)a.prow; a.Hkv_a = 1;
-  }
-  if ((e = launch_decode_dense(a, s.dtype, ctx)) != hipSuccess) return hip_fail(e, "decode_dense");
+  const char* where = "decode_dense";
+  hipError_t e = run_decode_dense(s, cv, q, k, v, o, (char*)ws, ctx, &where);
+  if (e != hipSuccess) return hip_fail(e, where);
   return KAS_OK;
 }
 

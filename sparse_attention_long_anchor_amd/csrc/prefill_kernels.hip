@@ -1344,7 +1344,7 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
     if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;
     ta = tb;
   }
-  return launch_attn(a, ctx);
+  return a.dense_out ? launch_prefill_dense(a, ctx) : launch_attn(a, ctx);
 }
 
 hipError_t launch_prefill_page_copy(const PageCopyArgs& c, LaunchCtx& ctx) {

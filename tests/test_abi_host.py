@@ -346,3 +346,25 @@ def test_noalloc_reuse_checks_without_gpu():
     r = L.kas_decode_reuse_noalloc(ctypes.byref(ok), None, fake, fake, fake, 8, None, fake, None)
     assert r == 1 and b"q is NULL" in L.kas_last_error()
     assert L.kas_decode_reuse_noalloc(None, fake, fake, fake, fake, 8, None, fake, None) == 1
+
+
+def test_anchor_dense_output_flag_without_gpu():
+    """anchor_dense_output takes 0 or 1. With 1 a decode anchor's workspace is
+    the larger of its own plan and the dense plan (the dense output reuses the
+    workspace after the selection); prefill needs no more room."""
+    import torch
+    b = _kas()
+    for d0, d1 in ((b.make_desc(1, 8, 2, 128, 2048, 10, torch.bfloat16),
+                    b.make_desc(1, 8, 2, 128, 2048, 10, torch.bfloat16, anchor_dense_output=1)),
+                   (b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16),
+                    b.make_desc(4, 32, 8, 128, 131072, 10, torch.bfloat16, anchor_dense_output=1))):
+        a0, a1 = b.workspace_size(d0, b.OP_DECODE_ANCHOR), b.workspace_size(d1, b.OP_DECODE_ANCHOR)
+        assert a1 == max(a0, b.workspace_size(d0, b.OP_DECODE_DENSE))
+        # other calls ignore the flag
+        assert b.workspace_size(d1, b.OP_DECODE_REUSE) == b.workspace_size(d0, b.OP_DECODE_REUSE)
+    p0 = b.make_desc(1, 8, 2, 128, 4096, 10, torch.bfloat16)
+    p1 = b.make_desc(1, 8, 2, 128, 4096, 10, torch.bfloat16, anchor_dense_output=1)
+    assert b.workspace_size(p1, b.OP_PREFILL_ANCHOR) == b.workspace_size(p0, b.OP_PREFILL_ANCHOR)
+    bad = b.make_desc(1, 8, 2, 128, 2048, 10, torch.bfloat16, anchor_dense_output=2)
+    assert _status(lambda: b.workspace_size(bad, b.OP_DECODE_ANCHOR)) == 1
+    assert b"anchor_dense_output" in b._load().kas_last_error()

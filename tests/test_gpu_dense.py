@@ -147,3 +147,76 @@ def test_prefill_dense_full_size_sampled_rows(name, rows):
     _say(f"    max|o-o_oracle| over sampled rows={worst:.3g}")
     assert worst <= TOL["bf16"]
     assert torch.isfinite(o.float()).all()
+
+
+# ---------------------------------------------------------------- anchor layers with a dense output
+
+ANCHOR_DENSE = [
+    # (label, phase, B, Hq, Hkv, D, N, dtype, varlen, page size)
+    ("decode_bf16_g4", "decode", 2, 32, 8, 128, 5037, "bf16", False, None),
+    ("decode_f32_d64", "decode", 1, 8, 2, 64, 2048, "f32", False, None),
+    ("decode_f16_varlen_paged", "decode", 3, 8, 2, 128, 3001, "f16", True, 64),
+    ("prefill_bf16_g4", "prefill", 1, 8, 2, 128, 640, "bf16", False, None),
+    ("prefill_f16_varlen", "prefill", 2, 8, 4, 64, 352, "f16", True, None),
+    ("prefill_bf16_paged", "prefill", 1, 8, 2, 128, 512, "bf16", False, 32),
+]
+
+
+@pytest.mark.parametrize("case", ANCHOR_DENSE, ids=[c[0] for c in ANCHOR_DENSE])
+def test_anchor_dense_output(case):
+    """kas_desc_t.anchor_dense_output = 1: the anchor call selects exactly the
+    sets it selects without the flag (bit for bit) and writes the dense
+    attention of the dense call (bit for bit), which the oracle's dense
+    attention checks as well."""
+    kas = _kas()
+    label, phase, B, Hq, Hkv, D, N, dt, varlen, P = case
+    w = inputgen.custom(phase, B, Hq, Hkv, D, N, dt, wid=zlib.crc32(label.encode()) % 1000 + 3, topk_pct=10)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    kc, vc = k, v                     # the contiguous cache, for the oracle
+    kw = {}
+    lens = None
+    if varlen:
+        lens = np.array([N, N // 2, 96][:B] if phase == "decode" else [N, 96][:B], dtype=np.int32)
+        kw["seq_lens"] = torch.as_tensor(lens, device=DEV)
+    if P is not None:
+        from test_gpu_kvcache import _paged
+        k, v, bt = _paged(k, v, P, seed=P)
+        kw["block_table"] = bt
+        if phase == "decode":
+            kw["seq_len"] = N
+    _say(f"[anchor dense output] {label}")
+    if phase == "decode":
+        idx, _ = kas.decode_anchor(q, k, v, 10, **kw)
+        idx_d, o_d = kas.decode_anchor(q, k, v, 10, dense_output=True, **kw)
+        o_ref = kas.decode_dense(q, k, v, **kw)
+    else:
+        idx, _ = kas.prefill_anchor(q, k, v, 10, **kw)
+        idx_d, o_d = kas.prefill_anchor(q, k, v, 10, dense_output=True, **kw)
+        o_ref = kas.prefill_dense(q, k, v, **kw)
+    torch.cuda.synchronize()
+    if varlen and phase == "decode":
+        for b in range(B):
+            kb = oracle.decode_k(int(lens[b]), 10)
+            assert torch.equal(idx[b, :, :kb], idx_d[b, :, :kb])
+    elif varlen:
+        off = oracle.prefill_offsets(N, 32, 10)
+        for b in range(B):
+            used = off[int(lens[b]) // 32]
+            assert torch.equal(idx[b, :, :used], idx_d[b, :, :used])
+    else:
+        assert torch.equal(idx, idx_d)
+    if varlen and phase == "prefill":
+        for b in range(B):
+            n = int(lens[b])
+            assert torch.equal(o_d[b, :, :n], o_ref[b, :, :n])
+    else:
+        assert torch.equal(o_d, o_ref)
+    # and against the oracle's dense attention (first sequence, its own keys)
+    qn, kn, vn = _np(q[:1]), _np(kc[:1]), _np(vc[:1])
+    if phase == "decode":
+        ref = oracle.dense_attention(qn[:, :, None, :], kn, vn, causal=False)[:, :, 0, :]
+    else:
+        ref = oracle.dense_attention(qn, kn, vn, causal=True)
+    err = max_abs(_np(o_d[:1]), ref)
+    _say(f"    sets bit-identical, output bit-identical to the dense call; max|o-o_oracle dense|={err:.3g}")
+    assert err <= TOL[dt]
