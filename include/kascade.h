@@ -350,10 +350,7 @@ typedef enum {
                                        longer prompts run their pooling and selection in tile ranges */
   KAS_OPT_PREFILL_SELECT_CAP = 3,   /* 0..8192 (default 8192): the largest first-digit bin the prefill
                                        Top-k resolves in LDS; larger bins take in-place passes */
-  KAS_OPT_PREFILL_SEPARATE_SELECT = 4, /* 1: the prefill Top-k runs as its own kernel after the pooling
-                                          pass; 0 / default -1: the pooling pass selects the rows it
-                                          wrote (pooling over all heads always takes the kernel) */
-  KAS_OPT_COUNT_ = 5
+  KAS_OPT_COUNT_ = 4
 } kas_option_t;
 /* KAS_ERR_INVALID_ARGUMENT for an unknown option or a value out of range. */
 kas_status_t kas_set_option(int32_t option, int64_t value);

@@ -33,7 +33,6 @@ from .binding import (  # noqa: F401
     OPT_DECODE_SELECT_ONE_PASS,
     OPT_PREFILL_POOL_MB,
     OPT_PREFILL_SELECT_CAP,
-    OPT_PREFILL_SEPARATE_SELECT,
     OP_DECODE_ANCHOR,
     OP_DECODE_REUSE,
     OP_PREFILL_ANCHOR,

@@ -139,7 +139,6 @@ def _check(rc: int, where: str) -> None:
 
 
 OPT_DECODE_SPLIT_ROWS, OPT_DECODE_SELECT_ONE_PASS, OPT_PREFILL_POOL_MB, OPT_PREFILL_SELECT_CAP = 0, 1, 2, 3
-OPT_PREFILL_SEPARATE_SELECT = 4
 
 
 def set_option(option: int, value: int) -> None:

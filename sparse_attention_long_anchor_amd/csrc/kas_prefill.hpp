@@ -38,7 +38,6 @@ struct PrefillArgs {
   // pass; null when the rows change after pooling (pool_all), then the select
   // histograms the rows itself
   int32_t* sel_pre;
-  int sel_fused;                    // the pooling pass runs the select on its own rows (no select launch)
   int sel_cap;                      // select: largest first-digit bin resolved in LDS
   // selection variants: pooled score = sum (0) or max (1) over the tile's rows
   // and the heads; pool_all: one set per tile over all heads, Hsel sets per

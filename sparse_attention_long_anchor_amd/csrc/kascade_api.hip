@@ -219,7 +219,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ------------------------------------------------------------------ tuning options
 
-static std::atomic<int64_t> g_options[KAS_OPT_COUNT_] = {{-1}, {-1}, {-1}, {-1}, {-1}};
+static std::atomic<int64_t> g_options[KAS_OPT_COUNT_] = {{-1}, {-1}, {-1}, {-1}};
 
 int64_t option_value(int id) {
   return (id >= 0 && id < KAS_OPT_COUNT_) ? g_options[id].load(std::memory_order_relaxed) : -1;
@@ -985,7 +985,6 @@ kas_status_t kas_set_option(int32_t option, int64_t value) {
       case KAS_OPT_DECODE_SELECT_ONE_PASS: ok = value == 0 || value == 1; break;
       case KAS_OPT_PREFILL_POOL_MB: ok = value >= 1 && value <= (int64_t(1) << 30); break;
       case KAS_OPT_PREFILL_SELECT_CAP: ok = value >= 0 && value <= 8192; break;
-      case KAS_OPT_PREFILL_SEPARATE_SELECT: ok = value == 0 || value == 1; break;
     }
     if (!ok) return fail(KAS_ERR_INVALID_ARGUMENT, "value %lld out of range for option %d", (long long)value, option);
   }

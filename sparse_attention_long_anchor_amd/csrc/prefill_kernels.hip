@@ -426,157 +426,6 @@ __global__ __launch_bounds__(64 * G, 2) void pre_stats_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------------ pass 2: pooled scores
 
-// ------------------------------------------------------------------ Top-k per tile
-
-// An exact radix select over a tile's pooled row (n = 32 t scores, rows
-// 128-byte aligned, so every access is a whole 16-byte load): the bin of the
-// k-th largest's first digit (bits 31..21), known from the pooling pass or
-// from a histogram pass over the row; the scores of that bin collected into
-// LDS in a pass over the row, digits 2 (bits 20..10) and 3 (bits 9..0)
-// resolved there (a bin too large for LDS is histogrammed in two more passes
-// over the row instead); a last pass writes the kept keys in index order
-// (P > tau, then the first r keys equal to tau) through workgroup scans.
-constexpr int kPreSelCap = 8192;   // LDS candidates of the k-th largest's first-digit bin
-
-// Exact Top-k of one pooled row by NT threads: P holds n scores (n a
-// multiple of 32, 0 < k < n, 16-byte aligned), the kept keys go to out in
-// index order. b1 >= 0: the first digit's bin of the k-th largest, the count
-// above it (ab1) and the bin's size (nb1) are known; else a pass histograms
-// the first digit. LDS: s_h (kBins1 words), s_cand (kPreSelCap), s_tmp (NT /
-// 64), s_res (2), s_nc (1). Passes keep four 16-byte loads per thread in
-// flight (indices past the row re-read its last vector and are not counted).
-template <int NT>
-__device__ __forceinline__ void select_row(const uint32_t* P, int n, uint32_t k, int32_t* out, int sel_cap,
-                                           int b1, uint32_t ab1, uint32_t nb1, uint32_t* s_h, uint32_t* s_cand,
-                                           uint32_t* s_tmp, int* s_res, uint32_t* s_nc) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n4 = n / 4;
-  // fn(v, valid) on the 16-byte vectors g0 + tid + NT q (q < 4) of each
-  // group; every thread runs every group (the candidate appends use wave-wide
-  // scans and shuffles), and indices past the row are loaded clamped and
-  // passed as invalid
-  auto pass = [&](auto&& fn) __attribute__((always_inline)) {
-    for (int g0 = 0; g0 < n4; g0 += 4 * NT) {
-      const int i0 = g0 + tid;
-      u32x4 v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = ldg16(P + 4 * min(i0 + NT * q, n4 - 1));
-#pragma unroll
-      for (int q = 0; q < 4; ++q) fn(v[q], i0 + NT * q < n4);
-    }
-  };
-  int b2, b3;
-  uint32_t ab2, ab3;
-  if (b1 >= 0) {
-    for (int i = tid; i < kBins2; i += NT) s_h[i] = 0u;
-    if (tid == 0) *s_nc = 0u;
-    __syncthreads();
-  } else {
-    for (int i = tid; i < kBins1; i += NT) s_h[i] = 0u;
-    if (tid == 0) *s_nc = 0u;
-    __syncthreads();
-    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
-      if (ok) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(&s_h[v[e] >> 21], 1u);
-      }
-    });
-    __syncthreads();
-    block_find_bin_nt<NT>(s_h, kBins1, k, s_tmp, s_res, b1, ab1);
-    nb1 = s_h[b1];
-    __syncthreads();
-    for (int i = tid; i < kBins2; i += NT) s_h[i] = 0u;
-    __syncthreads();
-  }
-  if (nb1 <= (uint32_t)sel_cap) {
-    // the bin's scores into LDS (wave-aggregated appends), digits 2 and 3 there
-    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c += (ok && (v[e] >> 21) == (uint32_t)b1) ? 1u : 0u;
-      const uint32_t inc = wave_incl_scan_u32(c);
-      uint32_t wbase = 0;
-      if (lane == 63 && inc) wbase = atomicAdd(s_nc, inc);
-      wbase = __shfl(wbase, 63);
-      uint32_t pos = wbase + inc - c;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ok && (v[e] >> 21) == (uint32_t)b1) s_cand[pos++] = v[e];
-    });
-    __syncthreads();
-    for (uint32_t i = tid; i < nb1; i += NT) atomicAdd(&s_h[(s_cand[i] >> 10) & 0x7ffu], 1u);
-    __syncthreads();
-    block_find_bin_nt<NT>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
-    for (int i = tid; i < kBins3; i += NT) s_h[i] = 0u;
-    __syncthreads();
-    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-    for (uint32_t i = tid; i < nb1; i += NT)
-      if ((s_cand[i] >> 10) == pre) atomicAdd(&s_h[s_cand[i] & 0x3ffu], 1u);
-    __syncthreads();
-    block_find_bin_nt<NT>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
-  } else {
-    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ok && (v[e] >> 21) == (uint32_t)b1) atomicAdd(&s_h[(v[e] >> 10) & 0x7ffu], 1u);
-    });
-    __syncthreads();
-    block_find_bin_nt<NT>(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
-    for (int i = tid; i < kBins3; i += NT) s_h[i] = 0u;
-    __syncthreads();
-    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ok && (v[e] >> 10) == pre) atomicAdd(&s_h[v[e] & 0x3ffu], 1u);
-    });
-    __syncthreads();
-    block_find_bin_nt<NT>(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
-  }
-  const uint32_t tau = (((uint32_t)b1 << 11 | (uint32_t)b2) << 10) | (uint32_t)b3;
-  const uint32_t r = k - ab1 - ab2 - ab3;
-  // stable compaction, 16 consecutive keys per thread per NT * 16-key chunk
-  // (n is a multiple of 32, so a thread's 16 keys are all in or all out)
-  constexpr int PER = 16;
-  uint32_t gt_run = 0, eq_run = 0;
-  for (int base = 0; base < n; base += NT * PER) {
-    const int j0 = base + tid * PER;
-    const bool in = j0 < n;
-    uint32_t u[PER];
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      const u32x4 v = ldg16(P + min(j0, n - PER) + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
-    }
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      gt += (in && u[i] > tau) ? 1u : 0u;
-      eq += (in && u[i] == tau) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<NT>((gt << 16) | eq, s_tmp, &tot);   // both below 2^16 per chunk
-    uint32_t g_ex = (ex >> 16) + gt_run;
-    uint32_t e_ex = (ex & 0xffffu) + eq_run;
-    if (in) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (u[i] > tau) {
-          const uint32_t pos = g_ex + min(e_ex, r);
-          if (pos < k) out[pos] = j0 + i;
-          ++g_ex;
-        } else if (u[i] == tau) {
-          if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = j0 + i;
-          ++e_ex;
-        }
-      }
-    }
-    gt_run += tot >> 16;
-    eq_run += tot & 0xffffu;
-  }
-}
-
 // One workgroup = tiles (t0 = 2p, t1 = 2p+1) of one KV head. For every staged
 // key block before a tile, each wave (query head) forms S = Q.K^T, the
 // probabilities exp2(s - lse_row), their sum over the tile's 32 rows; the G
@@ -594,15 +443,9 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   __shared__ __align__(1024) char s_k1[KD::BLKB];
   __shared__ __align__(1024) char s_k2[KD::BLKB];
   __shared__ float s_col[2][2][G][64];
-  // the first-digit histograms and the select (G >= 4: with one or two waves
-  // per workgroup their LDS would cost occupancy; the select kernel takes
-  // those shapes)
-  constexpr bool HIST = G >= 4;
-  __shared__ uint32_t s_h1[HIST ? 2 : 1][HIST ? kBins1 : 1];   // the two tiles' first-digit histograms
-  __shared__ uint32_t s_cand[HIST ? kPreSelCap : 1];           // the select's candidates (sel_fused)
+  __shared__ uint32_t s_h1[2][kBins1];     // first-digit histograms of the two tiles' pooled rows
   __shared__ uint32_t s_tmp[G];
   __shared__ int s_res[2];
-  __shared__ uint32_t s_nc;
   const int pa0 = a.t_begin / 2;
   const int npairs = (a.t_end + 1) / 2 - pa0;
   const WorkItem it = work_item(blockIdx.x, npairs, a.Hkv, a.Hkv * a.B, true);
@@ -620,10 +463,9 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   const int64_t lse_off = ((int64_t)b * a.Hq + h) * a.N;   // row statistics of this head
   // cleared before the first block's end barrier, whose wait covers LDS stores;
   // every histogram update comes after that barrier
-  const bool hist = HIST && a.sel_pre != nullptr;
-  if constexpr (HIST)
-    if (hist)
-      for (int i = threadIdx.x; i < 2 * kBins1; i += 64 * G) (&s_h1[0][0])[i] = 0u;
+  const bool hist = a.sel_pre != nullptr;
+  if (hist)
+    for (int i = threadIdx.x; i < 2 * kBins1; i += 64 * G) (&s_h1[0][0])[i] = 0u;
   u32x4 qa0[KC], qa1[KC];
   float lse0[16], lse1[16];
   {
@@ -722,8 +564,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < G; ++x) sum = pool(sum, s_col[kb & 1][tile][x][n32]);
       (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
-      if constexpr (HIST)
-        if (hist) atomicAdd(&s_h1[tile][__float_as_uint(sum) >> 21], 1u);
+      if (hist) atomicAdd(&s_h1[tile][__float_as_uint(sum) >> 21], 1u);
     }
   };
   const int w1 = G > 1 ? 1 : 0;
@@ -777,30 +618,19 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
       emit(0, kb, 0);
     }
   }
-  // each tile's first-digit bin of the k-th largest pooled score; then either
-  // the select here, on the rows this workgroup just wrote (their reads
-  // overlap the other workgroups' matrix work), or the bin for the select kernel
-  if constexpr (HIST) if (hist) {
+  // each tile's first-digit bin of the k-th largest pooled score, for the select
+  if (hist) {
     __syncthreads();
     for (int tile = 0; tile < (has1 ? 2 : 1); ++tile) {
       const int t = tile ? t1 : t0;
-      const int n = kTile * t;
       const uint32_t kt = (uint32_t)(a.offsets[t + 1] - a.offsets[t]);
-      int32_t* sel_out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.total + a.offsets[t];
-      if (t >= 1 && kt > 0 && kt < (uint32_t)n) {   // uniform over the workgroup
+      if (t >= 1 && kt > 0 && kt < (uint32_t)(kTile * t)) {   // uniform over the workgroup
         int b1;
         uint32_t ab1;
         block_find_bin_nt<64 * G>(s_h1[tile], kBins1, kt, s_tmp, s_res, b1, ab1);
-        const uint32_t nb1 = s_h1[tile][b1];
-        if (a.sel_fused) {
-          // s_h1[tile] serves as the select's histogram from here on
-          select_row<64 * G>(reinterpret_cast<const uint32_t*>(tile ? out1 : out0), n, kt, sel_out, a.sel_cap,
-                             b1, ab1, nb1, s_h1[tile], s_cand, s_tmp, s_res, &s_nc);
-        } else if (threadIdx.x == 0) {
-          reinterpret_cast<int4*>(a.sel_pre)[((int64_t)b * a.Hkv + g) * a.T + t] = int4{b1, (int)ab1, (int)nb1, 0};
-        }
-      } else if (a.sel_fused && t >= 1 && kt >= (uint32_t)n) {
-        for (int j = threadIdx.x; j < n; j += 64 * G) sel_out[j] = j;
+        if (threadIdx.x == 0)
+          reinterpret_cast<int4*>(a.sel_pre)[((int64_t)b * a.Hkv + g) * a.T + t] =
+              int4{b1, (int)ab1, (int)s_h1[tile][b1], 0};
       }
     }
   }
@@ -829,11 +659,20 @@ __global__ __launch_bounds__(256) void pre_pool_heads_kernel(PrefillArgs a) {
   }
 }
 
-// One workgroup per (tile, KV head): the exact Top-k of the tile's pooled row
-// (select_row), for the pooled rows the pooling pass did not select itself
-// (pooling over all heads, or the separate select chosen by the tuning
-// option). The first digit's bin comes from the pooling pass (sel_pre) when it
-// histogrammed the final row.
+// ------------------------------------------------------------------ Top-k per tile
+
+// One workgroup per (tile, KV head): an exact radix select over the tile's
+// pooled row (n = 32 t scores, rows 128-byte aligned, so every access is a
+// whole 16-byte load): the bin of the k-th largest's first digit (bits
+// 31..21), from the pooling pass (sel_pre) or a histogram pass over the row;
+// the scores of that bin collected into LDS in a pass over the row, digits 2
+// (bits 20..10) and 3 (bits 9..0) resolved there (a bin too large for LDS is
+// histogrammed in two more passes over the row instead); a
+// last pass writes the kept keys in index order (P > tau, then the first r
+// keys equal to tau) through workgroup scans. Passes keep four 16-byte loads
+// per thread in flight (indices past the row re-read its last vector and are
+// not counted).
+constexpr int kPreSelCap = 8192;   // LDS candidates of the k-th largest's first-digit bin
 __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   __shared__ uint32_t s_h[kBins1];
   __shared__ uint32_t s_cand[kPreSelCap];
@@ -844,26 +683,147 @@ __global__ __launch_bounds__(256) void pre_select_kernel(PrefillArgs a) {
   const int t = a.t_end - 1 - it.i;
   const int g = it.g, b = it.b;
   if (t < 1 || t >= tiles_of(a, b)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = kTile * t;
   const int o0 = a.offsets[t];
   const uint32_t k = (uint32_t)(a.offsets[t + 1] - o0);
   if (k == 0) return;
   int32_t* out = a.idx_out + ((int64_t)b * a.Hsel + g) * a.total + o0;   // g < Hsel
   if (k >= (uint32_t)n) {
-    for (int j = threadIdx.x; j < n; j += 256) out[j] = j;
+    for (int j = tid; j < n; j += 256) out[j] = j;
     return;
   }
   const uint32_t* P = reinterpret_cast<const uint32_t*>(a.pooled + pool_slot(a, b, g, t));
-  int b1 = -1;
-  uint32_t ab1 = 0, nb1 = 0;
+  const int n4 = n / 4;
+  // fn(v, valid) on the 16-byte vectors g0 + tid + 256 q (q < 4) of each
+  // group; every thread runs every group (the candidate appends use wave-wide
+  // scans and shuffles), and indices past the row are loaded clamped and
+  // passed as invalid
+  auto pass = [&](auto&& fn) __attribute__((always_inline)) {
+    for (int g0 = 0; g0 < n4; g0 += 4 * 256) {
+      const int i0 = g0 + tid;
+      u32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = ldg16(P + 4 * min(i0 + 256 * q, n4 - 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fn(v[q], i0 + 256 * q < n4);
+    }
+  };
+  int b1, b2, b3;
+  uint32_t ab1, ab2, ab3, nb1;
   if (a.sel_pre) {
     // the pooling pass histogrammed the row's first digit and found its bin
     const int4 pre = reinterpret_cast<const int4*>(a.sel_pre)[((int64_t)b * a.Hsel + g) * a.T + t];
     b1 = pre.x;
     ab1 = (uint32_t)pre.y;
     nb1 = (uint32_t)pre.z;
+    for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
+    if (tid == 0) s_nc = 0u;
+    __syncthreads();
+  } else {
+    for (int i = tid; i < kBins1; i += 256) s_h[i] = 0u;
+    if (tid == 0) s_nc = 0u;
+    __syncthreads();
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&s_h[v[e] >> 21], 1u);
+      }
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins1, k, s_tmp, s_res, b1, ab1);
+    nb1 = s_h[b1];
+    __syncthreads();
+    for (int i = tid; i < kBins2; i += 256) s_h[i] = 0u;
+    __syncthreads();
   }
-  select_row<256>(P, n, k, out, a.sel_cap, b1, ab1, nb1, s_h, s_cand, s_tmp, s_res, &s_nc);
+  if (nb1 <= (uint32_t)a.sel_cap) {
+    // the bin's scores into LDS (wave-aggregated appends), digits 2 and 3 there
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += (ok && (v[e] >> 21) == (uint32_t)b1) ? 1u : 0u;
+      const uint32_t inc = wave_incl_scan_u32(c);
+      uint32_t wbase = 0;
+      if (lane == 63 && inc) wbase = atomicAdd(&s_nc, inc);
+      wbase = __shfl(wbase, 63);
+      uint32_t pos = wbase + inc - c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 21) == (uint32_t)b1) s_cand[pos++] = v[e];
+    });
+    __syncthreads();
+    for (uint32_t i = tid; i < nb1; i += 256) atomicAdd(&s_h[(s_cand[i] >> 10) & 0x7ffu], 1u);
+    __syncthreads();
+    block_find_bin(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += 256) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    for (uint32_t i = tid; i < nb1; i += 256)
+      if ((s_cand[i] >> 10) == pre) atomicAdd(&s_h[s_cand[i] & 0x3ffu], 1u);
+    __syncthreads();
+    block_find_bin(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  } else {
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 21) == (uint32_t)b1) atomicAdd(&s_h[(v[e] >> 10) & 0x7ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins2, k - ab1, s_tmp, s_res, b2, ab2);
+    for (int i = tid; i < kBins3; i += 256) s_h[i] = 0u;
+    __syncthreads();
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    pass([&](const u32x4& v, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok && (v[e] >> 10) == pre) atomicAdd(&s_h[v[e] & 0x3ffu], 1u);
+    });
+    __syncthreads();
+    block_find_bin(s_h, kBins3, k - ab1 - ab2, s_tmp, s_res, b3, ab3);
+  }
+  const uint32_t tau = (((uint32_t)b1 << 11 | (uint32_t)b2) << 10) | (uint32_t)b3;
+  const uint32_t r = k - ab1 - ab2 - ab3;
+  // stable compaction, 16 consecutive keys per thread per 4096-key chunk
+  // (n is a multiple of 32, so a thread's 16 keys are all in or all out)
+  constexpr int PER = 16;
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int base = 0; base < n; base += 256 * PER) {
+    const int j0 = base + tid * PER;
+    const bool in = j0 < n;
+    uint32_t u[PER];
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 v = ldg16(P + min(j0, n - PER) + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[4 * q + e] = v[e];
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      gt += (in && u[i] > tau) ? 1u : 0u;
+      eq += (in && u[i] == tau) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan_256((gt << 16) | eq, s_tmp, &tot);   // both below 2^16 per chunk
+    uint32_t g_ex = (ex >> 16) + gt_run;
+    uint32_t e_ex = (ex & 0xffffu) + eq_run;
+    if (in) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (u[i] > tau) {
+          const uint32_t pos = g_ex + min(e_ex, r);
+          if (pos < k) out[pos] = j0 + i;
+          ++g_ex;
+        } else if (u[i] == tau) {
+          if (e_ex < r && g_ex + e_ex < k) out[g_ex + e_ex] = j0 + i;
+          ++e_ex;
+        }
+      }
+    }
+    gt_run += tot >> 16;
+    eq_run += tot & 0xffffu;
+  }
 }
 
 // ------------------------------------------------------------------ sparse tile attention
@@ -1344,12 +1304,7 @@ hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) { return launch_
 
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   hipError_t e;
-  // no first-digit bins from the pooling pass when the heads' rows are summed
-  // after pooling, or for groups of fewer than 4 heads (see pre_pool_kernel)
-  if (a.pool_all || a.G < 4) a.sel_pre = nullptr;
-  // the pooling pass selects its own rows unless they change afterwards or the
-  // tuning option asks for the separate select kernel
-  a.sel_fused = a.sel_pre != nullptr && option_value(KAS_OPT_PREFILL_SEPARATE_SELECT) != 1;
+  if (a.pool_all) a.sel_pre = nullptr;   // the heads' rows are summed after pooling
   if ((e = launch_offsets(a, ctx)) != hipSuccess) return e;
   if (!grid_fits((int64_t)((a.T + 1) / 2) * a.Hkv * a.B)) return hipErrorInvalidConfiguration;
   ctx.begin(K_PRE_STATS);
@@ -1383,12 +1338,10 @@ hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
       else KAS_LAUNCH_P(pre_pool_heads_kernel<0>, dim3(tb - ta, a.B), dim3(256), ctx, a);
       if ((e = ctx.end(K_PRE_POOL_HEADS)) != hipSuccess) return e;
     }
-    if (!a.sel_fused) {
-      dim3 grid((unsigned)((int64_t)(tb - ta) * a.Hsel * a.B));
-      ctx.begin(K_PRE_SELECT);
-      KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx, a);
-      if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;
-    }
+    dim3 grid((unsigned)((int64_t)(tb - ta) * a.Hsel * a.B));
+    ctx.begin(K_PRE_SELECT);
+    KAS_LAUNCH_P(pre_select_kernel, grid, dim3(256), ctx, a);
+    if ((e = ctx.end(K_PRE_SELECT)) != hipSuccess) return e;
     ta = tb;
   }
   return a.dense_out ? launch_prefill_dense(a, ctx) : launch_attn(a, ctx);

@@ -282,7 +282,7 @@ def test_qo_stride_validation_without_gpu():
 
 def test_tuning_options_without_gpu():
     b = _kas()
-    for opt in range(5):
+    for opt in range(4):
         assert b.get_option(opt) == -1
     b.set_option(b.OPT_DECODE_SPLIT_ROWS, 64)
     try:
@@ -292,7 +292,7 @@ def test_tuning_options_without_gpu():
     assert b.get_option(b.OPT_DECODE_SPLIT_ROWS) == -1
     for opt, val in [(b.OPT_DECODE_SPLIT_ROWS, 8), (b.OPT_DECODE_SPLIT_ROWS, 4096),
                      (b.OPT_DECODE_SELECT_ONE_PASS, 2), (b.OPT_PREFILL_POOL_MB, 0),
-                     (b.OPT_PREFILL_SELECT_CAP, 8193), (b.OPT_PREFILL_SEPARATE_SELECT, 2), (5, 1), (-1, 1)]:
+                     (b.OPT_PREFILL_SELECT_CAP, 8193), (4, 1), (-1, 1)]:
         assert _status(lambda: b.set_option(opt, val)) == 1, (opt, val)
     # a smaller pooled-score cap shrinks the prefill anchor workspace
     import torch

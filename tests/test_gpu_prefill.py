@@ -205,22 +205,3 @@ def test_prefill_pooling_in_tile_ranges(kas_options):
     torch.cuda.synchronize()
     assert torch.equal(gidx, gidx2) and torch.equal(go, go2)
     _check_tiles(w, q, k, v, 10, gidx2, go2, (1, 17, 40, 63), "pool_ranges")
-
-
-@pytest.mark.parametrize("G", [4, 8, 2])
-def test_prefill_select_in_pooling_pass_matches_select_kernel(G, kas_options):
-    """For groups of 4 or more heads the pooling pass selects the rows it wrote
-    (KAS_OPT_PREFILL_SEPARATE_SELECT 0); the separate select kernel (option 1)
-    gives the same index sets and outputs bit for bit. Groups of 2 always take
-    the kernel (both settings agree trivially)."""
-    kas = _kas()
-    Hkv = 2
-    w = inputgen.custom("prefill", 1, G * Hkv, Hkv, 128, 2048, "bf16", wid=63 + G)
-    q, k, v = inputgen.layer_inputs(w, 0, DEV)
-    kas_options(kas.OPT_PREFILL_SEPARATE_SELECT, 0)
-    gidx, go = kas.prefill_anchor(q, k, v, 10)
-    kas_options(kas.OPT_PREFILL_SEPARATE_SELECT, 1)
-    gidx2, go2 = kas.prefill_anchor(q, k, v, 10)
-    torch.cuda.synchronize()
-    assert torch.equal(gidx, gidx2) and torch.equal(go, go2)
-    _check_tiles(w, q, k, v, 10, gidx, go, (1, 2, 31, 63), f"select_paths_g{G}")
