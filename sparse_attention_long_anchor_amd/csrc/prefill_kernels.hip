@@ -443,7 +443,11 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   __shared__ __align__(1024) char s_k1[KD::BLKB];
   __shared__ __align__(1024) char s_k2[KD::BLKB];
   __shared__ float s_col[2][2][G][64];
-  __shared__ uint32_t s_h1[2][kBins1];     // first-digit histograms of the two tiles' pooled rows
+  // first-digit histograms of the two tiles' pooled rows (G >= 4: with one or
+  // two waves per workgroup their LDS would cost a wave per SIMD; the select
+  // kernel histograms those rows itself)
+  constexpr bool HIST = G >= 4;
+  __shared__ uint32_t s_h1[HIST ? 2 : 1][HIST ? kBins1 : 1];
   __shared__ uint32_t s_tmp[G];
   __shared__ int s_res[2];
   const int pa0 = a.t_begin / 2;
@@ -463,9 +467,10 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
   const int64_t lse_off = ((int64_t)b * a.Hq + h) * a.N;   // row statistics of this head
   // cleared before the first block's end barrier, whose wait covers LDS stores;
   // every histogram update comes after that barrier
-  const bool hist = a.sel_pre != nullptr;
-  if (hist)
-    for (int i = threadIdx.x; i < 2 * kBins1; i += 64 * G) (&s_h1[0][0])[i] = 0u;
+  const bool hist = HIST && a.sel_pre != nullptr;
+  if constexpr (HIST)
+    if (hist)
+      for (int i = threadIdx.x; i < 2 * kBins1; i += 64 * G) (&s_h1[0][0])[i] = 0u;
   u32x4 qa0[KC], qa1[KC];
   float lse0[16], lse1[16];
   {
@@ -564,7 +569,8 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
 #pragma unroll
       for (int x = 0; x < G; ++x) sum = pool(sum, s_col[kb & 1][tile][x][n32]);
       (tile == 0 ? out0 : out1)[kTile * kb + n32] = sum;
-      if (hist) atomicAdd(&s_h1[tile][__float_as_uint(sum) >> 21], 1u);
+      if constexpr (HIST)
+        if (hist) atomicAdd(&s_h1[tile][__float_as_uint(sum) >> 21], 1u);
     }
   };
   const int w1 = G > 1 ? 1 : 0;
@@ -619,7 +625,7 @@ __global__ __launch_bounds__(64 * G, 2) void pre_pool_kernel(PrefillArgs a) {
     }
   }
   // each tile's first-digit bin of the k-th largest pooled score, for the select
-  if (hist) {
+  if constexpr (HIST) if (hist) {
     __syncthreads();
     for (int tile = 0; tile < (has1 ? 2 : 1); ++tile) {
       const int t = tile ? t1 : t0;
@@ -1304,7 +1310,9 @@ hipError_t launch_prefill_dense(PrefillArgs& a, LaunchCtx& ctx) { return launch_
 
 hipError_t launch_prefill_anchor(PrefillArgs& a, LaunchCtx& ctx) {
   hipError_t e;
-  if (a.pool_all) a.sel_pre = nullptr;   // the heads' rows are summed after pooling
+  // no first-digit bins from the pooling pass when the heads' rows are summed
+  // after pooling, or for groups of fewer than 4 heads (see pre_pool_kernel)
+  if (a.pool_all || a.G < 4) a.sel_pre = nullptr;
   if ((e = launch_offsets(a, ctx)) != hipSuccess) return e;
   if (!grid_fits((int64_t)((a.T + 1) / 2) * a.Hkv * a.B)) return hipErrorInvalidConfiguration;
   ctx.begin(K_PRE_STATS);
