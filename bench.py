@@ -501,6 +501,22 @@ def main():
     wall_k = time.perf_counter() - t1
     log(f"[bench] per-kernel timing pass: {args.steps} steps in {wall_k:.3f} s")
 
+    # The decode step again, captured once in a HIP graph and replayed (how a
+    # serving loop would run it: the same kernels on the same inputs, without
+    # host launch work). Reported beside the eager figures; the replay's index
+    # sets and output are compared bit for bit with the eager step's.
+    dec_graph = None
+    if do_dec:
+        _, d_idx, d_o, _, _, _ = dec_state
+        run_decode_step(wd, dec_state, inputgen, kas)
+        torch.cuda.synchronize()
+        ref_o = d_o.clone()
+        ref_idx = {a_: t_.clone() for a_, t_ in d_idx.items()}
+        g_ms = graph_step_ms(wd, dec_state, run_decode_step, args.steps, torch, inputgen, kas)
+        same = bool(torch.equal(ref_o, d_o)) and all(torch.equal(ref_idx[a_], d_idx[a_]) for a_ in ref_idx)
+        dec_graph = (g_ms, same)
+        log(f"[bench] decode step from a HIP graph: {g_ms:.4f} ms, outputs bit-identical to eager: {same}")
+
     kern_ms = {}
     for name in kas.profile_names():
         ms, n = kas.profile_query(name)
@@ -540,6 +556,13 @@ def main():
             "ms_per_step": round(step_ms, 4),
             "tokens_per_s": round(wd.batch / (step_ms * 1e-3), 2),
         }
+        if dec_graph is not None:
+            g_ms, same = dec_graph
+            out["decode"]["graph"] = {
+                "ms_per_step": round(g_ms, 4), "tokens_per_s": round(wd.batch / (g_ms * 1e-3), 2),
+                "GB_per_s": round(step_bytes / (g_ms * 1e-3) / 1e9, 2),
+                "bit_identical_to_eager": same,
+                "note": "the whole step captured once in a HIP graph and replayed; value stays the eager figure"}
         n_anc, n_reu = len(anc) * args.steps, len(reu) * args.steps
         ops = {"decode_attn": n_reu, "decode_attn_anchor": n_anc, "decode_score": n_anc}
         for name, b in kern_b.items():
