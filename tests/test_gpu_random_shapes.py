@@ -1,0 +1,97 @@
+"""GPU parity over shapes drawn at random once, from a seeded generator, so
+every run checks the same cases. Each case runs the anchor and a reuse layer
+through the C ABI and checks them against the CPU oracle with the same helpers
+and tolerances as the fixed-shape tests: index sets equal except near ties,
+outputs within the dtype's tolerance, k = N against dense attention.
+
+Decode: B 1-3, 1-4 KV heads, 1-8 query heads per KV head, D 64 or 128,
+N 1-12000 keys (a third of the cases below 300), 1-100 %, fp32, bf16 or
+fp16. Prefill: B 1-2, 1-2 KV heads, 1-8 query heads per KV head, D 64 or 128,
+1-24 tiles, 1-100 %, bf16 or fp16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import oracle
+from parity_util import TOL, max_abs
+from test_gpu_decode import _check_anchor, _check_reuse
+from test_gpu_prefill import _check_reuse_tiles, _check_tiles
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _decode_cases(n, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 300)) if i % 3 == 0 else int(rng.integers(300, 12001))
+        out.append((int(rng.integers(1, 4)), int(rng.choice([1, 2, 4])), int(rng.choice([1, 2, 4, 8])),
+                    int(rng.choice([64, 128])), N, int(rng.integers(1, 101)),
+                    str(rng.choice(["bf16", "f16", "f32"])), int(rng.integers(0, 1000))))
+    return out
+
+
+def _prefill_cases(n, seed=20261204):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 3)), int(rng.choice([1, 2])), int(rng.choice([1, 2, 4, 8])),
+             int(rng.choice([64, 128])), int(rng.integers(1, 25)), int(rng.integers(1, 101)),
+             str(rng.choice(["bf16", "f16"])), int(rng.integers(0, 1000))) for _ in range(n)]
+
+
+DECODE_CASES = _decode_cases(40)
+PREFILL_CASES = _prefill_cases(40)
+
+
+def _id(c):
+    return "B{}_Hkv{}_G{}_D{}_N{}_pct{}_{}_w{}".format(*c)
+
+
+def _kas():
+    import sparse_attention_long_anchor_amd as kas
+    return kas
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[_id(c) for c in DECODE_CASES])
+def test_decode_random_shapes(case):
+    B, Hkv, G, D, N, pct, dt, wid = case
+    label = f"random decode B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} wid{wid}"
+    w = inputgen.custom("decode", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx, o = _check_anchor(w, q, k, v, pct, label)
+    if oracle.decode_k(N, pct) == N:
+        dense = oracle.dense_attention(_np(q)[:, :, None, :], _np(k), _np(v), causal=False)[:, :, 0, :]
+        assert max_abs(_np(o), dense) <= TOL[dt]
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(wid).integers(0, Hkv, Hkv).astype(np.int32)
+    _check_reuse(w, q2, k2, v2, idx, hm, pct, label)
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[_id((c[0], c[1], c[2], c[3], 32 * c[4], c[5], c[6], c[7])) for c in PREFILL_CASES])
+def test_prefill_random_shapes(case):
+    B, Hkv, G, D, T, pct, dt, wid = case
+    N = 32 * T
+    label = f"random prefill B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} wid{wid}"
+    print(f"[prefill anchor] {label}", flush=True)
+    kas = _kas()
+    w = inputgen.custom("prefill", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    gidx, go = kas.prefill_anchor(q, k, v, pct)
+    torch.cuda.synchronize()
+    _check_tiles(w, q, k, v, pct, gidx, go, range(T), label)
+    if pct == 100:
+        dense = oracle.dense_attention(_np(q), _np(k), _np(v), causal=True)
+        assert max_abs(_np(go), dense) <= TOL[dt]
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(wid).integers(0, Hkv, Hkv).astype(np.int32)
+    print(f"[prefill reuse] {label}", flush=True)
+    o2 = kas.prefill_reuse(q2, k2, v2, gidx, torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    _check_reuse_tiles(w, q2, k2, v2, pct, gidx, hm, o2, range(T), label)
