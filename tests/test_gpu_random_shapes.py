@@ -7,7 +7,11 @@ outputs within the dtype's tolerance, k = N against dense attention.
 Decode: B 1-3, 1-4 KV heads, 1-8 query heads per KV head, D 64 or 128,
 N 1-12000 keys (a third of the cases below 300), 1-100 %, fp32, bf16 or
 fp16. Prefill: B 1-2, 1-2 KV heads, 1-8 query heads per KV head, D 64 or 128,
-1-24 tiles, 1-100 %, bf16 or fp16.
+1-24 tiles, 1-100 %, bf16 or fp16. Varlen and paged caches (the same
+helpers as the fixed kv-cache tests): per-sequence lengths drawn in [1, N]
+with one sequence at full length, page sizes 16-1024 (bf16 and fp16; a
+paged fp32 cache is unsupported), every sequence against the oracle and
+the paged calls against the contiguous ones.
 """
 import numpy as np
 import pytest
@@ -17,6 +21,7 @@ import inputgen
 import oracle
 from parity_util import TOL, max_abs
 from test_gpu_decode import _check_anchor, _check_reuse
+from test_gpu_kvcache import _check_prefill_paged, _check_prefill_varlen, _check_varlen
 from test_gpu_prefill import _check_reuse_tiles, _check_tiles
 
 pytestmark = pytest.mark.gpu
@@ -42,12 +47,39 @@ def _prefill_cases(n, seed=20261204):
              str(rng.choice(["bf16", "f16"])), int(rng.integers(0, 1000))) for _ in range(n)]
 
 
+def _kv_cases(n, phase, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dec = phase == "decode"
+        dt = str(rng.choice(["bf16", "f16", "f32"] if dec else ["bf16", "f16"]))
+        paged = dt != "f32" and rng.random() < 0.75
+        P = int(rng.choice([16, 32, 64, 128, 256, 1024])) if paged else 0
+        N = int(rng.integers(1, 9001)) if dec else 32 * int(rng.integers(1, 25))
+        out.append((int(rng.integers(1, 5)), int(rng.choice([1, 2, 4])), int(rng.choice([1, 2, 4, 8])),
+                    int(rng.choice([64, 128])), N, int(rng.integers(1, 101)), dt, P, int(rng.integers(0, 1000))))
+    return out
+
+
 DECODE_CASES = _decode_cases(40)
 PREFILL_CASES = _prefill_cases(40)
+KV_DECODE_CASES = _kv_cases(20, "decode", 20261205)
+KV_PREFILL_CASES = _kv_cases(12, "prefill", 20261206)
 
 
 def _id(c):
     return "B{}_Hkv{}_G{}_D{}_N{}_pct{}_{}_w{}".format(*c)
+
+
+def _kv_id(c):
+    return "B{}_Hkv{}_G{}_D{}_N{}_pct{}_{}_P{}_w{}".format(*c)
+
+
+def _lengths(B, N, wid, step=1):
+    """Per-sequence lengths in [1, N] (multiples of `step`), the first at N."""
+    L = np.random.default_rng(wid).integers(1, N // step + 1, B) * step
+    L[0] = N
+    return L.astype(np.int32)
 
 
 def _kas():
@@ -95,3 +127,24 @@ def test_prefill_random_shapes(case):
     o2 = kas.prefill_reuse(q2, k2, v2, gidx, torch.as_tensor(hm, device=DEV), pct)
     torch.cuda.synchronize()
     _check_reuse_tiles(w, q2, k2, v2, pct, gidx, hm, o2, range(T), label)
+
+
+@pytest.mark.parametrize("case", KV_DECODE_CASES, ids=[_kv_id(c) for c in KV_DECODE_CASES])
+def test_decode_varlen_paged_random_shapes(case):
+    B, Hkv, G, D, N, pct, dt, P, wid = case
+    label = f"random decode varlen B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} P{P} wid{wid}"
+    w = inputgen.custom("decode", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    _check_varlen(w, q, k, v, _lengths(B, N, wid), pct, label, P or None)
+
+
+@pytest.mark.parametrize("case", KV_PREFILL_CASES, ids=[_kv_id(c) for c in KV_PREFILL_CASES])
+def test_prefill_varlen_paged_random_shapes(case):
+    B, Hkv, G, D, N, pct, dt, P, wid = case
+    label = f"random prefill varlen B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} P{P} wid{wid}"
+    w = inputgen.custom("prefill", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    lens = _lengths(B, N, wid)
+    ref = _check_prefill_varlen(w, q, k, v, lens, pct, label)
+    if P:
+        _check_prefill_paged(w, q, k, v, lens, pct, P, ref)
