@@ -11,7 +11,10 @@ fp16. Prefill: B 1-2, 1-2 KV heads, 1-8 query heads per KV head, D 64 or 128,
 helpers as the fixed kv-cache tests): per-sequence lengths drawn in [1, N]
 with one sequence at full length, page sizes 16-1024 (bf16 and fp16; a
 paged fp32 cache is unsupported), every sequence against the oracle and
-the paged calls against the contiguous ones.
+the paged calls against the contiguous ones. Selection variants: pooling
+over all heads and max-pooling, decode and prefill; proposal-refined
+decode reuse with a pool of 1-100 % drawn at or above the refined layer's
+share.
 """
 import numpy as np
 import pytest
@@ -23,6 +26,9 @@ from parity_util import TOL, max_abs
 from test_gpu_decode import _check_anchor, _check_reuse
 from test_gpu_kvcache import _check_prefill_paged, _check_prefill_varlen, _check_varlen
 from test_gpu_prefill import _check_reuse_tiles, _check_tiles
+from test_gpu_variants import _check_decode as _check_decode_variant
+from test_gpu_variants import _check_prefill_tiles as _check_prefill_variant
+from test_gpu_variants import _check_refine
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +71,13 @@ DECODE_CASES = _decode_cases(40)
 PREFILL_CASES = _prefill_cases(40)
 KV_DECODE_CASES = _kv_cases(20, "decode", 20261205)
 KV_PREFILL_CASES = _kv_cases(12, "prefill", 20261206)
+# (pool_scope, pool_op) other than the default (0, 0), drawn per case
+VARIANT_DECODE_CASES = [c + (v,) for c, v in zip(_decode_cases(12, seed=20261207),
+                        np.random.default_rng(7).integers(0, 3, 12).tolist())]
+VARIANT_PREFILL_CASES = [c + (v,) for c, v in zip(_prefill_cases(12, seed=20261208),
+                         np.random.default_rng(8).integers(0, 3, 12).tolist())]
+VARIANTS = [(0, 1), (1, 0), (1, 1)]
+REFINE_CASES = [c + (int(np.random.default_rng(c[7]).integers(c[5], 101)),) for c in _decode_cases(16, seed=20261209)]
 
 
 def _id(c):
@@ -148,3 +161,61 @@ def test_prefill_varlen_paged_random_shapes(case):
     ref = _check_prefill_varlen(w, q, k, v, lens, pct, label)
     if P:
         _check_prefill_paged(w, q, k, v, lens, pct, P, ref)
+
+
+@pytest.mark.parametrize("case", VARIANT_DECODE_CASES, ids=[_id(c[:8]) + f"_v{c[8]}" for c in VARIANT_DECODE_CASES])
+def test_decode_variant_random_shapes(case):
+    B, Hkv, G, D, N, pct, dt, wid, vi = case
+    scope, op = VARIANTS[vi]
+    label = f"random decode variant B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} scope{scope} op{op} wid{wid}"
+    w = inputgen.custom("decode", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    idx = _check_decode_variant(w, q, k, v, pct, scope, op, label)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    kas = _kas()
+    if scope:
+        o2 = kas.decode_reuse(q2, k2, v2, idx, None, pct)
+        hm = np.zeros(Hkv, np.int32)
+    else:
+        hm = np.random.default_rng(wid).integers(0, Hkv, Hkv).astype(np.int32)
+        o2 = kas.decode_reuse(q2, k2, v2, idx, torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    ref = oracle.decode_reuse(_np(q2), _np(k2), _np(v2), idx.cpu().numpy(), hm)
+    assert max_abs(_np(o2), ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("case", VARIANT_PREFILL_CASES,
+                         ids=[_id((c[0], c[1], c[2], c[3], 32 * c[4], c[5], "bf16", c[7])) + f"_v{c[8]}"
+                              for c in VARIANT_PREFILL_CASES])
+def test_prefill_variant_random_shapes(case):
+    B, Hkv, G, D, T, pct, _, wid, vi = case
+    scope, op = VARIANTS[vi]
+    N = 32 * T
+    label = f"random prefill variant B{B} Hkv{Hkv} G{G} D{D} N{N} pct{pct} scope{scope} op{op} wid{wid}"
+    print(f"[prefill anchor] {label}", flush=True)
+    kas = _kas()
+    w = inputgen.custom("prefill", B, Hkv * G, Hkv, D, N, "bf16", wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    gidx, go = kas.prefill_anchor(q, k, v, pct, pool_scope=scope, pool_op=op)
+    torch.cuda.synchronize()
+    _check_prefill_variant(w, q, k, v, pct, scope, op, gidx, go, range(T), label)
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.zeros(Hkv, np.int32) if scope else np.random.default_rng(wid).integers(0, Hkv, Hkv).astype(np.int32)
+    o2 = kas.prefill_reuse(q2, k2, v2, gidx, None if scope else torch.as_tensor(hm, device=DEV), pct)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_reuse(_np(q2), _np(k2), _np(v2), gidx.cpu().numpy(), hm, pct)
+    assert max_abs(_np(o2), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", REFINE_CASES, ids=[_id(c[:8]) + f"_pool{c[8]}" for c in REFINE_CASES])
+def test_decode_refine_random_shapes(case):
+    B, Hkv, G, D, N, pct, dt, wid, ppct = case
+    label = f"random decode refine B{B} Hkv{Hkv} G{G} D{D} N{N} {dt} pct{pct} pool{ppct} wid{wid}"
+    print(f"[decode refine] {label}", flush=True)
+    kas = _kas()
+    w = inputgen.custom("decode", B, Hkv * G, Hkv, D, N, dt, wid=wid, topk_pct=pct)
+    q, k, v = inputgen.layer_inputs(w, 0, DEV)
+    pool, _ = kas.decode_anchor(q, k, v, ppct)                      # the proposal layer
+    q2, k2, v2 = inputgen.layer_inputs(w, 1, DEV)
+    hm = np.random.default_rng(wid).integers(0, Hkv, Hkv).astype(np.int32)
+    _check_refine(w, q2, k2, v2, pool, hm, pct, label)
